@@ -1,0 +1,255 @@
+/*
+ * tria.h - C ABI of the block-sparse, mixed-precision (int8 / int4 / skip) causal
+ * attention library for one AMD Instinct MI355X (gfx950).
+ *
+ * Method.  The TriAttention summary page (rit.work, "TriAttention: sparse
+ * mixed-precision attention") describes it in its section on which links can be
+ * skipped and which must not be removed: the attention matrix is cut into
+ * (query block, key block) tiles, and each tile is skipped, computed at 4 bits or
+ * computed at 8 bits according to its distance from the diagonal.  Each head keeps
+ * one pair of boundaries (hi, keep); the first key block and the diagonal block are
+ * always kept at 8 bits.  The section on calibration adds that one fused prefill
+ * kernel groups the kept tiles by precision and reduces them into one normalised
+ * result, and that the prepared keys and values then go to a compressed KV cache
+ * that generation reads.  The KV layout is grouped-query attention (llmis.ru
+ * chapter 3.5, section 4): query head h uses KV head h / (Hq / Hkv).
+ *
+ * Conventions for every call.
+ *  - Device pointers are caller-owned (for example PyTorch tensors).  The library
+ *    never allocates or frees device memory and keeps no device state.
+ *  - Device calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the legacy default stream).  Host-only calls are synchronous.
+ *  - Every argument is validated before anything is enqueued; a non-OK status
+ *    means nothing was enqueued.  tria_last_error() returns the message of the
+ *    last non-OK status on the calling thread.  No C++ exception crosses the ABI.
+ *  - Tensors are dense and contiguous in BHSD order: [batch][head][token][dim].
+ *  - Supported shapes: head_dim in {64, 128}; block in {64, 128};
+ *    n_q_heads % n_kv_heads == 0; seq_len >= 1; n_kv_heads <= TRIA_MAX_KV_HEADS.
+ *  - Thread safety: calls may come from several host threads; the only library
+ *    state is the thread-local error message.
+ */
+#ifndef TRIA_H
+#define TRIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tria_status {
+  TRIA_OK = 0,
+  TRIA_ERR_INVALID_ARG = 1,      /* null pointer, bad shape, hi > keep, corrupt header */
+  TRIA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head_dim, block, head count) */
+  TRIA_ERR_BUFFER_TOO_SMALL = 3, /* a caller buffer is smaller than required */
+  TRIA_ERR_HIP = 4               /* the HIP runtime reported an error at launch */
+} tria_status;
+
+#define TRIA_MAX_KV_HEADS 128
+
+/* Problem shape.  seq_len is the prompt length n for prefill, and the number of
+ * token rows in the K/V source tensors for the cache packer. */
+typedef struct tria_dims {
+  int32_t batch;      /* b */
+  int32_t n_q_heads;  /* Hq */
+  int32_t n_kv_heads; /* Hkv */
+  int32_t head_dim;   /* d */
+  int32_t block;      /* B, tokens per block on both the query and key side */
+  int32_t reserved;   /* must be 0 */
+  int64_t seq_len;    /* n */
+} tria_dims;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* tria_last_error(void);
+/* Library version, (major << 16) | minor. */
+int32_t tria_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* (1) Policy expander.  Host only.                                           */
+/* ------------------------------------------------------------------------- */
+/*
+ * Tile actions (TriAttention page, section on which links can be skipped: the
+ * three actions, the distance rule, the two protected blocks and the per-head
+ * boundary pair whose size does not grow with the context).  For query head h
+ * with boundaries (hi[h], keep[h]), query block qb and causal key block kb <= qb,
+ * with distance delta = qb - kb:
+ *     int8  if kb == 0 or delta == 0 or delta <= hi[h]
+ *     int4  else if delta <= keep[h]
+ *     skip  otherwise.
+ * Boundaries are in blocks, inclusive, with 0 <= hi[h] <= keep[h]; values at or
+ * above nb - 1 mean "everything" (nb = ceil(seq_len / block)).
+ *
+ * Schedule blob written to sched_host (little-endian int32 words):
+ *   words 0..15  header: [0] TRIA_SCHED_MAGIC, [1] TRIA_SCHED_VERSION, [2] batch,
+ *                [3] n_q_heads, [4] n_kv_heads, [5] head_dim, [6] block, [7] nb,
+ *                [8] n_units = batch * n_q_heads * nb, [9] 0,
+ *                [10] seq_len low 32 bits, [11] seq_len high 32 bits, [12..15] 0.
+ *   then n_units records of 8 int32, one work unit = (b, h, qb):
+ *                {b, h, qb, lo8, lo4, hi4, sink, ntiles}
+ *     int8 range  [lo8, qb], the longest run of int8 blocks ending at qb:
+ *                 lo8 = qb - hi[h] if that is >= 2, else 0 (block 0 joins the
+ *                 run when it is adjacent to it)
+ *     int4 range  [lo4, hi4] = [max(1, qb - keep[h]), qb - hi[h] - 1],
+ *                 stored as (0, -1) when empty
+ *     sink        1 if block 0 is int8 but lies outside the int8 range (lo8 > 0)
+ *     ntiles      (qb - lo8 + 1) + sink + (hi4 - lo4 + 1)
+ *   Record order: ntiles descending, ties by (b, h, qb) ascending (longest work
+ *   first, so a GPU that launches work groups in order balances its load).
+ * Total size: TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * n_units.
+ *
+ * n_policy_heads must equal n_q_heads.  If sched_host is NULL or sched_bytes is
+ * too small, *sched_bytes_needed (if non-NULL) receives the size and the call
+ * returns TRIA_ERR_BUFFER_TOO_SMALL (sched_host == NULL with a non-NULL
+ * sched_bytes_needed is the size query and returns TRIA_OK).
+ * The caller copies the blob to device memory for tria_prefill.
+ */
+#define TRIA_SCHED_MAGIC 0x48435354 /* "TSCH" */
+#define TRIA_SCHED_VERSION 1
+#define TRIA_SCHED_HEADER_BYTES 64
+#define TRIA_SCHED_UNIT_BYTES 32
+tria_status tria_build_policy(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                              int32_t n_policy_heads, void* sched_host, size_t sched_bytes,
+                              size_t* sched_bytes_needed);
+
+/* ------------------------------------------------------------------------- */
+/* (2) Quantiser.  Device, asynchronous.                                      */
+/* ------------------------------------------------------------------------- */
+/*
+ * Per-row symmetric quantisation of Q [b][Hq][n][d] and K [b][Hkv][n][d] (bf16)
+ * to 8-bit and 4-bit codes (TriAttention page, section on which links can be
+ * skipped: tiles are computed at 8 or 4 bits).  A row is the d values of one
+ * token of one head.  With qmax = 127 (int8) or 7 (int4), in IEEE fp32:
+ *     amax  = max_i |x_i|
+ *     scale = amax / qmax                     (correctly rounded division)
+ *     r     = qmax / amax                     (correctly rounded division)
+ *     code  = clamp(rint(x_i * r), -qmax, qmax)   (fp32 product, ties to even)
+ * A row with amax == 0 has scale 0 and all codes 0.  Inputs must be finite.
+ * Outputs: q8 int8 [b][Hq][n][d]; q4 uint8 [b][Hq][n][d/2] with byte j =
+ * (c[2j] & 0xF) | (c[2j+1] << 4) (two's-complement nibbles, low nibble first);
+ * q8s, q4s fp32 [b][Hq][n] (the scales).  k8, k4, k8s, k4s likewise with Hkv.
+ * Q is quantised unscaled; sm_scale is applied to the scores in tria_prefill.
+ */
+tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const void* k_bf16,
+                             int8_t* q8, uint8_t* q4, float* q8s, float* q4s,
+                             int8_t* k8, uint8_t* k4, float* k8s, float* k4s, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* (3) Fused prefill.  Device, asynchronous.                                  */
+/* ------------------------------------------------------------------------- */
+/*
+ * Causal block-sparse attention over the schedule (TriAttention page, section on
+ * calibration: one fused kernel groups kept blocks by precision and produces one
+ * normalised result).  For query row i of head h (KV head g, query block qb):
+ *   J_i   = { j <= i : tile (qb, j / block) is not skipped }
+ *   S_ij  = dot(Qc_i, Kc_j) in exact integer arithmetic, with the codes of the
+ *           tile's precision (both Q and K use 4-bit codes in an int4 tile)
+ *   t_ij  = S_ij * sq_i * sk_j * sm_scale * log2(e)   (sq, sk: that precision's scales)
+ *   M_i   = an integer >= max_j t_ij
+ *   P_ij  = bf16_rne(fp32(2^(t_ij - M_i)))            (the weights fed to P.V)
+ *   out_i = sum_j P_ij * V_j / sum_j P_ij             (fp32 out, V in bf16)
+ * Because M_i is an integer, the result does not depend on which integer the
+ * kernel's running maximum settled on (power-of-two rescaling commutes with the
+ * bf16 rounding); results agree with a fixed-M evaluation up to fp32 summation
+ * order.  Skipped tiles are never read.
+ * Inputs: the device copy of tria_build_policy's blob, the outputs of
+ * tria_quantize_qk, and V bf16 [b][Hkv][n][d].  out fp32 [b][Hq][n][d].
+ * lse (may be NULL) fp32 [b][Hq][n] receives M_i + log2(sum_j P_ij), the base-2
+ * log of the softmax denominator in units of t.
+ */
+tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes,
+                         const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
+                         const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
+                         const void* v_bf16, float sm_scale, float* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* (4) Compressed KV cache.                                                   */
+/* ------------------------------------------------------------------------- */
+/*
+ * The cache holds, for one query position t = ctx_len - 1 (current block
+ * c = t / block), only the key blocks the policy keeps, each at its precision
+ * (TriAttention page, section on calibration: prepared keys and values go to a
+ * compressed KV cache so that generation reads less; section on infrastructure
+ * plans: a special cache layout).  The policy is per KV head: pass
+ * n_policy_heads == n_kv_heads, or n_policy_heads == n_q_heads to merge each
+ * group by the maximum of hi and of keep (the union of the kept sets).
+ * For KV head g with (hi, keep):
+ *     int8 blocks: {0} union {kb <= c : c - kb <= hi}       (block c always)
+ *     int4 blocks: {kb >= 1 : hi < c - kb <= keep}
+ * Each K and V row of a stored block is quantised with the tria_quantize_qk
+ * contract at the block's precision (V too, unlike prefill).
+ *
+ * Byte layout (little-endian):
+ *   [0, 64)  header: int32 magic TRIA_CACHE_MAGIC, int32 version, int32 batch,
+ *            int32 n_kv_heads, int32 head_dim, int32 block, int32 nb (= c + 1),
+ *            int32 cur_block (= c), int64 ctx_len, int64 total_bytes,
+ *            int64 dir_offset (= 64), int64 data_offset.
+ *   [64, 64 + 64*batch*n_kv_heads)  directory, one 64-byte entry per (b, g),
+ *            b-major: int64 offset (from the blob start to the pair's first
+ *            record), int32 n8, int32 n4, int32 hi, int32 keep, int32 lo8,
+ *            int32 sink, int32 lo4, int32 hi4, int32 zero[4].  The stored int8
+ *            blocks are [block 0 if sink] then lo8..c; the int4 blocks lo4..hi4
+ *            ((0, -1) when none); lo8, sink, lo4, hi4 follow the schedule's rule
+ *            for query block c.  hi, keep are the (merged) KV-head boundaries.
+ *   data_offset = round_up(64 + 64*batch*n_kv_heads, 256); the pairs' records
+ *            follow in (b, g) order, each pair's n8 int8 records (ascending
+ *            block) then its n4 int4 records (ascending block).
+ *   int8 record, 2*B*d + 8*B bytes:
+ *            K codes int8 [B][d] | V codes int8 [d][B] in feed order |
+ *            K scales fp32 [B] | V scales fp32 [B]
+ *   int4 record, B*d + 8*B bytes:
+ *            K codes [B][d/2] packed along d (low nibble = even dim) |
+ *            V codes [d][B/2] in feed order, packed (low nibble = even position) |
+ *            K scales fp32 [B] | V scales fp32 [B]
+ *   Feed order of the transposed V codes: within each group of 64 token
+ *   positions, position 16*q + 8*s + p (q in 0..3, s in 0..1, p in 0..7) holds
+ *   token 32*s + 16*(p / 4) + 4*q + (p % 4) of that group.  (This is the order in
+ *   which the decode kernel's matrix instructions consume keys, so each lane
+ *   loads one contiguous run.)
+ *   Tokens at or beyond ctx_len in the current block have zero codes and scales.
+ * tria_kv_cache_bytes gives the exact total; ctx_len must satisfy
+ * 1 <= ctx_len <= dims->seq_len (the K/V tensors hold seq_len rows).
+ */
+#define TRIA_CACHE_MAGIC 0x43564B54 /* "TKVC" */
+#define TRIA_CACHE_VERSION 1
+#define TRIA_CACHE_HEADER_BYTES 64
+#define TRIA_CACHE_DIR_ENTRY_BYTES 64
+tria_status tria_kv_cache_bytes(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                int32_t n_policy_heads, int64_t ctx_len, size_t* bytes);
+/* Packs K, V bf16 [b][Hkv][seq_len][d] into `cache` (cache_bytes >= the size above). */
+tria_status tria_pack_kv_cache(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                               int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16,
+                               const void* v_bf16, void* cache, size_t cache_bytes, void* stream);
+/* Synchronous host-side validation of a cache's header and directory against
+ * dims and ctx_len (copies them from device memory; for debugging and tests).
+ * Returns TRIA_ERR_INVALID_ARG on any mismatch or corruption. */
+tria_status tria_check_cache(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                             int64_t ctx_len);
+
+/* ------------------------------------------------------------------------- */
+/* (5) Decode.  Device, asynchronous.                                         */
+/* ------------------------------------------------------------------------- */
+/*
+ * One query token per sequence at position t = ctx_len - 1 attends over the
+ * stored blocks of the packed cache (reading only them: decode is bound by memory
+ * traffic, llmis.ru chapter 3.5 section 2, so reading fewer bytes is the win).
+ * For query head h (KV head g) and each stored token j <= t of block precision a:
+ *     s_j = dot(qc^a, kc_j^a) * sq^a * sk_j^a * sm_scale
+ *     p_j = exp(s_j - max_j s_j)
+ *     out = sum_j p_j * sv_j^a * vc_j^a / sum_j p_j          (fp32)
+ * where q's row is quantised with the tria_quantize_qk contract at each
+ * precision.  q bf16 [b][Hq][d]; out fp32 [b][Hq][d].  The kernel reads shapes
+ * and offsets from the cache header (written by tria_pack_kv_cache for the same
+ * dims and ctx_len); a header that does not match writes NaN to `out`.
+ * workspace: device memory of at least tria_decode_workspace_bytes bytes for the
+ * split-KV partial results; its contents need no initialisation.
+ */
+tria_status tria_decode_workspace_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
+tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                        int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRIA_H */

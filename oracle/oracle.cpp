@@ -1,0 +1,530 @@
+// oracle.cpp - plain, slow CPU reference for the block-sparse mixed-precision
+// (int8 / int4 / skip) causal attention path.
+//
+// TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check of __graft_entry__ and
+// the cpu_baseline leg of bench.py may load this library.  It shares no code,
+// header, table or constant with the GPU library: every layout and constant below
+// is re-derived from the written contract and the pages it cites.
+//
+// Sources (cited by page and section):
+//  * TriAttention summary page (rit.work, "TriAttention: sparse mixed-precision
+//    attention"), section "which links can be skipped and which must not be
+//    removed": three actions per tile (skip / 4 bits / 8 bits) chosen by distance
+//    from the diagonal; the first key block and the diagonal block are always kept
+//    at high precision; one pair of boundaries per head.
+//  * same page, section "how calibration distributes compute between heads":
+//    kept blocks are grouped by precision and reduced into one normalised result;
+//    prepared keys and values go to a compressed KV cache read during generation.
+//  * llmis.ru chapter 3.5 ("attention variants for inference"), section 2: the KV
+//    cache byte formula 2*L*h*d_h*n*b*p; section 4: grouped-query attention.
+//
+// Readings taken where the pages are silent (each also listed in the design
+// notes): boundaries inclusive and in blocks; per-row symmetric quantiser with
+// qmax 127 / 7 and fp32 scales; both Q and K at 4 bits in an int4 tile; V in bf16
+// for prefill; softmax weights rounded to bf16 after subtracting an integer
+// maximum (power-of-two contract); cache and decode policies per KV head.
+//
+// Everything is double precision unless the contract fixes a narrower type.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+// ---------------------------------------------------------------- bf16 / fp32
+float bf16_to_float(uint16_t b) {
+  uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Round a finite float to bfloat16, nearest with ties to even (written out on the
+// bit pattern: add half an ulp of the kept part, minus one when the kept lsb is 0).
+uint16_t float_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- tile actions
+enum { ACT_NONCAUSAL = -1, ACT_SKIP = 0, ACT_INT4 = 4, ACT_INT8 = 8 };
+
+// The distance-to-diagonal rule with the two protected blocks.
+int tile_action(int64_t qb, int64_t kb, int64_t hi, int64_t keep) {
+  if (kb > qb) return ACT_NONCAUSAL;
+  int64_t dist = qb - kb;
+  if (kb == 0 || dist == 0) return ACT_INT8;  // protected: first key block, diagonal
+  if (dist <= hi) return ACT_INT8;
+  if (dist <= keep) return ACT_INT4;
+  return ACT_SKIP;
+}
+
+// ---------------------------------------------------------------- quantiser
+// Symmetric per-row quantiser: scale = amax/qmax, code = clamp(rint(x*(qmax/amax))).
+void quantize_row(const uint16_t* x, int d, int qmax, int8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < d; ++i) amax = std::max(amax, std::fabs(bf16_to_float(x[i])));
+  if (amax == 0.0f) {
+    *scale = 0.0f;
+    for (int i = 0; i < d; ++i) codes[i] = 0;
+    return;
+  }
+  const float fq = static_cast<float>(qmax);
+  *scale = amax / fq;
+  const float r = fq / amax;
+  for (int i = 0; i < d; ++i) {
+    float c = std::rint(bf16_to_float(x[i]) * r);
+    c = std::min(std::max(c, -fq), fq);
+    codes[i] = static_cast<int8_t>(c);
+  }
+}
+
+uint8_t pack_pair(int8_t even, int8_t odd) {
+  return static_cast<uint8_t>((static_cast<uint8_t>(even) & 0x0Fu) |
+                              ((static_cast<uint8_t>(odd) & 0x0Fu) << 4));
+}
+
+// ---------------------------------------------------------------- threading
+template <class F>
+void parallel_for(int64_t count, int nthreads, F fn) {
+  if (nthreads < 1) nthreads = 1;
+  std::atomic<int64_t> next{0};
+  auto worker = [&]() {
+    for (;;) {
+      int64_t i = next.fetch_add(1);
+      if (i >= count) break;
+      fn(i);
+    }
+  };
+  std::vector<std::thread> pool;
+  for (int t = 1; t < nthreads; ++t) pool.emplace_back(worker);
+  worker();
+  for (auto& th : pool) th.join();
+}
+
+struct QuantRows {  // codes and scales of a set of rows at one precision
+  std::vector<int8_t> codes;
+  std::vector<float> scales;
+};
+
+QuantRows quantize_all(const uint16_t* x, int64_t rows, int d, int qmax, int nthreads) {
+  QuantRows r;
+  r.codes.resize(static_cast<size_t>(rows) * d);
+  r.scales.resize(static_cast<size_t>(rows));
+  parallel_for((rows + 1023) / 1024, nthreads, [&](int64_t c) {
+    for (int64_t i = c * 1024; i < std::min(rows, (c + 1) * 1024); ++i)
+      quantize_row(x + i * d, d, qmax, &r.codes[i * d], &r.scales[i]);
+  });
+  return r;
+}
+
+// Per-KV-head boundaries: either given per KV head, or merged from per-query-head
+// values by the group maximum (the union of what the group's heads keep).
+void kv_policy(int n_q_heads, int n_kv_heads, const int32_t* hi, const int32_t* keep,
+               int n_policy_heads, std::vector<int64_t>& hk, std::vector<int64_t>& kk) {
+  hk.assign(n_kv_heads, 0);
+  kk.assign(n_kv_heads, 0);
+  if (n_policy_heads == n_kv_heads) {
+    for (int g = 0; g < n_kv_heads; ++g) { hk[g] = hi[g]; kk[g] = keep[g]; }
+    return;
+  }
+  const int G = n_q_heads / n_kv_heads;
+  for (int h = 0; h < n_q_heads; ++h) {
+    hk[h / G] = std::max<int64_t>(hk[h / G], hi[h]);
+    kk[h / G] = std::max<int64_t>(kk[h / G], keep[h]);
+  }
+}
+
+// Position -> token within a 64-token group of the transposed V codes (the
+// documented feed order of the cache).
+int feed_token(int pos) {
+  int grp = pos / 64, w = pos % 64;
+  int q = w / 16, s = (w % 16) / 8, p = w % 8;
+  return grp * 64 + 32 * s + 16 * (p / 4) + 4 * q + (p % 4);
+}
+
+void put_i32(uint8_t* dst, int32_t v) { std::memcpy(dst, &v, 4); }
+void put_i64(uint8_t* dst, int64_t v) { std::memcpy(dst, &v, 8); }
+void put_f32(uint8_t* dst, float v) { std::memcpy(dst, &v, 4); }
+
+}  // namespace
+
+extern "C" {
+
+// ============================================================ pins and helpers
+// The pages' KV-cache formula (llmis.ru chapter 3.5, section 2): keys and values
+// of L layers, h heads of size d_h, n tokens, batch b, p bytes per element.
+int64_t oracle_kv_formula_bytes(int64_t L, int64_t h, int64_t d_h, int64_t n, int64_t b, int64_t p) {
+  return 2 * L * h * d_h * n * b * p;
+}
+
+int oracle_tile_action(int64_t qb, int64_t kb, int64_t hi, int64_t keep) {
+  return tile_action(qb, kb, hi, keep);
+}
+
+float oracle_bf16_to_float(uint16_t b) { return bf16_to_float(b); }
+uint16_t oracle_float_to_bf16(float f) { return float_to_bf16(f); }
+
+void oracle_quantize_rows(const uint16_t* x, int64_t rows, int d, int qmax, int8_t* codes,
+                          float* scales) {
+  for (int64_t i = 0; i < rows; ++i) quantize_row(x + i * d, d, qmax, codes + i * d, scales + i);
+}
+
+void oracle_pack_nibbles(const int8_t* codes, int64_t count, uint8_t* out) {
+  for (int64_t j = 0; j < count / 2; ++j) out[j] = pack_pair(codes[2 * j], codes[2 * j + 1]);
+}
+
+// Dense softmax attention in double, with an arbitrary key mask (1 = keep):
+// out_i = sum_j mask_ij exp(scale q_i.k_j) v_j / sum_j mask_ij exp(scale q_i.k_j).
+// q, k have dk columns and v, out have dv.  Rows with no kept key get zeros.
+void oracle_dense_attention(const double* q, const double* k, const double* v, int64_t nq,
+                            int64_t nk, int dk, int dv, const uint8_t* mask, double scale,
+                            double* out) {
+  std::vector<double> s(static_cast<size_t>(nk));
+  for (int64_t i = 0; i < nq; ++i) {
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < nk; ++j) {
+      if (!mask[i * nk + j]) continue;
+      double acc = 0.0;
+      for (int c = 0; c < dk; ++c) acc += q[i * dk + c] * k[j * dk + c];
+      s[j] = scale * acc;
+      mx = std::max(mx, s[j]);
+    }
+    double den = 0.0;
+    for (int c = 0; c < dv; ++c) out[i * dv + c] = 0.0;
+    if (mx == -INFINITY) continue;
+    for (int64_t j = 0; j < nk; ++j) {
+      if (!mask[i * nk + j]) continue;
+      double p = std::exp(s[j] - mx);
+      den += p;
+      for (int c = 0; c < dv; ++c) out[i * dv + c] += p * v[j * dv + c];
+    }
+    for (int c = 0; c < dv; ++c) out[i * dv + c] /= den;
+  }
+}
+
+// ============================================================ (1) schedule
+int64_t oracle_schedule_bytes(int64_t batch, int64_t n_q_heads, int64_t nb) {
+  return 64 + 32 * batch * n_q_heads * nb;
+}
+
+// Builds the canonical schedule from the per-tile action map: for each unit the
+// int8 run that ends at the diagonal, the int4 blocks, and block 0 when it is
+// int8 but not part of the run.  Returns 0, or -1 if the action map is not of
+// the documented shape (which would mean the rule itself is broken).
+int oracle_build_schedule(int batch, int n_q_heads, int n_kv_heads, int head_dim, int block,
+                          int64_t seq_len, const int32_t* hi, const int32_t* keep,
+                          int32_t* out, int64_t out_words) {
+  const int64_t nb = (seq_len + block - 1) / block;
+  const int64_t n_units = static_cast<int64_t>(batch) * n_q_heads * nb;
+  if (out_words < 16 + 8 * n_units) return -1;
+  struct Unit { int32_t f[8]; };
+  std::vector<Unit> units;
+  units.reserve(static_cast<size_t>(n_units));
+  for (int b = 0; b < batch; ++b)
+    for (int h = 0; h < n_q_heads; ++h)
+      for (int64_t qb = 0; qb < nb; ++qb) {
+        std::vector<int> act(static_cast<size_t>(qb + 1));
+        for (int64_t kb = 0; kb <= qb; ++kb) act[kb] = tile_action(qb, kb, hi[h], keep[h]);
+        int64_t lo8 = qb;
+        while (lo8 > 0 && act[lo8 - 1] == ACT_INT8) --lo8;
+        // block 0 is int8 by protection; if the run stops above it, it is the sink
+        int32_t sink = (lo8 > 0 && act[0] == ACT_INT8) ? 1 : 0;
+        int64_t lo4 = -1, hi4 = -1, n4 = 0, kept = 0;
+        for (int64_t kb = 0; kb <= qb; ++kb) {
+          if (act[kb] != ACT_SKIP) ++kept;
+          if (act[kb] == ACT_INT4) {
+            if (lo4 < 0) lo4 = kb;
+            hi4 = kb;
+            ++n4;
+          }
+        }
+        if (n4 == 0) { lo4 = 0; hi4 = -1; }
+        if (n4 != hi4 - lo4 + 1 && n4 != 0) return -1;          // int4 blocks not contiguous
+        if (kept != (qb - lo8 + 1) + sink + n4) return -1;      // int8 blocks not {0} u run
+        Unit u;
+        int32_t f[8] = {b, h, static_cast<int32_t>(qb), static_cast<int32_t>(lo8),
+                        static_cast<int32_t>(lo4), static_cast<int32_t>(hi4), sink,
+                        static_cast<int32_t>(kept)};
+        std::memcpy(u.f, f, sizeof f);
+        units.push_back(u);
+      }
+  std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) {
+    if (a.f[7] != b.f[7]) return a.f[7] > b.f[7];
+    if (a.f[0] != b.f[0]) return a.f[0] < b.f[0];
+    if (a.f[1] != b.f[1]) return a.f[1] < b.f[1];
+    return a.f[2] < b.f[2];
+  });
+  std::memset(out, 0, sizeof(int32_t) * 16);
+  out[0] = 0x48435354;  // "TSCH"
+  out[1] = 1;
+  out[2] = batch; out[3] = n_q_heads; out[4] = n_kv_heads; out[5] = head_dim; out[6] = block;
+  out[7] = static_cast<int32_t>(nb);
+  out[8] = static_cast<int32_t>(n_units);
+  out[10] = static_cast<int32_t>(seq_len & 0xFFFFFFFF);
+  out[11] = static_cast<int32_t>(seq_len >> 32);
+  for (int64_t i = 0; i < n_units; ++i) std::memcpy(out + 16 + 8 * i, units[i].f, 32);
+  return 0;
+}
+
+// ============================================================ (3) prefill
+// Follows the method row by row: keep the keys of non-skipped tiles, score them
+// with the codes of the tile's precision, take an integer maximum, round the
+// weights to bf16 and normalise by their sum.  `units` lists (b, h, qb) triples
+// whose rows are computed (NULL with n_units = -1: all of them).  out and lse are
+// full-size arrays; only the selected rows are written.  reference_mode = 1 keeps
+// the weights in double (no bf16 rounding), for the exactness pins.
+int oracle_prefill(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
+                   const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* hi,
+                   const int32_t* keep, float sm_scale, int reference_mode, const int32_t* units,
+                   int64_t n_units, float* out, float* lse, int nthreads) {
+  const int G = n_q_heads / n_kv_heads;
+  const int64_t nb = (n + block - 1) / block;
+  std::vector<int32_t> all;
+  if (units == nullptr || n_units < 0) {
+    for (int b = 0; b < batch; ++b)
+      for (int h = 0; h < n_q_heads; ++h)
+        for (int64_t qb = 0; qb < nb; ++qb) {
+          all.push_back(b); all.push_back(h); all.push_back(static_cast<int32_t>(qb));
+        }
+    units = all.data();
+    n_units = static_cast<int64_t>(all.size() / 3);
+  }
+  const int64_t k_rows = static_cast<int64_t>(batch) * n_kv_heads * n;
+  QuantRows k8 = quantize_all(k, k_rows, d, 127, nthreads);
+  QuantRows k4 = quantize_all(k, k_rows, d, 7, nthreads);
+  const double log2e = 1.4426950408889634074;
+  const double c = static_cast<double>(sm_scale) * log2e;
+
+  parallel_for(n_units, nthreads, [&](int64_t u) {
+    const int b = units[3 * u], h = units[3 * u + 1];
+    const int64_t qb = units[3 * u + 2];
+    const int g = h / G;
+    const int64_t kbase = (static_cast<int64_t>(b) * n_kv_heads + g) * n;
+    const int64_t qbase = (static_cast<int64_t>(b) * n_q_heads + h) * n;
+    std::vector<int8_t> qc8(d), qc4(d);
+    std::vector<double> t, w;
+    std::vector<int64_t> keys;
+    std::vector<double> o(d);
+    for (int64_t i = qb * block; i < std::min(n, (qb + 1) * block); ++i) {
+      float sq8, sq4;
+      quantize_row(q + (qbase + i) * d, d, 127, qc8.data(), &sq8);
+      quantize_row(q + (qbase + i) * d, d, 7, qc4.data(), &sq4);
+      keys.clear();
+      t.clear();
+      for (int64_t j = 0; j <= i; ++j) {
+        const int a = tile_action(qb, j / block, hi[h], keep[h]);
+        if (a == ACT_SKIP) continue;
+        const int8_t* qc = (a == ACT_INT8) ? qc8.data() : qc4.data();
+        const int8_t* kc = (a == ACT_INT8) ? &k8.codes[(kbase + j) * d] : &k4.codes[(kbase + j) * d];
+        int64_t s = 0;
+        for (int x = 0; x < d; ++x) s += static_cast<int64_t>(qc[x]) * kc[x];
+        const double sq = (a == ACT_INT8) ? sq8 : sq4;
+        const double sk = (a == ACT_INT8) ? k8.scales[kbase + j] : k4.scales[kbase + j];
+        keys.push_back(j);
+        t.push_back(static_cast<double>(s) * sq * sk * c);
+      }
+      const double mx = *std::max_element(t.begin(), t.end());
+      const double M = std::ceil(mx);
+      w.resize(t.size());
+      double l = 0.0;
+      for (size_t x = 0; x < t.size(); ++x) {
+        const double e = std::exp2(t[x] - M);
+        if (reference_mode) {
+          w[x] = e;
+        } else {
+          // fp32 first, then bf16; values below the normal fp32 range count as 0
+          const float ef = static_cast<float>(e);
+          w[x] = (ef < 0x1p-126f) ? 0.0 : static_cast<double>(bf16_to_float(float_to_bf16(ef)));
+        }
+        l += w[x];
+      }
+      std::fill(o.begin(), o.end(), 0.0);
+      for (size_t x = 0; x < keys.size(); ++x) {
+        const uint16_t* vr = v + (kbase + keys[x]) * d;
+        for (int y = 0; y < d; ++y) o[y] += w[x] * static_cast<double>(bf16_to_float(vr[y]));
+      }
+      for (int y = 0; y < d; ++y) out[(qbase + i) * d + y] = static_cast<float>(o[y] / l);
+      if (lse) lse[qbase + i] = static_cast<float>(M + std::log2(l));
+    }
+  });
+  return 0;
+}
+
+// ============================================================ (4) cache
+// Stored blocks of one KV head for query block c: the tile rule applied to the
+// row of block c (int8 = protected blocks and the hi band, int4 = the keep band).
+static void stored_sets(int64_t c, int64_t hi, int64_t keep, std::vector<int64_t>& b8,
+                        std::vector<int64_t>& b4) {
+  b8.clear();
+  b4.clear();
+  for (int64_t kb = 0; kb <= c; ++kb) {
+    int a = tile_action(c, kb, hi, keep);
+    if (a == ACT_INT8) b8.push_back(kb);
+    if (a == ACT_INT4) b4.push_back(kb);
+  }
+}
+
+int64_t oracle_cache_bytes(int batch, int n_q_heads, int n_kv_heads, int d, int block,
+                           int64_t ctx_len, const int32_t* hi, const int32_t* keep,
+                           int n_policy_heads) {
+  std::vector<int64_t> hk, kk, b8, b4;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  const int64_t c = (ctx_len - 1) / block;
+  int64_t total = 64 + 64 * static_cast<int64_t>(batch) * n_kv_heads;
+  total = (total + 255) / 256 * 256;
+  for (int b = 0; b < batch; ++b)
+    for (int g = 0; g < n_kv_heads; ++g) {
+      stored_sets(c, hk[g], kk[g], b8, b4);
+      total += static_cast<int64_t>(b8.size()) * (2LL * block * d + 8LL * block) +
+               static_cast<int64_t>(b4.size()) * (static_cast<int64_t>(block) * d + 8LL * block);
+    }
+  return total;
+}
+
+// Writes the documented cache bytes.  Returns 0, or -1 if out_bytes is too small.
+int oracle_pack_cache(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
+                      int64_t ctx_len, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                      const uint16_t* k, const uint16_t* v, uint8_t* out, int64_t out_bytes) {
+  const int64_t total = oracle_cache_bytes(batch, n_q_heads, n_kv_heads, d, block, ctx_len, hi,
+                                           keep, n_policy_heads);
+  if (out_bytes < total) return -1;
+  std::memset(out, 0, static_cast<size_t>(total));
+  std::vector<int64_t> hk, kk, b8, b4;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  const int64_t c = (ctx_len - 1) / block;
+  const int64_t dir = 64;
+  int64_t data = (64 + 64 * static_cast<int64_t>(batch) * n_kv_heads + 255) / 256 * 256;
+  put_i32(out + 0, 0x43564B54);  // "TKVC"
+  put_i32(out + 4, 1);
+  put_i32(out + 8, batch);
+  put_i32(out + 12, n_kv_heads);
+  put_i32(out + 16, d);
+  put_i32(out + 20, block);
+  put_i32(out + 24, static_cast<int32_t>(c + 1));
+  put_i32(out + 28, static_cast<int32_t>(c));
+  put_i64(out + 32, ctx_len);
+  put_i64(out + 40, total);
+  put_i64(out + 48, dir);
+  put_i64(out + 56, data);
+  std::vector<int8_t> codes(d);
+  float scale;
+  int64_t off = data;
+  for (int b = 0; b < batch; ++b)
+    for (int g = 0; g < n_kv_heads; ++g) {
+      stored_sets(c, hk[g], kk[g], b8, b4);
+      int64_t lo8 = c;
+      while (lo8 > 0 && std::find(b8.begin(), b8.end(), lo8 - 1) != b8.end()) --lo8;
+      const int32_t sink = (lo8 > 0) ? 1 : 0;  // block 0 is always among b8
+      uint8_t* e = out + dir + 64 * (static_cast<int64_t>(b) * n_kv_heads + g);
+      put_i64(e + 0, off);
+      put_i32(e + 8, static_cast<int32_t>(b8.size()));
+      put_i32(e + 12, static_cast<int32_t>(b4.size()));
+      put_i32(e + 16, static_cast<int32_t>(hk[g]));
+      put_i32(e + 20, static_cast<int32_t>(kk[g]));
+      put_i32(e + 24, static_cast<int32_t>(lo8));
+      put_i32(e + 28, sink);
+      put_i32(e + 32, b4.empty() ? 0 : static_cast<int32_t>(b4.front()));
+      put_i32(e + 36, b4.empty() ? -1 : static_cast<int32_t>(b4.back()));
+      const int64_t src = (static_cast<int64_t>(b) * n_kv_heads + g) * n;
+      for (int pass = 0; pass < 2; ++pass) {
+        const std::vector<int64_t>& blocks = pass == 0 ? b8 : b4;
+        const int qmax = pass == 0 ? 127 : 7;
+        const int64_t kbytes = pass == 0 ? static_cast<int64_t>(block) * d : static_cast<int64_t>(block) * d / 2;
+        for (int64_t kb : blocks) {
+          uint8_t* rk = out + off;
+          uint8_t* rv = rk + kbytes;
+          uint8_t* rks = rv + kbytes;
+          uint8_t* rvs = rks + 4LL * block;
+          std::vector<int8_t> vcodes(static_cast<size_t>(block) * d, 0);  // [token][dim]
+          for (int r = 0; r < block; ++r) {
+            const int64_t tok = kb * block + r;
+            if (tok >= ctx_len) continue;  // beyond the context: zero codes and scales
+            quantize_row(k + (src + tok) * d, d, qmax, codes.data(), &scale);
+            put_f32(rks + 4 * r, scale);
+            if (pass == 0) {
+              for (int x = 0; x < d; ++x) rk[static_cast<int64_t>(r) * d + x] = static_cast<uint8_t>(codes[x]);
+            } else {
+              for (int x = 0; x < d / 2; ++x)
+                rk[static_cast<int64_t>(r) * (d / 2) + x] = pack_pair(codes[2 * x], codes[2 * x + 1]);
+            }
+            quantize_row(v + (src + tok) * d, d, qmax, &vcodes[static_cast<size_t>(r) * d], &scale);
+            put_f32(rvs + 4 * r, scale);
+          }
+          // V codes transposed: row = dim, columns = token positions in feed order
+          for (int x = 0; x < d; ++x) {
+            for (int pos = 0; pos < block; ++pos) {
+              const int8_t cv = vcodes[static_cast<size_t>(feed_token(pos)) * d + x];
+              if (pass == 0) {
+                rv[static_cast<int64_t>(x) * block + pos] = static_cast<uint8_t>(cv);
+              } else if (pos % 2 == 0) {
+                const int8_t cv1 = vcodes[static_cast<size_t>(feed_token(pos + 1)) * d + x];
+                rv[static_cast<int64_t>(x) * (block / 2) + pos / 2] = pack_pair(cv, cv1);
+              }
+            }
+          }
+          off += 2 * kbytes + 8LL * block;
+        }
+      }
+    }
+  return 0;
+}
+
+// ============================================================ (5) decode
+// One query token at t = ctx_len - 1 per sequence.  Works from the raw bf16 K/V
+// and the policy (it never reads a packed cache): the stored set of block c, the
+// query quantised at each precision, exact integer dots, softmax in double.
+int oracle_decode(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
+                  int64_t ctx_len, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                  const uint16_t* k, const uint16_t* v, const uint16_t* q, float sm_scale,
+                  float* out, int nthreads) {
+  std::vector<int64_t> hk, kk;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  const int G = n_q_heads / n_kv_heads;
+  const int64_t t_pos = ctx_len - 1, c = t_pos / block;
+  parallel_for(static_cast<int64_t>(batch) * n_q_heads, nthreads, [&](int64_t bh) {
+    const int b = static_cast<int>(bh / n_q_heads), h = static_cast<int>(bh % n_q_heads);
+    const int g = h / G;
+    std::vector<int8_t> qc8(d), qc4(d), kc(d), vc(d);
+    float sq8, sq4, sk, sv;
+    quantize_row(q + bh * d, d, 127, qc8.data(), &sq8);
+    quantize_row(q + bh * d, d, 7, qc4.data(), &sq4);
+    const int64_t src = (static_cast<int64_t>(b) * n_kv_heads + g) * n;
+    std::vector<double> s;
+    std::vector<int64_t> toks;
+    std::vector<int> prec;
+    for (int64_t j = 0; j <= t_pos; ++j) {
+      const int a = tile_action(c, j / block, hk[g], kk[g]);
+      if (a == ACT_SKIP) continue;
+      const int qmax = a == ACT_INT8 ? 127 : 7;
+      quantize_row(k + (src + j) * d, d, qmax, kc.data(), &sk);
+      const int8_t* qc = a == ACT_INT8 ? qc8.data() : qc4.data();
+      int64_t dot = 0;
+      for (int x = 0; x < d; ++x) dot += static_cast<int64_t>(qc[x]) * kc[x];
+      const double sqa = a == ACT_INT8 ? sq8 : sq4;
+      s.push_back(static_cast<double>(dot) * sqa * sk * static_cast<double>(sm_scale));
+      toks.push_back(j);
+      prec.push_back(qmax);
+    }
+    const double mx = *std::max_element(s.begin(), s.end());
+    std::vector<double> o(d, 0.0);
+    double den = 0.0;
+    for (size_t x = 0; x < s.size(); ++x) {
+      const double p = std::exp(s[x] - mx);
+      den += p;
+      quantize_row(v + (src + toks[x]) * d, d, prec[x], vc.data(), &sv);
+      for (int y = 0; y < d; ++y) o[y] += p * static_cast<double>(sv) * vc[y];
+    }
+    for (int y = 0; y < d; ++y) out[bh * d + y] = static_cast<float>(o[y] / den);
+  });
+  return 0;
+}
+
+}  // extern "C"
