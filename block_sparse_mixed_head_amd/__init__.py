@@ -1,0 +1,158 @@
+"""Block-sparse, mixed-precision (int8 / int4 / skip) causal attention on MI355X.
+
+Thin torch-facing wrappers over the C ABI (include/tria.h, libtria.so).  PyTorch
+provides device memory and the current stream; every step of the attention path
+runs in the library's HIP kernels.  The five calls of the path:
+
+  build_policy   per-head (hi, keep) -> schedule of per-(b, h, q-block) units
+  quantize_qk    per-row int8 / int4 codes and fp32 scales of Q and K
+  prefill        fused block-sparse causal attention over the schedule
+  pack_kv_cache  compressed int8 / int4 KV cache for one query position
+  decode         one-token attention over the compressed cache
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import TriaError, check, dims as make_dims  # noqa: F401
+
+__all__ = ["Dims", "build_policy", "quantize_qk", "prefill", "kv_cache_bytes", "pack_kv_cache",
+           "check_cache", "decode_workspace_bytes", "decode", "TriaError", "Quantized"]
+
+Dims = _lib.Dims
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _require(t: torch.Tensor, dtype, shape, name: str) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous CUDA {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} cuda={t.is_cuda}")
+
+
+# ------------------------------------------------------------------ (1) policy
+def build_policy(d: Dims, hi, keep) -> np.ndarray:
+    """Host schedule blob (int32 words) for per-query-head (hi, keep)."""
+    hi, keep = _i32(hi), _i32(keep)
+    need = C.c_size_t(0)
+    check(_lib.lib.tria_build_policy(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), None, 0,
+                                     C.byref(need)))
+    out = np.zeros(need.value // 4, dtype=np.int32)
+    check(_lib.lib.tria_build_policy(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi),
+                                     out.ctypes.data, need.value, C.byref(need)))
+    return out
+
+
+# ------------------------------------------------------------------ (2) quantiser
+@dataclass
+class Quantized:
+    q8: torch.Tensor
+    q4: torch.Tensor
+    q8s: torch.Tensor
+    q4s: torch.Tensor
+    k8: torch.Tensor
+    k4: torch.Tensor
+    k8s: torch.Tensor
+    k4s: torch.Tensor
+
+
+def quantize_qk(d: Dims, q: torch.Tensor, k: torch.Tensor, out: Optional[Quantized] = None) -> Quantized:
+    b, hq, hk, hd, n = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(q, torch.bfloat16, (b, hq, n, hd), "q")
+    _require(k, torch.bfloat16, (b, hk, n, hd), "k")
+    dev = q.device
+    if out is None:
+        out = Quantized(
+            torch.empty((b, hq, n, hd), dtype=torch.int8, device=dev),
+            torch.empty((b, hq, n, hd // 2), dtype=torch.uint8, device=dev),
+            torch.empty((b, hq, n), dtype=torch.float32, device=dev),
+            torch.empty((b, hq, n), dtype=torch.float32, device=dev),
+            torch.empty((b, hk, n, hd), dtype=torch.int8, device=dev),
+            torch.empty((b, hk, n, hd // 2), dtype=torch.uint8, device=dev),
+            torch.empty((b, hk, n), dtype=torch.float32, device=dev),
+            torch.empty((b, hk, n), dtype=torch.float32, device=dev))
+    check(_lib.lib.tria_quantize_qk(C.byref(d), _ptr(q), _ptr(k), _ptr(out.q8), _ptr(out.q4), _ptr(out.q8s),
+                                    _ptr(out.q4s), _ptr(out.k8), _ptr(out.k4), _ptr(out.k8s), _ptr(out.k4s),
+                                    _stream(dev)))
+    return out
+
+
+# ------------------------------------------------------------------ (3) prefill
+def prefill(d: Dims, sched_dev: torch.Tensor, qz: Quantized, v: torch.Tensor, sm_scale: float,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sched_dev: the build_policy blob copied to the device (any dtype, contiguous)."""
+    b, hq, hk, hd, n = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(v, torch.bfloat16, (b, hk, n, hd), "v")
+    if out is None:
+        out = torch.empty((b, hq, n, hd), dtype=torch.float32, device=v.device)
+    _require(out, torch.float32, (b, hq, n, hd), "out")
+    if lse is not None:
+        _require(lse, torch.float32, (b, hq, n), "lse")
+    nbytes = sched_dev.numel() * sched_dev.element_size()
+    check(_lib.lib.tria_prefill(C.byref(d), _ptr(sched_dev), nbytes, _ptr(qz.q8), _ptr(qz.q4), _ptr(qz.q8s),
+                                _ptr(qz.q4s), _ptr(qz.k8), _ptr(qz.k4), _ptr(qz.k8s), _ptr(qz.k4s), _ptr(v),
+                                float(sm_scale), _ptr(out), _ptr(lse), _stream(v.device)))
+    return out
+
+
+# ------------------------------------------------------------------ (4) cache
+def kv_cache_bytes(d: Dims, hi, keep, ctx_len: int) -> int:
+    hi, keep = _i32(hi), _i32(keep)
+    out = C.c_size_t(0)
+    check(_lib.lib.tria_kv_cache_bytes(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len,
+                                       C.byref(out)))
+    return out.value
+
+
+def pack_kv_cache(d: Dims, hi, keep, ctx_len: int, k: torch.Tensor, v: torch.Tensor,
+                  cache: Optional[torch.Tensor] = None) -> torch.Tensor:
+    b, hk, hd, n = d.batch, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(k, torch.bfloat16, (b, hk, n, hd), "k")
+    _require(v, torch.bfloat16, (b, hk, n, hd), "v")
+    hi, keep = _i32(hi), _i32(keep)
+    nbytes = kv_cache_bytes(d, hi, keep, ctx_len)
+    if cache is None:
+        cache = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    check(_lib.lib.tria_pack_kv_cache(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, _ptr(k),
+                                      _ptr(v), _ptr(cache), cache.numel(), _stream(k.device)))
+    return cache
+
+
+def check_cache(d: Dims, cache: torch.Tensor, ctx_len: int) -> None:
+    check(_lib.lib.tria_check_cache(C.byref(d), _ptr(cache), cache.numel(), ctx_len))
+
+
+# ------------------------------------------------------------------ (5) decode
+def decode_workspace_bytes(d: Dims, ctx_len: int) -> int:
+    out = C.c_size_t(0)
+    check(_lib.lib.tria_decode_workspace_bytes(C.byref(d), ctx_len, C.byref(out)))
+    return out.value
+
+
+def decode(d: Dims, cache: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale: float,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(d, ctx_len), dtype=torch.uint8, device=q.device)
+    check(_lib.lib.tria_decode(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(q), float(sm_scale),
+                               _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out

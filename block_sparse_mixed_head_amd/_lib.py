@@ -1,0 +1,70 @@
+"""ctypes binding of libtria.so (argument marshalling only).
+
+The names mirror the C ABI in include/tria.h.  Every compute step runs in the HIP
+kernels behind it; if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtria.so")
+
+TRIA_OK, TRIA_ERR_INVALID_ARG, TRIA_ERR_UNSUPPORTED, TRIA_ERR_BUFFER_TOO_SMALL, TRIA_ERR_HIP = range(5)
+SCHED_HEADER_BYTES = 64
+SCHED_UNIT_BYTES = 32
+
+
+class TriaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"tria status {status}: {msg}")
+        self.status = status
+
+
+class Dims(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("block", C.c_int32), ("reserved", C.c_int32),
+                ("seq_len", C.c_int64)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(block_sparse_mixed_head_amd/build.py) first")
+    lib = C.CDLL(LIB_PATH)
+    P, sz, i32, i64, f32 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64, C.c_float
+    D = C.POINTER(Dims)
+    sigs = {
+        "tria_last_error": (C.c_char_p, []),
+        "tria_version": (i32, []),
+        "tria_build_policy": (C.c_int, [D, P, P, i32, P, sz, C.POINTER(sz)]),
+        "tria_quantize_qk": (C.c_int, [D, P, P] + [P] * 8 + [P]),
+        "tria_prefill": (C.c_int, [D, P, sz] + [P] * 8 + [P, f32, P, P, P]),
+        "tria_kv_cache_bytes": (C.c_int, [D, P, P, i32, i64, C.POINTER(sz)]),
+        "tria_pack_kv_cache": (C.c_int, [D, P, P, i32, i64, P, P, P, sz, P]),
+        "tria_check_cache": (C.c_int, [D, P, sz, i64]),
+        "tria_decode_workspace_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
+        "tria_decode": (C.c_int, [D, P, sz, i64, P, f32, P, P, sz, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quantize_qk", "tria_prefill",
+            "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_check_cache",
+            "tria_decode_workspace_bytes", "tria_decode"]
+
+
+def check(status: int) -> None:
+    if status != TRIA_OK:
+        raise TriaError(status, lib.tria_last_error().decode())
+
+
+def dims(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, block: int, seq_len: int) -> Dims:
+    return Dims(batch, n_q_heads, n_kv_heads, head_dim, block, 0, seq_len)

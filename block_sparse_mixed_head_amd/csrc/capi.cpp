@@ -1,0 +1,381 @@
+// capi.cpp - the C ABI declared in include/tria.h: argument validation, the host
+// policy expander, size queries and kernel launches.  Nothing here allocates
+// device memory; device work is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "tria.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+tria_status fail(tria_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tria_status fail(tria_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  if (getenv("TRIA_LOG")) fprintf(stderr, "tria: %s\n", buf);
+  return st;
+}
+
+tria_status ok() {
+  g_error.clear();
+  return TRIA_OK;
+}
+
+tria_status check_dims(const tria_dims* d) {
+  if (!d) return fail(TRIA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->reserved != 0) return fail(TRIA_ERR_INVALID_ARG, "dims.reserved must be 0");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->seq_len < 1)
+    return fail(TRIA_ERR_INVALID_ARG, "batch, heads and seq_len must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(TRIA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(TRIA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->block != 64 && d->block != 128)
+    return fail(TRIA_ERR_UNSUPPORTED, "block %d not supported (64 or 128)", d->block);
+  if (d->n_kv_heads > TRIA_MAX_KV_HEADS)
+    return fail(TRIA_ERR_UNSUPPORTED, "n_kv_heads %d above %d", d->n_kv_heads, TRIA_MAX_KV_HEADS);
+  const int64_t nb = (d->seq_len + d->block - 1) / d->block;
+  if ((int64_t)d->batch * d->n_q_heads * nb > INT32_MAX)
+    return fail(TRIA_ERR_UNSUPPORTED, "too many (batch, head, block) units");
+  return TRIA_OK;
+}
+
+tria_status check_policy(const int32_t* hi, const int32_t* keep, int32_t n) {
+  if (!hi || !keep) return fail(TRIA_ERR_INVALID_ARG, "hi/keep is NULL");
+  for (int32_t h = 0; h < n; ++h) {
+    if (hi[h] < 0 || keep[h] < hi[h])
+      return fail(TRIA_ERR_INVALID_ARG, "head %d: need 0 <= hi (%d) <= keep (%d)", h, hi[h], keep[h]);
+  }
+  return TRIA_OK;
+}
+
+tria::Shape shape_of(const tria_dims* d) {
+  return tria::Shape{d->batch, d->n_q_heads, d->n_kv_heads, d->head_dim, d->block, d->seq_len};
+}
+
+// Per-KV-head boundaries (merged by group maximum when given per query head).
+tria_status kv_policy(const tria_dims* d, const int32_t* hi, const int32_t* keep, int32_t n_policy,
+                      tria::KvPolicy& pol) {
+  if (n_policy != d->n_kv_heads && n_policy != d->n_q_heads)
+    return fail(TRIA_ERR_INVALID_ARG, "n_policy_heads %d must be n_kv_heads (%d) or n_q_heads (%d)", n_policy,
+                d->n_kv_heads, d->n_q_heads);
+  tria_status st = check_policy(hi, keep, n_policy);
+  if (st != TRIA_OK) return st;
+  std::memset(&pol, 0, sizeof pol);
+  const int G = n_policy == d->n_kv_heads ? 1 : d->n_q_heads / d->n_kv_heads;
+  for (int h = 0; h < n_policy; ++h) {
+    const int g = h / G;
+    pol.hi[g] = std::max(pol.hi[g], hi[h]);
+    pol.keep[g] = std::max(pol.keep[g], keep[h]);
+  }
+  return TRIA_OK;
+}
+
+struct Stored {
+  int64_t n8, n4;
+};
+
+// Stored blocks of one KV head for current block c (the tile rule for query block c).
+Stored stored_count(int64_t c, int64_t hi, int64_t keep) {
+  const int64_t lo8 = (c - hi >= 2) ? c - hi : 0;
+  const int64_t sink = lo8 > 0 ? 1 : 0;
+  int64_t lo4 = std::max<int64_t>(1, c - keep), hi4 = c - hi - 1;
+  const int64_t n4 = lo4 > hi4 ? 0 : hi4 - lo4 + 1;
+  return Stored{c - lo8 + 1 + sink, n4};
+}
+
+tria::CacheGeom cache_geom(const tria_dims* d, const tria::KvPolicy& pol, int64_t ctx_len) {
+  tria::CacheGeom g;
+  g.ctx_len = ctx_len;
+  g.cur_block = (int32_t)((ctx_len - 1) / d->block);
+  g.data_offset = (64 + 64LL * d->batch * d->n_kv_heads + 255) / 256 * 256;
+  g.rec8_bytes = 2LL * d->block * d->head_dim + 8LL * d->block;
+  g.rec4_bytes = (int64_t)d->block * d->head_dim + 8LL * d->block;
+  int64_t per_batch = 0;
+  for (int gk = 0; gk < d->n_kv_heads; ++gk) {
+    const Stored s = stored_count(g.cur_block, pol.hi[gk], pol.keep[gk]);
+    per_batch += s.n8 * g.rec8_bytes + s.n4 * g.rec4_bytes;
+  }
+  g.batch_bytes = per_batch;
+  g.total_bytes = g.data_offset + per_batch * d->batch;
+  return g;
+}
+
+tria_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TRIA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define NONNULL(p)                                                           \
+  do {                                                                       \
+    if (!(p)) return fail(TRIA_ERR_INVALID_ARG, "%s is NULL", #p);           \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* tria_last_error(void) { return g_error.c_str(); }
+
+int32_t tria_version(void) { return (1 << 16) | 0; }
+
+// ------------------------------------------------------------------ (1) policy
+tria_status tria_build_policy(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                              int32_t n_policy_heads, void* sched_host, size_t sched_bytes,
+                              size_t* sched_bytes_needed) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  if (n_policy_heads != dims->n_q_heads)
+    return fail(TRIA_ERR_INVALID_ARG, "n_policy_heads %d != n_q_heads %d", n_policy_heads, dims->n_q_heads);
+  st = check_policy(hi, keep, n_policy_heads);
+  if (st != TRIA_OK) return st;
+  const int64_t nb = (dims->seq_len + dims->block - 1) / dims->block;
+  const int64_t n_units = (int64_t)dims->batch * dims->n_q_heads * nb;
+  const size_t need = TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * (size_t)n_units;
+  if (sched_bytes_needed) *sched_bytes_needed = need;
+  if (!sched_host) {
+    if (sched_bytes_needed) return ok();
+    return fail(TRIA_ERR_INVALID_ARG, "sched_host and sched_bytes_needed are both NULL");
+  }
+  if (sched_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule needs %zu bytes, got %zu", need, sched_bytes);
+
+  // Expand (hi, keep) into per-unit ranges.  Units are generated in (b, h, qb)
+  // order and placed by a stable counting sort on ntiles (descending).
+  std::vector<int32_t> rec((size_t)n_units * 8);
+  std::vector<int64_t> count(nb + 2, 0);
+  int64_t u = 0;
+  for (int b = 0; b < dims->batch; ++b)
+    for (int h = 0; h < dims->n_q_heads; ++h)
+      for (int64_t qb = 0; qb < nb; ++qb, ++u) {
+        const int64_t H = hi[h], K = keep[h];
+        const int64_t lo8 = (qb - H >= 2) ? qb - H : 0;
+        const int64_t sink = lo8 > 0 ? 1 : 0;
+        int64_t lo4 = std::max<int64_t>(1, qb - K), hi4 = qb - H - 1;
+        if (lo4 > hi4) {
+          lo4 = 0;
+          hi4 = -1;
+        }
+        const int64_t ntiles = (qb - lo8 + 1) + sink + (hi4 - lo4 + 1);
+        int32_t* r = &rec[(size_t)u * 8];
+        r[0] = b;
+        r[1] = h;
+        r[2] = (int32_t)qb;
+        r[3] = (int32_t)lo8;
+        r[4] = (int32_t)lo4;
+        r[5] = (int32_t)hi4;
+        r[6] = (int32_t)sink;
+        r[7] = (int32_t)ntiles;
+        count[ntiles]++;
+      }
+  // start position of each ntiles bucket, largest first
+  std::vector<int64_t> start(nb + 2, 0);
+  int64_t pos = 0;
+  for (int64_t t = nb + 1; t >= 0; --t) {
+    start[t] = pos;
+    pos += count[t];
+  }
+  int32_t* out = static_cast<int32_t*>(sched_host);
+  std::memset(out, 0, TRIA_SCHED_HEADER_BYTES);
+  out[0] = TRIA_SCHED_MAGIC;
+  out[1] = TRIA_SCHED_VERSION;
+  out[2] = dims->batch;
+  out[3] = dims->n_q_heads;
+  out[4] = dims->n_kv_heads;
+  out[5] = dims->head_dim;
+  out[6] = dims->block;
+  out[7] = (int32_t)nb;
+  out[8] = (int32_t)n_units;
+  out[10] = (int32_t)(dims->seq_len & 0xFFFFFFFF);
+  out[11] = (int32_t)(dims->seq_len >> 32);
+  int32_t* units = out + TRIA_SCHED_HEADER_BYTES / 4;
+  for (int64_t i = 0; i < n_units; ++i) {
+    const int32_t* r = &rec[(size_t)i * 8];
+    std::memcpy(units + 8 * start[r[7]]++, r, 32);
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ (2) quantiser
+tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const void* k_bf16, int8_t* q8,
+                             uint8_t* q4, float* q8s, float* q4s, int8_t* k8, uint8_t* k4, float* k8s,
+                             float* k4s, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(q_bf16);
+  NONNULL(k_bf16);
+  NONNULL(q8);
+  NONNULL(q4);
+  NONNULL(q8s);
+  NONNULL(q4s);
+  NONNULL(k8);
+  NONNULL(k4);
+  NONNULL(k8s);
+  NONNULL(k4s);
+  return launched(tria::launch_quantize(shape_of(dims), q_bf16, k_bf16, q8, q4, q8s, q4s, k8, k4, k8s, k4s,
+                                        static_cast<hipStream_t>(stream)),
+                  "quantize launch");
+}
+
+// ------------------------------------------------------------------ (3) prefill
+tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes, const int8_t* q8,
+                         const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
+                         const uint8_t* k4, const float* k8s, const float* k4s, const void* v_bf16,
+                         float sm_scale, float* out, float* lse, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(sched_dev);
+  NONNULL(q8);
+  NONNULL(q4);
+  NONNULL(q8s);
+  NONNULL(q4s);
+  NONNULL(k8);
+  NONNULL(k4);
+  NONNULL(k8s);
+  NONNULL(k4s);
+  NONNULL(v_bf16);
+  NONNULL(out);
+  const int64_t nb = (dims->seq_len + dims->block - 1) / dims->block;
+  const int64_t n_units = (int64_t)dims->batch * dims->n_q_heads * nb;
+  const size_t need = TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * (size_t)n_units;
+  if (sched_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule for these dims needs %zu bytes, got %zu", need, sched_bytes);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int32_t* units = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(sched_dev) + TRIA_SCHED_HEADER_BYTES);
+  return launched(tria::launch_prefill(shape_of(dims), units, n_units, q8, q4, q8s, q4s, k8, k4, k8s, k4s, v_bf16,
+                                       sm_scale, out, lse, static_cast<hipStream_t>(stream)),
+                  "prefill launch");
+}
+
+// ------------------------------------------------------------------ (4) cache
+tria_status tria_kv_cache_bytes(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                int32_t n_policy_heads, int64_t ctx_len, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  if (ctx_len < 1 || ctx_len > dims->seq_len)
+    return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld outside [1, seq_len=%lld]", (long long)ctx_len,
+                (long long)dims->seq_len);
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  *bytes = (size_t)cache_geom(dims, pol, ctx_len).total_bytes;
+  return ok();
+}
+
+tria_status tria_pack_kv_cache(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                               int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16, const void* v_bf16,
+                               void* cache, size_t cache_bytes, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(k_bf16);
+  NONNULL(v_bf16);
+  NONNULL(cache);
+  if (ctx_len < 1 || ctx_len > dims->seq_len)
+    return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld outside [1, seq_len=%lld]", (long long)ctx_len,
+                (long long)dims->seq_len);
+  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
+    return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads above 65535");
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  const tria::CacheGeom g = cache_geom(dims, pol, ctx_len);
+  if ((int64_t)cache_bytes < g.total_bytes)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache needs %lld bytes, got %zu", (long long)g.total_bytes, cache_bytes);
+  return launched(tria::launch_pack(shape_of(dims), pol, g, k_bf16, v_bf16, cache, static_cast<hipStream_t>(stream)),
+                  "pack launch");
+}
+
+tria_status tria_check_cache(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(cache);
+  const int64_t pairs = (int64_t)dims->batch * dims->n_kv_heads;
+  const int64_t dir_end = 64 + 64 * pairs;
+  if ((int64_t)cache_bytes < dir_end) return fail(TRIA_ERR_INVALID_ARG, "cache smaller than its directory");
+  std::vector<uint8_t> h((size_t)dir_end);
+  hipError_t e = hipMemcpy(h.data(), cache, (size_t)dir_end, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(TRIA_ERR_HIP, "reading the cache header: %s", hipGetErrorString(e));
+  int32_t hd[8];
+  int64_t h64[4];
+  std::memcpy(hd, h.data(), 32);
+  std::memcpy(h64, h.data() + 32, 32);
+  const int64_t c = (ctx_len - 1) / dims->block;
+  const int64_t data_off = (dir_end + 255) / 256 * 256;
+  if (hd[0] != TRIA_CACHE_MAGIC || hd[1] != TRIA_CACHE_VERSION) return fail(TRIA_ERR_INVALID_ARG, "bad cache magic/version");
+  if (hd[2] != dims->batch || hd[3] != dims->n_kv_heads || hd[4] != dims->head_dim || hd[5] != dims->block)
+    return fail(TRIA_ERR_INVALID_ARG, "cache shape does not match dims");
+  if (h64[0] != ctx_len || hd[7] != c || hd[6] != c + 1) return fail(TRIA_ERR_INVALID_ARG, "cache ctx_len does not match");
+  if (h64[1] > (int64_t)cache_bytes || h64[2] != 64 || h64[3] != data_off)
+    return fail(TRIA_ERR_INVALID_ARG, "cache sizes/offsets corrupt");
+  const int64_t rec8 = 2LL * dims->block * dims->head_dim + 8LL * dims->block;
+  const int64_t rec4 = (int64_t)dims->block * dims->head_dim + 8LL * dims->block;
+  int64_t expect = data_off;
+  for (int64_t p = 0; p < pairs; ++p) {
+    int64_t off;
+    int32_t f[12];
+    std::memcpy(&off, h.data() + 64 + 64 * p, 8);
+    std::memcpy(f, h.data() + 64 + 64 * p + 8, 48);
+    const int32_t n8 = f[0], n4 = f[1], H = f[2], K = f[3], lo8 = f[4], sink = f[5], lo4 = f[6], hi4 = f[7];
+    const Stored s = stored_count(c, H, K);
+    const int64_t lo8e = (c - H >= 2) ? c - H : 0;
+    if (off != expect || H < 0 || K < H || n8 != s.n8 || n4 != s.n4 || lo8 != lo8e || sink != (lo8e > 0 ? 1 : 0) ||
+        (n4 > 0 && (lo4 != std::max<int64_t>(1, c - K) || hi4 != c - H - 1)) || (n4 == 0 && (lo4 != 0 || hi4 != -1)))
+      return fail(TRIA_ERR_INVALID_ARG, "directory entry %lld corrupt", (long long)p);
+    expect += n8 * rec8 + n4 * rec4;
+  }
+  if (expect != h64[1]) return fail(TRIA_ERR_INVALID_ARG, "cache total_bytes corrupt");
+  return ok();
+}
+
+// ------------------------------------------------------------------ (5) decode
+tria_status tria_decode_workspace_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  *bytes = (size_t)tria::decode_workspace_bytes(shape_of(dims), ctx_len);
+  return ok();
+}
+
+tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                        const void* q_bf16, float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(cache);
+  NONNULL(q_bf16);
+  NONNULL(out);
+  NONNULL(workspace);
+  if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int G = dims->n_q_heads / dims->n_kv_heads;
+  if (G > 32) return fail(TRIA_ERR_UNSUPPORTED, "more than 32 query heads per KV head");
+  if ((int64_t)dims->batch * dims->n_kv_heads > 4096) return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads above 4096");
+  const int64_t dir_end = 64 + 64LL * dims->batch * dims->n_kv_heads;
+  if ((int64_t)cache_bytes < dir_end) return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache smaller than its directory");
+  const tria::Shape s = shape_of(dims);
+  const int64_t need = tria::decode_workspace_bytes(s, ctx_len);
+  if ((int64_t)ws_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "decode workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
+  return launched(tria::launch_decode(s, ctx_len, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                  "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// kernels.h - internal launch interface between the C-ABI layer (capi.cpp) and the
+// gfx950 kernels.  Not part of the public ABI; shapes here are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tria {
+
+struct Shape {
+  int batch, hq, hkv, d, blk;
+  int64_t n;
+};
+
+// Per-row symmetric int8 / int4 quantisation of Q and K (one launch for both).
+hipError_t launch_quantize(const Shape& s, const void* q, const void* k, int8_t* q8, uint8_t* q4,
+                           float* q8s, float* q4s, int8_t* k8, uint8_t* k4, float* k8s, float* k4s,
+                           hipStream_t stream);
+
+// Fused block-sparse prefill over the unit records of a schedule (device memory).
+hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int8_t* q8,
+                          const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
+                          const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
+                          float sm_scale, float* out, float* lse, hipStream_t stream);
+
+// Per-KV-head policy passed by value to the cache kernels.
+struct KvPolicy {
+  int32_t hi[128];
+  int32_t keep[128];
+};
+
+// Cache geometry shared by the packer and decode launchers (host side).
+struct CacheGeom {
+  int64_t ctx_len;
+  int32_t cur_block;     // c = (ctx_len - 1) / blk
+  int64_t data_offset;   // first record byte
+  int64_t rec8_bytes;    // 2*B*d + 8*B
+  int64_t rec4_bytes;    // B*d + 8*B
+  int64_t batch_bytes;   // record bytes of one batch element (all KV heads)
+  int64_t total_bytes;
+};
+
+hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& g, const void* k,
+                       const void* v, void* cache, hipStream_t stream);
+
+// Decode: split-KV partials into `workspace`, then a merge into `out`.
+int64_t decode_max_items(const Shape& s, int64_t ctx_len);
+int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len);
+hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
+                         const void* q, float sm_scale, float* out, void* workspace, hipStream_t stream);
+
+}  // namespace tria

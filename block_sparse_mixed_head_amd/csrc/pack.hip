@@ -1,0 +1,220 @@
+// pack.hip - builds the compressed mixed-precision KV cache for one query position.
+//
+// TriAttention summary page (rit.work), section on calibration: the prepared keys
+// and values go to a compressed KV cache so that generation reads less of it; the
+// section on infrastructure plans adds that this needs its own cache layout.  For
+// query position t = ctx_len - 1 (current block c) and the KV head's (hi, keep),
+// the stored blocks are the ones the tile rule keeps for query block c: block 0
+// and blocks within hi of c at int8, blocks within keep at int4, nothing else.
+// Every K and V row of a stored block is quantised per row at its block's
+// precision (same contract as the Q/K quantiser).
+//
+// Layout (bytes, documented in tria.h): header, one 64-byte directory entry per
+// (batch, KV head), then per pair its int8 records and its int4 records:
+//   K codes [B][d] | V codes [d][B] in feed order | K scales [B] | V scales [B]
+// V is stored transposed, with the tokens of each 64-token group permuted into the
+// order the decode kernel's bf16 MFMA consumes them, so a decode lane reads one
+// contiguous 16-byte run per output column.
+//
+// One work group per stored block (grid x = block slot in the pair, y = pair); each
+// group computes its record offset from the policy (every batch element has the
+// same layout because the policy is per KV head).  V codes go through LDS for the
+// transpose.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tria {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct PackArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  uint8_t* cache;
+  int64_t n;  // token rows in the K/V source
+  int batch, hkv;
+  KvPolicy pol;
+  CacheGeom geo;
+};
+
+struct Blocks {  // the stored set of one KV head for current block c
+  int lo8, sink, n8, lo4, hi4, n4;
+};
+
+__device__ __forceinline__ Blocks stored_blocks(int c, int hi, int keep) {
+  Blocks s;
+  s.lo8 = (c - hi >= 2) ? c - hi : 0;  // block 0 joins the run when adjacent
+  s.sink = s.lo8 > 0 ? 1 : 0;
+  s.n8 = c - s.lo8 + 1 + s.sink;
+  s.lo4 = c - keep > 1 ? c - keep : 1;
+  s.hi4 = c - hi - 1;
+  if (s.lo4 > s.hi4) {
+    s.lo4 = 0;
+    s.hi4 = -1;
+  }
+  s.n4 = s.hi4 - s.lo4 + 1;
+  return s;
+}
+
+// token held at position p of a 64-token group in the transposed V layout
+__device__ __forceinline__ int feed_token(int p) {
+  const int q = p >> 4, s = (p >> 3) & 1, pp = p & 7;
+  return 32 * s + 16 * (pp >> 2) + 4 * q + (pp & 3);
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;  // rows per pass
+  __shared__ __attribute__((aligned(16))) int8_t vbuf[BLK][D];
+
+  const int pair = blockIdx.y, j = blockIdx.x;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int c = a.geo.cur_block;
+  const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
+  if (j >= st.n8 + st.n4) return;
+  int64_t pair_off = a.geo.data_offset + (int64_t)b * a.geo.batch_bytes;
+  for (int gg = 0; gg < g; ++gg) {
+    const Blocks o = stored_blocks(c, a.pol.hi[gg], a.pol.keep[gg]);
+    pair_off += (int64_t)o.n8 * a.geo.rec8_bytes + (int64_t)o.n4 * a.geo.rec4_bytes;
+  }
+  const bool is4 = j >= st.n8;
+  const int kb = !is4 ? ((st.sink && j == 0) ? 0 : st.lo8 + j - st.sink) : st.lo4 + (j - st.n8);
+  const int64_t off = !is4 ? pair_off + (int64_t)j * a.geo.rec8_bytes
+                           : pair_off + (int64_t)st.n8 * a.geo.rec8_bytes + (int64_t)(j - st.n8) * a.geo.rec4_bytes;
+  uint8_t* rec = a.cache + off;
+  constexpr int KB8 = BLK * D, KB4 = BLK * D / 2;
+  const int kbytes = is4 ? KB4 : KB8;
+  const int tid = threadIdx.x;
+
+  if (j == 0 && tid == 0) {
+    int32_t* e = reinterpret_cast<int32_t*>(a.cache + 64 + 64 * (int64_t)pair);
+    *reinterpret_cast<int64_t*>(e) = pair_off;
+    e[2] = st.n8;
+    e[3] = st.n4;
+    e[4] = a.pol.hi[g];
+    e[5] = a.pol.keep[g];
+    e[6] = st.lo8;
+    e[7] = st.sink;
+    e[8] = st.lo4;
+    e[9] = st.hi4;
+    e[10] = e[11] = e[12] = e[13] = 0;
+    if (pair == 0) {
+      int32_t* hd = reinterpret_cast<int32_t*>(a.cache);
+      hd[0] = 0x43564B54;  // "TKVC"
+      hd[1] = 1;
+      hd[2] = a.batch;
+      hd[3] = a.hkv;
+      hd[4] = D;
+      hd[5] = BLK;
+      hd[6] = c + 1;
+      hd[7] = c;
+      int64_t* h64 = reinterpret_cast<int64_t*>(a.cache);
+      h64[4] = a.geo.ctx_len;
+      h64[5] = a.geo.total_bytes;
+      h64[6] = 64;
+      h64[7] = a.geo.data_offset;
+    }
+  }
+
+  const int64_t src0 = ((int64_t)b * a.hkv + g) * a.n;
+  const int part = tid % TPR;
+  float* ks_out = reinterpret_cast<float*>(rec + 2 * kbytes);
+  float* vs_out = ks_out + BLK;
+#pragma unroll 1
+  for (int p = 0; p < BLK / RPP; ++p) {
+    const int r = p * RPP + tid / TPR;
+    const int64_t tok = (int64_t)kb * BLK + r;
+    const bool valid = tok < a.geo.ctx_len;
+    float xk[8], xv[8];
+    uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0);
+    if (valid) {
+      rk = *reinterpret_cast<const uint4*>(a.k + (src0 + tok) * D + part * 8);
+      rv = *reinterpret_cast<const uint4*>(a.v + (src0 + tok) * D + part * 8);
+    }
+    bf16x8_to_f32(rk, xk);
+    bf16x8_to_f32(rv, xv);
+    uint32_t k8w[2], k4w, v8w[2], v4w;
+    float ks8, ks4, vs8, vs4;
+    quantize8<TPR>(xk, k8w, k4w, ks8, ks4);
+    quantize8<TPR>(xv, v8w, v4w, vs8, vs4);
+    if (!is4) {
+      *reinterpret_cast<uint2*>(rec + r * D + part * 8) = make_uint2(k8w[0], k8w[1]);
+      *reinterpret_cast<uint2*>(&vbuf[r][part * 8]) = make_uint2(v8w[0], v8w[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(rec + r * (D / 2) + part * 4) = k4w;
+      uint32_t e0 = 0, e1 = 0;  // int4 codes as sign-extended bytes
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int code = ((int)(v4w << (28 - 4 * i))) >> 28;
+        if (i < 4) e0 |= ((uint32_t)code & 0xFFu) << (8 * i);
+        else e1 |= ((uint32_t)code & 0xFFu) << (8 * (i - 4));
+      }
+      *reinterpret_cast<uint2*>(&vbuf[r][part * 8]) = make_uint2(e0, e1);
+    }
+    if (part == 0) {
+      ks_out[r] = is4 ? ks4 : ks8;
+      vs_out[r] = is4 ? vs4 : vs8;
+    }
+  }
+  __syncthreads();
+  // transposed V codes in feed order
+  uint8_t* vt = rec + kbytes;
+  if (!is4) {
+    constexpr int CPR = BLK / 16;  // 16-byte chunks per output row
+    for (int ch = tid; ch < D * CPR; ch += kThreads) {
+      const int d = ch / CPR, p0 = (ch % CPR) * 16;
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int p = p0 + i;
+        const int tok = (p & ~63) + feed_token(p & 63);
+        w[i / 4] |= ((uint32_t)(uint8_t)vbuf[tok][d]) << (8 * (i % 4));
+      }
+      *reinterpret_cast<uint4*>(vt + (int64_t)d * BLK + p0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    constexpr int CPR = BLK / 32;  // 16-byte chunks (32 positions) per output row
+    for (int ch = tid; ch < D * CPR; ch += kThreads) {
+      const int d = ch / CPR, p0 = (ch % CPR) * 32;
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int p = p0 + i;
+        const int tok = (p & ~63) + feed_token(p & 63);
+        w[i / 8] |= ((uint32_t)vbuf[tok][d] & 0xFu) << (4 * (i % 8));
+      }
+      *reinterpret_cast<uint4*>(vt + (int64_t)d * (BLK / 2) + p0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int D, int BLK>
+hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
+  hipLaunchKernelGGL((pack_kernel<D, BLK>), dim3(max_stored, a.batch * a.hkv), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const void* k,
+                       const void* v, void* cache, hipStream_t stream) {
+  PackArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.n = s.n;
+  a.batch = s.batch;
+  a.hkv = s.hkv;
+  a.pol = pol;
+  a.geo = geo;
+  const int max_stored = geo.cur_block + 1;
+  if (s.d == 128 && s.blk == 128) return launch_t<128, 128>(a, max_stored, stream);
+  if (s.d == 128 && s.blk == 64) return launch_t<128, 64>(a, max_stored, stream);
+  if (s.d == 64 && s.blk == 128) return launch_t<64, 128>(a, max_stored, stream);
+  return launch_t<64, 64>(a, max_stored, stream);
+}
+
+}  // namespace tria

@@ -1,0 +1,153 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* the library loads and exports every function include/tria.h declares;
+* tria_build_policy (host) matches the oracle's schedule bit for bit on the five
+  workloads and on random shapes, including ragged sequence lengths;
+* tria_kv_cache_bytes matches the oracle's cache size;
+* validation returns the documented status codes and enqueues nothing.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tria():
+    import block_sparse_mixed_head_amd as t
+    return t
+
+
+def test_library_exports_every_declared_symbol(tria):
+    from block_sparse_mixed_head_amd import _lib
+    header = open(os.path.join(ROOT, "include", "tria.h")).read()
+    declared = set(re.findall(r"\b(tria_[a-z_0-9]+)\s*\(", header))
+    assert declared, "no declarations parsed"
+    for name in sorted(declared):
+        assert hasattr(_lib.lib, name), name
+    assert declared == set(_lib.EXPORTED)
+    assert _lib.lib.tria_version() >> 16 == 1
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+def test_schedule_bit_exact_on_workloads(tria, cid):
+    c = synth.CONFIGS[cid]
+    hi, keep = c.policy()
+    d = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
+    mine = tria.build_policy(d, hi, keep)
+    ref = oracle.build_schedule(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len, hi, keep)
+    assert mine.dtype == np.int32 and np.array_equal(mine, ref)
+
+
+def test_schedule_bit_exact_random_shapes(tria):
+    rng = np.random.default_rng(0)
+    for _ in range(40):
+        blk = int(rng.choice([64, 128]))
+        hd = int(rng.choice([64, 128]))
+        hk = int(rng.integers(1, 4))
+        hq = hk * int(rng.integers(1, 5))
+        b = int(rng.integers(1, 3))
+        n = int(rng.integers(1, 20 * blk))
+        nb = (n + blk - 1) // blk
+        hi = rng.integers(0, nb + 2, size=hq).astype(np.int32)
+        keep = (hi + rng.integers(0, nb + 2, size=hq)).astype(np.int32)
+        d = tria.make_dims(b, hq, hk, hd, blk, n)
+        assert np.array_equal(tria.build_policy(d, hi, keep),
+                              oracle.build_schedule(b, hq, hk, hd, blk, n, hi, keep))
+
+
+def test_tiny_workload_tile_counts(tria):
+    c = synth.CONFIGS[1]
+    hi, keep = c.policy()
+    d = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
+    units = tria.build_policy(d, hi, keep)[16:].reshape(-1, 8)
+    per_head = {}
+    for b, h, qb, lo8, lo4, hi4, sink, nt in units:
+        e = per_head.setdefault(h, [0, 0])
+        e[0] += (qb - lo8 + 1) + sink
+        e[1] += hi4 - lo4 + 1
+    # 26 int8 and 7 int4 tiles per head, 3 skipped, of the 36 causal tiles
+    assert per_head == {0: [26, 7], 1: [26, 7]}
+
+
+@pytest.mark.parametrize("cid", [2, 4, 5])
+def test_cache_bytes_match_oracle(tria, cid):
+    c = synth.CONFIGS[cid]
+    hi, keep = c.policy()
+    d = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
+    for ctx in (1, c.block, c.seq_len - 77, c.seq_len):
+        assert tria.kv_cache_bytes(d, hi, keep, ctx) == oracle.cache_bytes(
+            c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, ctx, hi, keep)
+
+
+def test_cache_bytes_dense_policy_pins_page_formula(tria):
+    # every block stored at int8: codes are the page's formula with p = 1 byte
+    b, hk, hd, blk, n = 2, 8, 128, 128, 4096
+    d = tria.make_dims(b, hk, hk, hd, blk, n)
+    top = np.full(hk, n // blk, np.int32)
+    header = (64 + 64 * b * hk + 255) // 256 * 256
+    assert tria.kv_cache_bytes(d, top, top, n) == header + oracle.kv_formula_bytes(1, hk, hd, n, b, 1) + 2 * hk * n * b * 4
+
+
+def test_decode_workspace_is_positive(tria):
+    d = tria.make_dims(16, 32, 8, 128, 128, 32768)
+    assert tria.decode_workspace_bytes(d, 32768) > 0
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_validation_errors(tria):
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    hi = np.array([1, 2], np.int32)
+    keep = np.array([3, 2], np.int32)
+    need = C.c_size_t(0)
+
+    def bp(d, h=hi, k=keep, n=2):
+        return L.tria_build_policy(C.byref(d), h.ctypes.data, k.ctypes.data, n, None, 0, C.byref(need))
+
+    good = tria.make_dims(1, 2, 1, 64, 64, 512)
+    assert bp(good) == _lib.TRIA_OK and need.value == 64 + 32 * 16
+    assert bp(tria.make_dims(1, 3, 2, 64, 64, 512), n=3) == _lib.TRIA_ERR_INVALID_ARG  # Hq % Hkv
+    assert bp(tria.make_dims(1, 2, 1, 96, 64, 512)) == _lib.TRIA_ERR_UNSUPPORTED       # head_dim
+    assert bp(tria.make_dims(1, 2, 1, 64, 32, 512)) == _lib.TRIA_ERR_UNSUPPORTED       # block
+    assert bp(tria.make_dims(1, 2, 1, 64, 64, 0)) == _lib.TRIA_ERR_INVALID_ARG         # seq_len
+    assert bp(good, h=np.array([4, 2], np.int32)) == _lib.TRIA_ERR_INVALID_ARG         # hi > keep
+    assert bp(good, h=np.array([-1, 2], np.int32)) == _lib.TRIA_ERR_INVALID_ARG        # hi < 0
+    assert bp(good, n=1) == _lib.TRIA_ERR_INVALID_ARG                                  # head count
+    assert b"keep" in L.tria_last_error() or b"n_policy" in L.tria_last_error()
+    small = np.zeros(10, np.int32)
+    assert L.tria_build_policy(C.byref(good), hi.ctypes.data, keep.ctypes.data, 2, small.ctypes.data, 40,
+                               C.byref(need)) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert need.value == 64 + 32 * 16
+    bad = tria.make_dims(1, 2, 1, 64, 64, 512)
+    bad.reserved = 1
+    assert bp(bad) == _lib.TRIA_ERR_INVALID_ARG
+    # device calls: validation happens before any HIP call, so these run without a GPU
+    z = C.c_void_p(0)
+    one = C.c_void_p(16)
+    assert L.tria_quantize_qk(C.byref(good), z, one, *([one] * 8), None) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_prefill(C.byref(good), one, 10, *([one] * 8), one, C.c_float(0.125), one, None,
+                          None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_prefill(C.byref(good), one, 1 << 20, *([one] * 8), one, C.c_float(-1.0), one, None,
+                          None) == _lib.TRIA_ERR_INVALID_ARG
+    sz = C.c_size_t(0)
+    assert L.tria_kv_cache_bytes(C.byref(good), hi.ctypes.data, keep.ctypes.data, 2, 0, C.byref(sz)) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_kv_cache_bytes(C.byref(good), hi.ctypes.data, keep.ctypes.data, 2, 513, C.byref(sz)) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_kv_cache_bytes(C.byref(good), hi.ctypes.data, keep.ctypes.data, 3, 100, C.byref(sz)) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_pack_kv_cache(C.byref(good), hi.ctypes.data, keep.ctypes.data, 2, 512, one, one, one, 100,
+                                None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_decode(C.byref(good), one, 1 << 20, 512, one, C.c_float(0.125), one, one, 16,
+                         None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    mqa = tria.make_dims(1, 64, 1, 64, 64, 512)
+    assert L.tria_decode(C.byref(mqa), one, 1 << 20, 512, one, C.c_float(0.125), one, one, 1 << 30,
+                         None) == _lib.TRIA_ERR_UNSUPPORTED

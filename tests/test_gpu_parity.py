@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: codes, scales, schedules and packed cache bytes bit-exact; attention outputs
+within max|diff| <= 2e-2 and mean relative error sum|diff| / sum|ref| <= 1e-3.
+Small shapes are compared element by element over every output; the full-size
+workloads (the launch configuration the benchmark times) on sampled query blocks
+the oracle recomputes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_REL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def tria():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_mixed_head_amd as t
+    return t
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str):
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    diff = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    mx = diff.max()
+    rel = diff.sum() / max(np.abs(ref).sum(), 1e-30)
+    print(f"[parity] {what}: max|diff|={mx:.3e} mean_rel={rel:.3e}", flush=True)
+    assert mx <= MAX_ABS and rel <= MEAN_REL, (what, mx, rel)
+
+
+def inputs(cfg):
+    q, k, v = synth.make_prefill_inputs(cfg)
+    return q, k, v
+
+
+def run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=False):
+    d = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
+    sched = torch.from_numpy(tria.build_policy(d, hi, keep)).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    qz = tria.quantize_qk(d, qd, kd)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda") if with_lse else None
+    out = tria.prefill(d, sched, qz, vd, 1.0 / math.sqrt(cfg.head_dim), lse=lse)
+    torch.cuda.synchronize()
+    return out, lse, qz
+
+
+# ------------------------------------------------------------------ quantiser
+@pytest.mark.parametrize("cid", [1, 2])
+def test_quantizer_bit_exact(tria, cid):
+    cfg = synth.CONFIGS[cid]
+    print(f"[case] quantize config {cid}", flush=True)
+    q, k, _ = inputs(cfg)
+    d = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
+    qz = tria.quantize_qk(d, dev(q), dev(k))
+    torch.cuda.synchronize()
+    for x, c8, c4, s8, s4 in ((q, qz.q8, qz.q4, qz.q8s, qz.q4s), (k, qz.k8, qz.k4, qz.k8s, qz.k4s)):
+        r8, rs8 = oracle.quantize_rows(x, 127)
+        r4, rs4 = oracle.quantize_rows(x, 7)
+        assert np.array_equal(c8.cpu().numpy(), r8)
+        assert np.array_equal(s8.cpu().numpy().view(np.uint32), rs8.view(np.uint32))
+        assert np.array_equal(c4.cpu().numpy(), oracle.pack_nibbles(r4))
+        assert np.array_equal(s4.cpu().numpy().view(np.uint32), rs4.view(np.uint32))
+
+
+def test_quantizer_edge_rows(tria):
+    # zero rows, constant rows, exact .5 ties, huge and tiny magnitudes
+    b, h, n, d = 1, 1, 64, 128
+    x = np.random.default_rng(0).standard_normal((b, h, n, d)).astype(np.float32)
+    x[0, 0, 0] = 0
+    x[0, 0, 1] = -3.5
+    x[0, 0, 2] = 0
+    x[0, 0, 2, 0] = 127.0
+    x[0, 0, 2, 1:6] = [0.5, 1.5, 2.5, -0.5, -2.5]
+    x[0, 0, 3] *= 1e30
+    x[0, 0, 4] *= 1e-30
+    bits = synth.float32_to_bf16_bits(x)
+    dd = tria.make_dims(b, h, h, d, 64, n)
+    qz = tria.quantize_qk(dd, dev(bits), dev(bits))
+    torch.cuda.synchronize()
+    r8, s8 = oracle.quantize_rows(bits, 127)
+    r4, s4 = oracle.quantize_rows(bits, 7)
+    assert np.array_equal(qz.q8.cpu().numpy(), r8) and np.array_equal(qz.k8.cpu().numpy(), r8)
+    assert np.array_equal(qz.q4.cpu().numpy(), oracle.pack_nibbles(r4))
+    assert np.array_equal(qz.q8s.cpu().numpy(), s8) and np.array_equal(qz.q4s.cpu().numpy(), s4)
+
+
+# ------------------------------------------------------------------ prefill, small shapes (every output)
+def small_cfg(b, hq, hk, d, n, blk, seed=21):
+    return synth.Config("small", b, hq, hk, d, n, blk, seed=seed)
+
+
+SMALL = [
+    # (b, hq, hk, d, n, blk, hi, keep)
+    (1, 2, 1, 64, 512, 64, [2, 2], [4, 4]),             # the tiny workload's shape and policy
+    (1, 4, 2, 128, 700, 128, [0, 1, 2, 6], [6, 3, 2, 6]),   # ragged n, B=128
+    (2, 3, 3, 64, 333, 64, [0, 1, 9], [0, 4, 9]),       # MHA, ragged, batch 2
+    (1, 4, 1, 128, 640, 64, [1, 0, 3, 0], [1, 9, 5, 2]),    # MQA, B=64, d=128
+    (1, 7, 1, 128, 1000, 128, [7, 0, 0, 1, 2, 3, 4], [7, 0, 7, 5, 4, 3, 6]),  # G=7 edge policies
+    (1, 2, 1, 64, 40, 64, [0, 3], [0, 3]),              # n < block
+    (1, 2, 2, 128, 129, 128, [0, 0], [0, 1]),            # one full block + one token
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"b{c[0]}h{c[1]}k{c[2]}d{c[3]}n{c[4]}B{c[5]}" for c in SMALL])
+def test_prefill_small_every_output(tria, case):
+    b, hq, hk, d, n, blk, hi, keep = case
+    print(f"[case] prefill small {case}", flush=True)
+    cfg = small_cfg(b, hq, hk, d, n, blk)
+    q, k, v = inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
+    ref, rlse = oracle.prefill(q, k, v, hi, keep, blk, 1.0 / math.sqrt(d), with_lse=True)
+    assert_close(out.cpu().numpy(), ref, f"prefill {case}")
+    assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
+
+
+def test_prefill_integer_inputs_and_determinism(tria):
+    # all blocks kept and integer rows with amax 127 (codes = values, scales 1):
+    # large exact integer scores; two runs must be bitwise equal
+    rng = np.random.default_rng(3)
+    b, hq, hk, d, n, blk = 1, 2, 1, 128, 300, 128
+    x = rng.integers(-127, 128, size=(b, hq + 2 * hk, n, d)).astype(np.float32)
+    x[..., 0] = 127.0
+    x[:, hq + hk:] = rng.integers(-9, 10, size=(b, hk, n, d))
+    bits = synth.float32_to_bf16_bits(x)
+    q, k, v = bits[:, :hq].copy(), bits[:, hq:hq + hk].copy(), bits[:, hq + hk:].copy()
+    top = np.full(hq, 99, np.int32)
+    cfg = small_cfg(b, hq, hk, d, n, blk)
+    out, _, _ = run_prefill(tria, cfg, q, k, v, top, top)
+    out2, _, _ = run_prefill(tria, cfg, q, k, v, top, top)
+    assert np.array_equal(out.cpu().numpy(), out2.cpu().numpy()), "not deterministic"
+    ref = oracle.prefill(q, k, v, top, top, blk, 1.0 / math.sqrt(d))
+    assert_close(out.cpu().numpy(), ref, "integer-exact all-kept")
+
+
+def test_prefill_skipped_blocks_never_read(tria):
+    # NaN in key/value rows of blocks that every query block either skips or has
+    # past the causal boundary must leave the output bit-identical
+    b, hq, hk, d, n, blk = 1, 2, 1, 128, 1024, 128
+    cfg = small_cfg(b, hq, hk, d, n, blk, seed=31)
+    q, k, v = inputs(cfg)
+    hi, keep = np.array([1, 0], np.int32), np.array([2, 2], np.int32)
+    base, _, _ = run_prefill(tria, cfg, q, k, v, hi, keep)
+    k2, v2 = k.copy(), v.copy()
+    # block 2 is skipped for query blocks >= 5 (distance > 2); poison only rows those
+    # blocks can see is impossible, so compare rows of query blocks >= 5 only
+    k2[..., 2 * blk:3 * blk, :] = 0x7FC0
+    v2[..., 2 * blk:3 * blk, :] = 0x7FC0
+    pois, _, _ = run_prefill(tria, cfg, q, k2, v2, hi, keep)
+    a = base.cpu().numpy()[:, :, 5 * blk:]
+    p = pois.cpu().numpy()[:, :, 5 * blk:]
+    assert np.array_equal(a, p)
+
+
+# ------------------------------------------------------------------ prefill, full-size workloads (sampled)
+def sample_units(cfg, hi, keep, per_head, heads=None, seed=0):
+    rng = np.random.default_rng(seed)
+    nb = cfg.nb
+    units = []
+    for bb in range(cfg.batch):
+        for h in (heads if heads is not None else range(cfg.n_q_heads)):
+            qbs = {0, nb - 1, min(nb - 1, keep[h] + 2)} | set(rng.integers(0, nb, size=per_head).tolist())
+            units += [(bb, h, int(x)) for x in sorted(qbs)]
+    return units
+
+
+@pytest.mark.parametrize("cid,per_head,heads", [(2, 3, None), (5, 2, [0, 1, 2, 3, 9, 27]), (3, 1, None)])
+def test_prefill_full_size_sampled(tria, cid, per_head, heads):
+    cfg = synth.CONFIGS[cid]
+    print(f"[case] prefill full-size config {cid}", flush=True)
+    q, k, v = inputs(cfg)
+    hi, keep = cfg.policy()
+    out, _, _ = run_prefill(tria, cfg, q, k, v, hi, keep)
+    units = sample_units(cfg, hi, keep, per_head, heads)
+    if cid == 5:
+        units = [u for u in units if u[0] in (0, 3)]
+    ref = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), units=units)
+    got, want = [], []
+    for (bb, h, qb) in units:
+        r0, r1 = qb * cfg.block, min(cfg.seq_len, (qb + 1) * cfg.block)
+        got.append(out[bb, h, r0:r1].cpu().numpy())
+        want.append(ref[bb, h, r0:r1])
+    assert_close(np.concatenate(got), np.concatenate(want), f"prefill config {cid} ({len(units)} sampled units)")
+    # every output row is finite
+    assert torch.isfinite(out).all().item()
+
+
+# ------------------------------------------------------------------ cache + decode
+DEC_SMALL = [
+    # (b, hq, hk, d, n, blk, ctx, hi, keep)  policies per KV head
+    (2, 4, 2, 64, 900, 64, 897, [1, 0], [5, 9]),
+    (1, 8, 2, 128, 1300, 128, 1300, [0, 2], [3, 10]),
+    (3, 7, 1, 128, 700, 64, 650, [2], [4]),
+    (1, 32, 1, 128, 512, 128, 500, [1], [2]),   # MQA with 32 query heads (two row groups)
+    (1, 2, 2, 64, 64, 64, 1, [0, 0], [0, 0]),   # a single token
+    (1, 4, 4, 128, 2000, 128, 2000, [99, 0, 0, 1], [99, 0, 99, 2]),
+]
+
+
+def _dec_case(tria, case, seed=41):
+    b, hq, hk, d, n, blk, ctx, hi, keep = case
+    cfg = synth.Config("dec", b, hq, hk, d, n, blk, seed=seed, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx, dev(k), dev(v))
+    out = tria.decode(dd, cache, ctx, dev(q), 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    return cfg, k, v, q, hi, keep, dd, cache, out
+
+
+@pytest.mark.parametrize("case", DEC_SMALL, ids=[f"b{c[0]}h{c[1]}k{c[2]}d{c[3]}ctx{c[6]}B{c[5]}" for c in DEC_SMALL])
+def test_pack_and_decode_small(tria, case):
+    print(f"[case] decode small {case}", flush=True)
+    cfg, k, v, q, hi, keep, dd, cache, out = _dec_case(tria, case)
+    b, hq, hk, d, n, blk, ctx = case[:7]
+    ref_blob = oracle.pack_cache(k, v, hi, keep, hq, blk, ctx)
+    assert cache.numel() == ref_blob.size
+    assert np.array_equal(cache.cpu().numpy(), ref_blob), "packed cache differs from the oracle's bytes"
+    tria.check_cache(dd, cache, ctx)
+    ref = oracle.decode(k, v, q, hi, keep, blk, ctx, 1.0 / math.sqrt(d))
+    assert_close(out.cpu().numpy(), ref, f"decode {case}")
+
+
+def test_pack_merges_query_head_policies(tria):
+    b, hq, hk, d, n, blk, ctx = 1, 4, 2, 64, 600, 64, 600
+    cfg = synth.Config("dec", b, hq, hk, d, n, blk, seed=5, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi = np.array([0, 2, 1, 1], np.int32)
+    keep = np.array([3, 2, 1, 6], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx, dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.cpu().numpy(), oracle.pack_cache(k, v, hi, keep, hq, blk, ctx))
+
+
+def test_decode_rejects_corrupt_cache(tria):
+    case = (1, 4, 2, 64, 900, 64, 897, [1, 0], [5, 9])
+    cfg, k, v, q, hi, keep, dd, cache, out = _dec_case(tria, case)
+    bad = cache.clone()
+    bad[0] = 0  # magic
+    from block_sparse_mixed_head_amd import TriaError
+    with pytest.raises(TriaError):
+        tria.check_cache(dd, bad, 897)
+    with pytest.raises(TriaError):
+        tria.check_cache(dd, cache, 896)  # wrong context length
+    o = tria.decode(dd, bad, 897, dev(q), 0.125)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all().item()
+    bad = cache.clone()
+    bad[64 + 8:64 + 12] = torch.tensor([255, 255, 0, 0], dtype=torch.uint8)  # n8 of pair 0
+    o = tria.decode(dd, bad, 897, dev(q), 0.125)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all().item()
+
+
+def test_decode_full_size_workload(tria):
+    cfg = synth.CONFIGS[4]
+    print("[case] pack + decode full-size config 4", flush=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = cfg.policy()
+    dd = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
+    kd, vd = dev(k), dev(v)
+    cache = tria.pack_kv_cache(dd, hi, keep, cfg.seq_len, kd, vd)
+    out = tria.decode(dd, cache, cfg.seq_len, dev(q), 1.0 / math.sqrt(cfg.head_dim))
+    torch.cuda.synchronize()
+    tria.check_cache(dd, cache, cfg.seq_len)
+    # byte-exact cache on a sample of pairs (directory entries + their records)
+    ref_blob = oracle.pack_cache(k, v, hi, keep, cfg.n_q_heads, cfg.block, cfg.seq_len)
+    got = cache.cpu().numpy()
+    assert got.size == ref_blob.size and np.array_equal(got, ref_blob)
+    ref = oracle.decode(k, v, q, hi, keep, cfg.block, cfg.seq_len, 1.0 / math.sqrt(cfg.head_dim))
+    assert_close(out.cpu().numpy(), ref, "decode config 4")
