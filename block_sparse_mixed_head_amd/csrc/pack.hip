@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     e[7] = st.sink;
     e[8] = st.lo4;
     e[9] = st.hi4;
-    e[10] = e[11] = e[12] = e[13] = 0;
+    e[10] = e[11] = e[12] = e[13] = e[14] = e[15] = 0;
     if (pair == 0) {
       int32_t* hd = reinterpret_cast<int32_t*>(a.cache);
       hd[0] = 0x43564B54;  // "TKVC"
@@ -117,6 +117,11 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
       h64[6] = 64;
       h64[7] = a.geo.data_offset;
     }
+  }
+
+  if (pair == 0 && j == 0) {  // the padding between the directory and the first record
+    const int64_t pad0 = 64 + 64LL * a.batch * a.hkv;
+    for (int64_t i = pad0 + tid; i < a.geo.data_offset; i += kThreads) a.cache[i] = 0;
   }
 
   const int64_t src0 = ((int64_t)b * a.hkv + g) * a.n;

@@ -270,25 +270,25 @@ __global__ void __launch_bounds__((Cfg<D, BLK>::THREADS)) prefill_kernel(Args a)
     for (int g = 0; g < 2; ++g) {
       const float ag = is4 ? a4[g] : a8[g];
       const float nM = -M[g];
+      const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int t = 0; t < C::NT; ++t) {
+        v2bf x[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int s = 2 * t + half;
-          v2f p01 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][0], ag, nM)),
-                     __builtin_amdgcn_exp2f(fmaf(u[g][s][1], ag, nM))};
-          v2f p23 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][2], ag, nM)),
-                     __builtin_amdgcn_exp2f(fmaf(u[g][s][3], ag, nM))};
-          const v2bf b01 = __builtin_convertvector(p01, v2bf);
-          const v2bf b23 = __builtin_convertvector(p23, v2bf);
-          const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
-          lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(b01, one, lsum[g], false);
-          lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(b23, one, lsum[g], false);
-          pb[g][t][4 * half + 0] = b01[0];
-          pb[g][t][4 * half + 1] = b01[1];
-          pb[g][t][4 * half + 2] = b23[0];
-          pb[g][t][4 * half + 3] = b23[1];
+          const v2f p01 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][0], ag, nM)),
+                           __builtin_amdgcn_exp2f(fmaf(u[g][s][1], ag, nM))};
+          const v2f p23 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][2], ag, nM)),
+                           __builtin_amdgcn_exp2f(fmaf(u[g][s][3], ag, nM))};
+          x[2 * half] = __builtin_convertvector(p01, v2bf);
+          x[2 * half + 1] = __builtin_convertvector(p23, v2bf);
+          lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half], one, lsum[g], false);
+          lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half + 1], one, lsum[g], false);
         }
+        // keys 16*(2t) + 4kq + 0..3, then 16*(2t+1) + 4kq + 0..3 (the B operand's k order)
+        pb[g][t] = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
+                                           __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
 
@@ -304,15 +304,9 @@ __global__ void __launch_bounds__((Cfg<D, BLK>::THREADS)) prefill_kernel(Args a)
             (lds_v4s*)((__attribute__((address_space(3))) uint8_t*)(v_lds) + v_off<C::VU>(r0, bcol, D)));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_v4s*)((__attribute__((address_space(3))) uint8_t*)(v_lds) + v_off<C::VU>(r1, bcol, D)));
-        v8bf vop;
-        vop[0] = __builtin_bit_cast(__bf16, lo[0]);
-        vop[1] = __builtin_bit_cast(__bf16, lo[1]);
-        vop[2] = __builtin_bit_cast(__bf16, lo[2]);
-        vop[3] = __builtin_bit_cast(__bf16, lo[3]);
-        vop[4] = __builtin_bit_cast(__bf16, hi[0]);
-        vop[5] = __builtin_bit_cast(__bf16, hi[1]);
-        vop[6] = __builtin_bit_cast(__bf16, hi[2]);
-        vop[7] = __builtin_bit_cast(__bf16, hi[3]);
+        // whole-vector concatenation (element-wise inserts of the halves have been
+        // folded incorrectly by the compiler)
+        const v8bf vop = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         O[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[0][t], O[0][d], 0, 0, 0);
         O[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[1][t], O[1][d], 0, 0, 0);
       }

@@ -187,7 +187,7 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
  *   [64, 64 + 64*batch*n_kv_heads)  directory, one 64-byte entry per (b, g),
  *            b-major: int64 offset (from the blob start to the pair's first
  *            record), int32 n8, int32 n4, int32 hi, int32 keep, int32 lo8,
- *            int32 sink, int32 lo4, int32 hi4, int32 zero[4].  The stored int8
+ *            int32 sink, int32 lo4, int32 hi4, int32 zero[6].  The stored int8
  *            blocks are [block 0 if sink] then lo8..c; the int4 blocks lo4..hi4
  *            ((0, -1) when none); lo8, sink, lo4, hi4 follow the schedule's rule
  *            for query block c.  hi, keep are the (merged) KV-head boundaries.
