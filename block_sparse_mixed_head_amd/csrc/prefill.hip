@@ -36,6 +36,7 @@
 //   * Registers are held to 256 per lane so two work groups share a CU: one
 //     group's softmax (VALU) runs while the other's MFMAs and loads proceed.
 #include <cfloat>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -59,7 +60,8 @@ struct Cfg {
   static constexpr int K_BYTES = SK * D;
   static constexpr int V_BYTES = SK * D * 2;
   static constexpr int STAGE = K_BYTES + V_BYTES + SK * 4;
-  static constexpr int Q4_BYTES = BLK * D / 2;  // packed int4 query codes of the block
+  static constexpr int Q4_STRIDE = D + 16;       // widened int4 query codes: padded rows
+  static constexpr int Q4_BYTES = BLK * Q4_STRIDE;
   static constexpr int LDS_BYTES = 2 * STAGE + Q4_BYTES;  // two stage buffers + query codes
   static constexpr int K8_INSTR = K_BYTES / 1024;   // 1 KB load instructions per stage
   static constexpr int K4_INSTR = K_BYTES / 2048;
@@ -181,16 +183,14 @@ __device__ __forceinline__ void compute_stage(const uint8_t* buf, int key_base, 
                                               const uint8_t* q4lds, RowState (&rs)[2], v4f (&O)[2][Cfg<D, BLK>::ND],
                                               int lr, int kq, After&& after_reads) {
   using C = Cfg<D, BLK>;
-  // int4 stages read this wave's packed query codes from LDS and widen them
+  // int4 stages read this wave's query codes (widened to 16*code) from LDS
   v4i q4op[IS4 ? 2 : 1][C::KS];
   if (IS4) {
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const uint2 w = *reinterpret_cast<const uint2*>(q4lds + (rs[g].row * (D / 2)) + ks * 32 + kq * 8);
-        q4op[IS4 ? g : 0][ks] = unpack16_x16(w.x, w.y);
-      }
+      for (int ks = 0; ks < C::KS; ++ks)
+        q4op[IS4 ? g : 0][ks] = *reinterpret_cast<const v4i*>(q4lds + rs[g].row * C::Q4_STRIDE + ks * 64 + kq * 16);
   }
   const uint8_t* kb = buf;
   const lds_u8* vb = (const lds_u8*)(buf + C::K_BYTES);
@@ -239,18 +239,22 @@ __device__ __forceinline__ void compute_stage(const uint8_t* buf, int key_base, 
     mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 16));
     mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 32));
   }
+  // The running maximum M only has to be an integer that keeps 2^(t - M) finite:
+  // it is raised (and O, l rescaled by an exact power of two) only when a row's
+  // stage maximum exceeds it by more than kSlack, so weights stay below 2^kSlack.
+  constexpr float kSlack = 8.0f;
   bool need = false;
   float Mc[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const float ag = IS4 ? rs[g].a4 : rs[g].a8;
     Mc[g] = ceilf(mx[g] * ag);  // -inf when the whole stage is masked for this row
-    need = need || (Mc[g] > rs[g].M);
+    need = need || (Mc[g] > rs[g].M + kSlack);
   }
   if (__ballot(need)) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const float Mn = fmaxf(rs[g].M, Mc[g]);
+      const float Mn = Mc[g] > rs[g].M + kSlack ? Mc[g] : rs[g].M;
       const float f = exp2f(rs[g].M - Mn);  // exact power of two; 0 on the first stage
       rs[g].M = Mn;
       rs[g].l *= f;
@@ -360,14 +364,15 @@ prefill_kernel(Args a) {
   // first stage in flight while the query state is set up
   issue(0, smem);
 
-  // packed int4 query codes of the block into LDS (rows past the end as zeros)
+  // int4 query codes of the block, widened once to 16*code, into LDS (rows past the
+  // end as zeros); each 16-byte group keeps the order unpack16_x16 gives the keys
 #pragma unroll
-  for (int i = tid; i < C::Q4_BYTES / 16; i += C::THREADS) {
-    const int r = i / (D / 32), c = i % (D / 32);
+  for (int i = tid; i < BLK * (D / 16); i += C::THREADS) {
+    const int r = i / (D / 16), c = i % (D / 16);
     const int64_t qi = (int64_t)qb * BLK + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (qi < n) val = *reinterpret_cast<const uint4*>(a.q4 + (qrow0 + qi) * (D / 2) + c * 16);
-    *reinterpret_cast<uint4*>(q4lds + r * (D / 2) + c * 16) = val;
+    uint2 val = make_uint2(0, 0);
+    if (qi < n) val = *reinterpret_cast<const uint2*>(a.q4 + (qrow0 + qi) * (D / 2) + c * 8);
+    *reinterpret_cast<v4i*>(q4lds + r * C::Q4_STRIDE + c * 16) = unpack16_x16(val.x, val.y);
   }
   v4i q8op[2][C::KS];
   RowState rs[2];
@@ -393,10 +398,15 @@ prefill_kernel(Args a) {
     for (int d = 0; d < C::ND; ++d) O[g][d] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int st = 0; st < nstages; ++st) {
-    // The loads write LDS asynchronously and count as loads, so the barrier alone does
-    // not wait for them: each wave drains its own, then the barrier makes all of them
-    // visible (stage st is in LDS) and frees the buffer of stage st-1.
+  // One stage: drain this wave's loads, barrier (stage st is in LDS and stage
+  // st-1's buffer is free), read the key scales, compute, and issue the next
+  // stage's loads after the stage's last LDS read (the compiler cannot tell LDS
+  // reads from the loads' LDS writes and would otherwise make the reads wait for
+  // them; the other work group on the CU computes while they are in flight).
+  // The loads write LDS asynchronously and count as loads, so the barrier alone
+  // does not wait for them: each wave drains its own first.
+  auto run = [&](auto is4_tag, auto diag_tag, int st) __attribute__((always_inline)) {
+    constexpr bool IS4 = decltype(is4_tag)::value, DIAG = decltype(diag_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const uint8_t* buf = smem + (st & 1) * C::STAGE;
@@ -404,26 +414,25 @@ prefill_kernel(Args a) {
     const float* sc = reinterpret_cast<const float*>(buf + C::K_BYTES + C::V_BYTES);
 #pragma unroll
     for (int s = 0; s < 4; ++s) ksc[s] = *reinterpret_cast<const float4*>(sc + s * 16 + kq * 4);
-    bool is4;
-    const int kb = tile_of(st / C::SPT, is4);
-    const int key_base = (st % C::SPT) * C::SK;
-    // The next stage's loads are issued once this wave's LDS reads of the stage are
-    // done (inside compute_stage, before its last MFMAs): the compiler cannot tell
-    // LDS reads from the loads' LDS writes and would otherwise wait for them.  The
-    // other work group on the CU computes while they are in flight.
     auto next = [&]() {
       if (st + 1 < nstages) issue(st + 1, smem + ((st + 1) & 1) * C::STAGE);
     };
-    if (kb == qb) {
-      // diagonal block: waves whose rows all precede the stage's keys skip it
-      if (key_base <= wave * 32 + 31) compute_stage<D, BLK, false, true>(buf, key_base, ksc, q8op, q4lds, rs, O, lr, kq, next);
-      else next();
-    } else if (is4) {
-      compute_stage<D, BLK, true, false>(buf, key_base, ksc, q8op, q4lds, rs, O, lr, kq, next);
-    } else {
-      compute_stage<D, BLK, false, false>(buf, key_base, ksc, q8op, q4lds, rs, O, lr, kq, next);
-    }
-  }
+    const int key_base = (st % C::SPT) * C::SK;
+    // diagonal block: waves whose rows all precede the stage's keys skip it
+    if (!DIAG || key_base <= wave * 32 + 31)
+      compute_stage<D, BLK, IS4, DIAG>(buf, key_base, ksc, q8op, q4lds, rs, O, lr, kq, next);
+    else
+      next();
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  // stages by kind, in schedule order: sink block, int4 range, int8 run, diagonal
+  // (one loop per kind keeps the accumulators in the same registers)
+  int st = 0;
+  for (; st < sink * C::SPT; ++st) run(F(), F(), st);
+  for (; st < (sink + n4) * C::SPT; ++st) run(T(), F(), st);
+  for (; st < (ntiles - 1) * C::SPT; ++st) run(F(), F(), st);
+  for (; st < nstages; ++st) run(F(), T(), st);
 
   // ---- epilogue: normalise and store (fp32), optional base-2 LSE
 #pragma unroll
