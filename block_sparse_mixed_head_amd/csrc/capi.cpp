@@ -370,6 +370,8 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
   const int64_t dir_end = 64 + 64LL * dims->batch * dims->n_kv_heads;
   if ((int64_t)cache_bytes < dir_end) return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache smaller than its directory");
   const tria::Shape s = shape_of(dims);
+  if (!tria::decode_units_fit(s, ctx_len))
+    return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads * ctx_len too large for one decode call");
   const int64_t need = tria::decode_workspace_bytes(s, ctx_len);
   if ((int64_t)ws_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "decode workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);

@@ -8,26 +8,30 @@
 //   s_j = dot(qc^a, kc_j^a) * sq^a * sk_j * sm_scale      (a = block precision)
 //   out = sum_j exp(s_j - max) * sv_j * vc_j / sum_j exp(s_j - max)
 //
-// gfx950 design (split-KV, two kernels):
-//   * The stored blocks of each (batch, KV head) pair are cut into items of up to
-//     kGroupsPerItem 64-token groups.  A persistent grid walks the items; each work
-//     group derives the item -> pair map from the cache directory itself (prefix
-//     over the directory in LDS), so the host needs no knowledge of the policy.
-//   * Each wavefront takes whole 64-token groups and serves all G query heads of
-//     the KV head at once (G rows padded to 16 per MFMA row group): every cache
-//     byte is read exactly once per step.
-//   * q.k: v_mfma_i32_16x16x64_i8 with K codes loaded straight from HBM into
-//     registers as the A operand (int4 groups widened to 16*code).
-//   * p.v: v_mfma_f32_16x16x32_bf16 with the V codes (stored transposed, in feed
-//     order, so each lane loads one 16-byte run) converted to bf16 exactly, and the
-//     fp32 weight p*sv split into a bf16 high part and a bf16 remainder, so the
-//     product keeps ~16 mantissa bits (fp32-class accuracy, no bf16 rounding of P).
-//   * Online softmax in fp32 (base 2); the four wavefronts of a work group merge in
-//     LDS; one partial (m, l, o[d]) per item and row goes to the workspace, and a
-//     second kernel merges the items of each pair.
-//   * The kernels validate the cache header and directory before reading any
+// gfx950 design (split-KV by bytes, two kernels):
+//   * The stored records of all (batch, KV head) pairs form one sequence of
+//     32-token steps; an int8 step costs two units (its bytes), an int4 step one.
+//     A persistent grid of wavefronts splits the units evenly (wave w owns the
+//     steps starting in [U*w/W, U*(w+1)/W)), so every wavefront streams the same
+//     number of bytes whatever the policy.  Each work group derives the split from
+//     the cache directory itself (prefix sums in LDS); the host needs no knowledge
+//     of the policy.
+//   * A wavefront serves all G query heads of a KV head at once (G rows padded to
+//     16 per MFMA row group), so every cache byte is read exactly once per step,
+//     and keeps the next step's loads in flight (register double buffer) while it
+//     computes the current one.
+//   * q.k: v_mfma_i32_16x16x64_i8 with K codes straight from HBM as the A operand
+//     (int4 steps widened to 16*code).  p.v: v_mfma_f32_16x16x32_bf16 with the V
+//     codes (stored per 32-token chunk, transposed, in the order the MFMA consumes
+//     them; a step reads one contiguous chunk with lane-contiguous loads) converted
+//     to bf16 exactly, and the fp32 weight p*sv split into a bf16 high part and a
+//     bf16 remainder, so the product keeps ~16 mantissa bits.
+//   * Online softmax in fp32 (base 2).  Each wavefront writes one partial
+//     (m, l, o[d]) per pair it touched; a second kernel merges a pair's partials.
+//   * Both kernels validate the cache header and directory before reading any
 //     record; on a mismatch nothing is read and the merge writes NaN.
 #include <cfloat>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -38,12 +42,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kGroupsPerItem = 8;  // 64-token groups per work item
-constexpr int kMaxPairs = 4096;    // directory entries kept in LDS
-constexpr int kMaxGrid = 2048;
+constexpr int kGrid = 512;                  // persistent work groups (two per CU)
+constexpr int kMaxWaves = kGrid * kWaves;
+constexpr int kMaxPairs = 4096;             // directory entries handled in LDS
 
-// workspace: [0,64) header {valid, n_pairs, total_items}; [64, 64 + 4*(P+1)) item
-// prefix per pair; partials from ws_part_offset: [item][row][D + 4] floats
+// workspace: [0,64) header {valid, n_pairs, n_slots, n_waves}; [64, 64 + 4*(P+1))
+// slot prefix per pair; partials from ws_part_offset: [slot][row][D + 4] floats
 // (o[0..D), m, l, 0, 0).
 __host__ __device__ inline int64_t ws_part_offset(int64_t pairs) {
   return (64 + 4 * (pairs + 1) + 255) / 256 * 256;
@@ -56,7 +60,6 @@ struct DecArgs {
   float* out;
   int64_t cache_bytes;
   int64_t ctx_len;
-  int64_t max_items;
   int batch, hq, hkv;
   float c;  // sm_scale * log2(e)
 };
@@ -76,39 +79,9 @@ __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
   geo.cur = (int)((a.ctx_len - 1) / BLK);
   geo.data_offset = (64 + 64LL * a.batch * a.hkv + 255) / 256 * 256;
   geo.total = h64[5];
-  return hd[0] == 0x43564B54 && hd[1] == 1 && hd[2] == a.batch && hd[3] == a.hkv && hd[4] == D &&
+  return hd[0] == 0x43564B54 && hd[1] == 2 && hd[2] == a.batch && hd[3] == a.hkv && hd[4] == D &&
          hd[5] == BLK && hd[6] == geo.cur + 1 && hd[7] == geo.cur && h64[4] == a.ctx_len &&
          geo.total <= a.cache_bytes && h64[6] == 64 && h64[7] == geo.data_offset;
-}
-
-struct Entry {
-  int64_t off;
-  int n8, n4, lo8, sink, lo4;
-};
-
-__device__ __forceinline__ Entry read_entry(const uint8_t* cache, int pair) {
-  const int32_t* e = reinterpret_cast<const int32_t*>(cache + 64 + 64 * (int64_t)pair);
-  Entry r;
-  r.off = *reinterpret_cast<const int64_t*>(e);
-  r.n8 = e[2];
-  r.n4 = e[3];
-  r.lo8 = e[6];
-  r.sink = e[7];
-  r.lo4 = e[8];
-  return r;
-}
-
-template <int D, int BLK>
-__device__ __forceinline__ bool entry_ok(const Entry& e, const Geo& geo) {
-  return e.n8 >= 1 && e.n4 >= 0 && e.n8 + e.n4 <= geo.cur + 1 && e.off >= geo.data_offset &&
-         e.off + (int64_t)e.n8 * geo.rec8 + (int64_t)e.n4 * geo.rec4 <= geo.total && e.lo8 >= 0 &&
-         e.lo8 <= geo.cur && (e.sink == 0 || e.sink == 1) && e.lo4 >= 0 && e.lo4 + e.n4 <= geo.cur + 1;
-}
-
-template <int BLK>
-__device__ __forceinline__ int items_of(const Entry& e) {
-  const int groups = (e.n8 + e.n4) * (BLK / 64);
-  return (groups + kGroupsPerItem - 1) / kGroupsPerItem;
 }
 
 // 8 signed bytes -> 8 bf16 (exact: |value| <= 127)
@@ -132,12 +105,298 @@ __device__ __forceinline__ v2i nib8_ordered_x16(uint32_t w) {
   return r;
 }
 
-template <int D, int BLK, int RG>
-__global__ void __launch_bounds__(kThreads) decode_split_kernel(DecArgs a) {
+// Exclusive prefix over the work group of one value per thread; returns the
+// prefix and sets `total`.  `tmp` holds kWaves ints; ends with a barrier.
+__device__ __forceinline__ int block_scan(int x, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = tmp[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - x;
+}
+
+// Wave-uniform copies (scalar registers): record bases and step indices built from
+// them keep the loads in the scalar-base + lane-offset form, with no per-lane
+// address arithmetic.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  return (int64_t)(((uint64_t)(uint32_t)uni((int)(x >> 32)) << 32) | (uint32_t)uni((int)x));
+}
+
+// Owner of unit u among W wavefronts splitting U units: the largest w with
+// floor(U*w/W) <= u.
+__device__ __forceinline__ int owner_of(int64_t u, int64_t U, int64_t W) {
+  return (int)(((u + 1) * W - 1) / U);
+}
+
+// Register buffers of one 32-token step.  Lane (lr, kq) holds, for S^T subtile s
+// (keys 16s..16s+15 of the step), key 16s + lr's dims [64ks + 16kq, +16) (int4:
+// packed), dim 16dt + lr of the keys at feed positions [8kq, +8), and the key /
+// value scales of keys 16s + 4kq + 0..3.
+template <int D>
+struct Buf8 {
+  v4i k[2][D / 64];
+  v2i v[D / 16];
+  float4 sk[2], sv[2];
+};
+template <int D>
+struct Buf4 {
+  v2i k[2][D / 64];
+  int v[D / 16];
+  float4 sk[2], sv[2];
+};
+
+template <int D, int BLK, bool IS4>
+struct StepIO {
+  using Buf = typename std::conditional<IS4, Buf4<D>, Buf8<D>>::type;
+
+  // Cache policy of the record loads: non-temporal.  The cache is streamed once
+  // per step; allocating it would evict (and write back) whatever the preceding
+  // kernels left dirty in the last-level cache, halving the read rate.
+  static constexpr int kNT = 2;
+  // Step h (chunk h) of the record at byte `roff` of the run's buffer resource
+  // (roff and h wave-uniform).  A chunk holds the K codes in operand order (unit
+  // (s, ks, kq, lr) = lane lr + 16kq of MFMA (s, ks)), the V codes as units (dt,
+  // kq, lr), then the K and V scales of its 32 tokens: every load below reads a
+  // contiguous run with lane l at offset l * size.
+  __device__ __forceinline__ static void load(Buf& r, __amdgpu_buffer_rsrc_t rs, int roff, int h, int lr, int kq) {
+    constexpr int KS = D / 64, ND = D / 16;
+    constexpr int KU = IS4 ? 8 : 16, VU = IS4 ? 4 : 8;  // bytes per lane of a K / V load
+    constexpr int KPART = 64 * KU * 2 * KS;              // = 32 * D (int4: 16 * D)
+    constexpr int CB = 2 * KPART + 256;
+    const int co = roff + h * CB;
+    const int lane = lr + 16 * kq;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (IS4)
+          r.k[s][ks] = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * KU + (s * KS + ks) * 64 * KU, co, kNT);
+        else
+          r.k[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * KU + (s * KS + ks) * 64 * KU, co, kNT);
+      }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      if constexpr (IS4)
+        r.v[dt] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * VU + KPART + dt * 64 * VU, co, kNT);
+      else
+        r.v[dt] = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * VU + KPART + dt * 64 * VU, co, kNT);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      r.sk[s] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, kq * 16 + 2 * KPART + 64 * s, co, kNT));
+      r.sv[s] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, kq * 16 + 2 * KPART + 128 + 64 * s, co, kNT));
+    }
+  }
+};
+
+template <int D, int RG>
+struct SegState {
+  float m[RG], l[RG];
+  v4f O[RG][D / 16];
+};
+
+// Maximum / sum over lanes l and l ^ 16, l ^ 32 (gfx950 lane-swap instructions:
+// VALU, no LDS round trip).
+__device__ __forceinline__ float xmax16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One 32-token step: scores, online softmax, O^T += V^T . P'^T.  mask_from = the
+// step's first key index at or past which keys are masked (>= 32: none).
+// With u = S * sk, t = u * a (a > 0 per query row), so the maximum is taken over u
+// and a enters the exponent: p = 2^(u * a - m).
+template <int D, int RG, bool IS4>
+__device__ __forceinline__ void compute_step(const typename std::conditional<IS4, Buf4<D>, Buf8<D>>::type& r,
+                                             const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_from,
+                                             SegState<D, RG>& st, int kq) {
   constexpr int KS = D / 64, ND = D / 16;
-  constexpr int ROWS = 16 * RG;
-  __shared__ int pfx[kMaxPairs + 1];
-  __shared__ __attribute__((aligned(16))) float mrg[ROWS][D + 4];
+  float u[RG][2][4];
+  float mt[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      v4i S = {0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        v4i kop;
+        if constexpr (IS4) {
+          const v2i w = r.k[s][ks];
+          kop = unpack16_x16((uint32_t)w[0], (uint32_t)w[1]);
+        } else {
+          kop = r.k[s][ks];
+        }
+        S = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[rg][ks], S, 0, 0, 0);
+      }
+      const float kv[4] = {r.sk[s].x, r.sk[s].y, r.sk[s].z, r.sk[s].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[rg][s][i] = (float)S[i] * kv[i];
+    }
+  }
+  if (mask_from < 32) {  // only the current block's tail (wave-uniform branch)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * s + 4 * kq + i >= mask_from) u[rg][s][i] = -INFINITY;
+  }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    float x = fmaxf(fmaxf(u[rg][0][0], u[rg][0][1]), fmaxf(u[rg][0][2], u[rg][0][3]));
+    x = fmaxf(x, fmaxf(fmaxf(u[rg][1][0], u[rg][1][1]), fmaxf(u[rg][1][2], u[rg][1][3])));
+    mt[rg] = xmax32(xmax16(x)) * ar[rg];  // -inf when the whole step is masked
+  }
+  bool need = false;
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) need = need || (mt[rg] > st.m[rg]);
+  if (__ballot(need)) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const float mn = fmaxf(st.m[rg], mt[rg]);
+      const float f = __builtin_amdgcn_exp2f(st.m[rg] - mn);  // 0 while m was -inf
+      st.m[rg] = mn;
+      st.l[rg] *= f;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) st.O[rg][d] *= f;
+    }
+  }
+  // weights p = 2^(u a - m); p' = p * sv split into a bf16 high part (truncated)
+  // and the bf16 of the exact remainder
+  v8bf bhi[RG], blo[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    // m is -inf only while every key seen so far was masked (then u is too)
+    const float nm = st.m[rg] == -INFINITY ? 0.0f : -st.m[rg];
+    v4i hw;
+    v2bf lw[4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float vv[4] = {r.sv[s].x, r.sv[s].y, r.sv[s].z, r.sv[s].w};
+      float pw[4], lo[4];
+      uint32_t hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(u[rg][s][i], ar[rg], nm));
+        st.l[rg] += p;
+        pw[i] = p * (IS4 ? vv[i] * (1.0f / 16.0f) : vv[i]);
+        hb[i] = __float_as_uint(pw[i]) & 0xFFFF0000u;
+        lo[i] = pw[i] - __uint_as_float(hb[i]);
+      }
+      hw[2 * s] = (int)__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
+      hw[2 * s + 1] = (int)__builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
+      lw[2 * s] = __builtin_convertvector((v2f{lo[0], lo[1]}), v2bf);
+      lw[2 * s + 1] = __builtin_convertvector((v2f{lo[2], lo[3]}), v2bf);
+    }
+    bhi[rg] = __builtin_bit_cast(v8bf, hw);
+    blo[rg] = __builtin_bit_cast(v8bf, __builtin_shufflevector(__builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3),
+                                                               __builtin_shufflevector(lw[2], lw[3], 0, 1, 2, 3),
+                                                               0, 1, 2, 3, 4, 5, 6, 7));
+  }
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    v2i w;
+    if constexpr (IS4)
+      w = nib8_ordered_x16((uint32_t)r.v[dt]);
+    else
+      w = r.v[dt];
+    const v8bf vop = i8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      st.O[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, bhi[rg], st.O[rg][dt], 0, 0, 0);
+      st.O[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo[rg], st.O[rg][dt], 0, 0, 0);
+    }
+  }
+}
+
+// Steps [j0, j1) of one precision run of a pair; rec0 = the run's first record.
+// The next step's loads are issued before the current step is computed; `pre` runs
+// once the first step's loads are in flight (the segment's query quantisation).
+template <int D, int BLK, int RG, bool IS4, class Pre>
+__device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes, int j0, int j1,
+                                          const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_jb,
+                                          int mask_first, SegState<D, RG>& st, int lr, int kq, Pre&& pre) {
+  using IO = StepIO<D, BLK, IS4>;
+  constexpr int SPB = BLK / 32;
+  if (j0 >= j1) return;
+  j0 = uni(j0);
+  j1 = uni(j1);
+  const int rb = uni((int)rec_bytes);
+  // the run's records as one buffer resource (dword 3: raw 32-bit data format)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(rec0))), (short)0, uni((j1 + SPB - 1) / SPB * rb), 0x00020000);
+  typename IO::Buf A, B;
+  auto ld = [&](typename IO::Buf& r, int j) __attribute__((always_inline)) {
+    IO::load(r, rs, (j / SPB) * rb, j % SPB, lr, kq);
+  };
+  // keys of step j at or past which keys are masked: only the current block's
+  // tail (ctx_len is inside block mask_jb of this run) is masked
+  auto mfrom = [&](int j) __attribute__((always_inline)) -> int {
+    return j / SPB == mask_jb ? mask_first - 32 * (j % SPB) : 1 << 30;
+  };
+  ld(A, j0);
+  pre();
+  for (int j = j0; j < j1; j += 2) {
+    ld(B, j + 1 < j1 ? j + 1 : j);  // past the end: reloads the current step (cached)
+    compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq);
+    if (j + 1 >= j1) break;
+    ld(A, j + 2 < j1 ? j + 2 : j + 1);
+    compute_step<D, RG, IS4>(B, qop, ar, mfrom(j + 1), st, kq);
+  }
+}
+
+// In-place exclusive prefix of arr[0..P), arr[P] = total (chunks of the group size).
+__device__ __forceinline__ void prefix_lds(int* arr, int P, int* tmp) {
+  int carry = 0;
+  for (int base = 0; base < P; base += kThreads) {
+    const int p = base + (int)threadIdx.x;
+    const int x = p < P ? arr[p] : 0;
+    int tot;
+    const int e = block_scan(x, tmp, tot);
+    if (p < P) arr[p] = carry + e;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) arr[P] = carry;
+  __syncthreads();
+}
+
+template <int D, int BLK, int RG>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RG == 1 ? 2 : 1, 2)))
+decode_split_kernel(DecArgs a) {
+  constexpr int KS = D / 64, ND = D / 16, SPB = BLK / 32;
+  __shared__ int n8p[kMaxPairs + 1];  // int8 records per pair, then their exclusive prefix
+  __shared__ int n4p[kMaxPairs + 1];  // int4 records per pair, then their exclusive prefix
+  __shared__ int slp[kMaxPairs + 1];  // partial slots per pair, then their exclusive prefix
+  __shared__ int tmp[kWaves];
   __shared__ int bad;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -149,315 +408,218 @@ __global__ void __launch_bounds__(kThreads) decode_split_kernel(DecArgs a) {
     if (blockIdx.x == 0 && tid == 0) reinterpret_cast<int*>(a.ws)[0] = 0;
     return;
   }
-  // ---- item prefix over the directory (validated), computed by wave 0
   if (tid == 0) bad = 0;
   __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 0; base < P; base += 64) {
-      const int p = base + lane;
-      int cnt = 0;
-      if (p < P) {
-        const Entry e = read_entry(a.cache, p);
-        if (!entry_ok<D, BLK>(e, geo)) bad = 1;
-        else cnt = items_of<BLK>(e);
-      }
-      int incl = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      if (p < P) pfx[p + 1] = carry + incl;
-      carry += __shfl(incl, 63);
-    }
-    if (lane == 0) pfx[0] = 0;
+  // ---- directory: record counts per pair, checked
+  for (int p = tid; p < P; p += kThreads) {
+    const int32_t* e = reinterpret_cast<const int32_t*>(a.cache + 64 + 64 * (int64_t)p);
+    const int n8 = e[2], n4 = e[3], lo8 = e[6], sink = e[7], lo4 = e[8];
+    // the int8 run ends at the current block; int4 records lie below it
+    const bool ok = n8 >= 1 && n4 >= 0 && n8 + n4 <= geo.cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
+                    lo8 + (n8 - sink) - 1 == geo.cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 &&
+                    lo4 + n4 <= geo.cur + 1;
+    if (!ok) bad = 1;
+    n8p[p] = ok ? n8 : 0;
+    n4p[p] = ok ? n4 : 0;
   }
   __syncthreads();
-  const int total = pfx[P];
-  if (bad || total > a.max_items) {
+  prefix_lds(n8p, P, tmp);
+  prefix_lds(n4p, P, tmp);
+  // ---- the split: U units, W wavefronts, W <= U / 2 so that every wavefront's
+  // range (>= 2 units) holds at least one step start
+  auto units_at = [&](int p) -> int64_t { return (int64_t)SPB * (2 * (int64_t)n8p[p] + n4p[p]); };
+  const int64_t U = uni64(units_at(P));
+  const int64_t W = (int64_t)gridDim.x * kWaves < U / 2 ? (int64_t)gridDim.x * kWaves : U / 2;
+  // records are contiguous in (b, g) order; pair p gets one partial slot per
+  // wavefront owning one of its steps
+  for (int p = tid; p < P; p += kThreads) {
+    const int64_t off = *reinterpret_cast<const int64_t*>(a.cache + 64 + 64 * (int64_t)p);
+    if (off != geo.data_offset + (int64_t)n8p[p] * geo.rec8 + (int64_t)n4p[p] * geo.rec4) bad = 1;
+    const int64_t u0 = units_at(p), u1 = units_at(p + 1);
+    const int64_t last = n4p[p + 1] > n4p[p] ? u1 - 1 : u1 - 2;  // start of the pair's last step
+    slp[p] = U >= 4 ? owner_of(last, U, W) - owner_of(u0, U, W) + 1 : 0;
+  }
+  __syncthreads();
+  if (bad || U < 4 || geo.data_offset + (int64_t)n8p[P] * geo.rec8 + (int64_t)n4p[P] * geo.rec4 > geo.total) {
     if (blockIdx.x == 0 && tid == 0) reinterpret_cast<int*>(a.ws)[0] = 0;
     return;
   }
-  if (blockIdx.x == 0 && tid == 0) {
+  prefix_lds(slp, P, tmp);
+  if (blockIdx.x == 0) {
     int* wsh = reinterpret_cast<int*>(a.ws);
-    wsh[0] = 1;
-    wsh[1] = P;
-    wsh[2] = total;
+    if (tid == 0) {
+      wsh[0] = 1;
+      wsh[1] = P;
+      wsh[2] = slp[P];
+      wsh[3] = (int)W;
+    }
+    for (int p = tid; p <= P; p += kThreads) wsh[16 + p] = slp[p];
   }
-  if (blockIdx.x == 0)
-    for (int p = tid; p <= P; p += kThreads) reinterpret_cast<int*>(a.ws)[16 + p] = pfx[p];
   float* part = a.ws + ws_part_offset(P) / 4;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // pair of this item: largest p with pfx[p] <= item
-    int lo = 0, hi = P - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pfx[mid] <= item) lo = mid;
-      else hi = mid - 1;
+  // ---- this wavefront's steps
+  const int64_t w = (int64_t)blockIdx.x * kWaves + uni(wave);
+  if (w >= W) return;
+  const int64_t lo = U * w / W, hi = U * (w + 1) / W;
+  // the pair holding unit lo
+  int p;
+  {
+    int l0 = 0, h0 = P - 1;
+    while (l0 < h0) {
+      const int mid = (l0 + h0 + 1) >> 1;
+      if (units_at(mid) <= lo) l0 = mid;
+      else h0 = mid - 1;
     }
-    const int pair = lo;
-    const int ii = item - pfx[pair];
-    const Entry e = read_entry(a.cache, pair);
-    const int groups = (e.n8 + e.n4) * (BLK / 64);
-    const int g_begin = ii * kGroupsPerItem;
-    const int g_end = min(groups, g_begin + kGroupsPerItem);
-    const int b = pair / a.hkv, gkv = pair % a.hkv;
+    p = uni(l0);
+  }
+  for (; p < P && uni64(units_at(p)) < hi; ++p) {
+    const int64_t u0 = uni64(units_at(p));
+    const int n8 = uni(n8p[p + 1] - n8p[p]), n4 = uni(n4p[p + 1] - n4p[p]);
+    const int s8 = n8 * SPB, s4 = n4 * SPB;
+    // owned int8 steps: start u0 + 2j in [lo, hi); int4 steps: u0 + 2*s8 + j
+    auto ceil2 = [](int64_t x) -> int64_t { return x <= 0 ? 0 : (x + 1) >> 1; };
+    auto clampn = [](int64_t x, int n) -> int { return x <= 0 ? 0 : (x >= n ? n : (int)x); };
+    const int j8a = clampn(ceil2(lo - u0), s8), j8b = clampn(ceil2(hi - u0), s8);
+    const int64_t base4 = u0 + 2LL * s8;
+    const int j4a = clampn(lo - base4, s4), j4b = clampn(hi - base4, s4);
+    if (j8a >= j8b && j4a >= j4b) continue;
+    const int slot = uni(slp[p]) + (int)(w - owner_of(u0, U, W));
+    const int b = p / a.hkv, gkv = p % a.hkv;
+    const uint8_t* rec0 =
+        a.cache + geo.data_offset + (int64_t)uni(n8p[p]) * geo.rec8 + (int64_t)uni(n4p[p]) * geo.rec4;
 
-    // ---- quantise this pair's G query rows (int8 + int4 codes as MFMA B operands)
+    // this pair's G query rows, quantised at both precisions (MFMA B operands)
     v4i q8op[RG][KS], q4op[RG][KS];
     float a8[RG], a4[RG];
+    auto quantise_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const int row = rg * 16 + lr;
+        const bool valid = row < G;
+        float x[KS][2][8];
+        float amax = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            if (valid)
+              raw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + gkv * G + row) * D + ks * 64 +
+                                                    kq * 16 + hh * 8);
+            bf16x8_to_f32(raw, x[ks][hh]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ks][hh][i]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        float sc8 = 0.f, sc4 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          uint32_t c8a[2], c8b[2], c4a, c4b;
+          codes_from_amax(x[ks][0], amax, c8a, c4a, sc8, sc4);
+          codes_from_amax(x[ks][1], amax, c8b, c4b, sc8, sc4);
+          q8op[rg][ks] = v4i{(int)c8a[0], (int)c8a[1], (int)c8b[0], (int)c8b[1]};
+          q4op[rg][ks] = unpack16_x16(c4a, c4b);
+        }
+        a8[rg] = fmaxf(sc8 * a.c, FLT_MIN);
+        a4[rg] = fmaxf(sc4 * a.c * (1.0f / 256.0f), FLT_MIN);
+      }
+    };
+
+    SegState<D, RG> st;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
+      st.m[rg] = -INFINITY;
+      st.l[rg] = 0.0f;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) st.O[rg][d] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    // the last int8 record is the current block; keys at or past ctx_len are masked
+    const int mask_first = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
+    const bool has8 = j8a < j8b;
+    run_steps<D, BLK, RG, false>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq, quantise_q);
+    run_steps<D, BLK, RG, true>(rec0 + (int64_t)n8 * geo.rec8, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq,
+                                [&]() __attribute__((always_inline)) {
+                                  if (!has8) quantise_q();
+                                });
+
+    // ---- the wavefront's partial for this pair
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      const float l = xsum32(xsum16(st.l[rg]));
       const int row = rg * 16 + lr;
-      const bool valid = row < G;
-      float x[KS][2][8];
-      float amax = 0.0f;
+      if (row < G) {
+        float* dst = part + ((int64_t)slot * G + row) * (D + 4);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint4 raw = make_uint4(0, 0, 0, 0);
-          if (valid)
-            raw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + gkv * G + row) * D + ks * 64 +
-                                                  kq * 16 + hh * 8);
-          bf16x8_to_f32(raw, x[ks][hh]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ks][hh][i]));
-        }
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      float s8 = 0.f, s4 = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint32_t c8a[2], c8b[2], c4a, c4b;
-        codes_from_amax(x[ks][0], amax, c8a, c4a, s8, s4);
-        codes_from_amax(x[ks][1], amax, c8b, c4b, s8, s4);
-        q8op[rg][ks] = v4i{(int)c8a[0], (int)c8a[1], (int)c8b[0], (int)c8b[1]};
-        q4op[rg][ks] = unpack16_x16(c4a, c4b);
-      }
-      a8[rg] = fmaxf(s8 * a.c, FLT_MIN);
-      a4[rg] = fmaxf(s4 * a.c * (1.0f / 256.0f), FLT_MIN);
-    }
-
-    float m[RG], l[RG];
-    v4f O[RG][ND];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      m[rg] = -INFINITY;
-      l[rg] = 0.0f;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) O[rg][d] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-
-    for (int gi = g_begin + wave; gi < g_end; gi += kWaves) {
-      const int jblk = gi / (BLK / 64), sub = gi % (BLK / 64);
-      const bool is4 = jblk >= e.n8;
-      const int kb = !is4 ? ((e.sink && jblk == 0) ? 0 : e.lo8 + jblk - e.sink) : e.lo4 + (jblk - e.n8);
-      const uint8_t* rec = a.cache + e.off +
-                           (!is4 ? (int64_t)jblk * geo.rec8
-                                 : (int64_t)e.n8 * geo.rec8 + (int64_t)(jblk - e.n8) * geo.rec4);
-      const int kbytes = is4 ? BLK * D / 2 : BLK * D;
-      const float* sk = reinterpret_cast<const float*>(rec + 2 * kbytes) + sub * 64;
-      const float* sv = sk + BLK;
-
-      // ---- loads: K codes (A operands), V^T codes, key and value scales
-      v4i kop[4][KS];
-      uint4 vraw[ND];
-      float4 skv[4], svv[4];
-      if (!is4) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            kop[s][ks] = *reinterpret_cast<const v4i*>(rec + (int64_t)(sub * 64 + 16 * s + lr) * D + ks * 64 + kq * 16);
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-          vraw[d] = *reinterpret_cast<const uint4*>(rec + kbytes + (int64_t)(d * 16 + lr) * BLK + sub * 64 + 16 * kq);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const uint2 p = *reinterpret_cast<const uint2*>(rec + (int64_t)(sub * 64 + 16 * s + lr) * (D / 2) + ks * 32 + kq * 8);
-            kop[s][ks] = unpack16_x16(p.x, p.y);
-          }
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const uint2 p = *reinterpret_cast<const uint2*>(rec + kbytes + (int64_t)(d * 16 + lr) * (BLK / 2) + (sub * 64 + 16 * kq) / 2);
-          const v2i lo = nib8_ordered_x16(p.x), hi = nib8_ordered_x16(p.y);
-          vraw[d] = make_uint4((uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)hi[0], (uint32_t)hi[1]);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        skv[s] = *reinterpret_cast<const float4*>(sk + 16 * s + 4 * kq);
-        svv[s] = *reinterpret_cast<const float4*>(sv + 16 * s + 4 * kq);
-      }
-
-      // ---- scores (S^T: lane = query row, 4 keys per 16-key subtile)
-      float t[RG][4][4];
-      float mt[RG];
-      const int64_t tok0 = (int64_t)kb * BLK + sub * 64;
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        mt[rg] = -INFINITY;
-        const float ar = is4 ? a4[rg] : a8[rg];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          v4i S = {0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            S = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[s][ks], is4 ? q4op[rg][ks] : q8op[rg][ks], S, 0, 0, 0);
-          const float kv[4] = {skv[s].x, skv[s].y, skv[s].z, skv[s].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = (float)S[i] * kv[i] * ar;
-            if (tok0 + 16 * s + 4 * kq + i >= a.ctx_len) x = -INFINITY;
-            t[rg][s][i] = x;
-            mt[rg] = fmaxf(mt[rg], x);
-          }
-        }
-        mt[rg] = fmaxf(mt[rg], __shfl_xor(mt[rg], 16));
-        mt[rg] = fmaxf(mt[rg], __shfl_xor(mt[rg], 32));
-      }
-      bool need = false;
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) need = need || (mt[rg] > m[rg]);
-      if (__ballot(need)) {
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          const float mn = fmaxf(m[rg], mt[rg]);
-          const float f = exp2f(m[rg] - mn);
-          m[rg] = mn;
-          l[rg] *= f;
-#pragma unroll
-          for (int d = 0; d < ND; ++d) O[rg][d] *= f;
-        }
-      }
-      // ---- weights: p = 2^(t - m); p' = p * sv split into bf16 hi + lo
-      v8bf bhi[RG][2], blo[RG][2];
-      const float vscale = is4 ? (1.0f / 16.0f) : 1.0f;
-#pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float vv[4] = {svv[s].x, svv[s].y, svv[s].z, svv[s].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // m is -inf only while every key seen so far was masked (then t is too)
-            const float p = exp2f(t[rg][s][i] - (m[rg] == -INFINITY ? 0.0f : m[rg]));
-            l[rg] += p;
-            const float pw = p * vv[i] * vscale;
-            const __bf16 h = (__bf16)pw;
-            const __bf16 r = (__bf16)(pw - (float)h);
-            bhi[rg][s >> 1][4 * (s & 1) + i] = h;
-            blo[rg][s >> 1][4 * (s & 1) + i] = r;
-          }
-        }
-      }
-      // ---- O^T += V^T . P'^T
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const v8bf vop = t2 == 0 ? i8x8_to_bf16(vraw[d].x, vraw[d].y) : i8x8_to_bf16(vraw[d].z, vraw[d].w);
-#pragma unroll
-          for (int rg = 0; rg < RG; ++rg) {
-            O[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, bhi[rg][t2], O[rg][d], 0, 0, 0);
-            O[rg][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo[rg][t2], O[rg][d], 0, 0, 0);
-          }
-        }
+        for (int dt = 0; dt < ND; ++dt)
+          *reinterpret_cast<float4*>(dst + dt * 16 + kq * 4) =
+              make_float4(st.O[rg][dt][0], st.O[rg][dt][1], st.O[rg][dt][2], st.O[rg][dt][3]);
+        if (kq == 0) *reinterpret_cast<float4*>(dst + D) = make_float4(st.m[rg], l, 0.0f, 0.0f);
       }
     }
-
-    // ---- merge the waves' partials in LDS (sequentially: deterministic)
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      l[rg] += __shfl_xor(l[rg], 16);
-      l[rg] += __shfl_xor(l[rg], 32);
-    }
-    for (int w = 0; w < kWaves; ++w) {
-      __syncthreads();
-      if (wave == w) {
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          const int row = rg * 16 + lr;
-          float* dst = &mrg[row][0];
-          if (w == 0) {
-#pragma unroll
-            for (int d = 0; d < ND; ++d) *reinterpret_cast<float4*>(dst + d * 16 + kq * 4) = make_float4(O[rg][d][0], O[rg][d][1], O[rg][d][2], O[rg][d][3]);
-            if (kq == 0) {
-              dst[D] = m[rg];
-              dst[D + 1] = l[rg];
-            }
-          } else {
-            const float m0 = dst[D], l0 = dst[D + 1];
-            const float mn = fmaxf(m0, m[rg]);
-            const float f0 = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - mn);
-            const float f1 = (m[rg] == -INFINITY) ? 0.0f : exp2f(m[rg] - mn);
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-              float4 o = *reinterpret_cast<float4*>(dst + d * 16 + kq * 4);
-              o.x = o.x * f0 + O[rg][d][0] * f1;
-              o.y = o.y * f0 + O[rg][d][1] * f1;
-              o.z = o.z * f0 + O[rg][d][2] * f1;
-              o.w = o.w * f0 + O[rg][d][3] * f1;
-              *reinterpret_cast<float4*>(dst + d * 16 + kq * 4) = o;
-            }
-            // all four lanes of the row have read m0/l0 before lane kq==0 writes
-            __builtin_amdgcn_wave_barrier();
-            if (kq == 0) {
-              dst[D] = mn;
-              dst[D + 1] = l0 * f0 + l[rg] * f1;
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // ---- write the item's partials for the G valid rows
-    float* dstp = part + (int64_t)item * G * (D + 4);
-    for (int i = tid; i < G * (D + 4); i += kThreads) {
-      const int row = i / (D + 4), col = i % (D + 4);
-      dstp[i] = col < D + 2 ? mrg[row][col] : 0.0f;
-    }
-    __syncthreads();  // mrg is reused by the next item
   }
 }
 
-// Merge of the items of each pair: one work group per (batch, query head).
+// Merge of the partials of each pair: one work group per (batch, query head), one
+// thread per output column; a pair's partials are read in parallel.
 template <int D>
 __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
-  const int bh = blockIdx.x;
+  constexpr int NW = D / 64;
+  __shared__ float fs[D];
+  __shared__ float red[NW];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.hq / a.hkv;
   const int pair = b * a.hkv + h / G, row = h % G;
   const int* wsh = reinterpret_cast<const int*>(a.ws);
   float* dst = a.out + (int64_t)bh * D;
   if (wsh[0] != 1 || wsh[1] != a.batch * a.hkv) {
-    dst[threadIdx.x] = __int_as_float(0x7FC00000);  // NaN: the cache did not validate
+    dst[t] = __int_as_float(0x7FC00000);  // NaN: the cache did not validate
     return;
   }
   const int P = wsh[1];
   const int i0 = wsh[16 + pair], i1 = wsh[16 + pair + 1];
   const float* part = a.ws + ws_part_offset(P) / 4;
+  auto rowp = [&](int it) { return part + ((int64_t)it * G + row) * (D + 4); };
+  // maximum of the partials' m
   float mx = -INFINITY;
-  for (int it = i0; it < i1; ++it) mx = fmaxf(mx, part[((int64_t)it * G + row) * (D + 4) + D]);
+  for (int it = i0 + t; it < i1; it += D) mx = fmaxf(mx, rowp(it)[D]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
   float l = 0.0f, o = 0.0f;
-  for (int it = i0; it < i1; ++it) {
-    const float* p = part + ((int64_t)it * G + row) * (D + 4);
-    const float f = p[D] == -INFINITY ? 0.0f : exp2f(p[D] - mx);
-    l += p[D + 1] * f;
-    o += p[threadIdx.x] * f;
+  for (int base = i0; base < i1; base += D) {
+    const int n = i1 - base < D ? i1 - base : D;
+    if (t < n) {
+      const float* pp = rowp(base + t);
+      const float m = pp[D];
+      const float f = m == -INFINITY ? 0.0f : exp2f(m - mx);
+      fs[t] = f;
+      l += pp[D + 1] * f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) o += fs[j] * rowp(base + j)[t];
+    __syncthreads();
   }
-  dst[threadIdx.x] = o / l;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) l += __shfl_xor(l, s);
+  if (lane == 0) red[wv] = l;
+  __syncthreads();
+  l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) l += red[w];
+  dst[t] = o / l;
 }
 
 template <int D, int BLK, int RG>
-hipError_t launch_t(const DecArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, BLK, RG>), dim3(grid), dim3(kThreads), 0, stream, a);
+hipError_t launch_t(const DecArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, BLK, RG>), dim3(kGrid), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.hq), dim3(D), 0, stream, a);
@@ -466,16 +628,16 @@ hipError_t launch_t(const DecArgs& a, int grid, hipStream_t stream) {
 
 }  // namespace
 
-int64_t decode_max_items(const Shape& s, int64_t ctx_len) {
-  const int64_t nb = (ctx_len - 1) / s.blk + 1;
-  const int64_t groups = nb * (s.blk / 64);
-  return (int64_t)s.batch * s.hkv * ((groups + kGroupsPerItem - 1) / kGroupsPerItem);
-}
-
 int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len) {
+  (void)ctx_len;  // the split is by wavefront: at most one partial per wavefront and pair boundary
   const int64_t pairs = (int64_t)s.batch * s.hkv;
   const int G = s.hq / s.hkv;
-  return ws_part_offset(pairs) + decode_max_items(s, ctx_len) * G * (s.d + 4) * 4;
+  return ws_part_offset(pairs) + (kMaxWaves + pairs) * G * (s.d + 4) * 4;
+}
+
+bool decode_units_fit(const Shape& s, int64_t ctx_len) {
+  const int64_t nb = (ctx_len - 1) / s.blk + 1;
+  return (int64_t)s.batch * s.hkv * nb * (s.blk / 32) * 2 < (1LL << 31);
 }
 
 hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
@@ -487,18 +649,16 @@ hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int
   a.out = out;
   a.cache_bytes = cache_bytes;
   a.ctx_len = ctx_len;
-  a.max_items = decode_max_items(s, ctx_len);
   a.batch = s.batch;
   a.hq = s.hq;
   a.hkv = s.hkv;
   a.c = sm_scale * 1.44269504088896340736f;
-  const int grid = (int)(a.max_items < kMaxGrid ? a.max_items : kMaxGrid);
   const int G = s.hq / s.hkv;
   const bool two = G > 16;
-  if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2>(a, grid, stream) : launch_t<128, 128, 1>(a, grid, stream);
-  if (s.d == 128 && s.blk == 64) return two ? launch_t<128, 64, 2>(a, grid, stream) : launch_t<128, 64, 1>(a, grid, stream);
-  if (s.d == 64 && s.blk == 128) return two ? launch_t<64, 128, 2>(a, grid, stream) : launch_t<64, 128, 1>(a, grid, stream);
-  return two ? launch_t<64, 64, 2>(a, grid, stream) : launch_t<64, 64, 1>(a, grid, stream);
+  if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2>(a, stream) : launch_t<128, 128, 1>(a, stream);
+  if (s.d == 128 && s.blk == 64) return two ? launch_t<128, 64, 2>(a, stream) : launch_t<128, 64, 1>(a, stream);
+  if (s.d == 64 && s.blk == 128) return two ? launch_t<64, 128, 2>(a, stream) : launch_t<64, 128, 1>(a, stream);
+  return two ? launch_t<64, 64, 2>(a, stream) : launch_t<64, 64, 1>(a, stream);
 }
 
 }  // namespace tria

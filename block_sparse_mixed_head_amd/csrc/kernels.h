@@ -43,7 +43,8 @@ hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& g, 
                        const void* v, void* cache, hipStream_t stream);
 
 // Decode: split-KV partials into `workspace`, then a merge into `out`.
-int64_t decode_max_items(const Shape& s, int64_t ctx_len);
+// decode_units_fit: the work split counts 32-token units in int32.
+bool decode_units_fit(const Shape& s, int64_t ctx_len);
 int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len);
 hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
                          const void* q, float sm_scale, float* out, void* workspace, hipStream_t stream);

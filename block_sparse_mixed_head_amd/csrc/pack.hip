@@ -10,11 +10,11 @@
 // precision (same contract as the Q/K quantiser).
 //
 // Layout (bytes, documented in tria.h): header, one 64-byte directory entry per
-// (batch, KV head), then per pair its int8 records and its int4 records:
-//   K codes [B][d] | V codes [d][B] in feed order | K scales [B] | V scales [B]
-// V is stored transposed, with the tokens of each 64-token group permuted into the
-// order the decode kernel's bf16 MFMA consumes them, so a decode lane reads one
-// contiguous 16-byte run per output column.
+// (batch, KV head), then per pair its int8 records and its int4 records.  A record
+// is B/32 chunks of 32 tokens, each self-contained: the K codes in the order of the
+// decode kernel's matrix operand, the V codes transposed with the tokens in the
+// order its bf16 MFMA consumes them, then the chunk's K and V scales.  One decode
+// step reads one chunk as a single contiguous run, each load lane-contiguous.
 //
 // One work group per stored block (grid x = block slot in the pair, y = pair); each
 // group computes its record offset from the policy (every batch element has the
@@ -58,17 +58,27 @@ __device__ __forceinline__ Blocks stored_blocks(int c, int hi, int keep) {
   return s;
 }
 
-// token held at position p of a 64-token group in the transposed V layout
-__device__ __forceinline__ int feed_token(int p) {
-  const int q = p >> 4, s = (p >> 3) & 1, pp = p & 7;
-  return 32 * s + 16 * (pp >> 2) + 4 * q + (pp & 3);
+// token held at position 8q + p of a 32-token chunk in the transposed V layout
+__device__ __forceinline__ int feed_token(int q, int p) { return 16 * (p >> 2) + 4 * q + (p & 3); }
+
+// 8 sign-extended int4 codes (bytes) -> 4 packed bytes, low nibble = even element
+__device__ __forceinline__ uint32_t pack8_nibbles(uint32_t lo, uint32_t hi) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t e = ((i < 2 ? lo : hi) >> (16 * (i & 1))) & 0xFFFFu;  // elements 2i, 2i+1
+    r |= ((e & 0xFu) | (((e >> 8) & 0xFu) << 4)) << (8 * i);
+  }
+  return r;
 }
 
 template <int D, int BLK>
 __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   constexpr int TPR = D / 8;
   constexpr int RPP = kThreads / TPR;  // rows per pass
+  __shared__ __attribute__((aligned(16))) int8_t kbuf[BLK][D];  // codes (int4: sign-extended bytes)
   __shared__ __attribute__((aligned(16))) int8_t vbuf[BLK][D];
+  __shared__ float ksb[BLK], vsb[BLK];
 
   const int pair = blockIdx.y, j = blockIdx.x;
   const int b = pair / a.hkv, g = pair % a.hkv;
@@ -85,8 +95,6 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   const int64_t off = !is4 ? pair_off + (int64_t)j * a.geo.rec8_bytes
                            : pair_off + (int64_t)st.n8 * a.geo.rec8_bytes + (int64_t)(j - st.n8) * a.geo.rec4_bytes;
   uint8_t* rec = a.cache + off;
-  constexpr int KB8 = BLK * D, KB4 = BLK * D / 2;
-  const int kbytes = is4 ? KB4 : KB8;
   const int tid = threadIdx.x;
 
   if (j == 0 && tid == 0) {
@@ -104,7 +112,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     if (pair == 0) {
       int32_t* hd = reinterpret_cast<int32_t*>(a.cache);
       hd[0] = 0x43564B54;  // "TKVC"
-      hd[1] = 1;
+      hd[1] = 2;  // format version
       hd[2] = a.batch;
       hd[3] = a.hkv;
       hd[4] = D;
@@ -126,8 +134,16 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
 
   const int64_t src0 = ((int64_t)b * a.hkv + g) * a.n;
   const int part = tid % TPR;
-  float* ks_out = reinterpret_cast<float*>(rec + 2 * kbytes);
-  float* vs_out = ks_out + BLK;
+  // int4 codes as sign-extended bytes
+  auto widen4 = [](uint32_t w, uint32_t& e0, uint32_t& e1) {
+    e0 = e1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int code = ((int)(w << (28 - 4 * i))) >> 28;
+      if (i < 4) e0 |= ((uint32_t)code & 0xFFu) << (8 * i);
+      else e1 |= ((uint32_t)code & 0xFFu) << (8 * (i - 4));
+    }
+  };
 #pragma unroll 1
   for (int p = 0; p < BLK / RPP; ++p) {
     const int r = p * RPP + tid / TPR;
@@ -146,53 +162,78 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     quantize8<TPR>(xk, k8w, k4w, ks8, ks4);
     quantize8<TPR>(xv, v8w, v4w, vs8, vs4);
     if (!is4) {
-      *reinterpret_cast<uint2*>(rec + r * D + part * 8) = make_uint2(k8w[0], k8w[1]);
+      *reinterpret_cast<uint2*>(&kbuf[r][part * 8]) = make_uint2(k8w[0], k8w[1]);
       *reinterpret_cast<uint2*>(&vbuf[r][part * 8]) = make_uint2(v8w[0], v8w[1]);
     } else {
-      *reinterpret_cast<uint32_t*>(rec + r * (D / 2) + part * 4) = k4w;
-      uint32_t e0 = 0, e1 = 0;  // int4 codes as sign-extended bytes
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int code = ((int)(v4w << (28 - 4 * i))) >> 28;
-        if (i < 4) e0 |= ((uint32_t)code & 0xFFu) << (8 * i);
-        else e1 |= ((uint32_t)code & 0xFFu) << (8 * (i - 4));
-      }
+      uint32_t e0, e1;
+      widen4(k4w, e0, e1);
+      *reinterpret_cast<uint2*>(&kbuf[r][part * 8]) = make_uint2(e0, e1);
+      widen4(v4w, e0, e1);
       *reinterpret_cast<uint2*>(&vbuf[r][part * 8]) = make_uint2(e0, e1);
     }
     if (part == 0) {
-      ks_out[r] = is4 ? ks4 : ks8;
-      vs_out[r] = is4 ? vs4 : vs8;
+      ksb[r] = is4 ? ks4 : ks8;
+      vsb[r] = is4 ? vs4 : vs8;
     }
   }
   __syncthreads();
-  // transposed V codes in feed order
-  uint8_t* vt = rec + kbytes;
-  if (!is4) {
-    constexpr int CPR = BLK / 16;  // 16-byte chunks per output row
-    for (int ch = tid; ch < D * CPR; ch += kThreads) {
-      const int d = ch / CPR, p0 = (ch % CPR) * 16;
-      uint32_t w[4] = {0, 0, 0, 0};
+  // the record, chunk by chunk, in 16-byte pieces
+  constexpr int KSL = D / 64;
+  const int kpart = is4 ? 16 * D : 32 * D;    // bytes of the K (and of the V) part of a chunk
+  const int cbytes = 2 * kpart + 256;
+  const int npieces = (BLK / 32) * cbytes / 16;
+  for (int pc = tid; pc < npieces; pc += kThreads) {
+    const int c = pc / (cbytes / 16), o = (pc % (cbytes / 16)) * 16;  // chunk, byte offset in it
+    uint32_t w[4];
+    if (o < kpart) {
+      // K: units of (s, ks, kq, lr) -> 16 dims 64ks + 16kq.. of token 32c + 16s + lr
+      const int usz = is4 ? 8 : 16;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int p = p0 + i;
-        const int tok = (p & ~63) + feed_token(p & 63);
-        w[i / 4] |= ((uint32_t)(uint8_t)vbuf[tok][d]) << (8 * (i % 4));
+      for (int h = 0; h < 2; ++h) {  // int4: two 8-byte units per piece
+        const int u = o / usz + h;
+        const int lr = u % 16, q = (u / 16) % 4, kk = (u / 64) % KSL, sub = u / (64 * KSL);
+        const int8_t* src = &kbuf[32 * c + 16 * sub + lr][64 * kk + 16 * q];
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        if (!is4) {
+          w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+          break;
+        }
+        w[2 * h] = pack8_nibbles(x.x, x.y);
+        w[2 * h + 1] = pack8_nibbles(x.z, x.w);
       }
-      *reinterpret_cast<uint4*>(vt + (int64_t)d * BLK + p0) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  } else {
-    constexpr int CPR = BLK / 32;  // 16-byte chunks (32 positions) per output row
-    for (int ch = tid; ch < D * CPR; ch += kThreads) {
-      const int d = ch / CPR, p0 = (ch % CPR) * 32;
-      uint32_t w[4] = {0, 0, 0, 0};
+    } else if (o < 2 * kpart) {
+      // V: units of (dt, kq, lr) -> 8 positions p of dim 16dt + lr, token 32c + feed_token(kq, p)
+      const int ov = o - kpart;
+      const int usz = is4 ? 4 : 8;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int p = p0 + i;
-        const int tok = (p & ~63) + feed_token(p & 63);
-        w[i / 8] |= ((uint32_t)vbuf[tok][d] & 0xFu) << (4 * (i % 8));
+      for (int h = 0; h < 4; ++h) {
+        if (!is4 && h >= 2) break;
+        const int u = ov / usz + h;
+        const int lr = u % 16, q = (u / 16) % 4, dt = u / 64;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int pp = 0; pp < 8; ++pp) {
+          const uint32_t x = (uint8_t)vbuf[32 * c + feed_token(q, pp)][16 * dt + lr];
+          if (pp < 4) lo |= x << (8 * pp);
+          else hi |= x << (8 * (pp - 4));
+        }
+        if (!is4) {
+          w[2 * h] = lo;
+          w[2 * h + 1] = hi;
+        } else {
+          w[h] = pack8_nibbles(lo, hi);
+        }
       }
-      *reinterpret_cast<uint4*>(vt + (int64_t)d * (BLK / 2) + p0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      // scales: K scales of the chunk's 32 tokens, then V scales
+      const int t0 = (o - 2 * kpart) / 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + i;
+        w[i] = __float_as_uint(t < 32 ? ksb[32 * c + t] : vsb[32 * c + t - 32]);
+      }
     }
+    *reinterpret_cast<uint4*>(rec + (int64_t)c * cbytes + o) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 

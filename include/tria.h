@@ -194,24 +194,23 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
  *   data_offset = round_up(64 + 64*batch*n_kv_heads, 256); the pairs' records
  *            follow in (b, g) order, each pair's n8 int8 records (ascending
  *            block) then its n4 int4 records (ascending block).
- *   int8 record, 2*B*d + 8*B bytes:
- *            K codes int8 [B][d] | V codes int8 [d][B] in feed order |
- *            K scales fp32 [B] | V scales fp32 [B]
- *   int4 record, B*d + 8*B bytes:
- *            K codes [B][d/2] packed along d (low nibble = even dim) |
- *            V codes [d][B/2] in feed order, packed (low nibble = even position) |
- *            K scales fp32 [B] | V scales fp32 [B]
- *   Feed order of the transposed V codes: within each group of 64 token
- *   positions, position 16*q + 8*s + p (q in 0..3, s in 0..1, p in 0..7) holds
- *   token 32*s + 16*(p / 4) + 4*q + (p % 4) of that group.  (This is the order in
- *   which the decode kernel's matrix instructions consume keys, so each lane
- *   loads one contiguous run.)
+ *   A record (int8: 2*B*d + 8*B bytes; int4: B*d + 8*B bytes) is B/32 chunks
+ *   of 32 tokens, chunk c = tokens 32c..32c+31 of the block, each laid out as
+ *     K codes: units (s, ks, q, r) in that nesting order (s in 0..1, ks in
+ *       0..d/64-1, q in 0..3, r in 0..15), unit = dims 64*ks + 16*q .. +15 of
+ *       token 32c + 16s + r: 16 int8 bytes (int4: 8 bytes, low nibble = even dim);
+ *     V codes: units (t, q, r) (t in 0..d/16-1), unit = dim 16t + r of the tokens
+ *       32c + 16*(p / 4) + 4*q + (p % 4) for p = 0..7: 8 int8 bytes (int4: 4
+ *       bytes, low nibble = even p);
+ *     K scales fp32 [32], then V scales fp32 [32] of the chunk's tokens.
+ *   (This is the order in which one decode step of 32 tokens consumes them: the
+ *   step reads one contiguous chunk and every lane of a load one contiguous unit.)
  *   Tokens at or beyond ctx_len in the current block have zero codes and scales.
  * tria_kv_cache_bytes gives the exact total; ctx_len must satisfy
  * 1 <= ctx_len <= dims->seq_len (the K/V tensors hold seq_len rows).
  */
 #define TRIA_CACHE_MAGIC 0x43564B54 /* "TKVC" */
-#define TRIA_CACHE_VERSION 1
+#define TRIA_CACHE_VERSION 2
 #define TRIA_CACHE_HEADER_BYTES 64
 #define TRIA_CACHE_DIR_ENTRY_BYTES 64
 tria_status tria_kv_cache_bytes(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
@@ -240,9 +239,14 @@ tria_status tria_check_cache(const tria_dims* dims, const void* cache, size_t ca
  * where q's row is quantised with the tria_quantize_qk contract at each
  * precision.  q bf16 [b][Hq][d]; out fp32 [b][Hq][d].  The kernel reads shapes
  * and offsets from the cache header (written by tria_pack_kv_cache for the same
- * dims and ctx_len); a header that does not match writes NaN to `out`.
+ * dims and ctx_len); a header or directory that does not match (shape, record
+ * counts, contiguous record offsets) writes NaN to `out` and reads no record.
  * workspace: device memory of at least tria_decode_workspace_bytes bytes for the
- * split-KV partial results; its contents need no initialisation.
+ * split-KV partial results; its contents need no initialisation.  Calls that
+ * share a workspace must be ordered on one stream.
+ * Errors: TRIA_ERR_UNSUPPORTED for more than 32 query heads per KV head, for
+ * batch * n_kv_heads above 4096, or when batch * n_kv_heads * ceil(ctx_len /
+ * block) * block / 16 reaches 2^31.
  */
 tria_status tria_decode_workspace_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
 tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes,

@@ -142,17 +142,66 @@ void kv_policy(int n_q_heads, int n_kv_heads, const int32_t* hi, const int32_t* 
   }
 }
 
-// Position -> token within a 64-token group of the transposed V codes (the
-// documented feed order of the cache).
-int feed_token(int pos) {
-  int grp = pos / 64, w = pos % 64;
-  int q = w / 16, s = (w % 16) / 8, p = w % 8;
-  return grp * 64 + 32 * s + 16 * (p / 4) + 4 * q + (p % 4);
-}
-
 void put_i32(uint8_t* dst, int32_t v) { std::memcpy(dst, &v, 4); }
 void put_i64(uint8_t* dst, int64_t v) { std::memcpy(dst, &v, 8); }
 void put_f32(uint8_t* dst, float v) { std::memcpy(dst, &v, 4); }
+
+// Token of position p (0..31) of a 32-token chunk in the transposed V codes
+// (the documented feed order of the cache): position 8q + p' holds token
+// 16(p' / 4) + 4q + p' % 4.
+int feed_token(int pos) {
+  int q = pos / 8, p = pos % 8;
+  return 16 * (p / 4) + 4 * q + (p % 4);
+}
+
+// One stored block as the cache's record: 32-token chunks, each holding
+//   K codes  [s 0..1][ks 0..d/64-1][kq 0..3][lr 0..15][16 dims 64ks+16kq..]  of token 32c+16s+lr
+//            (int4: the 16 dims packed into 8 bytes, low nibble = even dim)
+//   V codes  [dt 0..d/16-1][kq 0..3][lr 0..15][8 positions]  of dim 16dt+lr, position p ->
+//            token 32c + 16(p/4) + 4kq + p%4  (int4: packed, low nibble = even position)
+//   K scales fp32 [32], V scales fp32 [32]
+// This is the order in which one decode step of 32 tokens consumes them.
+void write_record(const int8_t* kc, const int8_t* vc, const float* ks, const float* vs, int block, int d,
+                  bool int4, uint8_t* rec) {
+  const int ksl = d / 64;
+  const int64_t part = int4 ? 16LL * d : 32LL * d;  // bytes of the K (and of the V) part of a chunk
+  for (int c = 0; c < block / 32; ++c) {
+    uint8_t* ck = rec + c * (2 * part + 256);
+    uint8_t* cv = ck + part;
+    uint8_t* cs = cv + part;
+    for (int s = 0; s < 2; ++s)
+      for (int kk = 0; kk < ksl; ++kk)
+        for (int q = 0; q < 4; ++q)
+          for (int lr = 0; lr < 16; ++lr) {
+            const int8_t* row = kc + static_cast<size_t>(32 * c + 16 * s + lr) * d + 64 * kk + 16 * q;
+            const int64_t unit = ((s * ksl + kk) * 4 + q) * 16 + lr;
+            for (int i = 0; i < 16; ++i) {
+              if (!int4) ck[unit * 16 + i] = static_cast<uint8_t>(row[i]);
+              else if (i % 2 == 0) ck[unit * 8 + i / 2] = pack_pair(row[i], row[i + 1]);
+            }
+          }
+    for (int dt = 0; dt < d / 16; ++dt)
+      for (int q = 0; q < 4; ++q)
+        for (int lr = 0; lr < 16; ++lr) {
+          const int64_t unit = (dt * 4 + q) * 16 + lr;
+          const int dim = 16 * dt + lr;
+          for (int p = 0; p < 8; ++p) {
+            const int8_t x = vc[static_cast<size_t>(32 * c + feed_token(8 * q + p)) * d + dim];
+            if (!int4) {
+              cv[unit * 8 + p] = static_cast<uint8_t>(x);
+            } else if (p % 2 == 0) {
+              const int8_t y = vc[static_cast<size_t>(32 * c + feed_token(8 * q + p + 1)) * d + dim];
+              cv[unit * 4 + p / 2] = pack_pair(x, y);
+            }
+          }
+        }
+    for (int t = 0; t < 32; ++t) {
+      put_f32(cs + 4 * t, ks[32 * c + t]);
+      put_f32(cs + 128 + 4 * t, vs[32 * c + t]);
+    }
+  }
+}
+
 
 }  // namespace
 
@@ -403,7 +452,7 @@ int oracle_pack_cache(int batch, int n_q_heads, int n_kv_heads, int d, int block
   const int64_t dir = 64;
   int64_t data = (64 + 64 * static_cast<int64_t>(batch) * n_kv_heads + 255) / 256 * 256;
   put_i32(out + 0, 0x43564B54);  // "TKVC"
-  put_i32(out + 4, 1);
+  put_i32(out + 4, 2);  // format version
   put_i32(out + 8, batch);
   put_i32(out + 12, n_kv_heads);
   put_i32(out + 16, d);
@@ -414,8 +463,6 @@ int oracle_pack_cache(int batch, int n_q_heads, int n_kv_heads, int d, int block
   put_i64(out + 40, total);
   put_i64(out + 48, dir);
   put_i64(out + 56, data);
-  std::vector<int8_t> codes(d);
-  float scale;
   int64_t off = data;
   for (int b = 0; b < batch; ++b)
     for (int g = 0; g < n_kv_heads; ++g) {
@@ -439,37 +486,16 @@ int oracle_pack_cache(int batch, int n_q_heads, int n_kv_heads, int d, int block
         const int qmax = pass == 0 ? 127 : 7;
         const int64_t kbytes = pass == 0 ? static_cast<int64_t>(block) * d : static_cast<int64_t>(block) * d / 2;
         for (int64_t kb : blocks) {
-          uint8_t* rk = out + off;
-          uint8_t* rv = rk + kbytes;
-          uint8_t* rks = rv + kbytes;
-          uint8_t* rvs = rks + 4LL * block;
-          std::vector<int8_t> vcodes(static_cast<size_t>(block) * d, 0);  // [token][dim]
+          // codes and scales of the block's rows (rows at or past ctx_len stay zero)
+          std::vector<int8_t> kcodes(static_cast<size_t>(block) * d, 0), vcodes(static_cast<size_t>(block) * d, 0);
+          std::vector<float> kscale(block, 0.0f), vscale(block, 0.0f);
           for (int r = 0; r < block; ++r) {
             const int64_t tok = kb * block + r;
-            if (tok >= ctx_len) continue;  // beyond the context: zero codes and scales
-            quantize_row(k + (src + tok) * d, d, qmax, codes.data(), &scale);
-            put_f32(rks + 4 * r, scale);
-            if (pass == 0) {
-              for (int x = 0; x < d; ++x) rk[static_cast<int64_t>(r) * d + x] = static_cast<uint8_t>(codes[x]);
-            } else {
-              for (int x = 0; x < d / 2; ++x)
-                rk[static_cast<int64_t>(r) * (d / 2) + x] = pack_pair(codes[2 * x], codes[2 * x + 1]);
-            }
-            quantize_row(v + (src + tok) * d, d, qmax, &vcodes[static_cast<size_t>(r) * d], &scale);
-            put_f32(rvs + 4 * r, scale);
+            if (tok >= ctx_len) continue;
+            quantize_row(k + (src + tok) * d, d, qmax, &kcodes[static_cast<size_t>(r) * d], &kscale[r]);
+            quantize_row(v + (src + tok) * d, d, qmax, &vcodes[static_cast<size_t>(r) * d], &vscale[r]);
           }
-          // V codes transposed: row = dim, columns = token positions in feed order
-          for (int x = 0; x < d; ++x) {
-            for (int pos = 0; pos < block; ++pos) {
-              const int8_t cv = vcodes[static_cast<size_t>(feed_token(pos)) * d + x];
-              if (pass == 0) {
-                rv[static_cast<int64_t>(x) * block + pos] = static_cast<uint8_t>(cv);
-              } else if (pos % 2 == 0) {
-                const int8_t cv1 = vcodes[static_cast<size_t>(feed_token(pos + 1)) * d + x];
-                rv[static_cast<int64_t>(x) * (block / 2) + pos / 2] = pack_pair(cv, cv1);
-              }
-            }
-          }
+          write_record(kcodes.data(), vcodes.data(), kscale.data(), vscale.data(), block, d, pass == 1, out + off);
           off += 2 * kbytes + 8LL * block;
         }
       }

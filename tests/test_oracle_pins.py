@@ -362,23 +362,51 @@ def test_cache_bytes_against_page_formula():
         2 * (2 * B * d + 8 * B) + (nb - 2) * (B * d + 8 * B))
 
 
-def test_packed_cache_holds_quantizer_codes():
-    b, hk, hq, n, d, B = 2, 2, 4, 700, 64, 64
+def _unpack_nibbles(a):
+    """uint8 [..., m] -> int8 [..., 2m], low nibble first, two's complement."""
+    lo, hi = (a & 0xF).astype(np.int8), (a >> 4).astype(np.int8)
+    out = np.stack([lo, hi], axis=-1).reshape(*a.shape[:-1], 2 * a.shape[-1])
+    out[out > 7] -= 16
+    return out
+
+
+def _read_record(rec, B, d, int4):
+    """Parses one record of the documented cache layout: 32-token chunks of
+    K codes [s][ks][kq][lr][16 dims], V codes [dt][kq][lr][8 positions], K and V scales."""
+    ksl, part = d // 64, (16 if int4 else 32) * d
+    kc, vc = np.zeros((B, d), np.int8), np.zeros((B, d), np.int8)
+    ks, vs = np.zeros(B, np.float32), np.zeros(B, np.float32)
+    tok = np.array([[16 * (p // 4) + 4 * q + (p % 4) for p in range(8)] for q in range(4)])  # [kq][p]
+    for c in range(B // 32):
+        ch = rec[c * (2 * part + 256):(c + 1) * (2 * part + 256)]
+        kp, vp, sp = ch[:part], ch[part:2 * part], ch[2 * part:]
+        kk = _unpack_nibbles(kp.reshape(2, ksl, 4, 16, 8)) if int4 else kp.view(np.int8).reshape(2, ksl, 4, 16, 16)
+        kc[32 * c:32 * c + 32] = kk.transpose(0, 3, 1, 2, 4).reshape(32, d)  # rows (s, lr), dims (ks, kq, i)
+        vv = _unpack_nibbles(vp.reshape(d // 16, 4, 16, 4)) if int4 else vp.view(np.int8).reshape(d // 16, 4, 16, 8)
+        for dt in range(d // 16):
+            for q in range(4):
+                vc[32 * c + tok[q], 16 * dt:16 * dt + 16] = vv[dt, q].T  # [p][lr]
+        ks[32 * c:32 * c + 32] = sp[:128].view(np.float32)
+        vs[32 * c:32 * c + 32] = sp[128:256].view(np.float32)
+    return kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("d,B", [(64, 64), (128, 128)])
+def test_packed_cache_holds_quantizer_codes(d, B):
+    b, hk, hq, n = 2, 2, 4, 700
     ctx = 650
     k = normal_bf16(15, 2, b * hk * n * d).reshape(b, hk, n, d)
     v = normal_bf16(15, 3, b * hk * n * d).reshape(b, hk, n, d)
     hi, keep = np.array([1, 3], np.int32), np.array([4, 5], np.int32)
     blob = oracle.pack_cache(k, v, hi, keep, hq, B, ctx)
     hdr = blob[:64].view(np.int32)
-    assert hdr[0] == 0x43564B54 and hdr[2] == b and hdr[3] == hk and hdr[7] == (ctx - 1) // B
+    assert hdr[0] == 0x43564B54 and hdr[1] == 2 and hdr[2] == b and hdr[3] == hk and hdr[7] == (ctx - 1) // B
     assert blob[:64].view(np.int64)[4] == ctx and blob[:64].view(np.int64)[5] == blob.size
     c = (ctx - 1) // B
     k8c, k8s = oracle.quantize_rows(k, 127)
     k4c, k4s = oracle.quantize_rows(k, 7)
     v8c, v8s = oracle.quantize_rows(v, 127)
     v4c, v4s = oracle.quantize_rows(v, 7)
-    # feed order of the transposed V codes, from the written layout
-    pos_tok = np.array([32 * s + 16 * (p // 4) + 4 * qq + (p % 4) for qq in range(4) for s in range(2) for p in range(8)])
     for bb in range(b):
         for g in range(hk):
             e = blob[64 + 64 * (bb * hk + g):][:64]
@@ -404,24 +432,14 @@ def test_packed_cache_holds_quantizer_codes():
                     vc_ref[~valid] = 0
                     ks_ref = np.where(valid, ks_ref, 0)
                     vs_ref = np.where(valid, vs_ref, 0)
-                    if qm == 127:
-                        kc = rec[:kbytes].view(np.int8).reshape(B, d)
-                        vt = rec[kbytes:2 * kbytes].view(np.int8).reshape(d, B)
-                    else:
-                        kc = np.empty((B, d), np.int8)
-                        pk = rec[:kbytes].reshape(B, d // 2)
-                        kc[:, 0::2], kc[:, 1::2] = (pk & 0xF).astype(np.int8), (pk >> 4).astype(np.int8)
-                        kc[kc > 7] -= 16
-                        pv = rec[kbytes:2 * kbytes].reshape(d, B // 2)
-                        vt = np.empty((d, B), np.int8)
-                        vt[:, 0::2], vt[:, 1::2] = (pv & 0xF).astype(np.int8), (pv >> 4).astype(np.int8)
-                        vt[vt > 7] -= 16
+                    kc, vc, ks, vs = _read_record(rec, B, d, qm == 7)
                     assert np.array_equal(kc, kc_ref)
-                    for grp in range(B // 64):
-                        assert np.array_equal(vt[:, grp * 64:(grp + 1) * 64], vc_ref[grp * 64 + pos_tok].T)
-                    assert np.array_equal(rec[2 * kbytes:2 * kbytes + 4 * B].view(np.float32), ks_ref)
-                    assert np.array_equal(rec[2 * kbytes + 4 * B:].view(np.float32), vs_ref)
+                    assert np.array_equal(vc, vc_ref)
+                    assert np.array_equal(ks, ks_ref)
+                    assert np.array_equal(vs, vs_ref)
                     off += 2 * kbytes + 8 * B
+            assert off == (int(blob[64 + 64 * (bb * hk + g) + 64:][:8].view(np.int64)[0])
+                           if bb * hk + g + 1 < b * hk else blob.size)
 
 
 # ---------------------------------------------------------------- decode
