@@ -23,7 +23,7 @@
 //   * q.k: v_mfma_i32_16x16x64_i8 with K codes straight from HBM as the A operand
 //     (int4 steps widened to 16*code).  p.v: v_mfma_f32_16x16x32_bf16 with the V
 //     codes (stored per 32-token chunk, transposed, in the order the MFMA consumes
-//     them; a step reads one contiguous chunk with lane-contiguous loads) converted
+//     them; a step reads one contiguous chunk with 1 KB lane-contiguous loads) converted
 //     to bf16 exactly, and the fp32 weight p*sv split into a bf16 high part and a
 //     bf16 remainder, so the product keeps ~16 mantissa bits.
 //   * Online softmax in fp32 (base 2).  Each wavefront writes one partial
@@ -145,19 +145,20 @@ __device__ __forceinline__ int owner_of(int64_t u, int64_t U, int64_t W) {
 
 // Register buffers of one 32-token step.  Lane (lr, kq) holds, for S^T subtile s
 // (keys 16s..16s+15 of the step), key 16s + lr's dims [64ks + 16kq, +16) (int4:
-// packed), dim 16dt + lr of the keys at feed positions [8kq, +8), and the key /
-// value scales of keys 16s + 4kq + 0..3.
+// packed), dim 16dt + lr of the keys at feed positions [8kq, +8) for every dim
+// group dt, and one of the chunk's 64 scales; the scales reach the lanes that use
+// them through LDS.
 template <int D>
 struct Buf8 {
   v4i k[2][D / 64];
-  v2i v[D / 16];
-  float4 sk[2], sv[2];
+  v4i v[D / 32];  // V units: dim groups 2m, 2m+1 (8 bytes each)
+  int sc;         // one dword of the chunk's 64 scales (lane l: K scale l, or V scale l - 32)
 };
 template <int D>
 struct Buf4 {
   v2i k[2][D / 64];
-  int v[D / 16];
-  float4 sk[2], sv[2];
+  v4i v[(D + 63) / 64];  // V units: dim groups 4m .. 4m+3 (4 bytes each)
+  int sc;
 };
 
 template <int D, int BLK, bool IS4>
@@ -175,32 +176,31 @@ struct StepIO {
   // contiguous run with lane l at offset l * size.
   __device__ __forceinline__ static void load(Buf& r, __amdgpu_buffer_rsrc_t rs, int roff, int h, int lr, int kq) {
     constexpr int KS = D / 64, ND = D / 16;
-    constexpr int KU = IS4 ? 8 : 16, VU = IS4 ? 4 : 8;  // bytes per lane of a K / V load
-    constexpr int KPART = 64 * KU * 2 * KS;              // = 32 * D (int4: 16 * D)
+    constexpr int KPART = IS4 ? 16 * D : 32 * D;  // bytes of the chunk's K (and V) part
     constexpr int CB = 2 * KPART + 256;
-    const int co = roff + h * CB;
+    const int co = uni(roff + h * CB);
     const int lane = lr + 16 * kq;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (IS4)
-          r.k[s][ks] = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * KU + (s * KS + ks) * 64 * KU, co, kNT);
-        else
-          r.k[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * KU + (s * KS + ks) * 64 * KU, co, kNT);
-      }
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      if constexpr (IS4)
-        r.v[dt] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * VU + KPART + dt * 64 * VU, co, kNT);
-      else
-        r.v[dt] = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * VU + KPART + dt * 64 * VU, co, kNT);
-    }
+    // region bases in the scalar offset, lane offsets in one register, each load a
+    // contiguous 1 KB (int4 K with d = 64: 512 B)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      r.sk[s] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, kq * 16 + 2 * KPART + 64 * s, co, kNT));
-      r.sv[s] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, kq * 16 + 2 * KPART + 128 + 64 * s, co, kNT));
+      if constexpr (!IS4) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          r.k[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + (s * KS + ks) * 1024, co, kNT);
+      } else if constexpr (KS == 2) {
+        const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + s * 1024, co, kNT);
+        r.k[s][0] = v2i{x[0], x[1]};
+        r.k[s][KS - 1] = v2i{x[2], x[3]};
+      } else {
+        r.k[s][0] = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8 + s * 512, co, kNT);
+      }
     }
+    const int vo = uni(co + KPART), so = uni(co + 2 * KPART);
+#pragma unroll
+    for (int m = 0; m < (IS4 ? (D + 63) / 64 : D / 32); ++m)
+      r.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + m * 1024, vo, kNT);
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, so, kNT);
   }
 };
 
@@ -236,8 +236,16 @@ __device__ __forceinline__ float xsum32(float x) {
 template <int D, int RG, bool IS4>
 __device__ __forceinline__ void compute_step(const typename std::conditional<IS4, Buf4<D>, Buf8<D>>::type& r,
                                              const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_from,
-                                             SegState<D, RG>& st, int kq) {
+                                             SegState<D, RG>& st, int kq, float* slot) {
   constexpr int KS = D / 64, ND = D / 16;
+  // the step's scales through the wave's LDS slot (one wavefront: in order, no barrier)
+  slot[threadIdx.x & 63] = __int_as_float(r.sc);
+  float4 skv[2], svv[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    skv[s] = *reinterpret_cast<const float4*>(slot + 16 * s + 4 * kq);
+    svv[s] = *reinterpret_cast<const float4*>(slot + 32 + 16 * s + 4 * kq);
+  }
   float u[RG][2][4];
   float mt[RG];
 #pragma unroll
@@ -256,7 +264,7 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
         }
         S = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[rg][ks], S, 0, 0, 0);
       }
-      const float kv[4] = {r.sk[s].x, r.sk[s].y, r.sk[s].z, r.sk[s].w};
+      const float kv[4] = {skv[s].x, skv[s].y, skv[s].z, skv[s].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[rg][s][i] = (float)S[i] * kv[i];
     }
@@ -301,7 +309,7 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
     v2bf lw[4];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const float vv[4] = {r.sv[s].x, r.sv[s].y, r.sv[s].z, r.sv[s].w};
+      const float vv[4] = {svv[s].x, svv[s].y, svv[s].z, svv[s].w};
       float pw[4], lo[4];
       uint32_t hb[4];
 #pragma unroll
@@ -326,9 +334,9 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
   for (int dt = 0; dt < ND; ++dt) {
     v2i w;
     if constexpr (IS4)
-      w = nib8_ordered_x16((uint32_t)r.v[dt]);
+      w = nib8_ordered_x16((uint32_t)r.v[dt / 4][dt % 4]);
     else
-      w = r.v[dt];
+      w = dt % 2 == 0 ? v2i{r.v[dt / 2][0], r.v[dt / 2][1]} : v2i{r.v[dt / 2][2], r.v[dt / 2][3]};
     const v8bf vop = i8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
@@ -339,12 +347,14 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
 }
 
 // Steps [j0, j1) of one precision run of a pair; rec0 = the run's first record.
-// The next step's loads are issued before the current step is computed; `pre` runs
-// once the first step's loads are in flight (the segment's query quantisation).
+// A ring of three register buffers keeps the loads of the next two steps in
+// flight while a step is computed; `pre` runs once the first loads are issued
+// (the segment's query quantisation).  Loads past the run's end fetch nothing,
+// so every record byte is read once.
 template <int D, int BLK, int RG, bool IS4, class Pre>
 __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes, int j0, int j1,
                                           const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_jb,
-                                          int mask_first, SegState<D, RG>& st, int lr, int kq, Pre&& pre) {
+                                          int mask_first, SegState<D, RG>& st, int lr, int kq, float* slot, Pre&& pre) {
   using IO = StepIO<D, BLK, IS4>;
   constexpr int SPB = BLK / 32;
   if (j0 >= j1) return;
@@ -354,23 +364,37 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
   // the run's records as one buffer resource (dword 3: raw 32-bit data format)
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(rec0))), (short)0, uni((j1 + SPB - 1) / SPB * rb), 0x00020000);
-  typename IO::Buf A, B;
+  // past the run's end, the same loads go through a resource with no records:
+  // the hardware range check returns zeros without a memory access, and the
+  // loads stay unconditional (a skipped load would make the wait counts unknown)
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(rec0))), (short)0, 0, 0x00020000);
+  typename IO::Buf A, B, C;
+  // each step's loads stay together in issue order (sched barriers), so waiting
+  // for the oldest buffer never waits for a younger one
   auto ld = [&](typename IO::Buf& r, int j) __attribute__((always_inline)) {
-    IO::load(r, rs, (j / SPB) * rb, j % SPB, lr, kq);
+    const bool in = j < j1;
+    __builtin_amdgcn_sched_barrier(0);
+    IO::load(r, in ? rs : none, in ? (j / SPB) * rb : 0, in ? j % SPB : 0, lr, kq);
+    __builtin_amdgcn_sched_barrier(0);
   };
   // keys of step j at or past which keys are masked: only the current block's
   // tail (ctx_len is inside block mask_jb of this run) is masked
   auto mfrom = [&](int j) __attribute__((always_inline)) -> int {
     return j / SPB == mask_jb ? mask_first - 32 * (j % SPB) : 1 << 30;
   };
-  ld(A, j0);
   pre();
-  for (int j = j0; j < j1; j += 2) {
-    ld(B, j + 1 < j1 ? j + 1 : j);  // past the end: reloads the current step (cached)
-    compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq);
-    if (j + 1 >= j1) break;
-    ld(A, j + 2 < j1 ? j + 2 : j + 1);
-    compute_step<D, RG, IS4>(B, qop, ar, mfrom(j + 1), st, kq);
+  // Step j is loaded into buffer (j - j0) % 3 and computed two loads later, so
+  // two steps are in flight during each compute.  Loads and their uses both sit
+  // inside the loop (nothing loaded before it is used in it), which keeps the
+  // compiler's wait counts exact; computes outside [j0, j1) are skipped.
+  for (int j = j0; j < j1 + 2; j += 3) {
+    ld(A, j);
+    if (j - 2 >= j0 && j - 2 < j1) compute_step<D, RG, IS4>(B, qop, ar, mfrom(j - 2), st, kq, slot);
+    ld(B, j + 1);
+    if (j - 1 >= j0 && j - 1 < j1) compute_step<D, RG, IS4>(C, qop, ar, mfrom(j - 1), st, kq, slot);
+    ld(C, j + 2);
+    if (j < j1) compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq, slot);
   }
 }
 
@@ -398,6 +422,7 @@ decode_split_kernel(DecArgs a) {
   __shared__ int slp[kMaxPairs + 1];  // partial slots per pair, then their exclusive prefix
   __shared__ int tmp[kWaves];
   __shared__ int bad;
+  __shared__ __attribute__((aligned(16))) float scl[kWaves][64];  // per-wave step scales
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, kq = lane >> 4;
@@ -491,6 +516,19 @@ decode_split_kernel(DecArgs a) {
     // this pair's G query rows, quantised at both precisions (MFMA B operands)
     v4i q8op[RG][KS], q4op[RG][KS];
     float a8[RG], a4[RG];
+    // the raw query rows are loaded first (unconditionally: padding rows re-read a
+    // valid row and are zeroed below), so they are the oldest loads in flight
+    v4i qraw[RG][KS][2];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = rg * 16 + lr < G ? rg * 16 + lr : G - 1;
+          qraw[rg][ks][hh] = *reinterpret_cast<const v4i*>(a.q + ((int64_t)b * a.hq + gkv * G + row) * D + ks * 64 +
+                                                           kq * 16 + hh * 8);
+        }
     auto quantise_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
@@ -502,16 +540,13 @@ decode_split_kernel(DecArgs a) {
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if (valid)
-              raw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + gkv * G + row) * D + ks * 64 +
-                                                    kq * 16 + hh * 8);
+            const v4i q4 = valid ? qraw[rg][ks][hh] : v4i{0, 0, 0, 0};
+            const uint4 raw = make_uint4((uint32_t)q4[0], (uint32_t)q4[1], (uint32_t)q4[2], (uint32_t)q4[3]);
             bf16x8_to_f32(raw, x[ks][hh]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ks][hh][i]));
           }
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        amax = xmax32(xmax16(amax));
         float sc8 = 0.f, sc4 = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -537,8 +572,9 @@ decode_split_kernel(DecArgs a) {
     // the last int8 record is the current block; keys at or past ctx_len are masked
     const int mask_first = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
     const bool has8 = j8a < j8b;
-    run_steps<D, BLK, RG, false>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq, quantise_q);
-    run_steps<D, BLK, RG, true>(rec0 + (int64_t)n8 * geo.rec8, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq,
+    run_steps<D, BLK, RG, false>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq, scl[wave],
+                                 quantise_q);
+    run_steps<D, BLK, RG, true>(rec0 + (int64_t)n8 * geo.rec8, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq, scl[wave],
                                 [&]() __attribute__((always_inline)) {
                                   if (!has8) quantise_q();
                                 });

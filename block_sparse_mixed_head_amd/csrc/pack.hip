@@ -13,8 +13,9 @@
 // (batch, KV head), then per pair its int8 records and its int4 records.  A record
 // is B/32 chunks of 32 tokens, each self-contained: the K codes in the order of the
 // decode kernel's matrix operand, the V codes transposed with the tokens in the
-// order its bf16 MFMA consumes them, then the chunk's K and V scales.  One decode
-// step reads one chunk as a single contiguous run, each load lane-contiguous.
+// order its bf16 MFMA consumes them, then the chunk's K and V scales.  K and V are
+// sequences of 16-byte lane units, so one decode step reads one contiguous chunk
+// with full 1 KB loads.
 //
 // One work group per stored block (grid x = block slot in the pair, y = pair); each
 // group computes its record offset from the policy (every batch element has the
@@ -186,42 +187,46 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     const int c = pc / (cbytes / 16), o = (pc % (cbytes / 16)) * 16;  // chunk, byte offset in it
     uint32_t w[4];
     if (o < kpart) {
-      // K: units of (s, ks, kq, lr) -> 16 dims 64ks + 16kq.. of token 32c + 16s + lr
-      const int usz = is4 ? 8 : 16;
+      if (!is4) {
+        // unit (s, ks, q, r): dims 64ks + 16q .. +15 of token 32c + 16s + r
+        const int u = o / 16;
+        const int r = u % 16, q = (u / 16) % 4, kk = (u / 64) % KSL, sub = u / (64 * KSL);
+        const uint4 x = *reinterpret_cast<const uint4*>(&kbuf[32 * c + 16 * sub + r][64 * kk + 16 * q]);
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+      } else {
+        // unit (s, q, r) of 8 * KSL bytes: for each ks, dims 64ks + 16q .. +15 packed
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // int4: two 8-byte units per piece
-        const int u = o / usz + h;
-        const int lr = u % 16, q = (u / 16) % 4, kk = (u / 64) % KSL, sub = u / (64 * KSL);
-        const int8_t* src = &kbuf[32 * c + 16 * sub + lr][64 * kk + 16 * q];
-        const uint4 x = *reinterpret_cast<const uint4*>(src);
-        if (!is4) {
-          w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-          break;
+        for (int h = 0; h < 2; ++h) {  // the piece's two 8-byte halves
+          const int e = o / 8 + h;       // 8-byte index in the K part
+          const int u = e / KSL, kk = e % KSL;
+          const int r = u % 16, q = (u / 16) % 4, sub = u / 64;
+          const uint4 x = *reinterpret_cast<const uint4*>(&kbuf[32 * c + 16 * sub + r][64 * kk + 16 * q]);
+          w[2 * h] = pack8_nibbles(x.x, x.y);
+          w[2 * h + 1] = pack8_nibbles(x.z, x.w);
         }
-        w[2 * h] = pack8_nibbles(x.x, x.y);
-        w[2 * h + 1] = pack8_nibbles(x.z, x.w);
       }
     } else if (o < 2 * kpart) {
-      // V: units of (dt, kq, lr) -> 8 positions p of dim 16dt + lr, token 32c + feed_token(kq, p)
-      const int ov = o - kpart;
-      const int usz = is4 ? 4 : 8;
+      // unit (m, q, r): for dim groups dt = per*m .. per*m + per - 1, the 8 positions p
+      // of dim 16dt + r (token 32c + feed_token(q, p)); int8: 8 bytes, int4: 4 bytes
+      const int u = (o - kpart) / 16;
+      const int r = u % 16, q = (u / 16) % 4, m = u / 64;
+      const int per = is4 ? 4 : 2;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if (!is4 && h >= 2) break;
-        const int u = ov / usz + h;
-        const int lr = u % 16, q = (u / 16) % 4, dt = u / 64;
+      for (int t = 0; t < 4; ++t) {
+        if (t >= per) break;
+        const int dim = 16 * (per * m + t) + r;
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int pp = 0; pp < 8; ++pp) {
-          const uint32_t x = (uint8_t)vbuf[32 * c + feed_token(q, pp)][16 * dt + lr];
+          const uint32_t x = (uint8_t)vbuf[32 * c + feed_token(q, pp)][dim];
           if (pp < 4) lo |= x << (8 * pp);
           else hi |= x << (8 * (pp - 4));
         }
         if (!is4) {
-          w[2 * h] = lo;
-          w[2 * h + 1] = hi;
+          w[2 * t] = lo;
+          w[2 * t + 1] = hi;
         } else {
-          w[h] = pack8_nibbles(lo, hi);
+          w[t] = pack8_nibbles(lo, hi);
         }
       }
     } else {

@@ -195,16 +195,20 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
  *            follow in (b, g) order, each pair's n8 int8 records (ascending
  *            block) then its n4 int4 records (ascending block).
  *   A record (int8: 2*B*d + 8*B bytes; int4: B*d + 8*B bytes) is B/32 chunks
- *   of 32 tokens, chunk c = tokens 32c..32c+31 of the block, each laid out as
- *     K codes: units (s, ks, q, r) in that nesting order (s in 0..1, ks in
- *       0..d/64-1, q in 0..3, r in 0..15), unit = dims 64*ks + 16*q .. +15 of
- *       token 32c + 16s + r: 16 int8 bytes (int4: 8 bytes, low nibble = even dim);
- *     V codes: units (t, q, r) (t in 0..d/16-1), unit = dim 16t + r of the tokens
- *       32c + 16*(p / 4) + 4*q + (p % 4) for p = 0..7: 8 int8 bytes (int4: 4
- *       bytes, low nibble = even p);
- *     K scales fp32 [32], then V scales fp32 [32] of the chunk's tokens.
+ *   of 32 tokens (chunk c = tokens 32c..32c+31 of the block): a K part and a V
+ *   part that are sequences of 16-byte units, then K scales fp32 [32] and V
+ *   scales fp32 [32].  Units are listed in nesting order; q in 0..3, r in 0..15:
+ *     int8 K (32*d bytes): unit (s, ks, q, r), s in 0..1, ks in 0..d/64-1 =
+ *       dims 64*ks + 16*q .. +15 of token 32c + 16s + r;
+ *     int4 K (16*d bytes): unit (s, q, r) = for ks = 0..d/64-1 the same 16 dims
+ *       packed into 8 bytes (low nibble = even dim);
+ *     int8 V (32*d bytes): unit (m, q, r), m in 0..d/32-1 = for dt = 2m, 2m+1:
+ *       8 bytes, byte p = dim 16*dt + r of token 32c + 16*(p/4) + 4*q + (p%4);
+ *     int4 V (16*d bytes): unit (m, q, r), m in 0..d/64-1 = for dt = 4m..4m+3:
+ *       those 8 positions packed into 4 bytes (low nibble = even p).
  *   (This is the order in which one decode step of 32 tokens consumes them: the
- *   step reads one contiguous chunk and every lane of a load one contiguous unit.)
+ *   step reads one contiguous chunk, each 1 KB load with lane 16q + r taking unit
+ *   (.., q, r).)
  *   Tokens at or beyond ctx_len in the current block have zero codes and scales.
  * tria_kv_cache_bytes gives the exact total; ctx_len must satisfy
  * 1 <= ctx_len <= dims->seq_len (the K/V tensors hold seq_len rows).

@@ -154,12 +154,17 @@ int feed_token(int pos) {
   return 16 * (p / 4) + 4 * q + (p % 4);
 }
 
-// One stored block as the cache's record: 32-token chunks, each holding
-//   K codes  [s 0..1][ks 0..d/64-1][kq 0..3][lr 0..15][16 dims 64ks+16kq..]  of token 32c+16s+lr
-//            (int4: the 16 dims packed into 8 bytes, low nibble = even dim)
-//   V codes  [dt 0..d/16-1][kq 0..3][lr 0..15][8 positions]  of dim 16dt+lr, position p ->
-//            token 32c + 16(p/4) + 4kq + p%4  (int4: packed, low nibble = even position)
-//   K scales fp32 [32], V scales fp32 [32]
+// One stored block as the cache's record: 32-token chunks, each holding a K part,
+// a V part and the chunk's scales, the parts being sequences of 16-byte units
+// (one per lane of a 1 KB load; lane = r + 16q):
+//   int8 K: unit (s, ks, q, r) = dims 64ks+16q .. +15 of token 32c+16s+r
+//   int4 K: unit (s, q, r)     = for ks = 0..d/64-1, dims 64ks+16q .. +15 packed into
+//                                8 bytes (low nibble = even dim)   [8*(d/64) bytes]
+//   int8 V: unit (m, q, r)     = for dt = 2m, 2m+1: 8 bytes, position p = dim 16dt+r of
+//                                token 32c + 16(p/4) + 4q + p%4
+//   int4 V: unit (m, q, r)     = for dt = 4m..4m+3: those 8 positions packed into 4
+//                                bytes (low nibble = even p)
+//   then K scales fp32 [32] and V scales fp32 [32].
 // This is the order in which one decode step of 32 tokens consumes them.
 void write_record(const int8_t* kc, const int8_t* vc, const float* ks, const float* vs, int block, int d,
                   bool int4, uint8_t* rec) {
@@ -169,39 +174,49 @@ void write_record(const int8_t* kc, const int8_t* vc, const float* ks, const flo
     uint8_t* ck = rec + c * (2 * part + 256);
     uint8_t* cv = ck + part;
     uint8_t* cs = cv + part;
-    for (int s = 0; s < 2; ++s)
-      for (int kk = 0; kk < ksl; ++kk)
+    // K part
+    int64_t o = 0;
+    if (!int4) {
+      for (int s = 0; s < 2; ++s)
+        for (int kk = 0; kk < ksl; ++kk)
+          for (int q = 0; q < 4; ++q)
+            for (int r = 0; r < 16; ++r) {
+              const int8_t* row = kc + static_cast<size_t>(32 * c + 16 * s + r) * d + 64 * kk + 16 * q;
+              for (int i = 0; i < 16; ++i) ck[o++] = static_cast<uint8_t>(row[i]);
+            }
+    } else {
+      for (int s = 0; s < 2; ++s)
         for (int q = 0; q < 4; ++q)
-          for (int lr = 0; lr < 16; ++lr) {
-            const int8_t* row = kc + static_cast<size_t>(32 * c + 16 * s + lr) * d + 64 * kk + 16 * q;
-            const int64_t unit = ((s * ksl + kk) * 4 + q) * 16 + lr;
-            for (int i = 0; i < 16; ++i) {
-              if (!int4) ck[unit * 16 + i] = static_cast<uint8_t>(row[i]);
-              else if (i % 2 == 0) ck[unit * 8 + i / 2] = pack_pair(row[i], row[i + 1]);
+          for (int r = 0; r < 16; ++r)
+            for (int kk = 0; kk < ksl; ++kk) {
+              const int8_t* row = kc + static_cast<size_t>(32 * c + 16 * s + r) * d + 64 * kk + 16 * q;
+              for (int i = 0; i < 16; i += 2) ck[o++] = pack_pair(row[i], row[i + 1]);
             }
-          }
-    for (int dt = 0; dt < d / 16; ++dt)
+    }
+    // V part
+    o = 0;
+    const int per = int4 ? 4 : 2;  // dim groups per unit
+    for (int m = 0; m < d / 16 / per; ++m)
       for (int q = 0; q < 4; ++q)
-        for (int lr = 0; lr < 16; ++lr) {
-          const int64_t unit = (dt * 4 + q) * 16 + lr;
-          const int dim = 16 * dt + lr;
-          for (int p = 0; p < 8; ++p) {
-            const int8_t x = vc[static_cast<size_t>(32 * c + feed_token(8 * q + p)) * d + dim];
-            if (!int4) {
-              cv[unit * 8 + p] = static_cast<uint8_t>(x);
-            } else if (p % 2 == 0) {
-              const int8_t y = vc[static_cast<size_t>(32 * c + feed_token(8 * q + p + 1)) * d + dim];
-              cv[unit * 4 + p / 2] = pack_pair(x, y);
+        for (int r = 0; r < 16; ++r)
+          for (int t = 0; t < per; ++t) {
+            const int dim = 16 * (per * m + t) + r;
+            for (int p = 0; p < 8; ++p) {
+              const int8_t x = vc[static_cast<size_t>(32 * c + feed_token(8 * q + p)) * d + dim];
+              if (!int4) {
+                cv[o++] = static_cast<uint8_t>(x);
+              } else if (p % 2 == 0) {
+                const int8_t y = vc[static_cast<size_t>(32 * c + feed_token(8 * q + p + 1)) * d + dim];
+                cv[o++] = pack_pair(x, y);
+              }
             }
           }
-        }
     for (int t = 0; t < 32; ++t) {
       put_f32(cs + 4 * t, ks[32 * c + t]);
       put_f32(cs + 128 + 4 * t, vs[32 * c + t]);
     }
   }
 }
-
 
 }  // namespace
 

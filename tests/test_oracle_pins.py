@@ -371,21 +371,31 @@ def _unpack_nibbles(a):
 
 
 def _read_record(rec, B, d, int4):
-    """Parses one record of the documented cache layout: 32-token chunks of
-    K codes [s][ks][kq][lr][16 dims], V codes [dt][kq][lr][8 positions], K and V scales."""
+    """Parses one record of the documented cache layout: 32-token chunks of a K part,
+    a V part (both sequences of 16-byte lane units, lane = r + 16q) and the scales."""
     ksl, part = d // 64, (16 if int4 else 32) * d
     kc, vc = np.zeros((B, d), np.int8), np.zeros((B, d), np.int8)
     ks, vs = np.zeros(B, np.float32), np.zeros(B, np.float32)
-    tok = np.array([[16 * (p // 4) + 4 * q + (p % 4) for p in range(8)] for q in range(4)])  # [kq][p]
+    tok = np.array([[16 * (p // 4) + 4 * q + (p % 4) for p in range(8)] for q in range(4)])  # [q][p]
     for c in range(B // 32):
         ch = rec[c * (2 * part + 256):(c + 1) * (2 * part + 256)]
         kp, vp, sp = ch[:part], ch[part:2 * part], ch[2 * part:]
-        kk = _unpack_nibbles(kp.reshape(2, ksl, 4, 16, 8)) if int4 else kp.view(np.int8).reshape(2, ksl, 4, 16, 16)
-        kc[32 * c:32 * c + 32] = kk.transpose(0, 3, 1, 2, 4).reshape(32, d)  # rows (s, lr), dims (ks, kq, i)
-        vv = _unpack_nibbles(vp.reshape(d // 16, 4, 16, 4)) if int4 else vp.view(np.int8).reshape(d // 16, 4, 16, 8)
-        for dt in range(d // 16):
-            for q in range(4):
-                vc[32 * c + tok[q], 16 * dt:16 * dt + 16] = vv[dt, q].T  # [p][lr]
+        if not int4:  # units (s, ks, q, r): dims 64ks + 16q + i of token 16s + r
+            kk = kp.view(np.int8).reshape(2, ksl, 4, 16, 16)
+            kc[32 * c:32 * c + 32] = kk.transpose(0, 3, 1, 2, 4).reshape(32, d)
+        else:         # units (s, q, r), ks inside: packed dims 64ks + 16q + i
+            kk = _unpack_nibbles(kp.reshape(2, 4, 16, ksl, 8))  # [s][q][r][ks][16]
+            kc[32 * c:32 * c + 32] = kk.transpose(0, 2, 3, 1, 4).reshape(32, d)
+        per = 4 if int4 else 2  # dim groups per unit
+        if not int4:
+            vv = vp.view(np.int8).reshape(d // 16 // per, 4, 16, per, 8)  # [m][q][r][t][p]
+        else:
+            vv = _unpack_nibbles(vp.reshape(d // 16 // per, 4, 16, per, 4))
+        for m in range(d // 16 // per):
+            for t in range(per):
+                dt = per * m + t
+                for q in range(4):
+                    vc[32 * c + tok[q], 16 * dt:16 * dt + 16] = vv[m, q, :, t, :].T  # [p][r]
         ks[32 * c:32 * c + 32] = sp[:128].view(np.float32)
         vs[32 * c:32 * c + 32] = sp[128:256].view(np.float32)
     return kc, vc, ks, vs
