@@ -34,6 +34,40 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, published
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 
+# HBM traffic of the prefill kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
+# kept with the source hash of the kernel it was measured on
+PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_kernel.llama3_8b_n8192.hbm_traffic.txt")
+PREFILL_SOURCES = [os.path.join(ROOT, "block_sparse_mixed_head_amd", "csrc", f)
+                   for f in ("prefill.hip", "device_common.h", "kernels.h")]
+
+
+def source_hash(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per prefill launch from the committed counter summary (FETCH_SIZE x
+    fetch factor + WRITE_SIZE x write factor, factors from a plain 1 GiB copy), or
+    None when the summary is missing or the kernel source changed since."""
+    try:
+        kv = {}
+        with open(PREFILL_TRAFFIC) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != source_hash(PREFILL_SOURCES):
+            return None
+        return (float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_factor"]) +
+                float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_factor"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -238,21 +272,28 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        # one query head's full prefill (all 64 query blocks) is the sample
-        h0 = 0
-        sample = [(0, h0, qb) for qb in range(n // blk)]
-        sel = units[(units[:, 1] == h0) & (units[:, 0] == 0)]
-        w_sample = kept_pairs(sel, blk, n)
-        qs, ks, vs = qh[:, h0:h0 + 1], kh[:, :1], vh[:, :1]
-        t0 = time.perf_counter()
-        oracle.prefill(qs, ks, vs, hi[h0:h0 + 1], keep[h0:h0 + 1], blk, sm, units=[(0, 0, qb) for (_, _, qb) in sample])
-        t_sample = time.perf_counter() - t0
+        # whole query heads of the same layer, one after another, until about 10 s of
+        # work is done (at most the 32 heads of the layer); scaled by kept pairs
+        G = hq // hk
+        t_sample, w_sample, heads = 0.0, 0, 0
+        for h0 in range(hq):
+            sel = units[(units[:, 1] == h0) & (units[:, 0] == 0)]
+            g0 = h0 // G
+            t0 = time.perf_counter()
+            oracle.prefill(qh[:, h0:h0 + 1], kh[:, g0:g0 + 1], vh[:, g0:g0 + 1], hi[h0:h0 + 1], keep[h0:h0 + 1],
+                           blk, sm)
+            t_sample += time.perf_counter() - t0
+            w_sample += kept_pairs(sel, blk, n)
+            heads += 1
+            if t_sample >= 10.0:
+                break
         est_total = t_sample * W / w_sample
         cpu = {"value": b * n / est_total, "unit": "tokens/s", "cores": oracle.nthreads(), "kind": "oracle",
-               "sample": f"oracle prefill of query head 0 (all {len(sample)} query blocks, {w_sample:.3g} kept "
-                         f"pairs) took {t_sample:.2f} s; scaled by kept pairs to the whole workload "
-                         f"({W:.3g} pairs); quantise/pack/decode are <1% of its work and not timed"}
-        log(f"[bench] cpu oracle sample {t_sample:.2f} s on {oracle.nthreads()} threads")
+               "sample": f"oracle prefill (quantisation + attention) of {heads} of the layer's {hq} query heads, "
+                         f"all query blocks ({w_sample:.3g} of {W:.3g} kept pairs), took {t_sample:.2f} s; "
+                         f"scaled by kept pairs to the whole workload; pack/decode are <1% of its work and not "
+                         f"timed"}
+        log(f"[bench] cpu oracle sample {heads} heads {t_sample:.2f} s on {oracle.nthreads()} threads")
 
     line = {
         "metric": "prefill tokens/s + decode HBM GB/s, block-sparse int8/int4 attn; % roofline",
@@ -270,13 +311,14 @@ def main():
         "config": {"workload": cfg.name, "batch": b, "seq_len": n, "n_q_heads": hq, "n_kv_heads": hk,
                    "head_dim": d, "block": blk, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved, "peak": peak_blend,
-                     "unit": "TFLOP/s", "frac": achieved / peak_blend, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak_blend, "traffic": measured_traffic(),
                      "work": f"4*d*W mixed ops per launch: 2dW int8 ops (QK^T) + 2dW bf16 flops (P.V), "
                              f"W = {W} kept causal pairs; peak = int8 {PEAK_INT8_TOPS:.0f} and bf16 "
                              f"{PEAK_BF16_TFLOPS:.0f} T/s combined in series"},
         "prefill": {"ms": p_mean * 1e3, "ms_median": p_med * 1e3, "ms_p10": p_p10 * 1e3, "ms_p90": p_p90 * 1e3,
                     "tokens_per_s": b * n / p_mean, "dense_equiv_tflops": dense_equiv,
-                    "effective_tflops": achieved, "kept_pairs": W,
+                    "effective_tflops": achieved, "frac_of_int8_peak": achieved / PEAK_INT8_TOPS,
+                    "kept_pairs": W,
                     "kept_density": W / (b * hq * n * (n + 1) / 2)},
         "kernels_ms": {"quantize": q_mean * 1e3, "prefill": p_mean * 1e3, "pack": k_mean * 1e3,
                        "decode_step_workload": d_mean * 1e3},

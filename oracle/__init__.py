@@ -61,7 +61,17 @@ def _c(a, dtype) -> np.ndarray:
 
 
 def nthreads() -> int:
-    return max(1, min(64, os.cpu_count() or 1))
+    """Worker threads: the cores this process may run on, capped by OMP_NUM_THREADS
+    when set (else by 16, a one-GPU share of a multi-GPU host)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "16"))
+    except ValueError:
+        cap = 16
+    return max(1, min(avail, cap))
 
 
 # ------------------------------------------------------------------ helpers
