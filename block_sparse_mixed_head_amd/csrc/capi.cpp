@@ -256,6 +256,8 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
   if (sched_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule for these dims needs %zu bytes, got %zu", need, sched_bytes);
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (dims->seq_len > INT32_MAX - dims->block)
+    return fail(TRIA_ERR_UNSUPPORTED, "prefill supports seq_len < 2^31 - block, got %lld", (long long)dims->seq_len);
   const int32_t* units = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(sched_dev) + TRIA_SCHED_HEADER_BYTES);
   return launched(tria::launch_prefill(shape_of(dims), units, n_units, q8, q4, q8s, q4s, k8, k4, k8s, k4s, v_bf16,
                                        sm_scale, out, lse, static_cast<hipStream_t>(stream)),

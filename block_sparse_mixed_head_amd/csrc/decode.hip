@@ -129,14 +129,6 @@ __device__ __forceinline__ int block_scan(int x, int* tmp, int& total) {
   return before + incl - x;
 }
 
-// Wave-uniform copies (scalar registers): record bases and step indices built from
-// them keep the loads in the scalar-base + lane-offset form, with no per-lane
-// address arithmetic.
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uni64(int64_t x) {
-  return (int64_t)(((uint64_t)(uint32_t)uni((int)(x >> 32)) << 32) | (uint32_t)uni((int)x));
-}
-
 // Owner of unit u among W wavefronts splitting U units: the largest w with
 // floor(U*w/W) <= u.
 __device__ __forceinline__ int owner_of(int64_t u, int64_t U, int64_t W) {
@@ -209,25 +201,6 @@ struct SegState {
   float m[RG], l[RG];
   v4f O[RG][D / 16];
 };
-
-// Maximum / sum over lanes l and l ^ 16, l ^ 32 (gfx950 lane-swap instructions:
-// VALU, no LDS round trip).
-__device__ __forceinline__ float xmax16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xmax32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xsum16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xsum32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // One 32-token step: scores, online softmax, O^T += V^T . P'^T.  mask_from = the
 // step's first key index at or past which keys are masked (>= 32: none).

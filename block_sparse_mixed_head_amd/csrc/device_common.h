@@ -7,6 +7,7 @@ namespace tria {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -81,6 +82,39 @@ __device__ __forceinline__ void quantize8(const float x[8], uint32_t codes8[2], 
   codes_from_amax(x, amax, codes8, codes4, s8, s4);
 }
 #pragma clang fp contract(on)
+
+// Maximum / sum over lanes l and l ^ 16, l ^ 32 (gfx950 lane-swap instructions:
+// VALU, no LDS round trip).
+__device__ __forceinline__ float xmax16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wave-uniform copies (scalar registers): bases built from them keep loads in the
+// scalar-base + lane-offset form, with no per-lane address arithmetic.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  return (int64_t)(((uint64_t)(uint32_t)uni((int)(x >> 32)) << 32) | (uint32_t)uni((int)x));
+}
+
+// Buffer resource over [base, base + bytes): loads at offsets past the end return 0
+// without touching memory (gfx950 descriptor word 3 for raw 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(base))),
+                                           (short)0, uni(bytes), 0x00020000);
+}
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 raw, float x[8]) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};

@@ -13,28 +13,34 @@
 // gfx950 design.  One work group per (b, h, q-block) unit, BLK/32 wavefronts, each
 // owning 32 query rows as two 16-row MFMA groups; the unit's kept key blocks are
 // streamed in 64-key stages.
-//   * K, V and key scales of a stage go straight from HBM into LDS with
-//     global_load_lds_dwordx4 (no staging registers), double-buffered: the next
-//     stage's loads are in flight while the current one is computed, one barrier
-//     per stage.  Each 1 KB load instruction fills a contiguous LDS range; the XOR
-//     swizzles of the LDS layouts are realised by the per-lane global addresses.
+//   * Software pipeline per wavefront: iteration s computes the softmax of stage s
+//     (VALU) together with the P.V product of stage s-1 (MFMA), then the scores of
+//     stage s+1.  A rescale of O (rare: the integer running maximum rises) is applied
+//     after stage s-1's product and before stage s's.
+//   * K, V and key scales go straight from memory into three-slot LDS rings with
+//     buffer_load ... lds (no staging registers), issued two iterations before
+//     their use.  These loads are written as inline asm: the compiler then does not
+//     treat every later read of a ring as waiting for every load into it; the kernel
+//     waits itself, for exactly the loads it needs (the next iteration's stay in
+//     flight).  One barrier per stage.  Each 1 KB load instruction
+//     fills a contiguous LDS range; the XOR swizzles of the LDS layouts are realised
+//     by the per-lane global offsets.  Rows past the sequence end read as zeros
+//     through the buffer resource's size (the causal mask discards them).
 //   * Scores are computed transposed, S^T = K . Q^T, with v_mfma_i32_16x16x64_i8:
-//     K (A operand) from LDS, the Q codes (B operand) in registers for the whole
-//     unit.  The 16x16 accumulator layout gives every lane one query row and four
-//     keys per 16-key subtile, so row maxima and sums are in-lane plus two
-//     cross-lane steps.
-//   * int4 stages: packed K nibbles are read from LDS and widened to int8 as
-//     16*code in registers (Q's int4 codes likewise, once per unit); gfx950 has no
-//     int4 MFMA.  The factor 256 is folded into the query-row scale.
+//     K (A operand) from LDS, the block's query codes (B operand) in registers for
+//     the whole unit.  The 16x16 accumulator layout gives every lane one query row
+//     and four keys per 16-key subtile, so row maxima and sums are in-lane plus two
+//     lane swaps.
+//   * int4 stages: packed K and Q nibbles are widened to int8 as 16*code in
+//     registers; gfx950 has no int4 MFMA.  The factor 256 is folded into the
+//     query-row scale.
 //   * fp32 softmax with an integer running maximum: rescales are exact powers of
 //     two, so rounding P to bf16 commutes with them and the result equals a
-//     final-maximum evaluation.  Rescaling is skipped unless some row's max rose.
-//     Only the diagonal block's stages carry the causal mask.
+//     final-maximum evaluation.
 //   * O^T = V^T . P^T with v_mfma_f32_16x16x32_bf16: the transposed scores are
 //     already the B operand layout, and V (row-major in LDS) is fed as V^T by
 //     ds_read_b64_tr_b16, so V needs no transpose pass.
-//   * Registers are held to 256 per lane so two work groups share a CU: one
-//     group's softmax (VALU) runs while the other's MFMAs and loads proceed.
+//   * Registers are held to 256 per lane so two work groups share a CU.
 #include <cfloat>
 #include <type_traits>
 
@@ -57,15 +63,15 @@ struct Cfg {
   static constexpr int VCH = D / 8;     // 16-byte chunks per bf16 V row
   static constexpr int VU = D / 16;     // 32-byte units per bf16 V row
   static constexpr int ND = D / 16;     // 16-wide output column groups
-  static constexpr int K_BYTES = SK * D;
-  static constexpr int V_BYTES = SK * D * 2;
-  static constexpr int STAGE = K_BYTES + V_BYTES + SK * 4;
-  static constexpr int Q4_STRIDE = D + 16;       // widened int4 query codes: padded rows
-  static constexpr int Q4_BYTES = BLK * Q4_STRIDE;
-  static constexpr int LDS_BYTES = 2 * STAGE + Q4_BYTES;  // two stage buffers + query codes
-  static constexpr int K8_INSTR = K_BYTES / 1024;   // 1 KB load instructions per stage
+  static constexpr int K_BYTES = SK * D;      // one K slot (int8; int4 uses half)
+  static constexpr int V_BYTES = SK * D * 2;  // one V slot
+  static constexpr int K8_INSTR = K_BYTES / 1024;  // 1 KB load instructions per stage
   static constexpr int K4_INSTR = K_BYTES / 2048;
   static constexpr int V_INSTR = V_BYTES / 1024;
+  static constexpr int K8N = K8_INSTR / WAVES;  // per wave
+  static constexpr int VN = V_INSTR / WAVES;
+  // loads per wave and stage: K pieces, V pieces, key scales
+  static constexpr int NPER = K8N + VN + 1;
 };
 
 struct Args {
@@ -87,237 +93,320 @@ struct Args {
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4f lds_v4f;
 
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* gsrc, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+// f(integral_constant<int, J>) for J = 0 .. N-1: array indices stay compile-time
+// constants from the start, so per-lane arrays live in registers.
+template <int J, int N, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>());
+    unroll<J + 1, N>(f);
+  }
 }
 
-// Per-lane byte offsets of the stage loads, relative to the stage's first key row
-// (computed once per work group).  Instruction i of a kind fills LDS bytes
-// [1024 i, 1024 i + 1024) of its region; lane l supplies the global address of
-// the 16 bytes that land at 1024 i + 16 l, which realises the XOR swizzles.
+// s_waitcnt immediate: at most vm vector-memory and lgkm LDS/scalar operations of
+// this wave still outstanding.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+// Raw buffer descriptor over [base, base + bytes) (bytes past the end read as 0),
+// wave-uniform, as four scalar registers.
+__device__ __forceinline__ v4u buffer_desc(const void* base, int bytes) {
+  const uint64_t p = (uint64_t)uni64(reinterpret_cast<int64_t>(base));
+  return v4u{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)uni(bytes), 0x00020000u};
+}
+
+// buffer_load ... lds: every active lane's 16 (4) bytes at desc + voff + soff go to
+// LDS address lds + 16 (4) * lane.  No register result; completion is counted by
+// vmcnt, which the caller waits for before the data is read (by any wave).
+__device__ __forceinline__ void dma16(v4u desc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(soff), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(v4u desc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(lds)
+               : "memory", "m0");
+}
+
+// Per-lane byte offsets, computed once per work group and held in registers.
+//   * Loads: piece j of a kind is the wave's instruction-sized share
+//     i = wave + j * WAVES of a stage; it covers LDS bytes [1024 i, 1024 i + 1024)
+//     of its slot, and lane l's 16 bytes land at 1024 i + 16 l, so the XOR swizzles
+//     of the LDS layouts are realised by the global offsets (relative to the
+//     stage's first key row).  Piece j starts 1024 * WAVES * j bytes after piece 0,
+//     in LDS and in memory alike: that distance is a whole number of swizzle
+//     periods of rows, so one offset per kind serves every piece.
+//   * LDS reads: every slot-relative read offset is one of these bases plus a
+//     compile-time constant (folded into the instruction's offset field): the
+//     swizzle term only depends on bits that the constant parts leave alone.
+// The values pass through an empty asm so the compiler treats them as opaque: it
+// neither rebuilds them inside the loop nor hoists further derived values into
+// registers.
 template <int D, int BLK>
-struct LoadPlan {
+struct LaneOffsets {
   using C = Cfg<D, BLK>;
-  static constexpr int K8N = (C::K8_INSTR + C::WAVES - 1) / C::WAVES;
-  static constexpr int K4N = (C::K4_INSTR + C::WAVES - 1) / C::WAVES;
-  static constexpr int VN = (C::V_INSTR + C::WAVES - 1) / C::WAVES;
-  uint32_t k8[K8N], k4[K4N], v[VN];
+  static constexpr int PIECE_STEP = 1024 * C::WAVES;
+  uint32_t gk8, gk4, gv, gs;      // global offsets of piece 0 (int8 K, int4 K, V) and of a key scale
+  uint32_t k8[C::KS], k4[C::KS];  // K reads (int8 / packed int4), per k-step
+  uint32_t vrow, vx;              // V reads: row part, and the XOR term of the 32-byte unit
 
   __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < K8N; ++j) {
-      const int p = (wave + j * C::WAVES) * 64 + lane, r = p / C::KCH, pc = p % C::KCH;
-      k8[j] = r * D + ((pc ^ (r & (C::KCH - 1))) << 4);
+    const int lr = lane & 15, kq = lane >> 4;
+    {
+      const unsigned p = wave * 64 + lane, pc = p % C::KCH, r = p / C::KCH;
+      gk8 = r * D + ((pc ^ (r & (C::KCH - 1))) << 4);
     }
-#pragma unroll
-    for (int j = 0; j < K4N; ++j) {
-      const int p = (wave + j * C::WAVES) * 64 + lane, r = p / C::K4CH, pc = p % C::K4CH;
-      k4[j] = r * (D / 2) + ((pc ^ (r & (C::K4CH - 1))) << 4);
+    {  // a wave past the int4 stage size never loads it (empty resource)
+      const unsigned p = (wave < C::K4_INSTR ? wave : 0) * 64 + lane, pc = p % C::K4CH, r = p / C::K4CH;
+      gk4 = r * (D / 2) + ((pc ^ (r & (C::K4CH - 1))) << 4);
     }
-#pragma unroll
-    for (int j = 0; j < VN; ++j) {
-      const int p = (wave + j * C::WAVES) * 64 + lane, r = p / C::VCH, pc = p % C::VCH;
-      v[j] = r * 2 * D + ((2 * ((pc >> 1) ^ (r & (C::VU - 1))) + (pc & 1)) << 4);
+    {
+      const unsigned p = wave * 64 + lane, pc = p % C::VCH, r = p / C::VCH;
+      gv = r * 2 * D + ((2 * ((pc >> 1) ^ (r & (C::VU - 1))) + (pc & 1)) << 4);
     }
+    gs = lane * 4;
+    // K row s*16 + lr, 16-byte chunk ks*4 + kq (int8) or 2ks + kq/2, half kq%2
+    // (int4); s*16 leaves the swizzle term (row mod chunks per row) unchanged
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      k8[ks] = lr * D + ((((ks << 2) + kq) ^ (lr & (C::KCH - 1))) << 4);
+      k4[ks] = lr * (D / 2) + ((((ks << 1) + (kq >> 1)) ^ (lr & (C::K4CH - 1))) << 4) + (kq & 1) * 8;
+    }
+    // V row 32t + 16h + 4kq + lr/4, 32-byte unit d at (d ^ (row mod VU)); 32t + 16h
+    // leaves the XOR term unchanged
+    const int vr = kq * 4 + (lr >> 2);
+    vrow = vr * 2 * D + (lr & 3) * 8;
+    vx = (vr & (C::VU - 1)) << 5;
+    asm volatile("" : "+v"(gk8));
+    asm volatile("" : "+v"(gk4));
+    asm volatile("" : "+v"(gv));
+    asm volatile("" : "+v"(gs));
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      asm volatile("" : "+v"(k8[ks]));
+      asm volatile("" : "+v"(k4[ks]));
+    }
+    asm volatile("" : "+v"(vrow));
+    asm volatile("" : "+v"(vx));
   }
 };
-
-// A row offset clamped to the last valid row (stages that run past the sequence
-// end re-read its last row: finite data that the causal mask discards).
-__device__ __forceinline__ uint32_t clamp_row(uint32_t off, uint32_t row_bytes, uint32_t last) {
-  const uint32_t r = off / row_bytes;
-  return r > last ? off - (r - last) * row_bytes : off;
-}
-
-// Issues the loads of one 64-key stage into an LDS buffer.
-template <int D, int BLK>
-__device__ __forceinline__ void load_stage(const Args& a, const LoadPlan<D, BLK>& lp, uint8_t* buf,
-                                           int64_t krow0, int64_t key0, bool is4, int wave, int lane) {
-  using C = Cfg<D, BLK>;
-  using LP = LoadPlan<D, BLK>;
-  const bool tail = key0 + C::SK > a.n;
-  const uint32_t last = (uint32_t)(a.n - 1 - key0);  // last valid row relative to key0 (tail only)
-  if (!is4) {
-    const int8_t* base = a.k8 + (krow0 + key0) * D;
-#pragma unroll
-    for (int j = 0; j < LP::K8N; ++j) {
-      const int i = wave + j * C::WAVES;
-      if (i < C::K8_INSTR) lds_dma16(base + (tail ? clamp_row(lp.k8[j], D, last) : lp.k8[j]), buf + i * 1024);
-    }
-  } else {
-    const uint8_t* base = a.k4 + (krow0 + key0) * (D / 2);
-#pragma unroll
-    for (int j = 0; j < LP::K4N; ++j) {
-      const int i = wave + j * C::WAVES;
-      if (i < C::K4_INSTR) lds_dma16(base + (tail ? clamp_row(lp.k4[j], D / 2, last) : lp.k4[j]), buf + i * 1024);
-    }
-  }
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v + (krow0 + key0) * D);
-#pragma unroll
-  for (int j = 0; j < LP::VN; ++j) {
-    const int i = wave + j * C::WAVES;
-    if (i < C::V_INSTR) lds_dma16(vbase + (tail ? clamp_row(lp.v[j], 2 * D, last) : lp.v[j]), buf + C::K_BYTES + i * 1024);
-  }
-  if (wave == C::WAVES - 1) {  // the 64 key scales, one per lane
-    const float* sbase = (is4 ? a.k4s : a.k8s) + krow0 + key0;
-    const uint32_t r = (tail && (uint32_t)lane > last) ? last : (uint32_t)lane;
-    lds_dma4(sbase + r, buf + C::K_BYTES + C::V_BYTES);
-  }
-}
 
 struct RowState {
   float M, l, a8, a4;
   int row;  // row index inside the q-block
 };
 
-// One 64-key stage for one wavefront (32 query rows).  DIAG: the stage lies in the
-// diagonal block and keys past a row are masked (key_base = first key of the stage
-// relative to the block start).
-template <int D, int BLK, bool IS4, bool DIAG, class After>
-__device__ __forceinline__ void compute_stage(const uint8_t* buf, int key_base, const float4 (&ksc)[4],
-                                              const v4i (&q8op)[2][Cfg<D, BLK>::KS],
-                                              const uint8_t* q4lds, RowState (&rs)[2], v4f (&O)[2][Cfg<D, BLK>::ND],
-                                              int lr, int kq, After&& after_reads) {
-  using C = Cfg<D, BLK>;
-  // int4 stages read this wave's query codes (widened to 16*code) from LDS
-  v4i q4op[IS4 ? 2 : 1][C::KS];
-  if (IS4) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        q4op[IS4 ? g : 0][ks] = *reinterpret_cast<const v4i*>(q4lds + rs[g].row * C::Q4_STRIDE + ks * 64 + kq * 16);
-  }
-  const uint8_t* kb = buf;
-  const lds_u8* vb = (const lds_u8*)(buf + C::K_BYTES);
+// The block's query codes of the wave's two row groups, for the whole unit: int8 as
+// MFMA operands, int4 packed (widened per int4 stage).
+template <int D>
+struct QCodes {
+  v4i q8[2][D / 64];
+  v2i q4[2][D / 64];
+};
 
-  // ---- S^T = K . Q^T
-  v4i S[2][4];
+// Scores of one 64-key stage for the wave's 32 rows: S^T = K . Q^T.
+template <int D, int BLK, bool IS4>
+__device__ __forceinline__ void qk_stage(const lds_u8* kb, const LaneOffsets<D, BLK>& lo, const QCodes<D>& q,
+                                         v4i (&S)[2][4]) {
+  using C = Cfg<D, BLK>;
+  v4i qop[2][C::KS];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if constexpr (IS4)
+        qop[g][ks] = unpack16_x16(q.q4[g][ks][0], q.q4[g][ks][1]);
+      else
+        qop[g][ks] = q.q8[g][ks];
+    }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     S[0][s] = v4i{0, 0, 0, 0};
     S[1][s] = v4i{0, 0, 0, 0};
-    const int r = s * 16 + lr;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       v4i kop;
-      if (!IS4) {
-        const int c = ks * 4 + kq;
-        kop = *reinterpret_cast<const v4i*>(kb + r * D + ((c ^ (r & (C::KCH - 1))) << 4));
+      if constexpr (!IS4) {
+        kop = *(const lds_v4i*)(kb + lo.k8[ks] + s * 16 * D);
       } else {
-        const int c = 2 * ks + (kq >> 1);
-        const uint2 w = *reinterpret_cast<const uint2*>(kb + r * (D / 2) + ((c ^ (r & (C::K4CH - 1))) << 4) + (kq & 1) * 8);
-        kop = unpack16_x16(w.x, w.y);
+        const v2i w = *(const lds_v2i*)(kb + lo.k4[ks] + s * 16 * (D / 2));
+        kop = unpack16_x16(w[0], w[1]);
       }
-      S[0][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, IS4 ? q4op[0][ks] : q8op[0][ks], S[0][s], 0, 0, 0);
-      S[1][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, IS4 ? q4op[IS4 ? 1 : 0][ks] : q8op[1][ks], S[1][s], 0, 0, 0);
+      S[0][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[0][ks], S[0][s], 0, 0, 0);
+      S[1][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[1][ks], S[1][s], 0, 0, 0);
     }
   }
+}
 
-  __builtin_amdgcn_sched_barrier(0);
-  // ---- softmax with the integer running maximum
+// Key scales of one stage for this lane's keys s*16 + kq*4 + 0..3.
+__device__ __forceinline__ void read_key_scales(const lds_f32* sc, int kq, v4f (&ksc)[4]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) ksc[s] = *(const lds_v4f*)(sc + s * 16 + kq * 4);
+}
+
+// One group (t, d) of O^T += V^T . P^T: two transposing reads give the V^T operand
+// for keys 32t + (16 per half) of column group d.
+template <int D, int BLK, int t, int d>
+__device__ __forceinline__ void pv_group(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo, const v8bf (&pb)[2][2],
+                                         v4f (&O)[2][Cfg<D, BLK>::ND]) {
+  const lds_u8* vb = vslot + lo.vrow + (lo.vx ^ (d << 5));
+  const v4s lo16 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 32 * t * 2 * D));
+  const v4s hi16 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + (32 * t + 16) * 2 * D));
+  // whole-vector concatenation (element-wise inserts of the halves have been folded
+  // incorrectly by the compiler)
+  const v8bf vop = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo16, hi16, 0, 1, 2, 3, 4, 5, 6, 7));
+  O[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[0][t], O[0][d], 0, 0, 0);
+  O[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[1][t], O[1][d], 0, 0, 0);
+}
+
+// Softmax of stage s interleaved with the P.V product of stage s-1.
+//
+// Softmax with the integer running maximum: M only has to be an integer that keeps
+// 2^(t - M) finite; it is raised (and O, l rescaled by an exact power of two) only
+// when a row's stage maximum exceeds it by more than kSlack, so weights stay below
+// 2^kSlack.  Produces the bf16 weights of stage s in the B operand layout (pcur)
+// and the rescale factor per row group (f, 1 when unchanged); returns whether any
+// row of the lane rescaled.  is4: an int4 stage; diag: a diagonal-block stage, keys
+// past a row are masked (key_base = first key of the stage relative to the block
+// start).
+//
+// The product O^T += V^T . P^T of stage s-1 (pprev, V slot vslot) is cut into
+// 2*ND groups (t, d) of two transposing LDS reads and two MFMAs, emitted between the
+// softmax's first three phases; scheduling barriers bound each region, so the
+// compiler overlaps the MFMAs with the softmax's VALU work without hoisting every V
+// read.  The product is complete before the new weights exist, so pprev and pcur
+// never share registers.
+template <int D, int BLK>
+__device__ __forceinline__ bool softmax_pv(bool is4, bool diag, const v4i (&S)[2][4], const v4f (&ksc)[4],
+                                           int key_base, RowState (&rs)[2], v8bf (&pcur)[2][2], float (&f)[2],
+                                           const v8bf (&pprev)[2][2], const lds_u8* vslot,
+                                           const LaneOffsets<D, BLK>& lo, v4f (&O)[2][Cfg<D, BLK>::ND], int kq) {
+  using C = Cfg<D, BLK>;
+  constexpr int NG = 2 * C::ND;  // product groups
+  constexpr float kSlack = 8.0f;
+  auto pv = [&](auto idx) __attribute__((always_inline)) {
+    constexpr int t = decltype(idx)::value / C::ND, d = decltype(idx)::value % C::ND;
+    pv_group<D, BLK, t, d>(vslot, lo, pprev, O);
+  };
+  // product groups [NG * k / 3, NG * (k + 1) / 3) go with softmax phase k
+  auto pv_part = [&](auto k) __attribute__((always_inline)) {
+    constexpr int K = decltype(k)::value;
+    unroll<NG * K / 3, NG * (K + 1) / 3>(pv);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   float u[2][4][4];
   float mx[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    mx[g] = -INFINITY;
+  // phases 0, 1: scaled scores and in-lane maxima of row groups 0 and 1
+  auto scores = [&](auto gtag) __attribute__((always_inline)) {
+    constexpr int g = decltype(gtag)::value;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float kv[4] = {ksc[s].x, ksc[s].y, ksc[s].z, ksc[s].w};
+      const float kv[4] = {ksc[s][0], ksc[s][1], ksc[s][2], ksc[s][3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = (float)S[g][s][i] * kv[i];
-        if (DIAG && (key_base + s * 16 + kq * 4 + i > rs[g].row)) x = -INFINITY;
-        u[g][s][i] = x;
-        mx[g] = fmaxf(mx[g], x);
-      }
+      for (int i = 0; i < 4; ++i) u[g][s][i] = (float)S[g][s][i] * kv[i];
     }
-    mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 16));
-    mx[g] = fmaxf(mx[g], __shfl_xor(mx[g], 32));
-  }
-  // The running maximum M only has to be an integer that keeps 2^(t - M) finite:
-  // it is raised (and O, l rescaled by an exact power of two) only when a row's
-  // stage maximum exceeds it by more than kSlack, so weights stay below 2^kSlack.
-  constexpr float kSlack = 8.0f;
+    if (diag) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key_base + s * 16 + kq * 4 + i > rs[g].row) u[g][s][i] = -INFINITY;
+    }
+    mx[g] = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx[g] = fmaxf(mx[g], u[g][s][i]);
+  };
+  scores(std::integral_constant<int, 0>());
+  pv_part(std::integral_constant<int, 0>());
+  scores(std::integral_constant<int, 1>());
+  pv_part(std::integral_constant<int, 1>());
+  // phase 2: row maxima across the four lanes of a row, new running maxima
   bool need = false;
-  float Mc[2];
+  float nM[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    const float ag = IS4 ? rs[g].a4 : rs[g].a8;
-    Mc[g] = ceilf(mx[g] * ag);  // -inf when the whole stage is masked for this row
-    need = need || (Mc[g] > rs[g].M + kSlack);
+    const float ag = is4 ? rs[g].a4 : rs[g].a8;
+    const float Mc = ceilf(xmax32(xmax16(mx[g])) * ag);  // -inf when the stage is masked for the row
+    const bool up = Mc > rs[g].M + kSlack;
+    need = need || up;
+    const float Mn = up ? Mc : rs[g].M;
+    f[g] = up ? exp2f(rs[g].M - Mn) : 1.0f;  // exact power of two; 0 on the first stage
+    rs[g].M = Mn;
+    rs[g].l *= f[g];
+    nM[g] = -Mn;
   }
-  if (__ballot(need)) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float Mn = Mc[g] > rs[g].M + kSlack ? Mc[g] : rs[g].M;
-      const float f = exp2f(rs[g].M - Mn);  // exact power of two; 0 on the first stage
-      rs[g].M = Mn;
-      rs[g].l *= f;
-#pragma unroll
-      for (int d = 0; d < C::ND; ++d) O[g][d] *= f;
-    }
-  }
-  v8bf pb[2][2];
+  pv_part(std::integral_constant<int, 2>());
+  // phases 3, 4: weights of row groups 0 and 1, their sums, the B operand layout
   const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const float ag = IS4 ? rs[g].a4 : rs[g].a8;
-    const float nM = -rs[g].M;
+  auto weights = [&](auto gtag) __attribute__((always_inline)) {
+    constexpr int g = decltype(gtag)::value;
+    const float ag = is4 ? rs[g].a4 : rs[g].a8;
+    float l = rs[g].l;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       v2bf x[4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int s = 2 * t + half;
-        const v2f p01 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][0], ag, nM)), __builtin_amdgcn_exp2f(fmaf(u[g][s][1], ag, nM))};
-        const v2f p23 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][2], ag, nM)), __builtin_amdgcn_exp2f(fmaf(u[g][s][3], ag, nM))};
+        const v2f p01 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][0], ag, nM[g])),
+                         __builtin_amdgcn_exp2f(fmaf(u[g][s][1], ag, nM[g]))};
+        const v2f p23 = {__builtin_amdgcn_exp2f(fmaf(u[g][s][2], ag, nM[g])),
+                         __builtin_amdgcn_exp2f(fmaf(u[g][s][3], ag, nM[g]))};
         x[2 * half] = __builtin_convertvector(p01, v2bf);
         x[2 * half + 1] = __builtin_convertvector(p23, v2bf);
-        rs[g].l = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half], one, rs[g].l, false);
-        rs[g].l = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half + 1], one, rs[g].l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half], one, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half + 1], one, l, false);
       }
       // keys 16*(2t) + 4kq + 0..3, then 16*(2t+1) + 4kq + 0..3: the B operand's k order
-      pb[g][t] = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
-                                         __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      pcur[g][t] = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
+                                           __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     }
-  }
+    rs[g].l = l;
+  };
+  weights(std::integral_constant<int, 0>());
+  weights(std::integral_constant<int, 1>());
+  return need;
+}
 
-  __builtin_amdgcn_sched_barrier(0);
-  // ---- O^T += V^T . P^T
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int r0 = 32 * t + kq * 4 + (lr >> 2);
-    const int r1 = r0 + 16;
-#pragma unroll
-    for (int d = 0; d < C::ND; ++d) {
-      const int off0 = r0 * 2 * D + ((d ^ (r0 & (C::VU - 1))) << 5) + (lr & 3) * 8;
-      const int off1 = r1 * 2 * D + ((d ^ (r1 & (C::VU - 1))) << 5) + (lr & 3) * 8;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + off0));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + off1));
-      // whole-vector concatenation (element-wise inserts of the halves have been
-      // folded incorrectly by the compiler)
-      const v8bf vop = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      O[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[0][t], O[0][d], 0, 0, 0);
-      O[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[1][t], O[1][d], 0, 0, 0);
-    }
-  }
-  // the last LDS read of the stage is issued: start the caller's next loads while
-  // the MFMAs drain
-  __builtin_amdgcn_sched_barrier(0);
-  after_reads();
+// O^T += V^T . P^T for one stage (the last one, after the loop).
+template <int D, int BLK>
+__device__ __forceinline__ void pv_stage(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo, const v8bf (&pb)[2][2],
+                                         v4f (&O)[2][Cfg<D, BLK>::ND]) {
+  using C = Cfg<D, BLK>;
+  unroll<0, 2 * C::ND>([&](auto idx) __attribute__((always_inline)) {
+    constexpr int t = decltype(idx)::value / C::ND, d = decltype(idx)::value % C::ND;
+    pv_group<D, BLK, t, d>(vslot, lo, pb, O);
+  });
 }
 
 template <int D, int BLK>
 __global__ void __launch_bounds__((Cfg<D, BLK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(Args a) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t q4lds[C::Q4_BYTES];
+  using LO = LaneOffsets<D, BLK>;
+  // three-slot rings
+  __shared__ __attribute__((aligned(1024))) uint8_t kring_[3 * C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vring_[3 * C::V_BYTES];
+  __shared__ __attribute__((aligned(16))) float sring_[3 * C::SK];
+  lds_u8* const kring = (lds_u8*)kring_;
+  lds_u8* const vring = (lds_u8*)vring_;
+  lds_f32* const sring = (lds_f32*)sring_;
+  auto kslot = [&](int r) __attribute__((always_inline)) { return kring + r * C::K_BYTES; };
+  auto vslot = [&](int r) __attribute__((always_inline)) { return vring + r * C::V_BYTES; };
+  auto sslot = [&](int r) __attribute__((always_inline)) { return sring + r * C::SK; };
+  auto lds_addr = [](const void __attribute__((address_space(3)))* p) __attribute__((always_inline)) {
+    return (uint32_t)uni((int)(uint32_t)(uintptr_t)p);
+  };
 
   const int32_t* u = a.units + 8 * (int64_t)blockIdx.x;
   const int b = u[0], h = u[1], qb = u[2], lo8 = u[3], lo4 = u[4], hi4 = u[5], sink = u[6];
@@ -336,45 +425,80 @@ prefill_kernel(Args a) {
   const int64_t krow0 = ((int64_t)b * a.hkv + g_kv) * n;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = uni(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, kq = lane >> 4;
 
-  // key block and precision of tile t of this unit: sink, int4 range, int8 range
-  auto tile_of = [&](int t, bool& is4) -> int {
-    if (t < sink) {
-      is4 = false;
-      return 0;
-    }
-    if (t < sink + n4) {
-      is4 = true;
-      return lo4 + (t - sink);
-    }
-    is4 = false;
-    return lo8 + (t - sink - n4);
-  };
+  // stage kinds, in schedule order: sink block, int4 range, int8 run, diagonal block
   const int nstages = ntiles * C::SPT;
+  const int e_sink = sink * C::SPT, e_int4 = (sink + n4) * C::SPT, e_int8 = (ntiles - 1) * C::SPT;
+  auto is4_of = [&](int st) __attribute__((always_inline)) { return st >= e_sink && st < e_int4; };
 
-  LoadPlan<D, BLK> lp;
-  lp.init(wave, lane);
-  auto issue = [&](int st, uint8_t* buf) {
-    bool is4n;
-    const int kbn = tile_of(st / C::SPT, is4n);
-    load_stage<D, BLK>(a, lp, buf, krow0, (int64_t)kbn * BLK + (st % C::SPT) * C::SK, is4n, wave, lane);
+  LO lo;
+  lo.init(wave, lane);
+
+  // Loads of stage st's K pieces and key scales into a K slot and a scale slot, and
+  // of stage st's V pieces into a V slot.  Each issues a fixed number of load
+  // instructions (K8N + 1, VN) whatever the stage, so the waits can count them: a
+  // stage past the last one, or a K piece past the int4 stage size, reads through an
+  // empty resource.  Resources and offsets are chosen by value, never by branching.
+  // Per-unit bases and the stage -> first key map in 32-bit scalar arithmetic (the
+  // host guarantees seq_len < 2^31), so a stage's addresses cost a few scalar
+  // instructions.
+  const uint64_t k8u = reinterpret_cast<uint64_t>(a.k8 + krow0 * D);
+  const uint64_t k4u = reinterpret_cast<uint64_t>(a.k4 + krow0 * (D / 2));
+  const uint64_t vu = reinterpret_cast<uint64_t>(a.v + krow0 * D);
+  const uint64_t s8u = reinterpret_cast<uint64_t>(a.k8s + krow0);
+  const uint64_t s4u = reinterpret_cast<uint64_t>(a.k4s + krow0);
+  const int n32 = (int)n, sink4 = sink + n4, d4 = lo4 - sink, d8 = lo8 - sink4;
+  auto key0_32 = [&](int st) __attribute__((always_inline)) -> int {
+    const int t = st / C::SPT;
+    const int kb = t < sink ? 0 : t + (t < sink4 ? d4 : d8);
+    return kb * BLK + (st % C::SPT) * C::SK;
   };
-  // first stage in flight while the query state is set up
-  issue(0, smem);
-
-  // int4 query codes of the block, widened once to 16*code, into LDS (rows past the
-  // end as zeros); each 16-byte group keeps the order unpack16_x16 gives the keys
+  // rows of the stage inside the sequence (0 for a stage past the last one)
+  auto rows_of = [&](bool valid, int key0) __attribute__((always_inline)) {
+    const int rem = n32 - key0;
+    return !valid ? 0 : (rem < C::SK ? (rem > 0 ? rem : 0) : C::SK);
+  };
+  auto issue_k = [&](int st, lds_u8* kd, lds_f32* sd) __attribute__((always_inline)) {
+    const bool valid = st < nstages;
+    st = valid ? st : nstages - 1;
+    const bool is4 = is4_of(st);
+    const int key0 = key0_32(st);
+    const int rows = rows_of(valid, key0);
+    // bases and offsets chosen by value (a select of two argument fields would
+    // become a scalar load from the argument block, with its wait)
+    const uint64_t kbase = is4 ? k4u + (uint32_t)key0 * (D / 2) : k8u + (uint32_t)key0 * D;
+    const int kbytes = rows * (is4 ? D / 2 : D);
+    const uint32_t off = lo.gk8 ^ ((lo.gk8 ^ lo.gk4) & (is4 ? ~0u : 0u));
 #pragma unroll
-  for (int i = tid; i < BLK * (D / 16); i += C::THREADS) {
-    const int r = i / (D / 16), c = i % (D / 16);
-    const int64_t qi = (int64_t)qb * BLK + r;
-    uint2 val = make_uint2(0, 0);
-    if (qi < n) val = *reinterpret_cast<const uint2*>(a.q4 + (qrow0 + qi) * (D / 2) + c * 8);
-    *reinterpret_cast<v4i*>(q4lds + r * C::Q4_STRIDE + c * 16) = unpack16_x16(val.x, val.y);
-  }
-  v4i q8op[2][C::KS];
+    for (int j = 0; j < C::K8N; ++j) {
+      const bool skip = is4 && wave + j * C::WAVES >= C::K4_INSTR;
+      dma16(buffer_desc(reinterpret_cast<const void*>(kbase), skip ? 0 : kbytes), off, j * LO::PIECE_STEP,
+            lds_addr(kd + (wave + j * C::WAVES) * 1024));
+    }
+    const uint64_t sbase = (is4 ? s4u : s8u) + (uint32_t)key0 * 4;
+    dma4(buffer_desc(reinterpret_cast<const void*>(sbase), rows * 4), lo.gs, lds_addr(sd));
+  };
+  auto issue_v = [&](int st, lds_u8* vd) __attribute__((always_inline)) {
+    const bool valid = st < nstages;
+    st = valid ? st : nstages - 1;
+    const int key0 = key0_32(st);
+    const v4u rv = buffer_desc(reinterpret_cast<const void*>(vu + (uint32_t)key0 * 2 * D), rows_of(valid, key0) * 2 * D);
+#pragma unroll
+    for (int j = 0; j < C::VN; ++j) dma16(rv, lo.gv, j * LO::PIECE_STEP, lds_addr(vd + (wave + j * C::WAVES) * 1024));
+  };
+
+  // ---- prologue: K and scales of stages 0..2, V of stage 0; V slot 2 (read with
+  // zero weights by the first iteration, as "stage -1") cleared
+  issue_k(0, kslot(0), sslot(0));
+  issue_k(1, kslot(1), sslot(1));
+  issue_k(2, kslot(2), sslot(2));
+  issue_v(0, vslot(0));
+  for (int i = tid; i < C::V_BYTES / 16; i += C::THREADS) *(lds_v4i*)(vslot(2) + i * 16) = v4i{0, 0, 0, 0};
+
+  // the block's query codes (rows past the end as zeros)
+  QCodes<D> q;
   RowState rs[2];
   v4f O[2][C::ND];
 #pragma unroll
@@ -384,8 +508,8 @@ prefill_kernel(Args a) {
     const bool valid = qi < n;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      q8op[g][ks] = v4i{0, 0, 0, 0};
-      if (valid) q8op[g][ks] = *reinterpret_cast<const v4i*>(a.q8 + (qrow0 + qi) * D + ks * 64 + kq * 16);
+      q.q8[g][ks] = valid ? *reinterpret_cast<const v4i*>(a.q8 + (qrow0 + qi) * D + ks * 64 + kq * 16) : v4i{0, 0, 0, 0};
+      q.q4[g][ks] = valid ? *reinterpret_cast<const v2i*>(a.q4 + (qrow0 + qi) * (D / 2) + ks * 32 + kq * 8) : v2i{0, 0};
     }
     const float sq8 = valid ? a.q8s[qrow0 + qi] : 0.0f;
     const float sq4 = valid ? a.q4s[qrow0 + qi] : 0.0f;
@@ -397,42 +521,63 @@ prefill_kernel(Args a) {
 #pragma unroll
     for (int d = 0; d < C::ND; ++d) O[g][d] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // every load above complete
+  __syncthreads();
 
-  // One stage: drain this wave's loads, barrier (stage st is in LDS and stage
-  // st-1's buffer is free), read the key scales, compute, and issue the next
-  // stage's loads after the stage's last LDS read (the compiler cannot tell LDS
-  // reads from the loads' LDS writes and would otherwise make the reads wait for
-  // them; the other work group on the CU computes while they are in flight).
-  // The loads write LDS asynchronously and count as loads, so the barrier alone
-  // does not wait for them: each wave drains its own first.
-  auto run = [&](auto is4_tag, auto diag_tag, int st) __attribute__((always_inline)) {
-    constexpr bool IS4 = decltype(is4_tag)::value, DIAG = decltype(diag_tag)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const uint8_t* buf = smem + (st & 1) * C::STAGE;
-    float4 ksc[4];
-    const float* sc = reinterpret_cast<const float*>(buf + C::K_BYTES + C::V_BYTES);
+  v4i S[2][4];
+  v4f ksc[4];
+  v8bf pprev[2][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ksc[s] = *reinterpret_cast<const float4*>(sc + s * 16 + kq * 4);
-    auto next = [&]() {
-      if (st + 1 < nstages) issue(st + 1, smem + ((st + 1) & 1) * C::STAGE);
-    };
-    const int key_base = (st % C::SPT) * C::SK;
-    // diagonal block: waves whose rows all precede the stage's keys skip it
-    if (!DIAG || key_base <= wave * 32 + 31)
-      compute_stage<D, BLK, IS4, DIAG>(buf, key_base, ksc, q8op, q4lds, rs, O, lr, kq, next);
-    else
-      next();
-  };
-  using T = std::true_type;
-  using F = std::false_type;
-  // stages by kind, in schedule order: sink block, int4 range, int8 run, diagonal
-  // (one loop per kind keeps the accumulators in the same registers)
-  int st = 0;
-  for (; st < sink * C::SPT; ++st) run(F(), F(), st);
-  for (; st < (sink + n4) * C::SPT; ++st) run(T(), F(), st);
-  for (; st < (ntiles - 1) * C::SPT; ++st) run(F(), F(), st);
-  for (; st < nstages; ++st) run(F(), T(), st);
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pprev[g][t] = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+  if (is4_of(0))
+    qk_stage<D, BLK, true>(kslot(0), lo, q, S);
+  else
+    qk_stage<D, BLK, false>(kslot(0), lo, q, S);
+  read_key_scales(sslot(0), kq, ksc);
+
+  // ---- iteration s (slot index R = s mod 3):
+  //   wait for this wave's loads of K(s+1), V(s-1) (issued two iterations ago; the
+  //   previous iteration's stay in flight) and for its reads of scales(s); barrier;
+  //   issue K(s+3), scales(s+3) into slot R and V(s+1) into slot R+1 (their previous
+  //   contents were last read before the barrier); softmax(s) with the product of
+  //   s-1 (V slot R+2); the scores of s+1 (K slot R+1) and the scales of s+1.
+  int R = 0;
+  for (int s = 0; s < nstages; ++s) {
+    const int R1 = R == 2 ? 0 : R + 1, R2 = R == 0 ? 2 : R - 1;
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::NPER, 0));
+    __builtin_amdgcn_s_barrier();
+    issue_k(s + 3, kslot(R), sslot(R));
+    issue_v(s + 1, vslot(R1));
+    v8bf pcur[2][2];
+    float f[2];
+    const bool need = softmax_pv<D, BLK>(is4_of(s), s >= e_int8, S, ksc, (s % C::SPT) * C::SK, rs, pcur, f, pprev,
+                                         vslot(R2), lo, O, kq);
+    if (__ballot(need)) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int d = 0; d < C::ND; ++d) O[g][d] *= f[g];
+    }
+    if (s + 1 < nstages) {
+      if (is4_of(s + 1))
+        qk_stage<D, BLK, true>(kslot(R1), lo, q, S);
+      else
+        qk_stage<D, BLK, false>(kslot(R1), lo, q, S);
+      read_key_scales(sslot(R1), kq, ksc);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) pprev[g][t] = pcur[g][t];
+    R = R1;
+  }
+  // product of the last stage, from V slot (nstages - 1) mod 3, whose loads were
+  // issued in the last iteration but one
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __syncthreads();
+  pv_stage<D, BLK>(vslot((nstages - 1) % 3), lo, pprev, O);
 
   // ---- epilogue: normalise and store (fp32), optional base-2 LSE
 #pragma unroll

@@ -156,6 +156,8 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
  * tria_quantize_qk, and V bf16 [b][Hkv][n][d].  out fp32 [b][Hq][n][d].
  * lse (may be NULL) fp32 [b][Hq][n] receives M_i + log2(sum_j P_ij), the base-2
  * log of the softmax denominator in units of t.
+ * Errors: TRIA_ERR_UNSUPPORTED for seq_len >= 2^31 - block (token indices are
+ * 32-bit inside the kernel).
  */
 tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes,
                          const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
