@@ -108,6 +108,20 @@ __device__ __forceinline__ void unroll(F&& f) {
   }
 }
 
+// Scheduling pattern for the current region: NDS LDS reads first, then NM times
+// {one MFMA, NV vector instructions, NDR LDS reads}: matrix and vector work issue
+// interleaved from the same wavefront (in-order issue would otherwise stall the
+// vector work behind a burst of MFMAs).
+template <int NDS, int NM, int NV, int NDR>
+__device__ __forceinline__ void interleave() {
+  if constexpr (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+  unroll<0, NM>([](auto) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    if constexpr (NDR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NDR, 0);
+  });
+}
+
 // s_waitcnt immediate: at most vm vector-memory and lgkm LDS/scalar operations of
 // this wave still outstanding.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
@@ -211,38 +225,65 @@ struct QCodes {
   v2i q4[2][D / 64];
 };
 
-// Scores of one 64-key stage for the wave's 32 rows: S^T = K . Q^T.
-template <int D, int BLK, bool IS4>
-__device__ __forceinline__ void qk_stage(const lds_u8* kb, const LaneOffsets<D, BLK>& lo, const QCodes<D>& q,
-                                         v4i (&S)[2][4]) {
-  using C = Cfg<D, BLK>;
-  v4i qop[2][C::KS];
+// Scores of one 64-key stage for the wave's 32 rows, S^T = K . Q^T, in two halves
+// (16-key subtiles 2*PART and 2*PART + 1).  qop: the query operands of the stage's
+// precision (int4 codes widened to 16*code).
+template <int D, bool IS4>
+__device__ __forceinline__ void qk_operands(const QCodes<D>& q, v4i (&qop)[2][D / 64]) {
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < D / 64; ++ks) {
       if constexpr (IS4)
         qop[g][ks] = unpack16_x16(q.q4[g][ks][0], q.q4[g][ks][1]);
       else
         qop[g][ks] = q.q8[g][ks];
     }
+}
+template <int D, int BLK, bool IS4, int PART>
+__device__ __forceinline__ void qk_read(const lds_u8* kb, const LaneOffsets<D, BLK>& lo, v4i (&kop)[2][D / 64]) {
+  using C = Cfg<D, BLK>;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int s = 2 * PART + j;
+      if constexpr (!IS4) {
+        kop[j][ks] = *(const lds_v4i*)(kb + lo.k8[ks] + s * 16 * D);
+      } else {
+        const v2i w = *(const lds_v2i*)(kb + lo.k4[ks] + s * 16 * (D / 2));
+        kop[j][ks] = unpack16_x16(w[0], w[1]);
+      }
+    }
+}
+template <int D, int PART>
+__device__ __forceinline__ void qk_mma(const v4i (&kop)[2][D / 64], const v4i (&qop)[2][D / 64], v4i (&S)[2][4]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = 2 * PART + j;
     S[0][s] = v4i{0, 0, 0, 0};
     S[1][s] = v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      v4i kop;
-      if constexpr (!IS4) {
-        kop = *(const lds_v4i*)(kb + lo.k8[ks] + s * 16 * D);
-      } else {
-        const v2i w = *(const lds_v2i*)(kb + lo.k4[ks] + s * 16 * (D / 2));
-        kop = unpack16_x16(w[0], w[1]);
-      }
-      S[0][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[0][ks], S[0][s], 0, 0, 0);
-      S[1][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[1][ks], S[1][s], 0, 0, 0);
+    for (int ks = 0; ks < D / 64; ++ks) {
+      S[0][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[j][ks], qop[0][ks], S[0][s], 0, 0, 0);
+      S[1][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[j][ks], qop[1][ks], S[1][s], 0, 0, 0);
     }
   }
+}
+template <int D, int BLK, bool IS4, int PART>
+__device__ __forceinline__ void qk_part(const lds_u8* kb, const LaneOffsets<D, BLK>& lo, const v4i (&qop)[2][D / 64],
+                                        v4i (&S)[2][4]) {
+  v4i kop[2][D / 64];
+  qk_read<D, BLK, IS4, PART>(kb, lo, kop);
+  qk_mma<D, PART>(kop, qop, S);
+}
+template <int D, int BLK, bool IS4>
+__device__ __forceinline__ void qk_stage(const lds_u8* kb, const LaneOffsets<D, BLK>& lo, const QCodes<D>& q,
+                                         v4i (&S)[2][4]) {
+  v4i qop[2][D / 64];
+  qk_operands<D, IS4>(q, qop);
+  qk_part<D, BLK, IS4, 0>(kb, lo, qop, S);
+  qk_part<D, BLK, IS4, 1>(kb, lo, qop, S);
 }
 
 // Key scales of one stage for this lane's keys s*16 + kq*4 + 0..3.
@@ -254,16 +295,23 @@ __device__ __forceinline__ void read_key_scales(const lds_f32* sc, int kq, v4f (
 // One group (t, d) of O^T += V^T . P^T: two transposing reads give the V^T operand
 // for keys 32t + (16 per half) of column group d.
 template <int D, int BLK, int t, int d>
-__device__ __forceinline__ void pv_group(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo, const v8bf (&pb)[2][2],
-                                         v4f (&O)[2][Cfg<D, BLK>::ND]) {
+__device__ __forceinline__ v8bf pv_read(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo) {
   const lds_u8* vb = vslot + lo.vrow + (lo.vx ^ (d << 5));
   const v4s lo16 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + 32 * t * 2 * D));
   const v4s hi16 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + (32 * t + 16) * 2 * D));
   // whole-vector concatenation (element-wise inserts of the halves have been folded
   // incorrectly by the compiler)
-  const v8bf vop = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo16, hi16, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo16, hi16, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <int D, int BLK, int t, int d>
+__device__ __forceinline__ void pv_mma(const v8bf& vop, const v8bf (&pb)[2][2], v4f (&O)[2][Cfg<D, BLK>::ND]) {
   O[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[0][t], O[0][d], 0, 0, 0);
   O[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[1][t], O[1][d], 0, 0, 0);
+}
+template <int D, int BLK, int t, int d>
+__device__ __forceinline__ void pv_group(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo, const v8bf (&pb)[2][2],
+                                         v4f (&O)[2][Cfg<D, BLK>::ND]) {
+  pv_mma<D, BLK, t, d>(pv_read<D, BLK, t, d>(vslot, lo), pb, O);
 }
 
 // Softmax of stage s interleaved with the P.V product of stage s-1.
@@ -273,7 +321,7 @@ __device__ __forceinline__ void pv_group(const lds_u8* vslot, const LaneOffsets<
 // when a row's stage maximum exceeds it by more than kSlack, so weights stay below
 // 2^kSlack.  Produces the bf16 weights of stage s in the B operand layout (pcur)
 // and the rescale factor per row group (f, 1 when unchanged); returns whether any
-// row of the lane rescaled.  is4: an int4 stage; diag: a diagonal-block stage, keys
+// row of the lane rescaled.  is4: an int4 stage; DIAG: a diagonal-block stage, keys
 // past a row are masked (key_base = first key of the stage relative to the block
 // start).
 //
@@ -282,23 +330,42 @@ __device__ __forceinline__ void pv_group(const lds_u8* vslot, const LaneOffsets<
 // softmax's first three phases; scheduling barriers bound each region, so the
 // compiler overlaps the MFMAs with the softmax's VALU work without hoisting every V
 // read.  The product is complete before the new weights exist, so pprev and pcur
-// never share registers.
-template <int D, int BLK>
-__device__ __forceinline__ bool softmax_pv(bool is4, bool diag, const v4i (&S)[2][4], const v4f (&ksc)[4],
-                                           int key_base, RowState (&rs)[2], v8bf (&pcur)[2][2], float (&f)[2],
-                                           const v8bf (&pprev)[2][2], const lds_u8* vslot,
-                                           const LaneOffsets<D, BLK>& lo, v4f (&O)[2][Cfg<D, BLK>::ND], int kq) {
+// never share registers.  The scores of stage s+1 (K slot kslot, precision QK4)
+// are computed in the weights phases 3 and 4, again one half per phase, into S
+// (whose stage-s values the scores phases consumed): every phase mixes matrix and
+// vector work.  between(k) runs after phase k's region (k = 0, 1, 2): the caller
+// spreads its memory-load issues over the iteration with it.
+template <int D, int BLK, bool QK4, bool DIAG, class Between>
+__device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4f (&ksc)[4],
+                                              int key_base, RowState (&rs)[2], v8bf (&pcur)[2][2], float (&f)[2],
+                                              const v8bf (&pprev)[2][2], const lds_u8* vslot,
+                                              const LaneOffsets<D, BLK>& lo, v4f (&O)[2][Cfg<D, BLK>::ND], int kq,
+                                              const lds_u8* kslot, const QCodes<D>& q, Between&& between) {
   using C = Cfg<D, BLK>;
   constexpr int NG = 2 * C::ND;  // product groups
   constexpr float kSlack = 8.0f;
-  auto pv = [&](auto idx) __attribute__((always_inline)) {
-    constexpr int t = decltype(idx)::value / C::ND, d = decltype(idx)::value % C::ND;
-    pv_group<D, BLK, t, d>(vslot, lo, pprev, O);
+  // Region k (k = 0, 1, 2) holds product groups [NG k / 3, NG (k + 1) / 3): their V
+  // reads come first, then softmax phase k's vector work (pinned to the region),
+  // then the MFMAs, which the interleave pattern spreads through the vector work.
+  constexpr int NGR = (NG + 2) / 3;  // largest region
+  v8bf vop[NGR];
+  auto pv_read_part = [&](auto k) __attribute__((always_inline)) {
+    constexpr int K = decltype(k)::value;
+    unroll<NG * K / 3, NG * (K + 1) / 3>([&](auto idx) __attribute__((always_inline)) {
+      constexpr int i = decltype(idx)::value, t = i / C::ND, d = i % C::ND;
+      vop[i - NG * K / 3] = pv_read<D, BLK, t, d>(vslot, lo);
+    });
   };
-  // product groups [NG * k / 3, NG * (k + 1) / 3) go with softmax phase k
   auto pv_part = [&](auto k) __attribute__((always_inline)) {
     constexpr int K = decltype(k)::value;
-    unroll<NG * K / 3, NG * (K + 1) / 3>(pv);
+    constexpr int NGK = NG * (K + 1) / 3 - NG * K / 3;  // groups in this region
+    unroll<NG * K / 3, NG * (K + 1) / 3>([&](auto idx) __attribute__((always_inline)) {
+      constexpr int i = decltype(idx)::value, t = i / C::ND, d = i % C::ND;
+      pv_mma<D, BLK, t, d>(vop[i - NG * K / 3], pprev, O);
+    });
+    interleave<0, 2 * NGK, (K < 2 ? 4 : 2), 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    between(k);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -313,7 +380,7 @@ __device__ __forceinline__ bool softmax_pv(bool is4, bool diag, const v4i (&S)[2
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[g][s][i] = (float)S[g][s][i] * kv[i];
     }
-    if (diag) {
+    if constexpr (DIAG) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -325,11 +392,19 @@ __device__ __forceinline__ bool softmax_pv(bool is4, bool diag, const v4i (&S)[2
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx[g] = fmaxf(mx[g], u[g][s][i]);
+    // pinned here: the compiler would otherwise move this vector work across the
+    // barrier or into other phases, away from the MFMAs it is meant to overlap
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(u[g][s][0]), "+v"(u[g][s][1]), "+v"(u[g][s][2]), "+v"(u[g][s][3]));
+    asm volatile("" : "+v"(mx[g]));
   };
+  pv_read_part(std::integral_constant<int, 0>());
   scores(std::integral_constant<int, 0>());
   pv_part(std::integral_constant<int, 0>());
+  pv_read_part(std::integral_constant<int, 1>());
   scores(std::integral_constant<int, 1>());
   pv_part(std::integral_constant<int, 1>());
+  pv_read_part(std::integral_constant<int, 2>());
   // phase 2: row maxima across the four lanes of a row, new running maxima
   bool need = false;
   float nM[2];
@@ -370,11 +445,25 @@ __device__ __forceinline__ bool softmax_pv(bool is4, bool diag, const v4i (&S)[2
       // keys 16*(2t) + 4kq + 0..3, then 16*(2t+1) + 4kq + 0..3: the B operand's k order
       pcur[g][t] = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
                                            __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+      asm volatile("" : "+v"(pcur[g][t]));  // pinned to this phase (see scores)
     }
+    asm volatile("" : "+v"(l));
     rs[g].l = l;
   };
+  // regions 3, 4: the next stage's K reads, then the weights of one row group, then
+  // half of the next stage's score MFMAs, interleaved with the weights
+  v4i qop[2][D / 64];
+  qk_operands<D, QK4>(q, qop);
+  v4i kop[2][D / 64];
+  qk_read<D, BLK, QK4, 0>(kslot, lo, kop);
   weights(std::integral_constant<int, 0>());
+  qk_mma<D, 0>(kop, qop, S);
+  interleave<0, 4 * C::KS, (QK4 ? 9 : 6), 0>();
+  __builtin_amdgcn_sched_barrier(0);
+  qk_read<D, BLK, QK4, 1>(kslot, lo, kop);
   weights(std::integral_constant<int, 1>());
+  qk_mma<D, 1>(kop, qop, S);
+  interleave<0, 4 * C::KS, (QK4 ? 9 : 6), 0>();
   return need;
 }
 
@@ -544,35 +633,58 @@ prefill_kernel(Args a) {
   //   contents were last read before the barrier); softmax(s) with the product of
   //   s-1 (V slot R+2); the scores of s+1 (K slot R+1) and the scales of s+1.
   int R = 0;
-  for (int s = 0; s < nstages; ++s) {
+  auto iter = [&](int s, auto qk4_tag, auto diag_tag) __attribute__((always_inline)) {
+    constexpr bool QK4 = decltype(qk4_tag)::value;  // precision of stage s+1
+    constexpr bool DIAG = decltype(diag_tag)::value;  // stage s in the diagonal block
     const int R1 = R == 2 ? 0 : R + 1, R2 = R == 0 ? 2 : R - 1;
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::NPER, 0));
     __builtin_amdgcn_s_barrier();
-    issue_k(s + 3, kslot(R), sslot(R));
-    issue_v(s + 1, vslot(R1));
     v8bf pcur[2][2];
     float f[2];
-    const bool need = softmax_pv<D, BLK>(is4_of(s), s >= e_int8, S, ksc, (s % C::SPT) * C::SK, rs, pcur, f, pprev,
-                                         vslot(R2), lo, O, kq);
+    // the loads of K(s+3) and scales(s+3), then of V(s+1), are issued between the
+    // softmax phases rather than all at once after the barrier, when every wave of
+    // the CU would queue them together.  After the last stage the scores step reads
+    // K slot R1 anyway (finite data, result unused).
+    auto between = [&](auto k) __attribute__((always_inline)) {
+      if constexpr (decltype(k)::value == 0) issue_k(s + 3, kslot(R), sslot(R));
+      if constexpr (decltype(k)::value == 1) issue_v(s + 1, vslot(R1));
+    };
+    const bool is4 = is4_of(s);
+    const int key_base = (s % C::SPT) * C::SK;
+    // the V read bases per column group (vx ^ 32d) are rebuilt in every iteration
+    // (one XOR each) rather than hoisted out of the loop into registers
+    LO lo_it = lo;
+    asm volatile("" : "+v"(lo_it.vx));
+    const bool need = softmax_pv_qk<D, BLK, QK4, DIAG>(is4, S, ksc, key_base, rs, pcur, f, pprev, vslot(R2), lo_it, O,
+                                                 kq, kslot(R1), q, between);
+    // the rescale of O applies to the products of stages up to s-1 (complete) and
+    // precedes the product of stage s (next iteration)
     if (__ballot(need)) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int d = 0; d < C::ND; ++d) O[g][d] *= f[g];
     }
-    if (s + 1 < nstages) {
-      if (is4_of(s + 1))
-        qk_stage<D, BLK, true>(kslot(R1), lo, q, S);
-      else
-        qk_stage<D, BLK, false>(kslot(R1), lo, q, S);
-      read_key_scales(sslot(R1), kq, ksc);
-    }
+    read_key_scales(sslot(R1), kq, ksc);
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int t = 0; t < 2; ++t) pprev[g][t] = pcur[g][t];
     R = R1;
-  }
+  };
+  // Four loops, so that each body has one precision for the scores of stage s+1 and
+  // one masking mode (two variants in one body would sit under branches, which
+  // split its scheduling regions and double its register needs): s+1 is an int4
+  // stage exactly for s in [b1, b2), and stages from e_int8 on are diagonal.
+  const int b1 = n4 > 0 ? (e_sink > 0 ? e_sink - 1 : 0) : 0;
+  const int b2 = n4 > 0 ? e_int4 - 1 : 0;
+  using T = std::true_type;
+  using F = std::false_type;
+  int s = 0;
+  for (; s < (b1 < e_int8 ? b1 : e_int8); ++s) iter(s, F(), F());
+  for (; s < b2; ++s) iter(s, T(), F());
+  for (; s < e_int8; ++s) iter(s, F(), F());
+  for (; s < nstages; ++s) iter(s, F(), T());
   // product of the last stage, from V slot (nstages - 1) mod 3, whose loads were
   // issued in the last iteration but one
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
