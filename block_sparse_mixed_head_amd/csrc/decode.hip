@@ -21,11 +21,12 @@
 //     and keeps the next step's loads in flight (register double buffer) while it
 //     computes the current one.
 //   * q.k: v_mfma_i32_16x16x64_i8 with K codes straight from HBM as the A operand
-//     (int4 steps widened to 16*code).  p.v: v_mfma_f32_16x16x32_bf16 with the V
+//     (int4 steps widened to 16*code).  p.v: v_mfma_f32_16x16x32_f16 with the V
 //     codes (stored per 32-token chunk, transposed, in the order the MFMA consumes
-//     them; a step reads one contiguous chunk with 1 KB lane-contiguous loads) converted
-//     to bf16 exactly, and the fp32 weight p*sv split into a bf16 high part and a
-//     bf16 remainder, so the product keeps ~16 mantissa bits.
+//     them; a step reads one contiguous chunk with 1 KB lane-contiguous loads) turned
+//     into fp16 exactly by byte permutes (a code plus a fixed bias, removed at the
+//     end), and the fp32 weight p*sv split into an fp16 high part and an fp16
+//     remainder, so the product keeps ~21 mantissa bits.
 //   * Online softmax in fp32 (base 2).  Each wavefront writes one partial
 //     (m, l, o[d]) per pair it touched; a second kernel merges a pair's partials.
 //   * Both kernels validate the cache header and directory before reading any
@@ -82,27 +83,6 @@ __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
   return hd[0] == 0x43564B54 && hd[1] == 2 && hd[2] == a.batch && hd[3] == a.hkv && hd[4] == D &&
          hd[5] == BLK && hd[6] == geo.cur + 1 && hd[7] == geo.cur && h64[4] == a.ctx_len &&
          geo.total <= a.cache_bytes && h64[6] == 64 && h64[7] == geo.data_offset;
-}
-
-// 8 signed bytes -> 8 bf16 (exact: |value| <= 127)
-__device__ __forceinline__ v8bf i8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  v8bf r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (__bf16)(float)(int)(int8_t)(w0 >> (8 * i));
-    r[4 + i] = (__bf16)(float)(int)(int8_t)(w1 >> (8 * i));
-  }
-  return r;
-}
-
-// 8 packed nibbles (one dword, low nibble first) -> 8 int8 holding 16*code, in
-// position order.
-__device__ __forceinline__ v2i nib8_ordered_x16(uint32_t w) {
-  const uint32_t e = nib_even_x16(w), o = nib_odd_x16(w);
-  v2i r;
-  r[0] = (int)__builtin_amdgcn_perm(o, e, 0x05010400u);
-  r[1] = (int)__builtin_amdgcn_perm(o, e, 0x07030602u);
-  return r;
 }
 
 // Exclusive prefix over the work group of one value per thread; returns the
@@ -167,7 +147,7 @@ struct StepIO {
   // kq, lr), then the K and V scales of its 32 tokens: every load below reads a
   // contiguous run with lane l at offset l * size.
   __device__ __forceinline__ static void load(Buf& r, __amdgpu_buffer_rsrc_t rs, int roff, int h, int lr, int kq) {
-    constexpr int KS = D / 64, ND = D / 16;
+    constexpr int KS = D / 64;
     constexpr int KPART = IS4 ? 16 * D : 32 * D;  // bytes of the chunk's K (and V) part
     constexpr int CB = 2 * KPART + 256;
     const int co = uni(roff + h * CB);
@@ -199,8 +179,39 @@ struct StepIO {
 template <int D, int RG>
 struct SegState {
   float m[RG], l[RG];
+  float c[RG];  // bias correction: sum over this lane's keys of bias * p' (see compute_step)
   v4f O[RG][D / 16];
+  int k;        // scale exponent of p' (wave-uniform)
 };
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// V codes to fp16 MFMA operands, exactly, with a known affine bias: the two's
+// complement sign is flipped and the code placed in the low mantissa byte of an
+// fp16 with exponent 2^10 (high byte 0x64) by byte permutes:
+//   int8 code v -> 1024 + (v + 128)        = 1152 + v
+//   int4 code c -> 1024 + 16 (c + 8)       = 1152 + 16 c   (nibble in bits 4..7)
+// The bias times the weights' sum is subtracted from O at the end; the 16 of int4
+// is folded into its weights.
+constexpr float kBias = 1152.0f;
+__device__ __forceinline__ v8h v8_to_f16(uint32_t w0, uint32_t w1) {
+  const uint32_t magic = 0x64646464u;
+  w0 ^= 0x80808080u;
+  w1 ^= 0x80808080u;
+  const v4i r = {(int)__builtin_amdgcn_perm(magic, w0, 0x04010400u), (int)__builtin_amdgcn_perm(magic, w0, 0x04030402u),
+                 (int)__builtin_amdgcn_perm(magic, w1, 0x04010400u), (int)__builtin_amdgcn_perm(magic, w1, 0x04030402u)};
+  return __builtin_bit_cast(v8h, r);
+}
+// 8 packed nibbles (low nibble first) -> 8 fp16 in position order
+__device__ __forceinline__ v8h v4_to_f16(uint32_t w) {
+  w ^= 0x88888888u;
+  const uint32_t e = (w << 4) & 0xF0F0F0F0u, o = w & 0xF0F0F0F0u;  // (c + 8) << 4 per byte: even, odd codes
+  // byte j of e and of o into the low bytes of the two halves, high bytes 0x64
+  auto pair = [&](uint32_t sel) { return (int)((__builtin_amdgcn_perm(o, e, sel) & 0x00FF00FFu) | 0x64006400u); };
+  const v4i r = {pair(0x04040000u), pair(0x05050101u), pair(0x06060202u), pair(0x07070303u)};
+  return __builtin_bit_cast(v8h, r);
+}
 
 // One 32-token step: scores, online softmax, O^T += V^T . P'^T.  mask_from = the
 // step's first key index at or past which keys are masked (>= 32: none).
@@ -267,54 +278,76 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
       const float f = __builtin_amdgcn_exp2f(st.m[rg] - mn);  // 0 while m was -inf
       st.m[rg] = mn;
       st.l[rg] *= f;
+      st.c[rg] *= f;
 #pragma unroll
       for (int d = 0; d < ND; ++d) st.O[rg][d] *= f;
     }
   }
-  // weights p = 2^(u a - m); p' = p * sv split into a bf16 high part (truncated)
-  // and the bf16 of the exact remainder
-  v8bf bhi[RG], blo[RG];
+  // the weights' scale 2^k keeps p' = p * sv * 2^k (p <= 1) inside fp16: lowered
+  // (O and c rescaled exactly) if a step's V scales would take it past 2^14
+  {
+    float smax = fmaxf(fmaxf(fmaxf(svv[0].x, svv[0].y), fmaxf(svv[0].z, svv[0].w)),
+                       fmaxf(fmaxf(svv[1].x, svv[1].y), fmaxf(svv[1].z, svv[1].w)));
+    if (__ballot(smax > __builtin_ldexpf(1.0f, 14 - st.k))) {
+      const int e = ilogbf(xmax32(xmax16(smax))) + 1;  // 2^e > max scale
+      const int kn = 14 - e;
+      const float f = __builtin_ldexpf(1.0f, kn - st.k);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        st.c[rg] *= f;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) st.O[rg][d] *= f;
+      }
+      st.k = kn;
+    }
+  }
+  // weights p = 2^(u a - m); p' = p * sv * 2^k (int4: / 16) split into an fp16 high
+  // part (rounded toward zero) and the fp16 of the remainder
+  const float wsc = __builtin_ldexpf(IS4 ? 1.0f / 16.0f : 1.0f, st.k);
+  v8h bhi[RG], blo[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     // m is -inf only while every key seen so far was masked (then u is too)
     const float nm = st.m[rg] == -INFINITY ? 0.0f : -st.m[rg];
-    v4i hw;
-    v2bf lw[4];
+    v2h hw[4], lw[4];
+    float psum = 0.0f;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const float vv[4] = {svv[s].x, svv[s].y, svv[s].z, svv[s].w};
-      float pw[4], lo[4];
-      uint32_t hb[4];
+      float pw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(u[rg][s][i], ar[rg], nm));
         st.l[rg] += p;
-        pw[i] = p * (IS4 ? vv[i] * (1.0f / 16.0f) : vv[i]);
-        hb[i] = __float_as_uint(pw[i]) & 0xFFFF0000u;
-        lo[i] = pw[i] - __uint_as_float(hb[i]);
+        pw[i] = p * (vv[i] * wsc);
+        psum += pw[i];
       }
-      hw[2 * s] = (int)__builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
-      hw[2 * s + 1] = (int)__builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
-      lw[2 * s] = __builtin_convertvector((v2f{lo[0], lo[1]}), v2bf);
-      lw[2 * s + 1] = __builtin_convertvector((v2f{lo[2], lo[3]}), v2bf);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v2h hi = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(pw[2 * h], pw[2 * h + 1]));
+        const v2f hf = __builtin_convertvector(hi, v2f);
+        hw[2 * s + h] = hi;
+        lw[2 * s + h] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(pw[2 * h] - hf[0], pw[2 * h + 1] - hf[1]));
+      }
     }
-    bhi[rg] = __builtin_bit_cast(v8bf, hw);
-    blo[rg] = __builtin_bit_cast(v8bf, __builtin_shufflevector(__builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3),
-                                                               __builtin_shufflevector(lw[2], lw[3], 0, 1, 2, 3),
-                                                               0, 1, 2, 3, 4, 5, 6, 7));
+    st.c[rg] = fmaf(kBias, psum, st.c[rg]);
+    bhi[rg] = __builtin_shufflevector(__builtin_shufflevector(hw[0], hw[1], 0, 1, 2, 3),
+                                      __builtin_shufflevector(hw[2], hw[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    blo[rg] = __builtin_shufflevector(__builtin_shufflevector(lw[0], lw[1], 0, 1, 2, 3),
+                                      __builtin_shufflevector(lw[2], lw[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
   }
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt) {
-    v2i w;
+    v8h vop;
     if constexpr (IS4)
-      w = nib8_ordered_x16((uint32_t)r.v[dt / 4][dt % 4]);
+      vop = v4_to_f16((uint32_t)r.v[dt / 4][dt % 4]);
     else
-      w = dt % 2 == 0 ? v2i{r.v[dt / 2][0], r.v[dt / 2][1]} : v2i{r.v[dt / 2][2], r.v[dt / 2][3]};
-    const v8bf vop = i8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+      vop = dt % 2 == 0 ? v8_to_f16((uint32_t)r.v[dt / 2][0], (uint32_t)r.v[dt / 2][1])
+                        : v8_to_f16((uint32_t)r.v[dt / 2][2], (uint32_t)r.v[dt / 2][3]);
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      st.O[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, bhi[rg], st.O[rg][dt], 0, 0, 0);
-      st.O[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, blo[rg], st.O[rg][dt], 0, 0, 0);
+      st.O[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, bhi[rg], st.O[rg][dt], 0, 0, 0);
+      st.O[rg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, blo[rg], st.O[rg][dt], 0, 0, 0);
     }
   }
 }
@@ -539,9 +572,11 @@ decode_split_kernel(DecArgs a) {
     for (int rg = 0; rg < RG; ++rg) {
       st.m[rg] = -INFINITY;
       st.l[rg] = 0.0f;
+      st.c[rg] = 0.0f;
 #pragma unroll
       for (int d = 0; d < ND; ++d) st.O[rg][d] = v4f{0.f, 0.f, 0.f, 0.f};
     }
+    st.k = 8;
     // the last int8 record is the current block; keys at or past ctx_len are masked
     const int mask_first = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
     const bool has8 = j8a < j8b;
@@ -556,13 +591,17 @@ decode_split_kernel(DecArgs a) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       const float l = xsum32(xsum16(st.l[rg]));
+      // O = (accumulated - bias correction) / 2^k (exact scaling)
+      const float c = xsum32(xsum16(st.c[rg]));
+      const float inv = __builtin_ldexpf(1.0f, -st.k);
       const int row = rg * 16 + lr;
       if (row < G) {
         float* dst = part + ((int64_t)slot * G + row) * (D + 4);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
           *reinterpret_cast<float4*>(dst + dt * 16 + kq * 4) =
-              make_float4(st.O[rg][dt][0], st.O[rg][dt][1], st.O[rg][dt][2], st.O[rg][dt][3]);
+              make_float4((st.O[rg][dt][0] - c) * inv, (st.O[rg][dt][1] - c) * inv, (st.O[rg][dt][2] - c) * inv,
+                          (st.O[rg][dt][3] - c) * inv);
         if (kq == 0) *reinterpret_cast<float4*>(dst + D) = make_float4(st.m[rg], l, 0.0f, 0.0f);
       }
     }

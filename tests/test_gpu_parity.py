@@ -284,3 +284,30 @@ def test_decode_full_size_workload(tria):
     assert got.size == ref_blob.size and np.array_equal(got, ref_blob)
     ref = oracle.decode(k, v, q, hi, keep, cfg.block, cfg.seq_len, 1.0 / math.sqrt(cfg.head_dim))
     assert_close(out.cpu().numpy(), ref, "decode config 4")
+
+
+@pytest.mark.gpu
+def test_decode_reuses_one_workspace(tria):
+    """Calls sharing one workspace: three decodes of different context lengths and
+    policies, with a rejected cache in between, all match the oracle."""
+    b, hq, hk, d, n, blk = 2, 8, 2, 128, 1400, 128
+    cfg = synth.Config("dec", b, hq, hk, d, n, blk, seed=77, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    kd, vd, qd = dev(k), dev(v), dev(q)
+    ws = torch.empty(tria.decode_workspace_bytes(dd, n), dtype=torch.uint8, device="cuda")
+    runs = [(1400, [1, 0], [6, 3]), (777, [0, 2], [2, 9]), (1400, [3, 3], [3, 3])]
+    for i, (ctx, hi, keep) in enumerate(runs):
+        print(f"[case] shared workspace run {i}: ctx {ctx}", flush=True)
+        hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+        cache = tria.pack_kv_cache(dd, hi, keep, ctx, kd, vd)
+        out = tria.decode(dd, cache, ctx, qd, 1.0 / math.sqrt(d), workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.decode(k, v, q, hi, keep, blk, ctx, 1.0 / math.sqrt(d))
+        assert_close(out.cpu().numpy(), ref, f"decode with a shared workspace, run {i}")
+        if i == 0:
+            bad = cache.clone()
+            bad[0] = 0
+            o = tria.decode(dd, bad, ctx, qd, 0.125, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.isnan(o).all().item()
