@@ -404,6 +404,59 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
   }
 }
 
+// block_scan of two values at once (same barriers); tmp holds 2 * kWaves ints.
+__device__ __forceinline__ int2 block_scan2(int x, int y, int* tmp, int& tx, int& ty) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ix = x, iy = y;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(ix, o), b = __shfl_up(iy, o);
+    if (lane >= o) {
+      ix += a;
+      iy += b;
+    }
+  }
+  if (lane == 63) {
+    tmp[wave] = ix;
+    tmp[kWaves + wave] = iy;
+  }
+  __syncthreads();
+  int bx = 0, by = 0;
+  tx = 0;
+  ty = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = tmp[w], u = tmp[kWaves + w];
+    bx += w < wave ? t : 0;
+    by += w < wave ? u : 0;
+    tx += t;
+    ty += u;
+  }
+  __syncthreads();
+  return make_int2(bx + ix - x, by + iy - y);
+}
+
+// In-place exclusive prefixes of a[0..P) and b[0..P), a[P], b[P] = totals.
+__device__ __forceinline__ void prefix2_lds(int* arr, int* brr, int P, int* tmp) {
+  int ca = 0, cb = 0;
+  for (int base = 0; base < P; base += kThreads) {
+    const int p = base + (int)threadIdx.x;
+    int ta, tb;
+    const int2 e = block_scan2(p < P ? arr[p] : 0, p < P ? brr[p] : 0, tmp, ta, tb);
+    if (p < P) {
+      arr[p] = ca + e.x;
+      brr[p] = cb + e.y;
+    }
+    ca += ta;
+    cb += tb;
+  }
+  if (threadIdx.x == 0) {
+    arr[P] = ca;
+    brr[P] = cb;
+  }
+  __syncthreads();
+}
+
 // In-place exclusive prefix of arr[0..P), arr[P] = total (chunks of the group size).
 __device__ __forceinline__ void prefix_lds(int* arr, int P, int* tmp) {
   int carry = 0;
@@ -426,7 +479,7 @@ decode_split_kernel(DecArgs a) {
   __shared__ int n8p[kMaxPairs + 1];  // int8 records per pair, then their exclusive prefix
   __shared__ int n4p[kMaxPairs + 1];  // int4 records per pair, then their exclusive prefix
   __shared__ int slp[kMaxPairs + 1];  // partial slots per pair, then their exclusive prefix
-  __shared__ int tmp[kWaves];
+  __shared__ int tmp[2 * kWaves];
   __shared__ int bad;
   __shared__ __attribute__((aligned(16))) float scl[kWaves][64];  // per-wave step scales
 
@@ -434,6 +487,27 @@ decode_split_kernel(DecArgs a) {
   const int lr = lane & 15, kq = lane >> 4;
   const int G = a.hq / a.hkv;
   const int P = a.batch * a.hkv;
+  // the directory entry of pair tid is loaded together with the header (the host
+  // checked that the directory lies inside the cache): one memory round trip
+  v4i ent[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (tid < P) {
+    const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)tid);
+    ent[0] = e[0];
+    ent[1] = e[1];
+    ent[2] = e[2];
+  }
+  auto entry = [&](int p, v4i (&x)[3]) __attribute__((always_inline)) {
+    if (p == tid) {
+      x[0] = ent[0];
+      x[1] = ent[1];
+      x[2] = ent[2];
+    } else {
+      const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+      x[0] = e[0];
+      x[1] = e[1];
+      x[2] = e[2];
+    }
+  };
   Geo geo;
   if (!header_ok<D, BLK>(a, geo)) {
     if (blockIdx.x == 0 && tid == 0) reinterpret_cast<int*>(a.ws)[0] = 0;
@@ -443,8 +517,9 @@ decode_split_kernel(DecArgs a) {
   __syncthreads();
   // ---- directory: record counts per pair, checked
   for (int p = tid; p < P; p += kThreads) {
-    const int32_t* e = reinterpret_cast<const int32_t*>(a.cache + 64 + 64 * (int64_t)p);
-    const int n8 = e[2], n4 = e[3], lo8 = e[6], sink = e[7], lo4 = e[8];
+    v4i e[3];
+    entry(p, e);
+    const int n8 = e[0][2], n4 = e[0][3], lo8 = e[1][2], sink = e[1][3], lo4 = e[2][0];
     // the int8 run ends at the current block; int4 records lie below it
     const bool ok = n8 >= 1 && n4 >= 0 && n8 + n4 <= geo.cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
                     lo8 + (n8 - sink) - 1 == geo.cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 &&
@@ -454,8 +529,7 @@ decode_split_kernel(DecArgs a) {
     n4p[p] = ok ? n4 : 0;
   }
   __syncthreads();
-  prefix_lds(n8p, P, tmp);
-  prefix_lds(n4p, P, tmp);
+  prefix2_lds(n8p, n4p, P, tmp);
   // ---- the split: U units, W wavefronts, W <= U / 2 so that every wavefront's
   // range (>= 2 units) holds at least one step start
   auto units_at = [&](int p) -> int64_t { return (int64_t)SPB * (2 * (int64_t)n8p[p] + n4p[p]); };
@@ -464,7 +538,9 @@ decode_split_kernel(DecArgs a) {
   // records are contiguous in (b, g) order; pair p gets one partial slot per
   // wavefront owning one of its steps
   for (int p = tid; p < P; p += kThreads) {
-    const int64_t off = *reinterpret_cast<const int64_t*>(a.cache + 64 + 64 * (int64_t)p);
+    v4i e[3];
+    entry(p, e);
+    const int64_t off = (int64_t)(((uint64_t)(uint32_t)e[0][1] << 32) | (uint32_t)e[0][0]);
     if (off != geo.data_offset + (int64_t)n8p[p] * geo.rec8 + (int64_t)n4p[p] * geo.rec4) bad = 1;
     const int64_t u0 = units_at(p), u1 = units_at(p + 1);
     const int64_t last = n4p[p + 1] > n4p[p] ? u1 - 1 : u1 - 2;  // start of the pair's last step
