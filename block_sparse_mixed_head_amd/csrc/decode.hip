@@ -685,59 +685,69 @@ decode_split_kernel(DecArgs a) {
 }
 
 // Merge of the partials of each pair: one work group per (batch, query head), one
-// thread per output column; a pair's partials are read in parallel.
+// thread per output column.  The pair's slot range and, for the first 16 slots,
+// every column value are loaded in two rounds with all loads in flight; thread t
+// also takes slot t's (m, l).  Then M = max m, f_i = 2^(m_i - M) through LDS, and
+// out = sum_i f_i o_i / sum_i f_i l_i.
 template <int D>
 __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
-  constexpr int NW = D / 64;
+  constexpr int NW = D / 64, BO = 16;
   __shared__ float fs[D];
-  __shared__ float red[NW];
+  __shared__ float red[2][NW];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int b = bh / a.hq, h = bh % a.hq;
   const int G = a.hq / a.hkv;
   const int pair = b * a.hkv + h / G, row = h % G;
   const int* wsh = reinterpret_cast<const int*>(a.ws);
   float* dst = a.out + (int64_t)bh * D;
-  if (wsh[0] != 1 || wsh[1] != a.batch * a.hkv) {
+  // header and slot range in one round (the workspace holds them for every pair)
+  const int valid = wsh[0], np = wsh[1], i0 = wsh[16 + pair], i1 = wsh[16 + pair + 1];
+  if (valid != 1 || np != a.batch * a.hkv) {
     dst[t] = __int_as_float(0x7FC00000);  // NaN: the cache did not validate
     return;
   }
-  const int P = wsh[1];
-  const int i0 = wsh[16 + pair], i1 = wsh[16 + pair + 1];
-  const float* part = a.ws + ws_part_offset(P) / 4;
+  const float* part = a.ws + ws_part_offset(np) / 4;
   auto rowp = [&](int it) { return part + ((int64_t)it * G + row) * (D + 4); };
-  // maximum of the partials' m
-  float mx = -INFINITY;
-  for (int it = i0 + t; it < i1; it += D) mx = fmaxf(mx, rowp(it)[D]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) red[wv] = mx;
-  __syncthreads();
-  mx = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
-  __syncthreads();
-  float l = 0.0f, o = 0.0f;
+  float o = 0.0f, lsum = 0.0f;
+  float M = -INFINITY;  // maximum over all slots (first chunk's pass computes it for <= D slots)
   for (int base = i0; base < i1; base += D) {
     const int n = i1 - base < D ? i1 - base : D;
-    if (t < n) {
-      const float* pp = rowp(base + t);
-      const float m = pp[D];
-      const float f = m == -INFINITY ? 0.0f : exp2f(m - mx);
-      fs[t] = f;
-      l += pp[D + 1] * f;
-    }
+    // slot base + t's (m, l), and the first BO slots' column t, all in flight
+    float2 ml = make_float2(-INFINITY, 0.0f);
+    if (t < n) ml = *reinterpret_cast<const float2*>(rowp(base + t) + D);
+    float oc[BO];
+#pragma unroll
+    for (int j = 0; j < BO; ++j) oc[j] = rowp(base + (j < n ? j : 0))[t];
+    float mx = ml.x;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+    if (lane == 0) red[0][wv] = mx;
     __syncthreads();
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) o += fs[j] * rowp(base + j)[t];
+    mx = red[0][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[0][w]);
+    // fold the running sums into the new maximum (exact powers of two apart, or 0)
+    const float Mn = fmaxf(M, mx);
+    const float fo = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+    o *= fo;
+    lsum *= fo;
+    M = Mn;
+    const float f = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
+    fs[t] = f;
+    lsum += t < n ? ml.y * f : 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < BO; ++j) o += j < n ? fs[j] * oc[j] : 0.0f;
+    for (int j = BO; j < n; ++j) o += fs[j] * rowp(base + j)[t];
     __syncthreads();
   }
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) l += __shfl_xor(l, s);
-  if (lane == 0) red[wv] = l;
+  for (int s = 32; s >= 1; s >>= 1) lsum += __shfl_xor(lsum, s);
+  if (lane == 0) red[1][wv] = lsum;
   __syncthreads();
-  l = 0.0f;
+  float l = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) l += red[w];
+  for (int w = 0; w < NW; ++w) l += red[1][w];
   dst[t] = o / l;
 }
 
