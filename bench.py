@@ -181,10 +181,10 @@ def main():
         return float(np.mean(ts)), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
     sched_dev.copy_(torch.from_numpy(sched_np.view(np.uint8)))
-    if args.only == "prefill":   # profiler run: a few prefill launches only
-        for _ in range(args.steps):
+    if args.only == "prefill":   # profiler run: a few prefill launches only, each
+        for _ in range(args.steps):   # synchronised as in the timed loop below
             tria.prefill(dims, sched_dev, qz, v, sm, out=out)
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         print("done", flush=True)
         return
     if args.only == "copy":      # profiler calibration: a plain 1 GiB device copy
