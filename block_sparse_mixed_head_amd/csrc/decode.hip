@@ -395,6 +395,12 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
   // inside the loop (nothing loaded before it is used in it), which keeps the
   // compiler's wait counts exact; computes outside [j0, j1) are skipped.
   for (int j = j0; j < j1 + 2; j += 3) {
+    // The two work groups sharing a CU would otherwise run at fixed relative
+    // priority (the older wave issues first), so the second one's waves finish their
+    // equal share well after the first one's.  Alternating the issue priority per
+    // ring trip, out of phase between the halves of the grid, shares the SIMD fairly.
+    if (((j / 3) + (blockIdx.x >= gridDim.x / 2)) & 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     ld(A, j);
     if (j - 2 >= j0 && j - 2 < j1) compute_step<D, RG, IS4>(B, qop, ar, mfrom(j - 2), st, kq, slot);
     ld(B, j + 1);
