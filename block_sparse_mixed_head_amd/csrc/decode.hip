@@ -47,11 +47,13 @@ constexpr int kGrid = 512;                  // persistent work groups (two per C
 constexpr int kMaxWaves = kGrid * kWaves;
 constexpr int kMaxPairs = 4096;             // directory entries handled in LDS
 
-// workspace: [0,64) header {valid, n_pairs, n_slots, n_waves}; [64, 64 + 4*(P+1))
-// slot prefix per pair; partials from ws_part_offset: [slot][row][D + 4] floats
-// (o[0..D), m, l, 0, 0).
+// workspace: [0,64) header {valid, n_pairs, n_slots, n_waves}; [64, 64 + 8*P) per pair
+// {first slot, slot count}; partials from ws_part_offset: [slot][row][D + 4] floats
+// (o[0..D), m, l, 0, 0).  Wavefront w writes pair p's partial to slot p + w: the
+// wavefronts of consecutive pairs share at most one wavefront, so the slots of
+// different (pair, wavefront) are distinct and fewer than W + P.
 __host__ __device__ inline int64_t ws_part_offset(int64_t pairs) {
-  return (64 + 4 * (pairs + 1) + 255) / 256 * 256;
+  return (64 + 8 * pairs + 255) / 256 * 256;
 }
 
 struct DecArgs {
@@ -85,34 +87,33 @@ __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
          geo.total <= a.cache_bytes && h64[6] == 64 && h64[7] == geo.data_offset;
 }
 
-// Exclusive prefix over the work group of one value per thread; returns the
-// prefix and sets `total`.  `tmp` holds kWaves ints; ends with a barrier.
-__device__ __forceinline__ int block_scan(int x, int* tmp, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = tmp[w];
-    before += w < wave ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + incl - x;
+// Inclusive prefix sum over the wavefront: DPP row shifts (1, 2, 4, 8) within each
+// row of 16 lanes, then the row broadcasts of lane 15 (into rows 1 and 3) and of
+// lane 31 (into rows 2 and 3).  Lanes without a source add the old value 0.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// floor(n / d) for 0 <= n < 2^52 and 0 < d < 2^52: the double quotient is within one
+// of the exact one (both operands are exact doubles), then corrected by one
+// comparison each way with exact 64-bit products.
+__device__ __forceinline__ int64_t floor_div(int64_t n, int64_t d) {
+  int64_t q = (int64_t)((double)n / (double)d);
+  if (q * d > n) --q;
+  else if ((q + 1) * d <= n) ++q;
+  return q;
 }
 
 // Owner of unit u among W wavefronts splitting U units: the largest w with
 // floor(U*w/W) <= u.
 __device__ __forceinline__ int owner_of(int64_t u, int64_t U, int64_t W) {
-  return (int)(((u + 1) * W - 1) / U);
+  return (int)floor_div((u + 1) * W - 1, U);
 }
 
 // Register buffers of one 32-token step.  Lane (lr, kq) holds, for S^T subtile s
@@ -413,15 +414,7 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
 // block_scan of two values at once (same barriers); tmp holds 2 * kWaves ints.
 __device__ __forceinline__ int2 block_scan2(int x, int y, int* tmp, int& tx, int& ty) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int ix = x, iy = y;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(ix, o), b = __shfl_up(iy, o);
-    if (lane >= o) {
-      ix += a;
-      iy += b;
-    }
-  }
+  const int ix = wave_scan_incl(x), iy = wave_scan_incl(y);
   if (lane == 63) {
     tmp[wave] = ix;
     tmp[kWaves + wave] = iy;
@@ -463,28 +456,13 @@ __device__ __forceinline__ void prefix2_lds(int* arr, int* brr, int P, int* tmp)
   __syncthreads();
 }
 
-// In-place exclusive prefix of arr[0..P), arr[P] = total (chunks of the group size).
-__device__ __forceinline__ void prefix_lds(int* arr, int P, int* tmp) {
-  int carry = 0;
-  for (int base = 0; base < P; base += kThreads) {
-    const int p = base + (int)threadIdx.x;
-    const int x = p < P ? arr[p] : 0;
-    int tot;
-    const int e = block_scan(x, tmp, tot);
-    if (p < P) arr[p] = carry + e;
-    carry += tot;
-  }
-  if (threadIdx.x == 0) arr[P] = carry;
-  __syncthreads();
-}
-
 template <int D, int BLK, int RG>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RG == 1 ? 2 : 1, 2)))
 decode_split_kernel(DecArgs a) {
   constexpr int KS = D / 64, ND = D / 16, SPB = BLK / 32;
   __shared__ int n8p[kMaxPairs + 1];  // int8 records per pair, then their exclusive prefix
   __shared__ int n4p[kMaxPairs + 1];  // int4 records per pair, then their exclusive prefix
-  __shared__ int slp[kMaxPairs + 1];  // partial slots per pair, then their exclusive prefix
+  __shared__ int first[kWaves];      // the pair holding each wavefront's first unit
   __shared__ int tmp[2 * kWaves];
   __shared__ int bad;
   __shared__ __attribute__((aligned(16))) float scl[kWaves][64];  // per-wave step scales
@@ -541,50 +519,48 @@ decode_split_kernel(DecArgs a) {
   auto units_at = [&](int p) -> int64_t { return (int64_t)SPB * (2 * (int64_t)n8p[p] + n4p[p]); };
   const int64_t U = uni64(units_at(P));
   const int64_t W = (int64_t)gridDim.x * kWaves < U / 2 ? (int64_t)gridDim.x * kWaves : U / 2;
-  // records are contiguous in (b, g) order; pair p gets one partial slot per
-  // wavefront owning one of its steps
+  // wavefront w owns the units [floor(U w / W), floor(U (w + 1) / W))
+  int64_t wlo[kWaves];
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) wlo[i] = floor_div(U * ((int64_t)blockIdx.x * kWaves + i), W);
+  int* wsh = reinterpret_cast<int*>(a.ws);
+  // records are contiguous in (b, g) order: check every pair's offset, find the pair
+  // holding each of this work group's first units, and (work group 0) publish each
+  // pair's slot range: the wavefronts owning its first and last step starts, every
+  // one in between owning at least one (W <= U / 2: ranges of >= 2 units)
   for (int p = tid; p < P; p += kThreads) {
     v4i e[3];
     entry(p, e);
     const int64_t off = (int64_t)(((uint64_t)(uint32_t)e[0][1] << 32) | (uint32_t)e[0][0]);
     if (off != geo.data_offset + (int64_t)n8p[p] * geo.rec8 + (int64_t)n4p[p] * geo.rec4) bad = 1;
     const int64_t u0 = units_at(p), u1 = units_at(p + 1);
-    const int64_t last = n4p[p + 1] > n4p[p] ? u1 - 1 : u1 - 2;  // start of the pair's last step
-    slp[p] = U >= 4 ? owner_of(last, U, W) - owner_of(u0, U, W) + 1 : 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i)
+      if (wlo[i] >= u0 && wlo[i] < u1) first[i] = p;
+    if (blockIdx.x == 0 && U >= 4) {
+      const int64_t last = n4p[p + 1] > n4p[p] ? u1 - 1 : u1 - 2;  // start of the pair's last step
+      const int o0 = owner_of(u0, U, W), o1 = owner_of(last, U, W);
+      *reinterpret_cast<int2*>(wsh + 16 + 2 * p) = make_int2(o0 + p, o1 - o0 + 1);
+    }
   }
   __syncthreads();
   if (bad || U < 4 || geo.data_offset + (int64_t)n8p[P] * geo.rec8 + (int64_t)n4p[P] * geo.rec4 > geo.total) {
-    if (blockIdx.x == 0 && tid == 0) reinterpret_cast<int*>(a.ws)[0] = 0;
+    if (blockIdx.x == 0 && tid == 0) wsh[0] = 0;
     return;
   }
-  prefix_lds(slp, P, tmp);
-  if (blockIdx.x == 0) {
-    int* wsh = reinterpret_cast<int*>(a.ws);
-    if (tid == 0) {
-      wsh[0] = 1;
-      wsh[1] = P;
-      wsh[2] = slp[P];
-      wsh[3] = (int)W;
-    }
-    for (int p = tid; p <= P; p += kThreads) wsh[16 + p] = slp[p];
+  if (blockIdx.x == 0 && tid == 0) {
+    wsh[0] = 1;
+    wsh[1] = P;
+    wsh[2] = (int)W + P;
+    wsh[3] = (int)W;
   }
   float* part = a.ws + ws_part_offset(P) / 4;
 
   // ---- this wavefront's steps
   const int64_t w = (int64_t)blockIdx.x * kWaves + uni(wave);
   if (w >= W) return;
-  const int64_t lo = U * w / W, hi = U * (w + 1) / W;
-  // the pair holding unit lo
-  int p;
-  {
-    int l0 = 0, h0 = P - 1;
-    while (l0 < h0) {
-      const int mid = (l0 + h0 + 1) >> 1;
-      if (units_at(mid) <= lo) l0 = mid;
-      else h0 = mid - 1;
-    }
-    p = uni(l0);
-  }
+  const int64_t lo = uni64(wlo[wave]), hi = floor_div(U * (w + 1), W);
+  int p = uni(first[wave]);
   for (; p < P && uni64(units_at(p)) < hi; ++p) {
     const int64_t u0 = uni64(units_at(p));
     const int n8 = uni(n8p[p + 1] - n8p[p]), n4 = uni(n4p[p + 1] - n4p[p]);
@@ -596,7 +572,7 @@ decode_split_kernel(DecArgs a) {
     const int64_t base4 = u0 + 2LL * s8;
     const int j4a = clampn(lo - base4, s4), j4b = clampn(hi - base4, s4);
     if (j8a >= j8b && j4a >= j4b) continue;
-    const int slot = uni(slp[p]) + (int)(w - owner_of(u0, U, W));
+    const int slot = p + (int)w;
     const int b = p / a.hkv, gkv = p % a.hkv;
     const uint8_t* rec0 =
         a.cache + geo.data_offset + (int64_t)uni(n8p[p]) * geo.rec8 + (int64_t)uni(n4p[p]) * geo.rec4;
@@ -707,7 +683,9 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   const int* wsh = reinterpret_cast<const int*>(a.ws);
   float* dst = a.out + (int64_t)bh * D;
   // header and slot range in one round (the workspace holds them for every pair)
-  const int valid = wsh[0], np = wsh[1], i0 = wsh[16 + pair], i1 = wsh[16 + pair + 1];
+  const int valid = wsh[0], np = wsh[1];
+  const int2 range = *reinterpret_cast<const int2*>(wsh + 16 + 2 * pair);
+  const int i0 = range.x, i1 = range.x + range.y;
   if (valid != 1 || np != a.batch * a.hkv) {
     dst[t] = __int_as_float(0x7FC00000);  // NaN: the cache did not validate
     return;
