@@ -85,13 +85,20 @@ __device__ __forceinline__ void quantize8(const float x[8], uint32_t codes8[2], 
 
 // Maximum / sum over lanes l and l ^ 16, l ^ 32 (gfx950 lane-swap instructions:
 // VALU, no LDS round trip).
+// max(a, b) for non-NaN operands as one v_max_f32: fmaxf would first quiet both
+// operands (they come from lane permutes, which the compiler cannot prove canonical)
+__device__ __forceinline__ float max_nonan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float xmax16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xmax32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nonan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xsum16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -415,7 +415,9 @@ __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4
     const bool up = Mc > rs[g].M + kSlack;
     need = need || up;
     const float Mn = up ? Mc : rs[g].M;
-    f[g] = up ? exp2f(rs[g].M - Mn) : 1.0f;  // exact power of two; 0 on the first stage
+    // M - Mn: an integer <= 0 (or -inf on the first stage), so the raw hardware exp2
+    // is exact (a factor below 2^-126 only scales away what it multiplies)
+    f[g] = up ? __builtin_amdgcn_exp2f(rs[g].M - Mn) : 1.0f;
     rs[g].M = Mn;
     rs[g].l *= f[g];
     nM[g] = -Mn;
