@@ -63,6 +63,7 @@ struct Cfg {
   static constexpr int VCH = D / 8;     // 16-byte chunks per bf16 V row
   static constexpr int VU = D / 16;     // 32-byte units per bf16 V row
   static constexpr int ND = D / 16;     // 16-wide output column groups
+  static constexpr int NO = ND + 1;     // output tiles: the ND column groups, then the row sums
   static constexpr int K_BYTES = SK * D;      // one K slot (int8; int4 uses half)
   static constexpr int V_BYTES = SK * D * 2;  // one V slot
   static constexpr int K8_INSTR = K_BYTES / 1024;  // 1 KB load instructions per stage
@@ -213,7 +214,7 @@ struct LaneOffsets {
 };
 
 struct RowState {
-  float M, l, a8, a4;
+  float M, a8, a4;
   int row;  // row index inside the q-block
 };
 
@@ -304,14 +305,27 @@ __device__ __forceinline__ v8bf pv_read(const lds_u8* vslot, const LaneOffsets<D
   return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo16, hi16, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 template <int D, int BLK, int t, int d>
-__device__ __forceinline__ void pv_mma(const v8bf& vop, const v8bf (&pb)[2][2], v4f (&O)[2][Cfg<D, BLK>::ND]) {
+__device__ __forceinline__ void pv_mma(const v8bf& vop, const v8bf (&pb)[2][2], v4f (&O)[2][Cfg<D, BLK>::NO]) {
   O[0][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[0][t], O[0][d], 0, 0, 0);
   O[1][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[1][t], O[1][d], 0, 0, 0);
 }
 template <int D, int BLK, int t, int d>
 __device__ __forceinline__ void pv_group(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo, const v8bf (&pb)[2][2],
-                                         v4f (&O)[2][Cfg<D, BLK>::ND]) {
+                                         v4f (&O)[2][Cfg<D, BLK>::NO]) {
   pv_mma<D, BLK, t, d>(pv_read<D, BLK, t, d>(vslot, lo), pb, O);
+}
+// Row sums l += sum_k P[q][k] on the matrix cores: an all-ones A operand in place of
+// V^T gives every row of tile ND the sum over the stage's keys of each query's bf16
+// weights (the same bf16 values the product uses).
+template <int D, int BLK>
+__device__ __forceinline__ void pv_rowsum(const v8bf (&pb)[2][2], v4f (&O)[2][Cfg<D, BLK>::NO]) {
+  constexpr int ND = Cfg<D, BLK>::ND;
+  const v8bf ones = __builtin_bit_cast(v8bf, v4i{0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80});
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    O[0][ND] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][t], O[0][ND], 0, 0, 0);
+    O[1][ND] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][t], O[1][ND], 0, 0, 0);
+  }
 }
 
 // Softmax of stage s interleaved with the P.V product of stage s-1.
@@ -339,7 +353,7 @@ template <int D, int BLK, bool QK4, bool DIAG, class Between>
 __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4f (&ksc)[4],
                                               int key_base, RowState (&rs)[2], v8bf (&pcur)[2][2], float (&f)[2],
                                               const v8bf (&pprev)[2][2], const lds_u8* vslot,
-                                              const LaneOffsets<D, BLK>& lo, v4f (&O)[2][Cfg<D, BLK>::ND], int kq,
+                                              const LaneOffsets<D, BLK>& lo, v4f (&O)[2][Cfg<D, BLK>::NO], int kq,
                                               const lds_u8* kslot, const QCodes<D>& q, Between&& between) {
   using C = Cfg<D, BLK>;
   constexpr int NG = 2 * C::ND;  // product groups
@@ -363,7 +377,8 @@ __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4
       constexpr int i = decltype(idx)::value, t = i / C::ND, d = i % C::ND;
       pv_mma<D, BLK, t, d>(vop[i - NG * K / 3], pprev, O);
     });
-    interleave<0, 2 * NGK, (K < 2 ? 4 : 2), 0>();
+    if constexpr (K == 2) pv_rowsum<D, BLK>(pprev, O);
+    interleave<0, 2 * NGK + (K == 2 ? 4 : 0), (K < 2 ? 4 : 2), 0>();
     __builtin_amdgcn_sched_barrier(0);
     between(k);
     __builtin_amdgcn_sched_barrier(0);
@@ -419,16 +434,13 @@ __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4
     // is exact (a factor below 2^-126 only scales away what it multiplies)
     f[g] = up ? __builtin_amdgcn_exp2f(rs[g].M - Mn) : 1.0f;
     rs[g].M = Mn;
-    rs[g].l *= f[g];
     nM[g] = -Mn;
   }
   pv_part(std::integral_constant<int, 2>());
-  // phases 3, 4: weights of row groups 0 and 1, their sums, the B operand layout
-  const v2bf one = {(__bf16)1.0f, (__bf16)1.0f};
+  // phases 3, 4: weights of row groups 0 and 1 in the B operand layout
   auto weights = [&](auto gtag) __attribute__((always_inline)) {
     constexpr int g = decltype(gtag)::value;
     const float ag = is4 ? rs[g].a4 : rs[g].a8;
-    float l = rs[g].l;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       v2bf x[4];
@@ -441,16 +453,12 @@ __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4
                          __builtin_amdgcn_exp2f(fmaf(u[g][s][3], ag, nM[g]))};
         x[2 * half] = __builtin_convertvector(p01, v2bf);
         x[2 * half + 1] = __builtin_convertvector(p23, v2bf);
-        l = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half], one, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(x[2 * half + 1], one, l, false);
       }
       // keys 16*(2t) + 4kq + 0..3, then 16*(2t+1) + 4kq + 0..3: the B operand's k order
       pcur[g][t] = __builtin_shufflevector(__builtin_shufflevector(x[0], x[1], 0, 1, 2, 3),
                                            __builtin_shufflevector(x[2], x[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
       asm volatile("" : "+v"(pcur[g][t]));  // pinned to this phase (see scores)
     }
-    asm volatile("" : "+v"(l));
-    rs[g].l = l;
   };
   // regions 3, 4: the next stage's K reads, then the weights of one row group, then
   // half of the next stage's score MFMAs, interleaved with the weights
@@ -472,12 +480,13 @@ __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4
 // O^T += V^T . P^T for one stage (the last one, after the loop).
 template <int D, int BLK>
 __device__ __forceinline__ void pv_stage(const lds_u8* vslot, const LaneOffsets<D, BLK>& lo, const v8bf (&pb)[2][2],
-                                         v4f (&O)[2][Cfg<D, BLK>::ND]) {
+                                         v4f (&O)[2][Cfg<D, BLK>::NO]) {
   using C = Cfg<D, BLK>;
   unroll<0, 2 * C::ND>([&](auto idx) __attribute__((always_inline)) {
     constexpr int t = decltype(idx)::value / C::ND, d = decltype(idx)::value % C::ND;
     pv_group<D, BLK, t, d>(vslot, lo, pb, O);
   });
+  pv_rowsum<D, BLK>(pb, O);
 }
 
 template <int D, int BLK>
@@ -591,7 +600,7 @@ prefill_kernel(Args a) {
   // the block's query codes (rows past the end as zeros)
   QCodes<D> q;
   RowState rs[2];
-  v4f O[2][C::ND];
+  v4f O[2][C::NO];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     rs[g].row = wave * 32 + g * 16 + lr;
@@ -608,9 +617,8 @@ prefill_kernel(Args a) {
     rs[g].a8 = fmaxf(sq8 * a.c, FLT_MIN);
     rs[g].a4 = fmaxf(sq4 * a.c * (1.0f / 256.0f), FLT_MIN);
     rs[g].M = -INFINITY;
-    rs[g].l = 0.0f;
 #pragma unroll
-    for (int d = 0; d < C::ND; ++d) O[g][d] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < C::NO; ++d) O[g][d] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // every load above complete
   __syncthreads();
@@ -665,7 +673,7 @@ prefill_kernel(Args a) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int d = 0; d < C::ND; ++d) O[g][d] *= f[g];
+        for (int d = 0; d < C::NO; ++d) O[g][d] *= f[g];
     }
     read_key_scales(sslot(R1), kq, ksc);
 #pragma unroll
@@ -696,9 +704,7 @@ prefill_kernel(Args a) {
   // ---- epilogue: normalise and store (fp32), optional base-2 LSE
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    float l = rs[g].l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = O[g][C::ND][0];  // the row sum (every row of the sums tile)
     const int64_t qi = (int64_t)qb * BLK + rs[g].row;
     if (qi < n) {
       const float inv = 1.0f / l;
