@@ -557,8 +557,12 @@ prefill_kernel(Args a) {
   };
   // rows of the stage inside the sequence (0 for a stage past the last one)
   auto rows_of = [&](bool valid, int key0) __attribute__((always_inline)) {
-    const int rem = n32 - key0;
-    return !valid ? 0 : (rem < C::SK ? (rem > 0 ? rem : 0) : C::SK);
+    // clamp(n - key0, 0, SK) on the scalar unit: as plain min/max the compiler forms
+    // a v_med3_i32 and moves the result back with v_readfirstlane
+    int rows;
+    asm("s_sub_i32 %0, %1, %2\n\ts_max_i32 %0, %0, 0\n\ts_min_i32 %0, %0, %3"
+        : "=&s"(rows) : "s"(n32), "s"(key0), "i"(C::SK) : "scc");
+    return valid ? rows : 0;
   };
   auto issue_k = [&](int st, lds_u8* kd, lds_f32* sd) __attribute__((always_inline)) {
     const bool valid = st < nstages;
