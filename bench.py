@@ -268,6 +268,33 @@ def main():
         print(json.dumps({"decode": dec}))
         return
 
+    # ------------------------------------------------------------ measured ceilings
+    # What the part sustains for the instructions and access pattern the kernels use
+    # (MFMA issue loops, a non-temporal streaming read of 1 GiB), so the fractions can
+    # also be read against measured ceilings; the roofline object keeps the published
+    # peaks.
+    sink = torch.zeros(tria._lib.PEAK_SINK_INTS, dtype=torch.int32, device="cuda")
+    rd_src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    iters = 20000
+    w_i8, w_bf, w_rd = tria.peak_mfma(0, iters, sink), tria.peak_mfma(1, iters, sink), tria.peak_read(rd_src, sink)
+    t_i8 = event_avg(lambda: tria.peak_mfma(0, iters, sink), 5)[1]
+    t_bf = event_avg(lambda: tria.peak_mfma(1, iters, sink), 5)[1]
+    t_rd = event_avg(lambda: tria.peak_read(rd_src, sink), 10)[1]
+    del rd_src
+    i8, bf, rd = w_i8 / t_i8 / 1e12, w_bf / t_bf / 1e12, w_rd / t_rd / 1e9
+    blend = 2.0 / (1.0 / i8 + 1.0 / bf)  # equal int8 ops and bf16 flops, in series
+    ceilings = {
+        "mfma_i8_tops": i8, "mfma_bf16_tflops": bf, "mfma_series_blend_tflops": blend, "hbm_read_gbps": rd,
+        "prefill_frac": achieved / blend,
+        "decode_frac": dec["GB_per_s"] / rd if dec else None,
+        "method": "median of 5 launches of 512 work groups x 4 wavefronts, each wavefront issuing "
+                  f"{iters} rounds of 8 independent v_mfma_i32_16x16x64_i8 / v_mfma_f32_16x16x32_bf16; "
+                  "median of 10 non-temporal streaming reads of 1 GiB (8192 wavefronts, one contiguous "
+                  "range each, 1 KB loads, 8 in flight)",
+    }
+    log(f"[bench] measured ceilings: int8 {i8:.0f} TOPS, bf16 {bf:.0f} TFLOPS, read {rd:.0f} GB/s; "
+        f"prefill {achieved / blend:.3f}, decode {ceilings['decode_frac'] or 0:.3f} of them")
+
     # ------------------------------------------------------------ CPU baseline (the oracle, sampled)
     cpu = None
     if not args.no_cpu_baseline:
@@ -323,6 +350,7 @@ def main():
         "kernels_ms": {"quantize": q_mean * 1e3, "prefill": p_mean * 1e3, "pack": k_mean * 1e3,
                        "decode_step_workload": d_mean * 1e3},
         "decode": dec,
+        "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

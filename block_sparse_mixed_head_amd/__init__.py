@@ -23,7 +23,8 @@ from . import _lib
 from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
 __all__ = ["Dims", "build_policy", "quantize_qk", "prefill", "kv_cache_bytes", "pack_kv_cache",
-           "check_cache", "decode_workspace_bytes", "decode", "TriaError", "Quantized"]
+           "check_cache", "decode_workspace_bytes", "decode", "peak_mfma", "peak_read", "TriaError",
+           "Quantized"]
 
 Dims = _lib.Dims
 
@@ -156,3 +157,23 @@ def decode(d: Dims, cache: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale
     check(_lib.lib.tria_decode(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(q), float(sm_scale),
                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out
+
+
+# ------------------------------------------------------------------ measured ceilings
+def peak_mfma(kind: int, iters: int, sink: torch.Tensor) -> float:
+    """Enqueues the MFMA issue loop (kind 0: int8 16x16x64, 1: bf16 16x16x32) on the
+    current stream of sink's device; returns the int8 ops (bf16 flops) of the launch."""
+    _require(sink, torch.int32, (_lib.PEAK_SINK_INTS,), "sink")
+    work = C.c_double(0.0)
+    check(_lib.lib.tria_peak_mfma(int(kind), int(iters), _ptr(sink), C.byref(work), _stream(sink.device)))
+    return work.value
+
+
+def peak_read(src: torch.Tensor, sink: torch.Tensor) -> float:
+    """Enqueues the streaming read of all of src (uint8, a multiple of 64 MiB) on the
+    current stream of its device; returns the bytes read."""
+    _require(src, torch.uint8, (src.numel(),), "src")
+    _require(sink, torch.int32, (_lib.PEAK_SINK_INTS,), "sink")
+    work = C.c_double(0.0)
+    check(_lib.lib.tria_peak_read(_ptr(src), src.numel(), _ptr(sink), C.byref(work), _stream(src.device)))
+    return work.value

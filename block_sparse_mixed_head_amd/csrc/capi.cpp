@@ -382,4 +382,25 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
                   "decode launch");
 }
 
+tria_status tria_peak_mfma(int32_t kind, int32_t iters, int32_t* sink, double* work, void* stream) {
+  NONNULL(sink);
+  NONNULL(work);
+  if (kind != 0 && kind != 1) return fail(TRIA_ERR_INVALID_ARG, "kind must be 0 (int8) or 1 (bf16)");
+  if (iters < 1) return fail(TRIA_ERR_INVALID_ARG, "iters must be >= 1");
+  *work = tria::peak_mfma_work(kind, iters);
+  return launched(tria::launch_peak_mfma(kind, iters, sink, static_cast<hipStream_t>(stream)), "peak mfma launch");
+}
+
+tria_status tria_peak_read(const void* src, int64_t bytes, int32_t* sink, double* work, void* stream) {
+  NONNULL(src);
+  NONNULL(sink);
+  NONNULL(work);
+  const int64_t align = tria::peak_read_align();
+  if (bytes <= 0 || bytes % align != 0)
+    return fail(TRIA_ERR_INVALID_ARG, "bytes must be a positive multiple of %lld", (long long)align);
+  if (bytes / TRIA_PEAK_READ_WAVES > INT32_MAX) return fail(TRIA_ERR_UNSUPPORTED, "bytes too large");
+  *work = (double)bytes;
+  return launched(tria::launch_peak_read(src, bytes, sink, static_cast<hipStream_t>(stream)), "peak read launch");
+}
+
 }  // extern "C"

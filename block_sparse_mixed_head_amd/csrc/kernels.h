@@ -49,4 +49,11 @@ int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len);
 hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
                          const void* q, float sm_scale, float* out, void* workspace, hipStream_t stream);
 
+// Measured ceilings (peaks.hip): an MFMA issue loop (kind 0: i8 16x16x64, 1: bf16
+// 16x16x32) and a non-temporal streaming read.  Work of one launch in ops / flops.
+double peak_mfma_work(int kind, int iters);
+hipError_t launch_peak_mfma(int kind, int iters, int* sink, hipStream_t stream);
+int64_t peak_read_align();
+hipError_t launch_peak_read(const void* src, int64_t bytes, int* sink, hipStream_t stream);
+
 }  // namespace tria

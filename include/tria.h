@@ -259,6 +259,31 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
                         int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
                         void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- Measured ceilings (measurement helpers, not part of the method) ---------
+ * Loops that bound what the part sustains for the instructions and the access
+ * pattern the kernels above use, so roofline fractions can be read against
+ * measured ceilings as well as against published peaks.  Each call validates its
+ * arguments, stores the work of one launch in *work (host) and enqueues the loop on
+ * `stream`; the caller times it with events on that stream.
+ * tria_peak_mfma: kind 0 = v_mfma_i32_16x16x64_i8 (*work in int8 ops), kind 1 =
+ *   v_mfma_f32_16x16x32_bf16 (*work in flops); 512 work groups of four wavefronts,
+ *   each wavefront issuing `iters` rounds of eight independent MFMAs; no memory
+ *   traffic.
+ * tria_peak_read: reads `bytes` of device memory at src once (TRIA_PEAK_READ_WAVES
+ *   wavefronts, each one contiguous range, 1 KB non-temporal loads, eight in
+ *   flight); bytes must be a positive multiple of TRIA_PEAK_READ_ALIGN; *work = bytes.
+ * sink: device int32[TRIA_PEAK_SINK_INTS], written by the loops (so that their
+ *   results are used); its contents are meaningless.
+ * Errors: TRIA_ERR_INVALID_ARG for a null pointer, kind not 0 or 1, iters < 1 or a
+ * size that is not a positive multiple of TRIA_PEAK_READ_ALIGN;
+ * TRIA_ERR_UNSUPPORTED when bytes / TRIA_PEAK_READ_WAVES exceeds 2^31 - 1.
+ */
+#define TRIA_PEAK_READ_WAVES 8192
+#define TRIA_PEAK_READ_ALIGN (8192LL * 8 * 1024)
+#define TRIA_PEAK_SINK_INTS 8192
+tria_status tria_peak_mfma(int32_t kind, int32_t iters, int32_t* sink, double* work, void* stream);
+tria_status tria_peak_read(const void* src, int64_t bytes, int32_t* sink, double* work, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,19 @@ def test_validation_errors(tria):
     mqa = tria.make_dims(1, 64, 1, 64, 64, 512)
     assert L.tria_decode(C.byref(mqa), one, 1 << 20, 512, one, C.c_float(0.125), one, one, 1 << 30,
                          None) == _lib.TRIA_ERR_UNSUPPORTED
+
+
+def test_peak_helpers_validate_arguments(tria):
+    """The measured-ceiling helpers check their arguments before any HIP call."""
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    work = C.c_double(0.0)
+    sink = C.c_void_p(16)
+    assert L.tria_peak_mfma(2, 10, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG   # kind
+    assert L.tria_peak_mfma(0, 0, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG    # iters
+    assert L.tria_peak_mfma(1, 10, None, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG   # sink
+    src = C.c_void_p(4096)
+    assert L.tria_peak_read(src, _lib.PEAK_READ_ALIGN + 1, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_peak_read(src, 0, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_peak_read(None, _lib.PEAK_READ_ALIGN, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG
+

@@ -311,3 +311,31 @@ def test_decode_reuses_one_workspace(tria):
             o = tria.decode(dd, bad, ctx, qd, 0.125, workspace=ws)
             torch.cuda.synchronize()
             assert torch.isnan(o).all().item()
+
+
+@pytest.mark.gpu
+def test_measured_ceilings_are_plausible(tria):
+    """The MFMA loops and the streaming read run and give rates inside what the part
+    can do: at most its published peaks (int8 5.0 POPS, bf16 2.5 PFLOPS, HBM 8 TB/s),
+    at least a fifth of them."""
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+
+    def rate(enqueue):
+        work = enqueue()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        work = enqueue()
+        e1.record()
+        e1.synchronize()
+        return work / (e0.elapsed_time(e1) * 1e-3)
+
+    i8 = rate(lambda: tria.peak_mfma(0, 2000, sink))
+    bf = rate(lambda: tria.peak_mfma(1, 2000, sink))
+    rd = rate(lambda: tria.peak_read(src, sink))
+    print(f"int8 {i8 / 1e12:.0f} TOPS, bf16 {bf / 1e12:.0f} TFLOPS, read {rd / 1e9:.0f} GB/s", flush=True)
+    assert 1.0e15 <= i8 <= 5.0e15
+    assert 0.5e15 <= bf <= 2.5e15
+    assert 1.6e12 <= rd <= 8.0e12
+
