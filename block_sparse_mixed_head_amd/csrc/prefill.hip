@@ -178,9 +178,12 @@ struct LaneOffsets {
       const unsigned p = wave * 64 + lane, pc = p % C::KCH, r = p / C::KCH;
       gk8 = r * D + ((pc ^ (r & (C::KCH - 1))) << 4);
     }
-    {  // a wave past the int4 stage size never loads it (empty resource)
+    {  // a wave past the int4 stage size never loads it (empty resource).  Packed rows
+       // are D/2 bytes: the chunk swizzle follows row / 4, so the 16 rows one MFMA
+       // operand read touches spread over distinct banks (row mod 4 would repeat
+       // every four rows)
       const unsigned p = (wave < C::K4_INSTR ? wave : 0) * 64 + lane, pc = p % C::K4CH, r = p / C::K4CH;
-      gk4 = r * (D / 2) + ((pc ^ (r & (C::K4CH - 1))) << 4);
+      gk4 = r * (D / 2) + ((pc ^ ((r >> 2) & (C::K4CH - 1))) << 4);
     }
     {
       const unsigned p = wave * 64 + lane, pc = p % C::VCH, r = p / C::VCH;
@@ -188,11 +191,12 @@ struct LaneOffsets {
     }
     gs = lane * 4;
     // K row s*16 + lr, 16-byte chunk ks*4 + kq (int8) or 2ks + kq/2, half kq%2
-    // (int4); s*16 leaves the swizzle term (row mod chunks per row) unchanged
+    // (int4); s*16 leaves the swizzle terms (row, or row / 4, mod chunks per row)
+    // unchanged
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       k8[ks] = lr * D + ((((ks << 2) + kq) ^ (lr & (C::KCH - 1))) << 4);
-      k4[ks] = lr * (D / 2) + ((((ks << 1) + (kq >> 1)) ^ (lr & (C::K4CH - 1))) << 4) + (kq & 1) * 8;
+      k4[ks] = lr * (D / 2) + ((((ks << 1) + (kq >> 1)) ^ ((lr >> 2) & (C::K4CH - 1))) << 4) + (kq & 1) * 8;
     }
     // V row 32t + 16h + 4kq + lr/4, 32-byte unit d at (d ^ (row mod VU)); 32t + 16h
     // leaves the XOR term unchanged
