@@ -225,7 +225,6 @@ def main():
         k4d, v4d = dev(k4h), dev(v4h)
         del k4h, v4h
         cache4 = tria.pack_kv_cache(dims4, h4, kp4, c4.seq_len, k4d, v4d)
-        del k4d, v4d
         q4 = dev(q4h)
         ws4 = torch.empty(tria.decode_workspace_bytes(dims4, c4.seq_len), dtype=torch.uint8, device="cuda")
         o4 = torch.empty((c4.batch, c4.n_q_heads, c4.head_dim), dtype=torch.float32, device="cuda")
@@ -248,6 +247,17 @@ def main():
             return
         dm, dmed, d10, d90 = event_avg(run_dec, args.reps, before=flush_caches)
         warm = event_avg(run_dec, args.reps)[0]
+        # per-token cache maintenance on this workload: in place inside a block (token
+        # 32767), and at a block start (token 32640 opens block 255: records move to
+        # another buffer)
+        c_prev = tria.pack_kv_cache(dims4, h4, kp4, c4.seq_len - 1, k4d, v4d)
+        upd_in = event_avg(lambda: tria.update_kv_cache(dims4, h4, kp4, c4.seq_len, k4d, v4d, c_prev), args.reps)
+        s0 = (c4.seq_len // c4.block - 1) * c4.block
+        c_blk = tria.pack_kv_cache(dims4, h4, kp4, s0, k4d, v4d)
+        c_out = torch.empty(tria.kv_cache_bytes(dims4, h4, kp4, s0 + 1), dtype=torch.uint8, device="cuda")
+        upd_bs = event_avg(lambda: tria.update_kv_cache(dims4, h4, kp4, s0 + 1, k4d, v4d, c_blk, out=c_out),
+                           args.reps)
+        del c_prev, c_blk, c_out, k4d, v4d
         hdr = (64 + 64 * c4.batch * c4.n_kv_heads + 255) // 256 * 256
         dbytes = decode_bytes(cache4.numel(), c4.batch, c4.n_q_heads, c4.head_dim, hdr)
         dense_bytes = 2 * c4.batch * c4.n_kv_heads * c4.seq_len * c4.head_dim * 2
@@ -260,8 +270,11 @@ def main():
             "cache_flushed": True,
             "us_per_call_warm_cache": warm * 1e6,
             "dense_bf16_cache_bytes": dense_bytes,
+            "cache_update_us": {"in_place_within_block": upd_in[1] * 1e6, "at_block_start": upd_bs[1] * 1e6,
+                                "note": "median; tria_update_kv_cache for one more token (all 128 pairs)"},
         }
-        log(f"[bench] decode {dm * 1e6:.1f} us, {dec['GB_per_s']:.0f} GB/s (warm {warm * 1e6:.1f} us)")
+        log(f"[bench] decode {dm * 1e6:.1f} us, {dec['GB_per_s']:.0f} GB/s (warm {warm * 1e6:.1f} us); "
+            f"cache update {upd_in[1] * 1e6:.1f} us in place, {upd_bs[1] * 1e6:.1f} us at a block start")
         del cache4, flush
 
     if args.only is not None:

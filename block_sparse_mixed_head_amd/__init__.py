@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
-__all__ = ["Dims", "build_policy", "quantize_qk", "prefill", "kv_cache_bytes", "pack_kv_cache",
+__all__ = ["Dims", "build_policy", "quantize_qk", "prefill", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
            "check_cache", "decode_workspace_bytes", "decode", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
@@ -133,6 +133,28 @@ def pack_kv_cache(d: Dims, hi, keep, ctx_len: int, k: torch.Tensor, v: torch.Ten
     check(_lib.lib.tria_pack_kv_cache(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, _ptr(k),
                                       _ptr(v), _ptr(cache), cache.numel(), _stream(k.device)))
     return cache
+
+
+def update_kv_cache(d: Dims, hi, keep, ctx_len: int, k: torch.Tensor, v: torch.Tensor, cache: torch.Tensor,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The cache for ctx_len from `cache`, the one packed for ctx_len - 1 from the same
+    k, v and policy.  Within a block it is updated in place (returned as is); when
+    token ctx_len - 1 starts a new block the records move and the result goes to
+    `out` (allocated when None)."""
+    b, hk, hd, n = d.batch, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(k, torch.bfloat16, (b, hk, n, hd), "k")
+    _require(v, torch.bfloat16, (b, hk, n, hd), "v")
+    _require(cache, torch.uint8, (cache.numel(),), "cache")
+    hi, keep = _i32(hi), _i32(keep)
+    if (ctx_len - 1) % d.block != 0:
+        dst = cache
+    else:
+        dst = out if out is not None else torch.empty(kv_cache_bytes(d, hi, keep, ctx_len), dtype=torch.uint8,
+                                                      device=k.device)
+    check(_lib.lib.tria_update_kv_cache(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, _ptr(k),
+                                        _ptr(v), _ptr(cache), cache.numel(), _ptr(dst), dst.numel(),
+                                        _stream(k.device)))
+    return dst
 
 
 def check_cache(d: Dims, cache: torch.Tensor, ctx_len: int) -> None:

@@ -299,8 +299,48 @@ tria_status tria_pack_kv_cache(const tria_dims* dims, const int32_t* hi, const i
   const tria::CacheGeom g = cache_geom(dims, pol, ctx_len);
   if ((int64_t)cache_bytes < g.total_bytes)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache needs %lld bytes, got %zu", (long long)g.total_bytes, cache_bytes);
-  return launched(tria::launch_pack(shape_of(dims), pol, g, k_bf16, v_bf16, cache, static_cast<hipStream_t>(stream)),
+  return launched(tria::launch_pack(shape_of(dims), pol, g, k_bf16, v_bf16, cache, nullptr, nullptr, false,
+                                    static_cast<hipStream_t>(stream)),
                   "pack launch");
+}
+
+tria_status tria_update_kv_cache(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                 int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16, const void* v_bf16,
+                                 const void* cache_in, size_t cache_in_bytes, void* cache_out, size_t cache_out_bytes,
+                                 void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(k_bf16);
+  NONNULL(v_bf16);
+  NONNULL(cache_in);
+  NONNULL(cache_out);
+  if (ctx_len < 2 || ctx_len > dims->seq_len)
+    return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld outside [2, seq_len=%lld]", (long long)ctx_len,
+                (long long)dims->seq_len);
+  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
+    return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads above 65535");
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  const tria::CacheGeom g = cache_geom(dims, pol, ctx_len);
+  const tria::CacheGeom go = cache_geom(dims, pol, ctx_len - 1);
+  if ((int64_t)cache_in_bytes < go.total_bytes)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache_in must hold the %lld-byte cache for ctx_len - 1, got %zu",
+                (long long)go.total_bytes, cache_in_bytes);
+  if ((int64_t)cache_out_bytes < g.total_bytes)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache_out needs %lld bytes, got %zu", (long long)g.total_bytes,
+                cache_out_bytes);
+  const bool boundary = g.cur_block != go.cur_block;
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(cache_in), o0 = reinterpret_cast<uintptr_t>(cache_out);
+  const bool in_place = i0 == o0;
+  if (in_place && boundary)
+    return fail(TRIA_ERR_INVALID_ARG, "ctx_len - 1 = %lld starts a new block: records move, so cache_out must be "
+                "another buffer", (long long)(ctx_len - 1));
+  if (!in_place && i0 < o0 + (uintptr_t)g.total_bytes && o0 < i0 + (uintptr_t)go.total_bytes)
+    return fail(TRIA_ERR_INVALID_ARG, "cache_in and cache_out overlap without being the same buffer");
+  return launched(tria::launch_pack(shape_of(dims), pol, g, k_bf16, v_bf16, cache_out, cache_in, &go, in_place,
+                                    static_cast<hipStream_t>(stream)),
+                  "cache update launch");
 }
 
 tria_status tria_check_cache(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len) {

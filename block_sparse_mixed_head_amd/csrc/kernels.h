@@ -39,8 +39,13 @@ struct CacheGeom {
   int64_t total_bytes;
 };
 
+// Packs the cache for g.ctx_len.  Update mode (old_cache non-null): old_cache holds the
+// cache for old_geo->ctx_len = g.ctx_len - 1 with the same policy and K/V; records it
+// holds for the same block and precision are reused (skipped in place, else copied).
+// only_current: in place, same current block: only the new token's row (append kernel).
 hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& g, const void* k,
-                       const void* v, void* cache, hipStream_t stream);
+                       const void* v, void* cache, const void* old_cache, const CacheGeom* old_geo,
+                       bool only_current, hipStream_t stream);
 
 // Decode: split-KV partials into `workspace`, then a merge into `out`.
 // decode_units_fit: the work split counts 32-token units in int32.

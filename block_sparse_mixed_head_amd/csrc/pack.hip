@@ -21,6 +21,15 @@
 // group computes its record offset from the policy (every batch element has the
 // same layout because the policy is per KV head).  V codes go through LDS for the
 // transpose.
+//
+// Update (the cache for ctx_len from the one for ctx_len - 1, same policy and K/V):
+// a block's record depends only on its rows and its precision, so a record of a
+// block before the new current block that the old layout stored at the same
+// precision is reused (left alone in place at an unchanged offset, else copied);
+// every other record (the current block, a block demoted from int8 to int4) is
+// quantised from the bf16 rows as above.  Within a block nothing moves and only the
+// new token's row of the current block changes: in place, one wavefront per pair
+// quantises that K and V row and writes its bytes into the record (append kernel).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,6 +43,9 @@ struct PackArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint8_t* cache;
+  const uint8_t* old;  // update: the cache for ctx_len - 1 (else null), geometry ogeo
+  CacheGeom ogeo;
+  int only_current;    // update in place within the current block: the new token's row only
   int64_t n;  // token rows in the K/V source
   int batch, hkv;
   KvPolicy pol;
@@ -81,16 +93,21 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   __shared__ __attribute__((aligned(16))) int8_t vbuf[BLK][D];
   __shared__ float ksb[BLK], vsb[BLK];
 
-  const int pair = blockIdx.y, j = blockIdx.x;
+  const int pair = blockIdx.y;
   const int b = pair / a.hkv, g = pair % a.hkv;
   const int c = a.geo.cur_block;
   const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
+  const int j = blockIdx.x;
   if (j >= st.n8 + st.n4) return;
-  int64_t pair_off = a.geo.data_offset + (int64_t)b * a.geo.batch_bytes;
-  for (int gg = 0; gg < g; ++gg) {
-    const Blocks o = stored_blocks(c, a.pol.hi[gg], a.pol.keep[gg]);
-    pair_off += (int64_t)o.n8 * a.geo.rec8_bytes + (int64_t)o.n4 * a.geo.rec4_bytes;
-  }
+  auto pair_offset = [&](const CacheGeom& geo) {
+    int64_t off = geo.data_offset + (int64_t)b * geo.batch_bytes;
+    for (int gg = 0; gg < g; ++gg) {
+      const Blocks o = stored_blocks(geo.cur_block, a.pol.hi[gg], a.pol.keep[gg]);
+      off += (int64_t)o.n8 * geo.rec8_bytes + (int64_t)o.n4 * geo.rec4_bytes;
+    }
+    return off;
+  };
+  const int64_t pair_off = pair_offset(a.geo);
   const bool is4 = j >= st.n8;
   const int kb = !is4 ? ((st.sink && j == 0) ? 0 : st.lo8 + j - st.sink) : st.lo4 + (j - st.n8);
   const int64_t off = !is4 ? pair_off + (int64_t)j * a.geo.rec8_bytes
@@ -131,6 +148,28 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   if (pair == 0 && j == 0) {  // the padding between the directory and the first record
     const int64_t pad0 = 64 + 64LL * a.batch * a.hkv;
     for (int64_t i = pad0 + tid; i < a.geo.data_offset; i += kThreads) a.cache[i] = 0;
+  }
+
+  if (a.old != nullptr && kb < c) {  // update: reuse the old record when it has this block and precision
+    const Blocks so = stored_blocks(a.ogeo.cur_block, a.pol.hi[g], a.pol.keep[g]);
+    int jo = -1;
+    if (!is4) {
+      if (kb == 0 && so.sink) jo = 0;
+      else if (kb >= so.lo8 && kb <= a.ogeo.cur_block) jo = so.sink + kb - so.lo8;
+    } else if (kb >= so.lo4 && kb <= so.hi4) {
+      jo = so.n8 + kb - so.lo4;
+    }
+    if (jo >= 0) {
+      const int64_t opair = pair_offset(a.ogeo);
+      const int64_t ooff = !is4 ? opair + (int64_t)jo * a.ogeo.rec8_bytes
+                                : opair + (int64_t)so.n8 * a.ogeo.rec8_bytes + (int64_t)(jo - so.n8) * a.ogeo.rec4_bytes;
+      if (a.old == a.cache && ooff == off) return;  // in place, same bytes
+      const int64_t n16 = (!is4 ? a.geo.rec8_bytes : a.geo.rec4_bytes) / 16;
+      const uint4* src = reinterpret_cast<const uint4*>(a.old + ooff);
+      uint4* dst = reinterpret_cast<uint4*>(rec);
+      for (int64_t i = tid; i < n16; i += kThreads) dst[i] = src[i];
+      return;
+    }
   }
 
   const int64_t src0 = ((int64_t)b * a.hkv + g) * a.n;
@@ -242,8 +281,65 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   }
 }
 
+// In place within the current block: token t = ctx_len - 1 (row r of block c, chunk
+// r / 32, position tk = r % 32) is the only change.  Lanes [0, TPR) quantise its K
+// row, lanes [TPR, 2 TPR) its V row, eight dims each (the quantiser contract of the
+// packer); K codes go to their operand-order unit (half of a 16-byte unit), V codes
+// byte by byte to their transposed positions, then the two scales and the header's
+// ctx_len.  Rows past t are already zero in a cache packed for ctx_len - 1.
+template <int D, int BLK>
+__global__ void __launch_bounds__(64) append_kernel(PackArgs a) {
+  constexpr int TPR = D / 8, KSL = D / 64;
+  constexpr int KPART = 32 * D, CBYTES = 2 * KPART + 256;
+  const int pair = blockIdx.x, lane = threadIdx.x;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int c = a.geo.cur_block;
+  int64_t pair_off = a.geo.data_offset + (int64_t)b * a.geo.batch_bytes;
+  for (int gg = 0; gg < g; ++gg) {
+    const Blocks o = stored_blocks(c, a.pol.hi[gg], a.pol.keep[gg]);
+    pair_off += (int64_t)o.n8 * a.geo.rec8_bytes + (int64_t)o.n4 * a.geo.rec4_bytes;
+  }
+  const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
+  const int64_t t = a.geo.ctx_len - 1;
+  const int r = (int)(t - (int64_t)c * BLK), cc = r / 32, tk = r % 32;
+  uint8_t* chunk = a.cache + pair_off + (int64_t)(st.n8 - 1) * a.geo.rec8_bytes + (int64_t)cc * CBYTES;
+  const bool isv = lane >= TPR;
+  const int part = lane % TPR;
+  const int64_t src = (((int64_t)b * a.hkv + g) * a.n + t) * D + part * 8;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (lane < 2 * TPR) raw = *reinterpret_cast<const uint4*>((isv ? a.v : a.k) + src);
+  float x[8];
+  bf16x8_to_f32(raw, x);
+  uint32_t w8[2], w4;
+  float s8, s4;
+  quantize8<TPR>(x, w8, w4, s8, s4);
+  if (lane < TPR) {
+    // dims 8 part .. +7 = half (part % 2) of unit (s, ks, q, rr) of token 16 s + rr
+    const int dim0 = part * 8, ks = dim0 / 64, q = (dim0 % 64) / 16;
+    const int u = (((tk / 16) * KSL + ks) * 4 + q) * 16 + tk % 16;
+    *reinterpret_cast<uint2*>(chunk + u * 16 + (part % 2) * 8) = make_uint2(w8[0], w8[1]);
+    if (part == 0) *reinterpret_cast<float*>(chunk + 2 * KPART + 4 * tk) = s8;
+  } else if (lane < 2 * TPR) {
+    // byte p of unit (m, qv, rr) holds dim 16 dt + rr (dt = 2m, 2m + 1) of the token
+    // at feed position 8 qv + p; for this token qv = (tk % 16) / 4, p = 4 (tk / 16) + tk % 4
+    const int qv = (tk % 16) / 4, p = 4 * (tk / 16) + tk % 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int dim = part * 8 + i, dt = dim / 16, rr = dim % 16;
+      const int u = ((dt / 2) * 4 + qv) * 16 + rr;
+      chunk[KPART + u * 16 + (dt % 2) * 8 + p] = (uint8_t)(w8[i / 4] >> (8 * (i % 4)));
+    }
+    if (part == 0) *reinterpret_cast<float*>(chunk + 2 * KPART + 4 * (32 + tk)) = s8;
+  }
+  if (pair == 0 && lane == 0) reinterpret_cast<int64_t*>(a.cache)[4] = a.geo.ctx_len;
+}
+
 template <int D, int BLK>
 hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
+  if (a.only_current) {
+    hipLaunchKernelGGL((append_kernel<D, BLK>), dim3(a.batch * a.hkv), dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((pack_kernel<D, BLK>), dim3(max_stored, a.batch * a.hkv), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -251,11 +347,15 @@ hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const void* k,
-                       const void* v, void* cache, hipStream_t stream) {
+                       const void* v, void* cache, const void* old_cache, const CacheGeom* old_geo,
+                       bool only_current, hipStream_t stream) {
   PackArgs a;
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.cache = static_cast<uint8_t*>(cache);
+  a.old = static_cast<const uint8_t*>(old_cache);
+  a.ogeo = old_geo ? *old_geo : geo;
+  a.only_current = only_current ? 1 : 0;
   a.n = s.n;
   a.batch = s.batch;
   a.hkv = s.hkv;

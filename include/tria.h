@@ -225,6 +225,30 @@ tria_status tria_kv_cache_bytes(const tria_dims* dims, const int32_t* hi, const 
 tria_status tria_pack_kv_cache(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
                                int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16,
                                const void* v_bf16, void* cache, size_t cache_bytes, void* stream);
+/* Incremental maintenance (one more token): given cache_in, the cache packed for
+ * ctx_len - 1 from the same K, V and policy, writes to cache_out exactly the cache
+ * tria_pack_kv_cache would write for ctx_len (byte for byte).  A block's record
+ * depends only on its rows and its precision, so every record of a block before
+ * the new current block that cache_in holds at the same precision is reused; the
+ * current block's record and, when t = ctx_len - 1 starts a new block, the record
+ * of the block leaving the int8 window (now int4) are quantised from K, V.  Blocks
+ * leaving the int4 window are dropped.  The rows read from K, V must be those
+ * cache_in was packed from.
+ *   Within a block (ctx_len - 1 not a multiple of the block size) cache_out may be
+ *   cache_in (in place: only the current block's record and the header's ctx_len
+ *   change; one work group per (batch, KV head)).  When t starts a new block the
+ *   records move: cache_out must then be another buffer, not overlapping cache_in,
+ *   of at least tria_kv_cache_bytes(ctx_len) bytes.
+ * Errors: TRIA_ERR_INVALID_ARG for ctx_len outside [2, seq_len], an in-place call
+ * at a block start or partially overlapping buffers; TRIA_ERR_BUFFER_TOO_SMALL
+ * when cache_in is smaller than the cache for ctx_len - 1 or cache_out than the
+ * one for ctx_len.  Device, asynchronous on `stream`; cache_in's contents are not
+ * validated (a cache that was not packed as stated gives a wrong result, never an
+ * access outside the two buffers). */
+tria_status tria_update_kv_cache(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                 int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16,
+                                 const void* v_bf16, const void* cache_in, size_t cache_in_bytes,
+                                 void* cache_out, size_t cache_out_bytes, void* stream);
 /* Synchronous host-side validation of a cache's header and directory against
  * dims and ctx_len (copies them from device memory; for debugging and tests).
  * Returns TRIA_ERR_INVALID_ARG on any mismatch or corruption. */

@@ -167,3 +167,27 @@ def test_peak_helpers_validate_arguments(tria):
     assert L.tria_peak_read(src, 0, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG
     assert L.tria_peak_read(None, _lib.PEAK_READ_ALIGN, sink, C.byref(work), None) == _lib.TRIA_ERR_INVALID_ARG
 
+
+def test_update_validates_buffers(tria):
+    """tria_update_kv_cache rejects, before any HIP call, an in-place call at a block
+    start, partially overlapping buffers, too-small buffers and ctx_len < 2."""
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    d = tria.make_dims(1, 2, 1, 64, 64, 512)
+    hi, keep = np.array([1], np.int32), np.array([3], np.int32)
+    old = tria.kv_cache_bytes(d, hi, keep, 128)     # ctx 128: blocks 0, 1
+    new = tria.kv_cache_bytes(d, hi, keep, 129)     # ctx 129: token 128 starts block 2
+    kv = C.c_void_p(1 << 20)
+
+    def upd(ctx, cin, nin, cout, nout):
+        return L.tria_update_kv_cache(C.byref(d), hi.ctypes.data, keep.ctypes.data, 1, ctx, kv, kv,
+                                      C.c_void_p(cin), nin, C.c_void_p(cout), nout, None)
+
+    base = 1 << 30
+    assert upd(129, base, old, base, new) == _lib.TRIA_ERR_INVALID_ARG                 # in place at a block start
+    assert upd(129, base, old, base + 64, new) == _lib.TRIA_ERR_INVALID_ARG            # partial overlap
+    assert upd(129, base, old - 1, base + (1 << 24), new) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert upd(129, base, old, base + (1 << 24), new - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert upd(1, base, old, base + (1 << 24), new) == _lib.TRIA_ERR_INVALID_ARG       # ctx_len < 2
+    assert upd(513, base, old, base + (1 << 24), new) == _lib.TRIA_ERR_INVALID_ARG     # past seq_len
+

@@ -235,6 +235,42 @@ def test_pack_and_decode_small(tria, case):
     assert_close(out.cpu().numpy(), ref, f"decode {case}")
 
 
+UPD_CASES = [
+    # (b, hq, hk, d, n, blk, ctx0, steps, hi, keep)  policies per KV head
+    (2, 4, 2, 64, 400, 64, 120, 150, [1, 0], [3, 5]),     # crosses block starts 128, 192, 256
+    (1, 8, 2, 128, 700, 128, 250, 140, [0, 2], [1, 4]),   # crosses 256, 384; hi = 0 demotes at once
+    (1, 2, 1, 64, 300, 64, 1, 140, [0], [2]),             # from a single token
+    (1, 4, 4, 128, 600, 128, 380, 20, [99, 0, 0, 1], [99, 0, 99, 2]),  # all-int8, protected-only, all-int4
+]
+
+
+@pytest.mark.parametrize("case", UPD_CASES, ids=[f"b{c[0]}k{c[2]}d{c[3]}B{c[5]}ctx{c[6]}+{c[7]}" for c in UPD_CASES])
+def test_update_matches_pack(tria, case):
+    """Appending tokens one at a time with tria_update_kv_cache gives, after every
+    step, the bytes of a cache packed from scratch for that ctx_len: compared with
+    the GPU packer at every step and with the oracle's packer at every block start
+    and at the end."""
+    print(f"[case] cache update {case}", flush=True)
+    b, hq, hk, d, n, blk, ctx0, steps, hi, keep = case
+    cfg = synth.Config("upd", b, hq, hk, d, n, blk, seed=43, decode=True)
+    k, v, _ = synth.make_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    kd, vd = dev(k), dev(v)
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx0, kd, vd)
+    for ctx in range(ctx0 + 1, ctx0 + steps + 1):
+        prev = cache
+        cache = tria.update_kv_cache(dd, hi, keep, ctx, kd, vd, cache)
+        assert (cache.data_ptr() == prev.data_ptr()) == ((ctx - 1) % blk != 0)
+        ref = tria.pack_kv_cache(dd, hi, keep, ctx, kd, vd)
+        assert cache.numel() == ref.numel()
+        assert torch.equal(cache, ref), f"ctx {ctx}: updated cache differs from the packed one"
+        if (ctx - 1) % blk == 0 or ctx == ctx0 + steps:
+            blob = oracle.pack_cache(k, v, hi, keep, hq, blk, ctx)
+            assert np.array_equal(cache.cpu().numpy(), blob), f"ctx {ctx}: differs from the oracle's bytes"
+            tria.check_cache(dd, cache, ctx)
+
+
 def test_pack_merges_query_head_policies(tria):
     b, hq, hk, d, n, blk, ctx = 1, 4, 2, 64, 600, 64, 600
     cfg = synth.Config("dec", b, hq, hk, d, n, blk, seed=5, decode=True)
