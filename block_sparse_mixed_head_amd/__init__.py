@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
 __all__ = ["Dims", "build_policy", "quantize_qk", "prefill", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
-           "check_cache", "decode_workspace_bytes", "decode", "peak_mfma", "peak_read", "TriaError",
+           "check_cache", "decode_workspace_bytes", "decode", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
 Dims = _lib.Dims
@@ -179,6 +179,30 @@ def decode(d: Dims, cache: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale
     check(_lib.lib.tria_decode(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(q), float(sm_scale),
                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out
+
+
+# ------------------------------------------------------------------ calibration
+def policy_cost(d: Dims, hi: int, keep: int, cost_int8: float = 1.0, cost_int4: float = 1.0) -> float:
+    """Cost of one head's (hi, keep): whole kept tiles x block^2, weighted per precision."""
+    out = C.c_double(0.0)
+    check(_lib.lib.tria_policy_cost(C.byref(d), int(hi), int(keep), float(cost_int8), float(cost_int4),
+                                    C.byref(out)))
+    return out.value
+
+
+def allocate_policy(d: Dims, err: np.ndarray, budget: float, cost_int8: float = 1.0, cost_int4: float = 1.0):
+    """Greedy per-head (hi, keep) under a cost budget from error tables err[h][hi][keep]
+    (shape (n_heads, K + 1, K + 1)); returns (hi, keep, total_cost, total_err)."""
+    err = np.ascontiguousarray(np.asarray(err, dtype=np.float64))
+    if err.ndim != 3 or err.shape[1] != err.shape[2]:
+        raise ValueError(f"err: expected (n_heads, K + 1, K + 1), got {err.shape}")
+    n_heads, K = err.shape[0], err.shape[1] - 1
+    hi = np.zeros(n_heads, np.int32)
+    keep = np.zeros(n_heads, np.int32)
+    tc, te = C.c_double(0.0), C.c_double(0.0)
+    check(_lib.lib.tria_allocate_policy(C.byref(d), n_heads, K, err.ctypes.data, float(cost_int8), float(cost_int4),
+                                        float(budget), hi.ctypes.data, keep.ctypes.data, C.byref(tc), C.byref(te)))
+    return hi, keep, tc.value, te.value
 
 
 # ------------------------------------------------------------------ measured ceilings

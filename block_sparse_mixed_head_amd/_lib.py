@@ -47,6 +47,9 @@ def _load() -> C.CDLL:
         "tria_check_cache": (C.c_int, [D, P, sz, i64]),
         "tria_decode_workspace_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
         "tria_decode": (C.c_int, [D, P, sz, i64, P, f32, P, P, sz, P]),
+        "tria_policy_cost": (C.c_int, [D, i32, i32, C.c_double, C.c_double, C.POINTER(C.c_double)]),
+        "tria_allocate_policy": (C.c_int, [D, i32, i32, P, C.c_double, C.c_double, C.c_double, P, P,
+                                           C.POINTER(C.c_double), C.POINTER(C.c_double)]),
         "tria_peak_mfma": (C.c_int, [i32, i32, P, C.POINTER(C.c_double), P]),
         "tria_peak_read": (C.c_int, [P, i64, P, C.POINTER(C.c_double), P]),
     }
@@ -61,7 +64,8 @@ lib = _load()
 
 EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quantize_qk", "tria_prefill",
             "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_update_kv_cache", "tria_check_cache",
-            "tria_decode_workspace_bytes", "tria_decode", "tria_peak_mfma", "tria_peak_read"]
+            "tria_decode_workspace_bytes", "tria_decode", "tria_policy_cost", "tria_allocate_policy",
+            "tria_peak_mfma", "tria_peak_read"]
 PEAK_READ_ALIGN = 8192 * 8 * 1024
 PEAK_SINK_INTS = 8192
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
+#include <queue>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -120,6 +122,30 @@ tria_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(TRIA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
+
+// Whole tiles of one head's policy summed over all query blocks (the tile rule:
+// int8 = block 0, the diagonal and distances <= hi; int4 = distances in (hi, keep]).
+void policy_tiles(int64_t nb, int64_t hi, int64_t keep, int64_t& t8, int64_t& t4) {
+  t8 = t4 = 0;
+  for (int64_t qb = 0; qb < nb; ++qb) {
+    const int64_t lo8 = qb - hi >= 2 ? qb - hi : 0;
+    t8 += qb - lo8 + 1 + (lo8 > 0 ? 1 : 0);
+    const int64_t lo4 = std::max<int64_t>(1, qb - keep), hi4 = qb - hi - 1;
+    if (hi4 >= lo4) t4 += hi4 - lo4 + 1;
+  }
+}
+
+// Cost of one head's policy: whole processed tiles (B*B query-key pairs each) weighted
+// by the cost of a pair at each precision.
+#pragma clang fp contract(off)  // the cost is compared bit for bit: no fused multiply-add
+double policy_cost_of(const tria_dims* d, int64_t hi, int64_t keep, double c8, double c4) {
+  const int64_t nb = (d->seq_len + d->block - 1) / d->block;
+  int64_t t8, t4;
+  policy_tiles(nb, hi, keep, t8, t4);
+  const double b2 = (double)d->block * (double)d->block;
+  return (c8 * (double)t8 + c4 * (double)t4) * b2;
+}
+#pragma clang fp contract(on)
 
 #define NONNULL(p)                                                           \
   do {                                                                       \
@@ -420,6 +446,123 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
   return launched(tria::launch_decode(s, ctx_len, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out, workspace,
                                       static_cast<hipStream_t>(stream)),
                   "decode launch");
+}
+
+// ------------------------------------------------------------------ (f2) calibration
+static tria_status check_costs(double c8, double c4) {
+  if (!(c8 > 0.0) || !(c4 > 0.0) || !std::isfinite(c8) || !std::isfinite(c4))
+    return fail(TRIA_ERR_INVALID_ARG, "pair costs must be finite and > 0");
+  return TRIA_OK;
+}
+
+tria_status tria_policy_cost(const tria_dims* dims, int32_t hi, int32_t keep, double cost_int8, double cost_int4,
+                             double* cost) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(cost);
+  if (hi < 0 || keep < hi) return fail(TRIA_ERR_INVALID_ARG, "need 0 <= hi (%d) <= keep (%d)", hi, keep);
+  st = check_costs(cost_int8, cost_int4);
+  if (st != TRIA_OK) return st;
+  *cost = policy_cost_of(dims, hi, keep, cost_int8, cost_int4);
+  return ok();
+}
+
+tria_status tria_allocate_policy(const tria_dims* dims, int32_t n_heads, int32_t max_bound, const double* err,
+                                 double cost_int8, double cost_int4, double budget, int32_t* hi_out,
+                                 int32_t* keep_out, double* total_cost, double* total_err) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(err);
+  NONNULL(hi_out);
+  NONNULL(keep_out);
+  if (n_heads < 1) return fail(TRIA_ERR_INVALID_ARG, "n_heads must be >= 1");
+  if (max_bound < 0 || max_bound > 65535) return fail(TRIA_ERR_INVALID_ARG, "max_bound must be in [0, 65535]");
+  st = check_costs(cost_int8, cost_int4);
+  if (st != TRIA_OK) return st;
+  if (!std::isfinite(budget)) return fail(TRIA_ERR_INVALID_ARG, "budget must be finite");
+  const size_t S = (size_t)max_bound + 1;
+  for (size_t h = 0; h < (size_t)n_heads; ++h)
+    for (size_t a = 0; a < S; ++a)
+      for (size_t k = a; k < S; ++k)
+        if (!std::isfinite(err[(h * S + a) * S + k]))
+          return fail(TRIA_ERR_INVALID_ARG, "err[%zu][%zu][%zu] is not finite", h, a, k);
+  auto E = [&](int h, int a, int k) { return err[((size_t)h * S + a) * S + k]; };
+  std::vector<double> ctab(S * S, -1.0);  // cost per (hi, keep): the same for every head
+  auto C = [&](int a, int k) {
+    double& c = ctab[(size_t)a * S + k];
+    if (c < 0.0) c = policy_cost_of(dims, a, k, cost_int8, cost_int4);
+    return c;
+  };
+  std::vector<int> hi(n_heads, 0), kp(n_heads, 0);
+  std::vector<unsigned> ver(n_heads, 0);
+  double total = 0.0;
+  for (int h = 0; h < n_heads; ++h) total += C(0, 0);
+  if (total > budget)
+    return fail(TRIA_ERR_INVALID_ARG, "budget %.17g is below the protected-only cost %.17g", budget, total);
+  // Greedy: every head starts at (0, 0); a step raises one head's keep by one block
+  // (move 0: one more block kept, at int4) or its hi by one (move 1: one more block at
+  // int8, keep raised with it when equal), choosing the move with the largest error
+  // reduction per unit of added cost among those that fit the budget (a reduction at
+  // no cost first; ties by head, then move).  Moves that reduce no error are never
+  // taken.  Candidates live in a heap; a head's entries are dropped once it moves.
+  struct Cand {
+    double score;
+    int h, move;
+    unsigned ver;
+  };
+  auto worse = [](const Cand& x, const Cand& y) {
+    if (x.score != y.score) return x.score < y.score;
+    if (x.h != y.h) return x.h > y.h;
+    return x.move > y.move;
+  };
+  std::priority_queue<Cand, std::vector<Cand>, decltype(worse)> heap(worse);
+  auto target = [&](int h, int move, int& a, int& k) {
+    a = hi[h];
+    k = kp[h];
+    if (move == 0) {
+      if (k >= max_bound) return false;
+      ++k;
+    } else {
+      if (a >= max_bound) return false;
+      ++a;
+      k = std::max(k, a);
+    }
+    return true;
+  };
+  auto push = [&](int h) {
+    for (int move = 0; move < 2; ++move) {
+      int a, k;
+      if (!target(h, move, a, k)) continue;
+      const double de = E(h, hi[h], kp[h]) - E(h, a, k);
+      if (!(de > 0.0)) continue;
+      const double dc = C(a, k) - C(hi[h], kp[h]);
+      heap.push(Cand{dc > 0.0 ? de / dc : INFINITY, h, move, ver[h]});
+    }
+  };
+  for (int h = 0; h < n_heads; ++h) push(h);
+  while (!heap.empty()) {
+    const Cand c = heap.top();
+    heap.pop();
+    if (c.ver != ver[c.h]) continue;
+    int a, k;
+    target(c.h, c.move, a, k);
+    const double dc = C(a, k) - C(hi[c.h], kp[c.h]);
+    if (total + dc > budget) continue;  // stays out of budget: totals only grow
+    total += dc;
+    hi[c.h] = a;
+    kp[c.h] = k;
+    ++ver[c.h];
+    push(c.h);
+  }
+  double esum = 0.0;
+  for (int h = 0; h < n_heads; ++h) {
+    hi_out[h] = hi[h];
+    keep_out[h] = kp[h];
+    esum += E(h, hi[h], kp[h]);
+  }
+  if (total_cost) *total_cost = total;
+  if (total_err) *total_err = esum;
+  return ok();
 }
 
 tria_status tria_peak_mfma(int32_t kind, int32_t iters, int32_t* sink, double* work, void* stream) {

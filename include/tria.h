@@ -283,6 +283,44 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
                         int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
                         void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------- */
+/* Calibration: cost model and allocator.  Host, synchronous.                 */
+/* ------------------------------------------------------------------------- */
+/*
+ * TriAttention summary page (rit.work), section on how calibration distributes
+ * compute between heads: each head's candidate boundary pairs get a compute cost
+ * that counts whole processed blocks (the QK product, the normalisation of the
+ * weights and the value aggregation), and one global allocator grants more context
+ * or more precision where the added work lowers the error most.  The error of a
+ * variant (measured after the output projection on a model) is an input here.
+ *
+ * tria_policy_cost: cost of one head's (hi, keep) over all query blocks of
+ *   dims->seq_len: (cost_int8 * T8 + cost_int4 * T4) * block^2, where T8 and T4
+ *   count the whole int8 and int4 tiles the tile rule keeps (the diagonal and a
+ *   ragged last block count as whole blocks).  cost_int8, cost_int4: the cost of one
+ *   query-key pair at each precision (finite, > 0; equal on gfx950, which has no
+ *   int4 MFMA, when the cost is prefill time).
+ * tria_allocate_policy: err = double[n_heads][max_bound + 1][max_bound + 1], err[h][hi]
+ *   [keep] the error of head h at (hi, keep) (entries with hi > keep are unused; used
+ *   entries finite).  Greedy: every head starts at (0, 0); a step applies the one move
+ *   with the largest error reduction per unit of added cost among those that keep the
+ *   summed cost <= budget, where a head's moves are keep + 1 (one more block kept, at
+ *   int4) and hi + 1 (one more block at int8; keep raised with it when equal), both
+ *   bounded by max_bound; a reduction at no added cost ranks first, ties go to the
+ *   lower head index, then to the keep move; moves that reduce no error are never
+ *   taken; it stops when no move fits.  Writes hi[n_heads], keep[n_heads] and (if
+ *   non-NULL) the summed cost and error.
+ * Errors: TRIA_ERR_INVALID_ARG for invalid dims, 0 <= hi <= keep violated, non-positive
+ * or non-finite costs, a non-finite budget or error entry, max_bound outside
+ * [0, 65535], or a budget below n_heads times the cost of (0, 0).
+ */
+tria_status tria_policy_cost(const tria_dims* dims, int32_t hi, int32_t keep, double cost_int8,
+                             double cost_int4, double* cost);
+tria_status tria_allocate_policy(const tria_dims* dims, int32_t n_heads, int32_t max_bound,
+                                 const double* err, double cost_int8, double cost_int4,
+                                 double budget, int32_t* hi, int32_t* keep, double* total_cost,
+                                 double* total_err);
+
 /* ---- Measured ceilings (measurement helpers, not part of the method) ---------
  * Loops that bound what the part sustains for the instructions and the access
  * pattern the kernels above use, so roofline fractions can be read against

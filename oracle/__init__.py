@@ -43,6 +43,9 @@ def load() -> C.CDLL:
             "oracle_cache_bytes": (i64, [C.c_int] * 5 + [i64, P, P, C.c_int]),
             "oracle_pack_cache": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, i64]),
             "oracle_decode": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, f32, P, C.c_int]),
+            "oracle_policy_cost": (f64, [i64, C.c_int, i64, i64, f64, f64]),
+            "oracle_allocate_policy": (C.c_int, [i64, C.c_int, C.c_int, C.c_int, P, f64, f64, f64, P, P,
+                                                 C.POINTER(f64), C.POINTER(f64)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -182,3 +185,23 @@ def decode(k, v, q, hi, keep, block: int, ctx_len: int, sm_scale: float, threads
     load().oracle_decode(b, hq, hk, d, block, n, ctx_len, _p(hi), _p(keep), hi.size, _p(k), _p(v),
                          _p(q), sm_scale, _p(out), threads or nthreads())
     return out
+
+
+def policy_cost(n: int, block: int, hi: int, keep: int, c8: float = 1.0, c4: float = 1.0) -> float:
+    """Cost of one head's (hi, keep): its kept tiles as whole blocks at each precision's pair cost."""
+    return float(load().oracle_policy_cost(n, block, hi, keep, c8, c4))
+
+
+def allocate_policy(n: int, block: int, err: np.ndarray, budget: float, c8: float = 1.0, c4: float = 1.0):
+    """Greedy per-head (hi, keep) under a cost budget; returns (hi, keep, total_cost, total_err),
+    or raises ValueError when the budget is below the protected-only cost."""
+    err = _c(err, np.float64)
+    H, K = err.shape[0], err.shape[1] - 1
+    hi = np.zeros(H, np.int32)
+    keep = np.zeros(H, np.int32)
+    tc, te = C.c_double(0.0), C.c_double(0.0)
+    if load().oracle_allocate_policy(n, block, H, K, _p(err), c8, c4, budget, _p(hi), _p(keep), C.byref(tc),
+                                     C.byref(te)):
+        raise ValueError("budget below the protected-only cost")
+    return hi, keep, tc.value, te.value
+

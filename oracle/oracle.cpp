@@ -568,4 +568,87 @@ int oracle_decode(int batch, int n_q_heads, int n_kv_heads, int d, int block, in
   return 0;
 }
 
+
+// ---------------------------------------------------------------- calibration
+// TriAttention summary page (rit.work), section on how calibration distributes
+// compute between heads: a variant's cost counts whole processed blocks (the QK
+// product, the weight normalisation and the value aggregation).  Here: every tile
+// the rule keeps, counted one by one, as block*block pairs at its precision's cost.
+double oracle_policy_cost(int64_t n, int block, int64_t hi, int64_t keep, double c8, double c4) {
+  const int64_t nb = (n + block - 1) / block;
+  int64_t t8 = 0, t4 = 0;
+  for (int64_t qb = 0; qb < nb; ++qb)
+    for (int64_t kb = 0; kb <= qb; ++kb) {
+      const int a = tile_action(qb, kb, hi, keep);
+      if (a == ACT_INT8) ++t8;
+      if (a == ACT_INT4) ++t4;
+    }
+  return (c8 * (double)t8 + c4 * (double)t4) * ((double)block * (double)block);
+}
+
+// Same section: one global allocator grants more context or more precision where the
+// added work lowers the error most.  Every head starts at (0, 0); at each step every
+// head's two moves are looked at -- keep + 1 (one more block kept), hi + 1 (one more
+// block at int8, keep raised with it when equal), both <= K -- and the move with the
+// largest error reduction per added cost that fits the budget is applied (a reduction
+// at no cost ranks above any ratio; ties: lower head, then the keep move); moves that
+// reduce no error are not taken.  err[h][hi][keep], (K + 1) x (K + 1) per head.
+// Returns 1 when the budget is below the protected-only cost, else 0.
+int oracle_allocate_policy(int64_t n, int block, int H, int K, const double* err, double c8, double c4,
+                           double budget, int32_t* hi, int32_t* keep, double* total_cost, double* total_err) {
+  const int64_t S = K + 1;
+  auto E = [&](int h, int64_t a, int64_t k) { return err[((int64_t)h * S + a) * S + k]; };
+  auto cost = [&](int64_t a, int64_t k) { return oracle_policy_cost(n, block, a, k, c8, c4); };
+  double total = 0.0;
+  for (int h = 0; h < H; ++h) {
+    hi[h] = 0;
+    keep[h] = 0;
+    total += cost(0, 0);
+  }
+  if (total > budget) return 1;
+  for (;;) {
+    bool found = false;
+    int bh = 0, bm = 0;
+    int64_t ba = 0, bk = 0;
+    double bscore = 0.0, bdc = 0.0;
+    for (int h = 0; h < H; ++h)
+      for (int m = 0; m < 2; ++m) {
+        int64_t a = hi[h], k = keep[h];
+        if (m == 0) {
+          if (k >= K) continue;
+          k += 1;
+        } else {
+          if (a >= K) continue;
+          a += 1;
+          if (k < a) k = a;
+        }
+        const double de = E(h, hi[h], keep[h]) - E(h, a, k);
+        if (!(de > 0.0)) continue;
+        const double dc = cost(a, k) - cost(hi[h], keep[h]);
+        if (total + dc > budget) continue;
+        const double score = dc > 0.0 ? de / dc : INFINITY;
+        // strictly better score wins; equal scores keep the earlier (head, move)
+        if (!found || score > bscore) {
+          found = true;
+          bh = h;
+          bm = m;
+          ba = a;
+          bk = k;
+          bscore = score;
+          bdc = dc;
+        }
+      }
+    if (!found) break;
+    (void)bm;
+    total += bdc;
+    hi[bh] = (int32_t)ba;
+    keep[bh] = (int32_t)bk;
+  }
+  double es = 0.0;
+  for (int h = 0; h < H; ++h) es += E(h, hi[h], keep[h]);
+  *total_cost = total;
+  *total_err = es;
+  return 0;
+}
+
 }  // extern "C"

@@ -191,3 +191,63 @@ def test_update_validates_buffers(tria):
     assert upd(1, base, old, base + (1 << 24), new) == _lib.TRIA_ERR_INVALID_ARG       # ctx_len < 2
     assert upd(513, base, old, base + (1 << 24), new) == _lib.TRIA_ERR_INVALID_ARG     # past seq_len
 
+
+def test_policy_cost_matches_oracle_and_schedule(tria):
+    """The library's cost equals the oracle's tile-by-tile count, and with unit pair
+    costs it is block^2 times the head's tiles in the prefill schedule."""
+    import oracle
+    rng = np.random.default_rng(3)
+    for _ in range(30):
+        blk = int(rng.choice([64, 128]))
+        n = int(rng.integers(1, 3000))
+        hi = int(rng.integers(0, 12))
+        keep = int(rng.integers(hi, 30))
+        c8, c4 = float(rng.uniform(0.2, 2.0)), float(rng.uniform(0.2, 2.0))
+        d = tria.make_dims(1, 1, 1, 64, blk, n)
+        assert tria.policy_cost(d, hi, keep, c8, c4) == oracle.policy_cost(n, blk, hi, keep, c8, c4)
+        sched = tria.build_policy(d, np.array([hi], np.int32), np.array([keep], np.int32))
+        units = sched[16:].reshape(-1, 8)
+        assert tria.policy_cost(d, hi, keep) == float(units[:, 7].sum()) * blk * blk
+
+
+def test_allocator_matches_oracle(tria):
+    """Greedy allocation: the library's heap-driven run equals the oracle's scan, bit
+    for bit (choices, summed cost and summed error), on random instances including
+    equal pair costs (raising precision is then free) and flat tables."""
+    import oracle
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        blk = int(rng.choice([64, 128]))
+        n = int(rng.integers(64, 5000))
+        H, K = int(rng.integers(1, 9)), int(rng.integers(0, 12))
+        e = rng.uniform(0.0, 1.0, size=(H, K + 1, K + 1))
+        if trial % 3 == 0:
+            e = np.sort(np.sort(e, axis=2)[:, :, ::-1], axis=1)[:, ::-1, :]
+        if trial % 5 == 0:
+            e = np.round(e, 1)  # ties
+        e = np.ascontiguousarray(e)
+        c8, c4 = (1.0, 1.0) if trial % 4 == 0 else (float(rng.uniform(0.5, 2)), float(rng.uniform(0.2, 1)))
+        d = tria.make_dims(1, H, 1, 64, blk, n)
+        base = H * oracle.policy_cost(n, blk, 0, 0, c8, c4)
+        budget = base * float(rng.uniform(1.0, 6.0))
+        got = tria.allocate_policy(d, e, budget, c8, c4)
+        want = oracle.allocate_policy(n, blk, e, budget, c8, c4)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), trial
+        assert got[2] == want[2] and got[3] == want[3], trial
+
+
+def test_allocator_validates(tria):
+    from block_sparse_mixed_head_amd import _lib
+    d = tria.make_dims(1, 2, 1, 64, 64, 512)
+    e = np.ones((2, 3, 3))
+    with pytest.raises(_lib.TriaError):
+        tria.allocate_policy(d, e, 0.0)                     # below the protected-only cost
+    with pytest.raises(_lib.TriaError):
+        tria.allocate_policy(d, e, 1e12, cost_int8=0.0)     # pair cost must be > 0
+    bad = e.copy()
+    bad[1, 0, 2] = np.nan
+    with pytest.raises(_lib.TriaError):
+        tria.allocate_policy(d, bad, 1e12)
+    with pytest.raises(_lib.TriaError):
+        tria.policy_cost(d, 3, 2)                           # hi > keep
+

@@ -509,3 +509,63 @@ def test_decode_matches_prefill_last_row():
     pre = oracle.prefill(qp, k, v, top, top, B, sm, reference_mode=True)
     dec = oracle.decode(k, v, qp[:, :, n - 1], top[:hk], top[:hk], B, n, sm)
     assert np.abs(pre[:, :, n - 1] - dec).max() < 1e-5
+
+
+# ------------------------------------------------------------------ calibration (cost model, allocator)
+@pytest.mark.parametrize("n,block", [(512, 64), (1000, 128), (64, 64), (8192, 128)])
+def test_policy_cost_closed_forms(n, block):
+    """Whole-tile costs of the extreme policies: protected only = block 0 and the
+    diagonal (2 nb - 1 tiles), everything int8 = all nb (nb + 1) / 2 causal tiles,
+    everything else int4 beyond the protected tiles."""
+    nb = -(-n // block)
+    b2 = float(block * block)
+    assert oracle.policy_cost(n, block, 0, 0, 1.0, 1.0) == (2 * nb - 1) * b2
+    assert oracle.policy_cost(n, block, nb - 1, nb - 1, 1.0, 1.0) == nb * (nb + 1) // 2 * b2
+    assert oracle.policy_cost(n, block, 0, nb - 1, 3.0, 0.5) == (3.0 * (2 * nb - 1) + 0.5 * (nb * (nb + 1) // 2 - (2 * nb - 1))) * b2
+    # hi beyond the sequence saturates
+    assert oracle.policy_cost(n, block, nb + 5, nb + 9, 1.0, 1.0) == nb * (nb + 1) // 2 * b2
+
+
+def _tables(rng, H, K, decreasing=True):
+    e = rng.uniform(0.1, 1.0, size=(H, K + 1, K + 1))
+    if decreasing:  # error falls with more context and more precision
+        e = np.sort(e, axis=2)[:, :, ::-1]
+        e = np.sort(e, axis=1)[:, ::-1, :]
+    return np.ascontiguousarray(e)
+
+
+def test_allocator_budget_extremes():
+    rng = np.random.default_rng(7)
+    n, block, H, K = 1024, 128, 4, 5
+    e = _tables(rng, H, K)
+    base = H * oracle.policy_cost(n, block, 0, 0)
+    hi, keep, tc, te = oracle.allocate_policy(n, block, e, base)
+    assert (hi == 0).all() and (keep == 0).all() and tc == base
+    hi, keep, tc, te = oracle.allocate_policy(n, block, e, 1e30)   # strictly decreasing tables, no limit
+    assert (hi == K).all() and (keep == K).all()
+    with pytest.raises(ValueError):
+        oracle.allocate_policy(n, block, e, base * 0.999)
+
+
+def test_allocator_against_brute_force():
+    """Tiny instances: the greedy choice fits the budget, its summed cost is the sum of
+    its heads' costs, and its summed error is never below the optimum over all
+    per-head (hi, keep) combinations that fit (greedy is a heuristic, not exact)."""
+    import itertools
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        n, block = int(rng.integers(64, 700)), 64
+        H, K = int(rng.integers(1, 4)), int(rng.integers(0, 4))
+        e = _tables(rng, H, K, decreasing=bool(trial % 2))
+        pairs = [(a, k) for a in range(K + 1) for k in range(a, K + 1)]
+        cost = {pk: oracle.policy_cost(n, block, pk[0], pk[1]) for pk in pairs}
+        base = H * cost[(0, 0)]
+        budget = base + rng.uniform(0, 1) * (H * max(cost.values()) - base)
+        hi, keep, tc, te = oracle.allocate_policy(n, block, e, budget)
+        assert tc <= budget
+        assert abs(tc - sum(cost[(int(hi[h]), int(keep[h]))] for h in range(H))) <= 1e-9 * max(tc, 1.0)
+        best = min(sum(e[h, a, k] for h, (a, k) in enumerate(choice))
+                   for choice in itertools.product(pairs, repeat=H)
+                   if sum(cost[c] for c in choice) <= budget)
+        assert te >= best - 1e-12
+
