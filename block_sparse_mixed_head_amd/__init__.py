@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
-__all__ = ["Dims", "build_policy", "quantize_qk", "prefill", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
+__all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "prefill", "prefill_varlen", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
            "check_cache", "decode_workspace_bytes", "decode", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
@@ -109,6 +109,42 @@ def prefill(d: Dims, sched_dev: torch.Tensor, qz: Quantized, v: torch.Tensor, sm
     check(_lib.lib.tria_prefill(C.byref(d), _ptr(sched_dev), nbytes, _ptr(qz.q8), _ptr(qz.q4), _ptr(qz.q8s),
                                 _ptr(qz.q4s), _ptr(qz.k8), _ptr(qz.k4), _ptr(qz.k8s), _ptr(qz.k4s), _ptr(v),
                                 float(sm_scale), _ptr(out), _ptr(lse), _stream(v.device)))
+    return out
+
+
+def _cu(cu_seqlens) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+
+
+def build_policy_varlen(d: Dims, hi, keep, cu_seqlens) -> np.ndarray:
+    """Schedule blob (int32 words) for sequences packed along the rows of one batch
+    element: d.batch == 1, d.seq_len = cu_seqlens[-1]."""
+    hi, keep, cu = _i32(hi), _i32(keep), _cu(cu_seqlens)
+    need = C.c_size_t(0)
+    check(_lib.lib.tria_build_policy_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), len(cu) - 1,
+                                            cu.ctypes.data, None, 0, C.byref(need)))
+    out = np.zeros(need.value // 4, dtype=np.int32)
+    check(_lib.lib.tria_build_policy_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), len(cu) - 1,
+                                            cu.ctypes.data, out.ctypes.data, need.value, C.byref(need)))
+    return out
+
+
+def prefill_varlen(d: Dims, cu_seqlens, sched_dev: torch.Tensor, qz: Quantized, v: torch.Tensor, sm_scale: float,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prefill of a variable-length batch over a build_policy_varlen blob on the device."""
+    hq, hk, hd, n = d.n_q_heads, d.n_kv_heads, d.head_dim, d.seq_len
+    cu = _cu(cu_seqlens)
+    _require(v, torch.bfloat16, (1, hk, n, hd), "v")
+    if out is None:
+        out = torch.empty((1, hq, n, hd), dtype=torch.float32, device=v.device)
+    _require(out, torch.float32, (1, hq, n, hd), "out")
+    if lse is not None:
+        _require(lse, torch.float32, (1, hq, n), "lse")
+    nbytes = sched_dev.numel() * sched_dev.element_size()
+    check(_lib.lib.tria_prefill_varlen(C.byref(d), len(cu) - 1, cu.ctypes.data, _ptr(sched_dev), nbytes,
+                                       _ptr(qz.q8), _ptr(qz.q4), _ptr(qz.q8s), _ptr(qz.q4s), _ptr(qz.k8),
+                                       _ptr(qz.k4), _ptr(qz.k8s), _ptr(qz.k4s), _ptr(v), float(sm_scale),
+                                       _ptr(out), _ptr(lse), _stream(v.device)))
     return out
 
 

@@ -41,6 +41,8 @@ def _load() -> C.CDLL:
         "tria_build_policy": (C.c_int, [D, P, P, i32, P, sz, C.POINTER(sz)]),
         "tria_quantize_qk": (C.c_int, [D, P, P] + [P] * 8 + [P]),
         "tria_prefill": (C.c_int, [D, P, sz] + [P] * 8 + [P, f32, P, P, P]),
+        "tria_build_policy_varlen": (C.c_int, [D, P, P, i32, i32, P, P, sz, C.POINTER(sz)]),
+        "tria_prefill_varlen": (C.c_int, [D, i32, P, P, sz] + [P] * 8 + [P, f32, P, P, P]),
         "tria_kv_cache_bytes": (C.c_int, [D, P, P, i32, i64, C.POINTER(sz)]),
         "tria_pack_kv_cache": (C.c_int, [D, P, P, i32, i64, P, P, P, sz, P]),
         "tria_update_kv_cache": (C.c_int, [D, P, P, i32, i64, P, P, P, sz, P, sz, P]),
@@ -63,6 +65,7 @@ def _load() -> C.CDLL:
 lib = _load()
 
 EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quantize_qk", "tria_prefill",
+            "tria_build_policy_varlen", "tria_prefill_varlen",
             "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_update_kv_cache", "tria_check_cache",
             "tria_decode_workspace_bytes", "tria_decode", "tria_policy_cost", "tria_allocate_policy",
             "tria_peak_mfma", "tria_peak_read"]

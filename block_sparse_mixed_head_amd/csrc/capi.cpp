@@ -161,6 +161,71 @@ const char* tria_last_error(void) { return g_error.c_str(); }
 int32_t tria_version(void) { return (1 << 16) | 0; }
 
 // ------------------------------------------------------------------ (1) policy
+// Units of `nb_of.size()` batch rows (sequences) with nb_of[b] query blocks each, in
+// (b, h, qb) order, placed by a stable counting sort on ntiles (descending), written
+// after the 64-byte header at `out`.
+static void expand_units(const std::vector<int64_t>& nb_of, int32_t hq, const int32_t* hi, const int32_t* keep,
+                         int32_t* units) {
+  int64_t n_units = 0, nbmax = 0;
+  for (int64_t nb : nb_of) {
+    n_units += hq * nb;
+    nbmax = std::max(nbmax, nb);
+  }
+  std::vector<int32_t> rec((size_t)n_units * 8);
+  std::vector<int64_t> count(nbmax + 2, 0);
+  int64_t u = 0;
+  for (size_t b = 0; b < nb_of.size(); ++b)
+    for (int h = 0; h < hq; ++h)
+      for (int64_t qb = 0; qb < nb_of[b]; ++qb, ++u) {
+        const int64_t H = hi[h], K = keep[h];
+        const int64_t lo8 = (qb - H >= 2) ? qb - H : 0;
+        const int64_t sink = lo8 > 0 ? 1 : 0;
+        int64_t lo4 = std::max<int64_t>(1, qb - K), hi4 = qb - H - 1;
+        if (lo4 > hi4) {
+          lo4 = 0;
+          hi4 = -1;
+        }
+        const int64_t ntiles = (qb - lo8 + 1) + sink + (hi4 - lo4 + 1);
+        int32_t* r = &rec[(size_t)u * 8];
+        r[0] = (int32_t)b;
+        r[1] = h;
+        r[2] = (int32_t)qb;
+        r[3] = (int32_t)lo8;
+        r[4] = (int32_t)lo4;
+        r[5] = (int32_t)hi4;
+        r[6] = (int32_t)sink;
+        r[7] = (int32_t)ntiles;
+        count[ntiles]++;
+      }
+  // start position of each ntiles bucket, largest first
+  std::vector<int64_t> start(nbmax + 2, 0);
+  int64_t pos = 0;
+  for (int64_t t = nbmax + 1; t >= 0; --t) {
+    start[t] = pos;
+    pos += count[t];
+  }
+  for (int64_t i = 0; i < n_units; ++i) {
+    const int32_t* r = &rec[(size_t)i * 8];
+    std::memcpy(units + 8 * start[r[7]]++, r, 32);
+  }
+}
+
+static void schedule_header(int32_t* out, int32_t version, int32_t rows, const tria_dims* dims, int64_t nb,
+                            int64_t n_units) {
+  std::memset(out, 0, TRIA_SCHED_HEADER_BYTES);
+  out[0] = TRIA_SCHED_MAGIC;
+  out[1] = version;
+  out[2] = rows;
+  out[3] = dims->n_q_heads;
+  out[4] = dims->n_kv_heads;
+  out[5] = dims->head_dim;
+  out[6] = dims->block;
+  out[7] = (int32_t)nb;
+  out[8] = (int32_t)n_units;
+  out[10] = (int32_t)(dims->seq_len & 0xFFFFFFFF);
+  out[11] = (int32_t)(dims->seq_len >> 32);
+}
+
 tria_status tria_build_policy(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
                               int32_t n_policy_heads, void* sched_host, size_t sched_bytes,
                               size_t* sched_bytes_needed) {
@@ -180,59 +245,62 @@ tria_status tria_build_policy(const tria_dims* dims, const int32_t* hi, const in
   }
   if (sched_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule needs %zu bytes, got %zu", need, sched_bytes);
-
-  // Expand (hi, keep) into per-unit ranges.  Units are generated in (b, h, qb)
-  // order and placed by a stable counting sort on ntiles (descending).
-  std::vector<int32_t> rec((size_t)n_units * 8);
-  std::vector<int64_t> count(nb + 2, 0);
-  int64_t u = 0;
-  for (int b = 0; b < dims->batch; ++b)
-    for (int h = 0; h < dims->n_q_heads; ++h)
-      for (int64_t qb = 0; qb < nb; ++qb, ++u) {
-        const int64_t H = hi[h], K = keep[h];
-        const int64_t lo8 = (qb - H >= 2) ? qb - H : 0;
-        const int64_t sink = lo8 > 0 ? 1 : 0;
-        int64_t lo4 = std::max<int64_t>(1, qb - K), hi4 = qb - H - 1;
-        if (lo4 > hi4) {
-          lo4 = 0;
-          hi4 = -1;
-        }
-        const int64_t ntiles = (qb - lo8 + 1) + sink + (hi4 - lo4 + 1);
-        int32_t* r = &rec[(size_t)u * 8];
-        r[0] = b;
-        r[1] = h;
-        r[2] = (int32_t)qb;
-        r[3] = (int32_t)lo8;
-        r[4] = (int32_t)lo4;
-        r[5] = (int32_t)hi4;
-        r[6] = (int32_t)sink;
-        r[7] = (int32_t)ntiles;
-        count[ntiles]++;
-      }
-  // start position of each ntiles bucket, largest first
-  std::vector<int64_t> start(nb + 2, 0);
-  int64_t pos = 0;
-  for (int64_t t = nb + 1; t >= 0; --t) {
-    start[t] = pos;
-    pos += count[t];
-  }
   int32_t* out = static_cast<int32_t*>(sched_host);
-  std::memset(out, 0, TRIA_SCHED_HEADER_BYTES);
-  out[0] = TRIA_SCHED_MAGIC;
-  out[1] = TRIA_SCHED_VERSION;
-  out[2] = dims->batch;
-  out[3] = dims->n_q_heads;
-  out[4] = dims->n_kv_heads;
-  out[5] = dims->head_dim;
-  out[6] = dims->block;
-  out[7] = (int32_t)nb;
-  out[8] = (int32_t)n_units;
-  out[10] = (int32_t)(dims->seq_len & 0xFFFFFFFF);
-  out[11] = (int32_t)(dims->seq_len >> 32);
+  schedule_header(out, TRIA_SCHED_VERSION, dims->batch, dims, nb, n_units);
+  expand_units(std::vector<int64_t>((size_t)dims->batch, nb), dims->n_q_heads, hi, keep,
+               out + TRIA_SCHED_HEADER_BYTES / 4);
+  return ok();
+}
+
+// Variable-length batch: checks cu_seqlens (host) against dims and returns the
+// per-sequence block counts and the unit count.
+static tria_status varlen_layout(const tria_dims* dims, int32_t n_seqs, const int64_t* cu, std::vector<int64_t>& nbs,
+                                 int64_t& n_units) {
+  if (dims->batch != 1) return fail(TRIA_ERR_INVALID_ARG, "a variable-length batch needs dims->batch == 1");
+  if (n_seqs < 1) return fail(TRIA_ERR_INVALID_ARG, "n_seqs must be >= 1");
+  NONNULL(cu);
+  if (cu[0] != 0 || cu[n_seqs] != dims->seq_len)
+    return fail(TRIA_ERR_INVALID_ARG, "cu_seqlens must start at 0 and end at seq_len (%lld)",
+                (long long)dims->seq_len);
+  nbs.assign((size_t)n_seqs, 0);
+  n_units = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (cu[i + 1] <= cu[i]) return fail(TRIA_ERR_INVALID_ARG, "sequence %d is empty or cu_seqlens decreases", i);
+    nbs[i] = (cu[i + 1] - cu[i] + dims->block - 1) / dims->block;
+    n_units += (int64_t)dims->n_q_heads * nbs[i];
+  }
+  return TRIA_OK;
+}
+
+tria_status tria_build_policy_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                     int32_t n_policy_heads, int32_t n_seqs, const int64_t* cu_seqlens,
+                                     void* sched_host, size_t sched_bytes, size_t* sched_bytes_needed) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  if (n_policy_heads != dims->n_q_heads)
+    return fail(TRIA_ERR_INVALID_ARG, "n_policy_heads %d != n_q_heads %d", n_policy_heads, dims->n_q_heads);
+  st = check_policy(hi, keep, n_policy_heads);
+  if (st != TRIA_OK) return st;
+  std::vector<int64_t> nbs;
+  int64_t n_units;
+  st = varlen_layout(dims, n_seqs, cu_seqlens, nbs, n_units);
+  if (st != TRIA_OK) return st;
+  const size_t need = TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * (size_t)n_units + 8 * (size_t)n_seqs;
+  if (sched_bytes_needed) *sched_bytes_needed = need;
+  if (!sched_host) {
+    if (sched_bytes_needed) return ok();
+    return fail(TRIA_ERR_INVALID_ARG, "sched_host and sched_bytes_needed are both NULL");
+  }
+  if (sched_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule needs %zu bytes, got %zu", need, sched_bytes);
+  int32_t* out = static_cast<int32_t*>(sched_host);
+  schedule_header(out, TRIA_SCHED_VERSION_VARLEN, n_seqs, dims, *std::max_element(nbs.begin(), nbs.end()), n_units);
   int32_t* units = out + TRIA_SCHED_HEADER_BYTES / 4;
-  for (int64_t i = 0; i < n_units; ++i) {
-    const int32_t* r = &rec[(size_t)i * 8];
-    std::memcpy(units + 8 * start[r[7]]++, r, 32);
+  expand_units(nbs, dims->n_q_heads, hi, keep, units);
+  int32_t* seqs = units + 8 * n_units;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    seqs[2 * i] = (int32_t)cu_seqlens[i];
+    seqs[2 * i + 1] = (int32_t)(cu_seqlens[i + 1] - cu_seqlens[i]);
   }
   return ok();
 }
@@ -285,8 +353,44 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
   if (dims->seq_len > INT32_MAX - dims->block)
     return fail(TRIA_ERR_UNSUPPORTED, "prefill supports seq_len < 2^31 - block, got %lld", (long long)dims->seq_len);
   const int32_t* units = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(sched_dev) + TRIA_SCHED_HEADER_BYTES);
-  return launched(tria::launch_prefill(shape_of(dims), units, n_units, q8, q4, q8s, q4s, k8, k4, k8s, k4s, v_bf16,
-                                       sm_scale, out, lse, static_cast<hipStream_t>(stream)),
+  return launched(tria::launch_prefill(shape_of(dims), units, n_units, nullptr, 0, q8, q4, q8s, q4s, k8, k4, k8s, k4s,
+                                       v_bf16, sm_scale, out, lse, static_cast<hipStream_t>(stream)),
+                  "prefill launch");
+}
+
+tria_status tria_prefill_varlen(const tria_dims* dims, int32_t n_seqs, const int64_t* cu_seqlens,
+                                const void* sched_dev, size_t sched_bytes, const int8_t* q8, const uint8_t* q4,
+                                const float* q8s, const float* q4s, const int8_t* k8, const uint8_t* k4,
+                                const float* k8s, const float* k4s, const void* v_bf16, float sm_scale, float* out,
+                                float* lse, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(sched_dev);
+  NONNULL(q8);
+  NONNULL(q4);
+  NONNULL(q8s);
+  NONNULL(q4s);
+  NONNULL(k8);
+  NONNULL(k4);
+  NONNULL(k8s);
+  NONNULL(k4s);
+  NONNULL(v_bf16);
+  NONNULL(out);
+  std::vector<int64_t> nbs;
+  int64_t n_units;
+  st = varlen_layout(dims, n_seqs, cu_seqlens, nbs, n_units);
+  if (st != TRIA_OK) return st;
+  const size_t need = TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * (size_t)n_units + 8 * (size_t)n_seqs;
+  if (sched_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule for this batch needs %zu bytes, got %zu", need, sched_bytes);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (dims->seq_len > INT32_MAX - dims->block)
+    return fail(TRIA_ERR_UNSUPPORTED, "prefill supports seq_len < 2^31 - block, got %lld", (long long)dims->seq_len);
+  const uint8_t* base = static_cast<const uint8_t*>(sched_dev);
+  const int32_t* units = reinterpret_cast<const int32_t*>(base + TRIA_SCHED_HEADER_BYTES);
+  const int32_t* seqs = units + 8 * n_units;
+  return launched(tria::launch_prefill(shape_of(dims), units, n_units, seqs, n_seqs, q8, q4, q8s, q4s, k8, k4, k8s,
+                                       k4s, v_bf16, sm_scale, out, lse, static_cast<hipStream_t>(stream)),
                   "prefill launch");
 }
 

@@ -17,9 +17,11 @@ hipError_t launch_quantize(const Shape& s, const void* q, const void* k, int8_t*
                            hipStream_t stream);
 
 // Fused block-sparse prefill over the unit records of a schedule (device memory).
-hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int8_t* q8,
-                          const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
-                          const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
+// seqs (device, or null): {start, length} of n_seqs sequences packed along the rows of
+// one batch element (s.batch == 1, s.n = total rows); a unit's b is its sequence.
+hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int32_t* seqs,
+                          int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
+                          const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
                           float sm_scale, float* out, float* lse, hipStream_t stream);
 
 // Per-KV-head policy passed by value to the cache kernels.

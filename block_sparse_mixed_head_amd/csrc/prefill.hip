@@ -88,8 +88,9 @@ struct Args {
   const uint16_t* v;
   float* out;
   float* lse;
-  int64_t n;
-  int batch, hq, hkv;
+  const int32_t* seqs;  // variable-length batch: {start, length} per sequence, else null
+  int64_t n;            // rows per (batch, head): the sequence length, or the packed total
+  int batch, hq, hkv;   // batch: the number of sequences when seqs is set
   float c;  // sm_scale * log2(e)
 };
 
@@ -516,17 +517,26 @@ prefill_kernel(Args a) {
   const int b = u[0], h = u[1], qb = u[2], lo8 = u[3], lo4 = u[4], hi4 = u[5], sink = u[6];
   const int n4 = hi4 - lo4 + 1;
   const int ntiles = u[7];
+  if (b < 0 || b >= a.batch) return;  // (checked before the sequence table is read)
+  // a variable-length batch packs its sequences along the rows of one batch element:
+  // unit b is sequence b, rows [seq0, seq0 + n)
+  int64_t seq0 = 0, n = a.n;
+  int bb = b;
+  if (a.seqs) {
+    seq0 = a.seqs[2 * b];
+    n = a.seqs[2 * b + 1];
+    bb = 0;
+  }
   {  // a malformed record is skipped rather than allowed to address out of range
-    const int64_t nbq = (a.n + BLK - 1) / BLK;
-    const bool bad = b < 0 || b >= a.batch || h < 0 || h >= a.hq || qb < 0 || qb >= nbq || lo8 < 0 ||
+    const int64_t nbq = (n + BLK - 1) / BLK;
+    const bool bad = seq0 < 0 || n < 1 || seq0 + n > a.n || h < 0 || h >= a.hq || qb < 0 || qb >= nbq || lo8 < 0 ||
                      lo8 > qb || sink < 0 || sink > 1 || (sink == 1 && lo8 == 0) || n4 < 0 ||
                      (n4 > 0 && (lo4 < 1 || hi4 >= lo8)) || ntiles != (qb - lo8 + 1) + sink + n4;
     if (bad) return;
   }
   const int g_kv = h / (a.hq / a.hkv);
-  const int64_t n = a.n;
-  const int64_t qrow0 = ((int64_t)b * a.hq + h) * n;
-  const int64_t krow0 = ((int64_t)b * a.hkv + g_kv) * n;
+  const int64_t qrow0 = ((int64_t)bb * a.hq + h) * a.n + seq0;
+  const int64_t krow0 = ((int64_t)bb * a.hkv + g_kv) * a.n + seq0;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
@@ -736,12 +746,13 @@ hipError_t launch_t(const Args& a, int64_t n_units, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int8_t* q8,
-                          const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
-                          const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
+hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int32_t* seqs,
+                          int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
+                          const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
                           float sm_scale, float* out, float* lse, hipStream_t stream) {
   Args a;
   a.units = units;
+  a.seqs = seqs;
   a.q8 = q8;
   a.q4 = q4;
   a.q8s = q8s;
@@ -754,7 +765,7 @@ hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units,
   a.out = out;
   a.lse = lse;
   a.n = s.n;
-  a.batch = s.batch;
+  a.batch = seqs ? n_seqs : s.batch;
   a.hq = s.hq;
   a.hkv = s.hkv;
   a.c = sm_scale * 1.44269504088896340736f;

@@ -106,6 +106,7 @@ int32_t tria_version(void);
  */
 #define TRIA_SCHED_MAGIC 0x48435354 /* "TSCH" */
 #define TRIA_SCHED_VERSION 1
+#define TRIA_SCHED_VERSION_VARLEN 2
 #define TRIA_SCHED_HEADER_BYTES 64
 #define TRIA_SCHED_UNIT_BYTES 32
 tria_status tria_build_policy(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
@@ -163,6 +164,38 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
                          const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
                          const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
                          const void* v_bf16, float sm_scale, float* out, float* lse, void* stream);
+
+/*
+ * Variable-length batches.  n_seqs causal sequences of different lengths packed
+ * along the rows of one batch element: dims->batch == 1, dims->seq_len = the total
+ * T, sequence s = rows [cu_seqlens[s], cu_seqlens[s + 1]) (host int64[n_seqs + 1],
+ * cu_seqlens[0] = 0, strictly increasing, cu_seqlens[n_seqs] = T).  Q, K, V and the
+ * quantiser's outputs use the [1][H][T][d] layout (tria_quantize_qk with the same
+ * dims quantises them: rows are rows).  Each sequence is attended on its own, its
+ * blocks counted from its first row (block 0 and its diagonal protected, as above):
+ * row i of sequence s gives exactly what tria_prefill gives for that sequence
+ * alone.
+ * tria_build_policy_varlen: as tria_build_policy, with header word [1] =
+ *   TRIA_SCHED_VERSION_VARLEN, [2] = n_seqs, [7] = the largest block count; units
+ *   {s, h, qb, ...} for every sequence s and its ceil(len_s / block) query blocks
+ *   (same record order: ntiles descending, ties by (s, h, qb)); then n_seqs
+ *   records {int32 start, int32 length}.  Size TRIA_SCHED_HEADER_BYTES +
+ *   TRIA_SCHED_UNIT_BYTES * n_units + 8 * n_seqs.
+ * tria_prefill_varlen: as tria_prefill over that schedule; out fp32 [1][Hq][T][d],
+ *   lse [1][Hq][T].  cu_seqlens must be the one the schedule was built from.
+ * Errors: TRIA_ERR_INVALID_ARG for dims->batch != 1, n_seqs < 1 or a cu_seqlens
+ * that does not start at 0, increase strictly and end at seq_len; otherwise as
+ * tria_build_policy and tria_prefill.
+ */
+tria_status tria_build_policy_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                     int32_t n_policy_heads, int32_t n_seqs, const int64_t* cu_seqlens,
+                                     void* sched_host, size_t sched_bytes, size_t* sched_bytes_needed);
+tria_status tria_prefill_varlen(const tria_dims* dims, int32_t n_seqs, const int64_t* cu_seqlens,
+                                const void* sched_dev, size_t sched_bytes, const int8_t* q8,
+                                const uint8_t* q4, const float* q8s, const float* q4s,
+                                const int8_t* k8, const uint8_t* k4, const float* k8s,
+                                const float* k4s, const void* v_bf16, float sm_scale, float* out,
+                                float* lse, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* (4) Compressed KV cache.                                                   */

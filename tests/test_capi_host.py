@@ -251,3 +251,45 @@ def test_allocator_validates(tria):
     with pytest.raises(_lib.TriaError):
         tria.policy_cost(d, 3, 2)                           # hi > keep
 
+
+def test_varlen_schedule_matches_oracle(tria):
+    """The variable-length schedule = each sequence's own schedule (the oracle's, for
+    that length alone) with its batch index replaced by the sequence index, all
+    units merged by a stable sort on ntiles (descending), then the {start, length}
+    table."""
+    import oracle
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        blk = int(rng.choice([64, 128]))
+        hq = int(rng.integers(1, 6))
+        lens = rng.integers(1, 700, size=int(rng.integers(1, 7)))
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        T = int(cu[-1])
+        hi = rng.integers(0, 6, size=hq).astype(np.int32)
+        keep = (hi + rng.integers(0, 8, size=hq)).astype(np.int32)
+        d = tria.make_dims(1, hq, 1, 64, blk, T)
+        blob = tria.build_policy_varlen(d, hi, keep, cu)
+        parts = []
+        for s_, L in enumerate(lens):
+            u = oracle.build_schedule(1, hq, 1, 64, blk, int(L), hi, keep)[16:].reshape(-1, 8).copy()
+            u[:, 0] = s_
+            parts.append(u)
+        allu = np.concatenate(parts)
+        want = allu[np.argsort(-allu[:, 7], kind="stable")]
+        n_units = len(want)
+        assert blob[1] == 2 and blob[2] == len(lens) and blob[8] == n_units
+        assert np.array_equal(blob[16:16 + 8 * n_units].reshape(-1, 8), want)
+        seqs = blob[16 + 8 * n_units:].reshape(-1, 2)
+        assert np.array_equal(seqs[:, 0], cu[:-1]) and np.array_equal(seqs[:, 1], lens)
+
+
+def test_varlen_validation(tria):
+    from block_sparse_mixed_head_amd import _lib
+    hi, keep = np.array([1], np.int32), np.array([2], np.int32)
+    d = tria.make_dims(1, 1, 1, 64, 64, 100)
+    for cu in ([0, 50, 99], [1, 50, 100], [0, 50, 50, 100]):
+        with pytest.raises(_lib.TriaError):
+            tria.build_policy_varlen(d, hi, keep, cu)
+    with pytest.raises(_lib.TriaError):
+        tria.build_policy_varlen(tria.make_dims(2, 1, 1, 64, 64, 100), hi, keep, [0, 100])
+

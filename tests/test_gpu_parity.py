@@ -127,6 +127,40 @@ def test_prefill_small_every_output(tria, case):
     assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
 
 
+VARLEN = [
+    # (hq, hk, d, blk, lengths, hi, keep)
+    (4, 2, 64, 64, [1, 199, 63, 437, 64], [0, 1, 2, 9], [0, 4, 3, 9]),
+    (4, 1, 128, 128, [300, 129, 7, 900], [1, 0, 3, 2], [5, 8, 3, 2]),
+    (2, 2, 128, 64, [640], [1, 2], [3, 7]),       # one sequence: the fixed-length path's result
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[f"h{c[0]}k{c[1]}d{c[2]}B{c[3]}s{len(c[4])}" for c in VARLEN])
+def test_prefill_varlen_every_output(tria, case):
+    """Sequences of different lengths packed along the rows of one batch element:
+    every output row (and LSE) equals the oracle's prefill of its sequence alone."""
+    hq, hk, d, blk, lens, hi, keep = case
+    print(f"[case] prefill varlen {case}", flush=True)
+    T = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    cfg = small_cfg(1, hq, hk, d, T, blk, seed=23)
+    q, k, v = inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(1, hq, hk, d, blk, T)
+    sched = torch.from_numpy(tria.build_policy_varlen(dd, hi, keep, cu)).cuda()
+    qz = tria.quantize_qk(dd, dev(q), dev(k))
+    lse = torch.empty((1, hq, T), dtype=torch.float32, device="cuda")
+    out = tria.prefill_varlen(dd, cu, sched, qz, dev(v), 1.0 / math.sqrt(d), lse=lse)
+    torch.cuda.synchronize()
+    got, glse = out.cpu().numpy(), lse.cpu().numpy()
+    for i in range(len(lens)):
+        s0, s1 = int(cu[i]), int(cu[i + 1])
+        ref, rlse = oracle.prefill(q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1], hi, keep, blk,
+                                   1.0 / math.sqrt(d), with_lse=True)
+        assert_close(got[:, :, s0:s1], ref, f"varlen {case} sequence {i}")
+        assert np.abs(glse[:, :, s0:s1] - rlse).max() < 1e-3
+
+
 def test_prefill_integer_inputs_and_determinism(tria):
     # all blocks kept and integer rows with amax 127 (codes = values, scales 1):
     # large exact integer scores; two runs must be bitwise equal
