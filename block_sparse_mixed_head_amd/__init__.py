@@ -23,6 +23,7 @@ from . import _lib
 from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
 __all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "prefill", "prefill_varlen", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
+           "kv_cache_bytes_varlen", "pack_kv_cache_varlen", "decode_varlen",
            "check_cache", "decode_workspace_bytes", "decode", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
@@ -193,6 +194,31 @@ def update_kv_cache(d: Dims, hi, keep, ctx_len: int, k: torch.Tensor, v: torch.T
     return dst
 
 
+def kv_cache_bytes_varlen(d: Dims, hi, keep, ctx_lens) -> int:
+    hi, keep, cl = _i32(hi), _i32(keep), _cu(ctx_lens)
+    out = C.c_size_t(0)
+    check(_lib.lib.tria_kv_cache_bytes_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), cl.ctypes.data,
+                                              C.byref(out)))
+    return out.value
+
+
+def pack_kv_cache_varlen(d: Dims, hi, keep, ctx_lens, k: torch.Tensor, v: torch.Tensor,
+                         cache: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Cache of a batch whose sequence b holds ctx_lens[b] tokens (version 3)."""
+    b, hk, hd, n = d.batch, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(k, torch.bfloat16, (b, hk, n, hd), "k")
+    _require(v, torch.bfloat16, (b, hk, n, hd), "v")
+    hi, keep, cl = _i32(hi), _i32(keep), _cu(ctx_lens)
+    if len(cl) != b:
+        raise ValueError(f"ctx_lens: expected {b} lengths, got {len(cl)}")
+    nbytes = kv_cache_bytes_varlen(d, hi, keep, cl)
+    if cache is None:
+        cache = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    check(_lib.lib.tria_pack_kv_cache_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), cl.ctypes.data,
+                                             _ptr(k), _ptr(v), _ptr(cache), cache.numel(), _stream(k.device)))
+    return cache
+
+
 def check_cache(d: Dims, cache: torch.Tensor, ctx_len: int) -> None:
     check(_lib.lib.tria_check_cache(C.byref(d), _ptr(cache), cache.numel(), ctx_len))
 
@@ -214,6 +240,20 @@ def decode(d: Dims, cache: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale
         workspace = torch.empty(decode_workspace_bytes(d, ctx_len), dtype=torch.uint8, device=q.device)
     check(_lib.lib.tria_decode(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(q), float(sm_scale),
                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out
+
+
+def decode_varlen(d: Dims, cache: torch.Tensor, q: torch.Tensor, sm_scale: float,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode over a pack_kv_cache_varlen cache: each sequence at its own length."""
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(d, d.seq_len), dtype=torch.uint8, device=q.device)
+    check(_lib.lib.tria_decode_varlen(C.byref(d), _ptr(cache), cache.numel(), _ptr(q), float(sm_scale), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out
 
 

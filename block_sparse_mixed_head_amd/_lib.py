@@ -46,6 +46,9 @@ def _load() -> C.CDLL:
         "tria_kv_cache_bytes": (C.c_int, [D, P, P, i32, i64, C.POINTER(sz)]),
         "tria_pack_kv_cache": (C.c_int, [D, P, P, i32, i64, P, P, P, sz, P]),
         "tria_update_kv_cache": (C.c_int, [D, P, P, i32, i64, P, P, P, sz, P, sz, P]),
+        "tria_kv_cache_bytes_varlen": (C.c_int, [D, P, P, i32, P, C.POINTER(sz)]),
+        "tria_pack_kv_cache_varlen": (C.c_int, [D, P, P, i32, P, P, P, P, sz, P]),
+        "tria_decode_varlen": (C.c_int, [D, P, sz, P, f32, P, P, sz, P]),
         "tria_check_cache": (C.c_int, [D, P, sz, i64]),
         "tria_decode_workspace_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
         "tria_decode": (C.c_int, [D, P, sz, i64, P, f32, P, P, sz, P]),
@@ -67,6 +70,7 @@ lib = _load()
 EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quantize_qk", "tria_prefill",
             "tria_build_policy_varlen", "tria_prefill_varlen",
             "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_update_kv_cache", "tria_check_cache",
+            "tria_kv_cache_bytes_varlen", "tria_pack_kv_cache_varlen", "tria_decode_varlen",
             "tria_decode_workspace_bytes", "tria_decode", "tria_policy_cost", "tria_allocate_policy",
             "tria_peak_mfma", "tria_peak_read"]
 PEAK_READ_ALIGN = 8192 * 8 * 1024

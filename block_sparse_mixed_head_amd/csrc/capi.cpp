@@ -473,6 +473,69 @@ tria_status tria_update_kv_cache(const tria_dims* dims, const int32_t* hi, const
                   "cache update launch");
 }
 
+// Variable-length batch: per-sequence lengths (host); geometry of the longest.
+static tria_status varlen_cache_geom(const tria_dims* dims, const tria::KvPolicy& pol, const int64_t* ctx_lens,
+                                     tria::CacheGeom& g) {
+  NONNULL(ctx_lens);
+  if (dims->batch > tria::kMaxVarlenBatch)
+    return fail(TRIA_ERR_UNSUPPORTED, "variable-length caches hold at most %d sequences", tria::kMaxVarlenBatch);
+  int64_t longest = 1;
+  for (int b = 0; b < dims->batch; ++b) {
+    if (ctx_lens[b] < 1 || ctx_lens[b] > dims->seq_len)
+      return fail(TRIA_ERR_INVALID_ARG, "ctx_lens[%d] = %lld outside [1, seq_len=%lld]", b, (long long)ctx_lens[b],
+                  (long long)dims->seq_len);
+    longest = std::max(longest, ctx_lens[b]);
+  }
+  g = cache_geom(dims, pol, longest);
+  int64_t total = g.data_offset;
+  for (int b = 0; b < dims->batch; ++b) {
+    const int64_t c = (ctx_lens[b] - 1) / dims->block;
+    for (int gk = 0; gk < dims->n_kv_heads; ++gk) {
+      const Stored s = stored_count(c, pol.hi[gk], pol.keep[gk]);
+      total += s.n8 * g.rec8_bytes + s.n4 * g.rec4_bytes;
+    }
+  }
+  g.total_bytes = total;
+  g.batch_bytes = 0;  // varies by sequence
+  return TRIA_OK;
+}
+
+tria_status tria_kv_cache_bytes_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                       int32_t n_policy_heads, const int64_t* ctx_lens, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  tria::CacheGeom g;
+  st = varlen_cache_geom(dims, pol, ctx_lens, g);
+  if (st != TRIA_OK) return st;
+  *bytes = (size_t)g.total_bytes;
+  return ok();
+}
+
+tria_status tria_pack_kv_cache_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                      int32_t n_policy_heads, const int64_t* ctx_lens, const void* k_bf16,
+                                      const void* v_bf16, void* cache, size_t cache_bytes, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(k_bf16);
+  NONNULL(v_bf16);
+  NONNULL(cache);
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  tria::CacheGeom g;
+  st = varlen_cache_geom(dims, pol, ctx_lens, g);
+  if (st != TRIA_OK) return st;
+  if ((int64_t)cache_bytes < g.total_bytes)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache needs %lld bytes, got %zu", (long long)g.total_bytes, cache_bytes);
+  return launched(tria::launch_pack_varlen(shape_of(dims), pol, g, ctx_lens, k_bf16, v_bf16, cache,
+                                           static_cast<hipStream_t>(stream)),
+                  "pack launch");
+}
+
 tria_status tria_check_cache(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len) {
   tria_status st = check_dims(dims);
   if (st != TRIA_OK) return st;
@@ -548,6 +611,32 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
   if ((int64_t)ws_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "decode workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
   return launched(tria::launch_decode(s, ctx_len, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out, workspace,
+                                      false, static_cast<hipStream_t>(stream)),
+                  "decode launch");
+}
+
+tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes, const void* q_bf16,
+                               float sm_scale, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(cache);
+  NONNULL(q_bf16);
+  NONNULL(out);
+  NONNULL(workspace);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int G = dims->n_q_heads / dims->n_kv_heads;
+  if (G > 32) return fail(TRIA_ERR_UNSUPPORTED, "more than 32 query heads per KV head");
+  if ((int64_t)dims->batch * dims->n_kv_heads > 4096) return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads above 4096");
+  const int64_t dir_end = 64 + 64LL * dims->batch * dims->n_kv_heads;
+  if ((int64_t)cache_bytes < dir_end) return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache smaller than its directory");
+  const tria::Shape s = shape_of(dims);
+  // sequences hold at most seq_len tokens each: the unit count is bounded with it
+  if (!tria::decode_units_fit(s, dims->seq_len))
+    return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads * seq_len too large for one decode call");
+  const int64_t need = tria::decode_workspace_bytes(s, dims->seq_len);
+  if ((int64_t)ws_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "decode workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
+  return launched(tria::launch_decode(s, 1, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out, workspace, true,
                                       static_cast<hipStream_t>(stream)),
                   "decode launch");
 }

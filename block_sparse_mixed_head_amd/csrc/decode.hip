@@ -64,7 +64,8 @@ struct DecArgs {
   int64_t cache_bytes;
   int64_t ctx_len;
   int batch, hq, hkv;
-  float c;  // sm_scale * log2(e)
+  float c;     // sm_scale * log2(e)
+  int varlen;  // version-3 cache: each directory entry holds its sequence's ctx_len
 };
 
 struct Geo {
@@ -82,9 +83,10 @@ __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
   geo.cur = (int)((a.ctx_len - 1) / BLK);
   geo.data_offset = (64 + 64LL * a.batch * a.hkv + 255) / 256 * 256;
   geo.total = h64[5];
-  return hd[0] == 0x43564B54 && hd[1] == 2 && hd[2] == a.batch && hd[3] == a.hkv && hd[4] == D &&
-         hd[5] == BLK && hd[6] == geo.cur + 1 && hd[7] == geo.cur && h64[4] == a.ctx_len &&
-         geo.total <= a.cache_bytes && h64[6] == 64 && h64[7] == geo.data_offset;
+  const bool common = hd[0] == 0x43564B54 && hd[2] == a.batch && hd[3] == a.hkv && hd[4] == D && hd[5] == BLK &&
+                      geo.total <= a.cache_bytes && h64[6] == 64 && h64[7] == geo.data_offset;
+  if (a.varlen) return common && hd[1] == 3 && hd[7] == -1;  // ctx_len per directory entry
+  return common && hd[1] == 2 && hd[6] == geo.cur + 1 && hd[7] == geo.cur && h64[4] == a.ctx_len;
 }
 
 // Inclusive prefix sum over the wavefront: DPP row shifts (1, 2, 4, 8) within each
@@ -463,6 +465,7 @@ decode_split_kernel(DecArgs a) {
   __shared__ int n8p[kMaxPairs + 1];  // int8 records per pair, then their exclusive prefix
   __shared__ int n4p[kMaxPairs + 1];  // int4 records per pair, then their exclusive prefix
   __shared__ int first[kWaves];      // the pair holding each wavefront's first unit
+  __shared__ int mfp[kMaxPairs];     // per pair: keys of the current block below ctx_len (the mask)
   __shared__ int tmp[2 * kWaves];
   __shared__ int bad;
   __shared__ __attribute__((aligned(16))) float scl[kWaves][64];  // per-wave step scales
@@ -504,13 +507,17 @@ decode_split_kernel(DecArgs a) {
     v4i e[3];
     entry(p, e);
     const int n8 = e[0][2], n4 = e[0][3], lo8 = e[1][2], sink = e[1][3], lo4 = e[2][0];
+    // the pair's position: the launch's ctx_len, or (version 3) its own
+    const int64_t ctx = a.varlen ? (int64_t)(((uint64_t)(uint32_t)e[2][3] << 32) | (uint32_t)e[2][2]) : a.ctx_len;
+    const bool pos_ok = ctx >= 1 && ctx <= (1LL << 40);
+    const int cur = pos_ok ? (int)((ctx - 1) / BLK) : 0;
     // the int8 run ends at the current block; int4 records lie below it
-    const bool ok = n8 >= 1 && n4 >= 0 && n8 + n4 <= geo.cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
-                    lo8 + (n8 - sink) - 1 == geo.cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 &&
-                    lo4 + n4 <= geo.cur + 1;
+    const bool ok = pos_ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
+                    lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1;
     if (!ok) bad = 1;
     n8p[p] = ok ? n8 : 0;
     n4p[p] = ok ? n4 : 0;
+    mfp[p] = (int)(ctx - (int64_t)cur * BLK);
   }
   __syncthreads();
   prefix2_lds(n8p, n4p, P, tmp);
@@ -636,7 +643,7 @@ decode_split_kernel(DecArgs a) {
     }
     st.k = 8;
     // the last int8 record is the current block; keys at or past ctx_len are masked
-    const int mask_first = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
+    const int mask_first = uni(mfp[p]);
     const bool has8 = j8a < j8b;
     run_steps<D, BLK, RG, false>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq, scl[wave],
                                  quantise_q);
@@ -759,7 +766,8 @@ bool decode_units_fit(const Shape& s, int64_t ctx_len) {
 }
 
 hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
-                         const void* q, float sm_scale, float* out, void* workspace, hipStream_t stream) {
+                         const void* q, float sm_scale, float* out, void* workspace, bool varlen,
+                         hipStream_t stream) {
   DecArgs a;
   a.cache = static_cast<const uint8_t*>(cache);
   a.q = static_cast<const uint16_t*>(q);
@@ -771,6 +779,7 @@ hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int
   a.hq = s.hq;
   a.hkv = s.hkv;
   a.c = sm_scale * 1.44269504088896340736f;
+  a.varlen = varlen ? 1 : 0;
   const int G = s.hq / s.hkv;
   const bool two = G > 16;
   if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2>(a, stream) : launch_t<128, 128, 1>(a, stream);

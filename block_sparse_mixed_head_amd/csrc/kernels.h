@@ -49,12 +49,22 @@ hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& g, 
                        const void* v, void* cache, const void* old_cache, const CacheGeom* old_geo,
                        bool only_current, hipStream_t stream);
 
+// Variable-length batch (s.batch <= kMaxVarlenBatch): sequence b holds ctxs[b] tokens
+// (host array); geo: data offset, record sizes, cur_block of the longest sequence and
+// total_bytes.  Writes the version-3 header and directory, then the records.
+constexpr int kMaxVarlenBatch = 256;
+hipError_t launch_pack_varlen(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const int64_t* ctxs,
+                              const void* k, const void* v, void* cache, hipStream_t stream);
+
 // Decode: split-KV partials into `workspace`, then a merge into `out`.
 // decode_units_fit: the work split counts 32-token units in int32.
 bool decode_units_fit(const Shape& s, int64_t ctx_len);
 int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len);
+// varlen: a version-3 cache (each directory entry holds its sequence's ctx_len; the
+// ctx_len argument is then ignored).
 hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
-                         const void* q, float sm_scale, float* out, void* workspace, hipStream_t stream);
+                         const void* q, float sm_scale, float* out, void* workspace, bool varlen,
+                         hipStream_t stream);
 
 // Measured ceilings (peaks.hip): an MFMA issue loop (kind 0: i8 16x16x64, 1: bf16
 // 16x16x32) and a non-temporal streaming read.  Work of one launch in ops / flops.

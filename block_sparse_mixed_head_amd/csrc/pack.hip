@@ -46,6 +46,8 @@ struct PackArgs {
   const uint8_t* old;  // update: the cache for ctx_len - 1 (else null), geometry ogeo
   CacheGeom ogeo;
   int only_current;    // update in place within the current block: the new token's row only
+  int varlen;          // per-sequence lengths ctxs[b] (the directory is written first)
+  int64_t ctxs[kMaxVarlenBatch];
   int64_t n;  // token rows in the K/V source
   int batch, hkv;
   KvPolicy pol;
@@ -95,7 +97,8 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
 
   const int pair = blockIdx.y;
   const int b = pair / a.hkv, g = pair % a.hkv;
-  const int c = a.geo.cur_block;
+  const int64_t ctx = a.varlen ? a.ctxs[b] : a.geo.ctx_len;
+  const int c = a.varlen ? (int)((ctx - 1) / BLK) : a.geo.cur_block;
   const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
   const int j = blockIdx.x;
   if (j >= st.n8 + st.n4) return;
@@ -107,7 +110,10 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     }
     return off;
   };
-  const int64_t pair_off = pair_offset(a.geo);
+  // variable lengths: the pair's offset from the directory (written by the
+  // directory kernel before this launch)
+  const int64_t pair_off =
+      a.varlen ? *reinterpret_cast<const int64_t*>(a.cache + 64 + 64 * (int64_t)pair) : pair_offset(a.geo);
   const bool is4 = j >= st.n8;
   const int kb = !is4 ? ((st.sink && j == 0) ? 0 : st.lo8 + j - st.sink) : st.lo4 + (j - st.n8);
   const int64_t off = !is4 ? pair_off + (int64_t)j * a.geo.rec8_bytes
@@ -115,7 +121,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   uint8_t* rec = a.cache + off;
   const int tid = threadIdx.x;
 
-  if (j == 0 && tid == 0) {
+  if (j == 0 && tid == 0 && !a.varlen) {
     int32_t* e = reinterpret_cast<int32_t*>(a.cache + 64 + 64 * (int64_t)pair);
     *reinterpret_cast<int64_t*>(e) = pair_off;
     e[2] = st.n8;
@@ -145,7 +151,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     }
   }
 
-  if (pair == 0 && j == 0) {  // the padding between the directory and the first record
+  if (pair == 0 && j == 0 && !a.varlen) {  // the padding between the directory and the first record
     const int64_t pad0 = 64 + 64LL * a.batch * a.hkv;
     for (int64_t i = pad0 + tid; i < a.geo.data_offset; i += kThreads) a.cache[i] = 0;
   }
@@ -188,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   for (int p = 0; p < BLK / RPP; ++p) {
     const int r = p * RPP + tid / TPR;
     const int64_t tok = (int64_t)kb * BLK + r;
-    const bool valid = tok < a.geo.ctx_len;
+    const bool valid = tok < ctx;
     float xk[8], xv[8];
     uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0);
     if (valid) {
@@ -281,6 +287,72 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   }
 }
 
+// Variable-length batch: one work group writes the header (version 3) and every
+// pair's directory entry from the per-sequence lengths; each entry also holds its
+// sequence's ctx_len (words 10-11).  Offsets are the running sum of the pairs'
+// record bytes in (b, g) order.
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) varlen_directory_kernel(PackArgs a) {
+  __shared__ int64_t part[kThreads];
+  const int tid = threadIdx.x;
+  const int P = a.batch * a.hkv;
+  int64_t carry = a.geo.data_offset;
+  for (int base = 0; base < P; base += kThreads) {
+    const int p = base + tid;
+    int64_t bytes = 0;
+    Blocks st{};
+    int64_t ctx = 1;
+    if (p < P) {
+      const int b = p / a.hkv, g = p % a.hkv;
+      ctx = a.ctxs[b];
+      st = stored_blocks((int)((ctx - 1) / BLK), a.pol.hi[g], a.pol.keep[g]);
+      bytes = (int64_t)st.n8 * a.geo.rec8_bytes + (int64_t)st.n4 * a.geo.rec4_bytes;
+    }
+    part[tid] = bytes;
+    __syncthreads();
+    int64_t before = 0, total = 0;  // exclusive prefix inside this chunk (plain loop: one group)
+    for (int i = 0; i < kThreads; ++i) {
+      before += i < tid ? part[i] : 0;
+      total += part[i];
+    }
+    if (p < P) {
+      const int g = p % a.hkv;
+      int32_t* e = reinterpret_cast<int32_t*>(a.cache + 64 + 64 * (int64_t)p);
+      *reinterpret_cast<int64_t*>(e) = carry + before;
+      e[2] = st.n8;
+      e[3] = st.n4;
+      e[4] = a.pol.hi[g];
+      e[5] = a.pol.keep[g];
+      e[6] = st.lo8;
+      e[7] = st.sink;
+      e[8] = st.lo4;
+      e[9] = st.hi4;
+      *reinterpret_cast<int64_t*>(e + 10) = ctx;
+      e[12] = e[13] = e[14] = e[15] = 0;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int32_t* hd = reinterpret_cast<int32_t*>(a.cache);
+    hd[0] = 0x43564B54;  // "TKVC"
+    hd[1] = 3;           // format version: per-pair ctx_len
+    hd[2] = a.batch;
+    hd[3] = a.hkv;
+    hd[4] = D;
+    hd[5] = BLK;
+    hd[6] = a.geo.cur_block + 1;  // blocks of the longest sequence
+    hd[7] = -1;                   // the current block varies by sequence
+    int64_t* h64 = reinterpret_cast<int64_t*>(a.cache);
+    h64[4] = 0;
+    h64[5] = a.geo.total_bytes;
+    h64[6] = 64;
+    h64[7] = a.geo.data_offset;
+  }
+  const int64_t pad0 = 64 + 64LL * a.batch * a.hkv;
+  for (int64_t i = pad0 + tid; i < a.geo.data_offset; i += kThreads) a.cache[i] = 0;
+}
+
 // In place within the current block: token t = ctx_len - 1 (row r of block c, chunk
 // r / 32, position tk = r % 32) is the only change.  Lanes [0, TPR) quantise its K
 // row, lanes [TPR, 2 TPR) its V row, eight dims each (the quantiser contract of the
@@ -340,11 +412,39 @@ hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
     hipLaunchKernelGGL((append_kernel<D, BLK>), dim3(a.batch * a.hkv), dim3(64), 0, stream, a);
     return hipGetLastError();
   }
+  if (a.varlen) {
+    hipLaunchKernelGGL((varlen_directory_kernel<D, BLK>), dim3(1), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((pack_kernel<D, BLK>), dim3(max_stored, a.batch * a.hkv), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_pack_varlen(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const int64_t* ctxs,
+                              const void* k, const void* v, void* cache, hipStream_t stream) {
+  PackArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.cache = static_cast<uint8_t*>(cache);
+  a.old = nullptr;
+  a.ogeo = geo;
+  a.only_current = 0;
+  a.varlen = 1;
+  for (int i = 0; i < kMaxVarlenBatch; ++i) a.ctxs[i] = i < s.batch ? ctxs[i] : 1;
+  a.n = s.n;
+  a.batch = s.batch;
+  a.hkv = s.hkv;
+  a.pol = pol;
+  a.geo = geo;
+  const int max_stored = geo.cur_block + 1;
+  if (s.d == 128 && s.blk == 128) return launch_t<128, 128>(a, max_stored, stream);
+  if (s.d == 128 && s.blk == 64) return launch_t<128, 64>(a, max_stored, stream);
+  if (s.d == 64 && s.blk == 128) return launch_t<64, 128>(a, max_stored, stream);
+  return launch_t<64, 64>(a, max_stored, stream);
+}
 
 hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const void* k,
                        const void* v, void* cache, const void* old_cache, const CacheGeom* old_geo,
@@ -356,6 +456,7 @@ hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& geo
   a.old = static_cast<const uint8_t*>(old_cache);
   a.ogeo = old_geo ? *old_geo : geo;
   a.only_current = only_current ? 1 : 0;
+  a.varlen = 0;
   a.n = s.n;
   a.batch = s.batch;
   a.hkv = s.hkv;

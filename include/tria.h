@@ -258,6 +258,23 @@ tria_status tria_kv_cache_bytes(const tria_dims* dims, const int32_t* hi, const 
 tria_status tria_pack_kv_cache(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
                                int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16,
                                const void* v_bf16, void* cache, size_t cache_bytes, void* stream);
+/* Variable-length batches: sequence b holds ctx_lens[b] tokens (host int64[batch],
+ * 1 <= ctx_lens[b] <= seq_len; batch <= 256), its query at t_b = ctx_lens[b] - 1 and
+ * current block c_b = t_b / block; its KV heads store the blocks of the rule above
+ * for c_b.  The layout is the one above with version 3: header word [6] = c + 1 and
+ * [7] = -1 (c of the longest sequence; the current block varies), int64 ctx_len
+ * (bytes 32..39) = 0, and every directory entry holds its sequence's ctx_len as int64
+ * in words 10-11.  tria_kv_cache_bytes_varlen gives the exact size; the pack is
+ * device, asynchronous.  Sequence b's records are byte for byte those
+ * tria_pack_kv_cache writes for a batch of that sequence alone at ctx_lens[b].
+ * Errors: TRIA_ERR_UNSUPPORTED above 256 sequences; TRIA_ERR_INVALID_ARG for a
+ * length outside [1, seq_len]. */
+tria_status tria_kv_cache_bytes_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                       int32_t n_policy_heads, const int64_t* ctx_lens, size_t* bytes);
+tria_status tria_pack_kv_cache_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                      int32_t n_policy_heads, const int64_t* ctx_lens,
+                                      const void* k_bf16, const void* v_bf16, void* cache,
+                                      size_t cache_bytes, void* stream);
 /* Incremental maintenance (one more token): given cache_in, the cache packed for
  * ctx_len - 1 from the same K, V and policy, writes to cache_out exactly the cache
  * tria_pack_kv_cache would write for ctx_len (byte for byte).  A block's record
@@ -311,10 +328,19 @@ tria_status tria_check_cache(const tria_dims* dims, const void* cache, size_t ca
  * batch * n_kv_heads above 4096, or when batch * n_kv_heads * ceil(ctx_len /
  * block) * block / 16 reaches 2^31.
  */
+/* tria_decode_varlen: decode over a version-3 (variable-length) cache: each
+ * sequence's query attends over its own ctx_len tokens (read from the directory),
+ * exactly as tria_decode does for that sequence alone.  The workspace is sized by
+ * tria_decode_workspace_bytes(dims, dims->seq_len).  A header or directory that does
+ * not validate (version 3, each entry consistent with its own ctx_len, contiguous
+ * offsets) writes NaN to `out` and reads no record. */
 tria_status tria_decode_workspace_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
 tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes,
                         int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
                         void* workspace, size_t ws_bytes, void* stream);
+tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                               const void* q_bf16, float sm_scale, float* out, void* workspace,
+                               size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Calibration: cost model and allocator.  Host, synchronous.                 */

@@ -269,6 +269,67 @@ def test_pack_and_decode_small(tria, case):
     assert_close(out.cpu().numpy(), ref, f"decode {case}")
 
 
+VARLEN_DEC = [
+    # (hq, hk, d, n, blk, ctx_lens, hi, keep)  policies per KV head
+    (8, 2, 128, 1300, 128, [1300, 1, 640, 129], [1, 0], [5, 3]),
+    (7, 1, 64, 900, 64, [65, 900, 333], [2], [6]),
+    (4, 4, 128, 700, 64, [700, 700], [99, 0, 0, 1], [99, 0, 99, 3]),   # equal lengths, edge policies
+]
+
+
+def _varlen_cache_from_oracle(k, v, hi, keep, hq, blk, d, ctx_lens):
+    """The expected version-3 bytes, spliced from the oracle's cache of each sequence
+    alone: header fields for the batch, each directory entry with its offset moved
+    and its sequence's ctx_len in words 10-11, then the sequences' records in order."""
+    b, hk = len(ctx_lens), k.shape[1]
+    data0 = (64 + 64 * b * hk + 255) // 256 * 256
+    one0 = (64 + 64 * hk + 255) // 256 * 256
+    blobs = [oracle.pack_cache(k[i:i + 1], v[i:i + 1], hi, keep, hq, blk, int(ctx_lens[i])) for i in range(b)]
+    recs = [bl[one0:] for bl in blobs]
+    total = data0 + sum(r.size for r in recs)
+    out = np.zeros(total, np.uint8)
+    hd = np.zeros(8, np.int32)
+    hd[:8] = [0x43564B54, 3, b, hk, d, blk, (max(ctx_lens) - 1) // blk + 1, -1]
+    out[0:32] = hd.view(np.uint8)
+    out[32:64] = np.array([0, total, 64, data0], np.int64).view(np.uint8)
+    pos = data0
+    for i, bl in enumerate(blobs):
+        for g in range(hk):
+            e = bl[64 + 64 * g: 128 + 64 * g].copy()
+            off = int(e[0:8].view(np.int64)[0])
+            e[0:8] = np.array([off - one0 + pos], np.int64).view(np.uint8)
+            e[40:48] = np.array([ctx_lens[i]], np.int64).view(np.uint8)
+            p_ = 64 + 64 * (i * hk + g)
+            out[p_:p_ + 64] = e
+        out[pos:pos + recs[i].size] = recs[i]
+        pos += recs[i].size
+    return out
+
+
+@pytest.mark.parametrize("case", VARLEN_DEC, ids=[f"h{c[0]}k{c[1]}d{c[2]}B{c[4]}b{len(c[5])}" for c in VARLEN_DEC])
+def test_varlen_cache_and_decode(tria, case):
+    """A batch whose sequences sit at different lengths: the packed bytes equal the
+    oracle's per-sequence caches spliced into the version-3 layout, and each
+    sequence's decode output equals the oracle's decode of that sequence alone."""
+    hq, hk, d, n, blk, ctx_lens, hi, keep = case
+    print(f"[case] varlen cache + decode {case}", flush=True)
+    b = len(ctx_lens)
+    cfg = synth.Config("vdec", b, hq, hk, d, n, blk, seed=47, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    cache = tria.pack_kv_cache_varlen(dd, hi, keep, ctx_lens, dev(k), dev(v))
+    out = tria.decode_varlen(dd, cache, dev(q), 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    want = _varlen_cache_from_oracle(k, v, hi, keep, hq, blk, d, ctx_lens)
+    assert cache.numel() == want.size
+    assert np.array_equal(cache.cpu().numpy(), want), "variable-length cache differs from the spliced oracle bytes"
+    got = out.cpu().numpy()
+    for i in range(b):
+        ref = oracle.decode(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, int(ctx_lens[i]), 1.0 / math.sqrt(d))
+        assert_close(got[i:i + 1], ref, f"varlen decode {case} sequence {i}")
+
+
 UPD_CASES = [
     # (b, hq, hk, d, n, blk, ctx0, steps, hi, keep)  policies per KV head
     (2, 4, 2, 64, 400, 64, 120, 150, [1, 0], [3, 5]),     # crosses block starts 128, 192, 256
