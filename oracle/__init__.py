@@ -44,6 +44,10 @@ def load() -> C.CDLL:
             "oracle_pack_cache": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, i64]),
             "oracle_decode": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, f32, P, C.c_int]),
             "oracle_policy_cost": (f64, [i64, C.c_int, i64, i64, f64, f64]),
+            "oracle_block_summaries": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, P, P, C.c_int]),
+            "oracle_skip_masks": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, f32, P, C.c_int]),
+            "oracle_decode_skip": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, P, f32, P,
+                                                           C.c_int]),
             "oracle_allocate_policy": (C.c_int, [i64, C.c_int, C.c_int, C.c_int, P, f64, f64, f64, P, P,
                                                  C.POINTER(f64), C.POINTER(f64)]),
         }
@@ -184,6 +188,56 @@ def decode(k, v, q, hi, keep, block: int, ctx_len: int, sm_scale: float, threads
     out = np.empty((b, hq, d), dtype=np.float32)
     load().oracle_decode(b, hq, hk, d, block, n, ctx_len, _p(hi), _p(keep), hi.size, _p(k), _p(v),
                          _p(q), sm_scale, _p(out), threads or nthreads())
+    return out
+
+
+def block_summaries(k, hi, keep, n_q_heads: int, block: int, ctx_len: int, threads: Optional[int] = None):
+    """Statistics of every stored record of the cache for ctx_len (record order, rmax =
+    cur_block + 1 slots per pair): (lo, hi) int8 [P][rmax][d], smax f32 [P][rmax],
+    nmax f64 [P][rmax]."""
+    k = _c(k, np.uint16)
+    b, hk, n, d = k.shape
+    hi, keep = _c(hi, np.int32), _c(keep, np.int32)
+    rmax = (ctx_len - 1) // block + 1
+    lo = np.zeros((b * hk, rmax, d), np.int8)
+    up = np.zeros((b * hk, rmax, d), np.int8)
+    smax = np.zeros((b * hk, rmax), np.float32)
+    nmax = np.zeros((b * hk, rmax), np.float64)
+    load().oracle_block_summaries(b, n_q_heads, hk, d, block, n, ctx_len, _p(hi), _p(keep), hi.size, _p(k), _p(lo),
+                                  _p(up), _p(smax), _p(nmax), threads or nthreads())
+    return lo, up, smax, nmax
+
+
+def skip_masks(k, q, hi, keep, block: int, ctx_len: int, thresholds, sm_scale: float,
+               threads: Optional[int] = None) -> np.ndarray:
+    """Per stored record (record order), bit i = query head g*G + i keeps it: uint32 [P][rmax]."""
+    k, q = _c(k, np.uint16), _c(q, np.uint16)
+    b, hk, n, d = k.shape
+    hq = q.shape[1]
+    hi, keep = _c(hi, np.int32), _c(keep, np.int32)
+    th = _c(thresholds, np.float32)
+    assert th.size == b * hq
+    rmax = (ctx_len - 1) // block + 1
+    masks = np.zeros((b * hk, rmax), np.uint32)
+    if load().oracle_skip_masks(b, hq, hk, d, block, n, ctx_len, _p(hi), _p(keep), hi.size, _p(k), _p(q), _p(th),
+                                sm_scale, _p(masks), threads or nthreads()):
+        raise ValueError("more than 32 query heads per KV head")
+    return masks
+
+
+def decode_skip(k, v, q, hi, keep, block: int, ctx_len: int, thresholds, sm_scale: float,
+                threads: Optional[int] = None):
+    """Decode with dynamic block skipping: out f32 [b][Hq][d]."""
+    k, v, q = _c(k, np.uint16), _c(v, np.uint16), _c(q, np.uint16)
+    b, hk, n, d = k.shape
+    hq = q.shape[1]
+    hi, keep = _c(hi, np.int32), _c(keep, np.int32)
+    th = _c(thresholds, np.float32)
+    assert th.size == b * hq
+    out = np.empty((b, hq, d), dtype=np.float32)
+    if load().oracle_decode_skip(b, hq, hk, d, block, n, ctx_len, _p(hi), _p(keep), hi.size, _p(k), _p(v), _p(q),
+                                 _p(th), sm_scale, _p(out), threads or nthreads()):
+        raise ValueError("more than 32 query heads per KV head")
     return out
 
 

@@ -436,6 +436,119 @@ static void stored_sets(int64_t c, int64_t hi, int64_t keep, std::vector<int64_t
   }
 }
 
+// ============================================================ (f4) dynamic block skipping
+// Source: rit.work page on ETA (Elastic Threshold Attention), section on how the
+// model decides which part of the context to read: before a block is loaded, a few
+// statistics of it (mean key, per-coordinate spread, largest key norm) give an upper
+// bound on any of its scores; a block whose bound falls below the head's threshold
+// is not read at all.  Same page: the whole cache stays stored, the statistics are
+// a small extra index.
+//
+// Readings (also in the design notes): the statistics are taken over the stored
+// codes of each stored block (all its rows; rows past ctx_len are zero), as
+//   lo[x], hi[x]  per-coordinate minimum and maximum code  (mean +- spread, as a box)
+//   smax          the largest row scale
+//   nmax          the largest (sk * sk) * |kc|^2 over rows, in double
+// For query head h (codes qc, scale sq at the block's precision) and a threshold
+// theta in logit units (sm_scale * q.k), with t = sm_scale * sq (double):
+//   box  = (t * smax) * max(sum_x max(qc_x lo_x, qc_x hi_x), 0)     >= any score
+//   norm = ((t * t) * |qc|^2) * nmax                                 >= any score^2
+// and the block is skipped for h iff theta > 0 and (box < theta or norm < theta^2).
+// The first key block and the current block are never skipped (the blocks the tile
+// rule always keeps).  A KV head's block is read if any of its query heads keeps it;
+// each head attends over the blocks it keeps.
+struct Summary {
+  std::vector<int8_t> lo, hi;
+  float smax = 0.0f;
+  double nmax = 0.0;
+};
+
+static Summary summarise_block(const uint16_t* krows, int64_t first_tok, int64_t ctx_len, int block, int d, int qmax) {
+  Summary s;
+  s.lo.assign(d, 0);
+  s.hi.assign(d, 0);
+  std::vector<int8_t> kc(d);
+  bool first = true;
+  for (int r = 0; r < block; ++r) {
+    float sk = 0.0f;
+    std::fill(kc.begin(), kc.end(), 0);
+    if (first_tok + r < ctx_len) quantize_row(krows + static_cast<int64_t>(r) * d, d, qmax, kc.data(), &sk);
+    int64_t n2 = 0;
+    for (int x = 0; x < d; ++x) {
+      n2 += static_cast<int64_t>(kc[x]) * kc[x];
+      s.lo[x] = first ? kc[x] : std::min(s.lo[x], kc[x]);
+      s.hi[x] = first ? kc[x] : std::max(s.hi[x], kc[x]);
+    }
+    first = false;
+    s.smax = std::max(s.smax, sk);
+    s.nmax = std::max(s.nmax, (static_cast<double>(sk) * static_cast<double>(sk)) * static_cast<double>(n2));
+  }
+  return s;
+}
+
+// Stored blocks of KV head g in cache record order: int8 blocks ascending, then int4.
+static void record_order(int64_t c, int64_t hi, int64_t keep, std::vector<int64_t>& blocks, std::vector<int>& qmaxs) {
+  std::vector<int64_t> b8, b4;
+  stored_sets(c, hi, keep, b8, b4);
+  blocks = b8;
+  blocks.insert(blocks.end(), b4.begin(), b4.end());
+  qmaxs.assign(b8.size(), 127);
+  qmaxs.insert(qmaxs.end(), b4.size(), 7);
+}
+
+static bool skip_for_head(const Summary& s, const int8_t* qc, float sq, float sm_scale, float theta, int d) {
+  int64_t box = 0, q2 = 0;
+  for (int x = 0; x < d; ++x) {
+    box += std::max(static_cast<int64_t>(qc[x]) * s.lo[x], static_cast<int64_t>(qc[x]) * s.hi[x]);
+    q2 += static_cast<int64_t>(qc[x]) * qc[x];
+  }
+  const double t = static_cast<double>(sm_scale) * static_cast<double>(sq);
+  const double bound = (t * static_cast<double>(s.smax)) * static_cast<double>(std::max<int64_t>(box, 0));
+  const double norm2 = ((t * t) * static_cast<double>(q2)) * s.nmax;
+  const double th = theta;
+  return th > 0.0 && (bound < th || norm2 < th * th);
+}
+
+// Keep masks of every stored record: bit i of masks[p * rmax + r] set = query head
+// g*G + i keeps record r of pair p = b * n_kv_heads + g.  rmax = c + 1.
+static void skip_masks(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n, int64_t ctx_len,
+                       const std::vector<int64_t>& hk, const std::vector<int64_t>& kk, const uint16_t* k,
+                       const uint16_t* q, const float* thresholds, float sm_scale, uint32_t* masks, int nthreads) {
+  const int G = n_q_heads / n_kv_heads;
+  const int64_t c = (ctx_len - 1) / block, rmax = c + 1;
+  parallel_for(static_cast<int64_t>(batch) * n_kv_heads, nthreads, [&](int64_t p) {
+    const int b = static_cast<int>(p / n_kv_heads), g = static_cast<int>(p % n_kv_heads);
+    std::vector<int64_t> blocks;
+    std::vector<int> qmaxs;
+    record_order(c, hk[g], kk[g], blocks, qmaxs);
+    std::vector<int8_t> qc8(static_cast<size_t>(G) * d), qc4(static_cast<size_t>(G) * d);
+    std::vector<float> sq8(G), sq4(G);
+    for (int i = 0; i < G; ++i) {
+      const uint16_t* qr = q + (static_cast<int64_t>(b) * n_q_heads + g * G + i) * d;
+      quantize_row(qr, d, 127, &qc8[static_cast<size_t>(i) * d], &sq8[i]);
+      quantize_row(qr, d, 7, &qc4[static_cast<size_t>(i) * d], &sq4[i]);
+    }
+    const int64_t src = (static_cast<int64_t>(b) * n_kv_heads + g) * n;
+    for (int64_t r = 0; r < rmax; ++r) masks[p * rmax + r] = 0;
+    for (size_t r = 0; r < blocks.size(); ++r) {
+      const int64_t kb = blocks[r];
+      uint32_t m = 0;
+      if (kb == 0 || kb == c) {
+        m = G == 32 ? 0xFFFFFFFFu : ((1u << G) - 1u);
+      } else {
+        const Summary s = summarise_block(k + (src + kb * block) * d, kb * block, ctx_len, block, d, qmaxs[r]);
+        for (int i = 0; i < G; ++i) {
+          const bool is8 = qmaxs[r] == 127;
+          const int8_t* qc = is8 ? &qc8[static_cast<size_t>(i) * d] : &qc4[static_cast<size_t>(i) * d];
+          const float th = thresholds[static_cast<int64_t>(b) * n_q_heads + g * G + i];
+          if (!skip_for_head(s, qc, is8 ? sq8[i] : sq4[i], sm_scale, th, d)) m |= 1u << i;
+        }
+      }
+      masks[p * rmax + static_cast<int64_t>(r)] = m;
+    }
+  });
+}
+
 int64_t oracle_cache_bytes(int batch, int n_q_heads, int n_kv_heads, int d, int block,
                            int64_t ctx_len, const int32_t* hi, const int32_t* keep,
                            int n_policy_heads) {
@@ -522,12 +635,12 @@ int oracle_pack_cache(int batch, int n_q_heads, int n_kv_heads, int d, int block
 // One query token at t = ctx_len - 1 per sequence.  Works from the raw bf16 K/V
 // and the policy (it never reads a packed cache): the stored set of block c, the
 // query quantised at each precision, exact integer dots, softmax in double.
-int oracle_decode(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
-                  int64_t ctx_len, const int32_t* hi, const int32_t* keep, int n_policy_heads,
-                  const uint16_t* k, const uint16_t* v, const uint16_t* q, float sm_scale,
-                  float* out, int nthreads) {
-  std::vector<int64_t> hk, kk;
-  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+// The decode of every (b, h); masks (or null): per stored record, the query heads
+// of its KV head that keep it (the dynamic skipping below).
+static int decode_masked(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n, int64_t ctx_len,
+                         const std::vector<int64_t>& hk, const std::vector<int64_t>& kk, const uint16_t* k,
+                         const uint16_t* v, const uint16_t* q, float sm_scale, float* out, const uint32_t* masks,
+                         int nthreads) {
   const int G = n_q_heads / n_kv_heads;
   const int64_t t_pos = ctx_len - 1, c = t_pos / block;
   parallel_for(static_cast<int64_t>(batch) * n_q_heads, nthreads, [&](int64_t bh) {
@@ -538,12 +651,19 @@ int oracle_decode(int batch, int n_q_heads, int n_kv_heads, int d, int block, in
     quantize_row(q + bh * d, d, 127, qc8.data(), &sq8);
     quantize_row(q + bh * d, d, 7, qc4.data(), &sq4);
     const int64_t src = (static_cast<int64_t>(b) * n_kv_heads + g) * n;
+    // record index of each stored block (for the masks)
+    std::vector<int64_t> rec_of(static_cast<size_t>(c + 1), -1), blocks;
+    std::vector<int> qmaxs;
+    record_order(c, hk[g], kk[g], blocks, qmaxs);
+    for (size_t r = 0; r < blocks.size(); ++r) rec_of[static_cast<size_t>(blocks[r])] = static_cast<int64_t>(r);
+    const int64_t pair_rec0 = (static_cast<int64_t>(b) * n_kv_heads + g) * (c + 1);
     std::vector<double> s;
     std::vector<int64_t> toks;
     std::vector<int> prec;
     for (int64_t j = 0; j <= t_pos; ++j) {
       const int a = tile_action(c, j / block, hk[g], kk[g]);
       if (a == ACT_SKIP) continue;
+      if (masks && !((masks[pair_rec0 + rec_of[static_cast<size_t>(j / block)]] >> (h % G)) & 1u)) continue;
       const int qmax = a == ACT_INT8 ? 127 : 7;
       quantize_row(k + (src + j) * d, d, qmax, kc.data(), &sk);
       const int8_t* qc = a == ACT_INT8 ? qc8.data() : qc4.data();
@@ -566,6 +686,16 @@ int oracle_decode(int batch, int n_q_heads, int n_kv_heads, int d, int block, in
     for (int y = 0; y < d; ++y) out[bh * d + y] = static_cast<float>(o[y] / den);
   });
   return 0;
+}
+
+int oracle_decode(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
+                  int64_t ctx_len, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                  const uint16_t* k, const uint16_t* v, const uint16_t* q, float sm_scale,
+                  float* out, int nthreads) {
+  std::vector<int64_t> hk, kk;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  return decode_masked(batch, n_q_heads, n_kv_heads, d, block, n, ctx_len, hk, kk, k, v, q, sm_scale, out, nullptr,
+                       nthreads);
 }
 
 
@@ -649,6 +779,67 @@ int oracle_allocate_policy(int64_t n, int block, int H, int K, const double* err
   *total_cost = total;
   *total_err = es;
   return 0;
+}
+
+
+// Statistics of every stored record (record order as in the cache; rmax = c + 1
+// slots per pair, unused slots zero): lo, hi [P][rmax][d], smax, nmax [P][rmax].
+int oracle_block_summaries(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
+                           int64_t ctx_len, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                           const uint16_t* k, int8_t* lo, int8_t* hi_out, float* smax, double* nmax,
+                           int nthreads) {
+  std::vector<int64_t> hk, kk;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  const int64_t c = (ctx_len - 1) / block, rmax = c + 1;
+  parallel_for(static_cast<int64_t>(batch) * n_kv_heads, nthreads, [&](int64_t p) {
+    const int g = static_cast<int>(p % n_kv_heads);
+    std::vector<int64_t> blocks;
+    std::vector<int> qmaxs;
+    record_order(c, hk[g], kk[g], blocks, qmaxs);
+    const int64_t src = p * n;
+    for (int64_t r = 0; r < rmax; ++r) {
+      Summary s;
+      if (r < static_cast<int64_t>(blocks.size()))
+        s = summarise_block(k + (src + blocks[r] * block) * d, blocks[r] * block, ctx_len, block, d, qmaxs[r]);
+      else {
+        s.lo.assign(d, 0);
+        s.hi.assign(d, 0);
+      }
+      std::memcpy(lo + (p * rmax + r) * d, s.lo.data(), static_cast<size_t>(d));
+      std::memcpy(hi_out + (p * rmax + r) * d, s.hi.data(), static_cast<size_t>(d));
+      smax[p * rmax + r] = s.smax;
+      nmax[p * rmax + r] = s.nmax;
+    }
+  });
+  return 0;
+}
+
+int oracle_skip_masks(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n, int64_t ctx_len,
+                      const int32_t* hi, const int32_t* keep, int n_policy_heads, const uint16_t* k,
+                      const uint16_t* q, const float* thresholds, float sm_scale, uint32_t* masks, int nthreads) {
+  if (n_q_heads / n_kv_heads > 32) return -1;
+  std::vector<int64_t> hk, kk;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  skip_masks(batch, n_q_heads, n_kv_heads, d, block, n, ctx_len, hk, kk, k, q, thresholds, sm_scale, masks, nthreads);
+  return 0;
+}
+
+// Decode with dynamic skipping: as oracle_decode, each query head attending only
+// over the tokens of the stored blocks it keeps (the masks above).
+int oracle_decode_skip(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n,
+                       int64_t ctx_len, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                       const uint16_t* k, const uint16_t* v, const uint16_t* q, const float* thresholds,
+                       float sm_scale, float* out, int nthreads) {
+  const int G = n_q_heads / n_kv_heads;
+  if (G > 32) return -1;
+  std::vector<int64_t> hk, kk;
+  kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
+  const int64_t c = (ctx_len - 1) / block, rmax = c + 1;
+  std::vector<uint32_t> masks(static_cast<size_t>(batch) * n_kv_heads * rmax);
+  skip_masks(batch, n_q_heads, n_kv_heads, d, block, n, ctx_len, hk, kk, k, q, thresholds, sm_scale, masks.data(),
+             nthreads);
+  return decode_masked(batch, n_q_heads, n_kv_heads, d, block, n, ctx_len, hk, kk, k, v, q, sm_scale, out,
+                       masks.data(), nthreads);
 }
 
 }  // extern "C"

@@ -27,6 +27,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 TID_Q, TID_K, TID_V, TID_OUTLIER, TID_POLICY, TID_DECODE_Q = 1, 2, 3, 4, 5, 6
+TID_BLOCK_MAG, TID_GAMMA = 7, 8
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -195,3 +196,30 @@ def make_decode_inputs(cfg: Config):
     v = normal_bf16(cfg.seed, TID_V, b * hk * n * d).reshape(b, hk, n, d)
     q = normal_bf16(cfg.seed, TID_DECODE_Q, b * hq * d).reshape(b, hq, d)
     return k, v, q
+
+
+def make_skip_decode_inputs(cfg: Config, mag_range: tuple[float, float] = (0.1, 1.0),
+                            gamma_range: tuple[float, float] = (0.6, 0.9)):
+    """Decode inputs with block structure, for dynamic block skipping.
+
+    K [b][Hkv][ctx][d]: N(0,1) rows times one magnitude per (b, KV head, block),
+    uniform on mag_range (stream 7); V and q as make_decode_inputs.  thresholds
+    [b][Hq] (fp32, logit units): gamma * ||q_bh||_2 with gamma uniform on
+    gamma_range per (b, h) (stream 8) -- with sm_scale = 1/sqrt(d) a block of
+    magnitude m has scores of order m * ||q|| * |cos|, so gamma sets how many blocks
+    a head keeps (a stand-in for a learned per-head, per-query threshold).
+    Returns k, v, q (bf16 bits) and thresholds.
+    """
+    b, hq, hk, d, n, blk = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.block
+    k, v, q = make_decode_inputs(cfg)
+    nb = (n + blk - 1) // blk
+    u = _open_unit(uniform_u64(cfg.seed, TID_BLOCK_MAG, 0, b * hk * nb)).reshape(b, hk, nb)
+    mag = (mag_range[0] + (mag_range[1] - mag_range[0]) * u).astype(np.float32)
+    kf = bf16_bits_to_float32(k).reshape(b, hk, n, d)
+    scale = np.repeat(mag, blk, axis=2)[:, :, :n, None]
+    k = float32_to_bf16_bits(kf * scale).reshape(b, hk, n, d)
+    g = _open_unit(uniform_u64(cfg.seed, TID_GAMMA, 0, b * hq)).reshape(b, hq)
+    gamma = gamma_range[0] + (gamma_range[1] - gamma_range[0]) * g
+    qn = np.sqrt((bf16_bits_to_float32(q).astype(np.float64) ** 2).sum(axis=-1))
+    thresholds = (gamma * qn).astype(np.float32)
+    return k, v, q, thresholds
