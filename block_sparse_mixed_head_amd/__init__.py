@@ -24,7 +24,8 @@ from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
 __all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "prefill", "prefill_varlen", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
            "kv_cache_bytes_varlen", "pack_kv_cache_varlen", "decode_varlen",
-           "check_cache", "decode_workspace_bytes", "decode", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
+           "check_cache", "decode_workspace_bytes", "decode", "block_summaries_bytes", "build_block_summaries",
+           "skip_masks", "decode_skip_workspace_bytes", "decode_skip", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
 Dims = _lib.Dims
@@ -254,6 +255,61 @@ def decode_varlen(d: Dims, cache: torch.Tensor, q: torch.Tensor, sm_scale: float
         workspace = torch.empty(decode_workspace_bytes(d, d.seq_len), dtype=torch.uint8, device=q.device)
     check(_lib.lib.tria_decode_varlen(C.byref(d), _ptr(cache), cache.numel(), _ptr(q), float(sm_scale), _ptr(out),
                                       _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out
+
+
+# ------------------------------------------------------------------ dynamic block skipping
+def block_summaries_bytes(d: Dims, ctx_len: int) -> int:
+    out = C.c_size_t(0)
+    check(_lib.lib.tria_block_summaries_bytes(C.byref(d), ctx_len, C.byref(out)))
+    return out.value
+
+
+def build_block_summaries(d: Dims, cache: torch.Tensor, ctx_len: int,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Statistics index of a cache (uint8 device buffer, tria_block_summaries_bytes)."""
+    if out is None:
+        out = torch.zeros(block_summaries_bytes(d, ctx_len), dtype=torch.uint8, device=cache.device)
+    check(_lib.lib.tria_build_block_summaries(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(out), out.numel(),
+                                              _stream(cache.device)))
+    return out
+
+
+def skip_masks(d: Dims, cache: torch.Tensor, ctx_len: int, summaries: torch.Tensor, q: torch.Tensor,
+               thresholds: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Keep bits per stored record: int32 view of uint32 [batch * n_kv_heads][rmax]."""
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    _require(thresholds, torch.float32, (b, hq), "thresholds")
+    rmax = (ctx_len - 1) // d.block + 1
+    if out is None:
+        out = torch.zeros((b * d.n_kv_heads, rmax), dtype=torch.int32, device=q.device)
+    check(_lib.lib.tria_skip_masks(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(summaries),
+                                   summaries.numel(), _ptr(q), _ptr(thresholds), float(sm_scale), _ptr(out),
+                                   out.numel() * 4, _stream(q.device)))
+    return out
+
+
+def decode_skip_workspace_bytes(d: Dims, ctx_len: int) -> int:
+    out = C.c_size_t(0)
+    check(_lib.lib.tria_decode_skip_workspace_bytes(C.byref(d), ctx_len, C.byref(out)))
+    return out.value
+
+
+def decode_skip(d: Dims, cache: torch.Tensor, ctx_len: int, summaries: torch.Tensor, q: torch.Tensor,
+                thresholds: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode reading only the records some query head keeps (fp32 [b][Hq][d])."""
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    _require(thresholds, torch.float32, (b, hq), "thresholds")
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_skip_workspace_bytes(d, ctx_len), dtype=torch.uint8, device=q.device)
+    check(_lib.lib.tria_decode_skip(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(summaries),
+                                    summaries.numel(), _ptr(q), _ptr(thresholds), float(sm_scale), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out
 
 

@@ -55,6 +55,11 @@ def _load() -> C.CDLL:
         "tria_policy_cost": (C.c_int, [D, i32, i32, C.c_double, C.c_double, C.POINTER(C.c_double)]),
         "tria_allocate_policy": (C.c_int, [D, i32, i32, P, C.c_double, C.c_double, C.c_double, P, P,
                                            C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+        "tria_block_summaries_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
+        "tria_build_block_summaries": (C.c_int, [D, P, sz, i64, P, sz, P]),
+        "tria_skip_masks": (C.c_int, [D, P, sz, i64, P, sz, P, P, f32, P, sz, P]),
+        "tria_decode_skip_workspace_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
+        "tria_decode_skip": (C.c_int, [D, P, sz, i64, P, sz, P, P, f32, P, P, sz, P]),
         "tria_peak_mfma": (C.c_int, [i32, i32, P, C.POINTER(C.c_double), P]),
         "tria_peak_read": (C.c_int, [P, i64, P, C.POINTER(C.c_double), P]),
     }
@@ -72,7 +77,8 @@ EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quanti
             "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_update_kv_cache", "tria_check_cache",
             "tria_kv_cache_bytes_varlen", "tria_pack_kv_cache_varlen", "tria_decode_varlen",
             "tria_decode_workspace_bytes", "tria_decode", "tria_policy_cost", "tria_allocate_policy",
-            "tria_peak_mfma", "tria_peak_read"]
+            "tria_block_summaries_bytes", "tria_build_block_summaries", "tria_skip_masks",
+            "tria_decode_skip_workspace_bytes", "tria_decode_skip", "tria_peak_mfma", "tria_peak_read"]
 PEAK_READ_ALIGN = 8192 * 8 * 1024
 PEAK_SINK_INTS = 8192
 

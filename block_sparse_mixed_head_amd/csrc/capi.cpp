@@ -615,6 +615,99 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
                   "decode launch");
 }
 
+// ------------------------------------------------------------------ (f4) dynamic block skipping
+static tria_status check_skip_call(const tria_dims* dims, int64_t ctx_len, const void* cache, size_t cache_bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(cache);
+  if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  if (dims->n_q_heads / dims->n_kv_heads > 32) return fail(TRIA_ERR_UNSUPPORTED, "more than 32 query heads per KV head");
+  if ((int64_t)dims->batch * dims->n_kv_heads > 4096) return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads above 4096");
+  const int64_t dir_end = 64 + 64LL * dims->batch * dims->n_kv_heads;
+  if ((int64_t)cache_bytes < dir_end) return fail(TRIA_ERR_BUFFER_TOO_SMALL, "cache smaller than its directory");
+  const tria::Shape s = shape_of(dims);
+  if (!tria::decode_units_fit(s, ctx_len))
+    return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads * ctx_len too large for one decode call");
+  const int64_t slots = (int64_t)dims->batch * dims->n_kv_heads * ((ctx_len - 1) / dims->block + 1);
+  if (slots > INT32_MAX / 2) return fail(TRIA_ERR_UNSUPPORTED, "too many record slots");
+  return TRIA_OK;
+}
+
+tria_status tria_block_summaries_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  *bytes = (size_t)tria::summaries_bytes(shape_of(dims), ctx_len);
+  return ok();
+}
+
+tria_status tria_build_block_summaries(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                                       void* summaries, size_t summaries_bytes, void* stream) {
+  tria_status st = check_skip_call(dims, ctx_len, cache, cache_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(summaries);
+  const int64_t need = tria::summaries_bytes(shape_of(dims), ctx_len);
+  if ((int64_t)summaries_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "summaries need %lld bytes, got %zu", (long long)need, summaries_bytes);
+  return launched(tria::launch_summaries(shape_of(dims), ctx_len, cache, (int64_t)cache_bytes, summaries,
+                                         static_cast<hipStream_t>(stream)),
+                  "summaries launch");
+}
+
+tria_status tria_skip_masks(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                            const void* summaries, size_t summaries_bytes, const void* q_bf16, const float* thresholds,
+                            float sm_scale, uint32_t* masks, size_t masks_bytes, void* stream) {
+  tria_status st = check_skip_call(dims, ctx_len, cache, cache_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(summaries);
+  NONNULL(q_bf16);
+  NONNULL(thresholds);
+  NONNULL(masks);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const tria::Shape s = shape_of(dims);
+  if ((int64_t)summaries_bytes < tria::summaries_bytes(s, ctx_len))
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "summaries smaller than tria_block_summaries_bytes");
+  const int64_t need = 4LL * dims->batch * dims->n_kv_heads * ((ctx_len - 1) / dims->block + 1);
+  if ((int64_t)masks_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "masks need %lld bytes, got %zu", (long long)need, masks_bytes);
+  return launched(tria::launch_skip_masks(s, ctx_len, cache, (int64_t)cache_bytes, summaries, q_bf16, thresholds,
+                                          sm_scale, masks, static_cast<hipStream_t>(stream)),
+                  "skip masks launch");
+}
+
+tria_status tria_decode_skip_workspace_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  *bytes = (size_t)tria::skip_workspace_bytes(shape_of(dims), ctx_len);
+  return ok();
+}
+
+tria_status tria_decode_skip(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                             const void* summaries, size_t summaries_bytes, const void* q_bf16,
+                             const float* thresholds, float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  tria_status st = check_skip_call(dims, ctx_len, cache, cache_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(summaries);
+  NONNULL(q_bf16);
+  NONNULL(thresholds);
+  NONNULL(out);
+  NONNULL(workspace);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const tria::Shape s = shape_of(dims);
+  if ((int64_t)summaries_bytes < tria::summaries_bytes(s, ctx_len))
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "summaries smaller than tria_block_summaries_bytes");
+  const int64_t need = tria::skip_workspace_bytes(s, ctx_len);
+  if ((int64_t)ws_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "skip workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
+  return launched(tria::launch_decode_skip(s, ctx_len, cache, (int64_t)cache_bytes, summaries, q_bf16, thresholds,
+                                           sm_scale, out, workspace, static_cast<hipStream_t>(stream)),
+                  "skip decode launch");
+}
+
 tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes, const void* q_bf16,
                                float sm_scale, float* out, void* workspace, size_t ws_bytes, void* stream) {
   tria_status st = check_dims(dims);

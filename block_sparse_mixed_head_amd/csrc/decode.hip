@@ -32,6 +32,7 @@
 //   * Both kernels validate the cache header and directory before reading any
 //     record; on a mismatch nothing is read and the merge writes NaN.
 #include <cfloat>
+#include <cstdlib>
 #include <type_traits>
 
 #include "device_common.h"
@@ -66,6 +67,8 @@ struct DecArgs {
   int batch, hq, hkv;
   float c;     // sm_scale * log2(e)
   int varlen;  // version-3 cache: each directory entry holds its sequence's ctx_len
+  const int* plan;  // dynamic skipping: per pair {offset, kept and stored counts, mask}, kept lists
+  int rmax;         // record slots per pair in the plan's lists
 };
 
 struct Geo {
@@ -223,7 +226,7 @@ __device__ __forceinline__ v8h v4_to_f16(uint32_t w) {
 template <int D, int RG, bool IS4>
 __device__ __forceinline__ void compute_step(const typename std::conditional<IS4, Buf4<D>, Buf8<D>>::type& r,
                                              const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_from,
-                                             SegState<D, RG>& st, int kq, float* slot) {
+                                             SegState<D, RG>& st, int kq, float* slot, uint32_t hoff) {
   constexpr int KS = D / 64, ND = D / 16;
   // the step's scales through the wave's LDS slot (one wavefront: in order, no barrier)
   slot[threadIdx.x & 63] = __int_as_float(r.sc);
@@ -265,6 +268,16 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
         for (int i = 0; i < 4; ++i)
           if (16 * s + 4 * kq + i >= mask_from) u[rg][s][i] = -INFINITY;
   }
+  if (hoff) {  // query rows (bit rg*16 + lr) that skip this block (wave-uniform branch)
+    const int lr = threadIdx.x & 15;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      if ((hoff >> (rg * 16 + lr)) & 1u)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u[rg][s][i] = -INFINITY;
+  }
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     float x = fmaxf(fmaxf(u[rg][0][0], u[rg][0][1]), fmaxf(u[rg][0][2], u[rg][0][3]));
@@ -278,7 +291,9 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       const float mn = fmaxf(st.m[rg], mt[rg]);
-      const float f = __builtin_amdgcn_exp2f(st.m[rg] - mn);  // 0 while m was -inf
+      // 0 while m was -inf; a row still without any key (every key so far masked or
+      // skipped for it) keeps its zero sums (exp2(-inf - -inf) would be NaN)
+      const float f = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[rg] - mn);
       st.m[rg] = mn;
       st.l[rg] *= f;
       st.c[rg] *= f;
@@ -355,21 +370,84 @@ __device__ __forceinline__ void compute_step(const typename std::conditional<IS4
   }
 }
 
+// Subtracts the V-code bias from O (c summed over the four lanes of each query row)
+// and restarts c: O then holds only the segment's true partial sums, so fp32 rounding
+// stays relative to them however many keys a segment has (once per ring trip).
+template <int D, int RG>
+__device__ __forceinline__ void fold_bias(SegState<D, RG>& st) {
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const float c = xsum32(xsum16(st.c[rg]));
+#pragma unroll
+    for (int d = 0; d < D / 16; ++d) st.O[rg][d] -= c;
+    st.c[rg] = 0.0f;
+  }
+}
+
 // Steps [j0, j1) of one precision run of a pair; rec0 = the run's first record.
 // A ring of three register buffers keeps the loads of the next two steps in
 // flight while a step is computed; `pre` runs once the first loads are issued
 // (the segment's query quantisation).  Loads past the run's end fetch nothing,
 // so every record byte is read once.
-template <int D, int BLK, int RG, bool IS4, class Pre>
+// SKIP: steps count the run's kept records only; kept record i is stored record
+// list[i].x (of nstored) and list[i].y has bit r set when query row r keeps it.
+template <int D, int BLK, int RG, bool IS4, bool SKIP, class Pre>
 __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes, int j0, int j1,
                                           const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_jb,
-                                          int mask_first, SegState<D, RG>& st, int lr, int kq, float* slot, Pre&& pre) {
+                                          int mask_first, SegState<D, RG>& st, int lr, int kq, float* slot, Pre&& pre,
+                                          const int2* list, int nstored, uint32_t hfull) {
   using IO = StepIO<D, BLK, IS4>;
   constexpr int SPB = BLK / 32;
   if (j0 >= j1) return;
   j0 = uni(j0);
   j1 = uni(j1);
   const int rb = uni((int)rec_bytes);
+  // keys of step j at or past which keys are masked: only the current block's
+  // tail (ctx_len is inside block mask_jb of this run) is masked
+  auto mfrom = [&](int j) __attribute__((always_inline)) -> int {
+    return j / SPB == mask_jb ? mask_first - 32 * (j % SPB) : 1 << 30;
+  };
+  if constexpr (SKIP) {
+    // every stored record of the run is addressable; only kept ones are loaded (the
+    // resource is built per load with the range or, past the window, an empty range)
+    void* const base = reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(rec0)));
+    const int nbytes = uni(nstored * rb);
+    const int lane = threadIdx.x & 63;
+    typename IO::Buf A, B, C;
+    pre();
+    // windows of up to 64 kept records: lane l holds the window's entry l, read by
+    // the whole wavefront with readlane (uniform index, no memory access per step)
+    for (int w0 = j0; w0 < j1;) {
+      const int r0 = uni(w0 / SPB);
+      const int w1 = uni((r0 + 64) * SPB < j1 ? (r0 + 64) * SPB : j1);
+      const int rlast = (w1 - 1) / SPB;
+      const int2 e = r0 + lane <= rlast ? list[r0 + lane] : make_int2(0, 0);
+      auto ld = [&](typename IO::Buf& r, int j) __attribute__((always_inline)) {
+        const bool in = j < w1;
+        const int rec = in ? __builtin_amdgcn_readlane(e.x, j / SPB - r0) : 0;
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, in ? nbytes : 0, 0x00020000);
+        __builtin_amdgcn_sched_barrier(0);
+        IO::load(r, rr, in ? rec * rb : 0, in ? j % SPB : 0, lr, kq);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto hoff = [&](int j) __attribute__((always_inline)) -> uint32_t {
+        return hfull & ~(uint32_t)__builtin_amdgcn_readlane(e.y, j / SPB - r0);
+      };
+      for (int j = w0; j < w1 + 2; j += 3) {
+        if (((j / 3) + (blockIdx.x >= gridDim.x / 2)) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+        ld(A, j);
+        if (j - 2 >= w0 && j - 2 < w1) compute_step<D, RG, IS4>(B, qop, ar, mfrom(j - 2), st, kq, slot, hoff(j - 2));
+        ld(B, j + 1);
+        if (j - 1 >= w0 && j - 1 < w1) compute_step<D, RG, IS4>(C, qop, ar, mfrom(j - 1), st, kq, slot, hoff(j - 1));
+        ld(C, j + 2);
+        if (j < w1) compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq, slot, hoff(j));
+        fold_bias(st);
+      }
+      w0 = w1;
+    }
+    return;
+  }
   // the run's records as one buffer resource (dword 3: raw 32-bit data format)
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(rec0))), (short)0, uni((j1 + SPB - 1) / SPB * rb), 0x00020000);
@@ -387,11 +465,6 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     IO::load(r, in ? rs : none, in ? (j / SPB) * rb : 0, in ? j % SPB : 0, lr, kq);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // keys of step j at or past which keys are masked: only the current block's
-  // tail (ctx_len is inside block mask_jb of this run) is masked
-  auto mfrom = [&](int j) __attribute__((always_inline)) -> int {
-    return j / SPB == mask_jb ? mask_first - 32 * (j % SPB) : 1 << 30;
-  };
   pre();
   // Step j is loaded into buffer (j - j0) % 3 and computed two loads later, so
   // two steps are in flight during each compute.  Loads and their uses both sit
@@ -405,11 +478,12 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     if (((j / 3) + (blockIdx.x >= gridDim.x / 2)) & 1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
     ld(A, j);
-    if (j - 2 >= j0 && j - 2 < j1) compute_step<D, RG, IS4>(B, qop, ar, mfrom(j - 2), st, kq, slot);
+    if (j - 2 >= j0 && j - 2 < j1) compute_step<D, RG, IS4>(B, qop, ar, mfrom(j - 2), st, kq, slot, 0u);
     ld(B, j + 1);
-    if (j - 1 >= j0 && j - 1 < j1) compute_step<D, RG, IS4>(C, qop, ar, mfrom(j - 1), st, kq, slot);
+    if (j - 1 >= j0 && j - 1 < j1) compute_step<D, RG, IS4>(C, qop, ar, mfrom(j - 1), st, kq, slot, 0u);
     ld(C, j + 2);
-    if (j < j1) compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq, slot);
+    if (j < j1) compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq, slot, 0u);
+    fold_bias(st);
   }
 }
 
@@ -458,7 +532,10 @@ __device__ __forceinline__ void prefix2_lds(int* arr, int* brr, int P, int* tmp)
   __syncthreads();
 }
 
-template <int D, int BLK, int RG>
+// SKIP: the per-pair counts, offsets and kept-record lists come from the plan
+// written by the skip kernels below (which validated the directory), and the split
+// is over the kept records' units.
+template <int D, int BLK, int RG, bool SKIP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RG == 1 ? 2 : 1, 2)))
 decode_split_kernel(DecArgs a) {
   constexpr int KS = D / 64, ND = D / 16, SPB = BLK / 32;
@@ -476,12 +553,17 @@ decode_split_kernel(DecArgs a) {
   const int P = a.batch * a.hkv;
   // the directory entry of pair tid is loaded together with the header (the host
   // checked that the directory lies inside the cache): one memory round trip
+  // (SKIP: the plan's pair entry, two vectors)
+  auto entry_ptr = [&](int p) __attribute__((always_inline)) -> const v4i* {
+    return SKIP ? reinterpret_cast<const v4i*>(a.plan + 8 * (int64_t)p)
+                : reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+  };
   v4i ent[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
   if (tid < P) {
-    const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)tid);
+    const v4i* e = entry_ptr(tid);
     ent[0] = e[0];
     ent[1] = e[1];
-    ent[2] = e[2];
+    if constexpr (!SKIP) ent[2] = e[2];
   }
   auto entry = [&](int p, v4i (&x)[3]) __attribute__((always_inline)) {
     if (p == tid) {
@@ -489,10 +571,10 @@ decode_split_kernel(DecArgs a) {
       x[1] = ent[1];
       x[2] = ent[2];
     } else {
-      const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+      const v4i* e = entry_ptr(p);
       x[0] = e[0];
       x[1] = e[1];
-      x[2] = e[2];
+      x[2] = SKIP ? v4i{0, 0, 0, 0} : e[2];
     }
   };
   Geo geo;
@@ -506,6 +588,16 @@ decode_split_kernel(DecArgs a) {
   for (int p = tid; p < P; p += kThreads) {
     v4i e[3];
     entry(p, e);
+    if constexpr (SKIP) {
+      // {offset lo, hi, kept int8, kept int4}, {stored int8, stored int4, mask, ok}
+      const int k8 = e[0][2], k4 = e[0][3], n8 = e[1][0], n4 = e[1][1], mf = e[1][2];
+      const bool ok = e[1][3] == 1 && k8 >= 1 && k4 >= 0 && k8 <= n8 && k4 <= n4 && mf >= 1 && mf <= BLK;
+      if (!ok) bad = 1;
+      n8p[p] = ok ? k8 : 0;
+      n4p[p] = ok ? k4 : 0;
+      mfp[p] = mf;
+      continue;
+    }
     const int n8 = e[0][2], n4 = e[0][3], lo8 = e[1][2], sink = e[1][3], lo4 = e[2][0];
     // the pair's position: the launch's ctx_len, or (version 3) its own
     const int64_t ctx = a.varlen ? (int64_t)(((uint64_t)(uint32_t)e[2][3] << 32) | (uint32_t)e[2][2]) : a.ctx_len;
@@ -539,7 +631,7 @@ decode_split_kernel(DecArgs a) {
     v4i e[3];
     entry(p, e);
     const int64_t off = (int64_t)(((uint64_t)(uint32_t)e[0][1] << 32) | (uint32_t)e[0][0]);
-    if (off != geo.data_offset + (int64_t)n8p[p] * geo.rec8 + (int64_t)n4p[p] * geo.rec4) bad = 1;
+    if (!SKIP && off != geo.data_offset + (int64_t)n8p[p] * geo.rec8 + (int64_t)n4p[p] * geo.rec4) bad = 1;
     const int64_t u0 = units_at(p), u1 = units_at(p + 1);
 #pragma unroll
     for (int i = 0; i < kWaves; ++i)
@@ -583,6 +675,17 @@ decode_split_kernel(DecArgs a) {
     const int b = p / a.hkv, gkv = p % a.hkv;
     const uint8_t* rec0 =
         a.cache + geo.data_offset + (int64_t)uni(n8p[p]) * geo.rec8 + (int64_t)uni(n4p[p]) * geo.rec4;
+    // SKIP: the pair's records start at its (validated) offset; n8s, n4s records stored
+    int n8s = n8, n4s = n4;
+    const int2* list = nullptr;
+    if constexpr (SKIP) {
+      const int* pe = a.plan + 8 * (int64_t)p;
+      rec0 = a.cache + (int64_t)(((uint64_t)(uint32_t)pe[1] << 32) | (uint32_t)pe[0]);
+      n8s = uni(pe[4]);
+      n4s = uni(pe[5]);
+      list = reinterpret_cast<const int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
+    }
+    const uint32_t hfull = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
 
     // this pair's G query rows, quantised at both precisions (MFMA B operands)
     v4i q8op[RG][KS], q4op[RG][KS];
@@ -645,12 +748,14 @@ decode_split_kernel(DecArgs a) {
     // the last int8 record is the current block; keys at or past ctx_len are masked
     const int mask_first = uni(mfp[p]);
     const bool has8 = j8a < j8b;
-    run_steps<D, BLK, RG, false>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq, scl[wave],
-                                 quantise_q);
-    run_steps<D, BLK, RG, true>(rec0 + (int64_t)n8 * geo.rec8, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq, scl[wave],
-                                [&]() __attribute__((always_inline)) {
-                                  if (!has8) quantise_q();
-                                });
+    run_steps<D, BLK, RG, false, SKIP>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq,
+                                       scl[wave], quantise_q, list, n8s, hfull);
+    run_steps<D, BLK, RG, true, SKIP>(rec0 + (int64_t)n8s * geo.rec8, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq,
+                                      scl[wave],
+                                      [&]() __attribute__((always_inline)) {
+                                        if (!has8) quantise_q();
+                                      },
+                                      SKIP ? list + n8 : nullptr, n4s, hfull);
 
     // ---- the wavefront's partial for this pair
 #pragma unroll
@@ -742,9 +847,356 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   dst[t] = o / l;
 }
 
-template <int D, int BLK, int RG>
+// ---- dynamic block skipping (ETA page, rit.work: section on how the model decides
+// which part of the context to read).  Per stored record a few statistics of its K
+// codes bound every score of the record; a record whose bound is below a query
+// head's threshold is skipped for that head, and a record every head of the group
+// skips is never read.
+//
+// Statistics index: a 64-byte header {magic, version 1, pairs, record slots per pair
+// (rmax = current block + 1), d, block, current block, 0, cache total bytes (int64)},
+// then per (pair, record slot) S = 2d + 16 bytes: lo[d], hi[d] (int8: per-coordinate
+// minimum and maximum code over the record's rows), the largest row scale (fp32), 0,
+// and the largest (scale * scale) * |codes|^2 over rows (fp64).
+constexpr int kSumMagic = 0x4D534254;  // "TBSM"
+__host__ __device__ constexpr int sum_stride(int d) { return 2 * d + 16; }
+
+struct SkipArgs {
+  const uint8_t* cache;
+  int64_t cache_bytes;
+  int64_t ctx_len;
+  const uint8_t* sums;
+  uint8_t* sums_out;
+  const uint16_t* q;
+  const float* th;
+  uint32_t* masks;  // [P][rmax] keep bits per stored record
+  int* plan;        // [P][8] pair entries, then [P][rmax] kept {record, mask} lists
+  float sm;
+  int batch, hq, hkv, rmax, nwin;
+};
+
+template <int D, int BLK>
+__device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
+  DecArgs a{};
+  a.cache = s.cache;
+  a.cache_bytes = s.cache_bytes;
+  a.ctx_len = s.ctx_len;
+  a.batch = s.batch;
+  a.hkv = s.hkv;
+  a.varlen = 0;
+  return header_ok<D, BLK>(a, geo);
+}
+
+// The index describes this cache's records: same pairs, slots, shape, current block
+// and total size (statistics of the current block itself are never used).
+template <int D, int BLK>
+__device__ __forceinline__ bool sums_ok(const SkipArgs& s, const Geo& geo) {
+  const int32_t* h = reinterpret_cast<const int32_t*>(s.sums);
+  const int64_t* h64 = reinterpret_cast<const int64_t*>(s.sums);
+  return h[0] == kSumMagic && h[1] == 1 && h[2] == s.batch * s.hkv && h[3] == s.rmax && h[4] == D && h[5] == BLK &&
+         h[6] == geo.cur && h64[4] == geo.total;
+}
+
+// One work group per (pair, record slot): the record's K codes are staged in LDS
+// with 16-byte loads, then per-coordinate ranges (thread per coordinate) and per-row
+// norms (256 / BLK threads per row) are reduced.
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
+  constexpr int KS = D / 64, SPB = BLK / 32, NG = kThreads / D, TPT = kThreads / BLK, S = sum_stride(D);
+  __shared__ __attribute__((aligned(16))) int8_t kc[BLK * D];  // int4 records use half
+  __shared__ int rng[2][NG][D];
+  __shared__ double nmw[kWaves];
+  __shared__ float smw[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.batch * a.hkv;
+  const int p = blockIdx.x / a.rmax, r = blockIdx.x % a.rmax;
+  Geo geo;
+  if (!skip_header_ok<D, BLK>(a, geo)) return;
+  uint8_t* dst = a.sums_out + 64 + (int64_t)blockIdx.x * S;
+  if (blockIdx.x == 0 && tid == 0) {
+    int32_t* h = reinterpret_cast<int32_t*>(a.sums_out);
+    int64_t* h64 = reinterpret_cast<int64_t*>(a.sums_out);
+    h[0] = kSumMagic;
+    h[1] = 1;
+    h[2] = P;
+    h[3] = a.rmax;
+    h[4] = D;
+    h[5] = BLK;
+    h[6] = geo.cur;
+    h[7] = 0;
+    h64[4] = geo.total;
+    h64[5] = h64[6] = h64[7] = 0;
+  }
+  const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+  const v4i e0 = e[0];
+  const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
+  const int n8 = e0[2], n4 = e0[3];
+  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax || off < geo.data_offset ||
+      off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 > geo.total)
+    return;
+  if (r >= n8 + n4) {  // unused slot: zeros
+    for (int i = tid; i < S / 4; i += kThreads) reinterpret_cast<int*>(dst)[i] = 0;
+    return;
+  }
+  const bool is4 = r >= n8;
+  const uint8_t* rec = a.cache + off + (is4 ? (int64_t)n8 * geo.rec8 + (int64_t)(r - n8) * geo.rec4 : (int64_t)r * geo.rec8);
+  const int kpart = is4 ? 16 * D : 32 * D, cb = 2 * kpart + 256;
+  for (int u = tid; u < SPB * kpart / 16; u += kThreads) {
+    const int h = u / (kpart / 16), o = (u % (kpart / 16)) * 16;
+    *reinterpret_cast<v4i*>(kc + h * kpart + o) = *reinterpret_cast<const v4i*>(rec + (int64_t)h * cb + o);
+  }
+  __syncthreads();
+  // code of row t, coordinate x in the chunk layout (int8 unit (s, ks, q, r) of 16
+  // bytes; int4 unit (s, q, r) of 8 * KS bytes, low nibble = even coordinate)
+  auto code = [&](int t, int x) __attribute__((always_inline)) -> int {
+    const int h = t / 32, s = (t % 32) / 16, rr = t % 16, ks = x / 64, q = (x % 64) / 16, el = x % 16;
+    if (!is4) return kc[h * kpart + ((s * KS + ks) * 4 + q) * 256 + rr * 16 + el];
+    const int b = (uint8_t)kc[h * kpart + ((s * 4 + q) * 16 + rr) * 8 * KS + ks * 8 + el / 2];
+    const int nib = (b >> (4 * (el & 1))) & 0xF;
+    return (nib ^ 8) - 8;
+  };
+  {
+    const int x = tid % D, tg = tid / D;
+    int lo = code(tg, x), hi = lo;
+    for (int t = tg + NG; t < BLK; t += NG) {
+      const int c = code(t, x);
+      lo = c < lo ? c : lo;
+      hi = c > hi ? c : hi;
+    }
+    rng[0][tg][x] = lo;
+    rng[1][tg][x] = hi;
+  }
+  double nv;
+  float sv;
+  {
+    const int t = tid / TPT, part = tid % TPT;
+    int n2 = 0;
+    for (int x = part * (D / TPT); x < (part + 1) * (D / TPT); ++x) {
+      const int c = code(t, x);
+      n2 += c * c;
+    }
+#pragma unroll
+    for (int o = TPT / 2; o >= 1; o >>= 1) n2 += __shfl_xor(n2, o, TPT);
+    sv = *reinterpret_cast<const float*>(rec + (int64_t)(t / 32) * cb + 2 * kpart + (t % 32) * 4);
+    nv = ((double)sv * (double)sv) * (double)n2;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double on = __shfl_xor(nv, o);
+    const float os = __shfl_xor(sv, o);
+    nv = on > nv ? on : nv;
+    sv = os > sv ? os : sv;
+  }
+  if (lane == 0) {
+    nmw[wave] = nv;
+    smw[wave] = sv;
+  }
+  __syncthreads();
+  if (tid < D) {
+    int lo = rng[0][0][tid], hi = rng[1][0][tid];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+      lo = rng[0][g][tid] < lo ? rng[0][g][tid] : lo;
+      hi = rng[1][g][tid] > hi ? rng[1][g][tid] : hi;
+    }
+    dst[tid] = (uint8_t)(int8_t)lo;
+    dst[D + tid] = (uint8_t)(int8_t)hi;
+  }
+  if (tid == 0) {
+    double n = nmw[0];
+    float m = smw[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      n = nmw[w] > n ? nmw[w] : n;
+      m = smw[w] > m ? smw[w] : m;
+    }
+    *reinterpret_cast<float*>(dst + 2 * D) = m;
+    *reinterpret_cast<int*>(dst + 2 * D + 4) = 0;
+    *reinterpret_cast<double*>(dst + 2 * D + 8) = n;
+  }
+}
+
+// Keep bits of every stored record: work group (pair, window of 256 / Gp records),
+// Gp = G rounded up to a power of two lanes per record (lane = one query head).
+// For query head h (codes qc, scale sq at the record's precision) and threshold th:
+//   box  = (t * smax) * max(sum_x max(qc_x lo_x, qc_x hi_x), 0),  t = sm_scale * sq
+//   norm = ((t * t) * |qc|^2) * nmax
+// skipped iff th > 0 and (box < th or norm < th * th), all in IEEE double in this
+// order (bit-reproducible).  The first and the current record are always kept.
+#pragma clang fp contract(off)
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) skip_decide_kernel(SkipArgs a) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR, S = sum_stride(D);
+  __shared__ __attribute__((aligned(16))) int8_t qc[2][32][D];
+  __shared__ float sq[2][32];
+  __shared__ int q2[2][32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = a.hq / a.hkv;
+  int Gp = 1;
+  while (Gp < G) Gp <<= 1;
+  const int rpw = kThreads / Gp;
+  const int p = blockIdx.x / a.nwin, win = blockIdx.x % a.nwin;
+  Geo geo;
+  if (!skip_header_ok<D, BLK>(a, geo) || !sums_ok<D, BLK>(a, geo)) return;
+  const v4i e0 = *reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+  const int n8 = e0[2], n4 = e0[3], nrec = n8 + n4;
+  if (n8 < 1 || n4 < 0 || nrec > a.rmax || win * rpw >= nrec) return;
+  const int b = p / a.hkv, g = p % a.hkv;
+  // the pair's G query rows at both precisions (the decode's quantiser)
+  for (int row0 = 0; row0 < G; row0 += RPP) {
+    const int row = row0 + tid / TPR, part = tid % TPR;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (row < G) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + row) * D + part * 8);
+      bf16x8_to_f32(raw, x);
+    }
+    uint32_t c8[2], c4;
+    float s8, s4;
+    quantize8<TPR>(x, c8, c4, s8, s4);
+    int n8sq = 0, n4sq = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int v8 = (int8_t)((c8[i / 4] >> (8 * (i % 4))) & 0xFFu);
+      const int v4 = (int)((c4 >> (4 * i)) & 0xFu);
+      const int v4s = (v4 ^ 8) - 8;
+      n8sq += v8 * v8;
+      n4sq += v4s * v4s;
+      if (row < G) {
+        qc[0][row][part * 8 + i] = (int8_t)v8;
+        qc[1][row][part * 8 + i] = (int8_t)v4s;
+      }
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) {
+      n8sq += __shfl_xor(n8sq, o, TPR);
+      n4sq += __shfl_xor(n4sq, o, TPR);
+    }
+    if (row < G && part == 0) {
+      sq[0][row] = s8;
+      sq[1][row] = s4;
+      q2[0][row] = n8sq;
+      q2[1][row] = n4sq;
+    }
+  }
+  __syncthreads();
+  const int rec = win * rpw + tid / Gp, h = tid % Gp;
+  bool keep = false;
+  if (rec < nrec && h < G) {
+    if (rec == 0 || rec == n8 - 1) {
+      keep = true;
+    } else {
+      const int pr = rec < n8 ? 0 : 1;
+      const uint8_t* sp = a.sums + 64 + ((int64_t)p * a.rmax + rec) * S;
+      const v4u* lo = reinterpret_cast<const v4u*>(sp);
+      const v4u* hi = reinterpret_cast<const v4u*>(sp + D);
+      const v4u* qv = reinterpret_cast<const v4u*>(&qc[pr][h][0]);
+      int box = 0;
+#pragma unroll
+      for (int w = 0; w < D / 16; ++w) {
+        const v4u l = lo[w], u = hi[w], qq = qv[w];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // per byte: the bound's coordinate is hi where the code is >= 0, else lo
+          const uint32_t neg = ((qq[i] >> 7) & 0x01010101u) * 0xFFu;
+          const uint32_t sel = (l[i] & neg) | (u[i] & ~neg);
+          box = __builtin_amdgcn_sdot4((int)qq[i], (int)sel, box, false);
+        }
+      }
+      const float smax = *reinterpret_cast<const float*>(sp + 2 * D);
+      const double nmax = *reinterpret_cast<const double*>(sp + 2 * D + 8);
+      const double t = (double)a.sm * (double)sq[pr][h];
+      const double bound = (t * (double)smax) * (double)(box > 0 ? box : 0);
+      const double norm2 = ((t * t) * (double)q2[pr][h]) * nmax;
+      const double th = (double)a.th[(int64_t)b * a.hq + g * G + h];
+      keep = !(th > 0.0 && (bound < th || norm2 < th * th));
+    }
+  }
+  const uint64_t bal = __ballot(keep);
+  if (rec < nrec && h == 0) {
+    const uint32_t gm = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
+    a.masks[(int64_t)p * a.rmax + rec] = (uint32_t)(bal >> (lane & ~(Gp - 1))) & gm;
+  }
+}
+#pragma clang fp contract(on)
+
+// One work group per pair: validates the directory entry (the decode's rules, and
+// that it starts where the previous pair's records end), then compacts the kept
+// records of each run into the plan's list and writes the pair entry
+// {offset lo, hi, kept int8, kept int4, stored int8, stored int4, keys of the
+// current block below ctx_len, ok}.
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) skip_compact_kernel(SkipArgs a) {
+  __shared__ int tmp[2 * kWaves];
+  const int tid = threadIdx.x, p = blockIdx.x;
+  const int P = a.batch * a.hkv;
+  int* pe = a.plan + 8 * (int64_t)p;
+  Geo geo;
+  bool ok = skip_header_ok<D, BLK>(a, geo) && sums_ok<D, BLK>(a, geo);
+  int64_t off = 0;
+  int n8 = 0, n4 = 0;
+  if (ok) {
+    const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+    const v4i e0 = e[0], e1 = e[1], e2 = e[2];
+    off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
+    n8 = e0[2];
+    n4 = e0[3];
+    const int lo8 = e1[2], sink = e1[3], lo4 = e2[0], cur = geo.cur;
+    int64_t expect = geo.data_offset;
+    if (p > 0) {
+      const v4i f = *reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)(p - 1));
+      expect = (int64_t)(((uint64_t)(uint32_t)f[1] << 32) | (uint32_t)f[0]) + (int64_t)f[2] * geo.rec8 +
+               (int64_t)f[3] * geo.rec4;
+    }
+    ok = n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
+         lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
+         off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total && cur + 1 == a.rmax;
+  }
+  if (!ok) {
+    if (tid < 8) pe[tid] = 0;
+    return;
+  }
+  int2* list = reinterpret_cast<int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
+  const uint32_t* m = a.masks + (int64_t)p * a.rmax;
+  int kept[2];
+#pragma unroll
+  for (int run = 0; run < 2; ++run) {
+    const int first = run ? n8 : 0, cnt = run ? n4 : n8, out0 = run ? kept[0] : 0;
+    int c = 0;
+    for (int i0 = 0; i0 < cnt; i0 += kThreads) {
+      const int i = i0 + tid;
+      const uint32_t mk = i < cnt ? m[first + i] : 0u;
+      const int f = mk != 0u ? 1 : 0;
+      int tot, unused;
+      const int2 ex = block_scan2(f, 0, tmp, tot, unused);
+      if (f) list[out0 + c + ex.x] = make_int2(i, (int)mk);
+      c += tot;
+    }
+    kept[run] = c;
+  }
+  if (tid == 0) {
+    pe[0] = (int)(uint32_t)off;
+    pe[1] = (int)(off >> 32);
+    pe[2] = kept[0];
+    pe[3] = kept[1];
+    pe[4] = n8;
+    pe[5] = n4;
+    pe[6] = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
+    pe[7] = 1;
+  }
+}
+
+// Work groups of the split kernel: kGrid, or fewer when TRIA_DECODE_GRID (1..kGrid) is
+// set -- a testing and tuning knob: fewer wavefronts give each one longer segments.
+int split_grid() {
+  const char* e = getenv("TRIA_DECODE_GRID");
+  if (!e) return kGrid;
+  const int g = atoi(e);
+  return g >= 1 && g <= kGrid ? g : kGrid;
+}
+
+template <int D, int BLK, int RG, bool SKIP = false>
 hipError_t launch_t(const DecArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, BLK, RG>), dim3(kGrid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, BLK, RG, SKIP>), dim3(split_grid()), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.hq), dim3(D), 0, stream, a);
@@ -780,12 +1232,117 @@ hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int
   a.hkv = s.hkv;
   a.c = sm_scale * 1.44269504088896340736f;
   a.varlen = varlen ? 1 : 0;
+  a.plan = nullptr;
+  a.rmax = 0;
   const int G = s.hq / s.hkv;
   const bool two = G > 16;
   if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2>(a, stream) : launch_t<128, 128, 1>(a, stream);
   if (s.d == 128 && s.blk == 64) return two ? launch_t<128, 64, 2>(a, stream) : launch_t<128, 64, 1>(a, stream);
   if (s.d == 64 && s.blk == 128) return two ? launch_t<64, 128, 2>(a, stream) : launch_t<64, 128, 1>(a, stream);
   return two ? launch_t<64, 64, 2>(a, stream) : launch_t<64, 64, 1>(a, stream);
+}
+
+int64_t summaries_bytes(const Shape& s, int64_t ctx_len) {
+  const int64_t rmax = (ctx_len - 1) / s.blk + 1;
+  return 64 + (int64_t)s.batch * s.hkv * rmax * sum_stride(s.d);
+}
+
+int64_t skip_workspace_bytes(const Shape& s, int64_t ctx_len) {
+  const int64_t pairs = (int64_t)s.batch * s.hkv, rmax = (ctx_len - 1) / s.blk + 1;
+  const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
+  return base + 32 * pairs + 8 * pairs * rmax + 4 * pairs * rmax;
+}
+
+namespace {
+SkipArgs skip_args(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, const void* sums,
+                   const void* q, const float* th, float sm_scale) {
+  SkipArgs a{};
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.cache_bytes = cache_bytes;
+  a.ctx_len = ctx_len;
+  a.sums = static_cast<const uint8_t*>(sums);
+  a.q = static_cast<const uint16_t*>(q);
+  a.th = th;
+  a.sm = sm_scale;
+  a.batch = s.batch;
+  a.hq = s.hq;
+  a.hkv = s.hkv;
+  a.rmax = (int)((ctx_len - 1) / s.blk + 1);
+  int gp = 1;
+  while (gp < s.hq / s.hkv) gp <<= 1;
+  const int rpw = kThreads / gp;
+  a.nwin = (a.rmax + rpw - 1) / rpw;
+  return a;
+}
+
+template <int D, int BLK>
+hipError_t launch_decide(const SkipArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((skip_decide_kernel<D, BLK>), dim3(a.batch * a.hkv * a.nwin), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int BLK>
+hipError_t launch_skip_t(const SkipArgs& sa, const DecArgs& da, bool two, hipStream_t stream) {
+  hipError_t e = launch_decide<D, BLK>(sa, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((skip_compact_kernel<D, BLK>), dim3(sa.batch * sa.hkv), dim3(kThreads), 0, stream, sa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return two ? launch_t<D, BLK, 2, true>(da, stream) : launch_t<D, BLK, 1, true>(da, stream);
+}
+}  // namespace
+
+hipError_t launch_summaries(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
+                            hipStream_t stream) {
+  SkipArgs a = skip_args(s, ctx_len, cache, cache_bytes, nullptr, nullptr, nullptr, 0.0f);
+  a.sums_out = static_cast<uint8_t*>(sums);
+  const dim3 grid((unsigned)((int64_t)s.batch * s.hkv * a.rmax));
+  if (s.d == 128 && s.blk == 128) hipLaunchKernelGGL((summaries_kernel<128, 128>), grid, dim3(kThreads), 0, stream, a);
+  else if (s.d == 128) hipLaunchKernelGGL((summaries_kernel<128, 64>), grid, dim3(kThreads), 0, stream, a);
+  else if (s.blk == 128) hipLaunchKernelGGL((summaries_kernel<64, 128>), grid, dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((summaries_kernel<64, 64>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_skip_masks(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
+                             const void* sums, const void* q, const float* thresholds, float sm_scale,
+                             uint32_t* masks, hipStream_t stream) {
+  SkipArgs a = skip_args(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale);
+  a.masks = masks;
+  if (s.d == 128 && s.blk == 128) return launch_decide<128, 128>(a, stream);
+  if (s.d == 128) return launch_decide<128, 64>(a, stream);
+  if (s.blk == 128) return launch_decide<64, 128>(a, stream);
+  return launch_decide<64, 64>(a, stream);
+}
+
+hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
+                              const void* sums, const void* q, const float* thresholds, float sm_scale, float* out,
+                              void* workspace, hipStream_t stream) {
+  SkipArgs sa = skip_args(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale);
+  const int64_t pairs = (int64_t)s.batch * s.hkv;
+  const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  sa.plan = reinterpret_cast<int*>(ws + base);
+  sa.masks = reinterpret_cast<uint32_t*>(ws + base + 32 * pairs + 8 * pairs * sa.rmax);
+  DecArgs da;
+  da.cache = static_cast<const uint8_t*>(cache);
+  da.q = static_cast<const uint16_t*>(q);
+  da.ws = static_cast<float*>(workspace);
+  da.out = out;
+  da.cache_bytes = cache_bytes;
+  da.ctx_len = ctx_len;
+  da.batch = s.batch;
+  da.hq = s.hq;
+  da.hkv = s.hkv;
+  da.c = sm_scale * 1.44269504088896340736f;
+  da.varlen = 0;
+  da.plan = sa.plan;
+  da.rmax = sa.rmax;
+  const bool two = s.hq / s.hkv > 16;
+  if (s.d == 128 && s.blk == 128) return launch_skip_t<128, 128>(sa, da, two, stream);
+  if (s.d == 128) return launch_skip_t<128, 64>(sa, da, two, stream);
+  if (s.blk == 128) return launch_skip_t<64, 128>(sa, da, two, stream);
+  return launch_skip_t<64, 64>(sa, da, two, stream);
 }
 
 }  // namespace tria

@@ -66,6 +66,20 @@ hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int
                          const void* q, float sm_scale, float* out, void* workspace, bool varlen,
                          hipStream_t stream);
 
+// Dynamic block skipping (decode.hip): the statistics index of a version-2 cache,
+// the keep bits of every stored record (uint32 [pairs][cur_block + 1]), and the
+// decode that reads only kept records.  q, thresholds: device.
+int64_t summaries_bytes(const Shape& s, int64_t ctx_len);
+int64_t skip_workspace_bytes(const Shape& s, int64_t ctx_len);
+hipError_t launch_summaries(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
+                            hipStream_t stream);
+hipError_t launch_skip_masks(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
+                             const void* sums, const void* q, const float* thresholds, float sm_scale,
+                             uint32_t* masks, hipStream_t stream);
+hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
+                              const void* sums, const void* q, const float* thresholds, float sm_scale, float* out,
+                              void* workspace, hipStream_t stream);
+
 // Measured ceilings (peaks.hip): an MFMA issue loop (kind 0: i8 16x16x64, 1: bf16
 // 16x16x32) and a non-temporal streaming read.  Work of one launch in ops / flops.
 double peak_mfma_work(int kind, int iters);

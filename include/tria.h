@@ -343,6 +343,66 @@ tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t 
                                size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Dynamic block skipping in decode (device, asynchronous on `stream`).       */
+/* ------------------------------------------------------------------------- */
+/*
+ * ETA page (rit.work, section on how the model decides which part of the context to
+ * read): before a block is read, a few statistics of its keys (mean key, spread of
+ * each coordinate, largest norm) bound its scores, and a block whose bound is below
+ * the head's threshold is not read; the whole cache stays stored and the statistics
+ * are a small extra index.  The learned predictor of the thresholds is not part of
+ * this library: thresholds are an input.
+ *
+ * Statistics of a stored record (its K codes, all rows): per-coordinate minimum and
+ * maximum code (lo, hi: the mean and spread as a box), the largest row scale smax,
+ * and the largest (scale * scale) * |codes|^2 over rows, nmax (double).  For query
+ * head h (codes qc and scale sq of q at the record's precision, the decode's
+ * quantiser) and threshold th (fp32, logit units: sm_scale * q.k), with
+ * t = sm_scale * sq in double:
+ *   box  = (t * smax) * max(sum_x max(qc_x lo_x, qc_x hi_x), 0)   (>= every score)
+ *   norm = ((t * t) * |qc|^2) * nmax                               (>= every score^2)
+ * the record is skipped for h iff th > 0 and (box < th or norm < th * th), computed
+ * in IEEE double in this order.  The first key block and the current block are never
+ * skipped.  Each query head attends over the records it keeps; a record no head of
+ * its KV head keeps is not read.
+ *
+ * tria_block_summaries_bytes / tria_build_block_summaries: the index of a version-2
+ *   cache for ctx_len: a 64-byte header {int32 magic "TBSM", 1, pairs, slots per pair
+ *   (rmax = (ctx_len - 1) / block + 1), head_dim, block, current block, 0; int64 the
+ *   cache's total_bytes at byte 32}, then per (pair, record slot) 2 * head_dim + 16
+ *   bytes {int8 lo[d], int8 hi[d], fp32 smax, int32 0, fp64 nmax}; slots past a pair's
+ *   records are zero.  One work group per slot reads the record's K codes once.  The
+ *   index stays valid while the cache keeps the same current block and total size
+ *   (tria_update_kv_cache within a block changes only the current record, whose
+ *   statistics are not used); rebuild it when a block starts.  A cache that does not
+ *   validate leaves the index without its header (later calls then reject it).
+ * tria_skip_masks: the keep bits of every stored record: masks = uint32 [pairs][rmax]
+ *   (record order of the cache: int8 records, then int4), bit i set = query head
+ *   g * G + i keeps the record; slots past a pair's records are not written.
+ *   q_bf16 [batch][n_q_heads][head_dim], thresholds fp32 [batch][n_q_heads] (device).
+ * tria_decode_skip: tria_decode reading only the records some head keeps; per head,
+ *   the attention over its kept records.  Three kernels: the keep bits (one lane per
+ *   (record, head)), a per-pair compaction of the kept records into the workspace
+ *   (with the directory checks of tria_decode), then the split-KV decode over the
+ *   kept records' bytes and the merge.  The workspace (tria_decode_skip_workspace_
+ *   bytes) holds the decode's partials and the plan.  A cache, or an index, that does
+ *   not validate writes NaN to `out` and reads no record.
+ * Limits: as tria_decode (G <= 32, batch * n_kv_heads <= 4096); version-2 caches. */
+tria_status tria_block_summaries_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
+tria_status tria_build_block_summaries(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                                       int64_t ctx_len, void* summaries, size_t summaries_bytes,
+                                       void* stream);
+tria_status tria_skip_masks(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                            const void* summaries, size_t summaries_bytes, const void* q_bf16,
+                            const float* thresholds, float sm_scale, uint32_t* masks,
+                            size_t masks_bytes, void* stream);
+tria_status tria_decode_skip_workspace_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
+tria_status tria_decode_skip(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                             const void* summaries, size_t summaries_bytes, const void* q_bf16,
+                             const float* thresholds, float sm_scale, float* out, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Calibration: cost model and allocator.  Host, synchronous.                 */
 /* ------------------------------------------------------------------------- */
 /*

@@ -16,4 +16,5 @@ from .gen import (  # noqa: F401
     uniform_u64,
     make_prefill_inputs,
     make_decode_inputs,
+    make_skip_decode_inputs,
 )

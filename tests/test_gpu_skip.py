@@ -1,0 +1,168 @@
+"""GPU parity of dynamic block skipping in decode (ETA page, rit.work: section on how
+the model decides which part of the context to read): the statistics index
+byte-exact against the oracle's, the keep bits bit-exact, and the skipping decode
+against the oracle's masked decode.  Inputs: seeded keys with one magnitude per
+(batch, KV head, block) and per-head thresholds gamma * ||q|| (synth)."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from test_gpu_parity import assert_close, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tria():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_mixed_head_amd as t
+    return t
+
+
+def parse_summaries(buf: torch.Tensor, pairs: int, rmax: int, d: int):
+    b = buf.cpu().numpy()
+    hdr, h64 = b[:64].view(np.int32), b[:64].view(np.int64)
+    S = 2 * d + 16
+    body = b[64:64 + pairs * rmax * S].reshape(pairs, rmax, S)
+    lo = body[:, :, :d].view(np.int8)
+    hi = body[:, :, d:2 * d].view(np.int8)
+    smax = np.ascontiguousarray(body[:, :, 2 * d:2 * d + 4]).view(np.float32)[..., 0]
+    pad = np.ascontiguousarray(body[:, :, 2 * d + 4:2 * d + 8]).view(np.int32)[..., 0]
+    nmax = np.ascontiguousarray(body[:, :, 2 * d + 8:2 * d + 16]).view(np.float64)[..., 0]
+    return hdr, h64, lo, hi, smax, pad, nmax
+
+
+SKIP_CASES = [
+    # (b, hq, hk, d, n, blk, ctx, hi, keep)  policies per KV head
+    (2, 8, 2, 128, 1300, 128, 1300, [0, 2], [3, 10]),
+    (2, 4, 2, 64, 900, 64, 897, [1, 0], [5, 9]),
+    (1, 32, 1, 128, 1100, 128, 1050, [1], [8]),              # G = 32: two row groups
+    (3, 12, 4, 128, 700, 64, 650, [2, 0, 1, 5], [4, 9, 9, 5]),  # G = 3: lanes padded to 4
+    (1, 4, 2, 128, 9000, 128, 8955, [3, 1], [40, 70]),       # 70 records per pair
+    (1, 2, 2, 64, 64, 64, 1, [0, 0], [0, 0]),                 # a single token
+]
+IDS = [f"b{c[0]}h{c[1]}k{c[2]}d{c[3]}ctx{c[6]}B{c[5]}" for c in SKIP_CASES]
+
+
+def _setup(tria, case, seed=61):
+    b, hq, hk, d, n, blk, ctx, hi, keep = case
+    cfg = synth.Config("skip", b, hq, hk, d, n, blk, seed=seed, decode=True)
+    k, v, q, th = synth.make_skip_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx, dev(k), dev(v))
+    sums = tria.build_block_summaries(dd, cache, ctx)
+    torch.cuda.synchronize()
+    return k, v, q, th, hi, keep, dd, cache, sums
+
+
+@pytest.mark.parametrize("case", SKIP_CASES, ids=IDS)
+def test_summaries_and_masks_match_oracle(tria, case):
+    print(f"[case] skip index + masks {case}", flush=True)
+    b, hq, hk, d, n, blk, ctx = case[:7]
+    k, v, q, th, hi, keep, dd, cache, sums = _setup(tria, case)
+    rmax = (ctx - 1) // blk + 1
+    assert sums.numel() == 64 + b * hk * rmax * (2 * d + 16)
+    hdr, h64, lo, up, smax, pad, nmax = parse_summaries(sums, b * hk, rmax, d)
+    assert list(hdr[:8]) == [0x4D534254, 1, b * hk, rmax, d, blk, rmax - 1, 0]
+    assert h64[4] == cache.numel() and not h64[5:].any()
+    rlo, rup, rsmax, rnmax = oracle.block_summaries(k, hi, keep, hq, blk, ctx)
+    assert np.array_equal(lo, rlo) and np.array_equal(up, rup)
+    assert np.array_equal(smax, rsmax) and np.array_equal(nmax, rnmax) and not pad.any()
+    sm = 1.0 / math.sqrt(d)
+    thd = torch.from_numpy(th).cuda()
+    masks = tria.skip_masks(dd, cache, ctx, sums, dev(q), thd, sm).cpu().numpy().view(np.uint32)
+    ref = oracle.skip_masks(k, q, hi, keep, blk, ctx, th, sm)
+    assert np.array_equal(masks, ref)
+    G = hq // hk
+    full = (1 << G) - 1
+    kept = [int(m) for m in ref.ravel() if m]
+    print(f"[skip] records kept by every head {sum(m == full for m in kept)}, by some {len(kept)} "
+          f"of {int((ref != 0).sum())} stored", flush=True)
+
+
+@pytest.mark.parametrize("case", SKIP_CASES, ids=IDS)
+def test_decode_skip_matches_oracle(tria, case):
+    print(f"[case] skip decode {case}", flush=True)
+    b, hq, hk, d, n, blk, ctx = case[:7]
+    k, v, q, th, hi, keep, dd, cache, sums = _setup(tria, case)
+    sm = 1.0 / math.sqrt(d)
+    thd = torch.from_numpy(th).cuda()
+    out = tria.decode_skip(dd, cache, ctx, sums, dev(q), thd, sm)
+    torch.cuda.synchronize()
+    ref = oracle.decode_skip(k, v, q, hi, keep, blk, ctx, th, sm)
+    assert_close(out.cpu().numpy(), ref, f"skip decode {case}")
+    # thresholds <= 0 keep everything: the plain decode, bit for bit
+    zero = tria.decode_skip(dd, cache, ctx, sums, dev(q), torch.zeros_like(thd), sm)
+    plain = tria.decode(dd, cache, ctx, dev(q), sm)
+    torch.cuda.synchronize()
+    assert torch.equal(zero, plain)
+    # +inf keeps only the first and the current block
+    inf = tria.decode_skip(dd, cache, ctx, sums, dev(q), torch.full_like(thd, float("inf")), sm)
+    torch.cuda.synchronize()
+    ref_inf = oracle.decode(k, v, q, np.zeros_like(hi), np.zeros_like(keep), blk, ctx, sm)
+    assert_close(inf.cpu().numpy(), ref_inf, f"skip decode +inf {case}")
+
+
+@pytest.mark.parametrize("grid", [1, 3])
+def test_decode_skip_long_segments(tria, grid, monkeypatch):
+    """Few work groups: each wavefront walks many kept records (several 64-entry
+    windows of the kept list), in both the skipping and the plain decode."""
+    case = (2, 8, 2, 128, 128 * 300, 128, 128 * 300 - 17, [4, 2], [150, 299])
+    print(f"[case] skip decode grid {grid} {case}", flush=True)
+    b, hq, hk, d, n, blk, ctx = case[:7]
+    k, v, q, th, hi, keep, dd, cache, sums = _setup(tria, case)
+    sm = 1.0 / math.sqrt(d)
+    thd = torch.from_numpy(th * 0.8).cuda()   # more records kept
+    monkeypatch.setenv("TRIA_DECODE_GRID", str(grid))
+    out = tria.decode_skip(dd, cache, ctx, sums, dev(q), thd, sm)
+    plain = tria.decode(dd, cache, ctx, dev(q), sm)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("TRIA_DECODE_GRID")
+    ref = oracle.decode_skip(k, v, q, hi, keep, blk, ctx, th * np.float32(0.8), sm)
+    assert_close(out.cpu().numpy(), ref, f"skip decode grid {grid}")
+    assert_close(plain.cpu().numpy(), oracle.decode(k, v, q, hi, keep, blk, ctx, sm), f"decode grid {grid}")
+
+
+def test_decode_skip_rejects_stale_index(tria):
+    case = SKIP_CASES[0]
+    k, v, q, th, hi, keep, dd, cache, sums = _setup(tria, case)
+    ctx, d = case[6], case[3]
+    thd = torch.from_numpy(th).cuda()
+    bad = sums.clone()
+    bad[24:28] = torch.tensor([0, 0, 0, 0], dtype=torch.uint8)   # current block 0 instead of its own
+    o = tria.decode_skip(dd, cache, ctx, bad, dev(q), thd, 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all().item()
+    badc = cache.clone()
+    badc[64 + 8:64 + 12] = torch.tensor([255, 255, 0, 0], dtype=torch.uint8)  # n8 of pair 0
+    o = tria.decode_skip(dd, badc, ctx, sums, dev(q), thd, 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all().item()
+
+
+def test_decode_skip_full_size(tria):
+    """The decode workload (b16, 32/8 heads, d128, ctx 32768, block 128) with block
+    structure in the keys: index and keep bits exact, outputs vs the oracle."""
+    cfg = synth.CONFIGS[4]
+    print("[case] skip decode full-size decode workload", flush=True)
+    k, v, q, th = synth.make_skip_decode_inputs(cfg)
+    hi, keep = cfg.policy()
+    dd = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
+    ctx, d = cfg.seq_len, cfg.head_dim
+    sm = 1.0 / math.sqrt(d)
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx, dev(k), dev(v))
+    sums = tria.build_block_summaries(dd, cache, ctx)
+    thd = torch.from_numpy(th).cuda()
+    masks = tria.skip_masks(dd, cache, ctx, sums, dev(q), thd, sm)
+    out = tria.decode_skip(dd, cache, ctx, sums, dev(q), thd, sm)
+    torch.cuda.synchronize()
+    ref_masks = oracle.skip_masks(k, q, hi, keep, cfg.block, ctx, th, sm)
+    assert np.array_equal(masks.cpu().numpy().view(np.uint32), ref_masks)
+    ref = oracle.decode_skip(k, v, q, hi, keep, cfg.block, ctx, th, sm)
+    assert_close(out.cpu().numpy(), ref, "skip decode full size")
