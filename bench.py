@@ -75,7 +75,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "copy", "step"], default=None)
+    p.add_argument("--only", choices=["prefill", "decode", "skip", "copy", "step"], default=None)
     p.add_argument("--reps", type=int, default=20)
     return p.parse_args()
 
@@ -216,10 +216,12 @@ def main():
 
     # ------------------------------------------------------------ decode workload (b16, ctx 32768)
     dec = None
-    if args.only in (None, "decode"):
+    if args.only in (None, "decode", "skip"):
         c4 = synth.CONFIGS[4]
         log(f"[bench] generating {c4.name}")
         k4h, v4h, q4h = synth.make_decode_inputs(c4)
+        # the same inputs with block structure in K and per-head thresholds (skipping)
+        k4s, th4 = synth.apply_block_structure(c4, k4h, q4h)
         h4, kp4 = c4.policy()
         dims4 = tria.make_dims(c4.batch, c4.n_q_heads, c4.n_kv_heads, c4.head_dim, c4.block, c4.seq_len)
         k4d, v4d = dev(k4h), dev(v4h)
@@ -238,6 +240,17 @@ def main():
 
         for _ in range(3):
             run_dec()
+        if args.only == "skip":      # profiler run: index build, then skipping decodes
+            k4s_d = dev(k4s)
+            cs = tria.pack_kv_cache(dims4, h4, kp4, c4.seq_len, k4s_d, v4d)
+            sm_ = tria.build_block_summaries(dims4, cs, c4.seq_len)
+            th_ = torch.from_numpy(th4).cuda()
+            for _ in range(args.steps):
+                flush_caches()
+                tria.decode_skip(dims4, cs, c4.seq_len, sm_, q4, th_, 1.0 / math.sqrt(c4.head_dim), out=o4)
+            torch.cuda.synchronize()
+            print("done", flush=True)
+            return
         if args.only == "decode":
             for _ in range(args.steps):
                 flush_caches()
@@ -257,8 +270,64 @@ def main():
         c_out = torch.empty(tria.kv_cache_bytes(dims4, h4, kp4, s0 + 1), dtype=torch.uint8, device="cuda")
         upd_bs = event_avg(lambda: tria.update_kv_cache(dims4, h4, kp4, s0 + 1, k4d, v4d, c_blk, out=c_out),
                            args.reps)
-        del c_prev, c_blk, c_out, k4d, v4d
+        del c_prev, c_blk, c_out, k4d
         hdr = (64 + 64 * c4.batch * c4.n_kv_heads + 255) // 256 * 256
+        # dynamic block skipping (ETA-style) on the same workload, keys with block
+        # structure: the index (built once per cache block), then the skipping decode
+        # (keep bits + compaction + split-KV over kept records + merge) against the
+        # plain decode of the same cache
+        ctx4, sm4 = c4.seq_len, 1.0 / math.sqrt(c4.head_dim)
+        ks_d = dev(k4s)
+        del k4s
+        cache_s = tria.pack_kv_cache(dims4, h4, kp4, ctx4, ks_d, v4d)
+        del ks_d, v4d
+        sums = tria.build_block_summaries(dims4, cache_s, ctx4)
+        sum_t = event_avg(lambda: tria.build_block_summaries(dims4, cache_s, ctx4, out=sums), args.reps,
+                          before=flush_caches)
+        thd = torch.from_numpy(th4).cuda()
+        wss = torch.empty(tria.decode_skip_workspace_bytes(dims4, ctx4), dtype=torch.uint8, device="cuda")
+
+        def run_skip():
+            tria.decode_skip(dims4, cache_s, ctx4, sums, q4, thd, sm4, out=o4, workspace=wss)
+
+        for _ in range(3):
+            run_skip()
+        sk = event_avg(run_skip, args.reps, before=flush_caches)
+        plain_s = event_avg(lambda: tria.decode(dims4, cache_s, ctx4, q4, sm4, out=o4, workspace=ws4), args.reps,
+                            before=flush_caches)
+        masks = tria.skip_masks(dims4, cache_s, ctx4, sums, q4, thd, sm4).cpu().numpy().view(np.uint32)
+        dirs = cache_s[:hdr].cpu().numpy()
+        rec8 = 2 * c4.block * c4.head_dim + 8 * c4.block
+        rec4 = c4.block * c4.head_dim + 8 * c4.block
+        G4 = c4.n_q_heads // c4.n_kv_heads
+        kept_b = stored_rec = head_keep = 0
+        for pi in range(c4.batch * c4.n_kv_heads):
+            n8, n4 = (int(x) for x in dirs[64 + 64 * pi + 8:64 + 64 * pi + 16].view(np.int32))
+            m = masks[pi, :n8 + n4]
+            kept_b += int((m[:n8] != 0).sum()) * rec8 + int((m[n8:] != 0).sum()) * rec4
+            stored_rec += n8 + n4
+            head_keep += sum(bin(int(x)).count("1") for x in m)
+        stored_b = cache_s.numel() - hdr
+        sum_read = stored_rec * (2 * c4.head_dim + 16)
+        io_b = c4.batch * c4.n_q_heads * c4.head_dim * (2 + 4)
+        skip = {
+            "us_per_call": sk[0] * 1e6, "us_p10": sk[2] * 1e6, "us_p90": sk[3] * 1e6,
+            "plain_decode_same_cache_us": plain_s[0] * 1e6,
+            "speedup_vs_plain": plain_s[0] / sk[0],
+            "kept_record_bytes": kept_b, "stored_record_bytes": stored_b,
+            "bytes_read_fraction": kept_b / stored_b,
+            "head_density": head_keep / (stored_rec * G4),
+            "algorithmic_bytes": kept_b + sum_read + io_b,
+            "GB_per_s": (kept_b + sum_read + io_b) / sk[0] / 1e9,
+            "index_bytes": sums.numel(), "index_fraction_of_cache": sums.numel() / cache_s.numel(),
+            "index_build_us": sum_t[1] * 1e6,
+            "inputs": "decode workload keys x one magnitude per (b, KV head, block) ~ U[0.1, 1]; "
+                      "threshold per (b, head) = gamma * ||q||, gamma ~ U[0.6, 0.9]",
+        }
+        log(f"[bench] skip decode {sk[0] * 1e6:.1f} us vs {plain_s[0] * 1e6:.1f} us plain on the same cache; "
+            f"reads {kept_b / stored_b:.3f} of the records, head density {skip['head_density']:.3f}, "
+            f"{skip['GB_per_s']:.0f} GB/s; index {sums.numel() / 1e6:.2f} MB built in {sum_t[1] * 1e6:.1f} us")
+        del cache_s, sums, wss
         dbytes = decode_bytes(cache4.numel(), c4.batch, c4.n_q_heads, c4.head_dim, hdr)
         dense_bytes = 2 * c4.batch * c4.n_kv_heads * c4.seq_len * c4.head_dim * 2
         dec = {
@@ -272,6 +341,7 @@ def main():
             "dense_bf16_cache_bytes": dense_bytes,
             "cache_update_us": {"in_place_within_block": upd_in[1] * 1e6, "at_block_start": upd_bs[1] * 1e6,
                                 "note": "median; tria_update_kv_cache for one more token (all 128 pairs)"},
+            "skip": skip,
         }
         log(f"[bench] decode {dm * 1e6:.1f} us, {dec['GB_per_s']:.0f} GB/s (warm {warm * 1e6:.1f} us); "
             f"cache update {upd_in[1] * 1e6:.1f} us in place, {upd_bs[1] * 1e6:.1f} us at a block start")

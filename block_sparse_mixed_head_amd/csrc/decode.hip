@@ -76,11 +76,18 @@ struct Geo {
   int cur;
 };
 
+// A 64-byte header as one load (every field in registers before any test, so the
+// tests cost no further memory round trips).
+struct Hdr64 {
+  int32_t w[16];
+  __device__ int64_t q(int i) const { return (int64_t)(((uint64_t)(uint32_t)w[2 * i + 1] << 32) | (uint32_t)w[2 * i]); }
+};
+
 // Validates the global header against the launch; returns false on mismatch.
 template <int D, int BLK>
-__device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
-  const int32_t* hd = reinterpret_cast<const int32_t*>(a.cache);
-  const int64_t* h64 = reinterpret_cast<const int64_t*>(a.cache);
+__device__ __forceinline__ bool header_ok_h(const DecArgs& a, const Hdr64& h, Geo& geo) {
+  const int32_t* hd = h.w;
+  const int64_t h64[8] = {0, 0, 0, 0, h.q(4), h.q(5), h.q(6), h.q(7)};
   geo.rec8 = 2LL * BLK * D + 8LL * BLK;
   geo.rec4 = (int64_t)BLK * D + 8LL * BLK;
   geo.cur = (int)((a.ctx_len - 1) / BLK);
@@ -90,6 +97,11 @@ __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
                       geo.total <= a.cache_bytes && h64[6] == 64 && h64[7] == geo.data_offset;
   if (a.varlen) return common && hd[1] == 3 && hd[7] == -1;  // ctx_len per directory entry
   return common && hd[1] == 2 && hd[6] == geo.cur + 1 && hd[7] == geo.cur && h64[4] == a.ctx_len;
+}
+template <int D, int BLK>
+__device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
+  const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  return header_ok_h<D, BLK>(a, h, geo);
 }
 
 // Inclusive prefix sum over the wavefront: DPP row shifts (1, 2, 4, 8) within each
@@ -414,14 +426,22 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     const int nbytes = uni(nstored * rb);
     const int lane = threadIdx.x & 63;
     typename IO::Buf A, B, C;
-    pre();
     // windows of up to 64 kept records: lane l holds the window's entry l, read by
-    // the whole wavefront with readlane (uniform index, no memory access per step)
+    // the whole wavefront with readlane (uniform index, no memory access per step).
+    // The first window's entries load together with the query rows, before `pre`.
+    auto window = [&](int w0, int& w1) __attribute__((always_inline)) -> int2 {
+      const int r0 = uni(w0 / SPB);
+      w1 = uni((r0 + 64) * SPB < j1 ? (r0 + 64) * SPB : j1);
+      const int rlast = (w1 - 1) / SPB;
+      return r0 + lane <= rlast ? list[r0 + lane] : make_int2(0, 0);
+    };
+    int w1f;
+    const int2 efirst = window(j0, w1f);
+    pre();
     for (int w0 = j0; w0 < j1;) {
       const int r0 = uni(w0 / SPB);
-      const int w1 = uni((r0 + 64) * SPB < j1 ? (r0 + 64) * SPB : j1);
-      const int rlast = (w1 - 1) / SPB;
-      const int2 e = r0 + lane <= rlast ? list[r0 + lane] : make_int2(0, 0);
+      int w1 = w1f;
+      const int2 e = w0 == j0 ? efirst : window(w0, w1);
       auto ld = [&](typename IO::Buf& r, int j) __attribute__((always_inline)) {
         const bool in = j < w1;
         const int rec = in ? __builtin_amdgcn_readlane(e.x, j / SPB - r0) : 0;
@@ -465,7 +485,6 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     IO::load(r, in ? rs : none, in ? (j / SPB) * rb : 0, in ? j % SPB : 0, lr, kq);
     __builtin_amdgcn_sched_barrier(0);
   };
-  pre();
   // Step j is loaded into buffer (j - j0) % 3 and computed two loads later, so
   // two steps are in flight during each compute.  Loads and their uses both sit
   // inside the loop (nothing loaded before it is used in it), which keeps the
@@ -482,6 +501,7 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     ld(B, j + 1);
     if (j - 1 >= j0 && j - 1 < j1) compute_step<D, RG, IS4>(C, qop, ar, mfrom(j - 1), st, kq, slot, 0u);
     ld(C, j + 2);
+    if (j == j0) pre();  // the query quantisation, once the first three steps' loads are in flight
     if (j < j1) compute_step<D, RG, IS4>(A, qop, ar, mfrom(j), st, kq, slot, 0u);
     fold_bias(st);
   }
@@ -755,7 +775,7 @@ decode_split_kernel(DecArgs a) {
                                       [&]() __attribute__((always_inline)) {
                                         if (!has8) quantise_q();
                                       },
-                                      SKIP ? list + n8 : nullptr, n4s, hfull);
+                                      SKIP ? list + n8s : nullptr, n4s, hfull);
 
     // ---- the wavefront's partial for this pair
 #pragma unroll
@@ -869,10 +889,10 @@ struct SkipArgs {
   uint8_t* sums_out;
   const uint16_t* q;
   const float* th;
-  uint32_t* masks;  // [P][rmax] keep bits per stored record
-  int* plan;        // [P][8] pair entries, then [P][rmax] kept {record, mask} lists
+  uint32_t* masks;  // or null: [P][rmax] keep bits per stored record
+  int* plan;        // or null: [P][8] pair entries, then [P][rmax] kept {record, mask} lists
   float sm;
-  int batch, hq, hkv, rmax, nwin;
+  int batch, hq, hkv, rmax;
 };
 
 template <int D, int BLK>
@@ -890,11 +910,9 @@ __device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
 // The index describes this cache's records: same pairs, slots, shape, current block
 // and total size (statistics of the current block itself are never used).
 template <int D, int BLK>
-__device__ __forceinline__ bool sums_ok(const SkipArgs& s, const Geo& geo) {
-  const int32_t* h = reinterpret_cast<const int32_t*>(s.sums);
-  const int64_t* h64 = reinterpret_cast<const int64_t*>(s.sums);
-  return h[0] == kSumMagic && h[1] == 1 && h[2] == s.batch * s.hkv && h[3] == s.rmax && h[4] == D && h[5] == BLK &&
-         h[6] == geo.cur && h64[4] == geo.total;
+__device__ __forceinline__ bool sums_ok(const SkipArgs& s, const Hdr64& h, const Geo& geo) {
+  return h.w[0] == kSumMagic && h.w[1] == 1 && h.w[2] == s.batch * s.hkv && h.w[3] == s.rmax && h.w[4] == D &&
+         h.w[5] == BLK && h.w[6] == geo.cur && h.q(4) == geo.total;
 }
 
 // One work group per (pair, record slot): the record's K codes are staged in LDS
@@ -1016,54 +1034,108 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
   }
 }
 
-// Keep bits of every stored record: work group (pair, window of 256 / Gp records),
-// Gp = G rounded up to a power of two lanes per record (lane = one query head).
-// For query head h (codes qc, scale sq at the record's precision) and threshold th:
+// The plan of one pair per work group, one lane per record slot (r = pass * 256 +
+// lane).  Keep bits: for query head h (codes qc, scale sq at the record's precision)
+// and threshold th,
 //   box  = (t * smax) * max(sum_x max(qc_x lo_x, qc_x hi_x), 0),  t = sm_scale * sq
 //   norm = ((t * t) * |qc|^2) * nmax
-// skipped iff th > 0 and (box < th or norm < th * th), all in IEEE double in this
-// order (bit-reproducible).  The first and the current record are always kept.
+// and h skips the record iff th > 0 and (box < th or norm < th * th), all in IEEE
+// double in this order (bit-reproducible); the first and the current record are
+// always kept.  With a plan buffer, the kept records of each run are listed in order
+// ({stored index in the run, keep bits}: int8 run from slot 0, int4 run from slot
+// n8) and the pair entry {offset lo, hi, kept int8, kept int4, stored int8, stored
+// int4, keys of the current block below ctx_len, ok} is written after the
+// directory checks of the decode (and that the pair's records start where the
+// previous pair's end).  With a masks buffer, the keep bits of every stored record.
 #pragma clang fp contract(off)
 template <int D, int BLK>
-__global__ void __launch_bounds__(kThreads) skip_decide_kernel(SkipArgs a) {
-  constexpr int TPR = D / 8, RPP = kThreads / TPR, S = sum_stride(D);
+__global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
+  constexpr int TPR = D / 8, S = sum_stride(D), KW = D / 16;
   __shared__ __attribute__((aligned(16))) int8_t qc[2][32][D];
   __shared__ float sq[2][32];
   __shared__ int q2[2][32];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int G = a.hq / a.hkv;
-  int Gp = 1;
-  while (Gp < G) Gp <<= 1;
-  const int rpw = kThreads / Gp;
-  const int p = blockIdx.x / a.nwin, win = blockIdx.x % a.nwin;
-  Geo geo;
-  if (!skip_header_ok<D, BLK>(a, geo) || !sums_ok<D, BLK>(a, geo)) return;
-  const v4i e0 = *reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
-  const int n8 = e0[2], n4 = e0[3], nrec = n8 + n4;
-  if (n8 < 1 || n4 < 0 || nrec > a.rmax || win * rpw >= nrec) return;
-  const int b = p / a.hkv, g = p % a.hkv;
-  // the pair's G query rows at both precisions (the decode's quantiser)
-  for (int row0 = 0; row0 < G; row0 += RPP) {
-    const int row = row0 + tid / TPR, part = tid % TPR;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (row < G) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + row) * D + part * 8);
-      bf16x8_to_f32(raw, x);
+  __shared__ float ths[32];
+  __shared__ int tmp[2 * kWaves];
+  const int tid = threadIdx.x;
+  const int G = a.hq / a.hkv, P = a.batch * a.hkv;
+  const int p = blockIdx.x, b = p / a.hkv, g = p % a.hkv;
+  // every load first, in one round trip: both headers, the directory entries of this
+  // pair and the previous one, the query rows and this lane's first index slot (no
+  // address depends on a loaded value; all lie inside their buffers)
+  const Hdr64 hc = *reinterpret_cast<const Hdr64*>(a.cache);
+  const Hdr64 hs = *reinterpret_cast<const Hdr64*>(a.sums);
+  const v4i* ep = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+  const v4i e0 = ep[0], e1 = ep[1], e2 = ep[2];
+  const v4i f = *reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)(p > 0 ? p - 1 : p));
+  uint4 qraw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = tid + i * kThreads, row = piece / TPR;
+    qraw[i] = make_uint4(0, 0, 0, 0);
+    if (row < G)
+      qraw[i] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + row) * D + (piece % TPR) * 8);
+  }
+  const float th_own = tid < G ? a.th[(int64_t)b * a.hq + g * G + tid] : 0.0f;
+  v4u lo[KW], hi[KW];
+  float smax = 0.0f;
+  double nmax = 0.0;
+  auto load_slot = [&](int r) __attribute__((always_inline)) {
+    if (r < a.rmax) {
+      const uint8_t* sp = a.sums + 64 + ((int64_t)p * a.rmax + r) * S;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) {
+        lo[w] = reinterpret_cast<const v4u*>(sp)[w];
+        hi[w] = reinterpret_cast<const v4u*>(sp + D)[w];
+      }
+      smax = *reinterpret_cast<const float*>(sp + 2 * D);
+      nmax = *reinterpret_cast<const double*>(sp + 2 * D + 8);
     }
+  };
+  load_slot(tid);
+  // ---- checks (uniform)
+  DecArgs da{};
+  da.cache_bytes = a.cache_bytes;
+  da.ctx_len = a.ctx_len;
+  da.batch = a.batch;
+  da.hkv = a.hkv;
+  Geo geo;
+  bool ok = header_ok_h<D, BLK>(da, hc, geo) && sums_ok<D, BLK>(a, hs, geo);
+  const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
+  const int n8 = e0[2], n4 = e0[3], nrec = n8 + n4;
+  {
+    const int lo8 = e1[2], sink = e1[3], lo4 = e2[0], cur = geo.cur;
+    const int64_t expect = p == 0 ? geo.data_offset
+                                  : (int64_t)(((uint64_t)(uint32_t)f[1] << 32) | (uint32_t)f[0]) +
+                                        (int64_t)f[2] * geo.rec8 + (int64_t)f[3] * geo.rec4;
+    ok = ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
+         lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
+         off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total && cur + 1 == a.rmax;
+  }
+  int* pe = a.plan ? a.plan + 8 * (int64_t)p : nullptr;
+  if (!ok) {
+    if (pe && tid < 8) pe[tid] = 0;
+    return;
+  }
+  // ---- the pair's G query rows at both precisions (the decode's quantiser)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int piece = tid + i * kThreads, row = piece / TPR, part = piece % TPR;
+    if (i * kThreads >= G * TPR) break;  // uniform
+    float x[8];
+    bf16x8_to_f32(qraw[i], x);
     uint32_t c8[2], c4;
     float s8, s4;
     quantize8<TPR>(x, c8, c4, s8, s4);
     int n8sq = 0, n4sq = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int v8 = (int8_t)((c8[i / 4] >> (8 * (i % 4))) & 0xFFu);
-      const int v4 = (int)((c4 >> (4 * i)) & 0xFu);
-      const int v4s = (v4 ^ 8) - 8;
+    for (int k = 0; k < 8; ++k) {
+      const int v8 = (int8_t)((c8[k / 4] >> (8 * (k % 4))) & 0xFFu);
+      const int v4 = (((int)((c4 >> (4 * k)) & 0xFu)) ^ 8) - 8;
       n8sq += v8 * v8;
-      n4sq += v4s * v4s;
+      n4sq += v4 * v4;
       if (row < G) {
-        qc[0][row][part * 8 + i] = (int8_t)v8;
-        qc[1][row][part * 8 + i] = (int8_t)v4s;
+        qc[0][row][part * 8 + k] = (int8_t)v8;
+        qc[1][row][part * 8 + k] = (int8_t)v4;
       }
     }
 #pragma unroll
@@ -1078,112 +1150,66 @@ __global__ void __launch_bounds__(kThreads) skip_decide_kernel(SkipArgs a) {
       q2[1][row] = n4sq;
     }
   }
+  if (tid < G) ths[tid] = th_own;
   __syncthreads();
-  const int rec = win * rpw + tid / Gp, h = tid % Gp;
-  bool keep = false;
-  if (rec < nrec && h < G) {
-    if (rec == 0 || rec == n8 - 1) {
-      keep = true;
-    } else {
-      const int pr = rec < n8 ? 0 : 1;
-      const uint8_t* sp = a.sums + 64 + ((int64_t)p * a.rmax + rec) * S;
-      const v4u* lo = reinterpret_cast<const v4u*>(sp);
-      const v4u* hi = reinterpret_cast<const v4u*>(sp + D);
-      const v4u* qv = reinterpret_cast<const v4u*>(&qc[pr][h][0]);
-      int box = 0;
+  const uint32_t gm = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
+  int2* list = a.plan ? reinterpret_cast<int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax : nullptr;
+  int c8 = 0, c4 = 0;
+  for (int r0 = 0; r0 < nrec; r0 += kThreads) {
+    const int r = r0 + tid;
+    if (r0 > 0) load_slot(r);
+    uint32_t mk = 0;
+    if (r < nrec) {
+      if (r == 0 || r == n8 - 1) {
+        mk = gm;
+      } else {
+        const int pr = r < n8 ? 0 : 1;
+        // per byte of q: the bound's coordinate is hi where the code is >= 0, else lo
+        const double th0 = 0.0;
+        for (int h = 0; h < G; ++h) {
+          const v4u* qv = reinterpret_cast<const v4u*>(&qc[pr][h][0]);
+          int box = 0;
 #pragma unroll
-      for (int w = 0; w < D / 16; ++w) {
-        const v4u l = lo[w], u = hi[w], qq = qv[w];
+          for (int w = 0; w < KW; ++w) {
+            const v4u qq = qv[w];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // per byte: the bound's coordinate is hi where the code is >= 0, else lo
-          const uint32_t neg = ((qq[i] >> 7) & 0x01010101u) * 0xFFu;
-          const uint32_t sel = (l[i] & neg) | (u[i] & ~neg);
-          box = __builtin_amdgcn_sdot4((int)qq[i], (int)sel, box, false);
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t neg = ((qq[i] >> 7) & 0x01010101u) * 0xFFu;
+              const uint32_t sel = (lo[w][i] & neg) | (hi[w][i] & ~neg);
+              box = __builtin_amdgcn_sdot4((int)qq[i], (int)sel, box, false);
+            }
+          }
+          const double t = (double)a.sm * (double)sq[pr][h];
+          const double bound = (t * (double)smax) * (double)(box > 0 ? box : 0);
+          const double norm2 = ((t * t) * (double)q2[pr][h]) * nmax;
+          const double th = (double)ths[h];
+          if (!(th > th0 && (bound < th || norm2 < th * th))) mk |= 1u << h;
         }
       }
-      const float smax = *reinterpret_cast<const float*>(sp + 2 * D);
-      const double nmax = *reinterpret_cast<const double*>(sp + 2 * D + 8);
-      const double t = (double)a.sm * (double)sq[pr][h];
-      const double bound = (t * (double)smax) * (double)(box > 0 ? box : 0);
-      const double norm2 = ((t * t) * (double)q2[pr][h]) * nmax;
-      const double th = (double)a.th[(int64_t)b * a.hq + g * G + h];
-      keep = !(th > 0.0 && (bound < th || norm2 < th * th));
+      if (a.masks) a.masks[(int64_t)p * a.rmax + r] = mk;
+    }
+    if (list) {
+      const int f8 = r < n8 && mk ? 1 : 0, f4 = r >= n8 && r < nrec && mk ? 1 : 0;
+      int t8, t4;
+      const int2 ex = block_scan2(f8, f4, tmp, t8, t4);
+      if (f8) list[c8 + ex.x] = make_int2(r, (int)mk);
+      if (f4) list[n8 + c4 + ex.y] = make_int2(r - n8, (int)mk);
+      c8 += t8;
+      c4 += t4;
     }
   }
-  const uint64_t bal = __ballot(keep);
-  if (rec < nrec && h == 0) {
-    const uint32_t gm = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
-    a.masks[(int64_t)p * a.rmax + rec] = (uint32_t)(bal >> (lane & ~(Gp - 1))) & gm;
-  }
-}
-#pragma clang fp contract(on)
-
-// One work group per pair: validates the directory entry (the decode's rules, and
-// that it starts where the previous pair's records end), then compacts the kept
-// records of each run into the plan's list and writes the pair entry
-// {offset lo, hi, kept int8, kept int4, stored int8, stored int4, keys of the
-// current block below ctx_len, ok}.
-template <int D, int BLK>
-__global__ void __launch_bounds__(kThreads) skip_compact_kernel(SkipArgs a) {
-  __shared__ int tmp[2 * kWaves];
-  const int tid = threadIdx.x, p = blockIdx.x;
-  const int P = a.batch * a.hkv;
-  int* pe = a.plan + 8 * (int64_t)p;
-  Geo geo;
-  bool ok = skip_header_ok<D, BLK>(a, geo) && sums_ok<D, BLK>(a, geo);
-  int64_t off = 0;
-  int n8 = 0, n4 = 0;
-  if (ok) {
-    const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
-    const v4i e0 = e[0], e1 = e[1], e2 = e[2];
-    off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
-    n8 = e0[2];
-    n4 = e0[3];
-    const int lo8 = e1[2], sink = e1[3], lo4 = e2[0], cur = geo.cur;
-    int64_t expect = geo.data_offset;
-    if (p > 0) {
-      const v4i f = *reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)(p - 1));
-      expect = (int64_t)(((uint64_t)(uint32_t)f[1] << 32) | (uint32_t)f[0]) + (int64_t)f[2] * geo.rec8 +
-               (int64_t)f[3] * geo.rec4;
-    }
-    ok = n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
-         lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
-         off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total && cur + 1 == a.rmax;
-  }
-  if (!ok) {
-    if (tid < 8) pe[tid] = 0;
-    return;
-  }
-  int2* list = reinterpret_cast<int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
-  const uint32_t* m = a.masks + (int64_t)p * a.rmax;
-  int kept[2];
-#pragma unroll
-  for (int run = 0; run < 2; ++run) {
-    const int first = run ? n8 : 0, cnt = run ? n4 : n8, out0 = run ? kept[0] : 0;
-    int c = 0;
-    for (int i0 = 0; i0 < cnt; i0 += kThreads) {
-      const int i = i0 + tid;
-      const uint32_t mk = i < cnt ? m[first + i] : 0u;
-      const int f = mk != 0u ? 1 : 0;
-      int tot, unused;
-      const int2 ex = block_scan2(f, 0, tmp, tot, unused);
-      if (f) list[out0 + c + ex.x] = make_int2(i, (int)mk);
-      c += tot;
-    }
-    kept[run] = c;
-  }
-  if (tid == 0) {
+  if (pe && tid == 0) {
     pe[0] = (int)(uint32_t)off;
     pe[1] = (int)(off >> 32);
-    pe[2] = kept[0];
-    pe[3] = kept[1];
+    pe[2] = c8;
+    pe[3] = c4;
     pe[4] = n8;
     pe[5] = n4;
     pe[6] = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
     pe[7] = 1;
   }
 }
+#pragma clang fp contract(on)
 
 // Work groups of the split kernel: kGrid, or fewer when TRIA_DECODE_GRID (1..kGrid) is
 // set -- a testing and tuning knob: fewer wavefronts give each one longer segments.
@@ -1250,7 +1276,7 @@ int64_t summaries_bytes(const Shape& s, int64_t ctx_len) {
 int64_t skip_workspace_bytes(const Shape& s, int64_t ctx_len) {
   const int64_t pairs = (int64_t)s.batch * s.hkv, rmax = (ctx_len - 1) / s.blk + 1;
   const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
-  return base + 32 * pairs + 8 * pairs * rmax + 4 * pairs * rmax;
+  return base + 32 * pairs + 8 * pairs * rmax;
 }
 
 namespace {
@@ -1268,25 +1294,18 @@ SkipArgs skip_args(const Shape& s, int64_t ctx_len, const void* cache, int64_t c
   a.hq = s.hq;
   a.hkv = s.hkv;
   a.rmax = (int)((ctx_len - 1) / s.blk + 1);
-  int gp = 1;
-  while (gp < s.hq / s.hkv) gp <<= 1;
-  const int rpw = kThreads / gp;
-  a.nwin = (a.rmax + rpw - 1) / rpw;
   return a;
 }
 
 template <int D, int BLK>
-hipError_t launch_decide(const SkipArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((skip_decide_kernel<D, BLK>), dim3(a.batch * a.hkv * a.nwin), dim3(kThreads), 0, stream, a);
+hipError_t launch_plan(const SkipArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((skip_plan_kernel<D, BLK>), dim3(a.batch * a.hkv), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int BLK>
 hipError_t launch_skip_t(const SkipArgs& sa, const DecArgs& da, bool two, hipStream_t stream) {
-  hipError_t e = launch_decide<D, BLK>(sa, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((skip_compact_kernel<D, BLK>), dim3(sa.batch * sa.hkv), dim3(kThreads), 0, stream, sa);
-  e = hipGetLastError();
+  const hipError_t e = launch_plan<D, BLK>(sa, stream);
   if (e != hipSuccess) return e;
   return two ? launch_t<D, BLK, 2, true>(da, stream) : launch_t<D, BLK, 1, true>(da, stream);
 }
@@ -1309,10 +1328,10 @@ hipError_t launch_skip_masks(const Shape& s, int64_t ctx_len, const void* cache,
                              uint32_t* masks, hipStream_t stream) {
   SkipArgs a = skip_args(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale);
   a.masks = masks;
-  if (s.d == 128 && s.blk == 128) return launch_decide<128, 128>(a, stream);
-  if (s.d == 128) return launch_decide<128, 64>(a, stream);
-  if (s.blk == 128) return launch_decide<64, 128>(a, stream);
-  return launch_decide<64, 64>(a, stream);
+  if (s.d == 128 && s.blk == 128) return launch_plan<128, 128>(a, stream);
+  if (s.d == 128) return launch_plan<128, 64>(a, stream);
+  if (s.blk == 128) return launch_plan<64, 128>(a, stream);
+  return launch_plan<64, 64>(a, stream);
 }
 
 hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
@@ -1323,7 +1342,7 @@ hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache
   const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   sa.plan = reinterpret_cast<int*>(ws + base);
-  sa.masks = reinterpret_cast<uint32_t*>(ws + base + 32 * pairs + 8 * pairs * sa.rmax);
+  sa.masks = nullptr;
   DecArgs da;
   da.cache = static_cast<const uint8_t*>(cache);
   da.q = static_cast<const uint16_t*>(q);

@@ -17,4 +17,5 @@ from .gen import (  # noqa: F401
     make_prefill_inputs,
     make_decode_inputs,
     make_skip_decode_inputs,
+    apply_block_structure,
 )

@@ -210,8 +210,16 @@ def make_skip_decode_inputs(cfg: Config, mag_range: tuple[float, float] = (0.1, 
     a head keeps (a stand-in for a learned per-head, per-query threshold).
     Returns k, v, q (bf16 bits) and thresholds.
     """
-    b, hq, hk, d, n, blk = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.block
     k, v, q = make_decode_inputs(cfg)
+    k, thresholds = apply_block_structure(cfg, k, q, mag_range, gamma_range)
+    return k, v, q, thresholds
+
+
+def apply_block_structure(cfg: Config, k: np.ndarray, q: np.ndarray, mag_range: tuple[float, float] = (0.1, 1.0),
+                          gamma_range: tuple[float, float] = (0.6, 0.9)):
+    """The block magnitudes and thresholds of make_skip_decode_inputs, applied to
+    existing decode inputs k [b][Hkv][ctx][d] and q [b][Hq][d] (bf16 bits)."""
+    b, hq, hk, d, n, blk = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.block
     nb = (n + blk - 1) // blk
     u = _open_unit(uniform_u64(cfg.seed, TID_BLOCK_MAG, 0, b * hk * nb)).reshape(b, hk, nb)
     mag = (mag_range[0] + (mag_range[1] - mag_range[0]) * u).astype(np.float32)
@@ -222,4 +230,4 @@ def make_skip_decode_inputs(cfg: Config, mag_range: tuple[float, float] = (0.1, 
     gamma = gamma_range[0] + (gamma_range[1] - gamma_range[0]) * g
     qn = np.sqrt((bf16_bits_to_float32(q).astype(np.float64) ** 2).sum(axis=-1))
     thresholds = (gamma * qn).astype(np.float32)
-    return k, v, q, thresholds
+    return k, thresholds
