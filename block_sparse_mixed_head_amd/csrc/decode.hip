@@ -1034,9 +1034,36 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
   }
 }
 
-// The plan of one pair per work group, one lane per record slot (r = pass * 256 +
-// lane).  Keep bits: for query head h (codes qc, scale sq at the record's precision)
-// and threshold th,
+// Exclusive prefix of two values over a work group of NW wavefronts (tmp: 2 * NW ints);
+// tx, ty = the totals.
+template <int NW>
+__device__ __forceinline__ int2 block_scan2_n(int x, int y, int* tmp, int& tx, int& ty) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ix = wave_scan_incl(x), iy = wave_scan_incl(y);
+  if (lane == 63) {
+    tmp[wave] = ix;
+    tmp[NW + wave] = iy;
+  }
+  __syncthreads();
+  int bx = 0, by = 0;
+  tx = 0;
+  ty = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = tmp[w], u = tmp[NW + w];
+    bx += w < wave ? t : 0;
+    by += w < wave ? u : 0;
+    tx += t;
+    ty += u;
+  }
+  __syncthreads();
+  return make_int2(bx + ix - x, by + iy - y);
+}
+
+// The plan of one pair per work group of 1024 lanes, one lane per (record slot, query
+// head): Gp = G rounded up to a power of two consecutive lanes per record, so a pass
+// covers 1024 / Gp records.  Keep bits: for query head h (codes qc, scale sq at the
+// record's precision) and threshold th,
 //   box  = (t * smax) * max(sum_x max(qc_x lo_x, qc_x hi_x), 0),  t = sm_scale * sq
 //   norm = ((t * t) * |qc|^2) * nmax
 // and h skips the record iff th > 0 and (box < th or norm < th * th), all in IEEE
@@ -1047,40 +1074,39 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
 // int4, keys of the current block below ctx_len, ok} is written after the
 // directory checks of the decode (and that the pair's records start where the
 // previous pair's end).  With a masks buffer, the keep bits of every stored record.
+constexpr int kPlanThreads = 1024;
 #pragma clang fp contract(off)
 template <int D, int BLK>
-__global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
-  constexpr int TPR = D / 8, S = sum_stride(D), KW = D / 16;
+__global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
+  constexpr int TPR = D / 8, S = sum_stride(D), KW = D / 16, NW = kPlanThreads / 64;
   __shared__ __attribute__((aligned(16))) int8_t qc[2][32][D];
   __shared__ float sq[2][32];
   __shared__ int q2[2][32];
   __shared__ float ths[32];
-  __shared__ int tmp[2 * kWaves];
-  const int tid = threadIdx.x;
+  __shared__ int tmp[2 * NW];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int G = a.hq / a.hkv, P = a.batch * a.hkv;
+  int Gp = 1;
+  while (Gp < G) Gp <<= 1;
+  const int rpp = kPlanThreads / Gp, h = tid % Gp;
   const int p = blockIdx.x, b = p / a.hkv, g = p % a.hkv;
   // every load first, in one round trip: both headers, the directory entries of this
-  // pair and the previous one, the query rows and this lane's first index slot (no
-  // address depends on a loaded value; all lie inside their buffers)
+  // pair and the previous one, the query rows, the thresholds and this lane's first
+  // index slot (no address depends on a loaded value; all lie inside their buffers)
   const Hdr64 hc = *reinterpret_cast<const Hdr64*>(a.cache);
   const Hdr64 hs = *reinterpret_cast<const Hdr64*>(a.sums);
   const v4i* ep = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
   const v4i e0 = ep[0], e1 = ep[1], e2 = ep[2];
   const v4i f = *reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)(p > 0 ? p - 1 : p));
-  uint4 qraw[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = tid + i * kThreads, row = piece / TPR;
-    qraw[i] = make_uint4(0, 0, 0, 0);
-    if (row < G)
-      qraw[i] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + row) * D + (piece % TPR) * 8);
-  }
+  const int qrow = tid / TPR, qpart = tid % TPR;  // G * TPR <= 512 pieces
+  uint4 qraw = make_uint4(0, 0, 0, 0);
+  if (qrow < G) qraw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + qrow) * D + qpart * 8);
   const float th_own = tid < G ? a.th[(int64_t)b * a.hq + g * G + tid] : 0.0f;
   v4u lo[KW], hi[KW];
   float smax = 0.0f;
   double nmax = 0.0;
   auto load_slot = [&](int r) __attribute__((always_inline)) {
-    if (r < a.rmax) {
+    if (r < a.rmax && h < G) {
       const uint8_t* sp = a.sums + 64 + ((int64_t)p * a.rmax + r) * S;
 #pragma unroll
       for (int w = 0; w < KW; ++w) {
@@ -1091,7 +1117,7 @@ __global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
       nmax = *reinterpret_cast<const double*>(sp + 2 * D + 8);
     }
   };
-  load_slot(tid);
+  load_slot(tid / Gp);
   // ---- checks (uniform)
   DecArgs da{};
   da.cache_bytes = a.cache_bytes;
@@ -1117,12 +1143,9 @@ __global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
     return;
   }
   // ---- the pair's G query rows at both precisions (the decode's quantiser)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int piece = tid + i * kThreads, row = piece / TPR, part = piece % TPR;
-    if (i * kThreads >= G * TPR) break;  // uniform
+  if (tid < 512) {  // whole TPR groups (uniform per group)
     float x[8];
-    bf16x8_to_f32(qraw[i], x);
+    bf16x8_to_f32(qraw, x);
     uint32_t c8[2], c4;
     float s8, s4;
     quantize8<TPR>(x, c8, c4, s8, s4);
@@ -1133,9 +1156,9 @@ __global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
       const int v4 = (((int)((c4 >> (4 * k)) & 0xFu)) ^ 8) - 8;
       n8sq += v8 * v8;
       n4sq += v4 * v4;
-      if (row < G) {
-        qc[0][row][part * 8 + k] = (int8_t)v8;
-        qc[1][row][part * 8 + k] = (int8_t)v4;
+      if (qrow < G) {
+        qc[0][qrow][qpart * 8 + k] = (int8_t)v8;
+        qc[1][qrow][qpart * 8 + k] = (int8_t)v4;
       }
     }
 #pragma unroll
@@ -1143,11 +1166,11 @@ __global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
       n8sq += __shfl_xor(n8sq, o, TPR);
       n4sq += __shfl_xor(n4sq, o, TPR);
     }
-    if (row < G && part == 0) {
-      sq[0][row] = s8;
-      sq[1][row] = s4;
-      q2[0][row] = n8sq;
-      q2[1][row] = n4sq;
+    if (qrow < G && qpart == 0) {
+      sq[0][qrow] = s8;
+      sq[1][qrow] = s4;
+      q2[0][qrow] = n8sq;
+      q2[1][qrow] = n4sq;
     }
   }
   if (tid < G) ths[tid] = th_own;
@@ -1155,43 +1178,44 @@ __global__ void __launch_bounds__(kThreads) skip_plan_kernel(SkipArgs a) {
   const uint32_t gm = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
   int2* list = a.plan ? reinterpret_cast<int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax : nullptr;
   int c8 = 0, c4 = 0;
-  for (int r0 = 0; r0 < nrec; r0 += kThreads) {
-    const int r = r0 + tid;
+  for (int r0 = 0; r0 < nrec; r0 += rpp) {
+    const int r = r0 + tid / Gp;
     if (r0 > 0) load_slot(r);
-    uint32_t mk = 0;
-    if (r < nrec) {
+    bool keep = false;
+    if (r < nrec && h < G) {
       if (r == 0 || r == n8 - 1) {
-        mk = gm;
+        keep = true;
       } else {
         const int pr = r < n8 ? 0 : 1;
         // per byte of q: the bound's coordinate is hi where the code is >= 0, else lo
-        const double th0 = 0.0;
-        for (int h = 0; h < G; ++h) {
-          const v4u* qv = reinterpret_cast<const v4u*>(&qc[pr][h][0]);
-          int box = 0;
+        const v4u* qv = reinterpret_cast<const v4u*>(&qc[pr][h][0]);
+        int box = 0;
 #pragma unroll
-          for (int w = 0; w < KW; ++w) {
-            const v4u qq = qv[w];
+        for (int w = 0; w < KW; ++w) {
+          const v4u qq = qv[w];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t neg = ((qq[i] >> 7) & 0x01010101u) * 0xFFu;
-              const uint32_t sel = (lo[w][i] & neg) | (hi[w][i] & ~neg);
-              box = __builtin_amdgcn_sdot4((int)qq[i], (int)sel, box, false);
-            }
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t neg = ((qq[i] >> 7) & 0x01010101u) * 0xFFu;
+            const uint32_t sel = (lo[w][i] & neg) | (hi[w][i] & ~neg);
+            box = __builtin_amdgcn_sdot4((int)qq[i], (int)sel, box, false);
           }
-          const double t = (double)a.sm * (double)sq[pr][h];
-          const double bound = (t * (double)smax) * (double)(box > 0 ? box : 0);
-          const double norm2 = ((t * t) * (double)q2[pr][h]) * nmax;
-          const double th = (double)ths[h];
-          if (!(th > th0 && (bound < th || norm2 < th * th))) mk |= 1u << h;
         }
+        const double t = (double)a.sm * (double)sq[pr][h];
+        const double bound = (t * (double)smax) * (double)(box > 0 ? box : 0);
+        const double norm2 = ((t * t) * (double)q2[pr][h]) * nmax;
+        const double th = (double)ths[h];
+        keep = !(th > 0.0 && (bound < th || norm2 < th * th));
       }
-      if (a.masks) a.masks[(int64_t)p * a.rmax + r] = mk;
     }
+    // the record's keep bits from its Gp lanes (aligned groups inside the wavefront)
+    const uint64_t bal = __ballot(keep);
+    const uint32_t mk = (uint32_t)(bal >> (lane & ~(Gp - 1))) & gm;
+    const bool lead = h == 0 && r < nrec;
+    if (lead && a.masks) a.masks[(int64_t)p * a.rmax + r] = mk;
     if (list) {
-      const int f8 = r < n8 && mk ? 1 : 0, f4 = r >= n8 && r < nrec && mk ? 1 : 0;
+      const int f8 = lead && r < n8 && mk ? 1 : 0, f4 = lead && r >= n8 && mk ? 1 : 0;
       int t8, t4;
-      const int2 ex = block_scan2(f8, f4, tmp, t8, t4);
+      const int2 ex = block_scan2_n<NW>(f8, f4, tmp, t8, t4);
       if (f8) list[c8 + ex.x] = make_int2(r, (int)mk);
       if (f4) list[n8 + c4 + ex.y] = make_int2(r - n8, (int)mk);
       c8 += t8;
@@ -1299,7 +1323,7 @@ SkipArgs skip_args(const Shape& s, int64_t ctx_len, const void* cache, int64_t c
 
 template <int D, int BLK>
 hipError_t launch_plan(const SkipArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((skip_plan_kernel<D, BLK>), dim3(a.batch * a.hkv), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((skip_plan_kernel<D, BLK>), dim3(a.batch * a.hkv), dim3(kPlanThreads), 0, stream, a);
   return hipGetLastError();
 }
 
