@@ -615,7 +615,165 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
                   "decode launch");
 }
 
+// ------------------------------------------------------------------ (f3) paged cache
+static int64_t paged_rmax(const tria_dims* d, int64_t ctx_len) { return (ctx_len - 1) / d->block + 1; }
+static int64_t paged_table_bytes_of(const tria_dims* d, int64_t ctx_len) {
+  const int64_t P = (int64_t)d->batch * d->n_kv_heads;
+  return 64 + 64 * P + 4 * P * paged_rmax(d, ctx_len);
+}
+static const int32_t kPagedMagic = 0x50564B54;  // "TKVP"
+
+// Stored blocks of one KV head for current block c in record order: {block, 8 or 4}.
+static void record_blocks(int64_t c, int64_t hi, int64_t keep, std::vector<std::pair<int64_t, int>>& out) {
+  out.clear();
+  const int64_t lo8 = (c - hi >= 2) ? c - hi : 0;
+  if (lo8 > 0) out.push_back({0, 8});
+  for (int64_t kb = lo8; kb <= c; ++kb) out.push_back({kb, 8});
+  for (int64_t kb = std::max<int64_t>(1, c - keep); kb <= c - hi - 1; ++kb) out.push_back({kb, 4});
+}
+
+tria_status tria_paged_page_bytes(const tria_dims* dims, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  *bytes = (size_t)(2LL * dims->block * dims->head_dim + 8LL * dims->block);
+  return ok();
+}
+
+tria_status tria_paged_table_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(bytes);
+  if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
+  *bytes = (size_t)paged_table_bytes_of(dims, ctx_len);
+  return ok();
+}
+
+tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                   int32_t n_policy_heads, int64_t ctx_len, int64_t n_pages, const void* old_table,
+                                   size_t old_table_bytes, const int32_t* free_pages, int32_t n_free, void* table,
+                                   size_t table_bytes, int32_t* n_used, int32_t* released, int32_t released_capacity,
+                                   int32_t* n_released) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(table);
+  NONNULL(n_used);
+  NONNULL(n_released);
+  if (ctx_len < 1 || ctx_len > dims->seq_len)
+    return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld outside [1, seq_len=%lld]", (long long)ctx_len,
+                (long long)dims->seq_len);
+  if (n_pages < 1 || n_pages > INT32_MAX) return fail(TRIA_ERR_INVALID_ARG, "n_pages must be in [1, 2^31 - 1]");
+  if (n_free < 0 || (n_free > 0 && !free_pages)) return fail(TRIA_ERR_INVALID_ARG, "free_pages is NULL");
+  if (released_capacity < 0 || (released_capacity > 0 && !released))
+    return fail(TRIA_ERR_INVALID_ARG, "released is NULL");
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  const int64_t need = paged_table_bytes_of(dims, ctx_len);
+  if ((int64_t)table_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "table needs %lld bytes, got %zu", (long long)need, table_bytes);
+  const int64_t P = (int64_t)dims->batch * dims->n_kv_heads;
+  const int64_t c = (ctx_len - 1) / dims->block, rmax = c + 1;
+  // the old table: same shape and policy, pages inside the pool, each page once
+  std::vector<uint8_t> used(static_cast<size_t>(n_pages), 0);
+  int64_t orm = 0, oc = 0;
+  const uint8_t* ot = static_cast<const uint8_t*>(old_table);
+  if (ot) {
+    if (old_table_bytes < 64) return fail(TRIA_ERR_INVALID_ARG, "old table smaller than its header");
+    int32_t h[8];
+    int64_t h64[4];
+    std::memcpy(h, ot, 32);
+    std::memcpy(h64, ot + 32, 32);
+    orm = h[6];
+    oc = h[7];
+    if (h[0] != kPagedMagic || h[1] != 4 || h[2] != dims->batch || h[3] != dims->n_kv_heads ||
+        h[4] != dims->head_dim || h[5] != dims->block || orm != oc + 1 || oc < 0 || h64[0] < 1 ||
+        (h64[0] - 1) / dims->block != oc || h64[2] != n_pages)
+      return fail(TRIA_ERR_INVALID_ARG, "old table header does not match (dims, n_pages)");
+    if ((int64_t)old_table_bytes < 64 + 64 * P + 4 * P * orm)
+      return fail(TRIA_ERR_INVALID_ARG, "old table smaller than its size");
+  }
+  std::vector<uint8_t> out(static_cast<size_t>(need), 0);
+  std::vector<int32_t> rel;
+  int64_t taken = 0;
+  std::vector<std::pair<int64_t, int>> nb, ob;
+  for (int64_t p = 0; p < P; ++p) {
+    const int g = (int)(p % dims->n_kv_heads);
+    record_blocks(c, pol.hi[g], pol.keep[g], nb);
+    std::vector<int32_t> opages;
+    if (ot) {
+      int32_t e[16];
+      std::memcpy(e, ot + 64 + 64 * p, 64);
+      if (e[4] != pol.hi[g] || e[5] != pol.keep[g])
+        return fail(TRIA_ERR_INVALID_ARG, "old table entry %lld holds another policy", (long long)p);
+      record_blocks(oc, pol.hi[g], pol.keep[g], ob);
+      if (e[2] + e[3] != (int64_t)ob.size()) return fail(TRIA_ERR_INVALID_ARG, "old table entry %lld corrupt", (long long)p);
+      opages.resize(ob.size());
+      std::memcpy(opages.data(), ot + 64 + 64 * P + 4 * (p * orm), 4 * ob.size());
+      for (int32_t pg : opages) {
+        if (pg < 0 || pg >= n_pages || used[pg]) return fail(TRIA_ERR_INVALID_ARG, "old table page %d invalid", pg);
+        used[pg] = 1;
+      }
+    }
+    int32_t* pages = reinterpret_cast<int32_t*>(out.data() + 64 + 64 * P + 4 * (p * rmax));
+    for (int64_t r = 0; r < rmax; ++r) pages[r] = -1;
+    std::vector<char> kept(opages.size(), 0);
+    for (size_t r = 0; r < nb.size(); ++r) {
+      int32_t pg = -1;
+      for (size_t o = 0; o < ob.size() && ot; ++o)
+        if (ob[o] == nb[r]) {
+          pg = opages[o];
+          kept[o] = 1;
+          break;
+        }
+      if (pg < 0) {
+        if (taken < n_free) pg = free_pages[taken];
+        ++taken;
+      }
+      pages[r] = pg;
+    }
+    for (size_t o = 0; o < opages.size(); ++o)
+      if (!kept[o]) rel.push_back(opages[o]);
+    int32_t e[16] = {0};
+    int64_t n8 = 0;
+    for (auto& x : nb) n8 += x.second == 8;
+    const int64_t lo8 = (c - pol.hi[g] >= 2) ? c - pol.hi[g] : 0;
+    e[2] = (int32_t)n8;
+    e[3] = (int32_t)(nb.size() - n8);
+    e[4] = pol.hi[g];
+    e[5] = pol.keep[g];
+    e[6] = (int32_t)lo8;
+    e[7] = lo8 > 0 ? 1 : 0;
+    e[8] = e[3] > 0 ? (int32_t)std::max<int64_t>(1, c - pol.keep[g]) : 0;
+    e[9] = e[3] > 0 ? (int32_t)(c - pol.hi[g] - 1) : -1;
+    std::memcpy(out.data() + 64 + 64 * p, e, 64);
+  }
+  *n_used = (int32_t)std::min<int64_t>(taken, INT32_MAX);
+  *n_released = (int32_t)rel.size();
+  if (taken > n_free)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "%lld free pages needed, %d given", (long long)taken, n_free);
+  if ((int64_t)rel.size() > released_capacity)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "%zu released pages, capacity %d", rel.size(), released_capacity);
+  // the free pages taken: inside the pool and not held by a kept record or twice
+  for (int64_t i = 0; i < taken; ++i) {
+    const int32_t pg = free_pages[i];
+    if (pg < 0 || pg >= n_pages) return fail(TRIA_ERR_INVALID_ARG, "free page %d outside the pool", pg);
+    if (used[pg] == 2) return fail(TRIA_ERR_INVALID_ARG, "free page %d given twice", pg);
+    // (a page this update releases is still held: it can be reused from the next call on)
+    if (used[pg] == 1) return fail(TRIA_ERR_INVALID_ARG, "free page %d is held by the old table", pg);
+    used[pg] = 2;
+  }
+  int32_t h[8] = {kPagedMagic, 4, dims->batch, dims->n_kv_heads, dims->head_dim, dims->block, (int32_t)rmax, (int32_t)c};
+  int64_t h64[4] = {ctx_len, 2LL * dims->block * dims->head_dim + 8LL * dims->block, n_pages, 0};
+  std::memcpy(out.data(), h, 32);
+  std::memcpy(out.data() + 32, h64, 32);
+  std::memcpy(table, out.data(), out.size());
+  if (!rel.empty()) std::memcpy(released, rel.data(), 4 * rel.size());
+  return ok();
+}
+
 // ------------------------------------------------------------------ (f4) dynamic block skipping
+
 static tria_status check_skip_call(const tria_dims* dims, int64_t ctx_len, const void* cache, size_t cache_bytes) {
   tria_status st = check_dims(dims);
   if (st != TRIA_OK) return st;
@@ -706,6 +864,57 @@ tria_status tria_decode_skip(const tria_dims* dims, const void* cache, size_t ca
   return launched(tria::launch_decode_skip(s, ctx_len, cache, (int64_t)cache_bytes, summaries, q_bf16, thresholds,
                                            sm_scale, out, workspace, static_cast<hipStream_t>(stream)),
                   "skip decode launch");
+}
+
+tria_status tria_pack_kv_cache_paged(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                     int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16,
+                                     const void* v_bf16, const void* table, size_t table_bytes,
+                                     const void* old_table, size_t old_table_bytes, void* pool,
+                                     size_t pool_bytes, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(k_bf16);
+  NONNULL(v_bf16);
+  NONNULL(table);
+  NONNULL(pool);
+  if (ctx_len < 1 || ctx_len > dims->seq_len)
+    return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld outside [1, seq_len=%lld]", (long long)ctx_len,
+                (long long)dims->seq_len);
+  if ((int64_t)dims->batch * dims->n_kv_heads > 65535)
+    return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads above 65535");
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  if ((int64_t)table_bytes < paged_table_bytes_of(dims, ctx_len))
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "table smaller than tria_paged_table_bytes");
+  if (old_table && old_table_bytes < 64) return fail(TRIA_ERR_INVALID_ARG, "old table smaller than its header");
+  const tria::CacheGeom g = cache_geom(dims, pol, ctx_len);
+  if ((int64_t)pool_bytes < g.rec8_bytes) return fail(TRIA_ERR_BUFFER_TOO_SMALL, "pool smaller than one page");
+  return launched(tria::launch_pack_paged(shape_of(dims), pol, g, k_bf16, v_bf16, table, (int64_t)table_bytes,
+                                          old_table, (int64_t)old_table_bytes, pool, (int64_t)pool_bytes,
+                                          static_cast<hipStream_t>(stream)),
+                  "paged pack launch");
+}
+
+tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t table_bytes, const void* pool,
+                              size_t pool_bytes, int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  tria_status st = check_skip_call(dims, ctx_len, table, table_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(pool);
+  NONNULL(q_bf16);
+  NONNULL(out);
+  NONNULL(workspace);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const tria::Shape s = shape_of(dims);
+  if ((int64_t)table_bytes < paged_table_bytes_of(dims, ctx_len))
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "table smaller than tria_paged_table_bytes");
+  const int64_t need = tria::skip_workspace_bytes(s, ctx_len);
+  if ((int64_t)ws_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
+  return launched(tria::launch_decode_paged(s, ctx_len, table, (int64_t)table_bytes, pool, (int64_t)pool_bytes,
+                                            q_bf16, sm_scale, out, workspace, static_cast<hipStream_t>(stream)),
+                  "paged decode launch");
 }
 
 tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes, const void* q_bf16,

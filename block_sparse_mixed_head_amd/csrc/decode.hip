@@ -69,6 +69,11 @@ struct DecArgs {
   int varlen;  // version-3 cache: each directory entry holds its sequence's ctx_len
   const int* plan;  // dynamic skipping: per pair {offset, kept and stored counts, mask}, kept lists
   int rmax;         // record slots per pair in the plan's lists
+  // paged cache: `cache` is the page table, records at pool + page * page_bytes (list
+  // entries hold pages)
+  int paged;
+  const uint8_t* pool;
+  int64_t page_bytes;
 };
 
 struct Geo {
@@ -102,6 +107,24 @@ template <int D, int BLK>
 __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
   const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
   return header_ok_h<D, BLK>(a, h, geo);
+}
+
+// Page table header (version 4) against the launch; geo.total = the table size.
+template <int D, int BLK>
+__device__ __forceinline__ bool paged_header_h(const DecArgs& a, const Hdr64& h, Geo& geo) {
+  geo.rec8 = 2LL * BLK * D + 8LL * BLK;
+  geo.rec4 = (int64_t)BLK * D + 8LL * BLK;
+  geo.cur = (int)((a.ctx_len - 1) / BLK);
+  geo.data_offset = 64 + 64LL * a.batch * a.hkv;
+  geo.total = geo.data_offset + 4LL * a.batch * a.hkv * (geo.cur + 1);
+  return h.w[0] == 0x50564B54 && h.w[1] == 4 && h.w[2] == a.batch && h.w[3] == a.hkv && h.w[4] == D &&
+         h.w[5] == BLK && h.w[6] == geo.cur + 1 && h.w[7] == geo.cur && h.q(4) == a.ctx_len &&
+         h.q(5) == geo.rec8 && geo.total <= a.cache_bytes;
+}
+template <int D, int BLK>
+__device__ __forceinline__ bool paged_header_ok(const DecArgs& a, Geo& geo) {
+  const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  return paged_header_h<D, BLK>(a, h, geo);
 }
 
 // Inclusive prefix sum over the wavefront: DPP row shifts (1, 2, 4, 8) within each
@@ -407,7 +430,7 @@ template <int D, int BLK, int RG, bool IS4, bool SKIP, class Pre>
 __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes, int j0, int j1,
                                           const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_jb,
                                           int mask_first, SegState<D, RG>& st, int lr, int kq, float* slot, Pre&& pre,
-                                          const int2* list, int nstored, uint32_t hfull) {
+                                          const int2* list, int64_t stride, uint32_t hfull) {
   using IO = StepIO<D, BLK, IS4>;
   constexpr int SPB = BLK / 32;
   if (j0 >= j1) return;
@@ -420,10 +443,10 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     return j / SPB == mask_jb ? mask_first - 32 * (j % SPB) : 1 << 30;
   };
   if constexpr (SKIP) {
-    // every stored record of the run is addressable; only kept ones are loaded (the
-    // resource is built per load with the range or, past the window, an empty range)
-    void* const base = reinterpret_cast<void*>(uni64(reinterpret_cast<int64_t>(rec0)));
-    const int nbytes = uni(nstored * rb);
+    // record i of the list at rec0 + i * stride; only listed records are loaded (the
+    // resource is built per load over the record or, past the window, empty)
+    const int64_t base0 = uni64(reinterpret_cast<int64_t>(rec0));
+    const int64_t strd = uni64(stride);
     const int lane = threadIdx.x & 63;
     typename IO::Buf A, B, C;
     // windows of up to 64 kept records: lane l holds the window's entry l, read by
@@ -445,9 +468,10 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
       auto ld = [&](typename IO::Buf& r, int j) __attribute__((always_inline)) {
         const bool in = j < w1;
         const int rec = in ? __builtin_amdgcn_readlane(e.x, j / SPB - r0) : 0;
-        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, in ? nbytes : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void*>(base0 + (int64_t)rec * strd), (short)0, in ? rb : 0, 0x00020000);
         __builtin_amdgcn_sched_barrier(0);
-        IO::load(r, rr, in ? rec * rb : 0, in ? j % SPB : 0, lr, kq);
+        IO::load(r, rr, 0, in ? j % SPB : 0, lr, kq);
         __builtin_amdgcn_sched_barrier(0);
       };
       auto hoff = [&](int j) __attribute__((always_inline)) -> uint32_t {
@@ -598,7 +622,7 @@ decode_split_kernel(DecArgs a) {
     }
   };
   Geo geo;
-  if (!header_ok<D, BLK>(a, geo)) {
+  if (!(SKIP && a.paged ? paged_header_ok<D, BLK>(a, geo) : header_ok<D, BLK>(a, geo))) {
     if (blockIdx.x == 0 && tid == 0) reinterpret_cast<int*>(a.ws)[0] = 0;
     return;
   }
@@ -663,7 +687,8 @@ decode_split_kernel(DecArgs a) {
     }
   }
   __syncthreads();
-  if (bad || U < 4 || geo.data_offset + (int64_t)n8p[P] * geo.rec8 + (int64_t)n4p[P] * geo.rec4 > geo.total) {
+  if (bad || U < 4 ||
+      (!(SKIP && a.paged) && geo.data_offset + (int64_t)n8p[P] * geo.rec8 + (int64_t)n4p[P] * geo.rec4 > geo.total)) {
     if (blockIdx.x == 0 && tid == 0) wsh[0] = 0;
     return;
   }
@@ -696,15 +721,21 @@ decode_split_kernel(DecArgs a) {
     const uint8_t* rec0 =
         a.cache + geo.data_offset + (int64_t)uni(n8p[p]) * geo.rec8 + (int64_t)uni(n4p[p]) * geo.rec4;
     // SKIP: the pair's records start at its (validated) offset; n8s, n4s records stored
-    int n8s = n8, n4s = n4;
+    int n8s = n8;
     const int2* list = nullptr;
+    const uint8_t* rec4 = nullptr;
+    int64_t stride8 = geo.rec8, stride4 = geo.rec4;
     if constexpr (SKIP) {
       const int* pe = a.plan + 8 * (int64_t)p;
       rec0 = a.cache + (int64_t)(((uint64_t)(uint32_t)pe[1] << 32) | (uint32_t)pe[0]);
       n8s = uni(pe[4]);
-      n4s = uni(pe[5]);
       list = reinterpret_cast<const int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
+      if (a.paged) {  // list entries are pages of the pool
+        rec0 = a.pool;
+        stride8 = stride4 = a.page_bytes;
+      }
     }
+    rec4 = SKIP && a.paged ? rec0 : rec0 + (int64_t)n8s * geo.rec8;
     const uint32_t hfull = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
 
     // this pair's G query rows, quantised at both precisions (MFMA B operands)
@@ -769,13 +800,12 @@ decode_split_kernel(DecArgs a) {
     const int mask_first = uni(mfp[p]);
     const bool has8 = j8a < j8b;
     run_steps<D, BLK, RG, false, SKIP>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq,
-                                       scl[wave], quantise_q, list, n8s, hfull);
-    run_steps<D, BLK, RG, true, SKIP>(rec0 + (int64_t)n8s * geo.rec8, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq,
-                                      scl[wave],
+                                       scl[wave], quantise_q, list, stride8, hfull);
+    run_steps<D, BLK, RG, true, SKIP>(rec4, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq, scl[wave],
                                       [&]() __attribute__((always_inline)) {
                                         if (!has8) quantise_q();
                                       },
-                                      SKIP ? list + n8s : nullptr, n4s, hfull);
+                                      SKIP ? list + n8s : nullptr, stride4, hfull);
 
     // ---- the wavefront's partial for this pair
 #pragma unroll
@@ -1235,6 +1265,55 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
 }
 #pragma clang fp contract(on)
 
+// Plan of a paged cache (every record kept): one work group per pair checks the
+// table header and the pair's entry (the decode's rules) and that every page lies
+// inside the pool, then lists the pair's records {page, all heads} (int8 run from
+// entry 0, int4 run from entry n8) and writes the pair entry as the skip plan does.
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) paged_plan_kernel(DecArgs a, int64_t pool_pages) {
+  const int tid = threadIdx.x, p = blockIdx.x;
+  const int P = a.batch * a.hkv, G = a.hq / a.hkv;
+  __shared__ int bad;
+  const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  const v4i* ep = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+  const v4i e0 = ep[0], e1 = ep[1], e2 = ep[2];
+  Geo geo;
+  const int rmax = (int)((a.ctx_len - 1) / BLK) + 1;
+  const int32_t* pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * rmax;
+  int pg0 = tid < rmax ? pages[tid] : 0;  // the first 256 pages with the headers
+  const int n8 = e0[2], n4 = e0[3], lo8 = e1[2], sink = e1[3], lo4 = e2[0];
+  bool ok = paged_header_h<D, BLK>(a, h, geo);
+  const int cur = geo.cur;
+  ok = ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
+       lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
+       a.rmax == rmax;
+  int* pe = const_cast<int*>(a.plan) + 8 * (int64_t)p;
+  if (!ok) {
+    if (tid < 8) pe[tid] = 0;
+    return;
+  }
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  int2* list = reinterpret_cast<int2*>(const_cast<int*>(a.plan) + 8 * (int64_t)P) + (int64_t)p * a.rmax;
+  const int gm = G >= 32 ? -1 : (int)((1u << G) - 1u);
+  for (int r = tid; r < n8 + n4; r += kThreads) {
+    const int pg = r < kThreads ? pg0 : pages[r];
+    if (pg < 0 || (int64_t)pg >= pool_pages) bad = 1;
+    list[r] = make_int2(pg, gm);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    pe[0] = 0;
+    pe[1] = 0;
+    pe[2] = n8;
+    pe[3] = n4;
+    pe[4] = n8;
+    pe[5] = n4;
+    pe[6] = (int)(a.ctx_len - (int64_t)cur * BLK);
+    pe[7] = bad ? 0 : 1;
+  }
+}
+
 // Work groups of the split kernel: kGrid, or fewer when TRIA_DECODE_GRID (1..kGrid) is
 // set -- a testing and tuning knob: fewer wavefronts give each one longer segments.
 int split_grid() {
@@ -1284,6 +1363,9 @@ hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int
   a.varlen = varlen ? 1 : 0;
   a.plan = nullptr;
   a.rmax = 0;
+  a.paged = 0;
+  a.pool = nullptr;
+  a.page_bytes = 0;
   const int G = s.hq / s.hkv;
   const bool two = G > 16;
   if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2>(a, stream) : launch_t<128, 128, 1>(a, stream);
@@ -1335,6 +1417,53 @@ hipError_t launch_skip_t(const SkipArgs& sa, const DecArgs& da, bool two, hipStr
 }
 }  // namespace
 
+hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* table, int64_t table_bytes,
+                               const void* pool, int64_t pool_bytes, const void* q, float sm_scale, float* out,
+                               void* workspace, hipStream_t stream) {
+  const int64_t pairs = (int64_t)s.batch * s.hkv;
+  const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
+  DecArgs da;
+  da.cache = static_cast<const uint8_t*>(table);
+  da.q = static_cast<const uint16_t*>(q);
+  da.ws = static_cast<float*>(workspace);
+  da.out = out;
+  da.cache_bytes = table_bytes;
+  da.ctx_len = ctx_len;
+  da.batch = s.batch;
+  da.hq = s.hq;
+  da.hkv = s.hkv;
+  da.c = sm_scale * 1.44269504088896340736f;
+  da.varlen = 0;
+  da.plan = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + base);
+  da.rmax = (int)((ctx_len - 1) / s.blk + 1);
+  da.paged = 1;
+  da.pool = static_cast<const uint8_t*>(pool);
+  da.page_bytes = 2LL * s.blk * s.d + 8LL * s.blk;
+  const int64_t pool_pages = pool_bytes / da.page_bytes;
+  const bool two = s.hq / s.hkv > 16;
+  auto run = [&](auto plan_kernel, auto split1, auto split2, auto merge, int D) -> hipError_t {
+    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)pairs), dim3(kThreads), 0, stream, da, pool_pages);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(two ? split2 : split1, dim3(split_grid()), dim3(kThreads), 0, stream, da);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(merge, dim3(s.batch * s.hq), dim3(D), 0, stream, da);
+    return hipGetLastError();
+  };
+  if (s.d == 128 && s.blk == 128)
+    return run(paged_plan_kernel<128, 128>, decode_split_kernel<128, 128, 1, true>,
+               decode_split_kernel<128, 128, 2, true>, decode_merge_kernel<128>, 128);
+  if (s.d == 128)
+    return run(paged_plan_kernel<128, 64>, decode_split_kernel<128, 64, 1, true>, decode_split_kernel<128, 64, 2, true>,
+               decode_merge_kernel<128>, 128);
+  if (s.blk == 128)
+    return run(paged_plan_kernel<64, 128>, decode_split_kernel<64, 128, 1, true>, decode_split_kernel<64, 128, 2, true>,
+               decode_merge_kernel<64>, 64);
+  return run(paged_plan_kernel<64, 64>, decode_split_kernel<64, 64, 1, true>, decode_split_kernel<64, 64, 2, true>,
+             decode_merge_kernel<64>, 64);
+}
+
 hipError_t launch_summaries(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
                             hipStream_t stream) {
   SkipArgs a = skip_args(s, ctx_len, cache, cache_bytes, nullptr, nullptr, nullptr, 0.0f);
@@ -1381,6 +1510,9 @@ hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache
   da.varlen = 0;
   da.plan = sa.plan;
   da.rmax = sa.rmax;
+  da.paged = 0;
+  da.pool = nullptr;
+  da.page_bytes = 0;
   const bool two = s.hq / s.hkv > 16;
   if (s.d == 128 && s.blk == 128) return launch_skip_t<128, 128>(sa, da, two, stream);
   if (s.d == 128) return launch_skip_t<128, 64>(sa, da, two, stream);

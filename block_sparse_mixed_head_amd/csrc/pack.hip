@@ -52,6 +52,12 @@ struct PackArgs {
   int batch, hkv;
   KvPolicy pol;
   CacheGeom geo;
+  // paged cache: records go to pool + page * page_bytes by the version-4 table for
+  // geo.ctx_len (else null); old_table (or null): the table the pool holds
+  const uint8_t* table;
+  const uint8_t* old_table;
+  int64_t table_bytes, old_table_bytes, pool_pages, page_bytes;
+  uint8_t* pool;
 };
 
 struct Blocks {  // the stored set of one KV head for current block c
@@ -121,7 +127,38 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   uint8_t* rec = a.cache + off;
   const int tid = threadIdx.x;
 
-  if (j == 0 && tid == 0 && !a.varlen) {
+  if (a.table) {  // paged: the record's page from the table (checked), nothing else written
+    const int P = a.batch * a.hkv, rmax = c + 1;
+    const int32_t* th = reinterpret_cast<const int32_t*>(a.table);
+    const int64_t* th64 = reinterpret_cast<const int64_t*>(a.table);
+    if (th[0] != 0x50564B54 || th[1] != 4 || th[2] != a.batch || th[3] != a.hkv || th[4] != D || th[5] != BLK ||
+        th[6] != rmax || th[7] != c || th64[4] != ctx || th64[5] != a.page_bytes ||
+        64 + 64LL * P + 4LL * P * rmax > a.table_bytes)
+      return;
+    const int32_t* e = th + 16 + 16 * pair;
+    if (e[2] != st.n8 || e[3] != st.n4) return;
+    const int page = th[16 + 16 * P + pair * rmax + j];
+    if (page < 0 || page >= a.pool_pages) return;
+    rec = a.pool + (int64_t)page * a.page_bytes;
+    if (a.old_table && kb < c) {  // a record the pool already holds at this page
+      const int32_t* oh = reinterpret_cast<const int32_t*>(a.old_table);
+      const int oc = oh[7], orm = oc + 1;
+      if (oh[0] == 0x50564B54 && oh[1] == 4 && oh[2] == a.batch && oh[3] == a.hkv && oh[4] == D && oh[5] == BLK &&
+          oh[6] == orm && oc >= 0 && 64 + 64LL * P + 4LL * P * orm <= a.old_table_bytes) {
+        const Blocks so = stored_blocks(oc, a.pol.hi[g], a.pol.keep[g]);
+        int jo = -1;
+        if (!is4) {
+          if (kb == 0 && so.sink) jo = 0;
+          else if (kb >= so.lo8 && kb <= oc) jo = so.sink + kb - so.lo8;
+        } else if (kb >= so.lo4 && kb <= so.hi4) {
+          jo = so.n8 + kb - so.lo4;
+        }
+        if (jo >= 0 && oh[16 + 16 * P + pair * orm + jo] == page) return;
+      }
+    }
+  }
+
+  if (j == 0 && tid == 0 && !a.varlen && !a.table) {
     int32_t* e = reinterpret_cast<int32_t*>(a.cache + 64 + 64 * (int64_t)pair);
     *reinterpret_cast<int64_t*>(e) = pair_off;
     e[2] = st.n8;
@@ -151,7 +188,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
     }
   }
 
-  if (pair == 0 && j == 0 && !a.varlen) {  // the padding between the directory and the first record
+  if (pair == 0 && j == 0 && !a.varlen && !a.table) {  // the padding between the directory and the first record
     const int64_t pad0 = 64 + 64LL * a.batch * a.hkv;
     for (int64_t i = pad0 + tid; i < a.geo.data_offset; i += kThreads) a.cache[i] = 0;
   }
@@ -439,6 +476,9 @@ hipError_t launch_pack_varlen(const Shape& s, const KvPolicy& pol, const CacheGe
   a.hkv = s.hkv;
   a.pol = pol;
   a.geo = geo;
+  a.table = a.old_table = nullptr;
+  a.pool = nullptr;
+  a.table_bytes = a.old_table_bytes = a.pool_pages = a.page_bytes = 0;
   const int max_stored = geo.cur_block + 1;
   if (s.d == 128 && s.blk == 128) return launch_t<128, 128>(a, max_stored, stream);
   if (s.d == 128 && s.blk == 64) return launch_t<128, 64>(a, max_stored, stream);
@@ -462,6 +502,39 @@ hipError_t launch_pack(const Shape& s, const KvPolicy& pol, const CacheGeom& geo
   a.hkv = s.hkv;
   a.pol = pol;
   a.geo = geo;
+  a.table = a.old_table = nullptr;
+  a.pool = nullptr;
+  a.table_bytes = a.old_table_bytes = a.pool_pages = a.page_bytes = 0;
+  const int max_stored = geo.cur_block + 1;
+  if (s.d == 128 && s.blk == 128) return launch_t<128, 128>(a, max_stored, stream);
+  if (s.d == 128 && s.blk == 64) return launch_t<128, 64>(a, max_stored, stream);
+  if (s.d == 64 && s.blk == 128) return launch_t<64, 128>(a, max_stored, stream);
+  return launch_t<64, 64>(a, max_stored, stream);
+}
+
+hipError_t launch_pack_paged(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const void* k, const void* v,
+                             const void* table, int64_t table_bytes, const void* old_table, int64_t old_table_bytes,
+                             void* pool, int64_t pool_bytes, hipStream_t stream) {
+  PackArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.cache = nullptr;
+  a.old = nullptr;
+  a.ogeo = geo;
+  a.only_current = 0;
+  a.varlen = 0;
+  a.n = s.n;
+  a.batch = s.batch;
+  a.hkv = s.hkv;
+  a.pol = pol;
+  a.geo = geo;
+  a.table = static_cast<const uint8_t*>(table);
+  a.old_table = static_cast<const uint8_t*>(old_table);
+  a.table_bytes = table_bytes;
+  a.old_table_bytes = old_table ? old_table_bytes : 0;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_bytes = geo.rec8_bytes;
+  a.pool_pages = pool_bytes / geo.rec8_bytes;
   const int max_stored = geo.cur_block + 1;
   if (s.d == 128 && s.blk == 128) return launch_t<128, 128>(a, max_stored, stream);
   if (s.d == 128 && s.blk == 64) return launch_t<128, 64>(a, max_stored, stream);

@@ -343,6 +343,70 @@ tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t 
                                size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Paged compressed cache (block table).                                      */
+/* ------------------------------------------------------------------------- */
+/*
+ * ZimaSpace page on attention memory (the section on the KV cache as per-token state
+ * kept for the whole conversation, and its closing list of memory levers): paged
+ * allocation of the KV cache cuts fragmentation when request lengths are not known in
+ * advance, beside lower cache precision; llmis.ru chapter 3.5 (its closing section on
+ * what grouped heads compose with): paging changes where the cache lives, not its
+ * size, so it composes with cache quantisation.  Here the records of the compressed cache (the version-2 record format,
+ * int8 or int4) live in a caller-owned pool of pages of tria_paged_page_bytes each
+ * (one int8 record; an int4 record uses the first half of its page), and a table maps
+ * every stored record to its page.  Going from ctx_len - 1 to ctx_len then moves no
+ * record: records that stay keep their pages, new ones (the current block, a block
+ * demoted from int8 to int4) take pages from the caller's free list, dropped ones
+ * release theirs.
+ *
+ * Table (version 4): 64-byte header {int32 magic "TKVP", 4, batch, n_kv_heads,
+ *   head_dim, block, rmax = c + 1, c (current block); int64 ctx_len, page bytes,
+ *   n_pages (pool size in pages), 0}, one 64-byte entry per (batch, KV head) laid out
+ *   as in version 2 with a zero offset {0, 0, n8, n4, hi, keep, lo8, sink, lo4, hi4,
+ *   0...}, then per pair rmax int32 page ids in record order (int8 records, then int4;
+ *   -1 past the pair's records).
+ *
+ * tria_paged_page_bytes, tria_paged_table_bytes: sizes.
+ * tria_build_paged_table (host, synchronous): the table for ctx_len (host buffer).
+ *   old_table (host, or NULL for a fresh cache): the table of the same cache at an
+ *   earlier ctx_len with the same dims, policy and n_pages.  A record whose (block,
+ *   precision) the old table stores keeps its page; every other record takes the next
+ *   page of free_pages (in pair order, then record order); *n_used = pages taken from
+ *   the front of free_pages; the old records not kept release their pages into
+ *   released (*n_released, in pair and record order).  Errors: BUFFER_TOO_SMALL when
+ *   n_free or released_capacity is short (*n_used, *n_released hold the needs);
+ *   INVALID_ARG when the old table does not match or a page is outside [0, n_pages),
+ *   repeated, or (for a free page) still held by the old table.  Nothing is written
+ *   on error.
+ * tria_pack_kv_cache_paged: writes into the pool (device) the records of the table
+ *   (device copy of a tria_build_paged_table result for this ctx_len and policy) from
+ *   the bf16 K, V rows, quantised as tria_pack_kv_cache does.  old_table (device, or
+ *   NULL): the table the pool currently holds; a record before the current block that
+ *   it maps to the same page and (block, precision) is left as it is, so a step
+ *   within a block rewrites one record per pair and a block start writes the new
+ *   ones.  A table whose header does not match the call, or a page outside the pool,
+ *   writes nothing.
+ * tria_decode_paged: tria_decode over a paged cache (the kernels of tria_decode_skip
+ *   with every record kept; the workspace of tria_decode_skip_workspace_bytes).  A
+ *   table that does not validate writes NaN to `out` and reads no record.  Results
+ *   equal tria_decode on the contiguous cache with the same content. */
+tria_status tria_paged_page_bytes(const tria_dims* dims, size_t* bytes);
+tria_status tria_paged_table_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
+tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                   int32_t n_policy_heads, int64_t ctx_len, int64_t n_pages,
+                                   const void* old_table, size_t old_table_bytes, const int32_t* free_pages,
+                                   int32_t n_free, void* table, size_t table_bytes, int32_t* n_used,
+                                   int32_t* released, int32_t released_capacity, int32_t* n_released);
+tria_status tria_pack_kv_cache_paged(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                     int32_t n_policy_heads, int64_t ctx_len, const void* k_bf16,
+                                     const void* v_bf16, const void* table, size_t table_bytes,
+                                     const void* old_table, size_t old_table_bytes, void* pool,
+                                     size_t pool_bytes, void* stream);
+tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t table_bytes, const void* pool,
+                              size_t pool_bytes, int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Dynamic block skipping in decode (device, asynchronous on `stream`).       */
 /* ------------------------------------------------------------------------- */
 /*
