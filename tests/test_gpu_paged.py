@@ -1,0 +1,138 @@
+"""GPU parity of the paged compressed cache: the pool the packer writes equals the
+oracle's (every stored record of the contiguous cache at its page), byte for byte,
+when packed fresh and while growing one token at a time across block starts with
+pages recycled; decode over the paged cache equals tria_decode over the contiguous
+cache bit for bit and the oracle's decode within tolerance."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from test_gpu_parity import assert_close, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tria():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_mixed_head_amd as t
+    return t
+
+
+def _held_pages(table: np.ndarray, P: int, rmax: int):
+    pages = table[64 + 64 * P:].view(np.int32).reshape(P, rmax)
+    return pages[pages >= 0]
+
+
+def _pool_matches(pool_gpu: torch.Tensor, pool_ref: np.ndarray, pages, page: int):
+    got = pool_gpu.cpu().numpy().reshape(-1, page)
+    ref = pool_ref.reshape(-1, page)
+    for pg in pages:
+        assert np.array_equal(got[pg], ref[pg]), f"page {pg}"
+
+
+PAGED = [
+    # (b, hq, hk, d, n, blk, ctx, hi, keep)
+    (2, 8, 2, 128, 1300, 128, 1300, [0, 2], [3, 10]),
+    (3, 7, 1, 128, 700, 64, 650, [2], [4]),
+    (1, 32, 1, 128, 512, 128, 500, [1], [2]),
+    (2, 4, 2, 64, 900, 64, 897, [1, 0], [5, 9]),
+    (1, 2, 2, 64, 64, 64, 1, [0, 0], [0, 0]),
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[f"b{c[0]}h{c[1]}k{c[2]}d{c[3]}ctx{c[6]}B{c[5]}" for c in PAGED])
+def test_paged_pack_and_decode(tria, case):
+    print(f"[case] paged {case}", flush=True)
+    b, hq, hk, d, n, blk, ctx, hi, keep = case
+    cfg = synth.Config("paged", b, hq, hk, d, n, blk, seed=71, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    page = tria.paged_page_bytes(dd)
+    P, rmax = b * hk, (ctx - 1) // blk + 1
+    n_pages = P * rmax + 7
+    free = np.random.default_rng(3).permutation(n_pages).astype(np.int32)   # scattered pages
+    table, used, _ = tria.build_paged_table(dd, hi, keep, ctx, n_pages, free)
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    kd, vd = dev(k), dev(v)
+    tdev = torch.from_numpy(table).cuda()
+    tria.pack_kv_cache_paged(dd, hi, keep, ctx, kd, vd, tdev, pool)
+    sm = 1.0 / math.sqrt(d)
+    out = tria.decode_paged(dd, tdev, pool, ctx, dev(q), sm)
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx, kd, vd)
+    plain = tria.decode(dd, cache, ctx, dev(q), sm)
+    torch.cuda.synchronize()
+    ref_pool = oracle.pack_paged(k, v, hi, keep, hq, blk, ctx, table, np.zeros(n_pages * page, np.uint8))
+    _pool_matches(pool, ref_pool, _held_pages(table, P, rmax), page)
+    assert torch.equal(out, plain)
+    assert_close(out.cpu().numpy(), oracle.decode(k, v, q, hi, keep, blk, ctx, sm), f"paged decode {case}")
+
+
+@pytest.mark.parametrize("case", [
+    (2, 8, 2, 128, 1200, 128, 250, 140, [1, 3], [4, 9]),
+    (1, 4, 4, 64, 700, 64, 1, 200, [0, 2, 5, 0], [0, 6, 5, 30]),
+], ids=["b2k2d128B128", "b1k4d64B64"])
+def test_paged_growth_token_by_token(tria, case):
+    """One token at a time: the host rebuilds the table from the previous one (pages
+    recycled through a free stack), the packer writes only what changed, and after
+    every step the held pages equal the oracle's records and decode equals the
+    contiguous decode bit for bit."""
+    b, hq, hk, d, n, blk, ctx0, steps, hi, keep = case
+    print(f"[case] paged growth {case}", flush=True)
+    cfg = synth.Config("paged-grow", b, hq, hk, d, n, blk, seed=73, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    page = tria.paged_page_bytes(dd)
+    P = b * hk
+    n_pages = P * ((ctx0 + steps - 1) // blk + 1) + 5
+    free = list(np.random.default_rng(9).permutation(n_pages).astype(np.int32))
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    kd, vd, qd = dev(k), dev(v), dev(q)
+    sm = 1.0 / math.sqrt(d)
+    old, old_dev = None, None
+    for ctx in range(ctx0, ctx0 + steps):
+        table, used, rel = tria.build_paged_table(dd, hi, keep, ctx, n_pages, np.array(free, np.int32), old)
+        free = free[used:] + list(rel)
+        tdev = torch.from_numpy(table).cuda()
+        tria.pack_kv_cache_paged(dd, hi, keep, ctx, kd, vd, tdev, pool, old_table=old_dev)
+        out = tria.decode_paged(dd, tdev, pool, ctx, qd, sm)
+        plain = tria.decode(dd, tria.pack_kv_cache(dd, hi, keep, ctx, kd, vd), ctx, qd, sm)
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain), ctx
+        c = (ctx - 1) // blk
+        if ctx == ctx0 + steps - 1 or (ctx - 1) % blk == 0:   # block starts and the last step
+            rmax = c + 1
+            ref_pool = oracle.pack_paged(k, v, hi, keep, hq, blk, ctx, table, np.zeros(n_pages * page, np.uint8))
+            _pool_matches(pool, ref_pool, _held_pages(table, P, rmax), page)
+        old, old_dev = table, tdev
+
+
+def test_paged_decode_rejects_bad_table(tria):
+    b, hq, hk, d, n, blk, ctx, hi, keep = PAGED[0]
+    cfg = synth.Config("paged", b, hq, hk, d, n, blk, seed=71, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = np.array(hi, np.int32), np.array(keep, np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    page = tria.paged_page_bytes(dd)
+    P, rmax = b * hk, (ctx - 1) // blk + 1
+    n_pages = P * rmax
+    table, _, _ = tria.build_paged_table(dd, hi, keep, ctx, n_pages, np.arange(n_pages, dtype=np.int32))
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    tdev = torch.from_numpy(table).cuda()
+    tria.pack_kv_cache_paged(dd, hi, keep, ctx, dev(k), dev(v), tdev, pool)
+    bad = table.copy()
+    bad[64 + 64 * P:64 + 64 * P + 4] = np.frombuffer(np.int32(n_pages + 3).tobytes(), np.uint8)  # page past the pool
+    o = tria.decode_paged(dd, torch.from_numpy(bad).cuda(), pool, ctx, dev(q), 0.125)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all().item()
+    bad = table.copy()
+    bad[0] = 0   # magic
+    o = tria.decode_paged(dd, torch.from_numpy(bad).cuda(), pool, ctx, dev(q), 0.125)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all().item()
