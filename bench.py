@@ -323,8 +323,44 @@ def main():
         c_out = torch.empty(tria.kv_cache_bytes(dims4, h4, kp4, s0 + 1), dtype=torch.uint8, device="cuda")
         upd_bs = event_avg(lambda: tria.update_kv_cache(dims4, h4, kp4, s0 + 1, k4d, v4d, c_blk, out=c_out),
                            args.reps)
-        del c_prev, c_blk, c_out, k4d
+        del c_prev, c_blk, c_out
         hdr = (64 + 64 * c4.batch * c4.n_kv_heads + 255) // 256 * 256
+        # the same cache in pages (page table built on the host, pool of int8-record
+        # pages): decode over it, and one more token per step as a paged update (the
+        # current block rewritten in place; at a block start only the new records)
+        pg_bytes = tria.paged_page_bytes(dims4)
+        rmax4 = (c4.seq_len - 1) // c4.block + 1
+        n_pages = c4.batch * c4.n_kv_heads * rmax4
+        free0 = np.arange(n_pages, dtype=np.int32)
+        tb, used0, _ = tria.build_paged_table(dims4, h4, kp4, c4.seq_len, n_pages, free0)
+        pool = torch.empty(n_pages * pg_bytes, dtype=torch.uint8, device="cuda")
+        tb_d = torch.from_numpy(tb).cuda()
+        tria.pack_kv_cache_paged(dims4, h4, kp4, c4.seq_len, k4d, v4d, tb_d, pool)
+        wsp = torch.empty(tria.decode_skip_workspace_bytes(dims4, c4.seq_len), dtype=torch.uint8, device="cuda")
+        run_pg = lambda: tria.decode_paged(dims4, tb_d, pool, c4.seq_len, q4, 1.0 / math.sqrt(c4.head_dim), out=o4,
+                                           workspace=wsp)
+        for _ in range(3):
+            run_pg()
+        pgd = event_avg(run_pg, args.reps, before=flush_caches)
+        # updates: token 32767 -> 32768 in place, and 32640 -> 32641 (block start)
+        t_prev, u_prev, _ = tria.build_paged_table(dims4, h4, kp4, c4.seq_len - 1, n_pages, free0)
+        tp_d = torch.from_numpy(t_prev).cuda()
+        upd_pin = event_avg(lambda: tria.pack_kv_cache_paged(dims4, h4, kp4, c4.seq_len, k4d, v4d, tb_d, pool,
+                                                             old_table=tp_d), args.reps)
+        t_s0, u_s0, _ = tria.build_paged_table(dims4, h4, kp4, s0, n_pages, free0)
+        t_s1, u_s1, rel_s1 = tria.build_paged_table(dims4, h4, kp4, s0 + 1, n_pages, free0[u_s0:], t_s0)
+        ts0_d, ts1_d = torch.from_numpy(t_s0).cuda(), torch.from_numpy(t_s1).cuda()
+        tria.pack_kv_cache_paged(dims4, h4, kp4, s0, k4d, v4d, ts0_d, pool)
+        upd_pbs = event_avg(lambda: tria.pack_kv_cache_paged(dims4, h4, kp4, s0 + 1, k4d, v4d, ts1_d, pool,
+                                                             old_table=ts0_d), args.reps)
+        paged = {"decode_us": pgd[0] * 1e6, "decode_us_p10": pgd[2] * 1e6, "page_bytes": pg_bytes,
+                 "pool_bytes": pool.numel(), "update_in_block_us": upd_pin[1] * 1e6,
+                 "update_block_start_us": upd_pbs[1] * 1e6, "new_pages_at_block_start": u_s1,
+                 "released_at_block_start": int(rel_s1.size),
+                 "note": "update = tria_pack_kv_cache_paged with the previous table (median)"}
+        log(f"[bench] paged cache: decode {pgd[0] * 1e6:.1f} us; update {upd_pin[1] * 1e6:.1f} us in a block, "
+            f"{upd_pbs[1] * 1e6:.1f} us at a block start ({u_s1} new pages)")
+        del pool, wsp, tb_d, tp_d, ts0_d, ts1_d, k4d
         # dynamic block skipping (ETA-style) on the same workload, keys with block
         # structure: the index (built once per cache block), then the skipping decode
         # (keep bits + compaction + split-KV over kept records + merge) against the
@@ -398,6 +434,7 @@ def main():
             "cache_update_us": {"in_place_within_block": upd_in[1] * 1e6, "at_block_start": upd_bs[1] * 1e6,
                                 "note": "median; tria_update_kv_cache for one more token (all 128 pairs)"},
             "skip": skip,
+            "paged": paged,
         }
         log(f"[bench] decode {dm * 1e6:.1f} us, {dec['GB_per_s']:.0f} GB/s (warm {warm * 1e6:.1f} us); "
             f"cache update {upd_in[1] * 1e6:.1f} us in place, {upd_bs[1] * 1e6:.1f} us at a block start")

@@ -93,20 +93,19 @@ __device__ __forceinline__ uint32_t pack8_nibbles(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// Record slot j of pair `pair` (the whole work group; every early return is uniform).
 template <int D, int BLK>
-__global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
+__device__ __forceinline__ void pack_record(const PackArgs& a, int pair, int j) {
   constexpr int TPR = D / 8;
   constexpr int RPP = kThreads / TPR;  // rows per pass
   __shared__ __attribute__((aligned(16))) int8_t kbuf[BLK][D];  // codes (int4: sign-extended bytes)
   __shared__ __attribute__((aligned(16))) int8_t vbuf[BLK][D];
   __shared__ float ksb[BLK], vsb[BLK];
 
-  const int pair = blockIdx.y;
   const int b = pair / a.hkv, g = pair % a.hkv;
   const int64_t ctx = a.varlen ? a.ctxs[b] : a.geo.ctx_len;
   const int c = a.varlen ? (int)((ctx - 1) / BLK) : a.geo.cur_block;
   const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
-  const int j = blockIdx.x;
   if (j >= st.n8 + st.n4) return;
   auto pair_offset = [&](const CacheGeom& geo) {
     int64_t off = geo.data_offset + (int64_t)b * geo.batch_bytes;
@@ -324,6 +323,90 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
   }
 }
 
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) pack_kernel(PackArgs a) {
+  pack_record<D, BLK>(a, blockIdx.y, blockIdx.x);
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void append_row(const PackArgs& a, uint8_t* rec, int b, int g, int64_t t, int c, int lane);
+
+// Paged update (an old table given): work group x of pair y writes the pair's new
+// records number x, x + gridDim.x, ... in record order, where a record is new unless
+// it lies before the current block and the old table maps the same (block,
+// precision) to the same page (the test pack_record repeats before writing).  When
+// both tables hold the same current block at the same page and the old one is
+// shorter, only the rows it lacks are written (work group 0, a wavefront per row).
+template <int D, int BLK>
+__global__ void __launch_bounds__(kThreads) paged_update_kernel(PackArgs a) {
+  __shared__ int tmp[2 * (kThreads / 64)];
+  __shared__ int list[kThreads];
+  const int pair = blockIdx.y, g = pair % a.hkv, tid = threadIdx.x;
+  const int P = a.batch * a.hkv, c = a.geo.cur_block, rmax = c + 1;
+  const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
+  const int32_t* th = reinterpret_cast<const int32_t*>(a.table);
+  const int32_t* oh = reinterpret_cast<const int32_t*>(a.old_table);
+  const int oc = oh[7], orm = oc + 1;
+  const bool old_ok = oh[0] == 0x50564B54 && oh[1] == 4 && oh[2] == a.batch && oh[3] == a.hkv && oh[4] == D &&
+                      oh[5] == BLK && oh[6] == orm && oc >= 0 && 64 + 64LL * P + 4LL * P * orm <= a.old_table_bytes &&
+                      64 + 64LL * P + 4LL * P * rmax <= a.table_bytes;
+  const Blocks so = stored_blocks(old_ok ? oc : 0, a.pol.hi[g], a.pol.keep[g]);
+  const int64_t octx = reinterpret_cast<const int64_t*>(a.old_table)[4];
+  const int cur_page = th[16 + 16 * P + pair * rmax + st.n8 - 1];
+  const bool same_cur = old_ok && oc == c && so.n8 == st.n8 && octx >= (int64_t)c * BLK + 1 && octx < a.geo.ctx_len &&
+                        oh[16 + 16 * P + pair * orm + so.n8 - 1] == cur_page && th[0] == 0x50564B54 &&
+                        th[1] == 4 && th[6] == rmax && th[7] == c && cur_page >= 0 && cur_page < a.pool_pages;
+  if (same_cur && blockIdx.x == 0) {
+    const int b = pair / a.hkv, wave = tid >> 6, lane = tid & 63;
+    uint8_t* rec = a.pool + (int64_t)cur_page * a.page_bytes;
+    for (int64_t t = octx + wave; t < a.geo.ctx_len; t += kThreads / 64) append_row<D, BLK>(a, rec, b, g, t, c, lane);
+  }
+  int done = 0;  // new records seen before this chunk
+  for (int j0 = 0; j0 < st.n8 + st.n4; j0 += kThreads) {
+    const int j = j0 + tid;
+    int fresh = 0;
+    if (j < st.n8 + st.n4) {
+      fresh = 1;
+      const bool is4 = j >= st.n8;
+      const int kb = !is4 ? ((st.sink && j == 0) ? 0 : st.lo8 + j - st.sink) : st.lo4 + (j - st.n8);
+      if (same_cur && kb == c) fresh = 0;  // its new rows are written above
+      if (old_ok && kb < c) {
+        int jo = -1;
+        if (!is4) {
+          if (kb == 0 && so.sink) jo = 0;
+          else if (kb >= so.lo8 && kb <= oc) jo = so.sink + kb - so.lo8;
+        } else if (kb >= so.lo4 && kb <= so.hi4) {
+          jo = so.n8 + kb - so.lo4;
+        }
+        if (jo >= 0 && oh[16 + 16 * P + pair * orm + jo] == th[16 + 16 * P + pair * rmax + j]) fresh = 0;
+      }
+    }
+    // exclusive prefix of the flags over the work group
+    const int lane = tid & 63, wave = tid >> 6;
+    int incl = fresh;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      before += w < wave ? tmp[w] : 0;
+      total += tmp[w];
+    }
+    if (fresh) list[before + incl - fresh] = j;
+    __syncthreads();
+    // this work group's share of the chunk's new records
+    for (int k = 0; k < total; ++k)
+      if ((done + k) % (int)gridDim.x == (int)blockIdx.x) pack_record<D, BLK>(a, pair, list[k]);
+    done += total;
+    __syncthreads();
+  }
+}
+
 // Variable-length batch: one work group writes the header (version 3) and every
 // pair's directory entry from the per-sequence lengths; each entry also holds its
 // sequence's ctx_len (words 10-11).  Offsets are the running sum of the pairs'
@@ -396,22 +479,14 @@ __global__ void __launch_bounds__(kThreads) varlen_directory_kernel(PackArgs a) 
 // packer); K codes go to their operand-order unit (half of a 16-byte unit), V codes
 // byte by byte to their transposed positions, then the two scales and the header's
 // ctx_len.  Rows past t are already zero in a cache packed for ctx_len - 1.
+// Token t (in current block c) of pair (b, g): its K and V rows quantised at int8 and
+// written into the block's int8 record `rec` (one wavefront, lanes 0..63).
 template <int D, int BLK>
-__global__ void __launch_bounds__(64) append_kernel(PackArgs a) {
+__device__ __forceinline__ void append_row(const PackArgs& a, uint8_t* rec, int b, int g, int64_t t, int c, int lane) {
   constexpr int TPR = D / 8, KSL = D / 64;
   constexpr int KPART = 32 * D, CBYTES = 2 * KPART + 256;
-  const int pair = blockIdx.x, lane = threadIdx.x;
-  const int b = pair / a.hkv, g = pair % a.hkv;
-  const int c = a.geo.cur_block;
-  int64_t pair_off = a.geo.data_offset + (int64_t)b * a.geo.batch_bytes;
-  for (int gg = 0; gg < g; ++gg) {
-    const Blocks o = stored_blocks(c, a.pol.hi[gg], a.pol.keep[gg]);
-    pair_off += (int64_t)o.n8 * a.geo.rec8_bytes + (int64_t)o.n4 * a.geo.rec4_bytes;
-  }
-  const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
-  const int64_t t = a.geo.ctx_len - 1;
   const int r = (int)(t - (int64_t)c * BLK), cc = r / 32, tk = r % 32;
-  uint8_t* chunk = a.cache + pair_off + (int64_t)(st.n8 - 1) * a.geo.rec8_bytes + (int64_t)cc * CBYTES;
+  uint8_t* chunk = rec + (int64_t)cc * CBYTES;
   const bool isv = lane >= TPR;
   const int part = lane % TPR;
   const int64_t src = (((int64_t)b * a.hkv + g) * a.n + t) * D + part * 8;
@@ -440,8 +515,24 @@ __global__ void __launch_bounds__(64) append_kernel(PackArgs a) {
     }
     if (part == 0) *reinterpret_cast<float*>(chunk + 2 * KPART + 4 * (32 + tk)) = s8;
   }
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(64) append_kernel(PackArgs a) {
+  const int pair = blockIdx.x, lane = threadIdx.x;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int c = a.geo.cur_block;
+  int64_t pair_off = a.geo.data_offset + (int64_t)b * a.geo.batch_bytes;
+  for (int gg = 0; gg < g; ++gg) {
+    const Blocks o = stored_blocks(c, a.pol.hi[gg], a.pol.keep[gg]);
+    pair_off += (int64_t)o.n8 * a.geo.rec8_bytes + (int64_t)o.n4 * a.geo.rec4_bytes;
+  }
+  const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
+  append_row<D, BLK>(a, a.cache + pair_off + (int64_t)(st.n8 - 1) * a.geo.rec8_bytes, b, g, a.geo.ctx_len - 1, c,
+                     lane);
   if (pair == 0 && lane == 0) reinterpret_cast<int64_t*>(a.cache)[4] = a.geo.ctx_len;
 }
+
 
 template <int D, int BLK>
 hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
@@ -453,6 +544,11 @@ hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
     hipLaunchKernelGGL((varlen_directory_kernel<D, BLK>), dim3(1), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.table && a.old_table) {  // paged update: only the new records (few per pair)
+    hipLaunchKernelGGL((paged_update_kernel<D, BLK>), dim3(max_stored < 4 ? max_stored : 4, a.batch * a.hkv),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((pack_kernel<D, BLK>), dim3(max_stored, a.batch * a.hkv), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
