@@ -293,3 +293,62 @@ def test_varlen_validation(tria):
     with pytest.raises(_lib.TriaError):
         tria.build_policy_varlen(tria.make_dims(2, 1, 1, 64, 64, 100), hi, keep, [0, 100])
 
+
+
+def test_skip_and_paged_calls_validate(tria):
+    """The skipping-decode and paged-cache entry points reject, before any HIP call,
+    NULL buffers, short buffers, bad scales and unsupported shapes (fake device
+    addresses: nothing may be enqueued)."""
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    d = tria.make_dims(2, 8, 2, 128, 128, 4096)
+    ctx = 1000
+    dev = C.c_void_p(1 << 30)
+    sz = C.c_size_t(0)
+    assert L.tria_block_summaries_bytes(C.byref(d), ctx, C.byref(sz)) == _lib.TRIA_OK
+    sums = sz.value
+    assert sums == 64 + 4 * 8 * (2 * 128 + 16)
+    assert L.tria_decode_skip_workspace_bytes(C.byref(d), ctx, C.byref(sz)) == _lib.TRIA_OK
+    ws = sz.value
+    assert ws > tria.decode_workspace_bytes(d, ctx)
+    cache = 1 << 20
+
+    def skip(cache_b=cache, sums_b=sums, q=dev, th=dev, sm=0.1, out=dev, w=dev, ws_b=ws, dims=d):
+        return L.tria_decode_skip(C.byref(dims), dev, cache_b, ctx, dev, sums_b, q, th, sm, out, w, ws_b, None)
+
+    assert skip(sums_b=sums - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert skip(ws_b=ws - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert skip(cache_b=64) == _lib.TRIA_ERR_BUFFER_TOO_SMALL           # smaller than the directory
+    assert skip(th=None) == _lib.TRIA_ERR_INVALID_ARG
+    assert skip(q=None) == _lib.TRIA_ERR_INVALID_ARG
+    assert skip(sm=0.0) == _lib.TRIA_ERR_INVALID_ARG
+    assert skip(sm=float("nan")) == _lib.TRIA_ERR_INVALID_ARG
+    assert skip(dims=tria.make_dims(1, 66, 2, 128, 128, 4096)) == _lib.TRIA_ERR_UNSUPPORTED   # G = 33
+    assert L.tria_build_block_summaries(C.byref(d), dev, cache, ctx, dev, sums - 1, None) == \
+        _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_skip_masks(C.byref(d), dev, cache, ctx, dev, sums, dev, dev, C.c_float(0.1), dev, 4 * 4 * 8 - 1,
+                             None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    # paged
+    assert L.tria_paged_table_bytes(C.byref(d), ctx, C.byref(sz)) == _lib.TRIA_OK
+    tb = sz.value
+    assert tb == 64 + 64 * 4 + 4 * 4 * 8
+    assert L.tria_paged_page_bytes(C.byref(d), C.byref(sz)) == _lib.TRIA_OK and sz.value == 2 * 128 * 128 + 8 * 128
+    page = sz.value
+    hi, keep = np.array([1, 2], np.int32), np.array([3, 5], np.int32)
+
+    def ppack(table_b=tb, pool_b=page * 64, ctx_=ctx, table=dev):
+        return L.tria_pack_kv_cache_paged(C.byref(d), hi.ctypes.data, keep.ctypes.data, 2, ctx_, dev, dev, table,
+                                          table_b, None, 0, dev, pool_b, None)
+
+    assert ppack(table_b=tb - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert ppack(pool_b=page - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert ppack(ctx_=4097) == _lib.TRIA_ERR_INVALID_ARG
+    assert ppack(table=None) == _lib.TRIA_ERR_INVALID_ARG
+
+    def pdec(table_b=tb, w_b=ws, pool=dev):
+        return L.tria_decode_paged(C.byref(d), dev, table_b, pool, page * 64, ctx, dev, C.c_float(0.1), dev, dev,
+                                   w_b, None)
+
+    assert pdec(table_b=tb - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert pdec(w_b=ws - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert pdec(pool=None) == _lib.TRIA_ERR_INVALID_ARG
