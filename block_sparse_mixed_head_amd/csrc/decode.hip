@@ -73,7 +73,7 @@ struct DecArgs {
   // entries hold pages)
   int paged;
   const uint8_t* pool;
-  int64_t page_bytes;
+  int64_t page_bytes, pool_pages;
 };
 
 struct Geo {
@@ -430,7 +430,8 @@ template <int D, int BLK, int RG, bool IS4, bool SKIP, class Pre>
 __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes, int j0, int j1,
                                           const v4i (&qop)[RG][D / 64], const float (&ar)[RG], int mask_jb,
                                           int mask_first, SegState<D, RG>& st, int lr, int kq, float* slot, Pre&& pre,
-                                          const int2* list, int64_t stride, uint32_t hfull) {
+                                          const int2* list, int64_t stride, uint32_t hfull,
+                                          const int32_t* pages = nullptr, int64_t pool_pages = 0) {
   using IO = StepIO<D, BLK, IS4>;
   constexpr int SPB = BLK / 32;
   if (j0 >= j1) return;
@@ -452,11 +453,20 @@ __device__ __forceinline__ void run_steps(const uint8_t* rec0, int64_t rec_bytes
     // windows of up to 64 kept records: lane l holds the window's entry l, read by
     // the whole wavefront with readlane (uniform index, no memory access per step).
     // The first window's entries load together with the query rows, before `pre`.
+    // (paged: the entries are the table's page ids, every head keeps every record; a
+    // page outside the pool is read as page 0 and poisons the segment's sums with NaN)
     auto window = [&](int w0, int& w1) __attribute__((always_inline)) -> int2 {
       const int r0 = uni(w0 / SPB);
       w1 = uni((r0 + 64) * SPB < j1 ? (r0 + 64) * SPB : j1);
       const int rlast = (w1 - 1) / SPB;
-      return r0 + lane <= rlast ? list[r0 + lane] : make_int2(0, 0);
+      if (!pages) return r0 + lane <= rlast ? list[r0 + lane] : make_int2(0, 0);
+      int pg = r0 + lane <= rlast ? pages[r0 + lane] : 0;
+      if (__ballot(pg < 0 || (int64_t)pg >= pool_pages)) {
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) st.l[rg] = __int_as_float(0x7FC00000);
+        pg = pg < 0 || (int64_t)pg >= pool_pages ? 0 : pg;
+      }
+      return make_int2(pg, (int)hfull);
     };
     int w1f;
     const int2 efirst = window(j0, w1f);
@@ -598,16 +608,18 @@ decode_split_kernel(DecArgs a) {
   // the directory entry of pair tid is loaded together with the header (the host
   // checked that the directory lies inside the cache): one memory round trip
   // (SKIP: the plan's pair entry, two vectors)
+  // entries from the skip plan, or (plain and paged) the cache directory / table
+  const bool from_plan = SKIP && !a.paged;
   auto entry_ptr = [&](int p) __attribute__((always_inline)) -> const v4i* {
-    return SKIP ? reinterpret_cast<const v4i*>(a.plan + 8 * (int64_t)p)
-                : reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
+    return from_plan ? reinterpret_cast<const v4i*>(a.plan + 8 * (int64_t)p)
+                     : reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
   };
   v4i ent[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
   if (tid < P) {
     const v4i* e = entry_ptr(tid);
     ent[0] = e[0];
     ent[1] = e[1];
-    if constexpr (!SKIP) ent[2] = e[2];
+    if (!from_plan) ent[2] = e[2];
   }
   auto entry = [&](int p, v4i (&x)[3]) __attribute__((always_inline)) {
     if (p == tid) {
@@ -618,7 +630,7 @@ decode_split_kernel(DecArgs a) {
       const v4i* e = entry_ptr(p);
       x[0] = e[0];
       x[1] = e[1];
-      x[2] = SKIP ? v4i{0, 0, 0, 0} : e[2];
+      x[2] = from_plan ? v4i{0, 0, 0, 0} : e[2];
     }
   };
   Geo geo;
@@ -632,7 +644,7 @@ decode_split_kernel(DecArgs a) {
   for (int p = tid; p < P; p += kThreads) {
     v4i e[3];
     entry(p, e);
-    if constexpr (SKIP) {
+    if (from_plan) {
       // {offset lo, hi, kept int8, kept int4}, {stored int8, stored int4, mask, ok}
       const int k8 = e[0][2], k4 = e[0][3], n8 = e[1][0], n4 = e[1][1], mf = e[1][2];
       const bool ok = e[1][3] == 1 && k8 >= 1 && k4 >= 0 && k8 <= n8 && k4 <= n4 && mf >= 1 && mf <= BLK;
@@ -723,16 +735,19 @@ decode_split_kernel(DecArgs a) {
     // SKIP: the pair's records start at its (validated) offset; n8s, n4s records stored
     int n8s = n8;
     const int2* list = nullptr;
+    const int32_t* pages = nullptr;
     const uint8_t* rec4 = nullptr;
     int64_t stride8 = geo.rec8, stride4 = geo.rec4;
     if constexpr (SKIP) {
-      const int* pe = a.plan + 8 * (int64_t)p;
-      rec0 = a.cache + (int64_t)(((uint64_t)(uint32_t)pe[1] << 32) | (uint32_t)pe[0]);
-      n8s = uni(pe[4]);
-      list = reinterpret_cast<const int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
-      if (a.paged) {  // list entries are pages of the pool
+      if (a.paged) {  // the table's page ids, records in the pool
         rec0 = a.pool;
         stride8 = stride4 = a.page_bytes;
+        pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * a.rmax;
+      } else {
+        const int* pe = a.plan + 8 * (int64_t)p;
+        rec0 = a.cache + (int64_t)(((uint64_t)(uint32_t)pe[1] << 32) | (uint32_t)pe[0]);
+        n8s = uni(pe[4]);
+        list = reinterpret_cast<const int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
       }
     }
     rec4 = SKIP && a.paged ? rec0 : rec0 + (int64_t)n8s * geo.rec8;
@@ -800,12 +815,13 @@ decode_split_kernel(DecArgs a) {
     const int mask_first = uni(mfp[p]);
     const bool has8 = j8a < j8b;
     run_steps<D, BLK, RG, false, SKIP>(rec0, geo.rec8, j8a, j8b, q8op, a8, n8 - 1, mask_first, st, lr, kq,
-                                       scl[wave], quantise_q, list, stride8, hfull);
+                                       scl[wave], quantise_q, list, stride8, hfull, pages, a.pool_pages);
     run_steps<D, BLK, RG, true, SKIP>(rec4, geo.rec4, j4a, j4b, q4op, a4, -1, 0, st, lr, kq, scl[wave],
                                       [&]() __attribute__((always_inline)) {
                                         if (!has8) quantise_q();
                                       },
-                                      SKIP ? list + n8s : nullptr, stride4, hfull);
+                                      SKIP && list ? list + n8s : nullptr, stride4, hfull, pages ? pages + n8s : nullptr,
+                                      a.pool_pages);
 
     // ---- the wavefront's partial for this pair
 #pragma unroll
@@ -1265,55 +1281,6 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
 }
 #pragma clang fp contract(on)
 
-// Plan of a paged cache (every record kept): one work group per pair checks the
-// table header and the pair's entry (the decode's rules) and that every page lies
-// inside the pool, then lists the pair's records {page, all heads} (int8 run from
-// entry 0, int4 run from entry n8) and writes the pair entry as the skip plan does.
-template <int D, int BLK>
-__global__ void __launch_bounds__(kThreads) paged_plan_kernel(DecArgs a, int64_t pool_pages) {
-  const int tid = threadIdx.x, p = blockIdx.x;
-  const int P = a.batch * a.hkv, G = a.hq / a.hkv;
-  __shared__ int bad;
-  const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
-  const v4i* ep = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
-  const v4i e0 = ep[0], e1 = ep[1], e2 = ep[2];
-  Geo geo;
-  const int rmax = (int)((a.ctx_len - 1) / BLK) + 1;
-  const int32_t* pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * rmax;
-  int pg0 = tid < rmax ? pages[tid] : 0;  // the first 256 pages with the headers
-  const int n8 = e0[2], n4 = e0[3], lo8 = e1[2], sink = e1[3], lo4 = e2[0];
-  bool ok = paged_header_h<D, BLK>(a, h, geo);
-  const int cur = geo.cur;
-  ok = ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
-       lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
-       a.rmax == rmax;
-  int* pe = const_cast<int*>(a.plan) + 8 * (int64_t)p;
-  if (!ok) {
-    if (tid < 8) pe[tid] = 0;
-    return;
-  }
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  int2* list = reinterpret_cast<int2*>(const_cast<int*>(a.plan) + 8 * (int64_t)P) + (int64_t)p * a.rmax;
-  const int gm = G >= 32 ? -1 : (int)((1u << G) - 1u);
-  for (int r = tid; r < n8 + n4; r += kThreads) {
-    const int pg = r < kThreads ? pg0 : pages[r];
-    if (pg < 0 || (int64_t)pg >= pool_pages) bad = 1;
-    list[r] = make_int2(pg, gm);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    pe[0] = 0;
-    pe[1] = 0;
-    pe[2] = n8;
-    pe[3] = n4;
-    pe[4] = n8;
-    pe[5] = n4;
-    pe[6] = (int)(a.ctx_len - (int64_t)cur * BLK);
-    pe[7] = bad ? 0 : 1;
-  }
-}
-
 // Work groups of the split kernel: kGrid, or fewer when TRIA_DECODE_GRID (1..kGrid) is
 // set -- a testing and tuning knob: fewer wavefronts give each one longer segments.
 int split_grid() {
@@ -1365,7 +1332,7 @@ hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int
   a.rmax = 0;
   a.paged = 0;
   a.pool = nullptr;
-  a.page_bytes = 0;
+  a.page_bytes = a.pool_pages = 0;
   const int G = s.hq / s.hkv;
   const bool two = G > 16;
   if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2>(a, stream) : launch_t<128, 128, 1>(a, stream);
@@ -1420,8 +1387,6 @@ hipError_t launch_skip_t(const SkipArgs& sa, const DecArgs& da, bool two, hipStr
 hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* table, int64_t table_bytes,
                                const void* pool, int64_t pool_bytes, const void* q, float sm_scale, float* out,
                                void* workspace, hipStream_t stream) {
-  const int64_t pairs = (int64_t)s.batch * s.hkv;
-  const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
   DecArgs da;
   da.cache = static_cast<const uint8_t*>(table);
   da.q = static_cast<const uint16_t*>(q);
@@ -1434,34 +1399,17 @@ hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* tabl
   da.hkv = s.hkv;
   da.c = sm_scale * 1.44269504088896340736f;
   da.varlen = 0;
-  da.plan = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + base);
+  da.plan = nullptr;
   da.rmax = (int)((ctx_len - 1) / s.blk + 1);
   da.paged = 1;
   da.pool = static_cast<const uint8_t*>(pool);
   da.page_bytes = 2LL * s.blk * s.d + 8LL * s.blk;
-  const int64_t pool_pages = pool_bytes / da.page_bytes;
+  da.pool_pages = pool_bytes / da.page_bytes;
   const bool two = s.hq / s.hkv > 16;
-  auto run = [&](auto plan_kernel, auto split1, auto split2, auto merge, int D) -> hipError_t {
-    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)pairs), dim3(kThreads), 0, stream, da, pool_pages);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(two ? split2 : split1, dim3(split_grid()), dim3(kThreads), 0, stream, da);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(merge, dim3(s.batch * s.hq), dim3(D), 0, stream, da);
-    return hipGetLastError();
-  };
-  if (s.d == 128 && s.blk == 128)
-    return run(paged_plan_kernel<128, 128>, decode_split_kernel<128, 128, 1, true>,
-               decode_split_kernel<128, 128, 2, true>, decode_merge_kernel<128>, 128);
-  if (s.d == 128)
-    return run(paged_plan_kernel<128, 64>, decode_split_kernel<128, 64, 1, true>, decode_split_kernel<128, 64, 2, true>,
-               decode_merge_kernel<128>, 128);
-  if (s.blk == 128)
-    return run(paged_plan_kernel<64, 128>, decode_split_kernel<64, 128, 1, true>, decode_split_kernel<64, 128, 2, true>,
-               decode_merge_kernel<64>, 64);
-  return run(paged_plan_kernel<64, 64>, decode_split_kernel<64, 64, 1, true>, decode_split_kernel<64, 64, 2, true>,
-             decode_merge_kernel<64>, 64);
+  if (s.d == 128 && s.blk == 128) return two ? launch_t<128, 128, 2, true>(da, stream) : launch_t<128, 128, 1, true>(da, stream);
+  if (s.d == 128) return two ? launch_t<128, 64, 2, true>(da, stream) : launch_t<128, 64, 1, true>(da, stream);
+  if (s.blk == 128) return two ? launch_t<64, 128, 2, true>(da, stream) : launch_t<64, 128, 1, true>(da, stream);
+  return two ? launch_t<64, 64, 2, true>(da, stream) : launch_t<64, 64, 1, true>(da, stream);
 }
 
 hipError_t launch_summaries(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
@@ -1512,7 +1460,7 @@ hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache
   da.rmax = sa.rmax;
   da.paged = 0;
   da.pool = nullptr;
-  da.page_bytes = 0;
+  da.page_bytes = da.pool_pages = 0;
   const bool two = s.hq / s.hkv > 16;
   if (s.d == 128 && s.blk == 128) return launch_skip_t<128, 128>(sa, da, two, stream);
   if (s.d == 128) return launch_skip_t<128, 64>(sa, da, two, stream);

@@ -386,10 +386,13 @@ tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t 
  *   within a block rewrites one record per pair and a block start writes the new
  *   ones.  A table whose header does not match the call, or a page outside the pool,
  *   writes nothing.
- * tria_decode_paged: tria_decode over a paged cache (the kernels of tria_decode_skip
- *   with every record kept; the workspace of tria_decode_skip_workspace_bytes).  A
- *   table that does not validate writes NaN to `out` and reads no record.  Results
- *   equal tria_decode on the contiguous cache with the same content. */
+ * tria_decode_paged: tria_decode over a paged cache: the split kernel reads the table's
+ *   directory entries (checked as tria_decode checks its directory) and each record's
+ *   page from the table (the workspace of tria_decode_skip_workspace_bytes).  A table
+ *   whose header or entries do not validate writes NaN to `out` and reads no record;
+ *   a page outside the pool makes the query heads of its (batch, KV head) NaN.
+ *   Results equal tria_decode on the contiguous cache with the same content, bit for
+ *   bit. */
 tria_status tria_paged_page_bytes(const tria_dims* dims, size_t* bytes);
 tria_status tria_paged_table_bytes(const tria_dims* dims, int64_t ctx_len, size_t* bytes);
 tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
