@@ -75,7 +75,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "skip", "copy", "step"], default=None)
+    p.add_argument("--only", choices=["prefill", "decode", "skip", "paged", "copy", "step"], default=None)
     p.add_argument("--reps", type=int, default=20)
     return p.parse_args()
 
@@ -269,7 +269,7 @@ def main():
 
     # ------------------------------------------------------------ decode workload (b16, ctx 32768)
     dec = None
-    if args.only in (None, "decode", "skip"):
+    if args.only in (None, "decode", "skip", "paged"):
         c4 = synth.CONFIGS[4]
         log(f"[bench] generating {c4.name}")
         k4h, v4h, q4h = synth.make_decode_inputs(c4)
@@ -301,6 +301,18 @@ def main():
             for _ in range(args.steps):
                 flush_caches()
                 tria.decode_skip(dims4, cs, c4.seq_len, sm_, q4, th_, 1.0 / math.sqrt(c4.head_dim), out=o4)
+            torch.cuda.synchronize()
+            print("done", flush=True)
+            return
+        if args.only == "paged":     # profiler run: the cache in pages, paged decodes
+            n_pg = c4.batch * c4.n_kv_heads * ((c4.seq_len - 1) // c4.block + 1)
+            tb_, _, _ = tria.build_paged_table(dims4, h4, kp4, c4.seq_len, n_pg, np.arange(n_pg, dtype=np.int32))
+            tb_d_ = torch.from_numpy(tb_).cuda()
+            pool_ = torch.empty(n_pg * tria.paged_page_bytes(dims4), dtype=torch.uint8, device="cuda")
+            tria.pack_kv_cache_paged(dims4, h4, kp4, c4.seq_len, k4d, v4d, tb_d_, pool_)
+            for _ in range(args.steps):
+                flush_caches()
+                tria.decode_paged(dims4, tb_d_, pool_, c4.seq_len, q4, 1.0 / math.sqrt(c4.head_dim), out=o4)
             torch.cuda.synchronize()
             print("done", flush=True)
             return
