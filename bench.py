@@ -251,9 +251,48 @@ def main():
 
     if args.only in (None, "step"):
         log(f"[bench] step: warmup {args.warmup}, timed {args.steps}")
-        sec = timed_loop(step, args.warmup, args.steps)
+        sec_eager = timed_loop(step, args.warmup, args.steps)
+        log(f"[bench] step (eager launches) {sec_eager * 1e3:.3f} ms")
+        # The same step with its device work (schedule upload, quantise, prefill, pack,
+        # decode) launched as one HIP graph per pinned schedule buffer: the host still
+        # expands the policy into the buffer every step.  Replays are checked against
+        # the eager step (bit for bit, eager work in between) before timing.
+        ref = (out.clone(), dout.clone(), cache.clone())
+        graphs = []
+        for slot in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                sched_dev.copy_(pinned[slot], non_blocking=True)
+                tria.quantize_qk(dims, q, k, out=qz)
+                tria.prefill(dims, sched_dev, qz, v, sm, out=out)
+                tria.pack_kv_cache(dims, hi, keep, ctx, k, v, cache=cache)
+                tria.decode(dims, cache, ctx, qdec, sm, out=dout, workspace=ws)
+            graphs.append(g)
+
+        def gstep(i: int):
+            buf = pinned[i % 2]
+            pinned_ev[i % 2].synchronize()
+            tria.check(tria._lib.lib.tria_build_policy(C.byref(dims), hi_c.ctypes.data, keep_c.ctypes.data, hq,
+                                                       C.c_void_p(buf.data_ptr()), sched_bytes, C.byref(need)))
+            graphs[i % 2].replay()
+            pinned_ev[i % 2].record(stream)
+
+        for i in range(4):
+            out.zero_()
+            dout.zero_()
+            step(i)            # eager work between the replays
+            torch.cuda.synchronize()
+            out.zero_()
+            dout.zero_()
+            gstep(i)
+            torch.cuda.synchronize()
+            if not (torch.equal(out, ref[0]) and torch.equal(dout, ref[1]) and torch.equal(cache, ref[2])):
+                raise SystemExit("graph replay differs from the eager step")
+        del ref
+        sec_graph = timed_loop(gstep, args.warmup, args.steps)
+        sec = sec_graph
         value = b * n / sec
-        log(f"[bench] step {sec * 1e3:.3f} ms -> {value:.4g} tokens/s")
+        log(f"[bench] step (graph launches) {sec * 1e3:.3f} ms -> {value:.4g} tokens/s")
 
         # per-kernel device times (events on the launch stream)
         p_mean, p_med, p_p10, p_p90 = event_avg(lambda: tria.prefill(dims, sched_dev, qz, v, sm, out=out), args.reps)
@@ -518,6 +557,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": sec * 1e3,
+        "ms_per_step_eager_launches": sec_eager * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
