@@ -141,3 +141,30 @@ def test_paged_decode_rejects_bad_table(tria):
     o = tria.decode_paged(dd, torch.from_numpy(bad).cuda(), pool, ctx, dev(q), 0.125)
     torch.cuda.synchronize()
     assert torch.isnan(o).all().item()
+
+
+def test_paged_full_size(tria):
+    """The decode workload (b16, 32/8 heads, d128, ctx 32768, block 128) in pages handed
+    out in a scattered order: every held page equals the oracle's record byte for byte,
+    and the paged decode equals the contiguous decode bit for bit."""
+    cfg = synth.CONFIGS[4]
+    print("[case] paged full-size decode workload", flush=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = cfg.policy()
+    dd = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
+    ctx, page = cfg.seq_len, tria.paged_page_bytes(dd)
+    P, rmax = cfg.batch * cfg.n_kv_heads, (ctx - 1) // cfg.block + 1
+    n_pages = P * rmax
+    free = np.random.default_rng(11).permutation(n_pages).astype(np.int32)
+    table, used, _ = tria.build_paged_table(dd, hi, keep, ctx, n_pages, free)
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    kd, vd = dev(k), dev(v)
+    tdev = torch.from_numpy(table).cuda()
+    tria.pack_kv_cache_paged(dd, hi, keep, ctx, kd, vd, tdev, pool)
+    sm = 1.0 / math.sqrt(cfg.head_dim)
+    out = tria.decode_paged(dd, tdev, pool, ctx, dev(q), sm)
+    plain = tria.decode(dd, tria.pack_kv_cache(dd, hi, keep, ctx, kd, vd), ctx, dev(q), sm)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain)
+    ref_pool = oracle.pack_paged(k, v, hi, keep, cfg.n_q_heads, cfg.block, ctx, table, np.zeros(n_pages * page, np.uint8))
+    _pool_matches(pool, ref_pool, _held_pages(table, P, rmax), page)
