@@ -26,7 +26,7 @@ __all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "prefil
            "kv_cache_bytes_varlen", "pack_kv_cache_varlen", "decode_varlen",
            "check_cache", "decode_workspace_bytes", "decode", "block_summaries_bytes", "build_block_summaries",
            "skip_masks", "decode_skip_workspace_bytes", "decode_skip", "paged_page_bytes", "paged_table_bytes",
-           "build_paged_table", "pack_kv_cache_paged", "decode_paged", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
+           "build_paged_table", "pack_kv_cache_paged", "decode_paged", "decode_paged_varlen", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
 Dims = _lib.Dims
@@ -272,32 +272,46 @@ def paged_table_bytes(d: Dims, ctx_len: int) -> int:
     return out.value
 
 
-def build_paged_table(d: Dims, hi, keep, ctx_len: int, n_pages: int, free_pages,
+def build_paged_table(d: Dims, hi, keep, ctx_len, n_pages: int, free_pages,
                       old_table: Optional[np.ndarray] = None):
-    """Host page table (uint8) for ctx_len; returns (table, pages taken from the front of
-    free_pages, released pages)."""
+    """Host page table (uint8); returns (table, pages taken from the front of free_pages,
+    released pages).  ctx_len: one length, or one per batch element (a variable-length
+    table, tria_build_paged_table_varlen)."""
     hi, keep = _i32(hi), _i32(keep)
     fp = _i32(free_pages)
-    table = np.zeros(paged_table_bytes(d, ctx_len), np.uint8)
+    lens = None if np.isscalar(ctx_len) else np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int64))
+    table = np.zeros(paged_table_bytes(d, int(ctx_len) if lens is None else int(lens.max())), np.uint8)
     ot = None if old_table is None else np.ascontiguousarray(old_table, dtype=np.uint8)
     cap = 1 << 20 if ot is None else max(1, ot.size // 4)
     rel = np.zeros(cap, np.int32)
     used, nrel = C.c_int32(0), C.c_int32(0)
-    check(_lib.lib.tria_build_paged_table(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, n_pages,
-                                          None if ot is None else ot.ctypes.data, 0 if ot is None else ot.size,
-                                          fp.ctypes.data if fp.size else None, fp.size, table.ctypes.data,
-                                          table.size, C.byref(used), rel.ctypes.data, cap, C.byref(nrel)))
+    common = (None if ot is None else ot.ctypes.data, 0 if ot is None else ot.size,
+              fp.ctypes.data if fp.size else None, fp.size, table.ctypes.data, table.size, C.byref(used),
+              rel.ctypes.data, cap, C.byref(nrel))
+    if lens is None:
+        check(_lib.lib.tria_build_paged_table(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, n_pages,
+                                              *common))
+    else:
+        check(_lib.lib.tria_build_paged_table_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi),
+                                                     lens.ctypes.data, n_pages, *common))
     return table, used.value, rel[:nrel.value].copy()
 
 
-def pack_kv_cache_paged(d: Dims, hi, keep, ctx_len: int, k: torch.Tensor, v: torch.Tensor, table: torch.Tensor,
+def pack_kv_cache_paged(d: Dims, hi, keep, ctx_len, k: torch.Tensor, v: torch.Tensor, table: torch.Tensor,
                         pool: torch.Tensor, old_table: Optional[torch.Tensor] = None) -> None:
-    """Writes the records of `table` (device copy of build_paged_table's result) into pool."""
+    """Writes the records of `table` (device copy of build_paged_table's result) into pool.
+    ctx_len: one length, or one per batch element (variable-length table)."""
     hi, keep = _i32(hi), _i32(keep)
-    check(_lib.lib.tria_pack_kv_cache_paged(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, _ptr(k),
-                                            _ptr(v), _ptr(table), table.numel(), _ptr(old_table),
-                                            0 if old_table is None else old_table.numel(), _ptr(pool), pool.numel(),
-                                            _stream(pool.device)))
+    ot = (_ptr(old_table), 0 if old_table is None else old_table.numel())
+    if np.isscalar(ctx_len):
+        check(_lib.lib.tria_pack_kv_cache_paged(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len,
+                                                _ptr(k), _ptr(v), _ptr(table), table.numel(), *ot, _ptr(pool),
+                                                pool.numel(), _stream(pool.device)))
+    else:
+        lens = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int64))
+        check(_lib.lib.tria_pack_kv_cache_paged_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi),
+                                                       lens.ctypes.data, _ptr(k), _ptr(v), _ptr(table), table.numel(),
+                                                       *ot, _ptr(pool), pool.numel(), _stream(pool.device)))
 
 
 def decode_paged(d: Dims, table: torch.Tensor, pool: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale: float,
@@ -311,6 +325,21 @@ def decode_paged(d: Dims, table: torch.Tensor, pool: torch.Tensor, ctx_len: int,
     check(_lib.lib.tria_decode_paged(C.byref(d), _ptr(table), table.numel(), _ptr(pool), pool.numel(), ctx_len,
                                      _ptr(q), float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(),
                                      _stream(q.device)))
+    return out
+
+
+def decode_paged_varlen(d: Dims, table: torch.Tensor, pool: torch.Tensor, q: torch.Tensor, sm_scale: float,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode over a variable-length paged cache: each sequence at its own length."""
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_skip_workspace_bytes(d, d.seq_len), dtype=torch.uint8, device=q.device)
+    check(_lib.lib.tria_decode_paged_varlen(C.byref(d), _ptr(table), table.numel(), _ptr(pool), pool.numel(),
+                                            _ptr(q), float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                            _stream(q.device)))
     return out
 
 

@@ -649,19 +649,31 @@ tria_status tria_paged_table_bytes(const tria_dims* dims, int64_t ctx_len, size_
   return ok();
 }
 
-tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
-                                   int32_t n_policy_heads, int64_t ctx_len, int64_t n_pages, const void* old_table,
-                                   size_t old_table_bytes, const int32_t* free_pages, int32_t n_free, void* table,
-                                   size_t table_bytes, int32_t* n_used, int32_t* released, int32_t released_capacity,
-                                   int32_t* n_released) {
+// The page table for per-pair current blocks (fixed length: one ctx_len; varlen: each
+// batch element's ctx_lens[b], header word 7 = -1 and each entry's words 10-11 = its
+// ctx_len).  A pair whose length is below the old table's starts afresh (all its old
+// pages released): its slot holds a new sequence.
+static tria_status build_paged(const tria_dims* dims, const int32_t* hi, const int32_t* keep, int32_t n_policy_heads,
+                               const int64_t* ctx_lens, int64_t ctx_len, int64_t n_pages, const void* old_table,
+                               size_t old_table_bytes, const int32_t* free_pages, int32_t n_free, void* table,
+                               size_t table_bytes, int32_t* n_used, int32_t* released, int32_t released_capacity,
+                               int32_t* n_released) {
   tria_status st = check_dims(dims);
   if (st != TRIA_OK) return st;
   NONNULL(table);
   NONNULL(n_used);
   NONNULL(n_released);
-  if (ctx_len < 1 || ctx_len > dims->seq_len)
-    return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld outside [1, seq_len=%lld]", (long long)ctx_len,
-                (long long)dims->seq_len);
+  const bool varlen = ctx_lens != nullptr;
+  const int64_t P = (int64_t)dims->batch * dims->n_kv_heads;
+  std::vector<int64_t> ctx_b(dims->batch);
+  int64_t cmax = 0;
+  for (int b = 0; b < dims->batch; ++b) {
+    ctx_b[b] = varlen ? ctx_lens[b] : ctx_len;
+    if (ctx_b[b] < 1 || ctx_b[b] > dims->seq_len)
+      return fail(TRIA_ERR_INVALID_ARG, "ctx_len %lld (batch element %d) outside [1, seq_len=%lld]",
+                  (long long)ctx_b[b], b, (long long)dims->seq_len);
+    cmax = std::max(cmax, (ctx_b[b] - 1) / dims->block);
+  }
   if (n_pages < 1 || n_pages > INT32_MAX) return fail(TRIA_ERR_INVALID_ARG, "n_pages must be in [1, 2^31 - 1]");
   if (n_free < 0 || (n_free > 0 && !free_pages)) return fail(TRIA_ERR_INVALID_ARG, "free_pages is NULL");
   if (released_capacity < 0 || (released_capacity > 0 && !released))
@@ -669,14 +681,13 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
   tria::KvPolicy pol;
   st = kv_policy(dims, hi, keep, n_policy_heads, pol);
   if (st != TRIA_OK) return st;
-  const int64_t need = paged_table_bytes_of(dims, ctx_len);
+  const int64_t rmax = cmax + 1;
+  const int64_t need = 64 + 64 * P + 4 * P * rmax;
   if ((int64_t)table_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "table needs %lld bytes, got %zu", (long long)need, table_bytes);
-  const int64_t P = (int64_t)dims->batch * dims->n_kv_heads;
-  const int64_t c = (ctx_len - 1) / dims->block, rmax = c + 1;
-  // the old table: same shape and policy, pages inside the pool, each page once
+  // the old table: same kind, shape, policy and pool; pages inside the pool, each once
   std::vector<uint8_t> used(static_cast<size_t>(n_pages), 0);
-  int64_t orm = 0, oc = 0;
+  int64_t orm = 0, oc_all = 0, octx_all = 0;
   const uint8_t* ot = static_cast<const uint8_t*>(old_table);
   if (ot) {
     if (old_table_bytes < 64) return fail(TRIA_ERR_INVALID_ARG, "old table smaller than its header");
@@ -685,11 +696,13 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
     std::memcpy(h, ot, 32);
     std::memcpy(h64, ot + 32, 32);
     orm = h[6];
-    oc = h[7];
+    oc_all = h[7];
+    octx_all = h64[0];
+    const bool okind = varlen ? (h[7] == -1 && h64[0] == 0 && orm >= 1)
+                              : (orm == oc_all + 1 && oc_all >= 0 && octx_all >= 1 && (octx_all - 1) / dims->block == oc_all);
     if (h[0] != kPagedMagic || h[1] != 4 || h[2] != dims->batch || h[3] != dims->n_kv_heads ||
-        h[4] != dims->head_dim || h[5] != dims->block || orm != oc + 1 || oc < 0 || h64[0] < 1 ||
-        (h64[0] - 1) / dims->block != oc || h64[2] != n_pages)
-      return fail(TRIA_ERR_INVALID_ARG, "old table header does not match (dims, n_pages)");
+        h[4] != dims->head_dim || h[5] != dims->block || !okind || h64[2] != n_pages)
+      return fail(TRIA_ERR_INVALID_ARG, "old table header does not match (kind, dims, n_pages)");
     if ((int64_t)old_table_bytes < 64 + 64 * P + 4 * P * orm)
       return fail(TRIA_ERR_INVALID_ARG, "old table smaller than its size");
   }
@@ -699,14 +712,20 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
   std::vector<std::pair<int64_t, int>> nb, ob;
   for (int64_t p = 0; p < P; ++p) {
     const int g = (int)(p % dims->n_kv_heads);
+    const int64_t ctx = ctx_b[p / dims->n_kv_heads], c = (ctx - 1) / dims->block;
     record_blocks(c, pol.hi[g], pol.keep[g], nb);
     std::vector<int32_t> opages;
+    bool fresh = false;
     if (ot) {
       int32_t e[16];
       std::memcpy(e, ot + 64 + 64 * p, 64);
+      int64_t octx = octx_all;
+      if (varlen) std::memcpy(&octx, ot + 64 + 64 * p + 40, 8);
+      if (octx < 1 || (octx - 1) / dims->block >= orm)
+        return fail(TRIA_ERR_INVALID_ARG, "old table entry %lld corrupt", (long long)p);
       if (e[4] != pol.hi[g] || e[5] != pol.keep[g])
         return fail(TRIA_ERR_INVALID_ARG, "old table entry %lld holds another policy", (long long)p);
-      record_blocks(oc, pol.hi[g], pol.keep[g], ob);
+      record_blocks((octx - 1) / dims->block, pol.hi[g], pol.keep[g], ob);
       if (e[2] + e[3] != (int64_t)ob.size()) return fail(TRIA_ERR_INVALID_ARG, "old table entry %lld corrupt", (long long)p);
       opages.resize(ob.size());
       std::memcpy(opages.data(), ot + 64 + 64 * P + 4 * (p * orm), 4 * ob.size());
@@ -714,13 +733,16 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
         if (pg < 0 || pg >= n_pages || used[pg]) return fail(TRIA_ERR_INVALID_ARG, "old table page %d invalid", pg);
         used[pg] = 1;
       }
+      fresh = ctx < octx;  // a shorter sequence is a new one
+    } else {
+      ob.clear();
     }
     int32_t* pages = reinterpret_cast<int32_t*>(out.data() + 64 + 64 * P + 4 * (p * rmax));
     for (int64_t r = 0; r < rmax; ++r) pages[r] = -1;
     std::vector<char> kept(opages.size(), 0);
     for (size_t r = 0; r < nb.size(); ++r) {
       int32_t pg = -1;
-      for (size_t o = 0; o < ob.size() && ot; ++o)
+      for (size_t o = 0; o < ob.size() && ot && !fresh; ++o)
         if (ob[o] == nb[r]) {
           pg = opages[o];
           kept[o] = 1;
@@ -746,6 +768,7 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
     e[7] = lo8 > 0 ? 1 : 0;
     e[8] = e[3] > 0 ? (int32_t)std::max<int64_t>(1, c - pol.keep[g]) : 0;
     e[9] = e[3] > 0 ? (int32_t)(c - pol.hi[g] - 1) : -1;
+    if (varlen) std::memcpy(&e[10], &ctx, 8);
     std::memcpy(out.data() + 64 + 64 * p, e, 64);
   }
   *n_used = (int32_t)std::min<int64_t>(taken, INT32_MAX);
@@ -754,22 +777,44 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "%lld free pages needed, %d given", (long long)taken, n_free);
   if ((int64_t)rel.size() > released_capacity)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "%zu released pages, capacity %d", rel.size(), released_capacity);
-  // the free pages taken: inside the pool and not held by a kept record or twice
+  // the free pages taken: inside the pool and not held by the old table or given twice
+  // (a page this update releases is still held: it can be reused from the next call on)
   for (int64_t i = 0; i < taken; ++i) {
     const int32_t pg = free_pages[i];
     if (pg < 0 || pg >= n_pages) return fail(TRIA_ERR_INVALID_ARG, "free page %d outside the pool", pg);
     if (used[pg] == 2) return fail(TRIA_ERR_INVALID_ARG, "free page %d given twice", pg);
-    // (a page this update releases is still held: it can be reused from the next call on)
     if (used[pg] == 1) return fail(TRIA_ERR_INVALID_ARG, "free page %d is held by the old table", pg);
     used[pg] = 2;
   }
-  int32_t h[8] = {kPagedMagic, 4, dims->batch, dims->n_kv_heads, dims->head_dim, dims->block, (int32_t)rmax, (int32_t)c};
-  int64_t h64[4] = {ctx_len, 2LL * dims->block * dims->head_dim + 8LL * dims->block, n_pages, 0};
+  const int32_t c7 = varlen ? -1 : (int32_t)cmax;
+  int32_t h[8] = {kPagedMagic, 4, dims->batch, dims->n_kv_heads, dims->head_dim, dims->block, (int32_t)rmax, c7};
+  int64_t h64[4] = {varlen ? 0 : ctx_len, 2LL * dims->block * dims->head_dim + 8LL * dims->block, n_pages, 0};
   std::memcpy(out.data(), h, 32);
   std::memcpy(out.data() + 32, h64, 32);
   std::memcpy(table, out.data(), out.size());
   if (!rel.empty()) std::memcpy(released, rel.data(), 4 * rel.size());
   return ok();
+}
+
+tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                   int32_t n_policy_heads, int64_t ctx_len, int64_t n_pages, const void* old_table,
+                                   size_t old_table_bytes, const int32_t* free_pages, int32_t n_free, void* table,
+                                   size_t table_bytes, int32_t* n_used, int32_t* released, int32_t released_capacity,
+                                   int32_t* n_released) {
+  return build_paged(dims, hi, keep, n_policy_heads, nullptr, ctx_len, n_pages, old_table, old_table_bytes,
+                     free_pages, n_free, table, table_bytes, n_used, released, released_capacity, n_released);
+}
+
+tria_status tria_build_paged_table_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                          int32_t n_policy_heads, const int64_t* ctx_lens, int64_t n_pages,
+                                          const void* old_table, size_t old_table_bytes, const int32_t* free_pages,
+                                          int32_t n_free, void* table, size_t table_bytes, int32_t* n_used,
+                                          int32_t* released, int32_t released_capacity, int32_t* n_released) {
+  if (!ctx_lens) return fail(TRIA_ERR_INVALID_ARG, "ctx_lens is NULL");
+  if (dims && dims->batch > tria::kMaxVarlenBatch)
+    return fail(TRIA_ERR_UNSUPPORTED, "batch above %d for a variable-length cache", tria::kMaxVarlenBatch);
+  return build_paged(dims, hi, keep, n_policy_heads, ctx_lens, 0, n_pages, old_table, old_table_bytes, free_pages,
+                     n_free, table, table_bytes, n_used, released, released_capacity, n_released);
 }
 
 // ------------------------------------------------------------------ (f4) dynamic block skipping
@@ -913,8 +958,64 @@ tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t t
   if ((int64_t)ws_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
   return launched(tria::launch_decode_paged(s, ctx_len, table, (int64_t)table_bytes, pool, (int64_t)pool_bytes,
-                                            q_bf16, sm_scale, out, workspace, static_cast<hipStream_t>(stream)),
+                                            q_bf16, sm_scale, out, workspace, false, static_cast<hipStream_t>(stream)),
                   "paged decode launch");
+}
+
+tria_status tria_pack_kv_cache_paged_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                            int32_t n_policy_heads, const int64_t* ctx_lens, const void* k_bf16,
+                                            const void* v_bf16, const void* table, size_t table_bytes,
+                                            const void* old_table, size_t old_table_bytes, void* pool,
+                                            size_t pool_bytes, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(ctx_lens);
+  NONNULL(k_bf16);
+  NONNULL(v_bf16);
+  NONNULL(table);
+  NONNULL(pool);
+  if (dims->batch > tria::kMaxVarlenBatch)
+    return fail(TRIA_ERR_UNSUPPORTED, "batch above %d for a variable-length cache", tria::kMaxVarlenBatch);
+  int64_t cmax = 1;
+  for (int b = 0; b < dims->batch; ++b) {
+    if (ctx_lens[b] < 1 || ctx_lens[b] > dims->seq_len)
+      return fail(TRIA_ERR_INVALID_ARG, "ctx_lens[%d] = %lld outside [1, seq_len=%lld]", b, (long long)ctx_lens[b],
+                  (long long)dims->seq_len);
+    cmax = std::max(cmax, ctx_lens[b]);
+  }
+  tria::KvPolicy pol;
+  st = kv_policy(dims, hi, keep, n_policy_heads, pol);
+  if (st != TRIA_OK) return st;
+  if ((int64_t)table_bytes < paged_table_bytes_of(dims, cmax))
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "table smaller than tria_paged_table_bytes(longest ctx_len)");
+  if (old_table && old_table_bytes < 64) return fail(TRIA_ERR_INVALID_ARG, "old table smaller than its header");
+  const tria::CacheGeom g = cache_geom(dims, pol, cmax);
+  if ((int64_t)pool_bytes < g.rec8_bytes) return fail(TRIA_ERR_BUFFER_TOO_SMALL, "pool smaller than one page");
+  return launched(tria::launch_pack_paged_varlen(shape_of(dims), pol, g, ctx_lens, k_bf16, v_bf16, table,
+                                                 (int64_t)table_bytes, old_table, (int64_t)old_table_bytes, pool,
+                                                 (int64_t)pool_bytes, static_cast<hipStream_t>(stream)),
+                  "paged varlen pack launch");
+}
+
+tria_status tria_decode_paged_varlen(const tria_dims* dims, const void* table, size_t table_bytes, const void* pool,
+                                     size_t pool_bytes, const void* q_bf16, float sm_scale, float* out,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  tria_status st = check_skip_call(dims, dims ? dims->seq_len : 1, table, table_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(pool);
+  NONNULL(q_bf16);
+  NONNULL(out);
+  NONNULL(workspace);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const tria::Shape s = shape_of(dims);
+  if ((int64_t)table_bytes < 64 + 64LL * dims->batch * dims->n_kv_heads)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "table smaller than its directory");
+  const int64_t need = tria::skip_workspace_bytes(s, dims->seq_len);
+  if ((int64_t)ws_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
+  return launched(tria::launch_decode_paged(s, 1, table, (int64_t)table_bytes, pool, (int64_t)pool_bytes, q_bf16,
+                                            sm_scale, out, workspace, true, static_cast<hipStream_t>(stream)),
+                  "paged varlen decode launch");
 }
 
 tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes, const void* q_bf16,

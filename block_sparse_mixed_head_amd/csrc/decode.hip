@@ -109,17 +109,21 @@ __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
   return header_ok_h<D, BLK>(a, h, geo);
 }
 
-// Page table header (version 4) against the launch; geo.total = the table size.
+// Page table header (version 4) against the launch; geo.total = the table size.  A
+// variable-length table (word 7 = -1, header ctx_len 0) holds each pair's ctx_len in its
+// entry and rmax (word 6) page slots per pair.
 template <int D, int BLK>
 __device__ __forceinline__ bool paged_header_h(const DecArgs& a, const Hdr64& h, Geo& geo) {
   geo.rec8 = 2LL * BLK * D + 8LL * BLK;
   geo.rec4 = (int64_t)BLK * D + 8LL * BLK;
   geo.cur = (int)((a.ctx_len - 1) / BLK);
   geo.data_offset = 64 + 64LL * a.batch * a.hkv;
-  geo.total = geo.data_offset + 4LL * a.batch * a.hkv * (geo.cur + 1);
-  return h.w[0] == 0x50564B54 && h.w[1] == 4 && h.w[2] == a.batch && h.w[3] == a.hkv && h.w[4] == D &&
-         h.w[5] == BLK && h.w[6] == geo.cur + 1 && h.w[7] == geo.cur && h.q(4) == a.ctx_len &&
-         h.q(5) == geo.rec8 && geo.total <= a.cache_bytes;
+  const int rmax = a.varlen ? h.w[6] : geo.cur + 1;
+  geo.total = geo.data_offset + 4LL * a.batch * a.hkv * rmax;
+  const bool common = h.w[0] == 0x50564B54 && h.w[1] == 4 && h.w[2] == a.batch && h.w[3] == a.hkv && h.w[4] == D &&
+                      h.w[5] == BLK && h.q(5) == geo.rec8 && rmax >= 1 && geo.total <= a.cache_bytes;
+  if (a.varlen) return common && h.w[7] == -1 && h.q(4) == 0;
+  return common && h.w[6] == geo.cur + 1 && h.w[7] == geo.cur && h.q(4) == a.ctx_len;
 }
 template <int D, int BLK>
 __device__ __forceinline__ bool paged_header_ok(const DecArgs& a, Geo& geo) {
@@ -639,6 +643,8 @@ decode_split_kernel(DecArgs a) {
     return;
   }
   if (tid == 0) bad = 0;
+  // page slots per pair of a paged table (variable length: the header's)
+  const int prmax = SKIP && a.paged ? (a.varlen ? reinterpret_cast<const int32_t*>(a.cache)[6] : a.rmax) : 0;
   __syncthreads();
   // ---- directory: record counts per pair, checked
   for (int p = tid; p < P; p += kThreads) {
@@ -661,7 +667,8 @@ decode_split_kernel(DecArgs a) {
     const int cur = pos_ok ? (int)((ctx - 1) / BLK) : 0;
     // the int8 run ends at the current block; int4 records lie below it
     const bool ok = pos_ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
-                    lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1;
+                    lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
+                    (!(SKIP && a.paged) || cur + 1 <= prmax);
     if (!ok) bad = 1;
     n8p[p] = ok ? n8 : 0;
     n4p[p] = ok ? n4 : 0;
@@ -742,7 +749,7 @@ decode_split_kernel(DecArgs a) {
       if (a.paged) {  // the table's page ids, records in the pool
         rec0 = a.pool;
         stride8 = stride4 = a.page_bytes;
-        pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * a.rmax;
+        pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * prmax;
       } else {
         const int* pe = a.plan + 8 * (int64_t)p;
         rec0 = a.cache + (int64_t)(((uint64_t)(uint32_t)pe[1] << 32) | (uint32_t)pe[0]);
@@ -1386,7 +1393,7 @@ hipError_t launch_skip_t(const SkipArgs& sa, const DecArgs& da, bool two, hipStr
 
 hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* table, int64_t table_bytes,
                                const void* pool, int64_t pool_bytes, const void* q, float sm_scale, float* out,
-                               void* workspace, hipStream_t stream) {
+                               void* workspace, bool varlen, hipStream_t stream) {
   DecArgs da;
   da.cache = static_cast<const uint8_t*>(table);
   da.q = static_cast<const uint16_t*>(q);
@@ -1398,7 +1405,7 @@ hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* tabl
   da.hq = s.hq;
   da.hkv = s.hkv;
   da.c = sm_scale * 1.44269504088896340736f;
-  da.varlen = 0;
+  da.varlen = varlen ? 1 : 0;  // (variable length: ctx_len 1, each pair's from the table)
   da.plan = nullptr;
   da.rmax = (int)((ctx_len - 1) / s.blk + 1);
   da.paged = 1;

@@ -83,12 +83,17 @@ hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache
 // Paged cache (decode.hip): decode over a version-4 page table and a page pool.
 hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* table, int64_t table_bytes,
                                const void* pool, int64_t pool_bytes, const void* q, float sm_scale, float* out,
-                               void* workspace, hipStream_t stream);
+                               void* workspace, bool varlen, hipStream_t stream);
 // Paged cache (pack.hip): records of the table for geo.ctx_len into the pool; records an
 // old table maps to the same page and (block, precision) are left as they are.
 hipError_t launch_pack_paged(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const void* k, const void* v,
                              const void* table, int64_t table_bytes, const void* old_table, int64_t old_table_bytes,
                              void* pool, int64_t pool_bytes, hipStream_t stream);
+
+hipError_t launch_pack_paged_varlen(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const int64_t* ctxs,
+                                    const void* k, const void* v, const void* table, int64_t table_bytes,
+                                    const void* old_table, int64_t old_table_bytes, void* pool, int64_t pool_bytes,
+                                    hipStream_t stream);
 
 // Measured ceilings (peaks.hip): an MFMA issue loop (kind 0: i8 16x16x64, 1: bf16
 // 16x16x32) and a non-temporal streaming read.  Work of one launch in ops / flops.

@@ -93,6 +93,11 @@ __device__ __forceinline__ uint32_t pack8_nibbles(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// ctx_len of pair p in a variable-length page table (entry words 10-11).
+__device__ __forceinline__ int64_t table_ctx(const uint8_t* table, int p) {
+  return *reinterpret_cast<const int64_t*>(table + 64 + 64 * (int64_t)p + 40);
+}
+
 // Record slot j of pair `pair` (the whole work group; every early return is uniform).
 template <int D, int BLK>
 __device__ __forceinline__ void pack_record(const PackArgs& a, int pair, int j) {
@@ -117,8 +122,9 @@ __device__ __forceinline__ void pack_record(const PackArgs& a, int pair, int j) 
   };
   // variable lengths: the pair's offset from the directory (written by the
   // directory kernel before this launch)
-  const int64_t pair_off =
-      a.varlen ? *reinterpret_cast<const int64_t*>(a.cache + 64 + 64 * (int64_t)pair) : pair_offset(a.geo);
+  const int64_t pair_off = a.table ? 0
+                           : a.varlen ? *reinterpret_cast<const int64_t*>(a.cache + 64 + 64 * (int64_t)pair)
+                                      : pair_offset(a.geo);
   const bool is4 = j >= st.n8;
   const int kb = !is4 ? ((st.sink && j == 0) ? 0 : st.lo8 + j - st.sink) : st.lo4 + (j - st.n8);
   const int64_t off = !is4 ? pair_off + (int64_t)j * a.geo.rec8_bytes
@@ -127,12 +133,15 @@ __device__ __forceinline__ void pack_record(const PackArgs& a, int pair, int j) 
   const int tid = threadIdx.x;
 
   if (a.table) {  // paged: the record's page from the table (checked), nothing else written
-    const int P = a.batch * a.hkv, rmax = c + 1;
+    const int P = a.batch * a.hkv;
     const int32_t* th = reinterpret_cast<const int32_t*>(a.table);
     const int64_t* th64 = reinterpret_cast<const int64_t*>(a.table);
+    const int rmax = th[6];
+    // fixed length: one ctx_len in the header; variable length: each entry's own
+    const bool kind_ok = a.varlen ? th[7] == -1 && th64[4] == 0 && table_ctx(a.table, pair) == ctx
+                                  : th[7] == c && th64[4] == ctx && rmax == c + 1;
     if (th[0] != 0x50564B54 || th[1] != 4 || th[2] != a.batch || th[3] != a.hkv || th[4] != D || th[5] != BLK ||
-        th[6] != rmax || th[7] != c || th64[4] != ctx || th64[5] != a.page_bytes ||
-        64 + 64LL * P + 4LL * P * rmax > a.table_bytes)
+        !kind_ok || rmax < c + 1 || th64[5] != a.page_bytes || 64 + 64LL * P + 4LL * P * rmax > a.table_bytes)
       return;
     const int32_t* e = th + 16 + 16 * pair;
     if (e[2] != st.n8 || e[3] != st.n4) return;
@@ -141,9 +150,12 @@ __device__ __forceinline__ void pack_record(const PackArgs& a, int pair, int j) 
     rec = a.pool + (int64_t)page * a.page_bytes;
     if (a.old_table && kb < c) {  // a record the pool already holds at this page
       const int32_t* oh = reinterpret_cast<const int32_t*>(a.old_table);
-      const int oc = oh[7], orm = oc + 1;
+      const int orm = oh[6];
+      const int64_t octx = a.varlen ? table_ctx(a.old_table, pair) : reinterpret_cast<const int64_t*>(a.old_table)[4];
+      const int oc = octx >= 1 ? (int)((octx - 1) / BLK) : -1;
       if (oh[0] == 0x50564B54 && oh[1] == 4 && oh[2] == a.batch && oh[3] == a.hkv && oh[4] == D && oh[5] == BLK &&
-          oh[6] == orm && oc >= 0 && 64 + 64LL * P + 4LL * P * orm <= a.old_table_bytes) {
+          (a.varlen ? oh[7] == -1 : oh[7] == oc) && oc >= 0 && oc < orm && octx <= ctx &&
+          64 + 64LL * P + 4LL * P * orm <= a.old_table_bytes) {
         const Blocks so = stored_blocks(oc, a.pol.hi[g], a.pol.keep[g]);
         int jo = -1;
         if (!is4) {
@@ -342,24 +354,31 @@ __global__ void __launch_bounds__(kThreads) paged_update_kernel(PackArgs a) {
   __shared__ int tmp[2 * (kThreads / 64)];
   __shared__ int list[kThreads];
   const int pair = blockIdx.y, g = pair % a.hkv, tid = threadIdx.x;
-  const int P = a.batch * a.hkv, c = a.geo.cur_block, rmax = c + 1;
+  const int P = a.batch * a.hkv;
+  const int64_t ctx = a.varlen ? a.ctxs[pair / a.hkv] : a.geo.ctx_len;
+  const int c = (int)((ctx - 1) / BLK);
   const Blocks st = stored_blocks(c, a.pol.hi[g], a.pol.keep[g]);
   const int32_t* th = reinterpret_cast<const int32_t*>(a.table);
   const int32_t* oh = reinterpret_cast<const int32_t*>(a.old_table);
-  const int oc = oh[7], orm = oc + 1;
-  const bool old_ok = oh[0] == 0x50564B54 && oh[1] == 4 && oh[2] == a.batch && oh[3] == a.hkv && oh[4] == D &&
-                      oh[5] == BLK && oh[6] == orm && oc >= 0 && 64 + 64LL * P + 4LL * P * orm <= a.old_table_bytes &&
+  const int rmax = th[6], orm = oh[6];
+  const int64_t octx = a.varlen ? table_ctx(a.old_table, pair) : reinterpret_cast<const int64_t*>(a.old_table)[4];
+  const int oc = octx >= 1 ? (int)((octx - 1) / BLK) : -1;
+  // both tables of this kind and shape (pack_record checks the new one fully before writing)
+  const bool new_ok = th[0] == 0x50564B54 && th[1] == 4 && rmax >= c + 1 && (a.varlen ? th[7] == -1 : th[7] == c) &&
                       64 + 64LL * P + 4LL * P * rmax <= a.table_bytes;
+  const bool old_ok = new_ok && oh[0] == 0x50564B54 && oh[1] == 4 && oh[2] == a.batch && oh[3] == a.hkv &&
+                      oh[4] == D && oh[5] == BLK && (a.varlen ? oh[7] == -1 : oh[7] == oc) && oc >= 0 && oc < orm &&
+                      octx <= ctx && 64 + 64LL * P + 4LL * P * orm <= a.old_table_bytes;
+  if (!new_ok) return;
   const Blocks so = stored_blocks(old_ok ? oc : 0, a.pol.hi[g], a.pol.keep[g]);
-  const int64_t octx = reinterpret_cast<const int64_t*>(a.old_table)[4];
   const int cur_page = th[16 + 16 * P + pair * rmax + st.n8 - 1];
-  const bool same_cur = old_ok && oc == c && so.n8 == st.n8 && octx >= (int64_t)c * BLK + 1 && octx < a.geo.ctx_len &&
-                        oh[16 + 16 * P + pair * orm + so.n8 - 1] == cur_page && th[0] == 0x50564B54 &&
-                        th[1] == 4 && th[6] == rmax && th[7] == c && cur_page >= 0 && cur_page < a.pool_pages;
+  const bool same_cur = old_ok && oc == c && so.n8 == st.n8 && octx >= (int64_t)c * BLK + 1 && octx < ctx &&
+                        oh[16 + 16 * P + pair * orm + so.n8 - 1] == cur_page && cur_page >= 0 &&
+                        cur_page < a.pool_pages && (!a.varlen || table_ctx(a.table, pair) == ctx);
   if (same_cur && blockIdx.x == 0) {
     const int b = pair / a.hkv, wave = tid >> 6, lane = tid & 63;
     uint8_t* rec = a.pool + (int64_t)cur_page * a.page_bytes;
-    for (int64_t t = octx + wave; t < a.geo.ctx_len; t += kThreads / 64) append_row<D, BLK>(a, rec, b, g, t, c, lane);
+    for (int64_t t = octx + wave; t < ctx; t += kThreads / 64) append_row<D, BLK>(a, rec, b, g, t, c, lane);
   }
   int done = 0;  // new records seen before this chunk
   for (int j0 = 0; j0 < st.n8 + st.n4; j0 += kThreads) {
@@ -540,7 +559,7 @@ hipError_t launch_t(const PackArgs& a, int max_stored, hipStream_t stream) {
     hipLaunchKernelGGL((append_kernel<D, BLK>), dim3(a.batch * a.hkv), dim3(64), 0, stream, a);
     return hipGetLastError();
   }
-  if (a.varlen) {
+  if (a.varlen && !a.table) {  // contiguous variable-length cache: its directory first
     hipLaunchKernelGGL((varlen_directory_kernel<D, BLK>), dim3(1), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -619,6 +638,38 @@ hipError_t launch_pack_paged(const Shape& s, const KvPolicy& pol, const CacheGeo
   a.ogeo = geo;
   a.only_current = 0;
   a.varlen = 0;
+  a.n = s.n;
+  a.batch = s.batch;
+  a.hkv = s.hkv;
+  a.pol = pol;
+  a.geo = geo;
+  a.table = static_cast<const uint8_t*>(table);
+  a.old_table = static_cast<const uint8_t*>(old_table);
+  a.table_bytes = table_bytes;
+  a.old_table_bytes = old_table ? old_table_bytes : 0;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.page_bytes = geo.rec8_bytes;
+  a.pool_pages = pool_bytes / geo.rec8_bytes;
+  const int max_stored = geo.cur_block + 1;
+  if (s.d == 128 && s.blk == 128) return launch_t<128, 128>(a, max_stored, stream);
+  if (s.d == 128 && s.blk == 64) return launch_t<128, 64>(a, max_stored, stream);
+  if (s.d == 64 && s.blk == 128) return launch_t<64, 128>(a, max_stored, stream);
+  return launch_t<64, 64>(a, max_stored, stream);
+}
+
+hipError_t launch_pack_paged_varlen(const Shape& s, const KvPolicy& pol, const CacheGeom& geo, const int64_t* ctxs,
+                                    const void* k, const void* v, const void* table, int64_t table_bytes,
+                                    const void* old_table, int64_t old_table_bytes, void* pool, int64_t pool_bytes,
+                                    hipStream_t stream) {
+  PackArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.cache = nullptr;
+  a.old = nullptr;
+  a.ogeo = geo;
+  a.only_current = 0;
+  a.varlen = 1;
+  for (int i = 0; i < kMaxVarlenBatch; ++i) a.ctxs[i] = i < s.batch ? ctxs[i] : 1;
   a.n = s.n;
   a.batch = s.batch;
   a.hkv = s.hkv;

@@ -409,6 +409,31 @@ tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t t
                               size_t pool_bytes, int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* Variable-length paged cache (continuous batching): each batch element's sequence at its
+ * own ctx_lens[b] (host array, 1 <= ctx_lens[b] <= seq_len, batch <= 256).  The table
+ * (same version 4) has header word 7 = -1 and ctx_len 0, rmax = c + 1 of the longest
+ * sequence page slots per pair, and each entry's words 10-11 = its sequence's ctx_len
+ * (size: tria_paged_table_bytes of the longest ctx_len).  The builder keeps pages per
+ * sequence as above; a sequence shorter than in the old table is a new sequence in its
+ * slot (its old pages are all released, none reused).  Pack: K, V [b][Hkv][seq_len][d],
+ * each sequence's rows at its own b; with the old table, each sequence writes only what
+ * changed for it.  Decode: each sequence's query attends over its own ctx_len tokens, as
+ * tria_decode does for that sequence alone (workspace: tria_decode_skip_workspace_bytes
+ * for seq_len). */
+tria_status tria_build_paged_table_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                          int32_t n_policy_heads, const int64_t* ctx_lens, int64_t n_pages,
+                                          const void* old_table, size_t old_table_bytes, const int32_t* free_pages,
+                                          int32_t n_free, void* table, size_t table_bytes, int32_t* n_used,
+                                          int32_t* released, int32_t released_capacity, int32_t* n_released);
+tria_status tria_pack_kv_cache_paged_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
+                                            int32_t n_policy_heads, const int64_t* ctx_lens, const void* k_bf16,
+                                            const void* v_bf16, const void* table, size_t table_bytes,
+                                            const void* old_table, size_t old_table_bytes, void* pool,
+                                            size_t pool_bytes, void* stream);
+tria_status tria_decode_paged_varlen(const tria_dims* dims, const void* table, size_t table_bytes, const void* pool,
+                                     size_t pool_bytes, const void* q_bf16, float sm_scale, float* out,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Dynamic block skipping in decode (device, asynchronous on `stream`).       */
 /* ------------------------------------------------------------------------- */

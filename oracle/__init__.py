@@ -44,9 +44,9 @@ def load() -> C.CDLL:
             "oracle_pack_cache": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, i64]),
             "oracle_decode": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, f32, P, C.c_int]),
             "oracle_policy_cost": (f64, [i64, C.c_int, i64, i64, f64, f64]),
-            "oracle_paged_table": (i64, [C.c_int] * 5 + [i64, P, P, C.c_int, i64, P, P, i64, P, P, i64,
+            "oracle_paged_table": (i64, [C.c_int] * 5 + [i64, P, P, P, C.c_int, i64, P, P, i64, P, P, i64,
                                                         C.POINTER(i64)]),
-            "oracle_pack_paged": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, P, i64]),
+            "oracle_pack_paged": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, P, C.c_int, P, P, P, P, i64]),
             "oracle_block_summaries": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, P, P, C.c_int]),
             "oracle_skip_masks": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, f32, P, C.c_int]),
             "oracle_decode_skip": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, P, f32, P,
@@ -244,34 +244,38 @@ def decode_skip(k, v, q, hi, keep, block: int, ctx_len: int, thresholds, sm_scal
     return out
 
 
-def paged_table(batch: int, n_q_heads: int, n_kv_heads: int, d: int, block: int, ctx_len: int, hi, keep,
+def paged_table(batch: int, n_q_heads: int, n_kv_heads: int, d: int, block: int, ctx_len, hi, keep,
                 n_pages: int, old_table: Optional[np.ndarray], free_pages, released_cap: int = 1 << 20):
-    """Page table bytes (uint8) for ctx_len, pages taken, pages released."""
+    """Page table bytes (uint8), pages taken, pages released.  ctx_len: one length, or
+    a sequence of lengths per batch element (variable-length table)."""
     hi, keep = _c(hi, np.int32), _c(keep, np.int32)
     fp = _c(free_pages, np.int32)
     P_ = batch * n_kv_heads
-    rmax = (ctx_len - 1) // block + 1
+    lens = None if np.isscalar(ctx_len) else _c(ctx_len, np.int64)
+    rmax = ((int(ctx_len) if lens is None else int(lens.max())) - 1) // block + 1
     table = np.zeros(64 + 64 * P_ + 4 * P_ * rmax, np.uint8)
     rel = np.zeros(max(released_cap, 1), np.int32)
     nrel = C.c_int64(0)
     ot = None if old_table is None else _c(old_table, np.uint8)
-    taken = load().oracle_paged_table(batch, n_q_heads, n_kv_heads, d, block, ctx_len, _p(hi), _p(keep), hi.size,
-                                      n_pages, _p(ot), _p(fp), fp.size, _p(table), _p(rel), released_cap,
-                                      C.byref(nrel))
+    taken = load().oracle_paged_table(batch, n_q_heads, n_kv_heads, d, block, 0 if lens is not None else ctx_len,
+                                      _p(lens), _p(hi), _p(keep), hi.size, n_pages, _p(ot), _p(fp), fp.size,
+                                      _p(table), _p(rel), released_cap, C.byref(nrel))
     if taken < 0:
         raise ValueError("too few free pages" if taken == -1 else "released list too small")
     return table, int(taken), rel[:nrel.value].copy()
 
 
-def pack_paged(k, v, hi, keep, n_q_heads: int, block: int, ctx_len: int, table: np.ndarray, pool: np.ndarray):
-    """Writes every stored record of the cache for ctx_len into its page of pool (uint8)."""
+def pack_paged(k, v, hi, keep, n_q_heads: int, block: int, ctx_len, table: np.ndarray, pool: np.ndarray):
+    """Writes every stored record of the cache for ctx_len (one length, or one per batch
+    element) into its page of pool (uint8)."""
     k, v = _c(k, np.uint16), _c(v, np.uint16)
     b, hk, n, d = k.shape
     hi, keep = _c(hi, np.int32), _c(keep, np.int32)
     t = _c(table, np.uint8)
+    lens = None if np.isscalar(ctx_len) else _c(ctx_len, np.int64)
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
-    if load().oracle_pack_paged(b, n_q_heads, hk, d, block, n, ctx_len, _p(hi), _p(keep), hi.size, _p(k), _p(v),
-                                _p(t), _p(pool), pool.size):
+    if load().oracle_pack_paged(b, n_q_heads, hk, d, block, n, 0 if lens is not None else ctx_len, _p(lens), _p(hi),
+                                _p(keep), hi.size, _p(k), _p(v), _p(t), _p(pool), pool.size):
         raise ValueError("table and pool do not match")
     return pool
 

@@ -852,29 +852,38 @@ int oracle_decode_skip(int batch, int n_q_heads, int n_kv_heads, int d, int bloc
 // theirs, in pair and record order.  Returns pages taken, or -1 (too few free
 // pages), -2 (released list too small).
 int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t ctx_len,
-                           const int32_t* hi, const int32_t* keep, int n_policy_heads, int64_t n_pages,
-                           const uint8_t* old_table, const int32_t* free_pages, int64_t n_free, uint8_t* table,
-                           int32_t* released, int64_t released_cap, int64_t* n_released) {
+                           const int64_t* ctx_lens, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                           int64_t n_pages, const uint8_t* old_table, const int32_t* free_pages, int64_t n_free,
+                           uint8_t* table, int32_t* released, int64_t released_cap, int64_t* n_released) {
   std::vector<int64_t> hk, kk;
   kv_policy(n_q_heads, n_kv_heads, hi, keep, n_policy_heads, hk, kk);
   const int64_t P = static_cast<int64_t>(batch) * n_kv_heads;
-  const int64_t c = (ctx_len - 1) / block, rmax = c + 1;
-  int64_t oc = -1, orm = 0;
+  // each sequence's length (variable-length tables: ctx_lens[b]) and the widest one
+  auto ctx_of = [&](int64_t p) { return ctx_lens ? ctx_lens[p / n_kv_heads] : ctx_len; };
+  int64_t rmax = 0;
+  for (int64_t p = 0; p < P; ++p) rmax = std::max(rmax, (ctx_of(p) - 1) / block + 1);
+  int64_t orm = 0;
   if (old_table) {
     int32_t v;
-    std::memcpy(&v, old_table + 28, 4);
-    oc = v;
-    orm = oc + 1;
+    std::memcpy(&v, old_table + 24, 4);
+    orm = v;
   }
   const int64_t bytes = 64 + 64 * P + 4 * P * rmax;
   std::memset(table, 0, static_cast<size_t>(bytes));
   int64_t taken = 0, nrel = 0;
   for (int64_t p = 0; p < P; ++p) {
     const int g = static_cast<int>(p % n_kv_heads);
+    const int64_t ctx = ctx_of(p), c = (ctx - 1) / block;
     std::vector<int64_t> blocks, oblocks;
     std::vector<int> qm, oqm;
     record_order(c, hk[g], kk[g], blocks, qm);
-    if (old_table) record_order(oc, hk[g], kk[g], oblocks, oqm);
+    int64_t octx = 0;
+    if (old_table) {
+      if (ctx_lens) std::memcpy(&octx, old_table + 64 + 64 * p + 40, 8);
+      else std::memcpy(&octx, old_table + 32, 8);
+      record_order((octx - 1) / block, hk[g], kk[g], oblocks, oqm);
+    }
+    const bool fresh = old_table && ctx < octx;  // a shorter sequence is a new sequence
     std::vector<int32_t> opages(oblocks.size());
     for (size_t o = 0; o < oblocks.size(); ++o)
       std::memcpy(&opages[o], old_table + 64 + 64 * P + 4 * (p * orm + static_cast<int64_t>(o)), 4);
@@ -882,7 +891,7 @@ int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int 
     for (int64_t r = 0; r < rmax; ++r) {
       int32_t pg = -1;
       if (r < static_cast<int64_t>(blocks.size())) {
-        for (size_t o = 0; o < oblocks.size(); ++o)
+        for (size_t o = 0; o < oblocks.size() && !fresh; ++o)
           if (oblocks[o] == blocks[r] && oqm[o] == qm[r] && !kept[o]) {
             pg = opages[o];
             kept[o] = true;
@@ -913,6 +922,7 @@ int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int 
     put_i32(e + 28, lo8 > 0 ? 1 : 0);
     put_i32(e + 32, b4.empty() ? 0 : static_cast<int32_t>(b4.front()));
     put_i32(e + 36, b4.empty() ? -1 : static_cast<int32_t>(b4.back()));
+    if (ctx_lens) put_i64(e + 40, ctx);
   }
   put_i32(table + 0, 0x50564B54);  // "TKVP"
   put_i32(table + 4, 4);
@@ -921,8 +931,8 @@ int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int 
   put_i32(table + 16, d);
   put_i32(table + 20, block);
   put_i32(table + 24, static_cast<int32_t>(rmax));
-  put_i32(table + 28, static_cast<int32_t>(c));
-  put_i64(table + 32, ctx_len);
+  put_i32(table + 28, ctx_lens ? -1 : static_cast<int32_t>(rmax - 1));
+  put_i64(table + 32, ctx_lens ? 0 : ctx_len);
   put_i64(table + 40, 2LL * block * d + 8LL * block);
   put_i64(table + 48, n_pages);
   *n_released = nrel;
@@ -933,28 +943,35 @@ int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int 
 // cache writer produces for it) at its page.  pool: n_pages * page bytes, pages not in
 // the table left as they are.
 int oracle_pack_paged(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t n, int64_t ctx_len,
-                      const int32_t* hi, const int32_t* keep, int n_policy_heads, const uint16_t* k,
-                      const uint16_t* v, const uint8_t* table, uint8_t* pool, int64_t pool_bytes) {
-  const int64_t total = oracle_cache_bytes(batch, n_q_heads, n_kv_heads, d, block, ctx_len, hi, keep, n_policy_heads);
-  std::vector<uint8_t> cache(static_cast<size_t>(total));
-  if (oracle_pack_cache(batch, n_q_heads, n_kv_heads, d, block, n, ctx_len, hi, keep, n_policy_heads, k, v,
-                        cache.data(), total))
-    return -1;
-  const int64_t P = static_cast<int64_t>(batch) * n_kv_heads;
-  const int64_t rmax = (ctx_len - 1) / block + 1, page = 2LL * block * d + 8LL * block;
-  for (int64_t p = 0; p < P; ++p) {
-    int64_t off;
-    int32_t n8, n4;
-    std::memcpy(&off, cache.data() + 64 + 64 * p, 8);
-    std::memcpy(&n8, cache.data() + 64 + 64 * p + 8, 4);
-    std::memcpy(&n4, cache.data() + 64 + 64 * p + 12, 4);
-    for (int64_t r = 0; r < n8 + n4; ++r) {
-      int32_t pg;
-      std::memcpy(&pg, table + 64 + 64 * P + 4 * (p * rmax + r), 4);
-      const int64_t rb = r < n8 ? 2LL * block * d + 8LL * block : static_cast<int64_t>(block) * d + 8LL * block;
-      if (pg < 0 || (pg + 1) * page > pool_bytes) return -2;
-      std::memcpy(pool + pg * page, cache.data() + off, static_cast<size_t>(rb));
-      off += rb;
+                      const int64_t* ctx_lens, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                      const uint16_t* k, const uint16_t* v, const uint8_t* table, uint8_t* pool, int64_t pool_bytes) {
+  const int64_t P = static_cast<int64_t>(batch) * n_kv_heads, page = 2LL * block * d + 8LL * block;
+  int32_t rmax;
+  std::memcpy(&rmax, table + 24, 4);
+  // one batch element at a time (its own length when the table is variable-length)
+  for (int b = 0; b < batch; ++b) {
+    const int64_t ctx = ctx_lens ? ctx_lens[b] : ctx_len;
+    const int64_t total = oracle_cache_bytes(1, n_q_heads, n_kv_heads, d, block, ctx, hi, keep, n_policy_heads);
+    std::vector<uint8_t> cache(static_cast<size_t>(total));
+    const int64_t src = static_cast<int64_t>(b) * n_kv_heads * n * d;
+    if (oracle_pack_cache(1, n_q_heads, n_kv_heads, d, block, n, ctx, hi, keep, n_policy_heads, k + src, v + src,
+                          cache.data(), total))
+      return -1;
+    for (int g = 0; g < n_kv_heads; ++g) {
+      const int64_t p = static_cast<int64_t>(b) * n_kv_heads + g;
+      int64_t off;
+      int32_t n8, n4;
+      std::memcpy(&off, cache.data() + 64 + 64 * g, 8);
+      std::memcpy(&n8, cache.data() + 64 + 64 * g + 8, 4);
+      std::memcpy(&n4, cache.data() + 64 + 64 * g + 12, 4);
+      for (int64_t r = 0; r < n8 + n4; ++r) {
+        int32_t pg;
+        std::memcpy(&pg, table + 64 + 64 * P + 4 * (p * rmax + r), 4);
+        const int64_t rb = r < n8 ? 2LL * block * d + 8LL * block : static_cast<int64_t>(block) * d + 8LL * block;
+        if (pg < 0 || (pg + 1) * page > pool_bytes) return -2;
+        std::memcpy(pool + pg * page, cache.data() + off, static_cast<size_t>(rb));
+        off += rb;
+      }
     }
   }
   return 0;

@@ -168,3 +168,51 @@ def test_paged_full_size(tria):
     assert torch.equal(out, plain)
     ref_pool = oracle.pack_paged(k, v, hi, keep, cfg.n_q_heads, cfg.block, ctx, table, np.zeros(n_pages * page, np.uint8))
     _pool_matches(pool, ref_pool, _held_pages(table, P, rmax), page)
+
+
+def test_varlen_paged_continuous_batching(tria):
+    """Three sequences in one paged cache advance at their own pace (a random subset
+    grows by one token per step) and a slot now and then starts a new, shorter
+    sequence.  Each step: host table from the previous one, the packer writes only
+    what changed, and decode equals the contiguous variable-length decode of the same
+    lengths bit for bit; every 25 steps the held pages equal the oracle's records."""
+    b, hq, hk, d, n, blk = 3, 8, 2, 128, 700, 64
+    cfg = synth.Config("paged-varlen", b, hq, hk, d, n, blk, seed=79, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    hi, keep = np.array([1, 3], np.int32), np.array([4, 8], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    page = tria.paged_page_bytes(dd)
+    P = b * hk
+    n_pages = P * ((n - 1) // blk + 1)
+    rng = np.random.default_rng(23)
+    free = list(rng.permutation(n_pages).astype(np.int32))
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    kd, vd, qd = dev(k), dev(v), dev(q)
+    sm = 1.0 / math.sqrt(d)
+    lens = np.array([1, 100, 250], np.int64)
+    old, old_dev = None, None
+    for step in range(150):
+        if step % 25 == 0:
+            print(f"[case] paged varlen step {step} lens {lens.tolist()}", flush=True)
+        table, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, np.array(free, np.int32), old)
+        free = free[used:] + list(rel)
+        tdev = torch.from_numpy(table).cuda()
+        tria.pack_kv_cache_paged(dd, hi, keep, lens, kd, vd, tdev, pool, old_table=old_dev)
+        out = tria.decode_paged_varlen(dd, tdev, pool, qd, sm)
+        cont = tria.pack_kv_cache_varlen(dd, hi, keep, lens, kd, vd)
+        ref = tria.decode_varlen(dd, cont, qd, sm)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), step
+        if step % 25 == 24:
+            rmax = int((lens.max() - 1) // blk + 1)
+            ref_pool = oracle.pack_paged(k, v, hi, keep, hq, blk, lens, table, np.zeros(n_pages * page, np.uint8))
+            _pool_matches(pool, ref_pool, _held_pages(table, P, rmax), page)
+        old, old_dev = table, tdev
+        last = (lens.copy(), out.cpu().numpy())
+        lens = np.minimum(lens + (rng.random(b) < 0.7), n)
+        if step in (60, 110):
+            lens[step % b] = 5 + step % 40       # a new sequence in this slot
+    # the last step against the oracle's decode of each sequence alone
+    for i in range(b):
+        r = oracle.decode(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, int(last[0][i]), sm)
+        assert_close(last[1][i:i + 1], r, f"paged varlen sequence {i}")

@@ -62,3 +62,30 @@ def test_paged_table_validation():
     bad[0] = 0
     with pytest.raises(TriaError):   # not a page table
         tria.build_paged_table(dd, hi, keep, 321, 64, np.arange(used, 64, dtype=np.int32), bad)
+
+
+def test_varlen_paged_table_matches_oracle():
+    """Sequences of one batch advance at their own pace (continuous batching): each step
+    a random subset grows by one token, and now and then a slot starts a new, shorter
+    sequence (its old pages all released).  Library table == oracle table every step."""
+    b, hq, hk, d, blk = 4, 8, 2, 64, 64
+    hi, keep = np.array([1, 2], np.int32), np.array([5, 9], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, 2000)
+    rng = np.random.default_rng(17)
+    n_pages = 400
+    free = list(rng.permutation(n_pages).astype(np.int32))
+    lens = np.array([1, 60, 64, 300], np.int64)
+    old = old_ref = None
+    for step in range(260):
+        t, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, free, old)
+        r, rused, rrel = oracle.paged_table(b, hq, hk, d, blk, lens, hi, keep, n_pages, old_ref, free)
+        assert np.array_equal(t, r), step
+        assert used == rused and np.array_equal(rel, rrel), step
+        free = free[used:] + list(rel)
+        old, old_ref = t, r
+        grow = rng.random(b) < 0.7
+        lens = lens + grow
+        if step % 37 == 36:
+            lens[step % b] = 1 + step % 50        # a new sequence in this slot
+    hdr = t[:64].view(np.int32)
+    assert hdr[7] == -1 and t[32:40].view(np.int64)[0] == 0
