@@ -411,6 +411,40 @@ def main():
                  "note": "update = tria_pack_kv_cache_paged with the previous table (median)"}
         log(f"[bench] paged cache: decode {pgd[0] * 1e6:.1f} us; update {upd_pin[1] * 1e6:.1f} us in a block, "
             f"{upd_pbs[1] * 1e6:.1f} us at a block start ({u_s1} new pages)")
+        # continuous batching: the 16 sequences at their own lengths (16K-32K tokens) in
+        # one pool; a step = every sequence one token longer: host table from the previous
+        # one, upload, paged update (only what changed), decode
+        rngv = np.random.default_rng(4)
+        lens = rngv.integers(c4.seq_len // 2, c4.seq_len - 200, c4.batch).astype(np.int64)
+        free_v = np.arange(n_pages, dtype=np.int32)
+        tv, usedv, _ = tria.build_paged_table(dims4, h4, kp4, lens, n_pages, free_v)
+        free_v = free_v[usedv:]
+        tv_d = torch.from_numpy(tv).cuda()
+        tria.pack_kv_cache_paged(dims4, h4, kp4, lens, k4d, v4d, tv_d, pool)
+        wsv = torch.empty(tria.decode_skip_workspace_bytes(dims4, c4.seq_len), dtype=torch.uint8, device="cuda")
+        host_us, dev_us = [], []
+        for it in range(args.reps + 3):
+            lens = lens + 1
+            h0 = time.perf_counter()
+            tv2, usedv, relv = tria.build_paged_table(dims4, h4, kp4, lens, n_pages, free_v, tv)
+            free_v = np.concatenate([free_v[usedv:], relv])
+            host_us.append((time.perf_counter() - h0) * 1e6)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tv2_d = torch.from_numpy(tv2).cuda(non_blocking=False)
+            tria.pack_kv_cache_paged(dims4, h4, kp4, lens, k4d, v4d, tv2_d, pool, old_table=tv_d)
+            tria.decode_paged_varlen(dims4, tv2_d, pool, q4, 1.0 / math.sqrt(c4.head_dim), out=o4, workspace=wsv)
+            e1.record(stream)
+            e1.synchronize()
+            dev_us.append(e0.elapsed_time(e1) * 1e3)
+            tv, tv_d = tv2, tv2_d
+        paged["continuous_batching"] = {
+            "sequences": c4.batch, "lengths": "16K-32K, each one token longer per step",
+            "step_device_us": float(np.median(dev_us[3:])), "table_build_host_us": float(np.median(host_us[3:])),
+            "note": "device: table upload + paged update + variable-length paged decode (median)"}
+        log(f"[bench] continuous batching (16 sequences, paged): {np.median(dev_us[3:]):.1f} us per step on the "
+            f"device (upload + update + decode), table build {np.median(host_us[3:]):.0f} us on the host")
+        del wsv
         del pool, wsp, tb_d, tp_d, ts0_d, ts1_d, k4d
         # dynamic block skipping (ETA-style) on the same workload, keys with block
         # structure: the index (built once per cache block), then the skipping decode

@@ -740,14 +740,25 @@ static tria_status build_paged(const tria_dims* dims, const int32_t* hi, const i
     int32_t* pages = reinterpret_cast<int32_t*>(out.data() + 64 + 64 * P + 4 * (p * rmax));
     for (int64_t r = 0; r < rmax; ++r) pages[r] = -1;
     std::vector<char> kept(opages.size(), 0);
+    // the old record of each (block, precision), by block
+    std::vector<int32_t> old8, old4;
+    if (ot && !fresh) {
+      for (size_t o = 0; o < ob.size(); ++o) {
+        std::vector<int32_t>& m = ob[o].second == 8 ? old8 : old4;
+        if ((int64_t)m.size() <= ob[o].first) m.resize(static_cast<size_t>(ob[o].first) + 1, -1);
+        m[static_cast<size_t>(ob[o].first)] = (int32_t)o;
+      }
+    }
     for (size_t r = 0; r < nb.size(); ++r) {
       int32_t pg = -1;
-      for (size_t o = 0; o < ob.size() && ot && !fresh; ++o)
-        if (ob[o] == nb[r]) {
+      const std::vector<int32_t>& m = nb[r].second == 8 ? old8 : old4;
+      if (nb[r].first < (int64_t)m.size()) {
+        const int32_t o = m[static_cast<size_t>(nb[r].first)];
+        if (o >= 0 && !kept[o]) {
           pg = opages[o];
           kept[o] = 1;
-          break;
         }
+      }
       if (pg < 0) {
         if (taken < n_free) pg = free_pages[taken];
         ++taken;
