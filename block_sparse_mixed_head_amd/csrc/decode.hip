@@ -37,6 +37,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "paged_skip.h"
 
 namespace tria {
 
@@ -613,7 +614,7 @@ decode_split_kernel(DecArgs a) {
   // checked that the directory lies inside the cache): one memory round trip
   // (SKIP: the plan's pair entry, two vectors)
   // entries from the skip plan, or (plain and paged) the cache directory / table
-  const bool from_plan = SKIP && !a.paged;
+  const bool from_plan = SKIP && a.plan != nullptr;
   auto entry_ptr = [&](int p) __attribute__((always_inline)) -> const v4i* {
     return from_plan ? reinterpret_cast<const v4i*>(a.plan + 8 * (int64_t)p)
                      : reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
@@ -746,15 +747,17 @@ decode_split_kernel(DecArgs a) {
     const uint8_t* rec4 = nullptr;
     int64_t stride8 = geo.rec8, stride4 = geo.rec4;
     if constexpr (SKIP) {
-      if (a.paged) {  // the table's page ids, records in the pool
-        rec0 = a.pool;
-        stride8 = stride4 = a.page_bytes;
-        pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * prmax;
-      } else {
+      if (from_plan) {  // kept records from the plan (entries: stored index, or page when paged)
         const int* pe = a.plan + 8 * (int64_t)p;
         rec0 = a.cache + (int64_t)(((uint64_t)(uint32_t)pe[1] << 32) | (uint32_t)pe[0]);
         n8s = uni(pe[4]);
         list = reinterpret_cast<const int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax;
+      } else {  // every record, pages from the table
+        pages = reinterpret_cast<const int32_t*>(a.cache + 64 + 64LL * P) + (int64_t)p * prmax;
+      }
+      if (a.paged) {
+        rec0 = a.pool;
+        stride8 = stride4 = a.page_bytes;
       }
     }
     rec4 = SKIP && a.paged ? rec0 : rec0 + (int64_t)n8s * geo.rec8;
@@ -946,10 +949,15 @@ struct SkipArgs {
   int* plan;        // or null: [P][8] pair entries, then [P][rmax] kept {record, mask} lists
   float sm;
   int batch, hq, hkv, rmax;
+  // paged cache: `cache` is the page table (fixed length), records in the pool
+  int paged;
+  const uint8_t* pool;
+  int64_t pool_pages;
 };
 
+// The cache header (contiguous) or the page table header (paged) against the launch.
 template <int D, int BLK>
-__device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
+__device__ __forceinline__ bool skip_header_h(const SkipArgs& s, const Hdr64& h, Geo& geo) {
   DecArgs a{};
   a.cache = s.cache;
   a.cache_bytes = s.cache_bytes;
@@ -957,7 +965,18 @@ __device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
   a.batch = s.batch;
   a.hkv = s.hkv;
   a.varlen = 0;
-  return header_ok<D, BLK>(a, geo);
+  return s.paged ? paged_header_h<D, BLK>(a, h, geo) : header_ok_h<D, BLK>(a, h, geo);
+}
+template <int D, int BLK>
+__device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
+  const Hdr64 h = *reinterpret_cast<const Hdr64*>(s.cache);
+  return skip_header_h<D, BLK>(s, h, geo);
+}
+
+// Page of record r of pair p in a paged table, or -1 when outside the pool.
+__device__ __forceinline__ int page_of(const SkipArgs& s, int p, int r) {
+  const int pg = reinterpret_cast<const int32_t*>(s.cache + 64 + 64LL * s.batch * s.hkv)[(int64_t)p * s.rmax + r];
+  return pg >= 0 && (int64_t)pg < s.pool_pages ? pg : -1;
 }
 
 // The index describes this cache's records: same pairs, slots, shape, current block
@@ -1002,15 +1021,19 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
   const v4i e0 = e[0];
   const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
   const int n8 = e0[2], n4 = e0[3];
-  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax || off < geo.data_offset ||
-      off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 > geo.total)
+  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax ||
+      (!a.paged && (off < geo.data_offset || off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 > geo.total)))
     return;
   if (r >= n8 + n4) {  // unused slot: zeros
     for (int i = tid; i < S / 4; i += kThreads) reinterpret_cast<int*>(dst)[i] = 0;
     return;
   }
   const bool is4 = r >= n8;
-  const uint8_t* rec = a.cache + off + (is4 ? (int64_t)n8 * geo.rec8 + (int64_t)(r - n8) * geo.rec4 : (int64_t)r * geo.rec8);
+  const int pg = a.paged ? page_of(a, p, r) : 0;
+  if (pg < 0) return;
+  const uint8_t* rec = a.paged ? a.pool + (int64_t)pg * (2LL * BLK * D + 8LL * BLK)
+                               : a.cache + off + (is4 ? (int64_t)n8 * geo.rec8 + (int64_t)(r - n8) * geo.rec4
+                                                      : (int64_t)r * geo.rec8);
   const int kpart = is4 ? 16 * D : 32 * D, cb = 2 * kpart + 256;
   for (int u = tid; u < SPB * kpart / 16; u += kThreads) {
     const int h = u / (kpart / 16), o = (u % (kpart / 16)) * 16;
@@ -1178,7 +1201,7 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
   da.batch = a.batch;
   da.hkv = a.hkv;
   Geo geo;
-  bool ok = header_ok_h<D, BLK>(da, hc, geo) && sums_ok<D, BLK>(a, hs, geo);
+  bool ok = skip_header_h<D, BLK>(a, hc, geo) && sums_ok<D, BLK>(a, hs, geo);
   const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
   const int n8 = e0[2], n4 = e0[3], nrec = n8 + n4;
   {
@@ -1188,7 +1211,8 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
                                         (int64_t)f[2] * geo.rec8 + (int64_t)f[3] * geo.rec4;
     ok = ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
          lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
-         off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total && cur + 1 == a.rmax;
+         (a.paged || (off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total)) &&
+         cur + 1 == a.rmax;
   }
   int* pe = a.plan ? a.plan + 8 * (int64_t)p : nullptr;
   if (!ok) {
@@ -1269,8 +1293,11 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
       const int f8 = lead && r < n8 && mk ? 1 : 0, f4 = lead && r >= n8 && mk ? 1 : 0;
       int t8, t4;
       const int2 ex = block_scan2_n<NW>(f8, f4, tmp, t8, t4);
-      if (f8) list[c8 + ex.x] = make_int2(r, (int)mk);
-      if (f4) list[n8 + c4 + ex.y] = make_int2(r - n8, (int)mk);
+      // (paged: the entry holds the record's page; a page outside the pool is read as
+      // page 0 and the pair's sums are poisoned with NaN by its keep bits of 0)
+      const int pg = a.paged && (f8 || f4) ? page_of(a, p, r) : 0;
+      if (f8) list[c8 + ex.x] = make_int2(a.paged ? (pg < 0 ? 0 : pg) : r, pg < 0 ? 0 : (int)mk);
+      if (f4) list[n8 + c4 + ex.y] = make_int2(a.paged ? (pg < 0 ? 0 : pg) : r - n8, pg < 0 ? 0 : (int)mk);
       c8 += t8;
       c4 += t4;
     }
@@ -1374,6 +1401,9 @@ SkipArgs skip_args(const Shape& s, int64_t ctx_len, const void* cache, int64_t c
   a.hq = s.hq;
   a.hkv = s.hkv;
   a.rmax = (int)((ctx_len - 1) / s.blk + 1);
+  a.paged = 0;
+  a.pool = nullptr;
+  a.pool_pages = 0;
   return a;
 }
 
@@ -1421,7 +1451,15 @@ hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* tabl
 
 hipError_t launch_summaries(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
                             hipStream_t stream) {
+  return launch_summaries_paged(s, ctx_len, cache, cache_bytes, sums, nullptr, 0, stream);
+}
+
+hipError_t launch_summaries_paged(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
+                                  const void* pool, int64_t pool_bytes, hipStream_t stream) {
   SkipArgs a = skip_args(s, ctx_len, cache, cache_bytes, nullptr, nullptr, nullptr, 0.0f);
+  a.paged = pool ? 1 : 0;
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.pool_pages = pool ? pool_bytes / (2LL * s.blk * s.d + 8LL * s.blk) : 0;
   a.sums_out = static_cast<uint8_t*>(sums);
   const dim3 grid((unsigned)((int64_t)s.batch * s.hkv * a.rmax));
   if (s.d == 128 && s.blk == 128) hipLaunchKernelGGL((summaries_kernel<128, 128>), grid, dim3(kThreads), 0, stream, a);
@@ -1445,7 +1483,19 @@ hipError_t launch_skip_masks(const Shape& s, int64_t ctx_len, const void* cache,
 hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
                               const void* sums, const void* q, const float* thresholds, float sm_scale, float* out,
                               void* workspace, hipStream_t stream) {
+  return launch_decode_skip_paged(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale, out, workspace,
+                                  nullptr, 0, stream);
+}
+
+hipError_t launch_decode_skip_paged(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
+                                    const void* sums, const void* q, const float* thresholds, float sm_scale,
+                                    float* out, void* workspace, const void* pool, int64_t pool_bytes,
+                                    hipStream_t stream) {
   SkipArgs sa = skip_args(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale);
+  const int64_t page_bytes = 2LL * s.blk * s.d + 8LL * s.blk;
+  sa.paged = pool ? 1 : 0;
+  sa.pool = static_cast<const uint8_t*>(pool);
+  sa.pool_pages = pool ? pool_bytes / page_bytes : 0;
   const int64_t pairs = (int64_t)s.batch * s.hkv;
   const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -1465,9 +1515,10 @@ hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache
   da.varlen = 0;
   da.plan = sa.plan;
   da.rmax = sa.rmax;
-  da.paged = 0;
-  da.pool = nullptr;
-  da.page_bytes = da.pool_pages = 0;
+  da.paged = sa.paged;
+  da.pool = sa.pool;
+  da.page_bytes = pool ? page_bytes : 0;
+  da.pool_pages = sa.pool_pages;
   const bool two = s.hq / s.hkv > 16;
   if (s.d == 128 && s.blk == 128) return launch_skip_t<128, 128>(sa, da, two, stream);
   if (s.d == 128) return launch_skip_t<128, 64>(sa, da, two, stream);

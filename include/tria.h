@@ -420,6 +420,20 @@ tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t t
  * changed for it.  Decode: each sequence's query attends over its own ctx_len tokens, as
  * tria_decode does for that sequence alone (workspace: tria_decode_skip_workspace_bytes
  * for seq_len). */
+/* Dynamic block skipping over a (fixed-length) paged cache: the statistics index and
+ * tria_decode_skip with records read through the table (index layout, thresholds,
+ * keep rule and workspace as for the contiguous cache; list entries hold pages).
+ * Results equal tria_decode_skip on the contiguous cache with the same content, bit
+ * for bit.  A page outside the pool leaves its index slot unwritten and, in decode,
+ * makes the query heads of its pair NaN. */
+tria_status tria_build_block_summaries_paged(const tria_dims* dims, const void* table, size_t table_bytes,
+                                             const void* pool, size_t pool_bytes, int64_t ctx_len, void* summaries,
+                                             size_t summaries_bytes, void* stream);
+tria_status tria_decode_skip_paged(const tria_dims* dims, const void* table, size_t table_bytes, const void* pool,
+                                   size_t pool_bytes, int64_t ctx_len, const void* summaries, size_t summaries_bytes,
+                                   const void* q_bf16, const float* thresholds, float sm_scale, float* out,
+                                   void* workspace, size_t ws_bytes, void* stream);
+
 tria_status tria_build_paged_table_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
                                           int32_t n_policy_heads, const int64_t* ctx_lens, int64_t n_pages,
                                           const void* old_table, size_t old_table_bytes, const int32_t* free_pages,

@@ -166,3 +166,34 @@ def test_decode_skip_full_size(tria):
     assert np.array_equal(masks.cpu().numpy().view(np.uint32), ref_masks)
     ref = oracle.decode_skip(k, v, q, hi, keep, cfg.block, ctx, th, sm)
     assert_close(out.cpu().numpy(), ref, "skip decode full size")
+
+
+@pytest.mark.parametrize("case", SKIP_CASES[:5], ids=IDS[:5])
+def test_skip_over_paged_cache_equals_contiguous(tria, case):
+    """The same cache in scattered pages: its statistics index equals the contiguous
+    cache's record for record (the header differs only in the size it names), and the
+    skipping decode over the pages equals the contiguous one bit for bit."""
+    print(f"[case] paged skip {case}", flush=True)
+    b, hq, hk, d, n, blk, ctx = case[:7]
+    k, v, q, th, hi, keep, dd, cache, sums = _setup(tria, case)
+    page = tria.paged_page_bytes(dd)
+    P, rmax = b * hk, (ctx - 1) // blk + 1
+    n_pages = P * rmax + 3
+    free = np.random.default_rng(5).permutation(n_pages).astype(np.int32)
+    table, _, _ = tria.build_paged_table(dd, hi, keep, ctx, n_pages, free)
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    tdev = torch.from_numpy(table).cuda()
+    tria.pack_kv_cache_paged(dd, hi, keep, ctx, dev(k), dev(v), tdev, pool)
+    psums = tria.build_block_summaries_paged(dd, tdev, pool, ctx)
+    sm = 1.0 / math.sqrt(d)
+    thd = torch.from_numpy(th).cuda()
+    out_p = tria.decode_skip_paged(dd, tdev, pool, ctx, psums, dev(q), thd, sm)
+    out_c = tria.decode_skip(dd, cache, ctx, sums, dev(q), thd, sm)
+    torch.cuda.synchronize()
+    a, c = psums.cpu().numpy(), sums.cpu().numpy()
+    assert np.array_equal(a[64:], c[64:]) and np.array_equal(a[:32], c[:32])
+    assert a[32:40].view(np.int64)[0] == table.size
+    assert torch.equal(out_p, out_c)
+    zero = tria.decode_skip_paged(dd, tdev, pool, ctx, psums, dev(q), torch.zeros_like(thd), sm)
+    torch.cuda.synchronize()
+    assert torch.equal(zero, tria.decode_paged(dd, tdev, pool, ctx, dev(q), sm))
