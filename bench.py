@@ -151,7 +151,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
-                                   "multi-GPU mode (see the sharding notes in DESIGN.md)",
+                                   "multi-GPU mode (each GPU would take whole (batch, KV head) groups; nothing here runs on more than one)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -169,7 +169,7 @@ def main():
         print(msg, file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------ step workload
-    cfg = synth.CONFIGS[2]
+    cfg = synth.CONFIGS["llama3_8b_layer"]
     b, hq, hk, d, n, blk = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.block
     sm = 1.0 / math.sqrt(d)
     log(f"[bench] generating {cfg.name}")
@@ -309,7 +309,7 @@ def main():
     # ------------------------------------------------------------ decode workload (b16, ctx 32768)
     dec = None
     if args.only in (None, "decode", "skip", "paged"):
-        c4 = synth.CONFIGS[4]
+        c4 = synth.CONFIGS["decode_b16"]
         log(f"[bench] generating {c4.name}")
         k4h, v4h, q4h = synth.make_decode_inputs(c4)
         # the same inputs with block structure in K and per-head thresholds (skipping)

@@ -163,17 +163,17 @@ class Config:
         return Config(**d)
 
 
-# The five workloads (shapes and policy recipes as the benchmark spec lists them).
+# The five synthetic workloads by name: shapes, policy recipes and seeds.
 CONFIGS = {
-    1: Config("tiny-prefill b1 h2/1 d64 n512 B64", 1, 2, 1, 64, 512, 64, seed=1,
+    "tiny": Config("tiny-prefill b1 h2/1 d64 n512 B64", 1, 2, 1, 64, 512, 64, seed=1,
               hi_range=(2, 2), keep_max=4, fixed={0: (2, 4), 1: (2, 4)}),
-    2: Config("llama3-8b-layer-prefill b1 h32/8 d128 n8192 B128", 1, 32, 8, 128, 8192, 128, seed=2,
+    "llama3_8b_layer": Config("llama3-8b-layer-prefill b1 h32/8 d128 n8192 B128", 1, 32, 8, 128, 8192, 128, seed=2,
               outliers=True, hi_range=(1, 8), keep_max=64),
-    3: Config("long-prefill b1 h32/8 d128 n65536 B128", 1, 32, 8, 128, 65536, 128, seed=3,
+    "long_prefill": Config("long-prefill b1 h32/8 d128 n65536 B128", 1, 32, 8, 128, 65536, 128, seed=3,
               outliers=True, hi_range=(2, 16), keep_max=128),
-    4: Config("decode b16 h32/8 d128 ctx32768 B128", 16, 32, 8, 128, 32768, 128, seed=4,
+    "decode_b16": Config("decode b16 h32/8 d128 ctx32768 B128", 16, 32, 8, 128, 32768, 128, seed=4,
               hi_range=(2, 16), keep_max=128, decode=True),
-    5: Config("batched-mixed-prefill b4 h28/4 d128 n16384 B128", 4, 28, 4, 128, 16384, 128, seed=5,
+    "batched_mixed": Config("batched-mixed-prefill b4 h28/4 d128 n16384 B128", 4, 28, 4, 128, 16384, 128, seed=5,
               hi_range=(0, 127), keep_max=127, fixed={0: (127, 127), 1: (0, 0), 2: (0, 127)}),
 }
 

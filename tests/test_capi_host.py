@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(tria):
     assert _lib.lib.tria_version() >> 16 == 1
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+@pytest.mark.parametrize("cid", ["tiny", "llama3_8b_layer", "long_prefill", "batched_mixed"])
 def test_schedule_bit_exact_on_workloads(tria, cid):
     c = synth.CONFIGS[cid]
     hi, keep = c.policy()
@@ -64,7 +64,7 @@ def test_schedule_bit_exact_random_shapes(tria):
 
 
 def test_tiny_workload_tile_counts(tria):
-    c = synth.CONFIGS[1]
+    c = synth.CONFIGS["tiny"]
     hi, keep = c.policy()
     d = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
     units = tria.build_policy(d, hi, keep)[16:].reshape(-1, 8)
@@ -77,7 +77,7 @@ def test_tiny_workload_tile_counts(tria):
     assert per_head == {0: [26, 7], 1: [26, 7]}
 
 
-@pytest.mark.parametrize("cid", [2, 4, 5])
+@pytest.mark.parametrize("cid", ["llama3_8b_layer", "decode_b16", "batched_mixed"])
 def test_cache_bytes_match_oracle(tria, cid):
     c = synth.CONFIGS[cid]
     hi, keep = c.policy()

@@ -147,7 +147,7 @@ def test_paged_full_size(tria):
     """The decode workload (b16, 32/8 heads, d128, ctx 32768, block 128) in pages handed
     out in a scattered order: every held page equals the oracle's record byte for byte,
     and the paged decode equals the contiguous decode bit for bit."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS["decode_b16"]
     print("[case] paged full-size decode workload", flush=True)
     k, v, q = synth.make_decode_inputs(cfg)
     hi, keep = cfg.policy()

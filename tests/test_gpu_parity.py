@@ -58,7 +58,7 @@ def run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=False):
 
 
 # ------------------------------------------------------------------ quantiser
-@pytest.mark.parametrize("cid", [1, 2])
+@pytest.mark.parametrize("cid", ["tiny", "llama3_8b_layer"])
 def test_quantizer_bit_exact(tria, cid):
     cfg = synth.CONFIGS[cid]
     print(f"[case] quantize config {cid}", flush=True)
@@ -211,7 +211,7 @@ def sample_units(cfg, hi, keep, per_head, heads=None, seed=0):
     return units
 
 
-@pytest.mark.parametrize("cid,per_head,heads", [(2, 3, None), (5, 2, [0, 1, 2, 3, 9, 27]), (3, 1, None)])
+@pytest.mark.parametrize("cid,per_head,heads", [("llama3_8b_layer", 3, None), ("batched_mixed", 2, [0, 1, 2, 3, 9, 27]), ("long_prefill", 1, None)])
 def test_prefill_full_size_sampled(tria, cid, per_head, heads):
     cfg = synth.CONFIGS[cid]
     print(f"[case] prefill full-size config {cid}", flush=True)
@@ -219,7 +219,7 @@ def test_prefill_full_size_sampled(tria, cid, per_head, heads):
     hi, keep = cfg.policy()
     out, _, _ = run_prefill(tria, cfg, q, k, v, hi, keep)
     units = sample_units(cfg, hi, keep, per_head, heads)
-    if cid == 5:
+    if cid == "batched_mixed":
         units = [u for u in units if u[0] in (0, 3)]
     ref = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), units=units)
     got, want = [], []
@@ -399,8 +399,8 @@ def test_decode_rejects_corrupt_cache(tria):
 
 
 def test_decode_full_size_workload(tria):
-    cfg = synth.CONFIGS[4]
-    print("[case] pack + decode full-size config 4", flush=True)
+    cfg = synth.CONFIGS["decode_b16"]
+    print("[case] pack + decode full-size decode workload b16 ctx32768", flush=True)
     k, v, q = synth.make_decode_inputs(cfg)
     hi, keep = cfg.policy()
     dd = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
@@ -414,7 +414,7 @@ def test_decode_full_size_workload(tria):
     got = cache.cpu().numpy()
     assert got.size == ref_blob.size and np.array_equal(got, ref_blob)
     ref = oracle.decode(k, v, q, hi, keep, cfg.block, cfg.seq_len, 1.0 / math.sqrt(cfg.head_dim))
-    assert_close(out.cpu().numpy(), ref, "decode config 4")
+    assert_close(out.cpu().numpy(), ref, "decode workload b16 ctx32768")
 
 
 @pytest.mark.gpu

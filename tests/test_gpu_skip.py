@@ -149,7 +149,7 @@ def test_decode_skip_rejects_stale_index(tria):
 def test_decode_skip_full_size(tria):
     """The decode workload (b16, 32/8 heads, d128, ctx 32768, block 128) with block
     structure in the keys: index and keep bits exact, outputs vs the oracle."""
-    cfg = synth.CONFIGS[4]
+    cfg = synth.CONFIGS["decode_b16"]
     print("[case] skip decode full-size decode workload", flush=True)
     k, v, q, th = synth.make_skip_decode_inputs(cfg)
     hi, keep = cfg.policy()
