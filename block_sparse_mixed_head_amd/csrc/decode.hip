@@ -951,6 +951,8 @@ struct SkipArgs {
   int batch, hq, hkv, rmax;
   // paged cache: `cache` is the page table (fixed length), records in the pool
   int paged;
+  int varlen;  // version-3 cache: each pair's ctx_len in its directory entry
+
   const uint8_t* pool;
   int64_t pool_pages;
 };
@@ -964,7 +966,7 @@ __device__ __forceinline__ bool skip_header_h(const SkipArgs& s, const Hdr64& h,
   a.ctx_len = s.ctx_len;
   a.batch = s.batch;
   a.hkv = s.hkv;
-  a.varlen = 0;
+  a.varlen = s.varlen;
   return s.paged ? paged_header_h<D, BLK>(a, h, geo) : header_ok_h<D, BLK>(a, h, geo);
 }
 template <int D, int BLK>
@@ -984,7 +986,7 @@ __device__ __forceinline__ int page_of(const SkipArgs& s, int p, int r) {
 template <int D, int BLK>
 __device__ __forceinline__ bool sums_ok(const SkipArgs& s, const Hdr64& h, const Geo& geo) {
   return h.w[0] == kSumMagic && h.w[1] == 1 && h.w[2] == s.batch * s.hkv && h.w[3] == s.rmax && h.w[4] == D &&
-         h.w[5] == BLK && h.w[6] == geo.cur && h.q(4) == geo.total;
+         h.w[5] == BLK && h.w[6] == (s.varlen ? -1 : geo.cur) && h.q(4) == geo.total;
 }
 
 // One work group per (pair, record slot): the record's K codes are staged in LDS
@@ -1012,7 +1014,7 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
     h[3] = a.rmax;
     h[4] = D;
     h[5] = BLK;
-    h[6] = geo.cur;
+    h[6] = a.varlen ? -1 : geo.cur;
     h[7] = 0;
     h64[4] = geo.total;
     h64[5] = h64[6] = h64[7] = 0;
@@ -1204,15 +1206,20 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
   bool ok = skip_header_h<D, BLK>(a, hc, geo) && sums_ok<D, BLK>(a, hs, geo);
   const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
   const int n8 = e0[2], n4 = e0[3], nrec = n8 + n4;
+  // this pair's ctx_len and current block (variable length: from its entry)
+  const int64_t pctx = a.varlen ? (int64_t)(((uint64_t)(uint32_t)e2[3] << 32) | (uint32_t)e2[2]) : a.ctx_len;
+  const bool pctx_ok = pctx >= 1 && pctx <= (1LL << 40);
+  const int cur = pctx_ok ? (int)((pctx - 1) / BLK) : 0;
+  ok = ok && pctx_ok;
   {
-    const int lo8 = e1[2], sink = e1[3], lo4 = e2[0], cur = geo.cur;
+    const int lo8 = e1[2], sink = e1[3], lo4 = e2[0];
     const int64_t expect = p == 0 ? geo.data_offset
                                   : (int64_t)(((uint64_t)(uint32_t)f[1] << 32) | (uint32_t)f[0]) +
                                         (int64_t)f[2] * geo.rec8 + (int64_t)f[3] * geo.rec4;
     ok = ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
          lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
          (a.paged || (off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total)) &&
-         cur + 1 == a.rmax;
+         (a.varlen ? cur + 1 <= a.rmax : cur + 1 == a.rmax);
   }
   int* pe = a.plan ? a.plan + 8 * (int64_t)p : nullptr;
   if (!ok) {
@@ -1309,7 +1316,7 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
     pe[3] = c4;
     pe[4] = n8;
     pe[5] = n4;
-    pe[6] = (int)(a.ctx_len - (int64_t)geo.cur * BLK);
+    pe[6] = (int)(pctx - (int64_t)cur * BLK);
     pe[7] = 1;
   }
 }
@@ -1402,6 +1409,7 @@ SkipArgs skip_args(const Shape& s, int64_t ctx_len, const void* cache, int64_t c
   a.hkv = s.hkv;
   a.rmax = (int)((ctx_len - 1) / s.blk + 1);
   a.paged = 0;
+  a.varlen = 0;
   a.pool = nullptr;
   a.pool_pages = 0;
   return a;
@@ -1451,12 +1459,13 @@ hipError_t launch_decode_paged(const Shape& s, int64_t ctx_len, const void* tabl
 
 hipError_t launch_summaries(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
                             hipStream_t stream) {
-  return launch_summaries_paged(s, ctx_len, cache, cache_bytes, sums, nullptr, 0, stream);
+  return launch_summaries_paged(s, ctx_len, cache, cache_bytes, sums, nullptr, 0, false, stream);
 }
 
 hipError_t launch_summaries_paged(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes, void* sums,
-                                  const void* pool, int64_t pool_bytes, hipStream_t stream) {
+                                  const void* pool, int64_t pool_bytes, bool varlen, hipStream_t stream) {
   SkipArgs a = skip_args(s, ctx_len, cache, cache_bytes, nullptr, nullptr, nullptr, 0.0f);
+  a.varlen = varlen ? 1 : 0;
   a.paged = pool ? 1 : 0;
   a.pool = static_cast<const uint8_t*>(pool);
   a.pool_pages = pool ? pool_bytes / (2LL * s.blk * s.d + 8LL * s.blk) : 0;
@@ -1484,14 +1493,15 @@ hipError_t launch_decode_skip(const Shape& s, int64_t ctx_len, const void* cache
                               const void* sums, const void* q, const float* thresholds, float sm_scale, float* out,
                               void* workspace, hipStream_t stream) {
   return launch_decode_skip_paged(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale, out, workspace,
-                                  nullptr, 0, stream);
+                                  nullptr, 0, false, stream);
 }
 
 hipError_t launch_decode_skip_paged(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
                                     const void* sums, const void* q, const float* thresholds, float sm_scale,
-                                    float* out, void* workspace, const void* pool, int64_t pool_bytes,
+                                    float* out, void* workspace, const void* pool, int64_t pool_bytes, bool varlen,
                                     hipStream_t stream) {
   SkipArgs sa = skip_args(s, ctx_len, cache, cache_bytes, sums, q, thresholds, sm_scale);
+  sa.varlen = varlen ? 1 : 0;
   const int64_t page_bytes = 2LL * s.blk * s.d + 8LL * s.blk;
   sa.paged = pool ? 1 : 0;
   sa.pool = static_cast<const uint8_t*>(pool);
@@ -1512,7 +1522,7 @@ hipError_t launch_decode_skip_paged(const Shape& s, int64_t ctx_len, const void*
   da.hq = s.hq;
   da.hkv = s.hkv;
   da.c = sm_scale * 1.44269504088896340736f;
-  da.varlen = 0;
+  da.varlen = sa.varlen;
   da.plan = sa.plan;
   da.rmax = sa.rmax;
   da.paged = sa.paged;

@@ -426,6 +426,18 @@ tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t t
  * Results equal tria_decode_skip on the contiguous cache with the same content, bit
  * for bit.  A page outside the pool leaves its index slot unwritten and, in decode,
  * makes the query heads of its pair NaN. */
+/* Dynamic block skipping over a variable-length (version-3) contiguous cache: each
+ * pair's statistics and plan follow its own ctx_len (read from the directory); the
+ * index (header word 6 = -1) and the workspace are sized for dims->seq_len
+ * (tria_block_summaries_bytes and tria_decode_skip_workspace_bytes of seq_len).
+ * Results per sequence equal tria_decode_skip of that sequence alone. */
+tria_status tria_build_block_summaries_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                                              void* summaries, size_t summaries_bytes, void* stream);
+tria_status tria_decode_skip_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                                    const void* summaries, size_t summaries_bytes, const void* q_bf16,
+                                    const float* thresholds, float sm_scale, float* out, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
 tria_status tria_build_block_summaries_paged(const tria_dims* dims, const void* table, size_t table_bytes,
                                              const void* pool, size_t pool_bytes, int64_t ctx_len, void* summaries,
                                              size_t summaries_bytes, void* stream);

@@ -197,3 +197,32 @@ def test_skip_over_paged_cache_equals_contiguous(tria, case):
     zero = tria.decode_skip_paged(dd, tdev, pool, ctx, psums, dev(q), torch.zeros_like(thd), sm)
     torch.cuda.synchronize()
     assert torch.equal(zero, tria.decode_paged(dd, tdev, pool, ctx, dev(q), sm))
+
+
+def test_skip_over_varlen_cache(tria):
+    """A variable-length batch (sequences at 1 to 1300 tokens): each sequence's index
+    records equal the oracle's statistics of that sequence alone, and the skipping
+    decode of each sequence equals the oracle's masked decode of it alone."""
+    b, hq, hk, d, n, blk = 4, 8, 2, 128, 1300, 128
+    lens = np.array([1300, 1, 700, 257], np.int64)
+    cfg = synth.Config("skip varlen", b, hq, hk, d, n, blk, seed=67, decode=True)
+    k, v, q, th = synth.make_skip_decode_inputs(cfg)
+    hi, keep = np.array([1, 2], np.int32), np.array([4, 9], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    cache = tria.pack_kv_cache_varlen(dd, hi, keep, lens, dev(k), dev(v))
+    sums = tria.build_block_summaries_varlen(dd, cache)
+    sm = 1.0 / math.sqrt(d)
+    out = tria.decode_skip_varlen(dd, cache, sums, dev(q), torch.from_numpy(th).cuda(), sm)
+    torch.cuda.synchronize()
+    rmax = (n - 1) // blk + 1
+    hdr, h64, lo, up, smax, pad, nmax = parse_summaries(sums, b * hk, rmax, d)
+    assert hdr[6] == -1
+    for i in range(b):
+        ctx = int(lens[i])
+        rlo, rup, rsmax, rnmax = oracle.block_summaries(k[i:i + 1], hi, keep, hq, blk, ctx)
+        rr = rlo.shape[1]
+        sl = slice(i * hk, (i + 1) * hk)
+        assert np.array_equal(lo[sl, :rr], rlo) and np.array_equal(up[sl, :rr], rup), i
+        assert np.array_equal(smax[sl, :rr], rsmax) and np.array_equal(nmax[sl, :rr], rnmax), i
+        ref = oracle.decode_skip(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, ctx, th[i:i + 1], sm)
+        assert_close(out[i:i + 1].cpu().numpy(), ref, f"varlen skip sequence {i} (ctx {ctx})")
