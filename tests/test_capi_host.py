@@ -352,3 +352,48 @@ def test_skip_and_paged_calls_validate(tria):
     assert pdec(table_b=tb - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
     assert pdec(w_b=ws - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
     assert pdec(pool=None) == _lib.TRIA_ERR_INVALID_ARG
+
+
+def test_varlen_and_paged_skip_calls_validate(tria):
+    """The variable-length and paged variants reject bad buffers before any HIP call."""
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    d = tria.make_dims(2, 8, 2, 128, 128, 4096)
+    dev = C.c_void_p(1 << 30)
+    sz = C.c_size_t(0)
+    assert L.tria_block_summaries_bytes(C.byref(d), 4096, C.byref(sz)) == _lib.TRIA_OK
+    sums = sz.value
+    assert L.tria_decode_skip_workspace_bytes(C.byref(d), 4096, C.byref(sz)) == _lib.TRIA_OK
+    ws = sz.value
+    cache = 1 << 20
+    assert L.tria_build_block_summaries_varlen(C.byref(d), dev, cache, dev, sums - 1, None) == \
+        _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_build_block_summaries_varlen(C.byref(d), None, cache, dev, sums, None) == _lib.TRIA_ERR_INVALID_ARG
+
+    def vskip(sums_b=sums, ws_b=ws, th=dev):
+        return L.tria_decode_skip_varlen(C.byref(d), dev, cache, dev, sums_b, dev, th, C.c_float(0.1), dev, dev, ws_b,
+                                         None)
+
+    assert vskip(sums_b=sums - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert vskip(ws_b=ws - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert vskip(th=None) == _lib.TRIA_ERR_INVALID_ARG
+    ctx = 1000
+    assert L.tria_paged_table_bytes(C.byref(d), ctx, C.byref(sz)) == _lib.TRIA_OK
+    tb = sz.value
+    assert L.tria_block_summaries_bytes(C.byref(d), ctx, C.byref(sz)) == _lib.TRIA_OK
+    psums = sz.value
+    assert L.tria_build_block_summaries_paged(C.byref(d), dev, tb - 1, dev, 1 << 24, ctx, dev, psums, None) == \
+        _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_build_block_summaries_paged(C.byref(d), dev, tb, None, 1 << 24, ctx, dev, psums, None) == \
+        _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_decode_skip_paged(C.byref(d), dev, tb, dev, 1 << 24, ctx, dev, psums - 1, dev, dev, C.c_float(0.1),
+                                    dev, dev, ws, None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    hi, keep = np.array([1, 2], np.int32), np.array([3, 5], np.int32)
+    lens = np.array([100, 5000], np.int64)      # past seq_len
+    assert L.tria_pack_kv_cache_paged_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, 2, lens.ctypes.data, dev,
+                                             dev, dev, tb, None, 0, dev, 1 << 24, None) == _lib.TRIA_ERR_INVALID_ARG
+    lens = np.array([100, 300], np.int64)
+    assert L.tria_pack_kv_cache_paged_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, 2, lens.ctypes.data, dev,
+                                             dev, dev, 64, None, 0, dev, 1 << 24, None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_decode_paged_varlen(C.byref(d), dev, tb, dev, 1 << 24, dev, C.c_float(0.1), dev, dev, ws - 1,
+                                      None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
