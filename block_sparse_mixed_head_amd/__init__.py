@@ -27,7 +27,8 @@ __all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "prefil
            "check_cache", "decode_workspace_bytes", "decode", "block_summaries_bytes", "build_block_summaries",
            "skip_masks", "decode_skip_workspace_bytes", "decode_skip", "paged_page_bytes", "paged_table_bytes",
            "build_paged_table", "pack_kv_cache_paged", "decode_paged", "decode_paged_varlen", "build_block_summaries_paged",
-           "decode_skip_paged", "build_block_summaries_varlen", "decode_skip_varlen", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
+           "decode_skip_paged", "build_block_summaries_varlen", "decode_skip_varlen",
+           "build_block_summaries_paged_varlen", "decode_skip_paged_varlen", "policy_cost", "allocate_policy", "peak_mfma", "peak_read", "TriaError",
            "Quantized"]
 
 Dims = _lib.Dims
@@ -380,6 +381,35 @@ def decode_skip_varlen(d: Dims, cache: torch.Tensor, summaries: torch.Tensor, q:
     check(_lib.lib.tria_decode_skip_varlen(C.byref(d), _ptr(cache), cache.numel(), _ptr(summaries), summaries.numel(),
                                            _ptr(q), _ptr(thresholds), float(sm_scale), _ptr(out), _ptr(workspace),
                                            workspace.numel(), _stream(q.device)))
+    return out
+
+
+def build_block_summaries_paged_varlen(d: Dims, table: torch.Tensor, pool: torch.Tensor,
+                                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Statistics index of a variable-length paged cache, sized for d.seq_len."""
+    if out is None:
+        out = torch.zeros(block_summaries_bytes(d, d.seq_len), dtype=torch.uint8, device=pool.device)
+    check(_lib.lib.tria_build_block_summaries_paged_varlen(C.byref(d), _ptr(table), table.numel(), _ptr(pool),
+                                                           pool.numel(), _ptr(out), out.numel(), _stream(pool.device)))
+    return out
+
+
+def decode_skip_paged_varlen(d: Dims, table: torch.Tensor, pool: torch.Tensor, summaries: torch.Tensor,
+                             q: torch.Tensor, thresholds: torch.Tensor, sm_scale: float,
+                             out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode_skip over a variable-length paged cache."""
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    _require(thresholds, torch.float32, (b, hq), "thresholds")
+    if out is None:
+        out = torch.empty((b, hq, hd), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_skip_workspace_bytes(d, d.seq_len), dtype=torch.uint8, device=q.device)
+    check(_lib.lib.tria_decode_skip_paged_varlen(C.byref(d), _ptr(table), table.numel(), _ptr(pool), pool.numel(),
+                                                 _ptr(summaries), summaries.numel(), _ptr(q), _ptr(thresholds),
+                                                 float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                                 _stream(q.device)))
     return out
 
 

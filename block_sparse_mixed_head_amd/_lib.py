@@ -71,6 +71,8 @@ def _load() -> C.CDLL:
         "tria_pack_kv_cache_paged_varlen": (C.c_int, [D, P, P, i32, P, P, P, P, sz, P, sz, P, sz, P]),
         "tria_build_block_summaries_paged": (C.c_int, [D, P, sz, P, sz, i64, P, sz, P]),
         "tria_build_block_summaries_varlen": (C.c_int, [D, P, sz, P, sz, P]),
+        "tria_build_block_summaries_paged_varlen": (C.c_int, [D, P, sz, P, sz, P, sz, P]),
+        "tria_decode_skip_paged_varlen": (C.c_int, [D, P, sz, P, sz, P, sz, P, P, f32, P, P, sz, P]),
         "tria_decode_skip_varlen": (C.c_int, [D, P, sz, P, sz, P, P, f32, P, P, sz, P]),
         "tria_decode_skip_paged": (C.c_int, [D, P, sz, P, sz, i64, P, sz, P, P, f32, P, P, sz, P]),
         "tria_decode_paged_varlen": (C.c_int, [D, P, sz, P, sz, P, f32, P, P, sz, P]),
@@ -95,7 +97,8 @@ EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quanti
             "tria_decode_skip_workspace_bytes", "tria_decode_skip", "tria_paged_page_bytes", "tria_paged_table_bytes",
             "tria_build_paged_table", "tria_build_paged_table_varlen", "tria_pack_kv_cache_paged", "tria_decode_paged",
             "tria_pack_kv_cache_paged_varlen", "tria_decode_paged_varlen", "tria_build_block_summaries_paged",
-            "tria_decode_skip_paged", "tria_build_block_summaries_varlen", "tria_decode_skip_varlen", "tria_peak_mfma",
+            "tria_decode_skip_paged", "tria_build_block_summaries_varlen", "tria_decode_skip_varlen",
+            "tria_build_block_summaries_paged_varlen", "tria_decode_skip_paged_varlen", "tria_peak_mfma",
             "tria_peak_read"]
 PEAK_READ_ALIGN = 8192 * 8 * 1024
 PEAK_SINK_INTS = 8192

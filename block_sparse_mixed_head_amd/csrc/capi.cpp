@@ -1055,6 +1055,47 @@ tria_status tria_decode_skip_varlen(const tria_dims* dims, const void* cache, si
                   "varlen skip decode launch");
 }
 
+tria_status tria_build_block_summaries_paged_varlen(const tria_dims* dims, const void* table, size_t table_bytes,
+                                                    const void* pool, size_t pool_bytes, void* summaries,
+                                                    size_t summaries_bytes, void* stream) {
+  tria_status st = check_skip_call(dims, dims ? dims->seq_len : 1, table, table_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(pool);
+  NONNULL(summaries);
+  const int64_t need = tria::summaries_bytes(shape_of(dims), dims->seq_len);
+  if ((int64_t)summaries_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "summaries need %lld bytes, got %zu", (long long)need, summaries_bytes);
+  return launched(tria::launch_summaries_paged(shape_of(dims), dims->seq_len, table, (int64_t)table_bytes, summaries,
+                                               pool, (int64_t)pool_bytes, true, static_cast<hipStream_t>(stream)),
+                  "paged varlen summaries launch");
+}
+
+tria_status tria_decode_skip_paged_varlen(const tria_dims* dims, const void* table, size_t table_bytes,
+                                          const void* pool, size_t pool_bytes, const void* summaries,
+                                          size_t summaries_bytes, const void* q_bf16, const float* thresholds,
+                                          float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                                          void* stream) {
+  tria_status st = check_skip_call(dims, dims ? dims->seq_len : 1, table, table_bytes);
+  if (st != TRIA_OK) return st;
+  NONNULL(pool);
+  NONNULL(summaries);
+  NONNULL(q_bf16);
+  NONNULL(thresholds);
+  NONNULL(out);
+  NONNULL(workspace);
+  if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const tria::Shape s = shape_of(dims);
+  if ((int64_t)summaries_bytes < tria::summaries_bytes(s, dims->seq_len))
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "summaries smaller than tria_block_summaries_bytes(seq_len)");
+  const int64_t need = tria::skip_workspace_bytes(s, dims->seq_len);
+  if ((int64_t)ws_bytes < need)
+    return fail(TRIA_ERR_BUFFER_TOO_SMALL, "skip workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
+  return launched(tria::launch_decode_skip_paged(s, dims->seq_len, table, (int64_t)table_bytes, summaries, q_bf16,
+                                                 thresholds, sm_scale, out, workspace, pool, (int64_t)pool_bytes, true,
+                                                 static_cast<hipStream_t>(stream)),
+                  "paged varlen skip decode launch");
+}
+
 tria_status tria_pack_kv_cache_paged_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
                                             int32_t n_policy_heads, const int64_t* ctx_lens, const void* k_bf16,
                                             const void* v_bf16, const void* table, size_t table_bytes,

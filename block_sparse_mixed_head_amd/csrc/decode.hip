@@ -975,9 +975,16 @@ __device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
   return skip_header_h<D, BLK>(s, h, geo);
 }
 
+// Page slots per pair of a paged table: the index's rmax, or (variable length) the
+// table's own (header word 6, checked against the table size by the header test).
+__device__ __forceinline__ int table_rmax(const SkipArgs& s) {
+  return s.varlen ? reinterpret_cast<const int32_t*>(s.cache)[6] : s.rmax;
+}
+
 // Page of record r of pair p in a paged table, or -1 when outside the pool.
 __device__ __forceinline__ int page_of(const SkipArgs& s, int p, int r) {
-  const int pg = reinterpret_cast<const int32_t*>(s.cache + 64 + 64LL * s.batch * s.hkv)[(int64_t)p * s.rmax + r];
+  const int pg =
+      reinterpret_cast<const int32_t*>(s.cache + 64 + 64LL * s.batch * s.hkv)[(int64_t)p * table_rmax(s) + r];
   return pg >= 0 && (int64_t)pg < s.pool_pages ? pg : -1;
 }
 
@@ -1023,7 +1030,7 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
   const v4i e0 = e[0];
   const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
   const int n8 = e0[2], n4 = e0[3];
-  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax ||
+  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax || (a.paged && n8 + n4 > table_rmax(a)) ||
       (!a.paged && (off < geo.data_offset || off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 > geo.total)))
     return;
   if (r >= n8 + n4) {  // unused slot: zeros
@@ -1219,7 +1226,7 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
     ok = ok && n8 >= 1 && n4 >= 0 && n8 + n4 <= cur + 1 && (sink == 0 || sink == 1) && lo8 >= 0 &&
          lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
          (a.paged || (off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total)) &&
-         (a.varlen ? cur + 1 <= a.rmax : cur + 1 == a.rmax);
+         (a.varlen ? cur + 1 <= a.rmax : cur + 1 == a.rmax) && (!a.paged || cur + 1 <= table_rmax(a));
   }
   int* pe = a.plan ? a.plan + 8 * (int64_t)p : nullptr;
   if (!ok) {

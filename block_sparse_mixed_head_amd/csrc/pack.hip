@@ -161,6 +161,7 @@ __device__ __forceinline__ void pack_record(const PackArgs& a, int pair, int j) 
         if (!is4) {
           if (kb == 0 && so.sink) jo = 0;
           else if (kb >= so.lo8 && kb <= oc) jo = so.sink + kb - so.lo8;
+          if (kb == oc && octx != (int64_t)(oc + 1) * BLK) jo = -1;  // the old current block, not yet full
         } else if (kb >= so.lo4 && kb <= so.hi4) {
           jo = so.n8 + kb - so.lo4;
         }
@@ -394,6 +395,7 @@ __global__ void __launch_bounds__(kThreads) paged_update_kernel(PackArgs a) {
         if (!is4) {
           if (kb == 0 && so.sink) jo = 0;
           else if (kb >= so.lo8 && kb <= oc) jo = so.sink + kb - so.lo8;
+          if (kb == oc && octx != (int64_t)(oc + 1) * BLK) jo = -1;  // the old current block, not yet full
         } else if (kb >= so.lo4 && kb <= so.hi4) {
           jo = so.n8 + kb - so.lo4;
         }

@@ -381,10 +381,11 @@ tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t 
  * tria_pack_kv_cache_paged: writes into the pool (device) the records of the table
  *   (device copy of a tria_build_paged_table result for this ctx_len and policy) from
  *   the bf16 K, V rows, quantised as tria_pack_kv_cache does.  old_table (device, or
- *   NULL): the table the pool currently holds; a record before the current block that
- *   it maps to the same page and (block, precision) is left as it is, so a step
- *   within a block rewrites one record per pair and a block start writes the new
- *   ones.  A table whose header does not match the call, or a page outside the pool,
+ *   NULL): the table the pool currently holds (any earlier ctx_len); a record before
+ *   the current block that it maps to the same page and (block, precision), and that
+ *   was complete there (not its partly filled current block), is left as it is, so a
+ *   step within a block writes only the new rows and a block start writes the new
+ *   records.  A table whose header does not match the call, or a page outside the pool,
  *   writes nothing.
  * tria_decode_paged: tria_decode over a paged cache: the split kernel reads the table's
  *   directory entries (checked as tria_decode checks its directory) and each record's
@@ -437,6 +438,18 @@ tria_status tria_decode_skip_varlen(const tria_dims* dims, const void* cache, si
                                     const void* summaries, size_t summaries_bytes, const void* q_bf16,
                                     const float* thresholds, float sm_scale, float* out, void* workspace,
                                     size_t ws_bytes, void* stream);
+
+/* The same over a variable-length paged cache (continuous batching): index and
+ * workspace sized for dims->seq_len; results per sequence equal tria_decode_skip_varlen
+ * on the contiguous cache with the same content, bit for bit. */
+tria_status tria_build_block_summaries_paged_varlen(const tria_dims* dims, const void* table, size_t table_bytes,
+                                                    const void* pool, size_t pool_bytes, void* summaries,
+                                                    size_t summaries_bytes, void* stream);
+tria_status tria_decode_skip_paged_varlen(const tria_dims* dims, const void* table, size_t table_bytes,
+                                          const void* pool, size_t pool_bytes, const void* summaries,
+                                          size_t summaries_bytes, const void* q_bf16, const float* thresholds,
+                                          float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                                          void* stream);
 
 tria_status tria_build_block_summaries_paged(const tria_dims* dims, const void* table, size_t table_bytes,
                                              const void* pool, size_t pool_bytes, int64_t ctx_len, void* summaries,

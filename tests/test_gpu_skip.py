@@ -226,3 +226,44 @@ def test_skip_over_varlen_cache(tria):
         assert np.array_equal(smax[sl, :rr], rsmax) and np.array_equal(nmax[sl, :rr], rnmax), i
         ref = oracle.decode_skip(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, ctx, th[i:i + 1], sm)
         assert_close(out[i:i + 1].cpu().numpy(), ref, f"varlen skip sequence {i} (ctx {ctx})")
+
+
+def test_skip_over_varlen_paged_cache(tria):
+    """A variable-length batch in scattered pages, grown over a few steps (one
+    sequence restarting shorter): its statistics index equals the contiguous
+    variable-length cache's record for record, the skipping decode equals the
+    contiguous one bit for bit, and with zero thresholds it equals the plain paged
+    decode."""
+    b, hq, hk, d, n, blk = 4, 8, 2, 128, 1300, 128
+    cfg = synth.Config("skip paged varlen", b, hq, hk, d, n, blk, seed=71, decode=True)
+    k, v, q, th = synth.make_skip_decode_inputs(cfg)
+    hi, keep = np.array([1, 2], np.int32), np.array([4, 9], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    page = tria.paged_page_bytes(dd)
+    n_pages = b * hk * ((n - 1) // blk + 1)
+    free = list(np.random.default_rng(13).permutation(n_pages).astype(np.int32))
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    kd, vd, qd, thd = dev(k), dev(v), dev(q), torch.from_numpy(th).cuda()
+    sm = 1.0 / math.sqrt(d)
+    old, old_dev = None, None
+    for lens in ([1280, 1, 700, 256], [1281, 2, 701, 257], [1282, 3, 5, 258], [1300, 129, 6, 259]):
+        lens = np.array(lens, np.int64)
+        print(f"[case] skip paged varlen lens {lens.tolist()}", flush=True)
+        table, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, np.array(free, np.int32), old)
+        free = free[used:] + list(rel)
+        tdev = torch.from_numpy(table).cuda()
+        tria.pack_kv_cache_paged(dd, hi, keep, lens, kd, vd, tdev, pool, old_table=old_dev)
+        old, old_dev = table, tdev
+        psums = tria.build_block_summaries_paged_varlen(dd, tdev, pool)
+        out_p = tria.decode_skip_paged_varlen(dd, tdev, pool, psums, qd, thd, sm)
+        cache = tria.pack_kv_cache_varlen(dd, hi, keep, lens, kd, vd)
+        sums = tria.build_block_summaries_varlen(dd, cache)
+        out_c = tria.decode_skip_varlen(dd, cache, sums, qd, thd, sm)
+        zero = tria.decode_skip_paged_varlen(dd, tdev, pool, psums, qd, torch.zeros_like(thd), sm)
+        plain = tria.decode_paged_varlen(dd, tdev, pool, qd, sm)
+        torch.cuda.synchronize()
+        a, c = psums.cpu().numpy(), sums.cpu().numpy()
+        assert np.array_equal(a[64:], c[64:]) and np.array_equal(a[:32], c[:32])
+        assert a[32:40].view(np.int64)[0] == table.size
+        assert torch.equal(out_p, out_c)
+        assert torch.equal(zero, plain)
