@@ -35,6 +35,24 @@ def _pool_matches(pool_gpu: torch.Tensor, pool_ref: np.ndarray, pages, page: int
         assert np.array_equal(got[pg], ref[pg]), f"page {pg}"
 
 
+def _records_match(pool_gpu: torch.Tensor, pool_ref: np.ndarray, table: np.ndarray, P: int, blk: int, d: int,
+                   page: int):
+    """Held records equal, each over its own length (an int4 record fills only part of
+    its page; the rest of a recycled page is not part of the cache)."""
+    got = pool_gpu.cpu().numpy().reshape(-1, page)
+    ref = pool_ref.reshape(-1, page)
+    rmax = table[:64].view(np.int32)[6]
+    ent = table[64:64 + 64 * P].view(np.int32).reshape(P, 16)
+    pages = table[64 + 64 * P:].view(np.int32).reshape(P, rmax)
+    for p in range(P):
+        n8, n4 = int(ent[p, 2]), int(ent[p, 3])
+        for j in range(n8 + n4):
+            pg = pages[p, j]
+            ln = 2 * blk * d + 8 * blk if j < n8 else blk * d + 8 * blk
+            bad = np.nonzero(got[pg, :ln] != ref[pg, :ln])[0]
+            assert bad.size == 0, f"pair {p} record {j} (n8 {n8}) page {pg}: first bad byte {bad[:1]}"
+
+
 PAGED = [
     # (b, hq, hk, d, n, blk, ctx, hi, keep)
     (2, 8, 2, 128, 1300, 128, 1300, [0, 2], [3, 10]),
@@ -110,6 +128,39 @@ def test_paged_growth_token_by_token(tria, case):
             rmax = c + 1
             ref_pool = oracle.pack_paged(k, v, hi, keep, hq, blk, ctx, table, np.zeros(n_pages * page, np.uint8))
             _pool_matches(pool, ref_pool, _held_pages(table, P, rmax), page)
+        old, old_dev = table, tdev
+
+
+def test_paged_growth_in_jumps(tria):
+    """Growth by several tokens at a time (within a block, across one, at a block's
+    end): the old table's partly filled current block keeps its page but is rewritten,
+    so after every step the held pages equal the oracle's records and decode equals
+    the contiguous decode bit for bit."""
+    b, hq, hk, d, n, blk = 2, 8, 2, 128, 700, 64
+    hi, keep = np.array([1, 2], np.int32), np.array([5, 4], np.int32)
+    cfg = synth.Config("paged-jumps", b, hq, hk, d, n, blk, seed=77, decode=True)
+    k, v, q = synth.make_decode_inputs(cfg)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    page = tria.paged_page_bytes(dd)
+    P = b * hk
+    n_pages = P * ((n - 1) // blk + 1) + 5
+    free = list(np.random.default_rng(11).permutation(n_pages).astype(np.int32))
+    pool = torch.zeros(n_pages * page, dtype=torch.uint8, device="cuda")
+    kd, vd, qd = dev(k), dev(v), dev(q)
+    sm = 1.0 / math.sqrt(d)
+    old, old_dev = None, None
+    for ctx in (70, 100, 128, 129, 190, 300, 320, 321, 700):
+        print(f"[case] paged jumps ctx {ctx}", flush=True)
+        table, used, rel = tria.build_paged_table(dd, hi, keep, ctx, n_pages, np.array(free, np.int32), old)
+        free = free[used:] + list(rel)
+        tdev = torch.from_numpy(table).cuda()
+        tria.pack_kv_cache_paged(dd, hi, keep, ctx, kd, vd, tdev, pool, old_table=old_dev)
+        out = tria.decode_paged(dd, tdev, pool, ctx, qd, sm)
+        plain = tria.decode(dd, tria.pack_kv_cache(dd, hi, keep, ctx, kd, vd), ctx, qd, sm)
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain), ctx
+        ref_pool = oracle.pack_paged(k, v, hi, keep, hq, blk, ctx, table, np.zeros(n_pages * page, np.uint8))
+        _records_match(pool, ref_pool, table, P, blk, d, page)
         old, old_dev = table, tdev
 
 
