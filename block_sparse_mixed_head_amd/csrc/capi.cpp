@@ -350,12 +350,15 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
   const size_t need = TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * (size_t)n_units;
   if (sched_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule for these dims needs %zu bytes, got %zu", need, sched_bytes);
+  if (sched_bytes != need)
+    return fail(TRIA_ERR_INVALID_ARG, "schedule for these dims is %zu bytes, got %zu", need, sched_bytes);
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (dims->seq_len > INT32_MAX - dims->block)
     return fail(TRIA_ERR_UNSUPPORTED, "prefill supports seq_len < 2^31 - block, got %lld", (long long)dims->seq_len);
-  const int32_t* units = reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(sched_dev) + TRIA_SCHED_HEADER_BYTES);
-  return launched(tria::launch_prefill(shape_of(dims), units, n_units, nullptr, 0, q8, q4, q8s, q4s, k8, k4, k8s, k4s,
-                                       v_bf16, sm_scale, out, lse, static_cast<hipStream_t>(stream)),
+  const int32_t* header = static_cast<const int32_t*>(sched_dev);
+  return launched(tria::launch_prefill(shape_of(dims), header, TRIA_SCHED_VERSION, nb, n_units, nullptr, 0, q8, q4,
+                                       q8s, q4s, k8, k4, k8s, k4s, v_bf16, sm_scale, out, lse,
+                                       static_cast<hipStream_t>(stream)),
                   "prefill launch");
 }
 
@@ -384,14 +387,17 @@ tria_status tria_prefill_varlen(const tria_dims* dims, int32_t n_seqs, const int
   const size_t need = TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * (size_t)n_units + 8 * (size_t)n_seqs;
   if (sched_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "schedule for this batch needs %zu bytes, got %zu", need, sched_bytes);
+  if (sched_bytes != need)
+    return fail(TRIA_ERR_INVALID_ARG, "schedule for this batch is %zu bytes, got %zu", need, sched_bytes);
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (dims->seq_len > INT32_MAX - dims->block)
     return fail(TRIA_ERR_UNSUPPORTED, "prefill supports seq_len < 2^31 - block, got %lld", (long long)dims->seq_len);
-  const uint8_t* base = static_cast<const uint8_t*>(sched_dev);
-  const int32_t* units = reinterpret_cast<const int32_t*>(base + TRIA_SCHED_HEADER_BYTES);
-  const int32_t* seqs = units + 8 * n_units;
-  return launched(tria::launch_prefill(shape_of(dims), units, n_units, seqs, n_seqs, q8, q4, q8s, q4s, k8, k4, k8s,
-                                       k4s, v_bf16, sm_scale, out, lse, static_cast<hipStream_t>(stream)),
+  const int32_t* header = static_cast<const int32_t*>(sched_dev);
+  const int32_t* seqs = header + TRIA_SCHED_HEADER_BYTES / 4 + 8 * n_units;
+  return launched(tria::launch_prefill(shape_of(dims), header, TRIA_SCHED_VERSION_VARLEN,
+                                       *std::max_element(nbs.begin(), nbs.end()), n_units, seqs, n_seqs, q8, q4, q8s,
+                                       q4s, k8, k4, k8s, k4s, v_bf16, sm_scale, out, lse,
+                                       static_cast<hipStream_t>(stream)),
                   "prefill launch");
 }
 

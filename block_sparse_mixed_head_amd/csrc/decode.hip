@@ -1513,7 +1513,6 @@ hipError_t launch_decode_skip_paged(const Shape& s, int64_t ctx_len, const void*
   sa.paged = pool ? 1 : 0;
   sa.pool = static_cast<const uint8_t*>(pool);
   sa.pool_pages = pool ? pool_bytes / page_bytes : 0;
-  const int64_t pairs = (int64_t)s.batch * s.hkv;
   const int64_t base = (decode_workspace_bytes(s, ctx_len) + 255) / 256 * 256;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   sa.plan = reinterpret_cast<int*>(ws + base);

@@ -19,10 +19,13 @@ hipError_t launch_quantize(const Shape& s, const void* q, const void* k, int8_t*
 // Fused block-sparse prefill over the unit records of a schedule (device memory).
 // seqs (device, or null): {start, length} of n_seqs sequences packed along the rows of
 // one batch element (s.batch == 1, s.n = total rows); a unit's b is its sequence.
-hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int32_t* seqs,
-                          int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
-                          const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
-                          float sm_scale, float* out, float* lse, hipStream_t stream);
+// header: the device schedule (64-byte header, then the n_units records, then, for a
+// variable-length batch, the n_seqs {start, length} records); version and nb: what
+// its header must hold.
+hipError_t launch_prefill(const Shape& s, const int32_t* header, int version, int64_t nb, int64_t n_units,
+                          const int32_t* seqs, int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s,
+                          const float* q4s, const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
+                          const void* v, float sm_scale, float* out, float* lse, hipStream_t stream);
 
 // Per-KV-head policy passed by value to the cache kernels.
 struct KvPolicy {

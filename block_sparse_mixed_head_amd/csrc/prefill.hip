@@ -46,6 +46,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "tria.h"
 
 namespace tria {
 
@@ -76,6 +77,7 @@ struct Cfg {
 };
 
 struct Args {
+  const int32_t* header;  // the schedule's 64-byte header (checked by every work group)
   const int32_t* units;
   const int8_t* q8;
   const uint8_t* q4;
@@ -92,7 +94,33 @@ struct Args {
   int64_t n;            // rows per (batch, head): the sequence length, or the packed total
   int batch, hq, hkv;   // batch: the number of sequences when seqs is set
   float c;  // sm_scale * log2(e)
+  // what the header must hold: version, block count (the largest one for a
+  // variable-length batch), unit count
+  int version, nb;
+  int64_t n_units;
+  int64_t rows_total;  // output rows: batch * hq * n (fixed length) or hq * n (packed)
 };
+
+// NaN in output rows [r0, r1) of the flat [rows][D] output and their LSE entries.
+template <int D>
+__device__ __forceinline__ void poison_rows(const Args& a, int64_t r0, int64_t r1) {
+  const float qn = __builtin_nanf("");
+  float4* o = reinterpret_cast<float4*>(a.out);
+  for (int64_t i = r0 * (D / 4) + threadIdx.x; i < r1 * (D / 4); i += blockDim.x) o[i] = make_float4(qn, qn, qn, qn);
+  if (a.lse)
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += blockDim.x) a.lse[r] = qn;
+}
+
+// The share of every output row that work group i poisons when the schedule header
+// does not describe the call (or its unit names no rows): the rows split evenly over
+// the grid, so together the work groups cover the whole output.
+template <int D>
+__device__ __forceinline__ void poison_share(const Args& a) {
+  const int64_t per = (a.rows_total + a.n_units - 1) / a.n_units;
+  const int64_t r0 = (int64_t)blockIdx.x * per;
+  const int64_t r1 = r0 + per < a.rows_total ? r0 + per : a.rows_total;
+  if (r0 < r1) poison_rows<D>(a, r0, r1);
+}
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) float lds_f32;
@@ -136,19 +164,21 @@ __device__ __forceinline__ v4u buffer_desc(const void* base, int bytes) {
 }
 
 // buffer_load ... lds: every active lane's 16 (4) bytes at desc + voff + soff go to
-// LDS address lds + 16 (4) * lane.  No register result; completion is counted by
-// vmcnt, which the caller waits for before the data is read (by any wave).
+// LDS address lds + 16 (4) * lane.  The LDS base travels in m0, given to the asm as
+// an input operand so the compiler itself loads m0 and knows it is in use.  No
+// register result; completion is counted by vmcnt, which the caller waits for before
+// the data is read (by any wave).
 __device__ __forceinline__ void dma16(v4u desc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(desc), "s"(soff), "s"(lds)
-               : "memory", "m0");
+               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds)
+               : "memory");
 }
 __device__ __forceinline__ void dma4(v4u desc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(desc), "s"(lds)
-               : "memory", "m0");
+               : "v"(voff), "s"(desc), "{m0}"(lds)
+               : "memory");
 }
 
 // Per-lane byte offsets, computed once per work group and held in registers.
@@ -513,26 +543,52 @@ prefill_kernel(Args a) {
     return (uint32_t)uni((int)(uint32_t)(uintptr_t)p);
   };
 
-  const int32_t* u = a.units + 8 * (int64_t)blockIdx.x;
-  const int b = u[0], h = u[1], qb = u[2], lo8 = u[3], lo4 = u[4], hi4 = u[5], sink = u[6];
+  // The header's first twelve words and the unit's record in one round trip (the
+  // host sized the schedule for n_units records); the empty asm keeps the five
+  // scalar loads together here rather than sunk past the header check.
+  const v4i* hp = reinterpret_cast<const v4i*>(a.header);
+  const v4i* up = reinterpret_cast<const v4i*>(a.units + 8 * (int64_t)blockIdx.x);
+  v4i h0 = hp[0], h1 = hp[1], h2 = hp[2], u0 = up[0], u1 = up[1];
+  asm volatile("" : "+s"(h0), "+s"(h1), "+s"(h2), "+s"(u0), "+s"(u1));
+  const int b = u0[0], h = u0[1], qb = u0[2], lo8 = u0[3], lo4 = u1[0], hi4 = u1[1], sink = u1[2];
   const int n4 = hi4 - lo4 + 1;
-  const int ntiles = u[7];
-  if (b < 0 || b >= a.batch) return;  // (checked before the sequence table is read)
+  const int ntiles = u1[3];
+  {  // a header that does not describe this call: NaN over every output row
+    // (compared without short-circuit branches)
+    const bool ok = (h0[0] == TRIA_SCHED_MAGIC) & (h0[1] == a.version) & (h0[2] == a.batch) & (h0[3] == a.hq) &
+                    (h1[0] == a.hkv) & (h1[1] == D) & (h1[2] == BLK) & (h1[3] == a.nb) &
+                    (h2[0] == (int32_t)a.n_units) & (h2[2] == (int32_t)(a.n & 0xFFFFFFFF)) &
+                    (h2[3] == (int32_t)(a.n >> 32));
+    if (!ok) {
+      poison_share<D>(a);
+      return;
+    }
+  }
   // a variable-length batch packs its sequences along the rows of one batch element:
   // unit b is sequence b, rows [seq0, seq0 + n)
   int64_t seq0 = 0, n = a.n;
   int bb = b;
-  if (a.seqs) {
+  if (b >= 0 && b < a.batch && a.seqs) {  // (b checked before the sequence table is read)
     seq0 = a.seqs[2 * b];
     n = a.seqs[2 * b + 1];
     bb = 0;
   }
-  {  // a malformed record is skipped rather than allowed to address out of range
+  {  // a malformed record computes nothing: NaN over its rows (or, when it names no
+     // rows, over the work group's share of the output)
     const int64_t nbq = (n + BLK - 1) / BLK;
-    const bool bad = seq0 < 0 || n < 1 || seq0 + n > a.n || h < 0 || h >= a.hq || qb < 0 || qb >= nbq || lo8 < 0 ||
-                     lo8 > qb || sink < 0 || sink > 1 || (sink == 1 && lo8 == 0) || n4 < 0 ||
+    const bool rows_ok = b >= 0 && b < a.batch && seq0 >= 0 && n >= 1 && seq0 + n <= a.n && h >= 0 && h < a.hq &&
+                         qb >= 0 && qb < nbq;
+    const bool bad = !rows_ok || lo8 < 0 || lo8 > qb || sink < 0 || sink > 1 || (sink == 1 && lo8 == 0) || n4 < 0 ||
                      (n4 > 0 && (lo4 < 1 || hi4 >= lo8)) || ntiles != (qb - lo8 + 1) + sink + n4;
-    if (bad) return;
+    if (bad) {
+      if (rows_ok) {
+        const int64_t r0 = ((int64_t)bb * a.hq + h) * a.n + seq0 + (int64_t)qb * BLK;
+        poison_rows<D>(a, r0, r0 + ((n - (int64_t)qb * BLK) < BLK ? (n - (int64_t)qb * BLK) : BLK));
+      } else {
+        poison_share<D>(a);
+      }
+      return;
+    }
   }
   const int g_kv = h / (a.hq / a.hkv);
   const int64_t qrow0 = ((int64_t)bb * a.hq + h) * a.n + seq0;
@@ -746,12 +802,17 @@ hipError_t launch_t(const Args& a, int64_t n_units, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill(const Shape& s, const int32_t* units, int64_t n_units, const int32_t* seqs,
-                          int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,
-                          const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s, const void* v,
-                          float sm_scale, float* out, float* lse, hipStream_t stream) {
+hipError_t launch_prefill(const Shape& s, const int32_t* header, int version, int64_t nb, int64_t n_units,
+                          const int32_t* seqs, int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s,
+                          const float* q4s, const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
+                          const void* v, float sm_scale, float* out, float* lse, hipStream_t stream) {
   Args a;
-  a.units = units;
+  a.header = header;
+  a.units = header + TRIA_SCHED_HEADER_BYTES / 4;
+  a.version = version;
+  a.nb = (int)nb;
+  a.n_units = n_units;
+  a.rows_total = (int64_t)(seqs ? 1 : s.batch) * s.hq * s.n;
   a.seqs = seqs;
   a.q8 = q8;
   a.q4 = q4;
