@@ -138,8 +138,18 @@ def test_validation_errors(tria):
     assert L.tria_quantize_qk(C.byref(good), z, one, *([one] * 8), None) == _lib.TRIA_ERR_INVALID_ARG
     assert L.tria_prefill(C.byref(good), one, 10, *([one] * 8), one, C.c_float(0.125), one, None,
                           None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
-    assert L.tria_prefill(C.byref(good), one, 1 << 20, *([one] * 8), one, C.c_float(-1.0), one, None,
+    assert L.tria_prefill(C.byref(good), one, 64 + 32 * 16, *([one] * 8), one, C.c_float(-1.0), one, None,
                           None) == _lib.TRIA_ERR_INVALID_ARG
+    assert b"sm_scale" in L.tria_last_error()
+    # a schedule larger than the dims imply is not the blob built for them
+    assert L.tria_prefill(C.byref(good), one, 64 + 32 * 16 + 4, *([one] * 8), one, C.c_float(0.125), one, None,
+                          None) == _lib.TRIA_ERR_INVALID_ARG
+    assert b"schedule" in L.tria_last_error()
+    cu = np.array([0, 200, 512], np.int64)
+    vneed = 64 + 32 * 2 * (4 + 5) + 8 * 2   # 2 heads x (4 + 5) query blocks, 2 {start, length} records
+    for nbytes, want in ((vneed - 1, _lib.TRIA_ERR_BUFFER_TOO_SMALL), (vneed + 8, _lib.TRIA_ERR_INVALID_ARG)):
+        assert L.tria_prefill_varlen(C.byref(good), 2, cu.ctypes.data, one, nbytes, *([one] * 8), one,
+                                     C.c_float(0.125), one, None, None) == want
     sz = C.c_size_t(0)
     assert L.tria_kv_cache_bytes(C.byref(good), hi.ctypes.data, keep.ctypes.data, 2, 0, C.byref(sz)) == _lib.TRIA_ERR_INVALID_ARG
     assert L.tria_kv_cache_bytes(C.byref(good), hi.ctypes.data, keep.ctypes.data, 2, 513, C.byref(sz)) == _lib.TRIA_ERR_INVALID_ARG
@@ -234,6 +244,19 @@ def test_allocator_matches_oracle(tria):
         want = oracle.allocate_policy(n, blk, e, budget, c8, c4)
         assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), trial
         assert got[2] == want[2] and got[3] == want[3], trial
+
+
+def test_allocator_follows_hand_worked_traces(tria):
+    """The library's allocator on the hand-worked instances the oracle is pinned to
+    (tests/test_oracle_pins.py): the same choices, cost and error at every budget."""
+    from test_oracle_pins import ALLOC_CASES, _B, _U
+    for name, n, err, c8, trace in ALLOC_CASES:
+        d = tria.make_dims(1, err.shape[0], 1, 64, _B, n)
+        for budget, hi, keep, cost, e64 in trace:
+            b = 1e30 if budget >= 1e9 else budget * _U
+            got_hi, got_keep, tc, te = tria.allocate_policy(d, err, b, c8, 1.0)
+            assert got_hi.tolist() == hi and got_keep.tolist() == keep, (name, budget, got_hi, got_keep)
+            assert tc == cost * _U and te * 64 == e64, (name, budget)
 
 
 def test_allocator_validates(tria):

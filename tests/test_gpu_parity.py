@@ -199,37 +199,145 @@ def test_prefill_skipped_blocks_never_read(tria):
     assert np.array_equal(a, p)
 
 
+def test_prefill_bad_schedule_gives_nan(tria):
+    """A schedule whose header does not describe the call gives NaN in every output row
+    and LSE; a malformed unit gives NaN in its own rows and leaves every other row as
+    the intact schedule computes it; a unit that names no rows (a head out of range)
+    gives NaN in its work group's even share of the output rows.  The kernel exits
+    normally in every case."""
+    b, hq, hk, d, n, blk = 1, 4, 2, 128, 700, 128
+    cfg = small_cfg(b, hq, hk, d, n, blk, seed=51)
+    q, k, v = inputs(cfg)
+    hi, keep = np.array([0, 1, 2, 6], np.int32), np.array([6, 3, 2, 6], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    blob = tria.build_policy(dd, hi, keep)
+    qz = tria.quantize_qk(dd, dev(q), dev(k))
+    vd = dev(v)
+    sm = 1.0 / math.sqrt(d)
+
+    def run(words):
+        out = torch.full((b, hq, n, d), 7.0, dtype=torch.float32, device="cuda")
+        lse = torch.full((b, hq, n), 7.0, dtype=torch.float32, device="cuda")
+        tria.prefill(dd, torch.from_numpy(words).cuda(), qz, vd, sm, out=out, lse=lse)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+    good, glse = run(blob)
+    assert np.isfinite(good).all() and np.isfinite(glse).all()
+    print("[case] bad schedule headers", flush=True)
+    for word, val in ((0, 0x1234), (1, 2), (2, 2), (3, 8), (4, 1), (5, 64), (6, 64), (7, 5), (8, 23), (10, n + 1),
+                      (11, 1)):
+        bad = blob.copy()
+        bad[word] = val
+        o, l = run(bad)
+        assert np.isnan(o).all() and np.isnan(l).all(), (word, val)
+    units = blob[16:].reshape(-1, 8)
+    i = int(np.nonzero((units[:, 0] == 0) & (units[:, 1] == 2) & (units[:, 2] == 3))[0][0])
+    rows = np.zeros((b, hq, n), bool)
+    rows[0, 2, 3 * blk:4 * blk] = True
+    print("[case] malformed units", flush=True)
+    for field, val in ((3, 4), (6, 2), (7, 99), (5, 0)):   # lo8 > qb, sink 2, ntiles, int4 range [0, 0] (block 0)
+        bad = blob.copy()
+        bad[16 + 8 * i + field] = val
+        o, l = run(bad)
+        assert np.isnan(o[rows]).all() and np.isnan(l[rows]).all(), (field, val)
+        assert np.array_equal(o[~rows], good[~rows]) and np.array_equal(l[~rows], glse[~rows]), (field, val)
+    print("[case] a unit that names no rows", flush=True)
+    bad = blob.copy()
+    bad[16 + 8 * i + 1] = 99                               # head 99 of 4
+    o, l = run(bad)
+    total, n_units = b * hq * n, units.shape[0]
+    per = -(-total // n_units)
+    share = np.zeros(total, bool)
+    share[i * per:min(total, (i + 1) * per)] = True
+    share = share.reshape(b, hq, n)
+    assert np.isnan(o[share]).all() and np.isnan(l[share]).all()
+    untouched = rows & ~share                                # the unit's own rows stay as they were
+    assert (o[untouched] == 7.0).all() and (l[untouched] == 7.0).all()
+    rest = ~rows & ~share
+    assert np.array_equal(o[rest], good[rest]) and np.array_equal(l[rest], glse[rest])
+
+
+def test_prefill_varlen_bad_schedule_gives_nan(tria):
+    """Variable-length batch: a header with the wrong sequence count, or the fixed-length
+    version, gives NaN everywhere."""
+    hq, hk, d, blk = 2, 1, 64, 64
+    lens = [100, 37, 200]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    cfg = small_cfg(1, hq, hk, d, T, blk, seed=52)
+    q, k, v = inputs(cfg)
+    hi, keep = np.array([0, 2], np.int32), np.array([1, 2], np.int32)
+    dd = tria.make_dims(1, hq, hk, d, blk, T)
+    blob = tria.build_policy_varlen(dd, hi, keep, cu)
+    qz = tria.quantize_qk(dd, dev(q), dev(k))
+    vd = dev(v)
+    print("[case] varlen bad schedule headers", flush=True)
+    for word, val in ((None, None), (1, 1), (2, 2), (7, 3)):
+        bad = blob.copy()
+        if word is not None:
+            bad[word] = val
+        out = tria.prefill_varlen(dd, cu, torch.from_numpy(bad).cuda(), qz, vd, 1.0 / math.sqrt(d))
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.isfinite(o).all() if word is None else np.isnan(o).all(), (word, val)
+
+
 # ------------------------------------------------------------------ prefill, full-size workloads (sampled)
-def sample_units(cfg, hi, keep, per_head, heads=None, seed=0):
-    rng = np.random.default_rng(seed)
+def sample_units(cfg, hi, keep, spread=29):
+    """Query blocks sampled per (batch element, head): the first and the last, the
+    blocks where the head's tile pattern changes shape (hi + 1: the last whose int8
+    run reaches block 0; hi + 2: the first with block 0 kept apart; keep + 1 and
+    keep + 2: the first whose int4 run ends at block 1 and the first with a skipped
+    block), and `spread` blocks spaced evenly over the sequence."""
     nb = cfg.nb
+    even = set(np.round(np.linspace(0, nb - 1, spread)).astype(int).tolist())
     units = []
     for bb in range(cfg.batch):
-        for h in (heads if heads is not None else range(cfg.n_q_heads)):
-            qbs = {0, nb - 1, min(nb - 1, keep[h] + 2)} | set(rng.integers(0, nb, size=per_head).tolist())
+        for h in range(cfg.n_q_heads):
+            edges = {int(hi[h]) + 1, int(hi[h]) + 2, int(keep[h]) + 1, int(keep[h]) + 2}
+            qbs = ({0, nb - 1} | {e for e in edges if e < nb} | even)
             units += [(bb, h, int(x)) for x in sorted(qbs)]
     return units
 
 
-@pytest.mark.parametrize("cid,per_head,heads", [("llama3_8b_layer", 3, None), ("batched_mixed", 2, [0, 1, 2, 3, 9, 27]), ("long_prefill", 1, None)])
-def test_prefill_full_size_sampled(tria, cid, per_head, heads):
-    cfg = synth.CONFIGS[cid]
-    print(f"[case] prefill full-size config {cid}", flush=True)
+def test_prefill_full_size_every_output(tria):
+    """The Llama-3-8B-shaped layer (n = 8192) at full size, every output element and
+    LSE entry against the oracle."""
+    cfg = synth.CONFIGS["llama3_8b_layer"]
+    print("[case] prefill full-size llama3_8b_layer, every output", flush=True)
     q, k, v = inputs(cfg)
     hi, keep = cfg.policy()
-    out, _, _ = run_prefill(tria, cfg, q, k, v, hi, keep)
-    units = sample_units(cfg, hi, keep, per_head, heads)
-    if cid == "batched_mixed":
-        units = [u for u in units if u[0] in (0, 3)]
-    ref = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), units=units)
-    got, want = [], []
+    out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
+    ref, rlse = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), with_lse=True)
+    assert_close(out.cpu().numpy(), ref, f"prefill {cfg.name} (every output)")
+    assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
+
+
+@pytest.mark.parametrize("cid", ["long_prefill", "batched_mixed"])
+def test_prefill_full_size_sampled(tria, cid):
+    """The long-prefill and batched mixed-policy workloads at full size (the launch
+    the benchmark times), every row of the sampled query blocks of every head and
+    batch element against the oracle; every output finite."""
+    cfg = synth.CONFIGS[cid]
+    q, k, v = inputs(cfg)
+    hi, keep = cfg.policy()
+    units = sample_units(cfg, hi, keep)
+    print(f"[case] prefill full-size {cid}: {len(units)} sampled units", flush=True)
+    out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
+    ref, rlse = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), units=units,
+                               with_lse=True)
+    got, want, gl, wl = [], [], [], []
+    o_np, l_np = out.cpu().numpy(), lse.cpu().numpy()
     for (bb, h, qb) in units:
         r0, r1 = qb * cfg.block, min(cfg.seq_len, (qb + 1) * cfg.block)
-        got.append(out[bb, h, r0:r1].cpu().numpy())
+        got.append(o_np[bb, h, r0:r1])
         want.append(ref[bb, h, r0:r1])
-    assert_close(np.concatenate(got), np.concatenate(want), f"prefill config {cid} ({len(units)} sampled units)")
-    # every output row is finite
-    assert torch.isfinite(out).all().item()
+        gl.append(l_np[bb, h, r0:r1])
+        wl.append(rlse[bb, h, r0:r1])
+    assert_close(np.concatenate(got), np.concatenate(want), f"prefill {cfg.name} ({len(units)} sampled units)")
+    assert np.abs(np.concatenate(gl) - np.concatenate(wl)).max() < 1e-3
+    assert np.isfinite(o_np).all() and np.isfinite(l_np).all()
 
 
 # ------------------------------------------------------------------ cache + decode
@@ -267,6 +375,42 @@ def test_pack_and_decode_small(tria, case):
     tria.check_cache(dd, cache, ctx)
     ref = oracle.decode(k, v, q, hi, keep, blk, ctx, 1.0 / math.sqrt(d))
     assert_close(out.cpu().numpy(), ref, f"decode {case}")
+
+
+def test_allocator_policy_through_prefill_and_decode(tria):
+    """Calibration (TriAttention summary page, section on how calibration distributes
+    compute between heads) feeding the hot path: the library's greedy allocator picks
+    per-query-head (hi, keep) from seeded synthetic error tables under a budget of
+    about half the dense cost; prefill over that policy, and the cache packed from it
+    (merged per KV head by the group maximum) with one-token decode, match the
+    oracle run on the same policy."""
+    b, hq, hk, d, n, blk = 1, 8, 2, 128, 1500, 128
+    nb = (n + blk - 1) // blk
+    K = nb - 1
+    rng = np.random.default_rng(77)
+    e = rng.uniform(0.0, 1.0, size=(hq, K + 1, K + 1))
+    e = np.ascontiguousarray(np.sort(np.sort(e, axis=2)[:, :, ::-1], axis=1)[:, ::-1, :])
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    dense = hq * tria.policy_cost(dd, K, K, 2.0, 1.0)
+    hi, keep, tc, _ = tria.allocate_policy(dd, e, 0.5 * dense, 2.0, 1.0)
+    o_hi, o_keep, o_tc, _ = oracle.allocate_policy(n, blk, e, 0.5 * dense, 2.0, 1.0)
+    assert np.array_equal(hi, o_hi) and np.array_equal(keep, o_keep) and tc == o_tc
+    print(f"[case] allocator policy hi={hi.tolist()} keep={keep.tolist()}", flush=True)
+    assert len(set(zip(hi.tolist(), keep.tolist()))) > 1, "expected the heads to differ"
+    cfg = small_cfg(b, hq, hk, d, n, blk, seed=78)
+    q, k, v = inputs(cfg)
+    out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
+    ref, rlse = oracle.prefill(q, k, v, hi, keep, blk, 1.0 / math.sqrt(d), with_lse=True)
+    assert_close(out.cpu().numpy(), ref, "prefill under the allocator's policy")
+    assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
+    ctx = n - 5
+    cache = tria.pack_kv_cache(dd, hi, keep, ctx, dev(k), dev(v))
+    assert np.array_equal(cache.cpu().numpy(), oracle.pack_cache(k, v, hi, keep, hq, blk, ctx))
+    qd = np.ascontiguousarray(q[:, :, ctx - 1])
+    o = tria.decode(dd, cache, ctx, dev(qd), 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    assert_close(o.cpu().numpy(), oracle.decode(k, v, qd, hi, keep, blk, ctx, 1.0 / math.sqrt(d)),
+                 "decode under the allocator's policy")
 
 
 VARLEN_DEC = [

@@ -569,3 +569,117 @@ def test_allocator_against_brute_force():
                    if sum(cost[c] for c in choice) <= budget)
         assert te >= best - 1e-12
 
+
+
+# ---------------------------------------------------------------- allocator: hand-worked greedy traces
+# TriAttention summary page (rit.work), section on how calibration distributes
+# compute between heads: one global allocator gives more context or more precision
+# where the added work lowers the error most.  The instances below are small enough
+# to run the greedy by hand.  Sequence of 4 blocks of 64 (n = 256, nb = 4); costs
+# in units of one tile (64 * 64 pairs).  Kept tiles per (hi, keep), from the tile
+# rule (10 causal tiles; block 0 and the diagonal always int8):
+#   (0,0): 7 int8            (0,1): 7 int8 + 2 int4    (0,2): 7 int8 + 3 int4
+#   (1,1): 9 int8            (1,2): 9 int8 + 1 int4    (2,2): 10 int8
+# With an int8 tile at 2 and an int4 tile at 1 the costs are 14, 16, 17, 18, 19, 20;
+# with both at 1 they are 7, 9, 10, 9, 10, 10.
+# Moves from (a, k): keep -> (a, k + 1) if k < K; hi -> (a + 1, max(k, a + 1)) if a < K.
+_N, _B = 256, 64
+_U = float(_B * _B)
+
+
+def _err_table(*heads, K=2):
+    """Error tables in units of 1/64 (exact in binary, so equal ratios tie exactly)."""
+    e = np.full((len(heads), K + 1, K + 1), 99.0)
+    for h, vals in enumerate(heads):
+        for (a, k), x in vals.items():
+            e[h, a, k] = x / 64.0
+    return e
+
+
+def test_allocator_cost_table_by_hand():
+    want = {(0, 0): (14, 7), (0, 1): (16, 9), (0, 2): (17, 10), (1, 1): (18, 9), (1, 2): (19, 10), (2, 2): (20, 10)}
+    for (a, k), (c21, c11) in want.items():
+        assert oracle.policy_cost(_N, _B, a, k, 2.0, 1.0) == c21 * _U
+        assert oracle.policy_cost(_N, _B, a, k, 1.0, 1.0) == c11 * _U
+
+
+# Instance A: two heads, int8 tile 2, int4 tile 1.  Errors (x 1/64):
+#   head 0: (0,0) 64, (0,1) 56, (0,2) 52, (1,1) 48, (1,2) 44, (2,2) 40
+#   head 1: (0,0) 64, (0,1) 56, (0,2) 40, (1,1) 60, (1,2) 50, (2,2) 49
+# Greedy by hand (score = error drop / cost added, per tile), start cost 28:
+#   1. h0 keep 8/2=4, h0 hi 16/4=4, h1 keep 8/2=4, h1 hi 4/4=1: a three-way tie;
+#      the lower head wins, and within it the keep move -> h0 (0,1), cost 30
+#   2. h0 keep 4/1=4, h0 hi 8/2=4, h1 keep 4, h1 hi 1 -> tie, h0 keep -> h0 (0,2), 31
+#   3. h0 hi (1,2) 8/2=4, h1 keep 4 -> tie, lower head -> h0 (1,2), 33
+#   4. h0 hi (2,2) 4/1=4, h1 keep 4 -> tie, lower head -> h0 (2,2), 34
+#   5. h1 keep 4, h1 hi 1 -> h1 (0,1), 36
+#   6. h1 keep (0,2) 16/1=16; h1 hi (1,1) raises the error (60 > 56) -> h1 (0,2), 37
+#   7. h1 hi (1,2) raises the error (50 > 40): no move lowers any error; stop.
+# Under a budget the trace stops where the next chosen move no longer fits and no
+# other move fits either (every move here costs at least one tile).
+_A = _err_table({(0, 0): 64, (0, 1): 56, (0, 2): 52, (1, 1): 48, (1, 2): 44, (2, 2): 40},
+                {(0, 0): 64, (0, 1): 56, (0, 2): 40, (1, 1): 60, (1, 2): 50, (2, 2): 49})
+_A_TRACE = [  # (budget in tiles, hi, keep, cost in tiles, error x 64)
+    (28, [0, 0], [0, 0], 28, 128),
+    (29, [0, 0], [0, 0], 28, 128),
+    (30, [0, 0], [1, 0], 30, 120),
+    (31, [0, 0], [2, 0], 31, 116),
+    (32, [0, 0], [2, 0], 31, 116),   # step 3's moves (h0 hi, h1 keep) both add 2
+    (33, [1, 0], [2, 0], 33, 108),
+    (34, [2, 0], [2, 0], 34, 104),
+    (35, [2, 0], [2, 0], 34, 104),   # h1 keep adds 2, h1 hi adds 4
+    (36, [2, 0], [2, 1], 36, 96),
+    (37, [2, 0], [2, 2], 37, 80),
+    (1e9, [2, 0], [2, 2], 37, 80),   # stops on step 7: nothing lowers an error
+]
+
+# Instance B: one head, int8 tile 2, int4 tile 1, where the best move may not fit.
+#   errors: (0,0) 64, (0,1) 60, (0,2) 58, (1,1) 32, (1,2) 30, (2,2) 16
+#   no limit: from (0,0) keep 4/2=2, hi 32/4=8 -> (1,1) [18]; keep (1,2) 2/1=2, hi
+#   (2,2) 16/2=8 -> (2,2) [20].  Budget 16: hi does not fit (18), keep does -> (0,1)
+#   [16]; nothing more fits.  Budget 19: -> (1,1) [18]; hi (2,2) needs 20, keep
+#   (1,2) fits -> (1,2) [19].
+_B_INST = _err_table({(0, 0): 64, (0, 1): 60, (0, 2): 58, (1, 1): 32, (1, 2): 30, (2, 2): 16})
+_B_TRACE = [(16, [0], [1], 16, 60), (19, [1], [2], 19, 30), (1e9, [2], [2], 20, 16)]
+
+# Instance C: one head, both tiles cost 1, so raising hi inside the kept range is
+# free.  errors: (0,0) 64, (0,1) 48, (0,2) 40, (1,1) 50, (1,2) 39, (2,2) 38
+#   from (0,0): keep 16/2=8, hi 14/2=7 -> (0,1) [9]; keep (0,2) 8/1=8, hi (1,1) raises
+#   the error -> (0,2) [10]; hi (1,2) drops 1 at no cost -> (1,2) [10]; hi (2,2) drops
+#   1 at no cost -> (2,2) [10].  Budget 9: stops at (0,1).
+_C_INST = _err_table({(0, 0): 64, (0, 1): 48, (0, 2): 40, (1, 1): 50, (1, 2): 39, (2, 2): 38})
+_C_TRACE = [(9, [0], [1], 9, 48), (10, [2], [2], 10, 38), (1e9, [2], [2], 10, 38)]
+
+# Instance D: free moves go first.  Five blocks (n = 320, K = 3), both tiles cost 1:
+# the cost depends on keep only, 9, 12, 14, 15 for keep 0..3.  Errors (x 1/64):
+#   head 0: (0,0) 64, (0,1) 43, (0,2) 33, (1,2) 32, (0,3) 31, (1,3) 8
+#   head 1: (0,0) 64, (0,1) 28, (0,2) 12, (0,3) 8;  every other entry 99
+# Start 18.  1. h0 keep 21/3=7, h1 keep 36/3=12 -> h1 (0,1) [21]; 2. h1 keep 16/2=8 ->
+# h1 (0,2) [23]; 3. h0 keep 7, h1 keep 4/1=4 -> h0 (0,1) [26]; 4. h0 keep 10/2=5 ->
+# h0 (0,2) [28]; 5. h0 hi (1,2) drops 1 at no cost, ahead of h1's 4 and h0's keep 2
+# -> h0 (1,2) [28]; 6. h0 keep (1,3) 24/1=24 -> h0 (1,3) [29]; 7. h1 keep -> (0,3)
+# [30]; nothing else lowers an error.  With 29 tiles the free move at step 5 is
+# what lets head 0 take the last tile (ranked after h1's 4, it would go to head 1).
+_D_INST = _err_table({(0, 0): 64, (0, 1): 43, (0, 2): 33, (1, 2): 32, (0, 3): 31, (1, 3): 8},
+                     {(0, 0): 64, (0, 1): 28, (0, 2): 12, (0, 3): 8}, K=3)
+_D_TRACE = [(18, [0, 0], [0, 0], 18, 128), (21, [0, 0], [0, 1], 21, 92), (23, [0, 0], [0, 2], 23, 76),
+            (26, [0, 0], [1, 2], 26, 55), (28, [1, 0], [2, 2], 28, 44), (29, [1, 0], [3, 2], 29, 20),
+            (30, [1, 0], [3, 3], 30, 16), (1e9, [1, 0], [3, 3], 30, 16)]
+
+# Instance E: a move that lowers no error is not taken, even where a later move would
+# lower it a lot.  One head, 4 blocks, int8 tile 2, int4 tile 1: (0,0), (0,1) and
+# (1,1) all 64, (0,2) 10 -> stays at (0,0) [14].
+_E_INST = _err_table({(0, 0): 64, (0, 1): 64, (1, 1): 64, (0, 2): 10})
+_E_TRACE = [(1e9, [0], [0], 14, 64)]
+
+ALLOC_CASES = [("A", _N, _A, 2.0, _A_TRACE), ("B", _N, _B_INST, 2.0, _B_TRACE), ("C", _N, _C_INST, 1.0, _C_TRACE),
+               ("D", 320, _D_INST, 1.0, _D_TRACE), ("E", _N, _E_INST, 2.0, _E_TRACE)]
+
+
+@pytest.mark.parametrize("name,n,err,c8,trace", ALLOC_CASES, ids=[c[0] for c in ALLOC_CASES])
+def test_allocator_hand_worked_traces(name, n, err, c8, trace):
+    for budget, hi, keep, cost, e64 in trace:
+        b = 1e30 if budget >= 1e9 else budget * _U
+        got_hi, got_keep, tc, te = oracle.allocate_policy(n, _B, err, b, c8, 1.0)
+        assert got_hi.tolist() == hi and got_keep.tolist() == keep, (name, budget, got_hi, got_keep)
+        assert tc == cost * _U and te * 64 == e64, (name, budget, tc / _U, te * 64)
