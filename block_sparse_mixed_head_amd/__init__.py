@@ -275,10 +275,11 @@ def paged_table_bytes(d: Dims, ctx_len: int) -> int:
 
 
 def build_paged_table(d: Dims, hi, keep, ctx_len, n_pages: int, free_pages,
-                      old_table: Optional[np.ndarray] = None):
+                      old_table: Optional[np.ndarray] = None, seq_ids=None):
     """Host page table (uint8); returns (table, pages taken from the front of free_pages,
     released pages).  ctx_len: one length, or one per batch element (a variable-length
-    table, tria_build_paged_table_varlen)."""
+    table, tria_build_paged_table_varlen, where seq_ids optionally names the sequence
+    of each slot: a slot whose id changed holds a new sequence)."""
     hi, keep = _i32(hi), _i32(keep)
     fp = _i32(free_pages)
     lens = None if np.isscalar(ctx_len) else np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int64))
@@ -294,8 +295,12 @@ def build_paged_table(d: Dims, hi, keep, ctx_len, n_pages: int, free_pages,
         check(_lib.lib.tria_build_paged_table(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi), ctx_len, n_pages,
                                               *common))
     else:
+        sids = None if seq_ids is None else np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        if sids is not None and sids.shape != lens.shape:
+            raise ValueError("seq_ids: one id per batch element")
         check(_lib.lib.tria_build_paged_table_varlen(C.byref(d), hi.ctypes.data, keep.ctypes.data, len(hi),
-                                                     lens.ctypes.data, n_pages, *common))
+                                                     lens.ctypes.data, None if sids is None else sids.ctypes.data,
+                                                     n_pages, *common))
     return table, used.value, rel[:nrel.value].copy()
 
 

@@ -64,7 +64,7 @@ def _load() -> C.CDLL:
         "tria_paged_table_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
         "tria_build_paged_table": (C.c_int, [D, P, P, i32, i64, i64, P, sz, P, i32, P, sz, C.POINTER(i32), P, i32,
                                              C.POINTER(i32)]),
-        "tria_build_paged_table_varlen": (C.c_int, [D, P, P, i32, P, i64, P, sz, P, i32, P, sz, C.POINTER(i32), P,
+        "tria_build_paged_table_varlen": (C.c_int, [D, P, P, i32, P, P, i64, P, sz, P, i32, P, sz, C.POINTER(i32), P,
                                                     i32, C.POINTER(i32)]),
         "tria_pack_kv_cache_paged": (C.c_int, [D, P, P, i32, i64, P, P, P, sz, P, sz, P, sz, P]),
         "tria_decode_paged": (C.c_int, [D, P, sz, P, sz, i64, P, f32, P, P, sz, P]),

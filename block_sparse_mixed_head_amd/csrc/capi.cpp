@@ -657,11 +657,13 @@ tria_status tria_paged_table_bytes(const tria_dims* dims, int64_t ctx_len, size_
 }
 
 // The page table for per-pair current blocks (fixed length: one ctx_len; varlen: each
-// batch element's ctx_lens[b], header word 7 = -1 and each entry's words 10-11 = its
-// ctx_len).  A pair whose length is below the old table's starts afresh (all its old
-// pages released): its slot holds a new sequence.
+// batch element's ctx_lens[b], header word 7 = -1, each entry's words 10-11 = its
+// ctx_len and words 12-13 its sequence id, seq_ids[b] or 0).  A pair whose length is
+// below the old table's, or whose sequence id differs from it, starts afresh (all its
+// old pages released): its slot holds a new sequence.
 static tria_status build_paged(const tria_dims* dims, const int32_t* hi, const int32_t* keep, int32_t n_policy_heads,
-                               const int64_t* ctx_lens, int64_t ctx_len, int64_t n_pages, const void* old_table,
+                               const int64_t* ctx_lens, const int64_t* seq_ids, int64_t ctx_len, int64_t n_pages,
+                               const void* old_table,
                                size_t old_table_bytes, const int32_t* free_pages, int32_t n_free, void* table,
                                size_t table_bytes, int32_t* n_used, int32_t* released, int32_t released_capacity,
                                int32_t* n_released) {
@@ -720,14 +722,18 @@ static tria_status build_paged(const tria_dims* dims, const int32_t* hi, const i
   for (int64_t p = 0; p < P; ++p) {
     const int g = (int)(p % dims->n_kv_heads);
     const int64_t ctx = ctx_b[p / dims->n_kv_heads], c = (ctx - 1) / dims->block;
+    const int64_t sid = varlen && seq_ids ? seq_ids[p / dims->n_kv_heads] : 0;
     record_blocks(c, pol.hi[g], pol.keep[g], nb);
     std::vector<int32_t> opages;
     bool fresh = false;
     if (ot) {
       int32_t e[16];
       std::memcpy(e, ot + 64 + 64 * p, 64);
-      int64_t octx = octx_all;
-      if (varlen) std::memcpy(&octx, ot + 64 + 64 * p + 40, 8);
+      int64_t octx = octx_all, osid = 0;
+      if (varlen) {
+        std::memcpy(&octx, ot + 64 + 64 * p + 40, 8);
+        std::memcpy(&osid, ot + 64 + 64 * p + 48, 8);
+      }
       if (octx < 1 || (octx - 1) / dims->block >= orm)
         return fail(TRIA_ERR_INVALID_ARG, "old table entry %lld corrupt", (long long)p);
       if (e[4] != pol.hi[g] || e[5] != pol.keep[g])
@@ -740,7 +746,7 @@ static tria_status build_paged(const tria_dims* dims, const int32_t* hi, const i
         if (pg < 0 || pg >= n_pages || used[pg]) return fail(TRIA_ERR_INVALID_ARG, "old table page %d invalid", pg);
         used[pg] = 1;
       }
-      fresh = ctx < octx;  // a shorter sequence is a new one
+      fresh = ctx < octx || sid != osid;  // a shorter sequence, or another id, is a new one
     } else {
       ob.clear();
     }
@@ -786,7 +792,10 @@ static tria_status build_paged(const tria_dims* dims, const int32_t* hi, const i
     e[7] = lo8 > 0 ? 1 : 0;
     e[8] = e[3] > 0 ? (int32_t)std::max<int64_t>(1, c - pol.keep[g]) : 0;
     e[9] = e[3] > 0 ? (int32_t)(c - pol.hi[g] - 1) : -1;
-    if (varlen) std::memcpy(&e[10], &ctx, 8);
+    if (varlen) {
+      std::memcpy(&e[10], &ctx, 8);
+      std::memcpy(&e[12], &sid, 8);
+    }
     std::memcpy(out.data() + 64 + 64 * p, e, 64);
   }
   *n_used = (int32_t)std::min<int64_t>(taken, INT32_MAX);
@@ -819,20 +828,21 @@ tria_status tria_build_paged_table(const tria_dims* dims, const int32_t* hi, con
                                    size_t old_table_bytes, const int32_t* free_pages, int32_t n_free, void* table,
                                    size_t table_bytes, int32_t* n_used, int32_t* released, int32_t released_capacity,
                                    int32_t* n_released) {
-  return build_paged(dims, hi, keep, n_policy_heads, nullptr, ctx_len, n_pages, old_table, old_table_bytes,
+  return build_paged(dims, hi, keep, n_policy_heads, nullptr, nullptr, ctx_len, n_pages, old_table, old_table_bytes,
                      free_pages, n_free, table, table_bytes, n_used, released, released_capacity, n_released);
 }
 
 tria_status tria_build_paged_table_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
-                                          int32_t n_policy_heads, const int64_t* ctx_lens, int64_t n_pages,
-                                          const void* old_table, size_t old_table_bytes, const int32_t* free_pages,
-                                          int32_t n_free, void* table, size_t table_bytes, int32_t* n_used,
-                                          int32_t* released, int32_t released_capacity, int32_t* n_released) {
+                                          int32_t n_policy_heads, const int64_t* ctx_lens, const int64_t* seq_ids,
+                                          int64_t n_pages, const void* old_table, size_t old_table_bytes,
+                                          const int32_t* free_pages, int32_t n_free, void* table, size_t table_bytes,
+                                          int32_t* n_used, int32_t* released, int32_t released_capacity,
+                                          int32_t* n_released) {
   if (!ctx_lens) return fail(TRIA_ERR_INVALID_ARG, "ctx_lens is NULL");
   if (dims && dims->batch > tria::kMaxVarlenBatch)
     return fail(TRIA_ERR_UNSUPPORTED, "batch above %d for a variable-length cache", tria::kMaxVarlenBatch);
-  return build_paged(dims, hi, keep, n_policy_heads, ctx_lens, 0, n_pages, old_table, old_table_bytes, free_pages,
-                     n_free, table, table_bytes, n_used, released, released_capacity, n_released);
+  return build_paged(dims, hi, keep, n_policy_heads, ctx_lens, seq_ids, 0, n_pages, old_table, old_table_bytes,
+                     free_pages, n_free, table, table_bytes, n_used, released, released_capacity, n_released);
 }
 
 // ------------------------------------------------------------------ (f4) dynamic block skipping

@@ -929,11 +929,14 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
 // head's threshold is skipped for that head, and a record every head of the group
 // skips is never read.
 //
-// Statistics index: a 64-byte header {magic, version 1, pairs, record slots per pair
+// Statistics index: a 64-byte header {magic, version 2, pairs, record slots per pair
 // (rmax = current block + 1), d, block, current block, 0, cache total bytes (int64)},
 // then per (pair, record slot) S = 2d + 16 bytes: lo[d], hi[d] (int8: per-coordinate
-// minimum and maximum code over the record's rows), the largest row scale (fp32), 0,
-// and the largest (scale * scale) * |codes|^2 over rows (fp64).
+// minimum and maximum code over the record's rows), the largest row scale (fp32), the
+// stamp (the pair's current block + 1 when the slot was built; 0 for an unused slot),
+// and the largest (scale * scale) * |codes|^2 over rows (fp64).  A slot's statistics
+// hold while its pair keeps the same current block: the record order, and every record
+// before the current one, depend only on it.
 constexpr int kSumMagic = 0x4D534254;  // "TBSM"
 __host__ __device__ constexpr int sum_stride(int d) { return 2 * d + 16; }
 
@@ -992,7 +995,7 @@ __device__ __forceinline__ int page_of(const SkipArgs& s, int p, int r) {
 // and total size (statistics of the current block itself are never used).
 template <int D, int BLK>
 __device__ __forceinline__ bool sums_ok(const SkipArgs& s, const Hdr64& h, const Geo& geo) {
-  return h.w[0] == kSumMagic && h.w[1] == 1 && h.w[2] == s.batch * s.hkv && h.w[3] == s.rmax && h.w[4] == D &&
+  return h.w[0] == kSumMagic && h.w[1] == 2 && h.w[2] == s.batch * s.hkv && h.w[3] == s.rmax && h.w[4] == D &&
          h.w[5] == BLK && h.w[6] == (s.varlen ? -1 : geo.cur) && h.q(4) == geo.total;
 }
 
@@ -1016,7 +1019,7 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
     int32_t* h = reinterpret_cast<int32_t*>(a.sums_out);
     int64_t* h64 = reinterpret_cast<int64_t*>(a.sums_out);
     h[0] = kSumMagic;
-    h[1] = 1;
+    h[1] = 2;
     h[2] = P;
     h[3] = a.rmax;
     h[4] = D;
@@ -1027,12 +1030,16 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
     h64[5] = h64[6] = h64[7] = 0;
   }
   const v4i* e = reinterpret_cast<const v4i*>(a.cache + 64 + 64 * (int64_t)p);
-  const v4i e0 = e[0];
+  const v4i e0 = e[0], e2 = e[2];
   const int64_t off = (int64_t)(((uint64_t)(uint32_t)e0[1] << 32) | (uint32_t)e0[0]);
   const int n8 = e0[2], n4 = e0[3];
-  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax || (a.paged && n8 + n4 > table_rmax(a)) ||
+  // the pair's current block (variable length: from its entry's ctx_len)
+  const int64_t pctx = a.varlen ? (int64_t)(((uint64_t)(uint32_t)e2[3] << 32) | (uint32_t)e2[2]) : a.ctx_len;
+  if (n8 < 1 || n4 < 0 || n8 + n4 > a.rmax || (a.paged && n8 + n4 > table_rmax(a)) || pctx < 1 ||
+      (pctx - 1) / BLK >= a.rmax ||
       (!a.paged && (off < geo.data_offset || off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 > geo.total)))
     return;
+  const int stamp = (int)((pctx - 1) / BLK) + 1;
   if (r >= n8 + n4) {  // unused slot: zeros
     for (int i = tid; i < S / 4; i += kThreads) reinterpret_cast<int*>(dst)[i] = 0;
     return;
@@ -1114,7 +1121,7 @@ __global__ void __launch_bounds__(kThreads) summaries_kernel(SkipArgs a) {
       m = smw[w] > m ? smw[w] : m;
     }
     *reinterpret_cast<float*>(dst + 2 * D) = m;
-    *reinterpret_cast<int*>(dst + 2 * D + 4) = 0;
+    *reinterpret_cast<int*>(dst + 2 * D + 4) = stamp;
     *reinterpret_cast<double*>(dst + 2 * D + 8) = n;
   }
 }
@@ -1203,6 +1210,9 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
     }
   };
   load_slot(tid / Gp);
+  // the stamp of index slot tid (a slot of this pair when tid < rmax)
+  const int stamp0 = tid < a.rmax ? *reinterpret_cast<const int*>(a.sums + 64 + ((int64_t)p * a.rmax + tid) * S + 2 * D + 4)
+                                  : 0;
   // ---- checks (uniform)
   DecArgs da{};
   da.cache_bytes = a.cache_bytes;
@@ -1227,6 +1237,15 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
          lo8 + (n8 - sink) - 1 == cur && sink == (lo8 > 0 ? 1 : 0) && lo4 >= 0 && lo4 + n4 <= cur + 1 &&
          (a.paged || (off == expect && off + (int64_t)n8 * geo.rec8 + (int64_t)n4 * geo.rec4 <= geo.total)) &&
          (a.varlen ? cur + 1 <= a.rmax : cur + 1 == a.rmax) && (!a.paged || cur + 1 <= table_rmax(a));
+  }
+  {  // every stored record's slot was built for this current block (a variable-length
+     // sequence that moved to another block, or restarted in one, leaves stale slots)
+    bool stale = false;
+    if (ok)
+      for (int r = tid; r < nrec; r += kPlanThreads)
+        stale = stale || (r == tid ? stamp0 : *reinterpret_cast<const int*>(a.sums + 64 + ((int64_t)p * a.rmax + r) * S +
+                                                                             2 * D + 4)) != cur + 1;
+    ok = ok && !__syncthreads_or(stale);
   }
   int* pe = a.plan ? a.plan + 8 * (int64_t)p : nullptr;
   if (!ok) {

@@ -415,8 +415,11 @@ tria_status tria_decode_paged(const tria_dims* dims, const void* table, size_t t
  * (same version 4) has header word 7 = -1 and ctx_len 0, rmax = c + 1 of the longest
  * sequence page slots per pair, and each entry's words 10-11 = its sequence's ctx_len
  * (size: tria_paged_table_bytes of the longest ctx_len).  The builder keeps pages per
- * sequence as above; a sequence shorter than in the old table is a new sequence in its
- * slot (its old pages are all released, none reused).  Pack: K, V [b][Hkv][seq_len][d],
+ * sequence as above.  seq_ids (host int64[batch], may be NULL for all 0) names the
+ * sequence each slot holds, kept in its entries' words 12-13: a slot whose id differs
+ * from the old table's, or whose sequence is shorter than there, holds a new sequence
+ * (its old pages are all released, none reused), so a finished request's slot can take
+ * a new prompt of any length.  Pack: K, V [b][Hkv][seq_len][d],
  * each sequence's rows at its own b; with the old table, each sequence writes only what
  * changed for it.  Decode: each sequence's query attends over its own ctx_len tokens, as
  * tria_decode does for that sequence alone (workspace: tria_decode_skip_workspace_bytes
@@ -460,10 +463,11 @@ tria_status tria_decode_skip_paged(const tria_dims* dims, const void* table, siz
                                    void* workspace, size_t ws_bytes, void* stream);
 
 tria_status tria_build_paged_table_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
-                                          int32_t n_policy_heads, const int64_t* ctx_lens, int64_t n_pages,
-                                          const void* old_table, size_t old_table_bytes, const int32_t* free_pages,
-                                          int32_t n_free, void* table, size_t table_bytes, int32_t* n_used,
-                                          int32_t* released, int32_t released_capacity, int32_t* n_released);
+                                          int32_t n_policy_heads, const int64_t* ctx_lens, const int64_t* seq_ids,
+                                          int64_t n_pages, const void* old_table, size_t old_table_bytes,
+                                          const int32_t* free_pages, int32_t n_free, void* table, size_t table_bytes,
+                                          int32_t* n_used, int32_t* released, int32_t released_capacity,
+                                          int32_t* n_released);
 tria_status tria_pack_kv_cache_paged_varlen(const tria_dims* dims, const int32_t* hi, const int32_t* keep,
                                             int32_t n_policy_heads, const int64_t* ctx_lens, const void* k_bf16,
                                             const void* v_bf16, const void* table, size_t table_bytes,
@@ -498,15 +502,21 @@ tria_status tria_decode_paged_varlen(const tria_dims* dims, const void* table, s
  * its KV head keeps is not read.
  *
  * tria_block_summaries_bytes / tria_build_block_summaries: the index of a version-2
- *   cache for ctx_len: a 64-byte header {int32 magic "TBSM", 1, pairs, slots per pair
+ *   cache for ctx_len: a 64-byte header {int32 magic "TBSM", 2, pairs, slots per pair
  *   (rmax = (ctx_len - 1) / block + 1), head_dim, block, current block, 0; int64 the
  *   cache's total_bytes at byte 32}, then per (pair, record slot) 2 * head_dim + 16
- *   bytes {int8 lo[d], int8 hi[d], fp32 smax, int32 0, fp64 nmax}; slots past a pair's
- *   records are zero.  One work group per slot reads the record's K codes once.  The
- *   index stays valid while the cache keeps the same current block and total size
- *   (tria_update_kv_cache within a block changes only the current record, whose
- *   statistics are not used); rebuild it when a block starts.  A cache that does not
- *   validate leaves the index without its header (later calls then reject it).
+ *   bytes {int8 lo[d], int8 hi[d], fp32 smax, int32 stamp, fp64 nmax}, stamp = the
+ *   pair's current block + 1 at build time; slots past a pair's records are zero.  One
+ *   work group per slot reads the record's K codes once.  The index stays valid while
+ *   the cache keeps the same current block and total size (tria_update_kv_cache within
+ *   a block changes only the current record, whose statistics are not used); rebuild
+ *   it when a block starts.  The decode checks every stored record's stamp against its
+ *   pair's current block, so an index left from another current block (a
+ *   variable-length sequence that moved on, or restarted in another block) does not
+ *   validate; a sequence restarted inside the same current block cannot be told
+ *   apart from its predecessor by the index, so its caller rebuilds the index.  A
+ *   cache that does not validate leaves the index without its header (later calls
+ *   then reject it).
  * tria_skip_masks: the keep bits of every stored record: masks = uint32 [pairs][rmax]
  *   (record order of the cache: int8 records, then int4), bit i set = query head
  *   g * G + i keeps the record; slots past a pair's records are not written.

@@ -44,7 +44,7 @@ def load() -> C.CDLL:
             "oracle_pack_cache": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, i64]),
             "oracle_decode": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, f32, P, C.c_int]),
             "oracle_policy_cost": (f64, [i64, C.c_int, i64, i64, f64, f64]),
-            "oracle_paged_table": (i64, [C.c_int] * 5 + [i64, P, P, P, C.c_int, i64, P, P, i64, P, P, i64,
+            "oracle_paged_table": (i64, [C.c_int] * 5 + [i64, P, P, P, P, C.c_int, i64, P, P, i64, P, P, i64,
                                                         C.POINTER(i64)]),
             "oracle_pack_paged": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, P, C.c_int, P, P, P, P, i64]),
             "oracle_block_summaries": (C.c_int, [C.c_int] * 5 + [i64, i64, P, P, C.c_int, P, P, P, P, P, C.c_int]),
@@ -245,9 +245,11 @@ def decode_skip(k, v, q, hi, keep, block: int, ctx_len: int, thresholds, sm_scal
 
 
 def paged_table(batch: int, n_q_heads: int, n_kv_heads: int, d: int, block: int, ctx_len, hi, keep,
-                n_pages: int, old_table: Optional[np.ndarray], free_pages, released_cap: int = 1 << 20):
+                n_pages: int, old_table: Optional[np.ndarray], free_pages, released_cap: int = 1 << 20,
+                seq_ids=None):
     """Page table bytes (uint8), pages taken, pages released.  ctx_len: one length, or
-    a sequence of lengths per batch element (variable-length table)."""
+    a sequence of lengths per batch element (variable-length table, where seq_ids
+    optionally names each slot's sequence)."""
     hi, keep = _c(hi, np.int32), _c(keep, np.int32)
     fp = _c(free_pages, np.int32)
     P_ = batch * n_kv_heads
@@ -257,8 +259,9 @@ def paged_table(batch: int, n_q_heads: int, n_kv_heads: int, d: int, block: int,
     rel = np.zeros(max(released_cap, 1), np.int32)
     nrel = C.c_int64(0)
     ot = None if old_table is None else _c(old_table, np.uint8)
+    sids = None if seq_ids is None else _c(seq_ids, np.int64)
     taken = load().oracle_paged_table(batch, n_q_heads, n_kv_heads, d, block, 0 if lens is not None else ctx_len,
-                                      _p(lens), _p(hi), _p(keep), hi.size, n_pages, _p(ot), _p(fp), fp.size,
+                                      _p(lens), _p(sids), _p(hi), _p(keep), hi.size, n_pages, _p(ot), _p(fp), fp.size,
                                       _p(table), _p(rel), released_cap, C.byref(nrel))
     if taken < 0:
         raise ValueError("too few free pages" if taken == -1 else "released list too small")

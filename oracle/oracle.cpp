@@ -847,12 +847,15 @@ int oracle_decode_skip(int batch, int n_q_heads, int n_kv_heads, int d, int bloc
 // out here from its definition): header {"TKVP", 4, batch, kv heads, d, block, c + 1,
 // c; ctx_len, page bytes, n_pages, 0}, one 64-byte entry per pair {0, 0, n8, n4, hi,
 // keep, lo8, sink, lo4, hi4, 0...}, then per pair c + 1 page ids in record order (-1
-// past its records).  A record whose (block, precision) the old table stores keeps
-// its page; every other takes the next free page; old records not kept release
-// theirs, in pair and record order.  Returns pages taken, or -1 (too few free
-// pages), -2 (released list too small).
+// past its records); a variable-length table also keeps each pair's ctx_len (entry
+// words 10-11) and its slot's sequence id (words 12-13).  A record whose (block,
+// precision) the old table stores keeps its page, unless its slot now holds a new
+// sequence (shorter, or another id); every other takes the next free page; old
+// records not kept release theirs, in pair and record order.  Returns pages taken,
+// or -1 (too few free pages), -2 (released list too small).
 int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int block, int64_t ctx_len,
-                           const int64_t* ctx_lens, const int32_t* hi, const int32_t* keep, int n_policy_heads,
+                           const int64_t* ctx_lens, const int64_t* seq_ids, const int32_t* hi, const int32_t* keep,
+                           int n_policy_heads,
                            int64_t n_pages, const uint8_t* old_table, const int32_t* free_pages, int64_t n_free,
                            uint8_t* table, int32_t* released, int64_t released_cap, int64_t* n_released) {
   std::vector<int64_t> hk, kk;
@@ -877,13 +880,20 @@ int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int 
     std::vector<int64_t> blocks, oblocks;
     std::vector<int> qm, oqm;
     record_order(c, hk[g], kk[g], blocks, qm);
-    int64_t octx = 0;
+    // the slot's sequence id (variable-length tables; 0 when none is given)
+    const int64_t sid = ctx_lens && seq_ids ? seq_ids[p / n_kv_heads] : 0;
+    int64_t octx = 0, osid = 0;
     if (old_table) {
-      if (ctx_lens) std::memcpy(&octx, old_table + 64 + 64 * p + 40, 8);
-      else std::memcpy(&octx, old_table + 32, 8);
+      if (ctx_lens) {
+        std::memcpy(&octx, old_table + 64 + 64 * p + 40, 8);
+        std::memcpy(&osid, old_table + 64 + 64 * p + 48, 8);
+      } else {
+        std::memcpy(&octx, old_table + 32, 8);
+      }
       record_order((octx - 1) / block, hk[g], kk[g], oblocks, oqm);
     }
-    const bool fresh = old_table && ctx < octx;  // a shorter sequence is a new sequence
+    // a shorter sequence, or one with another id, is a new sequence in the slot
+    const bool fresh = old_table && (ctx < octx || sid != osid);
     std::vector<int32_t> opages(oblocks.size());
     for (size_t o = 0; o < oblocks.size(); ++o)
       std::memcpy(&opages[o], old_table + 64 + 64 * P + 4 * (p * orm + static_cast<int64_t>(o)), 4);
@@ -922,7 +932,10 @@ int64_t oracle_paged_table(int batch, int n_q_heads, int n_kv_heads, int d, int 
     put_i32(e + 28, lo8 > 0 ? 1 : 0);
     put_i32(e + 32, b4.empty() ? 0 : static_cast<int32_t>(b4.front()));
     put_i32(e + 36, b4.empty() ? -1 : static_cast<int32_t>(b4.back()));
-    if (ctx_lens) put_i64(e + 40, ctx);
+    if (ctx_lens) {
+      put_i64(e + 40, ctx);
+      put_i64(e + 48, sid);
+    }
   }
   put_i32(table + 0, 0x50564B54);  // "TKVP"
   put_i32(table + 4, 4);

@@ -223,13 +223,16 @@ def test_paged_full_size(tria):
 
 def test_varlen_paged_continuous_batching(tria):
     """Three sequences in one paged cache advance at their own pace (a random subset
-    grows by one token per step) and a slot now and then starts a new, shorter
-    sequence.  Each step: host table from the previous one, the packer writes only
+    grows by one token per step) and a slot now and then starts a new sequence with
+    other keys and values, shorter or longer than the one it held, under a new
+    sequence id.  Each step: host table from the previous one, the packer writes only
     what changed, and decode equals the contiguous variable-length decode of the same
-    lengths bit for bit; every 25 steps the held pages equal the oracle's records."""
+    lengths and contents bit for bit; every 25 steps the held pages equal the oracle's
+    records."""
     b, hq, hk, d, n, blk = 3, 8, 2, 128, 700, 64
     cfg = synth.Config("paged-varlen", b, hq, hk, d, n, blk, seed=79, decode=True)
     k, v, q = synth.make_decode_inputs(cfg)
+    k_alt, v_alt, _ = synth.make_decode_inputs(cfg.scaled(seed=80))   # contents of new sequences
     hi, keep = np.array([1, 3], np.int32), np.array([4, 8], np.int32)
     dd = tria.make_dims(b, hq, hk, d, blk, n)
     page = tria.paged_page_bytes(dd)
@@ -241,11 +244,24 @@ def test_varlen_paged_continuous_batching(tria):
     kd, vd, qd = dev(k), dev(v), dev(q)
     sm = 1.0 / math.sqrt(d)
     lens = np.array([1, 100, 250], np.int64)
+    ids = np.arange(b, dtype=np.int64)
+    k, v = k.copy(), v.copy()      # the slots' current contents (host copies for the oracle)
+
+    def restart(slot, length):
+        """A new sequence in `slot`: other keys and values, a new id."""
+        k[slot], k_alt[slot] = k_alt[slot].copy(), k[slot].copy()
+        v[slot], v_alt[slot] = v_alt[slot].copy(), v[slot].copy()
+        kd[slot].copy_(dev(k[slot:slot + 1])[0])
+        vd[slot].copy_(dev(v[slot:slot + 1])[0])
+        ids[slot] += 10
+        lens[slot] = length
+
     old, old_dev = None, None
     for step in range(150):
         if step % 25 == 0:
             print(f"[case] paged varlen step {step} lens {lens.tolist()}", flush=True)
-        table, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, np.array(free, np.int32), old)
+        table, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, np.array(free, np.int32), old,
+                                                  seq_ids=ids)
         free = free[used:] + list(rel)
         tdev = torch.from_numpy(table).cuda()
         tria.pack_kv_cache_paged(dd, hi, keep, lens, kd, vd, tdev, pool, old_table=old_dev)
@@ -262,7 +278,10 @@ def test_varlen_paged_continuous_batching(tria):
         last = (lens.copy(), out.cpu().numpy())
         lens = np.minimum(lens + (rng.random(b) < 0.7), n)
         if step in (60, 110):
-            lens[step % b] = 5 + step % 40       # a new sequence in this slot
+            restart(step % b, 5 + step % 40)                    # a new, shorter sequence
+        if step in (40, 90):
+            slot = int(np.argmin(lens))
+            restart(slot, min(n, int(lens[slot]) + 150))         # a new, longer sequence
     # the last step against the oracle's decode of each sequence alone
     for i in range(b):
         r = oracle.decode(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, int(last[0][i]), sm)

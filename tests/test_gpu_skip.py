@@ -37,6 +37,17 @@ def parse_summaries(buf: torch.Tensor, pairs: int, rmax: int, d: int):
     return hdr, h64, lo, hi, smax, pad, nmax
 
 
+def expected_stamps(cache: torch.Tensor, pairs: int, rmax: int, blk: int, ctx_of_pair) -> np.ndarray:
+    """The index's per-slot stamps: the pair's current block + 1 on its stored records
+    (n8 + n4 from the cache directory), 0 on unused slots."""
+    dirs = cache[:64 + 64 * pairs].cpu().numpy()
+    st = np.zeros((pairs, rmax), np.int32)
+    for p in range(pairs):
+        n8, n4 = (int(x) for x in dirs[64 + 64 * p + 8:64 + 64 * p + 16].view(np.int32))
+        st[p, :n8 + n4] = (int(ctx_of_pair(p)) - 1) // blk + 1
+    return st
+
+
 SKIP_CASES = [
     # (b, hq, hk, d, n, blk, ctx, hi, keep)  policies per KV head
     (2, 8, 2, 128, 1300, 128, 1300, [0, 2], [3, 10]),
@@ -69,11 +80,12 @@ def test_summaries_and_masks_match_oracle(tria, case):
     rmax = (ctx - 1) // blk + 1
     assert sums.numel() == 64 + b * hk * rmax * (2 * d + 16)
     hdr, h64, lo, up, smax, pad, nmax = parse_summaries(sums, b * hk, rmax, d)
-    assert list(hdr[:8]) == [0x4D534254, 1, b * hk, rmax, d, blk, rmax - 1, 0]
+    assert list(hdr[:8]) == [0x4D534254, 2, b * hk, rmax, d, blk, rmax - 1, 0]
     assert h64[4] == cache.numel() and not h64[5:].any()
     rlo, rup, rsmax, rnmax = oracle.block_summaries(k, hi, keep, hq, blk, ctx)
     assert np.array_equal(lo, rlo) and np.array_equal(up, rup)
-    assert np.array_equal(smax, rsmax) and np.array_equal(nmax, rnmax) and not pad.any()
+    assert np.array_equal(smax, rsmax) and np.array_equal(nmax, rnmax)
+    assert np.array_equal(pad, expected_stamps(cache, b * hk, rmax, blk, lambda p: ctx))
     sm = 1.0 / math.sqrt(d)
     thd = torch.from_numpy(th).cuda()
     masks = tria.skip_masks(dd, cache, ctx, sums, dev(q), thd, sm).cpu().numpy().view(np.uint32)
@@ -217,6 +229,7 @@ def test_skip_over_varlen_cache(tria):
     rmax = (n - 1) // blk + 1
     hdr, h64, lo, up, smax, pad, nmax = parse_summaries(sums, b * hk, rmax, d)
     assert hdr[6] == -1
+    assert np.array_equal(pad, expected_stamps(cache, b * hk, rmax, blk, lambda p: lens[p // hk]))
     for i in range(b):
         ctx = int(lens[i])
         rlo, rup, rsmax, rnmax = oracle.block_summaries(k[i:i + 1], hi, keep, hq, blk, ctx)
@@ -226,6 +239,40 @@ def test_skip_over_varlen_cache(tria):
         assert np.array_equal(smax[sl, :rr], rsmax) and np.array_equal(nmax[sl, :rr], rnmax), i
         ref = oracle.decode_skip(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, ctx, th[i:i + 1], sm)
         assert_close(out[i:i + 1].cpu().numpy(), ref, f"varlen skip sequence {i} (ctx {ctx})")
+
+
+def test_stale_varlen_index_gives_nan(tria):
+    """A variable-length index reused after a sequence that is not the longest moved to
+    another block with the same record count (so the cache's size is unchanged): the
+    stamps of that sequence's slots no longer match, so the index does not validate
+    and the whole output is NaN, as for any index that does not validate; with a
+    fresh index every output is finite."""
+    b, hq, hk, d, n, blk = 4, 8, 2, 128, 1300, 128
+    hi, keep = np.array([1, 1], np.int32), np.array([1, 1], np.int32)   # int8 {0, c-1, c} for c >= 2
+    cfg = synth.Config("skip stale", b, hq, hk, d, n, blk, seed=69, decode=True)
+    k, v, q, th = synth.make_skip_decode_inputs(cfg)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    sm = 1.0 / math.sqrt(d)
+    thd = torch.from_numpy(th).cuda()
+    kd, vd, qd = dev(k), dev(v), dev(q)
+    for old_lens, new_lens, moved in (([1300, 300, 700, 257], [1300, 400, 700, 257], 1),   # 300 -> 400: block 2 -> 3
+                                      ([1300, 300, 700, 257], [1300, 300, 450, 257], 2)):  # restart 700 -> 450: 5 -> 3
+        print(f"[case] stale varlen index {old_lens} -> {new_lens}", flush=True)
+        c_old = tria.pack_kv_cache_varlen(dd, hi, keep, np.array(old_lens, np.int64), kd, vd)
+        stale = tria.build_block_summaries_varlen(dd, c_old)
+        c_new = tria.pack_kv_cache_varlen(dd, hi, keep, np.array(new_lens, np.int64), kd, vd)
+        assert c_new.numel() == c_old.numel()
+        fresh = tria.build_block_summaries_varlen(dd, c_new)
+        got = tria.decode_skip_varlen(dd, c_new, stale, qd, thd, sm)
+        want = tria.decode_skip_varlen(dd, c_new, fresh, qd, thd, sm)
+        torch.cuda.synchronize()
+        got, want = got.cpu().numpy(), want.cpu().numpy()
+        assert np.isnan(got).all(), moved
+        assert np.isfinite(want).all()
+        for i in range(b):   # the fresh index against the oracle, sequence by sequence
+            ctx = int(new_lens[i])
+            ref = oracle.decode_skip(k[i:i + 1], v[i:i + 1], q[i:i + 1], hi, keep, blk, ctx, th[i:i + 1], sm)
+            assert_close(want[i:i + 1], ref, f"fresh index, sequence {i} (ctx {ctx})")
 
 
 def test_skip_over_varlen_paged_cache(tria):

@@ -66,8 +66,9 @@ def test_paged_table_validation():
 
 def test_varlen_paged_table_matches_oracle():
     """Sequences of one batch advance at their own pace (continuous batching): each step
-    a random subset grows by one token, and now and then a slot starts a new, shorter
-    sequence (its old pages all released).  Library table == oracle table every step."""
+    a random subset grows by one token, and now and then a slot starts a new sequence,
+    shorter or longer than the one it held, under a new sequence id (its old pages all
+    released, none reused).  Library table == oracle table every step."""
     b, hq, hk, d, blk = 4, 8, 2, 64, 64
     hi, keep = np.array([1, 2], np.int32), np.array([5, 9], np.int32)
     dd = tria.make_dims(b, hq, hk, d, blk, 2000)
@@ -75,17 +76,39 @@ def test_varlen_paged_table_matches_oracle():
     n_pages = 400
     free = list(rng.permutation(n_pages).astype(np.int32))
     lens = np.array([1, 60, 64, 300], np.int64)
+    ids = np.arange(b, dtype=np.int64)
+    P = b * hk
     old = old_ref = None
+    restarted = None
+    n_longer = 0
     for step in range(260):
-        t, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, free, old)
-        r, rused, rrel = oracle.paged_table(b, hq, hk, d, blk, lens, hi, keep, n_pages, old_ref, free)
+        t, used, rel = tria.build_paged_table(dd, hi, keep, lens, n_pages, free, old, seq_ids=ids)
+        r, rused, rrel = oracle.paged_table(b, hq, hk, d, blk, lens, hi, keep, n_pages, old_ref, free, seq_ids=ids)
         assert np.array_equal(t, r), step
         assert used == rused and np.array_equal(rel, rrel), step
+        ents = t[64:64 + 64 * P].reshape(P, 64)
+        assert np.array_equal(ents[:, 48:56].view(np.int64)[:, 0], np.repeat(ids, hk)), step
+        if restarted is not None:   # the restarted slot's pairs hold none of their old pages
+            rm, orm = t[:64].view(np.int32)[6], old[:64].view(np.int32)[6]
+            new_pages = t[64 + 64 * P:].view(np.int32).reshape(P, rm)
+            old_pages = old[64 + 64 * P:].view(np.int32).reshape(P, orm)
+            for p in range(restarted * hk, (restarted + 1) * hk):
+                held, before = set(new_pages[p][new_pages[p] >= 0]), set(old_pages[p][old_pages[p] >= 0])
+                assert not held & before and before <= set(rel.tolist()), (step, p)
+            restarted = None
         free = free[used:] + list(rel)
         old, old_ref = t, r
         grow = rng.random(b) < 0.7
         lens = lens + grow
         if step % 37 == 36:
-            lens[step % b] = 1 + step % 50        # a new sequence in this slot
+            lens[step % b] = 1 + step % 50        # a new, shorter sequence in this slot
+            ids[step % b] += 100
+            restarted = step % b
+        elif step % 29 == 28 and lens[(step + 1) % b] < 1700:
+            restarted = (step + 1) % b            # a new, longer sequence in this slot
+            lens[restarted] += 1 + int(rng.integers(1, 250))
+            ids[restarted] += 1000
+            n_longer += 1
+    assert n_longer >= 5
     hdr = t[:64].view(np.int32)
     assert hdr[7] == -1 and t[32:40].view(np.int64)[0] == 0
