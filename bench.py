@@ -1,21 +1,26 @@
 """Benchmark of the block-sparse mixed-precision attention path on one MI355X.
 
-A step is one pass of the whole path over one batch of the Llama-3-8B-shaped
-layer (b=1, 32 query / 8 KV heads, d=128, n=8192, block 128, seeded policies
-hi ~ U[1,8], keep ~ U[hi,64], K with four x8 outlier channels):
+A step is one pass of the whole path over one batch of the long-prefill workload
+(the largest of the path's workloads: b=1, 32 query / 8 KV heads, d=128,
+n=65536, block 128, seeded policies hi ~ U[2,16], keep ~ U[hi,128], K with four
+x8 outlier channels):
   policy expansion (host) + schedule upload, Q/K quantisation, fused prefill,
   compressed-cache packing for the last position, one-token decode.
 `value` is whole-step prompt tokens per second with inputs already in HBM.
 
 The JSON line also carries
-  * roofline: the prefill kernel (the dominant one) against the MFMA roofline,
-    from its average launch time measured with HIP events on its stream;
+  * roofline: the prefill kernel (the dominant one) on the step's workload against
+    the MFMA roofline, from its average launch time measured with HIP events on
+    its stream;
+  * prefill_workloads: the same prefill measurement on the Llama-3-8B-shaped layer
+    (n=8192) and the batched mixed-policy workload (b=4, 28/4 heads, n=16384);
   * decode: the decode kernels on the decode workload (b=16, ctx 32768) against
     8 TB/s, with the last-level cache flushed between launches;
-  * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+  * cpu_baseline: the CPU oracle timed on a bounded sample of the step's workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prefill|decode|copy]  (--only is for profiler runs)
+       [--workload long_prefill|llama3_8b_layer|batched_mixed]
+       [--only prefill|decode|skip|paged|copy|step]  (--only is for profiler runs)
 """
 import argparse
 import ctypes as C
@@ -35,8 +40,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 
 # HBM traffic of the prefill kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE passes,
-# kept with the source hash of the kernel it was measured on
-PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_kernel.llama3_8b_n8192.hbm_traffic.txt")
+# per workload, kept with the source hash of the kernel it was measured on
+PREFILL_TRAFFIC = {
+    "long_prefill": os.path.join(ROOT, "profiles", "prefill_kernel.long_prefill_n65536.hbm_traffic.txt"),
+    "llama3_8b_layer": os.path.join(ROOT, "profiles", "prefill_kernel.llama3_8b_n8192.hbm_traffic.txt"),
+    "batched_mixed": os.path.join(ROOT, "profiles", "prefill_kernel.batched_mixed_b4_n16384.hbm_traffic.txt"),
+}
 PREFILL_SOURCES = [os.path.join(ROOT, "block_sparse_mixed_head_amd", "csrc", f)
                    for f in ("prefill.hip", "device_common.h", "kernels.h")]
 
@@ -50,13 +59,14 @@ def source_hash(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """Bytes per prefill launch from the committed counter summary (FETCH_SIZE x
-    fetch factor + WRITE_SIZE x write factor, factors from a plain 1 GiB copy), or
-    None when the summary is missing or the kernel source changed since."""
+def measured_traffic(workload: str):
+    """Bytes per prefill launch from the committed counter summary of the workload
+    (FETCH_SIZE x fetch factor + WRITE_SIZE x write factor, factors from a plain
+    1 GiB copy), or None when the summary is missing or the kernel source changed
+    since."""
     try:
         kv = {}
-        with open(PREFILL_TRAFFIC) as f:
+        with open(PREFILL_TRAFFIC[workload]) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -76,8 +86,22 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", choices=["prefill", "decode", "skip", "paged", "copy", "step"], default=None)
+    p.add_argument("--workload", choices=["long_prefill", "llama3_8b_layer", "batched_mixed"],
+                   default="long_prefill", help="the step's prefill workload")
     p.add_argument("--reps", type=int, default=20)
     return p.parse_args()
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kept_pairs(units: np.ndarray, block: int, n: int) -> int:
@@ -169,32 +193,35 @@ def main():
         print(msg, file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------ step workload
-    cfg = synth.CONFIGS["llama3_8b_layer"]
+    cfg = synth.CONFIGS[args.workload]
     b, hq, hk, d, n, blk = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.block
     sm = 1.0 / math.sqrt(d)
-    log(f"[bench] generating {cfg.name}")
-    qh, kh, vh = synth.make_prefill_inputs(cfg)
-    hi, keep = cfg.policy()
-    q, k, v = dev(qh), dev(kh), dev(vh)
-    dims = tria.make_dims(b, hq, hk, d, blk, n)
-    sched_np = tria.build_policy(dims, hi, keep)
-    units = sched_np[16:].reshape(-1, 8)
-    W = kept_pairs(units, blk, n)
-    sched_bytes = sched_np.nbytes
-    pinned = [torch.empty(sched_bytes, dtype=torch.uint8).pin_memory() for _ in range(2)]
-    pinned_ev = [torch.cuda.Event() for _ in range(2)]
-    sched_dev = torch.empty(sched_bytes, dtype=torch.uint8, device="cuda")
-    qz = tria.quantize_qk(dims, q, k)
-    out = torch.empty((b, hq, n, d), dtype=torch.float32, device="cuda")
-    ctx = n
-    cache_n = tria.kv_cache_bytes(dims, hi, keep, ctx)
-    cache = torch.empty(cache_n, dtype=torch.uint8, device="cuda")
-    ws = torch.empty(tria.decode_workspace_bytes(dims, ctx), dtype=torch.uint8, device="cuda")
-    qdec = q[:, :, ctx - 1].contiguous()
-    dout = torch.empty((b, hq, d), dtype=torch.float32, device="cuda")
-    hi_c = np.ascontiguousarray(hi, np.int32)
-    keep_c = np.ascontiguousarray(keep, np.int32)
-    need = C.c_size_t(0)
+    qh = kh = vh = None
+    if args.only in (None, "step", "prefill"):
+        log(f"[bench] generating {cfg.name}")
+        qh, kh, vh = synth.make_prefill_inputs(cfg)
+        hi, keep = cfg.policy()
+        q, k, v = dev(qh), dev(kh), dev(vh)
+        dims = tria.make_dims(b, hq, hk, d, blk, n)
+        sched_np = tria.build_policy(dims, hi, keep)
+        units = sched_np[16:].reshape(-1, 8)
+        W = kept_pairs(units, blk, n)
+        sched_bytes = sched_np.nbytes
+        pinned = [torch.empty(sched_bytes, dtype=torch.uint8).pin_memory() for _ in range(2)]
+        pinned_ev = [torch.cuda.Event() for _ in range(2)]
+        sched_dev = torch.empty(sched_bytes, dtype=torch.uint8, device="cuda")
+        qz = tria.quantize_qk(dims, q, k)
+        out = torch.empty((b, hq, n, d), dtype=torch.float32, device="cuda")
+        ctx = n
+        cache_n = tria.kv_cache_bytes(dims, hi, keep, ctx)
+        cache = torch.empty(cache_n, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(tria.decode_workspace_bytes(dims, ctx), dtype=torch.uint8, device="cuda")
+        qdec = q[:, :, ctx - 1].contiguous()
+        dout = torch.empty((b, hq, d), dtype=torch.float32, device="cuda")
+        hi_c = np.ascontiguousarray(hi, np.int32)
+        keep_c = np.ascontiguousarray(keep, np.int32)
+        need = C.c_size_t(0)
+        sched_dev.copy_(torch.from_numpy(sched_np.view(np.uint8)))
 
     def step(i: int):
         buf = pinned[i % 2]
@@ -233,7 +260,24 @@ def main():
         ts = np.array(ts)
         return float(np.mean(ts)), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
-    sched_dev.copy_(torch.from_numpy(sched_np.view(np.uint8)))
+    def prefill_stats(name, dims_, sched_, qz_, v_, out_, W_, b_, hq_, d_, n_, reps):
+        """Prefill alone on one workload: HIP-event times and the MFMA roofline."""
+        mean, med, p10, p90 = event_avg(lambda: tria.prefill(dims_, sched_, qz_, v_, 1.0 / math.sqrt(d_), out=out_),
+                                        reps)
+        ops = 4.0 * d_ * W_                                # 2dW int8 ops + 2dW bf16 flops
+        t_roof = 2.0 * d_ * W_ / (PEAK_INT8_TOPS * 1e12) + 2.0 * d_ * W_ / (PEAK_BF16_TFLOPS * 1e12)
+        achieved = ops / mean / 1e12
+        res = {"workload": synth.CONFIGS[name].name, "ms": mean * 1e3, "ms_median": med * 1e3, "ms_p10": p10 * 1e3,
+               "ms_p90": p90 * 1e3, "tokens_per_s": b_ * n_ / mean,
+               "dense_equiv_tflops": 4.0 * b_ * hq_ * d_ * n_ * n_ / 2 / mean / 1e12,
+               "effective_tflops": achieved, "frac_of_roofline": t_roof / mean,
+               "frac_of_int8_peak": achieved / PEAK_INT8_TOPS, "kept_pairs": W_,
+               "kept_density": W_ / (b_ * hq_ * n_ * (n_ + 1) / 2), "t_roof_ms": t_roof * 1e3,
+               "traffic_bytes": measured_traffic(name)}
+        log(f"[bench] prefill {name}: {mean * 1e3:.3f} ms, {achieved:.1f} T mixed ops/s, "
+            f"frac {t_roof / mean:.3f} (roofline {t_roof * 1e3:.3f} ms)")
+        return res
+
     if args.only == "prefill":   # profiler run: a few prefill launches only, each
         for _ in range(args.steps):   # synchronised as in the timed loop below
             tria.prefill(dims, sched_dev, qz, v, sm, out=out)
@@ -249,8 +293,10 @@ def main():
         print("done", flush=True)
         return
 
+    prefill_main = None
+    prefill_others = {}
     if args.only in (None, "step"):
-        log(f"[bench] step: warmup {args.warmup}, timed {args.steps}")
+        log(f"[bench] step on {cfg.name}: warmup {args.warmup}, timed {args.steps}")
         sec_eager = timed_loop(step, args.warmup, args.steps)
         log(f"[bench] step (eager launches) {sec_eager * 1e3:.3f} ms")
         # The same step with its device work (schedule upload, quantise, prefill, pack,
@@ -295,16 +341,33 @@ def main():
         log(f"[bench] step (graph launches) {sec * 1e3:.3f} ms -> {value:.4g} tokens/s")
 
         # per-kernel device times (events on the launch stream)
-        p_mean, p_med, p_p10, p_p90 = event_avg(lambda: tria.prefill(dims, sched_dev, qz, v, sm, out=out), args.reps)
+        prefill_main = prefill_stats(args.workload, dims, sched_dev, qz, v, out, W, b, hq, d, n, args.reps)
         q_mean = event_avg(lambda: tria.quantize_qk(dims, q, k, out=qz), args.reps)[0]
         k_mean = event_avg(lambda: tria.pack_kv_cache(dims, hi, keep, ctx, k, v, cache=cache), args.reps)[0]
         d_mean = event_avg(lambda: tria.decode(dims, cache, ctx, qdec, sm, out=dout, workspace=ws), args.reps)[0]
-        ops = 4.0 * d * W                                  # 2dW int8 ops + 2dW bf16 flops
-        t_roof = 2.0 * d * W / (PEAK_INT8_TOPS * 1e12) + 2.0 * d * W / (PEAK_BF16_TFLOPS * 1e12)
-        peak_blend = ops / t_roof / 1e12                   # = 3333 T(FL)OP/s for equal op counts
-        achieved = ops / p_mean / 1e12
-        dense_equiv = 4.0 * b * hq * d * n * n / 2 / p_mean / 1e12
-        log(f"[bench] prefill {p_mean * 1e3:.3f} ms, {achieved:.1f} T mixed ops/s, frac {t_roof / p_mean:.3f}")
+        del graphs, q, k, v, qz, out, cache, ws, sched_dev
+        torch.cuda.empty_cache()
+
+        # the other prefill workloads, prefill alone (their inputs drawn from the same recipe)
+        for name in ("llama3_8b_layer", "long_prefill", "batched_mixed"):
+            if name == args.workload:
+                continue
+            c = synth.CONFIGS[name]
+            log(f"[bench] generating {c.name}")
+            qo, ko, vo = (dev(x) for x in synth.make_prefill_inputs(c))
+            ho, kpo = c.policy()
+            do = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
+            so = tria.build_policy(do, ho, kpo)
+            Wo = kept_pairs(so[16:].reshape(-1, 8), c.block, c.seq_len)
+            sdo = torch.from_numpy(so).cuda()
+            qzo = tria.quantize_qk(do, qo, ko)
+            oo = torch.empty((c.batch, c.n_q_heads, c.seq_len, c.head_dim), dtype=torch.float32, device="cuda")
+            for _ in range(2):
+                tria.prefill(do, sdo, qzo, vo, 1.0 / math.sqrt(c.head_dim), out=oo)
+            prefill_others[name] = prefill_stats(name, do, sdo, qzo, vo, oo, Wo, c.batch, c.n_q_heads, c.head_dim,
+                                                 c.seq_len, args.reps)
+            del qo, ko, vo, qzo, oo, sdo
+            torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode workload (b16, ctx 32768)
     dec = None
@@ -544,6 +607,7 @@ def main():
     del rd_src
     i8, bf, rd = w_i8 / t_i8 / 1e12, w_bf / t_bf / 1e12, w_rd / t_rd / 1e9
     blend = 2.0 / (1.0 / i8 + 1.0 / bf)  # equal int8 ops and bf16 flops, in series
+    achieved = prefill_main["effective_tflops"]
     ceilings = {
         "mfma_i8_tops": i8, "mfma_bf16_tflops": bf, "mfma_series_blend_tflops": blend, "hbm_read_gbps": rd,
         "prefill_frac": achieved / blend,
@@ -560,16 +624,16 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        # whole query heads of the same layer, one after another, until about 10 s of
-        # work is done (at most the 32 heads of the layer); scaled by kept pairs
+        # whole query heads of the step's workload, one after another, until about 10 s
+        # of work is done (at most all heads); scaled by kept pairs to the whole step
         G = hq // hk
         t_sample, w_sample, heads = 0.0, 0, 0
         for h0 in range(hq):
             sel = units[(units[:, 1] == h0) & (units[:, 0] == 0)]
             g0 = h0 // G
             t0 = time.perf_counter()
-            oracle.prefill(qh[:, h0:h0 + 1], kh[:, g0:g0 + 1], vh[:, g0:g0 + 1], hi[h0:h0 + 1], keep[h0:h0 + 1],
-                           blk, sm)
+            oracle.prefill(qh[:1, h0:h0 + 1], kh[:1, g0:g0 + 1], vh[:1, g0:g0 + 1], hi[h0:h0 + 1],
+                           keep[h0:h0 + 1], blk, sm)
             t_sample += time.perf_counter() - t0
             w_sample += kept_pairs(sel, blk, n)
             heads += 1
@@ -577,11 +641,13 @@ def main():
                 break
         est_total = t_sample * W / w_sample
         cpu = {"value": b * n / est_total, "unit": "tokens/s", "cores": oracle.nthreads(), "kind": "oracle",
-               "sample": f"oracle prefill (quantisation + attention) of {heads} of the layer's {hq} query heads, "
-                         f"all query blocks ({w_sample:.3g} of {W:.3g} kept pairs), took {t_sample:.2f} s; "
-                         f"scaled by kept pairs to the whole workload; pack/decode are <1% of its work and not "
-                         f"timed"}
-        log(f"[bench] cpu oracle sample {heads} heads {t_sample:.2f} s on {oracle.nthreads()} threads")
+               "cpu_model": cpu_model(),
+               "sample": f"oracle prefill (quantisation + attention) of {heads} of the workload's {hq} query heads "
+                         f"(batch element 0), all query blocks ({w_sample:.3g} of {W:.3g} kept pairs), took "
+                         f"{t_sample:.2f} s on {oracle.nthreads()} threads; the whole step's time is extrapolated "
+                         f"by kept pairs (est. {est_total:.1f} s); pack/decode are <1% of its work and not timed"}
+        log(f"[bench] cpu oracle sample {heads} heads {t_sample:.2f} s on {oracle.nthreads()} threads "
+            f"-> est. {est_total:.1f} s for the step's prefill")
 
     line = {
         "metric": "prefill tokens/s + decode HBM GB/s, block-sparse int8/int4 attn; % roofline",
@@ -599,17 +665,16 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16, K outlier channels x8, seeded per-head policies)",
         "config": {"workload": cfg.name, "batch": b, "seq_len": n, "n_q_heads": hq, "n_kv_heads": hk,
                    "head_dim": d, "block": blk, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved, "peak": peak_blend,
-                     "unit": "TFLOP/s", "frac": achieved / peak_blend, "traffic": measured_traffic(),
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": achieved,
+                     "peak": 4.0 * d * W / (prefill_main["t_roof_ms"] * 1e-3) / 1e12,
+                     "unit": "TFLOP/s", "frac": prefill_main["frac_of_roofline"],
+                     "traffic": prefill_main["traffic_bytes"],
                      "work": f"4*d*W mixed ops per launch: 2dW int8 ops (QK^T) + 2dW bf16 flops (P.V), "
                              f"W = {W} kept causal pairs; peak = int8 {PEAK_INT8_TOPS:.0f} and bf16 "
                              f"{PEAK_BF16_TFLOPS:.0f} T/s combined in series"},
-        "prefill": {"ms": p_mean * 1e3, "ms_median": p_med * 1e3, "ms_p10": p_p10 * 1e3, "ms_p90": p_p90 * 1e3,
-                    "tokens_per_s": b * n / p_mean, "dense_equiv_tflops": dense_equiv,
-                    "effective_tflops": achieved, "frac_of_int8_peak": achieved / PEAK_INT8_TOPS,
-                    "kept_pairs": W,
-                    "kept_density": W / (b * hq * n * (n + 1) / 2)},
-        "kernels_ms": {"quantize": q_mean * 1e3, "prefill": p_mean * 1e3, "pack": k_mean * 1e3,
+        "prefill": prefill_main,
+        "prefill_workloads": prefill_others,
+        "kernels_ms": {"quantize": q_mean * 1e3, "prefill": prefill_main["ms"], "pack": k_mean * 1e3,
                        "decode_step_workload": d_mean * 1e3},
         "decode": dec,
         "measured_ceilings": ceilings,

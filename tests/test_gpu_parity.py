@@ -19,6 +19,21 @@ pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-2
 MEAN_REL = 1e-3
+# The base-2 log-sum-exp M + log2(l) (an optional output with no stated tolerance):
+# the kernel forms t in fp32 and the oracle in double, so a weight whose fp32 value
+# lies within rounding of a bf16 rounding boundary can round one way on the GPU and
+# the other in the oracle.  One such flip changes l by at most 2^-8 of that weight,
+# hence the LSE by at most log2(1 + 2^-8) = 5.6e-3 when that weight dominates its
+# row.  Bound: 1e-2 on every row (room for about two flips of a dominant weight),
+# and 1e-5 on the mean over rows (flips are rare).
+LSE_MAX = 1e-2
+LSE_MEAN = 1e-5
+
+
+def assert_lse_close(gpu: np.ndarray, ref: np.ndarray, what: str):
+    diff = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    print(f"[parity] {what} LSE: max|diff|={diff.max():.3e} mean={diff.mean():.3e}", flush=True)
+    assert diff.max() <= LSE_MAX and diff.mean() <= LSE_MEAN, (what, diff.max(), diff.mean())
 
 
 @pytest.fixture(scope="module")
@@ -124,7 +139,7 @@ def test_prefill_small_every_output(tria, case):
     out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
     ref, rlse = oracle.prefill(q, k, v, hi, keep, blk, 1.0 / math.sqrt(d), with_lse=True)
     assert_close(out.cpu().numpy(), ref, f"prefill {case}")
-    assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
+    assert_lse_close(lse.cpu().numpy(), rlse, "prefill")
 
 
 VARLEN = [
@@ -158,7 +173,7 @@ def test_prefill_varlen_every_output(tria, case):
         ref, rlse = oracle.prefill(q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1], hi, keep, blk,
                                    1.0 / math.sqrt(d), with_lse=True)
         assert_close(got[:, :, s0:s1], ref, f"varlen {case} sequence {i}")
-        assert np.abs(glse[:, :, s0:s1] - rlse).max() < 1e-3
+        assert_lse_close(glse[:, :, s0:s1], rlse, f"varlen sequence {i}")
 
 
 def test_prefill_integer_inputs_and_determinism(tria):
@@ -311,7 +326,7 @@ def test_prefill_full_size_every_output(tria):
     out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
     ref, rlse = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), with_lse=True)
     assert_close(out.cpu().numpy(), ref, f"prefill {cfg.name} (every output)")
-    assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
+    assert_lse_close(lse.cpu().numpy(), rlse, "prefill")
 
 
 @pytest.mark.parametrize("cid", ["long_prefill", "batched_mixed"])
@@ -336,7 +351,7 @@ def test_prefill_full_size_sampled(tria, cid):
         gl.append(l_np[bb, h, r0:r1])
         wl.append(rlse[bb, h, r0:r1])
     assert_close(np.concatenate(got), np.concatenate(want), f"prefill {cfg.name} ({len(units)} sampled units)")
-    assert np.abs(np.concatenate(gl) - np.concatenate(wl)).max() < 1e-3
+    assert_lse_close(np.concatenate(gl), np.concatenate(wl), f"prefill {cfg.name}")
     assert np.isfinite(o_np).all() and np.isfinite(l_np).all()
 
 
@@ -402,7 +417,7 @@ def test_allocator_policy_through_prefill_and_decode(tria):
     out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
     ref, rlse = oracle.prefill(q, k, v, hi, keep, blk, 1.0 / math.sqrt(d), with_lse=True)
     assert_close(out.cpu().numpy(), ref, "prefill under the allocator's policy")
-    assert np.abs(lse.cpu().numpy() - rlse).max() < 1e-3
+    assert_lse_close(lse.cpu().numpy(), rlse, "prefill")
     ctx = n - 5
     cache = tria.pack_kv_cache(dd, hi, keep, ctx, dev(k), dev(v))
     assert np.array_equal(cache.cpu().numpy(), oracle.pack_cache(k, v, hi, keep, hq, blk, ctx))
