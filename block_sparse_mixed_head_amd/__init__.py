@@ -247,6 +247,18 @@ def decode(d: Dims, cache: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale
     return out
 
 
+def decode_noalloc(d: Dims, cache: torch.Tensor, ctx_len: int, q: torch.Tensor, sm_scale: float,
+                   out: torch.Tensor) -> torch.Tensor:
+    """decode with the library's own scratch (tria_decode_noalloc): no workspace, and
+    nothing allocated here either (the caller passes out)."""
+    b, hq, hd = d.batch, d.n_q_heads, d.head_dim
+    _require(q, torch.bfloat16, (b, hq, hd), "q")
+    _require(out, torch.float32, (b, hq, hd), "out")
+    check(_lib.lib.tria_decode_noalloc(C.byref(d), _ptr(cache), cache.numel(), ctx_len, _ptr(q), float(sm_scale),
+                                       _ptr(out), _stream(q.device)))
+    return out
+
+
 def decode_varlen(d: Dims, cache: torch.Tensor, q: torch.Tensor, sm_scale: float,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Decode over a pack_kv_cache_varlen cache: each sequence at its own length."""

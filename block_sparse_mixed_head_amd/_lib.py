@@ -52,6 +52,7 @@ def _load() -> C.CDLL:
         "tria_check_cache": (C.c_int, [D, P, sz, i64]),
         "tria_decode_workspace_bytes": (C.c_int, [D, i64, C.POINTER(sz)]),
         "tria_decode": (C.c_int, [D, P, sz, i64, P, f32, P, P, sz, P]),
+        "tria_decode_noalloc": (C.c_int, [D, P, sz, i64, P, f32, P, P]),
         "tria_policy_cost": (C.c_int, [D, i32, i32, C.c_double, C.c_double, C.POINTER(C.c_double)]),
         "tria_allocate_policy": (C.c_int, [D, i32, i32, P, C.c_double, C.c_double, C.c_double, P, P,
                                            C.POINTER(C.c_double), C.POINTER(C.c_double)]),
@@ -92,7 +93,8 @@ EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quanti
             "tria_build_policy_varlen", "tria_prefill_varlen",
             "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_update_kv_cache", "tria_check_cache",
             "tria_kv_cache_bytes_varlen", "tria_pack_kv_cache_varlen", "tria_decode_varlen",
-            "tria_decode_workspace_bytes", "tria_decode", "tria_policy_cost", "tria_allocate_policy",
+            "tria_decode_workspace_bytes", "tria_decode", "tria_decode_noalloc", "tria_policy_cost",
+            "tria_allocate_policy",
             "tria_block_summaries_bytes", "tria_build_block_summaries", "tria_skip_masks",
             "tria_decode_skip_workspace_bytes", "tria_decode_skip", "tria_paged_page_bytes", "tria_paged_table_bytes",
             "tria_build_paged_table", "tria_build_paged_table_varlen", "tria_pack_kv_cache_paged", "tria_decode_paged",

@@ -595,15 +595,15 @@ tria_status tria_decode_workspace_bytes(const tria_dims* dims, int64_t ctx_len, 
   return ok();
 }
 
-tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
-                        const void* q_bf16, float sm_scale, float* out, void* workspace, size_t ws_bytes,
-                        void* stream) {
+// The checks tria_decode and tria_decode_noalloc share (all before any HIP call);
+// *need: the workspace the call takes.
+static tria_status check_decode_call(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                                     const void* q_bf16, float sm_scale, float* out, int64_t* need) {
   tria_status st = check_dims(dims);
   if (st != TRIA_OK) return st;
   NONNULL(cache);
   NONNULL(q_bf16);
   NONNULL(out);
-  NONNULL(workspace);
   if (ctx_len < 1) return fail(TRIA_ERR_INVALID_ARG, "ctx_len must be >= 1");
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   const int G = dims->n_q_heads / dims->n_kv_heads;
@@ -614,11 +614,49 @@ tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_b
   const tria::Shape s = shape_of(dims);
   if (!tria::decode_units_fit(s, ctx_len))
     return fail(TRIA_ERR_UNSUPPORTED, "batch * n_kv_heads * ctx_len too large for one decode call");
-  const int64_t need = tria::decode_workspace_bytes(s, ctx_len);
+  *need = tria::decode_workspace_bytes(s, ctx_len);
+  return TRIA_OK;
+}
+
+tria_status tria_decode_noalloc(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                                const void* q_bf16, float sm_scale, float* out, void* stream) {
+  int64_t need = 0;
+  tria_status st = check_decode_call(dims, cache, cache_bytes, ctx_len, q_bf16, sm_scale, out, &need);
+  if (st != TRIA_OK) return st;
+  if (need > tria::decode_scratch_capacity())
+    return fail(TRIA_ERR_UNSUPPORTED,
+                "this decode needs %lld bytes of scratch; the entry point that allocates nothing holds %lld "
+                "(use tria_decode with a workspace)",
+                (long long)need, (long long)tria::decode_scratch_capacity());
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(TRIA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd);
+    if (e != hipSuccess) return fail(TRIA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if ((int)sd != cur)
+      return fail(TRIA_ERR_INVALID_ARG, "stream belongs to device %d but device %d is current", (int)sd, cur);
+  }
+  void* ws = nullptr;
+  e = tria::decode_scratch(&ws);
+  if (e != hipSuccess) return fail(TRIA_ERR_HIP, "decode scratch address: %s", hipGetErrorString(e));
+  return launched(tria::launch_decode(shape_of(dims), ctx_len, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out, ws,
+                                      false, static_cast<hipStream_t>(stream)),
+                  "decode launch");
+}
+
+tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes, int64_t ctx_len,
+                        const void* q_bf16, float sm_scale, float* out, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  int64_t need = 0;
+  tria_status st = check_decode_call(dims, cache, cache_bytes, ctx_len, q_bf16, sm_scale, out, &need);
+  if (st != TRIA_OK) return st;
+  NONNULL(workspace);
   if ((int64_t)ws_bytes < need)
     return fail(TRIA_ERR_BUFFER_TOO_SMALL, "decode workspace needs %lld bytes, got %zu", (long long)need, ws_bytes);
-  return launched(tria::launch_decode(s, ctx_len, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out, workspace,
-                                      false, static_cast<hipStream_t>(stream)),
+  return launched(tria::launch_decode(shape_of(dims), ctx_len, cache, (int64_t)cache_bytes, q_bf16, sm_scale, out,
+                                      workspace, false, static_cast<hipStream_t>(stream)),
                   "decode launch");
 }
 

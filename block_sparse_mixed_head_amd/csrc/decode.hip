@@ -33,6 +33,7 @@
 //     record; on a mismatch nothing is read and the merge writes NaN.
 #include <cfloat>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -1367,6 +1368,37 @@ hipError_t launch_t(const DecArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the decode entry point that allocates nothing: the split kernel's
+// partials and slot table live here instead of in a caller workspace.  Each device
+// holds its own copy of the array for as long as the process runs.  In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get the
+// address hipGetSymbolAddress returns on the device, kept per device below.
+namespace {
+constexpr int64_t kScratchBytes = 64LL << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+int64_t decode_scratch_capacity() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return hipSuccess;
+}
 
 int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len) {
   (void)ctx_len;  // the split is by wavefront: at most one partial per wavefront and pair boundary

@@ -68,6 +68,11 @@ int64_t decode_workspace_bytes(const Shape& s, int64_t ctx_len);
 hipError_t launch_decode(const Shape& s, int64_t ctx_len, const void* cache, int64_t cache_bytes,
                          const void* q, float sm_scale, float* out, void* workspace, bool varlen,
                          hipStream_t stream);
+// The decode's scratch for callers that cannot allocate (decode.hip): a file-scope
+// device array of decode_scratch_capacity() bytes; decode_scratch(&p) gives its
+// address on the current device (looked up once per device).
+int64_t decode_scratch_capacity();
+hipError_t decode_scratch(void** ptr);
 
 // Dynamic block skipping (decode.hip): the statistics index of a version-2 cache,
 // the keep bits of every stored record (uint32 [pairs][cur_block + 1]), and the

@@ -338,6 +338,20 @@ tria_status tria_decode_workspace_bytes(const tria_dims* dims, int64_t ctx_len, 
 tria_status tria_decode(const tria_dims* dims, const void* cache, size_t cache_bytes,
                         int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
                         void* workspace, size_t ws_bytes, void* stream);
+/* tria_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * results as tria_decode, with the workspace replaced by a library-owned device array
+ * of 64 MiB per GPU (held from the library's first use on that GPU until the process
+ * ends; it needs no initialisation).  Nothing is allocated by the call.  Every call
+ * tria_decode accepts fits, except with 32 query heads per KV head and head_dim 128
+ * above 1922 (batch, KV head) pairs: a call whose tria_decode_workspace_bytes exceeds
+ * 64 MiB returns TRIA_ERR_UNSUPPORTED before any HIP call; a stream of another device
+ * than the current one, TRIA_ERR_INVALID_ARG.  All calls on one GPU share its array, so calls that overlap
+ * on one GPU (different streams, or host threads) race: serialise them, e.g. on one
+ * stream.  Other arguments and errors as tria_decode. */
+tria_status tria_decode_noalloc(const tria_dims* dims, const void* cache, size_t cache_bytes,
+                                int64_t ctx_len, const void* q_bf16, float sm_scale, float* out,
+                                void* stream);
 tria_status tria_decode_varlen(const tria_dims* dims, const void* cache, size_t cache_bytes,
                                const void* q_bf16, float sm_scale, float* out, void* workspace,
                                size_t ws_bytes, void* stream);

@@ -163,6 +163,28 @@ def test_validation_errors(tria):
                          None) == _lib.TRIA_ERR_UNSUPPORTED
 
 
+def test_decode_noalloc_validates(tria):
+    """The decode entry point that allocates nothing rejects, before any HIP call, a
+    call whose workspace exceeds its 64 MiB scratch, and the decode's bad arguments."""
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    one = C.c_void_p(16)
+    big = tria.make_dims(2048, 32, 1, 128, 128, 4096)    # 32 query heads per KV head, 2048 pairs
+    assert tria.decode_workspace_bytes(big, 4096) > 64 << 20
+    assert L.tria_decode_noalloc(C.byref(big), one, 1 << 30, 4096, one, C.c_float(0.125), one,
+                                 None) == _lib.TRIA_ERR_UNSUPPORTED
+    assert b"64" in L.tria_last_error() or b"scratch" in L.tria_last_error()
+    ok = tria.make_dims(1922, 32, 1, 128, 128, 4096)     # the largest that fits
+    assert tria.decode_workspace_bytes(ok, 4096) <= 64 << 20
+    good = tria.make_dims(1, 2, 1, 64, 64, 512)
+    assert L.tria_decode_noalloc(C.byref(good), one, 10, 512, one, C.c_float(0.125), one,
+                                 None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL     # cache below its directory
+    assert L.tria_decode_noalloc(C.byref(good), one, 1 << 20, 0, one, C.c_float(0.125), one,
+                                 None) == _lib.TRIA_ERR_INVALID_ARG          # ctx_len
+    assert L.tria_decode_noalloc(C.byref(good), one, 1 << 20, 512, one, C.c_float(0.125), None,
+                                 None) == _lib.TRIA_ERR_INVALID_ARG          # out
+
+
 def test_peak_helpers_validate_arguments(tria):
     """The measured-ceiling helpers check their arguments before any HIP call."""
     from block_sparse_mixed_head_amd import _lib
