@@ -112,8 +112,8 @@ __device__ __forceinline__ void poison_rows(const Args& a, int64_t r0, int64_t r
 }
 
 // The share of every output row that work group i poisons when the schedule header
-// does not describe the call (or its unit names no rows): the rows split evenly over
-// the grid, so together the work groups cover the whole output.
+// does not describe the call: the rows split evenly over the grid, so together the
+// work groups cover the whole output.
 template <int D>
 __device__ __forceinline__ void poison_share(const Args& a) {
   const int64_t per = (a.rows_total + a.n_units - 1) / a.n_units;
@@ -163,15 +163,16 @@ __device__ __forceinline__ v4u buffer_desc(const void* base, int bytes) {
   return v4u{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)uni(bytes), 0x00020000u};
 }
 
-// buffer_load ... lds: every active lane's 16 (4) bytes at desc + voff + soff go to
-// LDS address lds + 16 (4) * lane.  The LDS base travels in m0, given to the asm as
+// buffer_load ... lds: every active lane's 16 (4) bytes at desc + voff go to
+// LDS address lds + 16 (4) * lane (whole offsets in voff, which the resource's range
+// check covers: bytes past the resource read as 0).  The LDS base travels in m0, given to the asm as
 // an input operand so the compiler itself loads m0 and knows it is in use.  No
 // register result; completion is counted by vmcnt, which the caller waits for before
 // the data is read (by any wave).
-__device__ __forceinline__ void dma16(v4u desc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+__device__ __forceinline__ void dma16(v4u desc, uint32_t voff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds)
+               : "v"(voff), "s"(desc), "{m0}"(lds)
                : "memory");
 }
 __device__ __forceinline__ void dma4(v4u desc, uint32_t voff, uint32_t lds) {
@@ -524,6 +525,66 @@ __device__ __forceinline__ void pv_stage(const lds_u8* vslot, const LaneOffsets<
   pv_rowsum<D, BLK>(pb, O);
 }
 
+// The work group's unit, checked: the schedule's header must describe the call and
+// the unit's record must be well formed.  A header that does not describe the call:
+// NaN over the work group's even share of all output rows (every work group does
+// the same and none computes, so the whole output is NaN).  A malformed record: NaN
+// over the rows it names (rows no other unit of a valid list holds), or nothing
+// written when it names no rows.  Either way false is returned.
+struct Unit {
+  int b, h, qb, lo8, lo4, hi4, sink, n4, ntiles, bb;
+  int64_t seq0, n;
+};
+template <int D, int BLK>
+__device__ __forceinline__ bool unit_of(const Args& a, Unit& un) {
+  // The header's first twelve words and the unit's record in one round trip (the
+  // host sized the schedule for n_units records); the empty asm keeps the five
+  // scalar loads together here rather than sunk past the header check.
+  const v4i* hp = reinterpret_cast<const v4i*>(a.header);
+  const v4i* up = reinterpret_cast<const v4i*>(a.units + 8 * (int64_t)blockIdx.x);
+  v4i h0 = hp[0], h1 = hp[1], h2 = hp[2], u0 = up[0], u1 = up[1];
+  asm volatile("" : "+s"(h0), "+s"(h1), "+s"(h2), "+s"(u0), "+s"(u1));
+  const int b = u0[0], h = u0[1], qb = u0[2], lo8 = u0[3], lo4 = u1[0], hi4 = u1[1], sink = u1[2];
+  const int n4 = hi4 - lo4 + 1;
+  const int ntiles = u1[3];
+  {  // a header that does not describe this call: NaN over every output row
+    // (compared without short-circuit branches)
+    const bool ok = (h0[0] == TRIA_SCHED_MAGIC) & (h0[1] == a.version) & (h0[2] == a.batch) & (h0[3] == a.hq) &
+                    (h1[0] == a.hkv) & (h1[1] == D) & (h1[2] == BLK) & (h1[3] == a.nb) &
+                    (h2[0] == (int32_t)a.n_units) & (h2[2] == (int32_t)(a.n & 0xFFFFFFFF)) &
+                    (h2[3] == (int32_t)(a.n >> 32));
+    if (!ok) {
+      poison_share<D>(a);
+      return false;
+    }
+  }
+  // a variable-length batch packs its sequences along the rows of one batch element:
+  // unit b is sequence b, rows [seq0, seq0 + n)
+  int64_t seq0 = 0, n = a.n;
+  int bb = b;
+  if (b >= 0 && b < a.batch && a.seqs) {  // (b checked before the sequence table is read)
+    seq0 = a.seqs[2 * b];
+    n = a.seqs[2 * b + 1];
+    bb = 0;
+  }
+  {  // a malformed record computes nothing: NaN over the rows it names, if any
+    const int64_t nbq = (n + BLK - 1) / BLK;
+    const bool rows_ok = b >= 0 && b < a.batch && seq0 >= 0 && n >= 1 && seq0 + n <= a.n && h >= 0 && h < a.hq &&
+                         qb >= 0 && qb < nbq;
+    const bool bad = !rows_ok || lo8 < 0 || lo8 > qb || sink < 0 || sink > 1 || (sink == 1 && lo8 == 0) || n4 < 0 ||
+                     (n4 > 0 && (lo4 < 1 || hi4 >= lo8)) || ntiles != (qb - lo8 + 1) + sink + n4;
+    if (bad) {
+      if (rows_ok) {
+        const int64_t r0 = ((int64_t)bb * a.hq + h) * a.n + seq0 + (int64_t)qb * BLK;
+        poison_rows<D>(a, r0, r0 + ((n - (int64_t)qb * BLK) < BLK ? (n - (int64_t)qb * BLK) : BLK));
+      }
+      return false;
+    }
+  }
+  un = Unit{b, h, qb, lo8, lo4, hi4, sink, n4, ntiles, bb, seq0, n};
+  return true;
+}
+
 template <int D, int BLK>
 __global__ void __launch_bounds__((Cfg<D, BLK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(Args a) {
@@ -543,56 +604,13 @@ prefill_kernel(Args a) {
     return (uint32_t)uni((int)(uint32_t)(uintptr_t)p);
   };
 
-  // The header's first twelve words and the unit's record in one round trip (the
-  // host sized the schedule for n_units records); the empty asm keeps the five
-  // scalar loads together here rather than sunk past the header check.
-  const v4i* hp = reinterpret_cast<const v4i*>(a.header);
-  const v4i* up = reinterpret_cast<const v4i*>(a.units + 8 * (int64_t)blockIdx.x);
-  v4i h0 = hp[0], h1 = hp[1], h2 = hp[2], u0 = up[0], u1 = up[1];
-  asm volatile("" : "+s"(h0), "+s"(h1), "+s"(h2), "+s"(u0), "+s"(u1));
-  const int b = u0[0], h = u0[1], qb = u0[2], lo8 = u0[3], lo4 = u1[0], hi4 = u1[1], sink = u1[2];
-  const int n4 = hi4 - lo4 + 1;
-  const int ntiles = u1[3];
-  {  // a header that does not describe this call: NaN over every output row
-    // (compared without short-circuit branches)
-    const bool ok = (h0[0] == TRIA_SCHED_MAGIC) & (h0[1] == a.version) & (h0[2] == a.batch) & (h0[3] == a.hq) &
-                    (h1[0] == a.hkv) & (h1[1] == D) & (h1[2] == BLK) & (h1[3] == a.nb) &
-                    (h2[0] == (int32_t)a.n_units) & (h2[2] == (int32_t)(a.n & 0xFFFFFFFF)) &
-                    (h2[3] == (int32_t)(a.n >> 32));
-    if (!ok) {
-      poison_share<D>(a);
-      return;
-    }
-  }
-  // a variable-length batch packs its sequences along the rows of one batch element:
-  // unit b is sequence b, rows [seq0, seq0 + n)
-  int64_t seq0 = 0, n = a.n;
-  int bb = b;
-  if (b >= 0 && b < a.batch && a.seqs) {  // (b checked before the sequence table is read)
-    seq0 = a.seqs[2 * b];
-    n = a.seqs[2 * b + 1];
-    bb = 0;
-  }
-  {  // a malformed record computes nothing: NaN over its rows (or, when it names no
-     // rows, over the work group's share of the output)
-    const int64_t nbq = (n + BLK - 1) / BLK;
-    const bool rows_ok = b >= 0 && b < a.batch && seq0 >= 0 && n >= 1 && seq0 + n <= a.n && h >= 0 && h < a.hq &&
-                         qb >= 0 && qb < nbq;
-    const bool bad = !rows_ok || lo8 < 0 || lo8 > qb || sink < 0 || sink > 1 || (sink == 1 && lo8 == 0) || n4 < 0 ||
-                     (n4 > 0 && (lo4 < 1 || hi4 >= lo8)) || ntiles != (qb - lo8 + 1) + sink + n4;
-    if (bad) {
-      if (rows_ok) {
-        const int64_t r0 = ((int64_t)bb * a.hq + h) * a.n + seq0 + (int64_t)qb * BLK;
-        poison_rows<D>(a, r0, r0 + ((n - (int64_t)qb * BLK) < BLK ? (n - (int64_t)qb * BLK) : BLK));
-      } else {
-        poison_share<D>(a);
-      }
-      return;
-    }
-  }
+  Unit un;
+  if (!unit_of<D, BLK>(a, un)) return;
+  const int h = un.h, qb = un.qb, lo8 = un.lo8, lo4 = un.lo4, sink = un.sink, n4 = un.n4, ntiles = un.ntiles;
+  const int64_t seq0 = un.seq0, n = un.n;
   const int g_kv = h / (a.hq / a.hkv);
-  const int64_t qrow0 = ((int64_t)bb * a.hq + h) * a.n + seq0;
-  const int64_t krow0 = ((int64_t)bb * a.hkv + g_kv) * a.n + seq0;
+  const int64_t qrow0 = ((int64_t)un.bb * a.hq + h) * a.n + seq0;
+  const int64_t krow0 = ((int64_t)un.bb * a.hkv + g_kv) * a.n + seq0;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6), lane = tid & 63;
@@ -648,7 +666,7 @@ prefill_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < C::K8N; ++j) {
       const bool skip = is4 && wave + j * C::WAVES >= C::K4_INSTR;
-      dma16(buffer_desc(reinterpret_cast<const void*>(kbase), skip ? 0 : kbytes), off, j * LO::PIECE_STEP,
+      dma16(buffer_desc(reinterpret_cast<const void*>(kbase), skip ? 0 : kbytes), off + j * LO::PIECE_STEP,
             lds_addr(kd + (wave + j * C::WAVES) * 1024));
     }
     const uint64_t sbase = (is4 ? s4u : s8u) + (uint32_t)key0 * 4;
@@ -660,7 +678,7 @@ prefill_kernel(Args a) {
     const int key0 = key0_32(st);
     const v4u rv = buffer_desc(reinterpret_cast<const void*>(vu + (uint32_t)key0 * 2 * D), rows_of(valid, key0) * 2 * D);
 #pragma unroll
-    for (int j = 0; j < C::VN; ++j) dma16(rv, lo.gv, j * LO::PIECE_STEP, lds_addr(vd + (wave + j * C::WAVES) * 1024));
+    for (int j = 0; j < C::VN; ++j) dma16(rv, lo.gv + j * LO::PIECE_STEP, lds_addr(vd + (wave + j * C::WAVES) * 1024));
   };
 
   // ---- prologue: K and scales of stages 0..2, V of stage 0; V slot 2 (read with

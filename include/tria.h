@@ -157,6 +157,13 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
  * tria_quantize_qk, and V bf16 [b][Hkv][n][d].  out fp32 [b][Hq][n][d].
  * lse (may be NULL) fp32 [b][Hq][n] receives M_i + log2(sum_j P_ij), the base-2
  * log of the softmax denominator in units of t.
+ * sched_bytes must be exactly the size the dims imply (TRIA_ERR_BUFFER_TOO_SMALL
+ * below it, TRIA_ERR_INVALID_ARG above it).  The device checks the schedule: a
+ * header that does not describe the call (magic, version, batch, heads, head_dim,
+ * block, block count, unit count, seq_len) makes every output row and LSE entry NaN;
+ * a malformed unit record computes nothing and makes the rows it names NaN (a record
+ * that names no rows writes nothing, so the rows of the unit it replaced keep what
+ * `out` held).  The kernels always exit normally.
  * Errors: TRIA_ERR_UNSUPPORTED for seq_len >= 2^31 - block (token indices are
  * 32-bit inside the kernel).
  */
