@@ -118,14 +118,14 @@ def decode_bytes(cache_bytes_total: int, batch: int, hq: int, d: int, header: in
     return (cache_bytes_total - header) + batch * hq * d * 2 + batch * hq * d * 4
 
 
-def skip_batch64(tria, c4, h4, kp4, reps, flush_caches, event_avg, log):
-    """Plain vs skipping decode on the decode workload's shapes at batch 64: keys
+def skip_at_batch(b, tria, c4, h4, kp4, reps, flush_caches, event_avg, log):
+    """Plain vs skipping decode on the decode workload's shapes at batch b: keys
     N(0,1) times one magnitude per (b, KV head, block) ~ U[0.1, 1], values and
-    queries N(0,1), thresholds 0.6-0.9 x ||q|| (torch generator, seed 64)."""
+    queries N(0,1), thresholds 0.6-0.9 x ||q|| (torch generator, seed b)."""
     import torch
-    b, hq, hk, d, n, blk = 64, c4.n_q_heads, c4.n_kv_heads, c4.head_dim, c4.seq_len, c4.block
+    hq, hk, d, n, blk = c4.n_q_heads, c4.n_kv_heads, c4.head_dim, c4.seq_len, c4.block
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(64)
+    gen.manual_seed(b)
     k = torch.empty((b, hk, n, d), dtype=torch.bfloat16, device="cuda")
     v = torch.empty_like(k)
     nb = n // blk
@@ -165,7 +165,7 @@ def skip_batch64(tria, c4, h4, kp4, reps, flush_caches, event_avg, log):
     res = {"workload": f"decode b{b} h{hq}/{hk} d{d} ctx{n} B{blk}", "cache_bytes": cache.numel(),
            "plain_us": tp * 1e6, "skip_us": ts * 1e6, "speedup": tp / ts, "bytes_read_fraction": kept / stored,
            "plain_GB_per_s": stored / tp / 1e9, "skip_GB_per_s_kept": kept / ts / 1e9}
-    log(f"[bench] batch 64: plain decode {tp * 1e6:.1f} us, skipping {ts * 1e6:.1f} us "
+    log(f"[bench] batch {b}: plain decode {tp * 1e6:.1f} us, skipping {ts * 1e6:.1f} us "
         f"({kept / stored:.3f} of the records read, x{tp / ts:.2f})")
     del cache, sums, ws, wss
     return res
@@ -565,9 +565,11 @@ def main():
             f"reads {kept_b / stored_b:.3f} of the records, head density {skip['head_density']:.3f}, "
             f"{skip['GB_per_s']:.0f} GB/s; index {sums.numel() / 1e6:.2f} MB built in {sum_t[1] * 1e6:.1f} us")
         del cache_s, sums, wss
-        # the same shapes at batch 64 (4x the cache): inputs drawn on the GPU from a
-        # seeded torch generator (timing only; parity at this batch is not checked)
-        skip["batch64"] = skip_batch64(tria, c4, h4, kp4, args.reps, flush_caches, event_avg, log)
+        # the same shapes at batch 32 and 64 (2x and 4x the cache), where the skipped
+        # bytes start to pay for the plan: inputs drawn on the GPU from a seeded torch
+        # generator (timing only; parity at these batches is not checked)
+        for bb in (32, 64):
+            skip[f"batch{bb}"] = skip_at_batch(bb, tria, c4, h4, kp4, args.reps, flush_caches, event_avg, log)
         dbytes = decode_bytes(cache4.numel(), c4.batch, c4.n_q_heads, c4.head_dim, hdr)
         dense_bytes = 2 * c4.batch * c4.n_kv_heads * c4.seq_len * c4.head_dim * 2
         dec = {

@@ -9,7 +9,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtria.so")
+# TRIA_LIBRARY: another build of the same library (the sanitizer-checked host build)
+LIB_PATH = os.environ.get("TRIA_LIBRARY") or os.path.join(HERE, "libtria.so")
 
 TRIA_OK, TRIA_ERR_INVALID_ARG, TRIA_ERR_UNSUPPORTED, TRIA_ERR_BUFFER_TOO_SMALL, TRIA_ERR_HIP = range(5)
 SCHED_HEADER_BYTES = 64

@@ -3,6 +3,12 @@
 Every HIP source is compiled with packed-fp32 instructions disabled (hipcc still
 vectorises ordinary float code otherwise) and with the default IEEE-correct fp32
 division that the quantiser's bit-exact contract relies on.
+
+`python block_sparse_mixed_head_amd/build.py --sanitize` builds a checking variant,
+_build/san/libtria_san.so, for the CPU tests only: the host code (capi.cpp: argument
+validation, schedule and page-table builders, the allocator) compiled by g++ with
+AddressSanitizer and UndefinedBehaviorSanitizer, linked with the unchanged GPU
+objects.  The binding loads it when TRIA_LIBRARY names it.
 """
 import os
 import subprocess
@@ -42,6 +48,26 @@ def _compile(src: str, objdir: str) -> str:
     return obj
 
 
+def build_sanitized() -> str:
+    """Host code with ASan + UBSan (g++), GPU objects as in build(); see the module doc."""
+    objdir = os.path.join(ROOT, "_build")
+    sandir = os.path.join(objdir, "san")
+    os.makedirs(sandir, exist_ok=True)
+    gpu = [s for s in SOURCES if s.endswith(".hip")]
+    with ThreadPoolExecutor(max_workers=len(gpu)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, objdir), gpu))
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+    capi = os.path.join(sandir, "capi.o")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+           "-I", INCLUDE, "-I", CSRC, *san, "-c", os.path.join(CSRC, "capi.cpp"), "-o", capi]
+    subprocess.run(cmd, check=True)
+    out = os.path.join(sandir, "libtria_san.so")
+    cmd = ["g++", "-shared", *san, capi, *objs, "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def build() -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -58,4 +84,4 @@ def build() -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build_sanitized() if "--sanitize" in sys.argv[1:] else build())

@@ -25,7 +25,7 @@ P = C.c_void_p
 def load() -> C.CDLL:
     global _lib
     if _lib is None:
-        path = library_path()
+        path = os.environ.get("ORACLE_LIBRARY") or library_path()  # (a sanitizer-checked build)
         if not os.path.exists(path):
             build()
         lib = C.CDLL(path)

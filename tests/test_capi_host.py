@@ -442,3 +442,42 @@ def test_varlen_and_paged_skip_calls_validate(tria):
                                              dev, dev, 64, None, 0, dev, 1 << 24, None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
     assert L.tria_decode_paged_varlen(C.byref(d), dev, tb, dev, 1 << 24, dev, C.c_float(0.1), dev, dev, ws - 1,
                                       None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+
+
+def test_paged_varlen_skip_calls_validate(tria):
+    """The variable-length paged skipping calls reject an index or workspace below their
+    sizes for dims->seq_len, a table smaller than its directory (the rest of the table
+    is checked on the device) and missing buffers before any HIP call."""
+    from block_sparse_mixed_head_amd import _lib
+    L = _lib.lib
+    d = tria.make_dims(2, 8, 2, 128, 128, 4096)
+    dev = C.c_void_p(1 << 30)
+    sz = C.c_size_t(0)
+    assert L.tria_paged_table_bytes(C.byref(d), 4096, C.byref(sz)) == _lib.TRIA_OK
+    tb = sz.value
+    assert L.tria_block_summaries_bytes(C.byref(d), 4096, C.byref(sz)) == _lib.TRIA_OK
+    sums = sz.value
+    assert L.tria_decode_skip_workspace_bytes(C.byref(d), 4096, C.byref(sz)) == _lib.TRIA_OK
+    ws = sz.value
+    pool = 1 << 24
+
+    def build(table_b=tb, pool_p=dev, sums_p=dev, sums_b=sums):
+        return L.tria_build_block_summaries_paged_varlen(C.byref(d), dev, table_b, pool_p, pool, sums_p, sums_b, None)
+
+    assert build(sums_b=sums - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    dir_end = 64 + 64 * 2 * 2
+    assert tb > dir_end
+    assert build(table_b=dir_end - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert build(pool_p=None) == _lib.TRIA_ERR_INVALID_ARG
+    assert build(sums_p=None) == _lib.TRIA_ERR_INVALID_ARG
+
+    def skip(table_b=tb, sums_b=sums, ws_b=ws, th=dev, q=dev, scale=0.1):
+        return L.tria_decode_skip_paged_varlen(C.byref(d), dev, table_b, dev, pool, dev, sums_b, q, th,
+                                               C.c_float(scale), dev, dev, ws_b, None)
+
+    assert skip(sums_b=sums - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert skip(ws_b=ws - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert skip(table_b=dir_end - 1) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert skip(th=None) == _lib.TRIA_ERR_INVALID_ARG
+    assert skip(q=None) == _lib.TRIA_ERR_INVALID_ARG
+    assert skip(scale=0.0) == _lib.TRIA_ERR_INVALID_ARG
