@@ -639,9 +639,9 @@ prefill_kernel(Args a) {
   const uint64_t s4u = reinterpret_cast<uint64_t>(a.k4s + krow0);
   const int n32 = (int)n, sink4 = sink + n4, d4 = lo4 - sink, d8 = lo8 - sink4;
   auto key0_32 = [&](int st) __attribute__((always_inline)) -> int {
-    const int t = st / C::SPT;
+    const int t = (int)((unsigned)st / C::SPT);  // (st >= 0: unsigned division is a shift)
     const int kb = t < sink ? 0 : t + (t < sink4 ? d4 : d8);
-    return kb * BLK + (st % C::SPT) * C::SK;
+    return kb * BLK + (int)((unsigned)st % C::SPT) * C::SK;
   };
   // rows of the stage inside the sequence (0 for a stage past the last one)
   auto rows_of = [&](bool valid, int key0) __attribute__((always_inline)) {
@@ -652,6 +652,8 @@ prefill_kernel(Args a) {
         : "=&s"(rows) : "s"(n32), "s"(key0), "i"(C::SK) : "scc");
     return valid ? rows : 0;
   };
+  // issue_k returns the stage's {first key, rows}; the V loads of the same stage,
+  // issued two iterations later, take them from there
   auto issue_k = [&](int st, lds_u8* kd, lds_f32* sd) __attribute__((always_inline)) {
     const bool valid = st < nstages;
     st = valid ? st : nstages - 1;
@@ -671,22 +673,21 @@ prefill_kernel(Args a) {
     }
     const uint64_t sbase = (is4 ? s4u : s8u) + (uint32_t)key0 * 4;
     dma4(buffer_desc(reinterpret_cast<const void*>(sbase), rows * 4), lo.gs, lds_addr(sd));
+    return make_int2(key0, rows);
   };
-  auto issue_v = [&](int st, lds_u8* vd) __attribute__((always_inline)) {
-    const bool valid = st < nstages;
-    st = valid ? st : nstages - 1;
-    const int key0 = key0_32(st);
-    const v4u rv = buffer_desc(reinterpret_cast<const void*>(vu + (uint32_t)key0 * 2 * D), rows_of(valid, key0) * 2 * D);
+  auto issue_v = [&](int2 kr, lds_u8* vd) __attribute__((always_inline)) {
+    const v4u rv = buffer_desc(reinterpret_cast<const void*>(vu + (uint32_t)kr.x * 2 * D), kr.y * 2 * D);
 #pragma unroll
     for (int j = 0; j < C::VN; ++j) dma16(rv, lo.gv + j * LO::PIECE_STEP, lds_addr(vd + (wave + j * C::WAVES) * 1024));
   };
 
   // ---- prologue: K and scales of stages 0..2, V of stage 0; V slot 2 (read with
   // zero weights by the first iteration, as "stage -1") cleared
-  issue_k(0, kslot(0), sslot(0));
-  issue_k(1, kslot(1), sslot(1));
-  issue_k(2, kslot(2), sslot(2));
-  issue_v(0, vslot(0));
+  // {first key, rows} of stages s + 1 and s + 2 for iteration s (from their K loads)
+  const int2 kr0 = issue_k(0, kslot(0), sslot(0));
+  int2 kr_next = issue_k(1, kslot(1), sslot(1));
+  int2 kr_next2 = issue_k(2, kslot(2), sslot(2));
+  issue_v(kr0, vslot(0));
   for (int i = tid; i < C::V_BYTES / 16; i += C::THREADS) *(lds_v4i*)(vslot(2) + i * 16) = v4i{0, 0, 0, 0};
 
   // the block's query codes (rows past the end as zeros)
@@ -747,9 +748,14 @@ prefill_kernel(Args a) {
     // softmax phases rather than all at once after the barrier, when every wave of
     // the CU would queue them together.  After the last stage the scores step reads
     // K slot R1 anyway (finite data, result unused).
+    int2 kr3;
     auto between = [&](auto k) __attribute__((always_inline)) {
-      if constexpr (decltype(k)::value == 0) issue_k(s + 3, kslot(R), sslot(R));
-      if constexpr (decltype(k)::value == 1) issue_v(s + 1, vslot(R1));
+      if constexpr (decltype(k)::value == 0) kr3 = issue_k(s + 3, kslot(R), sslot(R));
+      if constexpr (decltype(k)::value == 1) {
+        issue_v(kr_next, vslot(R1));
+        kr_next = kr_next2;
+        kr_next2 = kr3;
+      }
     };
     const bool is4 = is4_of(s);
     const int key_base = (s % C::SPT) * C::SK;
