@@ -856,13 +856,14 @@ decode_split_kernel(DecArgs a) {
 }
 
 // Merge of the partials of each pair: one work group per (batch, query head), one
-// thread per output column.  The pair's slot range and, for the first 16 slots,
-// every column value are loaded in two rounds with all loads in flight; thread t
-// also takes slot t's (m, l).  Then M = max m, f_i = 2^(m_i - M) through LDS, and
+// thread per output column.  The pair's slot range and, for the first 32 slots (a
+// pair spans about W / P + 1 of them: 17 at 2048 wavefronts and 128 pairs), every
+// column value are loaded in two rounds with all loads in flight; thread t also
+// takes slot t's (m, l).  Then M = max m, f_i = 2^(m_i - M) through LDS, and
 // out = sum_i f_i o_i / sum_i f_i l_i.
 template <int D>
 __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
-  constexpr int NW = D / 64, BO = 16;
+  constexpr int NW = D / 64, BO = 32;
   __shared__ float fs[D];
   __shared__ float red[2][NW];
   const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
