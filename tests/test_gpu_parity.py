@@ -126,6 +126,7 @@ SMALL = [
     (1, 7, 1, 128, 1000, 128, [7, 0, 0, 1, 2, 3, 4], [7, 0, 7, 5, 4, 3, 6]),  # G=7 edge policies
     (1, 2, 1, 64, 40, 64, [0, 3], [0, 3]),              # n < block
     (1, 2, 2, 128, 129, 128, [0, 0], [0, 1]),            # one full block + one token
+    (2, 4, 2, 128, 1, 128, [0, 1, 2, 3], [1, 2, 3, 4]),   # a single token (one unit per head, one row)
 ]
 
 
