@@ -385,7 +385,7 @@ __device__ __forceinline__ void pv_rowsum(const v8bf (&pb)[2][2], v4f (&O)[2][Cf
 // (whose stage-s values the scores phases consumed): every phase mixes matrix and
 // vector work.  between(k) runs after phase k's region (k = 0, 1, 2): the caller
 // spreads its memory-load issues over the iteration with it.
-template <int D, int BLK, bool QK4, bool DIAG, class Between>
+template <int D, int BLK, bool QK4, bool DIAG, bool NEXT, class Between>
 __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4f (&ksc)[4],
                                               int key_base, RowState (&rs)[2], v8bf (&pcur)[2][2], float (&f)[2],
                                               const v8bf (&pprev)[2][2], const lds_u8* vslot,
@@ -498,18 +498,24 @@ __device__ __forceinline__ bool softmax_pv_qk(bool is4, v4i (&S)[2][4], const v4
   };
   // regions 3, 4: the next stage's K reads, then the weights of one row group, then
   // half of the next stage's score MFMAs, interleaved with the weights
-  v4i qop[2][D / 64];
-  qk_operands<D, QK4>(q, qop);
-  v4i kop[2][D / 64];
-  qk_read<D, BLK, QK4, 0>(kslot, lo, kop);
-  weights(std::integral_constant<int, 0>());
-  qk_mma<D, 0>(kop, qop, S);
-  interleave<0, 4 * C::KS, (QK4 ? 9 : 6), 0>();
-  __builtin_amdgcn_sched_barrier(0);
-  qk_read<D, BLK, QK4, 1>(kslot, lo, kop);
-  weights(std::integral_constant<int, 1>());
-  qk_mma<D, 1>(kop, qop, S);
-  interleave<0, 4 * C::KS, (QK4 ? 9 : 6), 0>();
+  // (NEXT false: the unit's last stage, which has no next one to score)
+  if constexpr (NEXT) {
+    v4i qop[2][D / 64];
+    qk_operands<D, QK4>(q, qop);
+    v4i kop[2][D / 64];
+    qk_read<D, BLK, QK4, 0>(kslot, lo, kop);
+    weights(std::integral_constant<int, 0>());
+    qk_mma<D, 0>(kop, qop, S);
+    interleave<0, 4 * C::KS, (QK4 ? 9 : 6), 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    qk_read<D, BLK, QK4, 1>(kslot, lo, kop);
+    weights(std::integral_constant<int, 1>());
+    qk_mma<D, 1>(kop, qop, S);
+    interleave<0, 4 * C::KS, (QK4 ? 9 : 6), 0>();
+  } else {
+    weights(std::integral_constant<int, 0>());
+    weights(std::integral_constant<int, 1>());
+  }
   return need;
 }
 
@@ -660,9 +666,16 @@ prefill_kernel(Args a) {
     const bool is4 = is4_of(st);
     const int key0 = key0_32(st);
     const int rows = rows_of(valid, key0);
-    // bases and offsets chosen by value (a select of two argument fields would
-    // become a scalar load from the argument block, with its wait)
-    const uint64_t kbase = is4 ? k4u + (uint32_t)key0 * (D / 2) : k8u + (uint32_t)key0 * D;
+    // bases chosen by value: a select of two argument fields becomes a scalar load
+    // from the argument block, with its wait.  At d = 64 the compiler turns the
+    // selects of the four bases into a lookup table in scratch memory, loaded in every
+    // iteration (its wait then covers the ring loads too), so there the choice is
+    // mask arithmetic; at d = 128 plain selects give fewer instructions.
+    const uint64_t m4 = D == 64 ? (uint64_t)uni64(is4 ? -1LL : 0LL) : 0;
+    auto pick = [&](uint64_t b8, uint64_t b4) __attribute__((always_inline)) -> uint64_t {
+      return D == 64 ? b8 ^ ((b8 ^ b4) & m4) : (is4 ? b4 : b8);
+    };
+    const uint64_t kbase = pick(k8u, k4u) + (uint32_t)key0 * (uint32_t)(is4 ? D / 2 : D);
     const int kbytes = rows * (is4 ? D / 2 : D);
     const uint32_t off = lo.gk8 ^ ((lo.gk8 ^ lo.gk4) & (is4 ? ~0u : 0u));
 #pragma unroll
@@ -671,7 +684,7 @@ prefill_kernel(Args a) {
       dma16(buffer_desc(reinterpret_cast<const void*>(kbase), skip ? 0 : kbytes), off + j * LO::PIECE_STEP,
             lds_addr(kd + (wave + j * C::WAVES) * 1024));
     }
-    const uint64_t sbase = (is4 ? s4u : s8u) + (uint32_t)key0 * 4;
+    const uint64_t sbase = pick(s8u, s4u) + (uint32_t)key0 * 4;
     dma4(buffer_desc(reinterpret_cast<const void*>(sbase), rows * 4), lo.gs, lds_addr(sd));
     return make_int2(key0, rows);
   };
@@ -736,9 +749,10 @@ prefill_kernel(Args a) {
   //   contents were last read before the barrier); softmax(s) with the product of
   //   s-1 (V slot R+2); the scores of s+1 (K slot R+1) and the scales of s+1.
   int R = 0;
-  auto iter = [&](int s, auto qk4_tag, auto diag_tag) __attribute__((always_inline)) {
+  auto iter = [&](int s, auto qk4_tag, auto diag_tag, auto next_tag) __attribute__((always_inline)) {
     constexpr bool QK4 = decltype(qk4_tag)::value;  // precision of stage s+1
     constexpr bool DIAG = decltype(diag_tag)::value;  // stage s in the diagonal block
+    constexpr bool NEXT = decltype(next_tag)::value;  // a stage s+1 exists
     const int R1 = R == 2 ? 0 : R + 1, R2 = R == 0 ? 2 : R - 1;
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::NPER, 0));
     __builtin_amdgcn_s_barrier();
@@ -746,8 +760,7 @@ prefill_kernel(Args a) {
     float f[2];
     // the loads of K(s+3) and scales(s+3), then of V(s+1), are issued between the
     // softmax phases rather than all at once after the barrier, when every wave of
-    // the CU would queue them together.  After the last stage the scores step reads
-    // K slot R1 anyway (finite data, result unused).
+    // the CU would queue them together.
     int2 kr3;
     auto between = [&](auto k) __attribute__((always_inline)) {
       if constexpr (decltype(k)::value == 0) kr3 = issue_k(s + 3, kslot(R), sslot(R));
@@ -763,7 +776,7 @@ prefill_kernel(Args a) {
     // (one XOR each) rather than hoisted out of the loop into registers
     LO lo_it = lo;
     asm volatile("" : "+v"(lo_it.vx));
-    const bool need = softmax_pv_qk<D, BLK, QK4, DIAG>(is4, S, ksc, key_base, rs, pcur, f, pprev, vslot(R2), lo_it, O,
+    const bool need = softmax_pv_qk<D, BLK, QK4, DIAG, NEXT>(is4, S, ksc, key_base, rs, pcur, f, pprev, vslot(R2), lo_it, O,
                                                  kq, kslot(R1), q, between);
     // the rescale of O applies to the products of stages up to s-1 (complete) and
     // precedes the product of stage s (next iteration)
@@ -783,16 +796,19 @@ prefill_kernel(Args a) {
   // Four loops, so that each body has one precision for the scores of stage s+1 and
   // one masking mode (two variants in one body would sit under branches, which
   // split its scheduling regions and double its register needs): s+1 is an int4
-  // stage exactly for s in [b1, b2), and stages from e_int8 on are diagonal.
+  // stage exactly for s in [b1, b2), and stages from e_int8 on are diagonal; the
+  // last stage, which has no next one to score, runs on its own.
   const int b1 = n4 > 0 ? (e_sink > 0 ? e_sink - 1 : 0) : 0;
   const int b2 = n4 > 0 ? e_int4 - 1 : 0;
   using T = std::true_type;
   using F = std::false_type;
   int s = 0;
-  for (; s < (b1 < e_int8 ? b1 : e_int8); ++s) iter(s, F(), F());
-  for (; s < b2; ++s) iter(s, T(), F());
-  for (; s < e_int8; ++s) iter(s, F(), F());
-  for (; s < nstages; ++s) iter(s, F(), T());
+  for (; s < (b1 < e_int8 ? b1 : e_int8); ++s) iter(s, F(), F(), T());
+  for (; s < b2; ++s) iter(s, T(), F(), T());
+  for (; s < e_int8; ++s) iter(s, F(), F(), T());
+  for (; s < nstages - 1; ++s) iter(s, F(), T(), T());
+  iter(s, F(), T(), F());  // the last stage: nothing left to score
+  ++s;
   // product of the last stage, from V slot (nstages - 1) mod 3, whose loads were
   // issued in the last iteration but one
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
