@@ -762,6 +762,14 @@ decode_split_kernel(DecArgs a) {
       }
     }
     rec4 = SKIP && a.paged ? rec0 : rec0 + (int64_t)n8s * geo.rec8;
+    if constexpr (SKIP) {  // pair-uniform: kept in scalar registers across the pair's steps
+      rec0 = reinterpret_cast<const uint8_t*>(uni64(reinterpret_cast<int64_t>(rec0)));
+      rec4 = reinterpret_cast<const uint8_t*>(uni64(reinterpret_cast<int64_t>(rec4)));
+      list = reinterpret_cast<const int2*>(uni64(reinterpret_cast<int64_t>(list)));
+      pages = reinterpret_cast<const int32_t*>(uni64(reinterpret_cast<int64_t>(pages)));
+      stride8 = uni64(stride8);
+      stride4 = uni64(stride4);
+    }
     const uint32_t hfull = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
 
     // this pair's G query rows, quantised at both precisions (MFMA B operands)
