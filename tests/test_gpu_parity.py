@@ -127,6 +127,7 @@ SMALL = [
     (1, 2, 1, 64, 40, 64, [0, 3], [0, 3]),              # n < block
     (1, 2, 2, 128, 129, 128, [0, 0], [0, 1]),            # one full block + one token
     (2, 4, 2, 128, 1, 128, [0, 1, 2, 3], [1, 2, 3, 4]),   # a single token (one unit per head, one row)
+    (1, 4, 2, 64, 700, 128, [0, 1, 2, 3], [2, 4, 3, 5]),    # d=64 with B=128: sink, int4 ranges, ragged
 ]
 
 
@@ -357,6 +358,7 @@ DEC_SMALL = [
     (1, 32, 1, 128, 512, 128, 500, [1], [2]),   # MQA with 32 query heads (two row groups)
     (1, 2, 2, 64, 64, 64, 1, [0, 0], [0, 0]),   # a single token
     (1, 4, 4, 128, 2000, 128, 2000, [99, 0, 0, 1], [99, 0, 99, 2]),
+    (1, 8, 2, 64, 700, 128, 650, [1, 0], [3, 5]),  # d=64 with B=128
 ]
 
 
