@@ -46,8 +46,9 @@ PREFILL_TRAFFIC = {
     "llama3_8b_layer": os.path.join(ROOT, "profiles", "prefill_kernel.llama3_8b_n8192.hbm_traffic.txt"),
     "batched_mixed": os.path.join(ROOT, "profiles", "prefill_kernel.batched_mixed_b4_n16384.hbm_traffic.txt"),
 }
+# the kernel and the host code that orders its work units (the order sets the L2 reuse)
 PREFILL_SOURCES = [os.path.join(ROOT, "block_sparse_mixed_head_amd", "csrc", f)
-                   for f in ("prefill.hip", "device_common.h", "kernels.h")]
+                   for f in ("prefill.hip", "device_common.h", "kernels.h", "capi.cpp")]
 
 
 def source_hash(paths) -> str:

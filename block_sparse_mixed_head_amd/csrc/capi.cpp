@@ -162,18 +162,79 @@ const char* tria_last_error(void) { return g_error.c_str(); }
 int32_t tria_version(void) { return (1 << 16) | 0; }
 
 // ------------------------------------------------------------------ (1) policy
-// Units of `nb_of.size()` batch rows (sequences) with nb_of[b] query blocks each, in
-// (b, h, qb) order, placed by a stable counting sort on ntiles (descending), written
-// after the 64-byte header at `out`.
+// Dispatch order of the units.  The prefill launches one work group per unit in
+// record order, and work group i runs on XCD i mod 8 (round-robin over the eight
+// XCDs, each with its own L2).  Consecutive query blocks of one query head read
+// overlapping key windows: run together on one XCD, they read each K/V tile within
+// a few stages of one another, so it is fetched into that L2 about once instead of
+// once per unit (the traffic beyond L2 costs power, and the part runs at its power
+// limit).  So each lane (batch row b, head h) is cut into chunks of kChunk
+// consecutive query blocks, taken from the last block down; a chunk's units run in
+// consecutive slots of one XCD.  Chunks go, largest (most tiles) first, to the XCD
+// with the least work so far among those with room for them, and each XCD runs its
+// chunks largest first, so the shortest units close the dispatch.  Record r of
+// XCD x goes to position 8 r + x while every XCD still has records; the rest
+// follow round-robin over the XCDs that still have them.
+constexpr int kXcds = 8;
+constexpr int64_t kChunk = 32;
+
+static void dispatch_order(const std::vector<int32_t>& rec, int64_t n_units, const std::vector<int64_t>& nb_of,
+                           int32_t hq, int32_t* units) {
+  struct Chunk {
+    int64_t first, count, work;  // records first .. first + count - 1 (q-blocks descending)
+  };
+  // records arrive in (b, h, qb ascending) order; a lane's chunks start at its last q-block
+  std::vector<Chunk> chunks;
+  std::vector<int64_t> order;  // record indices, each lane's q-blocks descending
+  order.reserve((size_t)n_units);
+  int64_t base = 0;
+  for (size_t b = 0; b < nb_of.size(); ++b)
+    for (int h = 0; h < hq; ++h, base += nb_of[b])
+      for (int64_t c0 = 0; c0 < nb_of[b]; c0 += kChunk) {
+        Chunk c{(int64_t)order.size(), std::min(kChunk, nb_of[b] - c0), 0};
+        for (int64_t i = 0; i < c.count; ++i) {
+          const int64_t r = base + nb_of[b] - 1 - (c0 + i);
+          order.push_back(r);
+          c.work += rec[(size_t)r * 8 + 7];
+        }
+        chunks.push_back(c);
+      }
+  std::vector<size_t> by_work(chunks.size());
+  for (size_t i = 0; i < by_work.size(); ++i) by_work[i] = i;
+  std::stable_sort(by_work.begin(), by_work.end(),
+                   [&](size_t a, size_t b) { return chunks[a].work > chunks[b].work; });
+  const int64_t room = (n_units + kXcds - 1) / kXcds;
+  std::vector<std::vector<size_t>> xcd(kXcds);
+  int64_t work[kXcds] = {0}, count[kXcds] = {0};
+  for (size_t c : by_work) {
+    int best = -1;
+    for (int x = 0; x < kXcds; ++x)
+      if (count[x] + chunks[c].count <= room && (best < 0 || work[x] < work[best])) best = x;
+    if (best < 0)  // no XCD has room for the whole chunk: the least loaded by units
+      for (int x = 0; x < kXcds; ++x)
+        if (best < 0 || count[x] < count[best]) best = x;
+    xcd[best].push_back(c);
+    work[best] += chunks[c].work;
+    count[best] += chunks[c].count;
+  }
+  // each XCD's records (its chunks in placement order: largest first)
+  std::vector<std::vector<int64_t>> seq(kXcds);
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t c : xcd[x])
+      for (int64_t i = 0; i < chunks[c].count; ++i) seq[x].push_back(order[(size_t)(chunks[c].first + i)]);
+  int64_t pos = 0;
+  for (size_t r = 0; pos < n_units; ++r)
+    for (int x = 0; x < kXcds; ++x)
+      if (r < seq[x].size()) std::memcpy(units + 8 * pos++, &rec[(size_t)seq[x][r] * 8], 32);
+}
+
+// Units of `nb_of.size()` batch rows (sequences) with nb_of[b] query blocks each,
+// written after the 64-byte header at `out` in the dispatch order above.
 static void expand_units(const std::vector<int64_t>& nb_of, int32_t hq, const int32_t* hi, const int32_t* keep,
                          int32_t* units) {
-  int64_t n_units = 0, nbmax = 0;
-  for (int64_t nb : nb_of) {
-    n_units += hq * nb;
-    nbmax = std::max(nbmax, nb);
-  }
+  int64_t n_units = 0;
+  for (int64_t nb : nb_of) n_units += hq * nb;
   std::vector<int32_t> rec((size_t)n_units * 8);
-  std::vector<int64_t> count(nbmax + 2, 0);
   int64_t u = 0;
   for (size_t b = 0; b < nb_of.size(); ++b)
     for (int h = 0; h < hq; ++h)
@@ -196,19 +257,8 @@ static void expand_units(const std::vector<int64_t>& nb_of, int32_t hq, const in
         r[5] = (int32_t)hi4;
         r[6] = (int32_t)sink;
         r[7] = (int32_t)ntiles;
-        count[ntiles]++;
       }
-  // start position of each ntiles bucket, largest first
-  std::vector<int64_t> start(nbmax + 2, 0);
-  int64_t pos = 0;
-  for (int64_t t = nbmax + 1; t >= 0; --t) {
-    start[t] = pos;
-    pos += count[t];
-  }
-  for (int64_t i = 0; i < n_units; ++i) {
-    const int32_t* r = &rec[(size_t)i * 8];
-    std::memcpy(units + 8 * start[r[7]]++, r, 32);
-  }
+  dispatch_order(rec, n_units, nb_of, hq, units);
 }
 
 static void schedule_header(int32_t* out, int32_t version, int32_t rows, const tria_dims* dims, int64_t nb,

@@ -40,7 +40,8 @@
 //   * O^T = V^T . P^T with v_mfma_f32_16x16x32_bf16: the transposed scores are
 //     already the B operand layout, and V (row-major in LDS) is fed as V^T by
 //     ds_read_b64_tr_b16, so V needs no transpose pass.
-//   * Registers are held to 256 per lane so two work groups share a CU.
+//   * Wavefronts per SIMD: as many as the LDS rings let share a CU, at most two
+//     (256 registers per lane); at head_dim 128 with 64-row blocks that is one.
 #include <cfloat>
 #include <type_traits>
 
@@ -74,6 +75,10 @@ struct Cfg {
   static constexpr int VN = V_INSTR / WAVES;
   // loads per wave and stage: K pieces, V pieces, key scales
   static constexpr int NPER = K8N + VN + 1;
+  // LDS per work group (the three-slot K, V and key-scale rings) and the wavefronts
+  // per SIMD it leaves room for (160 KB of LDS and four SIMDs per CU), at most two
+  static constexpr int LDS = 3 * (K_BYTES + V_BYTES + SK * 4);
+  static constexpr int OCC = (160 * 1024 / LDS) * WAVES / 4 < 2 ? (160 * 1024 / LDS) * WAVES / 4 : 2;
 };
 
 struct Args {
@@ -601,7 +606,8 @@ __device__ __forceinline__ bool unit_of(const Args& a, Unit& un) {
 }
 
 template <int D, int BLK>
-__global__ void __launch_bounds__((Cfg<D, BLK>::THREADS)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__((Cfg<D, BLK>::THREADS))
+__attribute__((amdgpu_waves_per_eu(Cfg<D, BLK>::OCC, Cfg<D, BLK>::OCC)))
 prefill_kernel(Args a) {
   using C = Cfg<D, BLK>;
   using LO = LaneOffsets<D, BLK>;
@@ -609,6 +615,7 @@ prefill_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t kring_[3 * C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t vring_[3 * C::V_BYTES];
   __shared__ __attribute__((aligned(16))) float sring_[3 * C::SK];
+  static_assert(sizeof(kring_) + sizeof(vring_) + sizeof(sring_) == C::LDS, "LDS budget");
   lds_u8* const kring = (lds_u8*)kring_;
   lds_u8* const vring = (lds_u8*)vring_;
   lds_f32* const sring = (lds_f32*)sring_;

@@ -94,8 +94,15 @@ int32_t tria_version(void);
  *                 stored as (0, -1) when empty
  *     sink        1 if block 0 is int8 but lies outside the int8 range (lo8 > 0)
  *     ntiles      (qb - lo8 + 1) + sink + (hi4 - lo4 + 1)
- *   Record order: ntiles descending, ties by (b, h, qb) ascending (longest work
- *   first, so a GPU that launches work groups in order balances its load).
+ *   Record order (the dispatch order; tria_prefill accepts the records in any
+ *   order): work group i runs on XCD i mod 8.  Each (b, h) is cut into chunks of
+ *   32 consecutive query blocks counted down from its last block; a chunk's
+ *   records run in consecutive slots of one XCD, so its units, whose key windows
+ *   overlap, share that XCD's L2.  Chunks go, most tiles first, to the XCD with the
+ *   fewest tiles so far among those holding at most ceil(n_units / 8) records with
+ *   it; each XCD runs its chunks most tiles first; record r of XCD x sits at
+ *   position 8 r + x while every XCD still has records, the rest follow
+ *   round-robin over those that do.
  * Total size: TRIA_SCHED_HEADER_BYTES + TRIA_SCHED_UNIT_BYTES * n_units.
  *
  * n_policy_heads must equal n_q_heads.  If sched_host is NULL or sched_bytes is
@@ -185,7 +192,7 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
  * tria_build_policy_varlen: as tria_build_policy, with header word [1] =
  *   TRIA_SCHED_VERSION_VARLEN, [2] = n_seqs, [7] = the largest block count; units
  *   {s, h, qb, ...} for every sequence s and its ceil(len_s / block) query blocks
- *   (same record order: ntiles descending, ties by (s, h, qb)); then n_seqs
+ *   (same dispatch order, a lane being one (s, h)); then n_seqs
  *   records {int32 start, int32 length}.  Size TRIA_SCHED_HEADER_BYTES +
  *   TRIA_SCHED_UNIT_BYTES * n_units + 8 * n_seqs.
  * tria_prefill_varlen: as tria_prefill over that schedule; out fp32 [1][Hq][T][d],

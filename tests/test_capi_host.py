@@ -1,8 +1,9 @@
 """Host-side checks of the C-ABI library (no GPU needed).
 
 * the library loads and exports every function include/tria.h declares;
-* tria_build_policy (host) matches the oracle's schedule bit for bit on the five
-  workloads and on random shapes, including ragged sequence lengths;
+* tria_build_policy (host) holds the oracle's unit records bit for bit on the five
+  workloads and on random shapes, including ragged sequence lengths, in a dispatch
+  order whose XCD placement and chunking are checked separately;
 * tria_kv_cache_bytes matches the oracle's cache size;
 * validation returns the documented status codes and enqueues nothing.
 """
@@ -36,6 +37,20 @@ def test_library_exports_every_declared_symbol(tria):
     assert _lib.lib.tria_version() >> 16 == 1
 
 
+def _by_unit(blob, n_units):
+    """Unit records sorted by (b, h, qb): the schedule's content without its order."""
+    u = blob[16:16 + 8 * n_units].reshape(-1, 8)
+    return u[np.lexsort((u[:, 2], u[:, 1], u[:, 0]))]
+
+
+def _same_schedule(mine, ref):
+    """Same header and the same unit records (the oracle lists them longest first;
+    the library in its dispatch order)."""
+    n = int(ref[8])
+    return (mine.dtype == np.int32 and mine.shape == ref.shape and np.array_equal(mine[:16], ref[:16])
+            and np.array_equal(_by_unit(mine, n), _by_unit(ref, n)))
+
+
 @pytest.mark.parametrize("cid", ["tiny", "llama3_8b_layer", "long_prefill", "batched_mixed"])
 def test_schedule_bit_exact_on_workloads(tria, cid):
     c = synth.CONFIGS[cid]
@@ -43,7 +58,90 @@ def test_schedule_bit_exact_on_workloads(tria, cid):
     d = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
     mine = tria.build_policy(d, hi, keep)
     ref = oracle.build_schedule(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len, hi, keep)
-    assert mine.dtype == np.int32 and np.array_equal(mine, ref)
+    assert _same_schedule(mine, ref)
+
+
+def _check_dispatch_order(units, xcds=8, chunk=32):
+    """The library's dispatch order: position p runs on XCD p mod 8 while all eight
+    XCDs still have records; each XCD's records are chunks of at most `chunk`
+    consecutive q-blocks of one (b, h), taken from the lane's last block down (a
+    chunk starts at nb - 1 - chunk * k), the chunks in non-increasing order of
+    their tiles.  The full rotation is found from the records themselves: in it,
+    the record at p either starts a chunk or continues the one at p - 8.  Returns
+    the tiles per XCD over the full rounds and the fraction of positions in them."""
+    n = len(units)
+    nb = {}
+    for b, h, qb in units[:, :3]:
+        nb[(b, h)] = max(nb.get((b, h), 0), qb + 1)
+
+    def starts(u):
+        return (nb[(u[0], u[1])] - 1 - u[2]) % chunk == 0
+
+    rounds = 0
+    while (rounds + 1) * xcds <= n:
+        ok = True
+        for x in range(xcds):
+            p = rounds * xcds + x
+            u = units[p]
+            if starts(u):
+                continue
+            prev = units[p - xcds] if p >= xcds else None
+            if prev is None or tuple(prev[:2]) != tuple(u[:2]) or prev[2] != u[2] + 1:
+                ok = False
+        if not ok:
+            break
+        rounds += 1
+    full = rounds * xcds
+    tiles = []
+    for x in range(xcds):
+        seq = units[x:full:xcds]
+        tiles.append(int(seq[:, 7].sum()))
+        works, i = [], 0
+        while i < len(seq):
+            j = i + 1
+            while j < len(seq) and not starts(seq[j]):
+                j += 1
+            assert j - i <= chunk
+            works.append(int(seq[i:j, 7].sum()))
+            i = j
+        # the last chunk may be cut by the end of the full rounds
+        assert all(a >= b for a, b in zip(works[:-2], works[1:-1])), works
+    return tiles, full / n
+
+
+@pytest.mark.parametrize("cid", ["llama3_8b_layer", "long_prefill", "batched_mixed"])
+def test_dispatch_order_on_workloads(tria, cid):
+    c = synth.CONFIGS[cid]
+    hi, keep = c.policy()
+    d = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
+    units = tria.build_policy(d, hi, keep)[16:].reshape(-1, 8)
+    tiles, frac = _check_dispatch_order(units)
+    assert frac == 1.0
+    # balanced to within one chunk of the largest size (32 units of at most nb tiles)
+    nb = (c.seq_len + c.block - 1) // c.block
+    assert max(tiles) - min(tiles) <= 32 * nb, tiles
+    assert max(tiles) / np.mean(tiles) < 1.01, tiles
+
+
+def test_dispatch_order_varlen_and_random_policies(tria):
+    """Shapes with whole 32-block chunks on every XCD: two batch rows of 16 heads, 64
+    query blocks each, random policies; and a variable-length batch of the same size
+    (sequence lengths that are not multiples of the chunk)."""
+    rng = np.random.default_rng(5)
+    for blk in (64, 128):
+        hi = rng.integers(0, 20, size=16).astype(np.int32)
+        keep = (hi + rng.integers(0, 50, size=16)).astype(np.int32)
+        d = tria.make_dims(2, 16, 4, 128, blk, 64 * blk)
+        units = tria.build_policy(d, hi, keep)[16:].reshape(-1, 8)
+        tiles, frac = _check_dispatch_order(units)
+        assert frac == 1.0 and max(tiles) - min(tiles) <= 32 * 64, tiles
+        lens = np.array([50 * blk + 7, 30 * blk, 48 * blk - 3], np.int64)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        d = tria.make_dims(1, 16, 4, 128, blk, int(cu[-1]))
+        blob = tria.build_policy_varlen(d, hi, keep, cu)
+        n_units = int(blob[8])
+        tiles, frac = _check_dispatch_order(blob[16:16 + 8 * n_units].reshape(-1, 8))
+        assert frac > 0.75, frac
 
 
 def test_schedule_bit_exact_random_shapes(tria):
@@ -59,8 +157,8 @@ def test_schedule_bit_exact_random_shapes(tria):
         hi = rng.integers(0, nb + 2, size=hq).astype(np.int32)
         keep = (hi + rng.integers(0, nb + 2, size=hq)).astype(np.int32)
         d = tria.make_dims(b, hq, hk, hd, blk, n)
-        assert np.array_equal(tria.build_policy(d, hi, keep),
-                              oracle.build_schedule(b, hq, hk, hd, blk, n, hi, keep))
+        mine = tria.build_policy(d, hi, keep)
+        assert _same_schedule(mine, oracle.build_schedule(b, hq, hk, hd, blk, n, hi, keep))
 
 
 def test_tiny_workload_tile_counts(tria):
@@ -300,7 +398,7 @@ def test_allocator_validates(tria):
 def test_varlen_schedule_matches_oracle(tria):
     """The variable-length schedule = each sequence's own schedule (the oracle's, for
     that length alone) with its batch index replaced by the sequence index, all
-    units merged by a stable sort on ntiles (descending), then the {start, length}
+    units together (in the library's dispatch order), then the {start, length}
     table."""
     import oracle
     rng = np.random.default_rng(9)
@@ -319,11 +417,11 @@ def test_varlen_schedule_matches_oracle(tria):
             u = oracle.build_schedule(1, hq, 1, 64, blk, int(L), hi, keep)[16:].reshape(-1, 8).copy()
             u[:, 0] = s_
             parts.append(u)
-        allu = np.concatenate(parts)
-        want = allu[np.argsort(-allu[:, 7], kind="stable")]
+        want = np.concatenate(parts)
+        want = want[np.lexsort((want[:, 2], want[:, 1], want[:, 0]))]
         n_units = len(want)
         assert blob[1] == 2 and blob[2] == len(lens) and blob[8] == n_units
-        assert np.array_equal(blob[16:16 + 8 * n_units].reshape(-1, 8), want)
+        assert np.array_equal(_by_unit(blob, n_units), want)
         seqs = blob[16 + 8 * n_units:].reshape(-1, 2)
         assert np.array_equal(seqs[:, 0], cu[:-1]) and np.array_equal(seqs[:, 1], lens)
 
