@@ -161,29 +161,22 @@ __device__ __forceinline__ void interleave() {
 // this wave still outstanding.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-// Raw buffer descriptor over [base, base + bytes) (bytes past the end read as 0),
-// wave-uniform, as four scalar registers.
-__device__ __forceinline__ v4u buffer_desc(const void* base, int bytes) {
-  const uint64_t p = (uint64_t)uni64(reinterpret_cast<int64_t>(base));
-  return v4u{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)uni(bytes), 0x00020000u};
-}
-
-// buffer_load ... lds: every active lane's 16 (4) bytes at desc + voff go to
-// LDS address lds + 16 (4) * lane (whole offsets in voff, which the resource's range
-// check covers: bytes past the resource read as 0).  The LDS base travels in m0, given to the asm as
-// an input operand so the compiler itself loads m0 and knows it is in use.  No
-// register result; completion is counted by vmcnt, which the caller waits for before
-// the data is read (by any wave).
-__device__ __forceinline__ void dma16(v4u desc, uint32_t voff, uint32_t lds) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+// buffer_load ... lds: every active lane's 16 (4) bytes at desc base + soff + voff
+// go to LDS address lds + 16 (4) * lane.  The range check covers soff + voff: lanes
+// at or past the resource's byte count read 0 without a memory access.  The LDS base travels
+// in m0, given to the asm as an input operand so the compiler itself loads m0 and
+// knows it is in use.  No register result; completion is counted by vmcnt, which
+// the caller waits for before the data is read (by any wave).
+__device__ __forceinline__ void dma16(v4u desc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(desc), "{m0}"(lds)
+               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds)
                : "memory");
 }
-__device__ __forceinline__ void dma4(v4u desc, uint32_t voff, uint32_t lds) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+__device__ __forceinline__ void dma4(v4u desc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(desc), "{m0}"(lds)
+               : "v"(voff), "s"(desc), "s"(soff), "{m0}"(lds)
                : "memory");
 }
 
@@ -592,7 +585,7 @@ __device__ __forceinline__ bool unit_of(const Args& a, Unit& un) {
     const bool rows_ok = b >= 0 && b < a.batch && seq0 >= 0 && n >= 1 && seq0 + n <= a.n && h >= 0 && h < a.hq &&
                          qb >= 0 && qb < nbq;
     const bool bad = !rows_ok || lo8 < 0 || lo8 > qb || sink < 0 || sink > 1 || (sink == 1 && lo8 == 0) || n4 < 0 ||
-                     (n4 > 0 && (lo4 < 1 || hi4 >= lo8)) || ntiles != (qb - lo8 + 1) + sink + n4;
+                     (n4 > 0 && (lo4 < 1 || hi4 != lo8 - 1)) || ntiles != (qb - lo8 + 1) + sink + n4;
     if (bad) {
       if (rows_ok) {
         const int64_t r0 = ((int64_t)bb * a.hq + h) * a.n + seq0 + (int64_t)qb * BLK;
@@ -651,19 +644,33 @@ prefill_kernel(Args a) {
   // instructions (K8N + 1, VN) whatever the stage, so the waits can count them: a
   // stage past the last one, or a K piece past the int4 stage size, reads through an
   // empty resource.  Resources and offsets are chosen by value, never by branching.
-  // Per-unit bases and the stage -> first key map in 32-bit scalar arithmetic (the
-  // host guarantees seq_len < 2^31), so a stage's addresses cost a few scalar
-  // instructions.
-  const uint64_t k8u = reinterpret_cast<uint64_t>(a.k8 + krow0 * D);
-  const uint64_t k4u = reinterpret_cast<uint64_t>(a.k4 + krow0 * (D / 2));
-  const uint64_t vu = reinterpret_cast<uint64_t>(a.v + krow0 * D);
-  const uint64_t s8u = reinterpret_cast<uint64_t>(a.k8s + krow0);
-  const uint64_t s4u = reinterpret_cast<uint64_t>(a.k4s + krow0);
-  const int n32 = (int)n, sink4 = sink + n4, d4 = lo4 - sink, d8 = lo8 - sink4;
-  auto key0_32 = [&](int st) __attribute__((always_inline)) -> int {
-    const int t = (int)((unsigned)st / C::SPT);  // (st >= 0: unsigned division is a shift)
-    const int kb = t < sink ? 0 : t + (t < sink4 ? d4 : d8);
-    return kb * BLK + (int)((unsigned)st % C::SPT) * C::SK;
+  // The resources start at the unit's rows (per-unit words: the low 32 bits of the
+  // base and its high 16); a stage passes its first key's byte offset as the scalar
+  // offset and ends the resource at its last row inside the sequence (byte count =
+  // that offset + its rows' bytes), so rows past the end read as zero.  Byte offsets
+  // are 32-bit (the host guarantees (seq_len + block) * 2 * head_dim < 2^31): a
+  // stage's addresses cost a few scalar instructions.
+  const uint64_t k8u = uni64(reinterpret_cast<int64_t>(a.k8 + krow0 * D));
+  const uint64_t k4u = uni64(reinterpret_cast<int64_t>(a.k4 + krow0 * (D / 2)));
+  const uint64_t vu = uni64(reinterpret_cast<int64_t>(a.v + krow0 * D));
+  const uint64_t s8u = uni64(reinterpret_cast<int64_t>(a.k8s + krow0));
+  const uint64_t s4u = uni64(reinterpret_cast<int64_t>(a.k4s + krow0));
+  auto w0_of = [](uint64_t p) __attribute__((always_inline)) { return (uint32_t)p; };
+  auto w1_of = [](uint64_t p) __attribute__((always_inline)) { return (uint32_t)(p >> 32) & 0xffffu; };
+  auto rsrc = [](uint32_t w0, uint32_t w1, int bytes) __attribute__((always_inline)) {
+    return v4u{(uint32_t)uni((int)w0), (uint32_t)uni((int)w1), (uint32_t)uni(bytes), 0x00020000u};
+  };
+  const int n32 = (int)n;
+  // The stages' first keys: the sink block's stages start at key 0; from stage e_sink
+  // on the keys are consecutive (the int4 range ends where the int8 run begins), so
+  // key0 = st * SK + key_off there.  PAST: st >= e_sink is known (every stage issued
+  // inside the loop, s + 3 >= 3 >= e_sink).
+  const int key_off = ((n4 > 0 ? lo4 : lo8) * C::SPT - e_sink) * C::SK;
+  auto key0_of = [&](int st, auto past_tag) __attribute__((always_inline)) -> int {
+    if constexpr (decltype(past_tag)::value)
+      return st * C::SK + key_off;
+    else
+      return st * C::SK + (st < e_sink ? 0 : key_off);
   };
   // rows of the stage inside the sequence (0 for a stage past the last one)
   auto rows_of = [&](bool valid, int key0) __attribute__((always_inline)) {
@@ -674,48 +681,55 @@ prefill_kernel(Args a) {
         : "=&s"(rows) : "s"(n32), "s"(key0), "i"(C::SK) : "scc");
     return valid ? rows : 0;
   };
+  constexpr int LOG2D = D == 128 ? 7 : 6;
+  static_assert((1 << LOG2D) == D, "head_dim 64 or 128");
   // issue_k returns the stage's {first key, rows}; the V loads of the same stage,
   // issued two iterations later, take them from there
-  auto issue_k = [&](int st, lds_u8* kd, lds_f32* sd) __attribute__((always_inline)) {
+  auto issue_k = [&](int st, lds_u8* kd, lds_f32* sd, auto past_tag) __attribute__((always_inline)) {
+    constexpr bool PAST = decltype(past_tag)::value;
     const bool valid = st < nstages;
-    st = valid ? st : nstages - 1;
-    const bool is4 = is4_of(st);
-    const int key0 = key0_32(st);
+    const bool is4 = PAST ? st < e_int4 : is4_of(st);
+    const int key0 = key0_of(st, past_tag);
     const int rows = rows_of(valid, key0);
-    // bases chosen by value: a select of two argument fields becomes a scalar load
-    // from the argument block, with its wait.  At d = 64 the compiler turns the
-    // selects of the four bases into a lookup table in scratch memory, loaded in every
-    // iteration (its wait then covers the ring loads too), so there the choice is
-    // mask arithmetic; at d = 128 plain selects give fewer instructions.
-    const uint64_t m4 = D == 64 ? (uint64_t)uni64(is4 ? -1LL : 0LL) : 0;
-    auto pick = [&](uint64_t b8, uint64_t b4) __attribute__((always_inline)) -> uint64_t {
-      return D == 64 ? b8 ^ ((b8 ^ b4) & m4) : (is4 ? b4 : b8);
+    // resource words chosen by value.  At d = 64 the compiler turns plain selects of
+    // several words into a lookup table in scratch memory, loaded in every
+    // iteration, so there the choice is mask arithmetic; at d = 128 plain selects
+    // give fewer instructions.
+    const uint32_t m4 = D == 64 ? (uint32_t)uni(is4 ? -1 : 0) : 0u;
+    auto pick = [&](uint32_t w8, uint32_t w4) __attribute__((always_inline)) -> uint32_t {
+      return D == 64 ? w8 ^ ((w8 ^ w4) & m4) : (is4 ? w4 : w8);
     };
-    const uint64_t kbase = pick(k8u, k4u) + (uint32_t)key0 * (uint32_t)(is4 ? D / 2 : D);
-    const int kbytes = rows * (is4 ? D / 2 : D);
+    const int sh = is4 ? LOG2D - 1 : LOG2D;  // log2 of the K row bytes
+    const uint32_t kw0 = pick(w0_of(k8u), w0_of(k4u)), kw1 = pick(w1_of(k8u), w1_of(k4u));
+    const int ksoff = key0 << sh;
+    const int kend = ksoff + (rows << sh);
     const uint32_t off = lo.gk8 ^ ((lo.gk8 ^ lo.gk4) & (is4 ? ~0u : 0u));
 #pragma unroll
     for (int j = 0; j < C::K8N; ++j) {
       const bool skip = is4 && wave + j * C::WAVES >= C::K4_INSTR;
-      dma16(buffer_desc(reinterpret_cast<const void*>(kbase), skip ? 0 : kbytes), off + j * LO::PIECE_STEP,
+      dma16(rsrc(kw0, kw1, skip ? 0 : kend), off + j * LO::PIECE_STEP, (uint32_t)ksoff,
             lds_addr(kd + (wave + j * C::WAVES) * 1024));
     }
-    const uint64_t sbase = pick(s8u, s4u) + (uint32_t)key0 * 4;
-    dma4(buffer_desc(reinterpret_cast<const void*>(sbase), rows * 4), lo.gs, lds_addr(sd));
+    const uint32_t sw0 = pick(w0_of(s8u), w0_of(s4u)), sw1 = pick(w1_of(s8u), w1_of(s4u));
+    dma4(rsrc(sw0, sw1, (key0 + rows) * 4), lo.gs, (uint32_t)(key0 * 4), lds_addr(sd));
     return make_int2(key0, rows);
   };
   auto issue_v = [&](int2 kr, lds_u8* vd) __attribute__((always_inline)) {
-    const v4u rv = buffer_desc(reinterpret_cast<const void*>(vu + (uint32_t)kr.x * 2 * D), kr.y * 2 * D);
+    const v4u rv = rsrc(w0_of(vu), w1_of(vu), (kr.x + kr.y) * 2 * D);
+    const uint32_t vsoff = (uint32_t)(kr.x * 2 * D);
 #pragma unroll
-    for (int j = 0; j < C::VN; ++j) dma16(rv, lo.gv + j * LO::PIECE_STEP, lds_addr(vd + (wave + j * C::WAVES) * 1024));
+    for (int j = 0; j < C::VN; ++j)
+      dma16(rv, lo.gv + j * LO::PIECE_STEP, vsoff, lds_addr(vd + (wave + j * C::WAVES) * 1024));
   };
 
   // ---- prologue: K and scales of stages 0..2, V of stage 0; V slot 2 (read with
   // zero weights by the first iteration, as "stage -1") cleared
   // {first key, rows} of stages s + 1 and s + 2 for iteration s (from their K loads)
-  const int2 kr0 = issue_k(0, kslot(0), sslot(0));
-  int2 kr_next = issue_k(1, kslot(1), sslot(1));
-  int2 kr_next2 = issue_k(2, kslot(2), sslot(2));
+  using T = std::true_type;
+  using F = std::false_type;
+  const int2 kr0 = issue_k(0, kslot(0), sslot(0), F());
+  int2 kr_next = issue_k(1, kslot(1), sslot(1), F());
+  int2 kr_next2 = issue_k(2, kslot(2), sslot(2), F());
   issue_v(kr0, vslot(0));
   for (int i = tid; i < C::V_BYTES / 16; i += C::THREADS) *(lds_v4i*)(vslot(2) + i * 16) = v4i{0, 0, 0, 0};
 
@@ -779,7 +793,7 @@ prefill_kernel(Args a) {
     // the CU would queue them together.
     int2 kr3;
     auto between = [&](auto k) __attribute__((always_inline)) {
-      if constexpr (decltype(k)::value == 0) kr3 = issue_k(s + 3, kslot(R), sslot(R));
+      if constexpr (decltype(k)::value == 0) kr3 = issue_k(s + 3, kslot(R), sslot(R), T());
       if constexpr (decltype(k)::value == 1) {
         issue_v(kr_next, vslot(R1));
         kr_next = kr_next2;
@@ -816,8 +830,6 @@ prefill_kernel(Args a) {
   // last stage, which has no next one to score, runs on its own.
   const int b1 = n4 > 0 ? (e_sink > 0 ? e_sink - 1 : 0) : 0;
   const int b2 = n4 > 0 ? e_int4 - 1 : 0;
-  using T = std::true_type;
-  using F = std::false_type;
   int s = 0;
   for (; s < (b1 < e_int8 ? b1 : e_int8); ++s) iter(s, F(), F(), T());
   for (; s < b2; ++s) iter(s, T(), F(), T());

@@ -168,11 +168,14 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
  * below it, TRIA_ERR_INVALID_ARG above it).  The device checks the schedule: a
  * header that does not describe the call (magic, version, batch, heads, head_dim,
  * block, block count, unit count, seq_len) makes every output row and LSE entry NaN;
- * a malformed unit record computes nothing and makes the rows it names NaN (a record
+ * a malformed unit record (one the builder could not have written: fields out of
+ * range, an int4 range that does not end at lo8 - 1, a tile count that disagrees)
+ * computes nothing and makes the rows it names NaN (a record
  * that names no rows writes nothing, so the rows of the unit it replaced keep what
  * `out` held).  The kernels always exit normally.
- * Errors: TRIA_ERR_UNSUPPORTED for seq_len >= 2^31 - block (token indices are
- * 32-bit inside the kernel).
+ * Errors: TRIA_ERR_UNSUPPORTED when (seq_len + block) * 2 * head_dim >= 2^31 (byte
+ * offsets within a head's rows are 32-bit inside the kernel: seq_len below 8.4 M
+ * tokens at head_dim 128).
  */
 tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes,
                          const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,

@@ -259,6 +259,17 @@ def test_prefill_bad_schedule_gives_nan(tria):
         o, l = run(bad)
         assert np.isnan(o[rows]).all() and np.isnan(l[rows]).all(), (field, val)
         assert np.array_equal(o[~rows], good[~rows]) and np.array_equal(l[~rows], glse[~rows]), (field, val)
+    print("[case] an int4 range that does not end where the int8 run begins", flush=True)
+    j = int(np.nonzero((units[:, 0] == 0) & (units[:, 1] == 0) & (units[:, 2] == 5))[0][0])
+    assert units[j, 5] - units[j, 4] >= 1 and units[j, 5] == units[j, 3] - 1
+    bad = blob.copy()
+    bad[16 + 8 * j + 5] -= 1   # hi4: one block short of lo8 - 1
+    bad[16 + 8 * j + 7] -= 1   # ntiles that agrees with the shorter range
+    o, l = run(bad)
+    rows2 = np.zeros((b, hq, n), bool)
+    rows2[0, 0, 5 * blk:] = True
+    assert np.isnan(o[rows2]).all() and np.isnan(l[rows2]).all()
+    assert np.array_equal(o[~rows2], good[~rows2]) and np.array_equal(l[~rows2], glse[~rows2])
     print("[case] a unit that names no rows", flush=True)
     bad = blob.copy()
     bad[16 + 8 * i + 1] = 99                               # head 99 of 4
