@@ -197,6 +197,38 @@ def test_prefill_integer_inputs_and_determinism(tria):
     assert_close(out.cpu().numpy(), ref, "integer-exact all-kept")
 
 
+def test_prefill_unit_order_does_not_matter(tria):
+    """The schedule's record order is a dispatch order only: the same records in a
+    random order give the same output and LSE bit for bit (every unit computes its
+    own rows alone)."""
+    b, hq, hk, d, n, blk = 2, 4, 2, 128, 1500, 128
+    cfg = small_cfg(b, hq, hk, d, n, blk, seed=61)
+    q, k, v = inputs(cfg)
+    hi, keep = np.array([1, 0, 3, 2], np.int32), np.array([9, 4, 3, 11], np.int32)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    blob = tria.build_policy(dd, hi, keep)
+    qz = tria.quantize_qk(dd, dev(q), dev(k))
+    vd = dev(v)
+
+    def run(words):
+        out = torch.empty((b, hq, n, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((b, hq, n), dtype=torch.float32, device="cuda")
+        tria.prefill(dd, torch.from_numpy(words).cuda(), qz, vd, 1.0 / math.sqrt(d), out=out, lse=lse)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+    o0, l0 = run(blob)
+    units = blob[16:].reshape(-1, 8)
+    for seed in (1, 2):
+        perm = np.random.default_rng(seed).permutation(len(units))
+        shuffled = blob.copy()
+        shuffled[16:] = units[perm].reshape(-1)
+        o1, l1 = run(shuffled)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1), seed
+    ref = oracle.prefill(q, k, v, hi, keep, blk, 1.0 / math.sqrt(d))
+    assert_close(o0, ref, "prefill under the dispatch order")
+
+
 def test_prefill_skipped_blocks_never_read(tria):
     # NaN in key/value rows of blocks that every query block either skips or has
     # past the causal boundary must leave the output bit-identical
