@@ -301,10 +301,9 @@ def main():
             f"frac {t_roof / mean:.3f} (roofline {t_roof * 1e3:.3f} ms)")
         return res
 
-    if args.only == "prefill":   # profiler run: a few prefill launches only, back to
-        for _ in range(args.steps):   # back as in the measurement below
-            tria.prefill(dims, sched_dev, qz, v, sm, out=out)
-        torch.cuda.synchronize()
+    if args.only == "prefill":   # profiler run: prefill launches only, back to back
+        # after the same ~50 ms of untimed launches as the measurement below
+        back_to_back(lambda: tria.prefill(dims, sched_dev, qz, v, sm, out=out), args.steps)
         print("done", flush=True)
         return
     if args.only == "copy":      # profiler calibration: a plain 1 GiB device copy
