@@ -379,9 +379,10 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
 
 // ------------------------------------------------------------------ (3) prefill
 // The kernel addresses a unit's K, V and key-scale rows with 32-bit byte offsets from
-// the unit's first row (the widest, a V row, is 2 * head_dim bytes).
+// the unit's first row (the widest, a V row, is 2 * head_dim bytes), up to three
+// stages of 64 keys past the sequence's last block.
 static bool prefill_len_ok(const tria_dims* d) {
-  return ((int64_t)d->seq_len + d->block) * 2 * d->head_dim <= (int64_t)INT32_MAX;
+  return ((int64_t)d->seq_len + 4 * (int64_t)d->block) * 2 * d->head_dim <= (int64_t)INT32_MAX;
 }
 tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes, const int8_t* q8,
                          const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
@@ -409,7 +410,7 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
     return fail(TRIA_ERR_INVALID_ARG, "schedule for these dims is %zu bytes, got %zu", need, sched_bytes);
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (!prefill_len_ok(dims))
-    return fail(TRIA_ERR_UNSUPPORTED, "prefill supports (seq_len + block) * 2 * head_dim < 2^31, got seq_len %lld",
+    return fail(TRIA_ERR_UNSUPPORTED, "prefill supports (seq_len + 4 * block) * 2 * head_dim < 2^31, got seq_len %lld",
                 (long long)dims->seq_len);
   const int32_t* header = static_cast<const int32_t*>(sched_dev);
   return launched(tria::launch_prefill(shape_of(dims), header, TRIA_SCHED_VERSION, nb, n_units, nullptr, 0, q8, q4,
@@ -447,7 +448,7 @@ tria_status tria_prefill_varlen(const tria_dims* dims, int32_t n_seqs, const int
     return fail(TRIA_ERR_INVALID_ARG, "schedule for this batch is %zu bytes, got %zu", need, sched_bytes);
   if (!(sm_scale > 0.0f) || sm_scale > 1e30f) return fail(TRIA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (!prefill_len_ok(dims))
-    return fail(TRIA_ERR_UNSUPPORTED, "prefill supports (seq_len + block) * 2 * head_dim < 2^31, got seq_len %lld",
+    return fail(TRIA_ERR_UNSUPPORTED, "prefill supports (seq_len + 4 * block) * 2 * head_dim < 2^31, got seq_len %lld",
                 (long long)dims->seq_len);
   const int32_t* header = static_cast<const int32_t*>(sched_dev);
   const int32_t* seqs = header + TRIA_SCHED_HEADER_BYTES / 4 + 8 * n_units;

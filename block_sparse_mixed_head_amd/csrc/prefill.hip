@@ -648,8 +648,9 @@ prefill_kernel(Args a) {
   // base and its high 16); a stage passes its first key's byte offset as the scalar
   // offset and ends the resource at its last row inside the sequence (byte count =
   // that offset + its rows' bytes), so rows past the end read as zero.  Byte offsets
-  // are 32-bit (the host guarantees (seq_len + block) * 2 * head_dim < 2^31): a
-  // stage's addresses cost a few scalar instructions.
+  // are 32-bit (the host guarantees (seq_len + 4 * block) * 2 * head_dim < 2^31,
+  // which covers the three stages issued past the last one): a stage's addresses
+  // cost a few scalar instructions.
   const uint64_t k8u = uni64(reinterpret_cast<int64_t>(a.k8 + krow0 * D));
   const uint64_t k4u = uni64(reinterpret_cast<int64_t>(a.k4 + krow0 * (D / 2)));
   const uint64_t vu = uni64(reinterpret_cast<int64_t>(a.v + krow0 * D));
@@ -701,8 +702,10 @@ prefill_kernel(Args a) {
     };
     const int sh = is4 ? LOG2D - 1 : LOG2D;  // log2 of the K row bytes
     const uint32_t kw0 = pick(w0_of(k8u), w0_of(k4u)), kw1 = pick(w1_of(k8u), w1_of(k4u));
+    // a stage with no rows (past the last) gets an empty resource: no lane in range
+    // whatever the offset
     const int ksoff = key0 << sh;
-    const int kend = ksoff + (rows << sh);
+    const int kend = rows > 0 ? ksoff + (rows << sh) : 0;
     const uint32_t off = lo.gk8 ^ ((lo.gk8 ^ lo.gk4) & (is4 ? ~0u : 0u));
 #pragma unroll
     for (int j = 0; j < C::K8N; ++j) {
@@ -711,11 +714,11 @@ prefill_kernel(Args a) {
             lds_addr(kd + (wave + j * C::WAVES) * 1024));
     }
     const uint32_t sw0 = pick(w0_of(s8u), w0_of(s4u)), sw1 = pick(w1_of(s8u), w1_of(s4u));
-    dma4(rsrc(sw0, sw1, (key0 + rows) * 4), lo.gs, (uint32_t)(key0 * 4), lds_addr(sd));
+    dma4(rsrc(sw0, sw1, rows > 0 ? (key0 + rows) * 4 : 0), lo.gs, (uint32_t)(key0 * 4), lds_addr(sd));
     return make_int2(key0, rows);
   };
   auto issue_v = [&](int2 kr, lds_u8* vd) __attribute__((always_inline)) {
-    const v4u rv = rsrc(w0_of(vu), w1_of(vu), (kr.x + kr.y) * 2 * D);
+    const v4u rv = rsrc(w0_of(vu), w1_of(vu), kr.y > 0 ? (kr.x + kr.y) * 2 * D : 0);
     const uint32_t vsoff = (uint32_t)(kr.x * 2 * D);
 #pragma unroll
     for (int j = 0; j < C::VN; ++j)

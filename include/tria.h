@@ -173,9 +173,9 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
  * computes nothing and makes the rows it names NaN (a record
  * that names no rows writes nothing, so the rows of the unit it replaced keep what
  * `out` held).  The kernels always exit normally.
- * Errors: TRIA_ERR_UNSUPPORTED when (seq_len + block) * 2 * head_dim >= 2^31 (byte
- * offsets within a head's rows are 32-bit inside the kernel: seq_len below 8.4 M
- * tokens at head_dim 128).
+ * Errors: TRIA_ERR_UNSUPPORTED when (seq_len + 4 * block) * 2 * head_dim >= 2^31
+ * (byte offsets within a head's rows are 32-bit inside the kernel: seq_len below
+ * 8.4 M tokens at head_dim 128).
  */
 tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes,
                          const int8_t* q8, const uint8_t* q4, const float* q8s, const float* q4s,

@@ -259,9 +259,9 @@ def test_validation_errors(tria):
     mqa = tria.make_dims(1, 64, 1, 64, 64, 512)
     assert L.tria_decode(C.byref(mqa), one, 1 << 20, 512, one, C.c_float(0.125), one, one, 1 << 30,
                          None) == _lib.TRIA_ERR_UNSUPPORTED
-    # prefill byte offsets within a head's rows are 32-bit: (seq_len + block) * 2 * d < 2^31
+    # prefill byte offsets within a head's rows are 32-bit: (seq_len + 4 block) * 2 d < 2^31
     for d, blk in ((128, 128), (64, 64)):
-        n = (1 << 31) // (2 * d) - blk + 1
+        n = (1 << 31) // (2 * d) - 4 * blk + 1
         big = tria.make_dims(1, 1, 1, d, blk, n)
         need = 64 + 32 * ((n + blk - 1) // blk)
         assert L.tria_prefill(C.byref(big), one, need, *([one] * 8), one, C.c_float(0.125), one, None,
