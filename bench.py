@@ -4,8 +4,9 @@ A step is one pass of the whole path over one batch of the long-prefill workload
 (the largest of the path's workloads: b=1, 32 query / 8 KV heads, d=128,
 n=65536, block 128, seeded policies hi ~ U[2,16], keep ~ U[hi,128], K with four
 x8 outlier channels):
-  policy expansion (host) + schedule upload, Q/K quantisation, fused prefill,
-  compressed-cache packing for the last position, one-token decode.
+  policy expansion (host) + schedule upload, K quantisation, fused prefill (which
+  quantises each query block itself: tria_prefill_bf16q), compressed-cache packing
+  for the last position, one-token decode.
 `value` is whole-step prompt tokens per second with inputs already in HBM.
 
 The JSON line also carries
@@ -211,7 +212,7 @@ def main():
         pinned = [torch.empty(sched_bytes, dtype=torch.uint8).pin_memory() for _ in range(2)]
         pinned_ev = [torch.cuda.Event() for _ in range(2)]
         sched_dev = torch.empty(sched_bytes, dtype=torch.uint8, device="cuda")
-        qz = tria.quantize_qk(dims, q, k)
+        kz = tria.quantize_k(dims, k)
         out = torch.empty((b, hq, n, d), dtype=torch.float32, device="cuda")
         ctx = n
         cache_n = tria.kv_cache_bytes(dims, hi, keep, ctx)
@@ -231,8 +232,8 @@ def main():
                                                    C.c_void_p(buf.data_ptr()), sched_bytes, C.byref(need)))
         sched_dev.copy_(buf, non_blocking=True)
         pinned_ev[i % 2].record(stream)
-        tria.quantize_qk(dims, q, k, out=qz)
-        tria.prefill(dims, sched_dev, qz, v, sm, out=out)
+        tria.quantize_k(dims, k, out=kz)                        # K codes; Q is quantised
+        tria.prefill_bf16q(dims, sched_dev, q, kz, v, sm, out=out)  # inside the prefill
         tria.pack_kv_cache(dims, hi, keep, ctx, k, v, cache=cache)
         tria.decode(dims, cache, ctx, qdec, sm, out=dout, workspace=ws)
 
@@ -282,11 +283,11 @@ def main():
         ts = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)])
         return float(ts.mean()), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
-    def prefill_stats(name, dims_, sched_, qz_, v_, out_, W_, b_, hq_, d_, n_, reps):
+    def prefill_stats(name, dims_, sched_, q_, kz_, v_, out_, W_, b_, hq_, d_, n_, reps):
         """Prefill alone on one workload, launched back to back: HIP-event times and
         the MFMA roofline."""
         mean, med, p10, p90 = back_to_back(
-            lambda: tria.prefill(dims_, sched_, qz_, v_, 1.0 / math.sqrt(d_), out=out_), reps)
+            lambda: tria.prefill_bf16q(dims_, sched_, q_, kz_, v_, 1.0 / math.sqrt(d_), out=out_), reps)
         ops = 4.0 * d_ * W_                                # 2dW int8 ops + 2dW bf16 flops
         t_roof = 2.0 * d_ * W_ / (PEAK_INT8_TOPS * 1e12) + 2.0 * d_ * W_ / (PEAK_BF16_TFLOPS * 1e12)
         achieved = ops / mean / 1e12
@@ -303,7 +304,7 @@ def main():
 
     if args.only == "prefill":   # profiler run: prefill launches only, back to back
         # after the same ~50 ms of untimed launches as the measurement below
-        back_to_back(lambda: tria.prefill(dims, sched_dev, qz, v, sm, out=out), args.steps)
+        back_to_back(lambda: tria.prefill_bf16q(dims, sched_dev, q, kz, v, sm, out=out), args.steps)
         print("done", flush=True)
         return
     if args.only == "copy":      # profiler calibration: a plain 1 GiB device copy
@@ -331,8 +332,8 @@ def main():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 sched_dev.copy_(pinned[slot], non_blocking=True)
-                tria.quantize_qk(dims, q, k, out=qz)
-                tria.prefill(dims, sched_dev, qz, v, sm, out=out)
+                tria.quantize_k(dims, k, out=kz)
+                tria.prefill_bf16q(dims, sched_dev, q, kz, v, sm, out=out)
                 tria.pack_kv_cache(dims, hi, keep, ctx, k, v, cache=cache)
                 tria.decode(dims, cache, ctx, qdec, sm, out=dout, workspace=ws)
             graphs.append(g)
@@ -364,11 +365,11 @@ def main():
 
         # per-kernel device times (events on the launch stream, launches back to back as
         # in the step)
-        prefill_main = prefill_stats(args.workload, dims, sched_dev, qz, v, out, W, b, hq, d, n, args.reps)
-        q_mean = back_to_back(lambda: tria.quantize_qk(dims, q, k, out=qz), args.reps)[0]
+        prefill_main = prefill_stats(args.workload, dims, sched_dev, q, kz, v, out, W, b, hq, d, n, args.reps)
+        q_mean = back_to_back(lambda: tria.quantize_k(dims, k, out=kz), args.reps)[0]
         k_mean = back_to_back(lambda: tria.pack_kv_cache(dims, hi, keep, ctx, k, v, cache=cache), args.reps)[0]
         d_mean = back_to_back(lambda: tria.decode(dims, cache, ctx, qdec, sm, out=dout, workspace=ws), args.reps)[0]
-        del graphs, q, k, v, qz, out, cache, ws, sched_dev
+        del graphs, q, k, v, kz, out, cache, ws, sched_dev
         torch.cuda.empty_cache()
 
         # the other prefill workloads, prefill alone (their inputs drawn from the same recipe)
@@ -383,13 +384,13 @@ def main():
             so = tria.build_policy(do, ho, kpo)
             Wo = kept_pairs(so[16:].reshape(-1, 8), c.block, c.seq_len)
             sdo = torch.from_numpy(so).cuda()
-            qzo = tria.quantize_qk(do, qo, ko)
+            kzo = tria.quantize_k(do, ko)
             oo = torch.empty((c.batch, c.n_q_heads, c.seq_len, c.head_dim), dtype=torch.float32, device="cuda")
             for _ in range(2):
-                tria.prefill(do, sdo, qzo, vo, 1.0 / math.sqrt(c.head_dim), out=oo)
-            prefill_others[name] = prefill_stats(name, do, sdo, qzo, vo, oo, Wo, c.batch, c.n_q_heads, c.head_dim,
-                                                 c.seq_len, args.reps)
-            del qo, ko, vo, qzo, oo, sdo
+                tria.prefill_bf16q(do, sdo, qo, kzo, vo, 1.0 / math.sqrt(c.head_dim), out=oo)
+            prefill_others[name] = prefill_stats(name, do, sdo, qo, kzo, vo, oo, Wo, c.batch, c.n_q_heads,
+                                                 c.head_dim, c.seq_len, args.reps)
+            del qo, ko, vo, kzo, oo, sdo
             torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode workload (b16, ctx 32768)
@@ -699,9 +700,10 @@ def main():
                              f"{PEAK_BF16_TFLOPS:.0f} T/s combined in series"},
         "prefill": prefill_main,
         "prefill_workloads": prefill_others,
-        "kernels_ms": {"quantize": q_mean * 1e3, "prefill": prefill_main["ms"], "pack": k_mean * 1e3,
+        "kernels_ms": {"quantize_k": q_mean * 1e3, "prefill_bf16q": prefill_main["ms"], "pack": k_mean * 1e3,
                        "decode_step_workload": d_mean * 1e3},
-        # prompt tokens/s of the quantiser and the prefill kernel together (their device times)
+        # prompt tokens/s of the K quantiser and the prefill kernel (which quantises Q)
+        # together (their device times)
         "quantise_plus_prefill_tokens_per_s": b * n / (q_mean + prefill_main["ms"] * 1e-3),
         "decode": dec,
         "measured_ceilings": ceilings,

@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import TriaError, check, dims as make_dims  # noqa: F401
 
-__all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "prefill", "prefill_varlen", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
+__all__ = ["Dims", "build_policy", "build_policy_varlen", "quantize_qk", "quantize_k", "prefill", "prefill_bf16q", "prefill_varlen", "kv_cache_bytes", "pack_kv_cache", "update_kv_cache",
            "kv_cache_bytes_varlen", "pack_kv_cache_varlen", "decode_varlen",
            "check_cache", "decode_workspace_bytes", "decode", "block_summaries_bytes", "build_block_summaries",
            "skip_masks", "decode_skip_workspace_bytes", "decode_skip", "paged_page_bytes", "paged_table_bytes",
@@ -99,6 +99,29 @@ def quantize_qk(d: Dims, q: torch.Tensor, k: torch.Tensor, out: Optional[Quantiz
     return out
 
 
+@dataclass
+class QuantizedK:
+    k8: torch.Tensor
+    k4: torch.Tensor
+    k8s: torch.Tensor
+    k4s: torch.Tensor
+
+
+def quantize_k(d: Dims, k: torch.Tensor, out: Optional[QuantizedK] = None) -> QuantizedK:
+    """K codes and scales alone (as quantize_qk writes them), for prefill_bf16q."""
+    b, hk, hd, n = d.batch, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(k, torch.bfloat16, (b, hk, n, hd), "k")
+    dev = k.device
+    if out is None:
+        out = QuantizedK(torch.empty((b, hk, n, hd), dtype=torch.int8, device=dev),
+                         torch.empty((b, hk, n, hd // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((b, hk, n), dtype=torch.float32, device=dev),
+                         torch.empty((b, hk, n), dtype=torch.float32, device=dev))
+    check(_lib.lib.tria_quantize_k(C.byref(d), _ptr(k), _ptr(out.k8), _ptr(out.k4), _ptr(out.k8s), _ptr(out.k4s),
+                                   _stream(dev)))
+    return out
+
+
 # ------------------------------------------------------------------ (3) prefill
 def prefill(d: Dims, sched_dev: torch.Tensor, qz: Quantized, v: torch.Tensor, sm_scale: float,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -114,6 +137,25 @@ def prefill(d: Dims, sched_dev: torch.Tensor, qz: Quantized, v: torch.Tensor, sm
     check(_lib.lib.tria_prefill(C.byref(d), _ptr(sched_dev), nbytes, _ptr(qz.q8), _ptr(qz.q4), _ptr(qz.q8s),
                                 _ptr(qz.q4s), _ptr(qz.k8), _ptr(qz.k4), _ptr(qz.k8s), _ptr(qz.k4s), _ptr(v),
                                 float(sm_scale), _ptr(out), _ptr(lse), _stream(v.device)))
+    return out
+
+
+def prefill_bf16q(d: Dims, sched_dev: torch.Tensor, q: torch.Tensor, kz, v: torch.Tensor, sm_scale: float,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """prefill with Q as bf16, quantised inside the kernel; kz: QuantizedK (or
+    Quantized) holding the K codes and scales."""
+    b, hq, hk, hd, n = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.seq_len
+    _require(q, torch.bfloat16, (b, hq, n, hd), "q")
+    _require(v, torch.bfloat16, (b, hk, n, hd), "v")
+    if out is None:
+        out = torch.empty((b, hq, n, hd), dtype=torch.float32, device=v.device)
+    _require(out, torch.float32, (b, hq, n, hd), "out")
+    if lse is not None:
+        _require(lse, torch.float32, (b, hq, n), "lse")
+    nbytes = sched_dev.numel() * sched_dev.element_size()
+    check(_lib.lib.tria_prefill_bf16q(C.byref(d), _ptr(sched_dev), nbytes, _ptr(q), _ptr(kz.k8), _ptr(kz.k4),
+                                      _ptr(kz.k8s), _ptr(kz.k4s), _ptr(v), float(sm_scale), _ptr(out), _ptr(lse),
+                                      _stream(v.device)))
     return out
 
 

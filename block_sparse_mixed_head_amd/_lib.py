@@ -42,6 +42,8 @@ def _load() -> C.CDLL:
         "tria_build_policy": (C.c_int, [D, P, P, i32, P, sz, C.POINTER(sz)]),
         "tria_quantize_qk": (C.c_int, [D, P, P] + [P] * 8 + [P]),
         "tria_prefill": (C.c_int, [D, P, sz] + [P] * 8 + [P, f32, P, P, P]),
+        "tria_prefill_bf16q": (C.c_int, [D, P, sz, P] + [P] * 4 + [P, f32, P, P, P]),
+        "tria_quantize_k": (C.c_int, [D, P] + [P] * 4 + [P]),
         "tria_build_policy_varlen": (C.c_int, [D, P, P, i32, i32, P, P, sz, C.POINTER(sz)]),
         "tria_prefill_varlen": (C.c_int, [D, i32, P, P, sz] + [P] * 8 + [P, f32, P, P, P]),
         "tria_kv_cache_bytes": (C.c_int, [D, P, P, i32, i64, C.POINTER(sz)]),
@@ -91,6 +93,7 @@ def _load() -> C.CDLL:
 lib = _load()
 
 EXPORTED = ["tria_last_error", "tria_version", "tria_build_policy", "tria_quantize_qk", "tria_prefill",
+            "tria_prefill_bf16q", "tria_quantize_k",
             "tria_build_policy_varlen", "tria_prefill_varlen",
             "tria_kv_cache_bytes", "tria_pack_kv_cache", "tria_update_kv_cache", "tria_check_cache",
             "tria_kv_cache_bytes_varlen", "tria_pack_kv_cache_varlen", "tria_decode_varlen",

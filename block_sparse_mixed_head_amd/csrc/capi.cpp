@@ -377,6 +377,20 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
                   "quantize launch");
 }
 
+tria_status tria_quantize_k(const tria_dims* dims, const void* k_bf16, int8_t* k8, uint8_t* k4, float* k8s,
+                            float* k4s, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(k_bf16);
+  NONNULL(k8);
+  NONNULL(k4);
+  NONNULL(k8s);
+  NONNULL(k4s);
+  return launched(tria::launch_quantize(shape_of(dims), nullptr, k_bf16, nullptr, nullptr, nullptr, nullptr, k8, k4,
+                                        k8s, k4s, static_cast<hipStream_t>(stream)),
+                  "quantize launch");
+}
+
 // ------------------------------------------------------------------ (3) prefill
 // The kernel addresses a unit's K, V and key-scale rows with 32-bit byte offsets from
 // the unit's first row (the widest, a V row, is 2 * head_dim bytes), up to three
@@ -384,17 +398,13 @@ tria_status tria_quantize_qk(const tria_dims* dims, const void* q_bf16, const vo
 static bool prefill_len_ok(const tria_dims* d) {
   return ((int64_t)d->seq_len + 4 * (int64_t)d->block) * 2 * d->head_dim <= (int64_t)INT32_MAX;
 }
-tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes, const int8_t* q8,
-                         const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
-                         const uint8_t* k4, const float* k8s, const float* k4s, const void* v_bf16,
-                         float sm_scale, float* out, float* lse, void* stream) {
-  tria_status st = check_dims(dims);
-  if (st != TRIA_OK) return st;
+// Validation and launch shared by tria_prefill (codes q8 .. q4s) and
+// tria_prefill_bf16q (qraw: bf16 Q quantised inside the kernel).
+static tria_status prefill_fixed(const tria_dims* dims, const void* sched_dev, size_t sched_bytes, const int8_t* q8,
+                                 const uint8_t* q4, const float* q8s, const float* q4s, const void* qraw,
+                                 const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
+                                 const void* v_bf16, float sm_scale, float* out, float* lse, void* stream) {
   NONNULL(sched_dev);
-  NONNULL(q8);
-  NONNULL(q4);
-  NONNULL(q8s);
-  NONNULL(q4s);
   NONNULL(k8);
   NONNULL(k4);
   NONNULL(k8s);
@@ -414,9 +424,33 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
                 (long long)dims->seq_len);
   const int32_t* header = static_cast<const int32_t*>(sched_dev);
   return launched(tria::launch_prefill(shape_of(dims), header, TRIA_SCHED_VERSION, nb, n_units, nullptr, 0, q8, q4,
-                                       q8s, q4s, k8, k4, k8s, k4s, v_bf16, sm_scale, out, lse,
+                                       q8s, q4s, qraw, k8, k4, k8s, k4s, v_bf16, sm_scale, out, lse,
                                        static_cast<hipStream_t>(stream)),
                   "prefill launch");
+}
+
+tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sched_bytes, const int8_t* q8,
+                         const uint8_t* q4, const float* q8s, const float* q4s, const int8_t* k8,
+                         const uint8_t* k4, const float* k8s, const float* k4s, const void* v_bf16,
+                         float sm_scale, float* out, float* lse, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(q8);
+  NONNULL(q4);
+  NONNULL(q8s);
+  NONNULL(q4s);
+  return prefill_fixed(dims, sched_dev, sched_bytes, q8, q4, q8s, q4s, nullptr, k8, k4, k8s, k4s, v_bf16, sm_scale,
+                       out, lse, stream);
+}
+
+tria_status tria_prefill_bf16q(const tria_dims* dims, const void* sched_dev, size_t sched_bytes, const void* q_bf16,
+                               const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
+                               const void* v_bf16, float sm_scale, float* out, float* lse, void* stream) {
+  tria_status st = check_dims(dims);
+  if (st != TRIA_OK) return st;
+  NONNULL(q_bf16);
+  return prefill_fixed(dims, sched_dev, sched_bytes, nullptr, nullptr, nullptr, nullptr, q_bf16, k8, k4, k8s, k4s,
+                       v_bf16, sm_scale, out, lse, stream);
 }
 
 tria_status tria_prefill_varlen(const tria_dims* dims, int32_t n_seqs, const int64_t* cu_seqlens,
@@ -454,7 +488,7 @@ tria_status tria_prefill_varlen(const tria_dims* dims, int32_t n_seqs, const int
   const int32_t* seqs = header + TRIA_SCHED_HEADER_BYTES / 4 + 8 * n_units;
   return launched(tria::launch_prefill(shape_of(dims), header, TRIA_SCHED_VERSION_VARLEN,
                                        *std::max_element(nbs.begin(), nbs.end()), n_units, seqs, n_seqs, q8, q4, q8s,
-                                       q4s, k8, k4, k8s, k4s, v_bf16, sm_scale, out, lse,
+                                       q4s, nullptr, k8, k4, k8s, k4s, v_bf16, sm_scale, out, lse,
                                        static_cast<hipStream_t>(stream)),
                   "prefill launch");
 }

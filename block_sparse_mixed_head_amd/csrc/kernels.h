@@ -11,12 +11,15 @@ struct Shape {
   int64_t n;
 };
 
-// Per-row symmetric int8 / int4 quantisation of Q and K (one launch for both).
+// Per-row symmetric int8 / int4 quantisation of Q and K (one launch for both; q null:
+// K only, the Q outputs untouched).
 hipError_t launch_quantize(const Shape& s, const void* q, const void* k, int8_t* q8, uint8_t* q4,
                            float* q8s, float* q4s, int8_t* k8, uint8_t* k4, float* k8s, float* k4s,
                            hipStream_t stream);
 
 // Fused block-sparse prefill over the unit records of a schedule (device memory).
+// qraw (device bf16 Q, or null): the kernel quantises each unit's query rows itself
+// (same codes as launch_quantize) and q8 .. q4s are not read.
 // seqs (device, or null): {start, length} of n_seqs sequences packed along the rows of
 // one batch element (s.batch == 1, s.n = total rows); a unit's b is its sequence.
 // header: the device schedule (64-byte header, then the n_units records, then, for a
@@ -24,8 +27,8 @@ hipError_t launch_quantize(const Shape& s, const void* q, const void* k, int8_t*
 // its header must hold.
 hipError_t launch_prefill(const Shape& s, const int32_t* header, int version, int64_t nb, int64_t n_units,
                           const int32_t* seqs, int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s,
-                          const float* q4s, const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
-                          const void* v, float sm_scale, float* out, float* lse, hipStream_t stream);
+                          const float* q4s, const void* qraw, const int8_t* k8, const uint8_t* k4, const float* k8s,
+                          const float* k4s, const void* v, float sm_scale, float* out, float* lse, hipStream_t stream);
 
 // Per-KV-head policy passed by value to the cache kernels.
 struct KvPolicy {

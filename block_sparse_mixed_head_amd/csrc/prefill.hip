@@ -88,6 +88,7 @@ struct Args {
   const uint8_t* q4;
   const float* q8s;
   const float* q4s;
+  const uint16_t* qraw;  // bf16 Q [rows][D] when the kernel quantises its own query rows
   const int8_t* k8;
   const uint8_t* k4;
   const float* k8s;
@@ -598,7 +599,10 @@ __device__ __forceinline__ bool unit_of(const Args& a, Unit& un) {
   return true;
 }
 
-template <int D, int BLK>
+// QRAW: the query rows arrive as bf16 and each work group quantises its own block
+// (the rows no other unit reads) in the prologue, with the quantiser's arithmetic
+// (the same codes and scales as tria_quantize_qk), instead of reading codes.
+template <int D, int BLK, bool QRAW>
 __global__ void __launch_bounds__((Cfg<D, BLK>::THREADS))
 __attribute__((amdgpu_waves_per_eu(Cfg<D, BLK>::OCC, Cfg<D, BLK>::OCC)))
 prefill_kernel(Args a) {
@@ -745,13 +749,43 @@ prefill_kernel(Args a) {
     rs[g].row = wave * 32 + g * 16 + lr;
     const int64_t qi = (int64_t)qb * BLK + rs[g].row;
     const bool valid = qi < n;
+    float sq8, sq4;
+    if constexpr (QRAW) {
+      // lane (lr, kq) holds columns 64 ks + 16 kq .. + 15 of its row, as the codes'
+      // operand layout below wants; the row's other columns sit in lanes lr + 16 kq'
+      // (lane distances 16 and 32), so the row maximum is two lane swaps away
+      float x[C::KS][2][8];
+      float amax = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      q.q8[g][ks] = valid ? *reinterpret_cast<const v4i*>(a.q8 + (qrow0 + qi) * D + ks * 64 + kq * 16) : v4i{0, 0, 0, 0};
-      q.q4[g][ks] = valid ? *reinterpret_cast<const v2i*>(a.q4 + (qrow0 + qi) * (D / 2) + ks * 32 + kq * 8) : v2i{0, 0};
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint4 w = valid ? *reinterpret_cast<const uint4*>(a.qraw + (qrow0 + qi) * D + ks * 64 + kq * 16 + hh * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
+          bf16x8_to_f32(w, x[ks][hh]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ks][hh][i]));
+        }
+      amax = xmax32(xmax16(amax));
+      sq8 = 0.0f;
+      sq4 = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        uint32_t c8a[2], c8b[2], c4a, c4b;
+        codes_from_amax(x[ks][0], amax, c8a, c4a, sq8, sq4);
+        codes_from_amax(x[ks][1], amax, c8b, c4b, sq8, sq4);
+        q.q8[g][ks] = v4i{(int)c8a[0], (int)c8a[1], (int)c8b[0], (int)c8b[1]};
+        q.q4[g][ks] = v2i{(int)c4a, (int)c4b};
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        q.q8[g][ks] = valid ? *reinterpret_cast<const v4i*>(a.q8 + (qrow0 + qi) * D + ks * 64 + kq * 16) : v4i{0, 0, 0, 0};
+        q.q4[g][ks] = valid ? *reinterpret_cast<const v2i*>(a.q4 + (qrow0 + qi) * (D / 2) + ks * 32 + kq * 8) : v2i{0, 0};
+      }
+      sq8 = valid ? a.q8s[qrow0 + qi] : 0.0f;
+      sq4 = valid ? a.q4s[qrow0 + qi] : 0.0f;
     }
-    const float sq8 = valid ? a.q8s[qrow0 + qi] : 0.0f;
-    const float sq4 = valid ? a.q4s[qrow0 + qi] : 0.0f;
     // a row of zeros has scale 0; a tiny positive factor keeps -inf * a = -inf
     rs[g].a8 = fmaxf(sq8 * a.c, FLT_MIN);
     rs[g].a4 = fmaxf(sq4 * a.c * (1.0f / 256.0f), FLT_MIN);
@@ -867,7 +901,10 @@ prefill_kernel(Args a) {
 template <int D, int BLK>
 hipError_t launch_t(const Args& a, int64_t n_units, hipStream_t stream) {
   using C = Cfg<D, BLK>;
-  hipLaunchKernelGGL((prefill_kernel<D, BLK>), dim3((unsigned)n_units), dim3(C::THREADS), 0, stream, a);
+  if (a.qraw)
+    hipLaunchKernelGGL((prefill_kernel<D, BLK, true>), dim3((unsigned)n_units), dim3(C::THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BLK, false>), dim3((unsigned)n_units), dim3(C::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -875,8 +912,8 @@ hipError_t launch_t(const Args& a, int64_t n_units, hipStream_t stream) {
 
 hipError_t launch_prefill(const Shape& s, const int32_t* header, int version, int64_t nb, int64_t n_units,
                           const int32_t* seqs, int n_seqs, const int8_t* q8, const uint8_t* q4, const float* q8s,
-                          const float* q4s, const int8_t* k8, const uint8_t* k4, const float* k8s, const float* k4s,
-                          const void* v, float sm_scale, float* out, float* lse, hipStream_t stream) {
+                          const float* q4s, const void* qraw, const int8_t* k8, const uint8_t* k4, const float* k8s,
+                          const float* k4s, const void* v, float sm_scale, float* out, float* lse, hipStream_t stream) {
   Args a;
   a.header = header;
   a.units = header + TRIA_SCHED_HEADER_BYTES / 4;
@@ -889,6 +926,7 @@ hipError_t launch_prefill(const Shape& s, const int32_t* header, int version, in
   a.q4 = q4;
   a.q8s = q8s;
   a.q4s = q4s;
+  a.qraw = static_cast<const uint16_t*>(qraw);
   a.k8 = k8;
   a.k4 = k4;
   a.k8s = k8s;

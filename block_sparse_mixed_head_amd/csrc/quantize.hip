@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(kThreads) quantize_rows_kernel(const uint16_t*
 hipError_t launch_quantize(const Shape& s, const void* q, const void* k, int8_t* q8, uint8_t* q4,
                            float* q8s, float* q4s, int8_t* k8, uint8_t* k4, float* k8s, float* k4s,
                            hipStream_t stream) {
-  const int64_t q_rows = (int64_t)s.batch * s.hq * s.n;
+  const int64_t q_rows = q ? (int64_t)s.batch * s.hq * s.n : 0;  // (no Q: K rows only)
   const int64_t k_rows = (int64_t)s.batch * s.hkv * s.n;
   const int64_t rows = q_rows + k_rows;
   const int rows_per_block = kThreads / (s.d / 8);

@@ -183,6 +183,30 @@ tria_status tria_prefill(const tria_dims* dims, const void* sched_dev, size_t sc
                          const void* v_bf16, float sm_scale, float* out, float* lse, void* stream);
 
 /*
+ * The same prefill (TriAttention page, section on calibration: one fused kernel per
+ * layer) with Q given as bf16 [b][Hq][n][d] (device): every work unit quantises its
+ * own query block in the kernel (section on which links can be skipped: 8- and 4-bit
+ * tiles), with the quantiser's formula above
+ * (the same codes and scales as tria_quantize_qk), so no Q codes pass through memory;
+ * K comes from tria_quantize_k (or tria_quantize_qk).  out and lse are bit for bit
+ * those of tria_quantize_qk + tria_prefill.  Arguments, validation and errors as
+ * tria_prefill.  Device, asynchronous.
+ */
+tria_status tria_prefill_bf16q(const tria_dims* dims, const void* sched_dev, size_t sched_bytes,
+                               const void* q_bf16, const int8_t* k8, const uint8_t* k4, const float* k8s,
+                               const float* k4s, const void* v_bf16, float sm_scale, float* out, float* lse,
+                               void* stream);
+
+/*
+ * The quantiser's K half alone (TriAttention page, section on which links can be
+ * skipped): k8, k4, k8s, k4s exactly as tria_quantize_qk writes them (for
+ * tria_prefill_bf16q, which quantises Q itself).  Errors as tria_quantize_qk.
+ * Device, asynchronous.
+ */
+tria_status tria_quantize_k(const tria_dims* dims, const void* k_bf16, int8_t* k8, uint8_t* k4, float* k8s,
+                            float* k4s, void* stream);
+
+/*
  * Variable-length batches.  n_seqs causal sequences of different lengths packed
  * along the rows of one batch element: dims->batch == 1, dims->seq_len = the total
  * T, sequence s = rows [cu_seqlens[s], cu_seqlens[s + 1]) (host int64[n_seqs + 1],

@@ -259,6 +259,19 @@ def test_validation_errors(tria):
     mqa = tria.make_dims(1, 64, 1, 64, 64, 512)
     assert L.tria_decode(C.byref(mqa), one, 1 << 20, 512, one, C.c_float(0.125), one, one, 1 << 30,
                          None) == _lib.TRIA_ERR_UNSUPPORTED
+    # the fused-Q prefill and the K-only quantiser validate like their two-step forms
+    need_good = 64 + 32 * 2 * 8   # 2 heads x 8 query blocks of the (1, 2, 1, 64, 64, 512) dims
+    assert L.tria_prefill_bf16q(C.byref(good), one, need_good, None, *([one] * 4), one, C.c_float(0.125), one,
+                                None, None) == _lib.TRIA_ERR_INVALID_ARG          # no Q
+    assert L.tria_prefill_bf16q(C.byref(good), one, need_good - 1, one, *([one] * 4), one, C.c_float(0.125), one,
+                                None, None) == _lib.TRIA_ERR_BUFFER_TOO_SMALL
+    assert L.tria_prefill_bf16q(C.byref(good), one, need_good, one, *([one] * 4), one, C.c_float(0.0), one,
+                                None, None) == _lib.TRIA_ERR_INVALID_ARG          # sm_scale 0
+    assert L.tria_prefill_bf16q(C.byref(good), one, need_good, one, one, one, one, None, one, C.c_float(0.125), one,
+                                None, None) == _lib.TRIA_ERR_INVALID_ARG          # no K scales
+    assert L.tria_quantize_k(C.byref(good), one, one, one, one, None, None) == _lib.TRIA_ERR_INVALID_ARG
+    assert L.tria_quantize_k(C.byref(tria.make_dims(1, 2, 1, 96, 64, 512)), one, one, one, one, one,
+                             None) == _lib.TRIA_ERR_UNSUPPORTED
     # prefill byte offsets within a head's rows are 32-bit: (seq_len + 4 block) * 2 d < 2^31
     for d, blk in ((128, 128), (64, 64)):
         n = (1 << 31) // (2 * d) - 4 * blk + 1

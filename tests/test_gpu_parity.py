@@ -144,6 +144,47 @@ def test_prefill_small_every_output(tria, case):
     assert_lse_close(lse.cpu().numpy(), rlse, "prefill")
 
 
+@pytest.mark.parametrize("case", SMALL, ids=[f"b{c[0]}h{c[1]}k{c[2]}d{c[3]}n{c[4]}B{c[5]}" for c in SMALL])
+def test_prefill_bf16q_equals_two_step(tria, case):
+    """prefill_bf16q (Q quantised inside the kernel) gives out and LSE bit for bit
+    those of quantize_qk + prefill, and quantize_k writes quantize_qk's K outputs."""
+    b, hq, hk, d, n, blk, hi, keep = case
+    print(f"[case] prefill bf16q {case}", flush=True)
+    cfg = small_cfg(b, hq, hk, d, n, blk, seed=71)
+    q, k, v = inputs(cfg)
+    dd = tria.make_dims(b, hq, hk, d, blk, n)
+    sched = torch.from_numpy(tria.build_policy(dd, np.array(hi, np.int32), np.array(keep, np.int32))).cuda()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    sm = 1.0 / math.sqrt(d)
+    qz = tria.quantize_qk(dd, qd, kd)
+    kz = tria.quantize_k(dd, kd)
+    for name in ("k8", "k4", "k8s", "k4s"):
+        assert torch.equal(getattr(qz, name), getattr(kz, name)), name
+    lse0 = torch.empty((b, hq, n), dtype=torch.float32, device="cuda")
+    lse1 = torch.empty_like(lse0)
+    out0 = tria.prefill(dd, sched, qz, vd, sm, lse=lse0)
+    out1 = tria.prefill_bf16q(dd, sched, qd, kz, vd, sm, lse=lse1)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+
+def test_prefill_bf16q_full_size_layer(tria):
+    """The Llama-3-8B-shaped layer: the fused path equals the two-step path on every
+    output (the two-step path is compared with the oracle on every output above)."""
+    c = synth.CONFIGS["llama3_8b_layer"]
+    print("[case] prefill bf16q full-size llama3_8b_layer", flush=True)
+    q, k, v = (dev(x) for x in synth.make_prefill_inputs(c))
+    hi, keep = c.policy()
+    dd = tria.make_dims(c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim, c.block, c.seq_len)
+    sched = torch.from_numpy(tria.build_policy(dd, hi, keep)).cuda()
+    sm = 1.0 / math.sqrt(c.head_dim)
+    qz = tria.quantize_qk(dd, q, k)
+    out0 = tria.prefill(dd, sched, qz, v, sm)
+    out1 = tria.prefill_bf16q(dd, sched, q, tria.quantize_k(dd, k), v, sm)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+
+
 VARLEN = [
     # (hq, hk, d, blk, lengths, hi, keep)
     (4, 2, 64, 64, [1, 199, 63, 437, 64], [0, 1, 2, 9], [0, 4, 3, 9]),
