@@ -283,9 +283,10 @@ def main():
         ts = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)])
         return float(ts.mean()), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
-    def prefill_stats(name, dims_, sched_, q_, kz_, v_, out_, W_, b_, hq_, d_, n_, reps):
+    def prefill_stats(name, dims_, sched_, q_, kz_, qz_, v_, out_, W_, b_, hq_, d_, n_, reps):
         """Prefill alone on one workload, launched back to back: HIP-event times and
-        the MFMA roofline."""
+        the MFMA roofline, for the step's kernel (each query block quantised inside
+        it) and for the attention alone (qz_: codes from tria_quantize_qk)."""
         mean, med, p10, p90 = back_to_back(
             lambda: tria.prefill_bf16q(dims_, sched_, q_, kz_, v_, 1.0 / math.sqrt(d_), out=out_), reps)
         ops = 4.0 * d_ * W_                                # 2dW int8 ops + 2dW bf16 flops
@@ -298,8 +299,14 @@ def main():
                "frac_of_int8_peak": achieved / PEAK_INT8_TOPS, "kept_pairs": W_,
                "kept_density": W_ / (b_ * hq_ * n_ * (n_ + 1) / 2), "t_roof_ms": t_roof * 1e3,
                "traffic_bytes": measured_traffic(name)}
+        # the attention alone: the same prefill over Q codes quantised beforehand
+        # (tria_quantize_qk + tria_prefill), timed the same way
+        a_mean = back_to_back(lambda: tria.prefill(dims_, sched_, qz_, v_, 1.0 / math.sqrt(d_), out=out_), reps)[0]
+        res["attention_only"] = {"kernel": "tria_prefill over tria_quantize_qk codes", "ms": a_mean * 1e3,
+                                 "frac_of_roofline": t_roof / a_mean}
         log(f"[bench] prefill {name}: {mean * 1e3:.3f} ms, {achieved:.1f} T mixed ops/s, "
-            f"frac {t_roof / mean:.3f} (roofline {t_roof * 1e3:.3f} ms)")
+            f"frac {t_roof / mean:.3f} (roofline {t_roof * 1e3:.3f} ms); over codes quantised beforehand "
+            f"{a_mean * 1e3:.3f} ms, frac {t_roof / a_mean:.3f}")
         return res
 
     if args.only == "prefill":   # profiler run: prefill launches only, back to back
@@ -365,7 +372,9 @@ def main():
 
         # per-kernel device times (events on the launch stream, launches back to back as
         # in the step)
-        prefill_main = prefill_stats(args.workload, dims, sched_dev, q, kz, v, out, W, b, hq, d, n, args.reps)
+        qz = tria.quantize_qk(dims, q, k)
+        prefill_main = prefill_stats(args.workload, dims, sched_dev, q, kz, qz, v, out, W, b, hq, d, n, args.reps)
+        del qz
         q_mean = back_to_back(lambda: tria.quantize_k(dims, k, out=kz), args.reps)[0]
         k_mean = back_to_back(lambda: tria.pack_kv_cache(dims, hi, keep, ctx, k, v, cache=cache), args.reps)[0]
         d_mean = back_to_back(lambda: tria.decode(dims, cache, ctx, qdec, sm, out=dout, workspace=ws), args.reps)[0]
@@ -385,12 +394,13 @@ def main():
             Wo = kept_pairs(so[16:].reshape(-1, 8), c.block, c.seq_len)
             sdo = torch.from_numpy(so).cuda()
             kzo = tria.quantize_k(do, ko)
+            qzo = tria.quantize_qk(do, qo, ko)
             oo = torch.empty((c.batch, c.n_q_heads, c.seq_len, c.head_dim), dtype=torch.float32, device="cuda")
             for _ in range(2):
                 tria.prefill_bf16q(do, sdo, qo, kzo, vo, 1.0 / math.sqrt(c.head_dim), out=oo)
-            prefill_others[name] = prefill_stats(name, do, sdo, qo, kzo, vo, oo, Wo, c.batch, c.n_q_heads,
+            prefill_others[name] = prefill_stats(name, do, sdo, qo, kzo, qzo, vo, oo, Wo, c.batch, c.n_q_heads,
                                                  c.head_dim, c.seq_len, args.reps)
-            del qo, ko, vo, kzo, oo, sdo
+            del qo, ko, vo, kzo, qzo, oo, sdo
             torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode workload (b16, ctx 32768)
