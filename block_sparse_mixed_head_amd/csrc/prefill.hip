@@ -744,6 +744,25 @@ prefill_kernel(Args a) {
   QCodes<D> q;
   RowState rs[2];
   v4f O[2][C::NO];
+  // QRAW: every bf16 load of both row groups is issued before any is used, each from
+  // a row inside the sequence (a row past the end re-reads row n - 1 and is zeroed
+  // after it lands).  A load under a per-lane condition would be followed by a write
+  // of zeros to its destination register on the other lanes, which must wait for the
+  // load: one memory round trip per load.  Lane (lr, kq) holds columns 64 ks + 16 kq
+  // .. + 15 of its row, as the codes' operand layout below wants.
+  uint4 qw[QRAW ? 2 : 1][C::KS][2];
+  if constexpr (QRAW) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int64_t qi = (int64_t)qb * BLK + wave * 32 + g * 16 + lr;
+      const int64_t qr = qi < n ? qi : n - 1;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          qw[g][ks][hh] = *reinterpret_cast<const uint4*>(a.qraw + (qrow0 + qr) * D + ks * 64 + kq * 16 + hh * 8);
+    }
+  }
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     rs[g].row = wave * 32 + g * 16 + lr;
@@ -751,17 +770,15 @@ prefill_kernel(Args a) {
     const bool valid = qi < n;
     float sq8, sq4;
     if constexpr (QRAW) {
-      // lane (lr, kq) holds columns 64 ks + 16 kq .. + 15 of its row, as the codes'
-      // operand layout below wants; the row's other columns sit in lanes lr + 16 kq'
-      // (lane distances 16 and 32), so the row maximum is two lane swaps away
+      // the row's other columns sit in lanes lr + 16 kq' (lane distances 16 and 32),
+      // so the row maximum is two lane swaps away
       float x[C::KS][2][8];
       float amax = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const uint4 w = valid ? *reinterpret_cast<const uint4*>(a.qraw + (qrow0 + qi) * D + ks * 64 + kq * 16 + hh * 8)
-                                : make_uint4(0u, 0u, 0u, 0u);
+          const uint4 w = valid ? qw[g][ks][hh] : make_uint4(0u, 0u, 0u, 0u);
           bf16x8_to_f32(w, x[ks][hh]);
 #pragma unroll
           for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[ks][hh][i]));
