@@ -265,14 +265,14 @@ def main():
     def back_to_back(fn, reps):
         """Per-launch device times of fn() launched back to back (an event between
         consecutive launches on the stream, one synchronisation at the end), the way a
-        serving loop keeps the part busy; untimed launches first, about 50 ms of them,
-        so that the clock has settled (a short kernel after an idle host gap otherwise
-        starts at a lower clock)."""
+        serving loop keeps the part busy; untimed launches first, about 300 ms of them,
+        so that the clock has settled (after the idle gap of the host's input
+        generation, the first ~100 ms of a short kernel run measurably slower)."""
         t0 = time.perf_counter()
         fn()
         torch.cuda.synchronize()
         one = time.perf_counter() - t0
-        for _ in range(max(1, min(2000, int(0.05 / max(one, 1e-5))))):
+        for _ in range(max(1, min(5000, int(0.3 / max(one, 1e-5))))):
             fn()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record(stream)
@@ -310,7 +310,7 @@ def main():
         return res
 
     if args.only == "prefill":   # profiler run: prefill launches only, back to back
-        # after the same ~50 ms of untimed launches as the measurement below
+        # after the same ~300 ms of untimed launches as the measurement below
         back_to_back(lambda: tria.prefill_bf16q(dims, sched_dev, q, kz, v, sm, out=out), args.steps)
         print("done", flush=True)
         return
