@@ -409,15 +409,24 @@ def test_prefill_full_size_every_output(tria):
 
 @pytest.mark.parametrize("cid", ["long_prefill", "batched_mixed"])
 def test_prefill_full_size_sampled(tria, cid):
-    """The long-prefill and batched mixed-policy workloads at full size (the launch
-    the benchmark times), every row of the sampled query blocks of every head and
-    batch element against the oracle; every output finite."""
+    """The long-prefill and batched mixed-policy workloads at full size, every row of
+    the sampled query blocks of every head and batch element against the oracle;
+    every output finite; and the launch the benchmark times (query blocks quantised
+    inside the kernel, K codes from tria_quantize_k) equal to it on every output."""
     cfg = synth.CONFIGS[cid]
     q, k, v = inputs(cfg)
     hi, keep = cfg.policy()
     units = sample_units(cfg, hi, keep)
     print(f"[case] prefill full-size {cid}: {len(units)} sampled units", flush=True)
     out, lse, _ = run_prefill(tria, cfg, q, k, v, hi, keep, with_lse=True)
+    dd = tria.make_dims(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block, cfg.seq_len)
+    qd, kd = dev(q), dev(k)
+    lse1 = torch.empty_like(lse)
+    out1 = tria.prefill_bf16q(dd, torch.from_numpy(tria.build_policy(dd, hi, keep)).cuda(), qd,
+                              tria.quantize_k(dd, kd), dev(v), 1.0 / math.sqrt(cfg.head_dim), lse=lse1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out1) and torch.equal(lse, lse1), "fused-Q prefill differs from the two-step path"
+    del out1, lse1, qd, kd
     ref, rlse = oracle.prefill(q, k, v, hi, keep, cfg.block, 1.0 / math.sqrt(cfg.head_dim), units=units,
                                with_lse=True)
     got, want, gl, wl = [], [], [], []
