@@ -89,6 +89,16 @@ struct Hdr64 {
   int32_t w[16];
   __device__ int64_t q(int i) const { return (int64_t)(((uint64_t)(uint32_t)w[2 * i + 1] << 32) | (uint32_t)w[2 * i]); }
 };
+// Every word of a loaded header in scalar registers at this point: the loads of all
+// sixteen are issued before it and waited for once.  Without it the compiler moves
+// the load of a word that only some tests read into the branch of those tests, one
+// more memory round trip each.  Called after the other loads of the same round.
+__device__ __forceinline__ void pin_hdr(Hdr64& h) {
+  asm volatile(""
+               : "+s"(h.w[0]), "+s"(h.w[1]), "+s"(h.w[2]), "+s"(h.w[3]), "+s"(h.w[4]), "+s"(h.w[5]), "+s"(h.w[6]),
+                 "+s"(h.w[7]), "+s"(h.w[8]), "+s"(h.w[9]), "+s"(h.w[10]), "+s"(h.w[11]), "+s"(h.w[12]),
+                 "+s"(h.w[13]), "+s"(h.w[14]), "+s"(h.w[15]));
+}
 
 // Validates the global header against the launch; returns false on mismatch.
 template <int D, int BLK>
@@ -107,7 +117,8 @@ __device__ __forceinline__ bool header_ok_h(const DecArgs& a, const Hdr64& h, Ge
 }
 template <int D, int BLK>
 __device__ __forceinline__ bool header_ok(const DecArgs& a, Geo& geo) {
-  const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  pin_hdr(h);
   return header_ok_h<D, BLK>(a, h, geo);
 }
 
@@ -129,7 +140,8 @@ __device__ __forceinline__ bool paged_header_h(const DecArgs& a, const Hdr64& h,
 }
 template <int D, int BLK>
 __device__ __forceinline__ bool paged_header_ok(const DecArgs& a, Geo& geo) {
-  const Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  Hdr64 h = *reinterpret_cast<const Hdr64*>(a.cache);
+  pin_hdr(h);
   return paged_header_h<D, BLK>(a, h, geo);
 }
 
@@ -640,13 +652,15 @@ decode_split_kernel(DecArgs a) {
     }
   };
   Geo geo;
-  if (!(SKIP && a.paged ? paged_header_ok<D, BLK>(a, geo) : header_ok<D, BLK>(a, geo))) {
+  Hdr64 hdr = *reinterpret_cast<const Hdr64*>(a.cache);
+  pin_hdr(hdr);
+  if (!(SKIP && a.paged ? paged_header_h<D, BLK>(a, hdr, geo) : header_ok_h<D, BLK>(a, hdr, geo))) {
     if (blockIdx.x == 0 && tid == 0) reinterpret_cast<int*>(a.ws)[0] = 0;
     return;
   }
   if (tid == 0) bad = 0;
   // page slots per pair of a paged table (variable length: the header's)
-  const int prmax = SKIP && a.paged ? (a.varlen ? reinterpret_cast<const int32_t*>(a.cache)[6] : a.rmax) : 0;
+  const int prmax = SKIP && a.paged ? (a.varlen ? hdr.w[6] : a.rmax) : 0;
   __syncthreads();
   // ---- directory: record counts per pair, checked
   for (int p = tid; p < P; p += kThreads) {
@@ -880,9 +894,12 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(DecArgs a) {
   const int pair = b * a.hkv + h / G, row = h % G;
   const int* wsh = reinterpret_cast<const int*>(a.ws);
   float* dst = a.out + (int64_t)bh * D;
-  // header and slot range in one round (the workspace holds them for every pair)
-  const int valid = wsh[0], np = wsh[1];
-  const int2 range = *reinterpret_cast<const int2*>(wsh + 16 + 2 * pair);
+  // header and slot range in one round (the workspace holds them for every pair; the
+  // empty asm needs all four at once, so the range load is not moved behind the
+  // header test, a second round trip)
+  int valid = wsh[0], np = wsh[1];
+  int2 range = *reinterpret_cast<const int2*>(wsh + 16 + 2 * pair);
+  asm volatile("" : "+s"(valid), "+s"(np), "+s"(range.x), "+s"(range.y));
   const int i0 = range.x, i1 = range.x + range.y;
   if (valid != 1 || np != a.batch * a.hkv) {
     dst[t] = __int_as_float(0x7FC00000);  // NaN: the cache did not validate
@@ -984,7 +1001,8 @@ __device__ __forceinline__ bool skip_header_h(const SkipArgs& s, const Hdr64& h,
 }
 template <int D, int BLK>
 __device__ __forceinline__ bool skip_header_ok(const SkipArgs& s, Geo& geo) {
-  const Hdr64 h = *reinterpret_cast<const Hdr64*>(s.cache);
+  Hdr64 h = *reinterpret_cast<const Hdr64*>(s.cache);
+  pin_hdr(h);
   return skip_header_h<D, BLK>(s, h, geo);
 }
 
@@ -1177,6 +1195,7 @@ __device__ __forceinline__ int2 block_scan2_n(int x, int y, int* tmp, int& tx, i
 // directory checks of the decode (and that the pair's records start where the
 // previous pair's end).  With a masks buffer, the keep bits of every stored record.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanStageBytes = 72 * 1024;  // LDS for the index slots of one pass
 #pragma clang fp contract(off)
 template <int D, int BLK>
 __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
@@ -1186,11 +1205,18 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
   __shared__ int q2[2][32];
   __shared__ float ths[32];
   __shared__ int tmp[2 * NW];
+  __shared__ int stale_w[NW];
+  // index slots of the current pass, copied from memory with whole-row loads (lanes
+  // reading 16 bytes each from a different 272-byte slot pull a cache line per lane
+  // per load, several times the slots' bytes)
+  constexpr int CHMAX = kPlanStageBytes / S, SWEEPS = (kPlanStageBytes / 16 + kPlanThreads - 1) / kPlanThreads;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[CHMAX * S];
   const int tid = threadIdx.x, lane = tid & 63;
   const int G = a.hq / a.hkv, P = a.batch * a.hkv;
   int Gp = 1;
   while (Gp < G) Gp <<= 1;
   const int rpp = kPlanThreads / Gp, h = tid % Gp;
+  const int CH = rpp < CHMAX ? rpp : CHMAX;  // slots per pass
   const int p = blockIdx.x, b = p / a.hkv, g = p % a.hkv;
   // every load first, in one round trip: both headers, the directory entries of this
   // pair and the previous one, the query rows, the thresholds and this lane's first
@@ -1204,25 +1230,26 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
   uint4 qraw = make_uint4(0, 0, 0, 0);
   if (qrow < G) qraw = *reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + qrow) * D + qpart * 8);
   const float th_own = tid < G ? a.th[(int64_t)b * a.hq + g * G + tid] : 0.0f;
-  v4u lo[KW], hi[KW];
-  float smax = 0.0f;
-  double nmax = 0.0;
-  auto load_slot = [&](int r) __attribute__((always_inline)) {
-    if (r < a.rmax && h < G) {
-      const uint8_t* sp = a.sums + 64 + ((int64_t)p * a.rmax + r) * S;
+  // slots r0 .. r0 + n - 1 (n <= CH, r0 + n <= rmax): lane t loads 16-byte pieces t,
+  // t + 1024, ... of their contiguous bytes, then writes them to the stage
+  v4u piece[SWEEPS];
+  auto stage_load = [&](int r0, int n) __attribute__((always_inline)) {
+    const v4u* src = reinterpret_cast<const v4u*>(a.sums + 64 + ((int64_t)p * a.rmax + r0) * S);
+    const int npieces = n * (S / 16);
 #pragma unroll
-      for (int w = 0; w < KW; ++w) {
-        lo[w] = reinterpret_cast<const v4u*>(sp)[w];
-        hi[w] = reinterpret_cast<const v4u*>(sp + D)[w];
-      }
-      smax = *reinterpret_cast<const float*>(sp + 2 * D);
-      nmax = *reinterpret_cast<const double*>(sp + 2 * D + 8);
-    }
+    for (int i = 0; i < SWEEPS; ++i)
+      if (tid + i * kPlanThreads < npieces) piece[i] = src[tid + i * kPlanThreads];
+    return npieces;
   };
-  load_slot(tid / Gp);
-  // the stamp of index slot tid (a slot of this pair when tid < rmax)
-  const int stamp0 = tid < a.rmax ? *reinterpret_cast<const int*>(a.sums + 64 + ((int64_t)p * a.rmax + tid) * S + 2 * D + 4)
-                                  : 0;
+  auto stage_store = [&](int npieces) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < SWEEPS; ++i)
+      if (tid + i * kPlanThreads < npieces) reinterpret_cast<v4u*>(stage)[tid + i * kPlanThreads] = piece[i];
+  };
+  // the first pass's slots with the other loads (the record count is not known yet:
+  // every slot the pass could use)
+  const int first_pieces = stage_load(0, a.rmax < CH ? a.rmax : CH);
+  stage_store(first_pieces);
   // ---- checks (uniform)
   DecArgs da{};
   da.cache_bytes = a.cache_bytes;
@@ -1251,11 +1278,22 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
   {  // every stored record's slot was built for this current block (a variable-length
      // sequence that moved to another block, or restarted in one, leaves stale slots)
     bool stale = false;
+    const int staged = a.rmax < CH ? a.rmax : CH;
+    __syncthreads();  // the stage written
     if (ok)
       for (int r = tid; r < nrec; r += kPlanThreads)
-        stale = stale || (r == tid ? stamp0 : *reinterpret_cast<const int*>(a.sums + 64 + ((int64_t)p * a.rmax + r) * S +
-                                                                             2 * D + 4)) != cur + 1;
-    ok = ok && !__syncthreads_or(stale);
+        stale = stale || (r < staged ? *reinterpret_cast<const int*>(stage + r * S + 2 * D + 4)
+                                     : *reinterpret_cast<const int*>(a.sums + 64 + ((int64_t)p * a.rmax + r) * S +
+                                                                     2 * D + 4)) != cur + 1;
+    // (a block OR through LDS: __syncthreads_or reads the work-group size from the
+    // kernel's hidden arguments, one more memory round trip)
+    const bool wave_stale = __ballot(stale) != 0;
+    if (lane == 0) stale_w[tid >> 6] = wave_stale;
+    __syncthreads();
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any = any || stale_w[w] != 0;
+    ok = ok && !any;
   }
   int* pe = a.plan ? a.plan + 8 * (int64_t)p : nullptr;
   if (!ok) {
@@ -1298,14 +1336,28 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
   const uint32_t gm = G >= 32 ? 0xFFFFFFFFu : (1u << G) - 1u;
   int2* list = a.plan ? reinterpret_cast<int2*>(a.plan + 8 * (int64_t)P) + (int64_t)p * a.rmax : nullptr;
   int c8 = 0, c4 = 0;
-  for (int r0 = 0; r0 < nrec; r0 += rpp) {
-    const int r = r0 + tid / Gp;
-    if (r0 > 0) load_slot(r);
+  for (int r0 = 0; r0 < nrec; r0 += CH) {
+    if (r0 > 0) {  // the next slots, once every lane has read the previous ones
+      __syncthreads();
+      stage_store(stage_load(r0, nrec - r0 < CH ? nrec - r0 : CH));
+      __syncthreads();
+    }
+    const int rl = tid / Gp, r = r0 + rl;
+    const bool in = rl < CH && r < nrec;
     bool keep = false;
-    if (r < nrec && h < G) {
+    if (in && h < G) {
       if (r == 0 || r == n8 - 1) {
         keep = true;
       } else {
+        const uint8_t* sp = stage + rl * S;
+        v4u lo[KW], hi[KW];
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+          lo[w] = reinterpret_cast<const v4u*>(sp)[w];
+          hi[w] = reinterpret_cast<const v4u*>(sp + D)[w];
+        }
+        const float smax = *reinterpret_cast<const float*>(sp + 2 * D);
+        const double nmax = *reinterpret_cast<const double*>(sp + 2 * D + 8);
         const int pr = r < n8 ? 0 : 1;
         // per byte of q: the bound's coordinate is hi where the code is >= 0, else lo
         const v4u* qv = reinterpret_cast<const v4u*>(&qc[pr][h][0]);
@@ -1330,7 +1382,7 @@ __global__ void __launch_bounds__(kPlanThreads) skip_plan_kernel(SkipArgs a) {
     // the record's keep bits from its Gp lanes (aligned groups inside the wavefront)
     const uint64_t bal = __ballot(keep);
     const uint32_t mk = (uint32_t)(bal >> (lane & ~(Gp - 1))) & gm;
-    const bool lead = h == 0 && r < nrec;
+    const bool lead = h == 0 && in;
     if (lead && a.masks) a.masks[(int64_t)p * a.rmax + r] = mk;
     if (list) {
       const int f8 = lead && r < n8 && mk ? 1 : 0, f4 = lead && r >= n8 && mk ? 1 : 0;
