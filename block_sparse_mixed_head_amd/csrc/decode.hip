@@ -1182,7 +1182,8 @@ __device__ __forceinline__ int2 block_scan2_n(int x, int y, int* tmp, int& tx, i
 
 // The plan of one pair per work group of 1024 lanes, one lane per (record slot, query
 // head): Gp = G rounded up to a power of two consecutive lanes per record, so a pass
-// covers 1024 / Gp records.  Keep bits: for query head h (codes qc, scale sq at the
+// covers 1024 / Gp records, or the index slots that fit the 72 KB stage in LDS if
+// fewer.  Keep bits: for query head h (codes qc, scale sq at the
 // record's precision) and threshold th,
 //   box  = (t * smax) * max(sum_x max(qc_x lo_x, qc_x hi_x), 0),  t = sm_scale * sq
 //   norm = ((t * t) * |qc|^2) * nmax
