@@ -56,6 +56,10 @@ SKIP_CASES = [
     (3, 12, 4, 128, 700, 64, 650, [2, 0, 1, 5], [4, 9, 9, 5]),  # G = 3: lanes padded to 4
     (1, 4, 2, 128, 9000, 128, 8955, [3, 1], [40, 70]),       # 70 records per pair
     (1, 2, 2, 64, 64, 64, 1, [0, 0], [0, 0]),                 # a single token
+    # more records than one pass of the plan stages in LDS (256 slots at G = 4, d = 128;
+    # 512 at G = 1, d = 64, where lanes past the stage idle)
+    (1, 4, 1, 128, 128 * 300, 128, 128 * 300 - 5, [3], [290]),
+    (1, 2, 2, 64, 64 * 600, 64, 64 * 600 - 3, [5, 2], [560, 590]),
 ]
 IDS = [f"b{c[0]}h{c[1]}k{c[2]}d{c[3]}ctx{c[6]}B{c[5]}" for c in SKIP_CASES]
 
