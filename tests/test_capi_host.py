@@ -600,3 +600,17 @@ def test_paged_varlen_skip_calls_validate(tria):
     assert skip(th=None) == _lib.TRIA_ERR_INVALID_ARG
     assert skip(q=None) == _lib.TRIA_ERR_INVALID_ARG
     assert skip(scale=0.0) == _lib.TRIA_ERR_INVALID_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more, it prints one JSON line saying so and
+    exits with status 2 before touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
